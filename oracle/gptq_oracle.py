@@ -1,0 +1,502 @@
+"""Plain, slow CPU oracle of the GPTQ layer quantizer (fp64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the GPU
+path (no kernels, headers, helpers or constants) and imports nothing from it.
+
+Sources (the pages this restates; every function cites the passage it follows):
+
+* GPTQ paper summary page (azimuth.plus, "GPTQ: accurate post-training
+  quantization for generative pre-trained transformers"), sections on the
+  layer-wise objective, the OBQ background, the three innovations (fixed
+  column order, lazy batched updates, Cholesky of the inverse Hessian with
+  dampening) and the statement of the one-layer procedure.
+* Hugging Face Transformers "Quantization concepts" guide, sections "Mapping
+  values to fewer bits" (affine and symmetric quantization), "Choose
+  granularity" (per-tensor / per-channel / per-group) and "Data types - int8
+  and int4" (two int4 values per byte, first value in the low nibble).
+* The "What is quantization" explainer (taqaniya), section "How does it work,
+  with a simple example" (the absmax int8 example with range -127..127).
+
+The page's display formulas for the objective, the OBS update and the algorithm
+listing were lost in extraction; the readings used here are:
+
+* objective: ||W X - What X||^2 with X in the (tokens x d_col) layout, i.e.
+  ||X (W - What)^T||_F^2, and H = 2 X^T X (unnormalised);
+* dampening: lambda = percdamp * mean(diag H), added to the diagonal;
+* U is the upper Cholesky factor of (H + lambda I)^-1, i.e. (H + lambda I)^-1 = U^T U;
+  row c of U, divided by U[c, c], is the OBS update direction after
+  columns 0..c-1 are eliminated;
+* the step for column c: quantize, err = (w_c - q(w_c)) / U[c, c],
+  w[c+1:] -= err * U[c, c+1:];
+* group scale/zero of a group are computed, at the group's first column, from
+  the current (already compensated) values of the group's columns;
+* asymmetric grid [0, 2^b - 1] with S = (max - min) / (2^b - 1),
+  Z = -round(min / S16); symmetric grid +-(2^(b-1) - 1) with S = absmax / (2^(b-1) - 1),
+  Z = 0; S16 = fp16(S) is the scale used for quantizing and stored;
+* a code is decided in float32: q = clamp(rne(fl32(fl32(w) / S16) + Z)), as the
+  GPU does, so both sides round the same value; everything else is fp64;
+* stored codes are unsigned: u = q (asymmetric) or q + 2^(b-1) (symmetric), stored
+  zero z = Z or 2^(b-1); dequantisation is fl32(S16) * fl32(u - z).
+"""
+from __future__ import annotations
+
+import dataclasses
+import itertools
+from typing import Iterable
+
+import numpy as np
+
+
+class NotPositiveDefinite(ValueError):
+    def __init__(self, k: int):
+        super().__init__(f"leading minor of order {k} is not positive definite")
+        self.k = k
+
+
+class NonFinite(ValueError):
+    pass
+
+
+# ---------------------------------------------------------------------------
+# Scalar quantizers, exactly as the concept guide writes them.
+
+def affine_params(vmin: float, vmax: float, qmin: int, qmax: int) -> tuple[float, int]:
+    """S = (vmax - vmin) / (qmax - qmin); Z = qmin - round(vmin / S).
+
+    [Quantization concepts guide, "Mapping values to fewer bits": scale and zero point]
+    """
+    S = (vmax - vmin) / (qmax - qmin)
+    Z = qmin - int(np.rint(vmin / S))
+    return S, Z
+
+
+def affine_quantize(x, S, Z, qmin, qmax):
+    """q = round(x / S + Z), clamped to the grid.  [same section: quantize formula]"""
+    return np.clip(np.rint(np.asarray(x, dtype=np.float64) / S + Z), qmin, qmax).astype(np.int64)
+
+
+def affine_dequantize(q, S, Z):
+    """x ~= S * (q - Z).  [same section: dequantize formula]"""
+    return S * (np.asarray(q, dtype=np.float64) - Z)
+
+
+def symmetric_quantize(x, absmax: float, qmax: int):
+    """Range [-a, a], zero point fixed at 0: q = round(x * qmax / a), clamped to +-qmax.
+
+    [Quantization concepts guide, "Mapping values to fewer bits": symmetric form;
+     explainer page, "How does it work": absmax example with int8 range -127..127]
+    """
+    return np.clip(np.rint(np.asarray(x, dtype=np.float64) * (qmax / absmax)), -qmax, qmax).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Quantizer settings of the layer quantizer.
+
+@dataclasses.dataclass(frozen=True)
+class Params:
+    bits: int = 4
+    group_size: int = 128      # 0 = one group per row (per-channel)
+    sym: bool = False
+    block_size: int = 128
+    percdamp: float = 0.01
+
+    @property
+    def qmin(self) -> int:
+        return -(2 ** (self.bits - 1) - 1) if self.sym else 0
+
+    @property
+    def qmax(self) -> int:
+        return (2 ** (self.bits - 1) - 1) if self.sym else 2 ** self.bits - 1
+
+    @property
+    def zero_offset(self) -> int:
+        """Shift from the signed symmetric grid to the stored unsigned code."""
+        return 2 ** (self.bits - 1) if self.sym else 0
+
+    def group(self, d_col: int) -> int:
+        return d_col if self.group_size == 0 else self.group_size
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def _fp16_round(S: np.ndarray) -> np.ndarray:
+    """Round the (fp64) scale to fp16 (nearest even); returned as fp64 values."""
+    with np.errstate(over="ignore"):
+        return np.asarray(S, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def group_params(vals: np.ndarray, p: Params):
+    """Scale and zero point of one group for every row at once.
+
+    ``vals`` is (rows, g): the current values of the group's columns.
+    Returns (S, S16, Z): pre-rounding scale (fp64), fp16-rounded scale (as fp64)
+    and the integer zero point on the signed/unsigned grid.
+
+    [Quantization concepts guide, "Mapping values to fewer bits" (asymmetric:
+     literal min/max; symmetric: [-a, a], Z = 0) and "Choose granularity"
+     (one scale per group of consecutive weights of a row)]
+    """
+    qmin, qmax = p.qmin, p.qmax
+    if p.sym:
+        a = np.max(np.abs(vals), axis=1)
+        S = np.where(a > 0, a / qmax, 1.0)
+        S16 = _fp16_round(S)
+        Z = np.zeros(vals.shape[0], dtype=np.int64)
+    else:
+        mn = np.min(vals, axis=1)
+        mx = np.max(vals, axis=1)
+        # A constant group has no range; widen it to include 0 (the constant then
+        # sits on the top or bottom grid point, up to the fp16 rounding of S), and
+        # use S = 1 when the group is all zero.
+        flat = mn == mx
+        mn = np.where(flat, np.minimum(mn, 0.0), mn)
+        mx = np.where(flat, np.maximum(mx, 0.0), mx)
+        S = np.where(mx > mn, (mx - mn) / (qmax - qmin), 1.0)
+        S16 = _fp16_round(S)
+        # Z = qmin - round(min / S16), decided in float32 (same precision as the GPU)
+        t = (_f32(mn) / _f32(S16)).astype(np.float32)
+        Z = (qmin - np.rint(t)).astype(np.int64)
+    if not np.all(np.isfinite(S16)) or np.any(S16 < 2.0 ** -14):
+        raise NonFinite("scale is not a normal fp16 number")
+    return S, S16, Z
+
+
+def decide_codes(w: np.ndarray, S16: np.ndarray, Z: np.ndarray, p: Params) -> np.ndarray:
+    """q = clamp(round(w / S16 + Z)) on the signed (or unsigned) grid, decided in float32.
+
+    [Quantization concepts guide, "Mapping values to fewer bits": quantize formula;
+     the clamp keeps compensated values that left the group's range on the grid]
+    """
+    t = (_f32(w) / _f32(S16)).astype(np.float32)
+    u = (t + Z.astype(np.float32)).astype(np.float32)
+    return np.clip(np.rint(u), p.qmin, p.qmax).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Hessian, dampening, Cholesky factor of the inverse.
+
+def hessian(x_chunks: Iterable[np.ndarray]) -> np.ndarray:
+    """H = 2 X^T X over all calibration tokens (X is tokens x d_col), fp64.
+
+    [GPTQ summary page, statement of the one-layer procedure: H = 2 X X^T with the
+     page's X of shape d_col x tokens; the same matrix in the tokens-major layout]
+    """
+    H = None
+    for x in x_chunks:
+        x = np.asarray(x, dtype=np.float64)
+        part = x.T @ x
+        H = part if H is None else H + part
+    return 2.0 * H
+
+
+def damp(H: np.ndarray, percdamp: float) -> tuple[np.ndarray, float]:
+    """H + lambda I with lambda = percdamp * mean(diag H).
+
+    [GPTQ summary page, "Innovation 3": a small damping term lambda I for near-singular H]
+    """
+    lam = percdamp * float(np.mean(np.diag(H)))
+    return H + lam * np.eye(H.shape[0]), lam
+
+
+def cholesky_lower(A: np.ndarray) -> np.ndarray:
+    """Textbook unblocked Cholesky A = L L^T (lower), with the LAPACK failure rule.
+
+    Raises NotPositiveDefinite(k) when the leading minor of order k is not
+    positive definite (k is 1-based).
+    """
+    n = A.shape[0]
+    L = np.zeros_like(A, dtype=np.float64)
+    for j in range(n):
+        d = A[j, j] - L[j, :j] @ L[j, :j]
+        if not (d > 0.0):
+            raise NotPositiveDefinite(j + 1)
+        L[j, j] = np.sqrt(d)
+        L[j + 1:, j] = (A[j + 1:, j] - L[j + 1:, :j] @ L[j, :j]) / L[j, j]
+    return L
+
+
+def prepare_u(H: np.ndarray, percdamp: float) -> tuple[np.ndarray, float]:
+    """U = upper Cholesky factor of (H + lambda I)^-1, computed once.
+
+    (H + lambda I)^-1 = U^T U.  Row c of U gives the compensation direction for
+    column c after columns 0..c-1 have been quantized.
+    [GPTQ summary page, "Innovation 3": Cholesky decomposition of H^-1 computed once
+     in advance, entries read row by row, plus dampening]
+    """
+    Hd, lam = damp(H, percdamp)
+    try:
+        L = np.linalg.cholesky(Hd)
+    except np.linalg.LinAlgError:
+        # locate the failing leading minor with the textbook factorization
+        cholesky_lower(Hd)
+        raise NotPositiveDefinite(-1)
+    Linv = np.linalg.inv(L)
+    Hinv = Linv.T @ Linv
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    U = np.linalg.cholesky(Hinv).T
+    return U, lam
+
+
+def trailing_not_pd_order(H: np.ndarray, percdamp: float) -> int:
+    """Order k of the smallest trailing principal submatrix of H + lambda I that is not
+    positive definite (0 if it is positive definite).  This is the failure index of a
+    Cholesky factorization that starts from the last column (reverse order)."""
+    Hd, _ = damp(H, percdamp)
+    R = Hd[::-1, ::-1]
+    try:
+        cholesky_lower(R)
+    except NotPositiveDefinite as e:
+        return e.k
+    return 0
+
+
+# ---------------------------------------------------------------------------
+# The column sweep.
+
+@dataclasses.dataclass
+class Result:
+    q: np.ndarray          # signed (sym) or unsigned (asym) integer codes, d_row x d_col
+    codes: np.ndarray      # stored unsigned codes u, uint8, d_row x d_col
+    S: np.ndarray          # pre-rounding scales, d_row x n_groups (fp64)
+    scales16: np.ndarray   # fp16 scales, d_row x n_groups (np.float16)
+    zeros: np.ndarray      # stored zero points z, d_row x n_groups (int64)
+    what: np.ndarray       # dequantized weights S16 * (q - Z), fp64
+    w_at_q: np.ndarray     # the value each weight had when it was quantized (fp64)
+    t_at_q: np.ndarray     # fl32(fl32(w) / S16) + Z, the pre-rounding code value (float32)
+
+
+def _n_groups(d_col: int, p: Params) -> int:
+    g = p.group(d_col)
+    return (d_col + g - 1) // g
+
+
+def _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p) -> Result:
+    codes = (Q + p.zero_offset).astype(np.uint8)
+    zeros = (Z + p.zero_offset).astype(np.int64) if not p.sym else np.full_like(Z, p.zero_offset)
+    return Result(q=Q, codes=codes, S=S, scales16=S16.astype(np.float16), zeros=zeros,
+                  what=what, w_at_q=w_at_q, t_at_q=t_at_q)
+
+
+def gptq(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
+    """Unblocked GPTQ on one layer, columns in natural order, all rows at once.
+
+    For c = 0 .. d_col-1: (at a group's first column) group scale/zero from the
+    current values; quantize column c; err = (w_c - what_c) / U[c, c];
+    w[:, c+1:] -= err * U[c, c+1:].
+    [GPTQ summary page: OBQ background (quantize one weight, update the remaining
+     full-precision weights to compensate, direction given by H^-1); "Innovation 1"
+     (one fixed column order shared by all rows, so H_F^-1 is shared); "Innovation 3"
+     (rows of the Cholesky factor of H^-1 give the updates)]
+    """
+    W = np.array(W, dtype=np.float64, copy=True)
+    d_row, d_col = W.shape
+    g = p.group(d_col)
+    ng = _n_groups(d_col, p)
+    Q = np.zeros((d_row, d_col), dtype=np.int64)
+    S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    for c in range(d_col):
+        k = c // g
+        if c % g == 0:
+            S[:, k], S16[:, k], Z[:, k] = group_params(W[:, c:c + g], p)
+        w = W[:, c].copy()
+        w_at_q[:, c] = w
+        t_at_q[:, c] = ((_f32(w) / _f32(S16[:, k])).astype(np.float32) + Z[:, k].astype(np.float32)).astype(np.float32)
+        q = decide_codes(w, S16[:, k], Z[:, k], p)
+        Q[:, c] = q
+        what[:, c] = S16[:, k] * (q - Z[:, k])
+        err = (w - what[:, c]) / U[c, c]
+        W[:, c + 1:] -= np.outer(err, U[c, c + 1:])
+    return _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p)
+
+
+def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
+    """GPTQ with lazy batched updates in blocks of B columns.
+
+    Inside a block the updates stay local to the block; the error block E
+    (err of every column of the block) is then applied to all later columns in one
+    matrix product W[:, b1:] -= E @ U[b0:b1, b1:].
+    [GPTQ summary page, "Innovation 2": process B = 128 columns together, keep the
+     intermediate updates inside the block, then one large matrix update]
+    Needs the group to lie inside one block (block_size % group_size == 0) or one
+    group per row; otherwise a group's first column would see values that lack
+    this block's pending updates.
+    """
+    W = np.array(W, dtype=np.float64, copy=True)
+    d_row, d_col = W.shape
+    g = p.group(d_col)
+    B = p.block_size
+    if not (p.group_size == 0 or B % g == 0):
+        raise ValueError("group must not straddle a block")
+    ng = _n_groups(d_col, p)
+    Q = np.zeros((d_row, d_col), dtype=np.int64)
+    S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    for b0 in range(0, d_col, B):
+        b1 = min(b0 + B, d_col)
+        Wb = W[:, b0:b1].copy()
+        Eb = np.zeros((d_row, b1 - b0))
+        for j in range(b1 - b0):
+            c = b0 + j
+            k = c // g
+            if c % g == 0:
+                src = Wb[:, j:j + g] if g <= B else W[:, c:c + g]
+                S[:, k], S16[:, k], Z[:, k] = group_params(src, p)
+            w = Wb[:, j].copy()
+            w_at_q[:, c] = w
+            t_at_q[:, c] = ((_f32(w) / _f32(S16[:, k])).astype(np.float32) + Z[:, k].astype(np.float32)).astype(np.float32)
+            q = decide_codes(w, S16[:, k], Z[:, k], p)
+            Q[:, c] = q
+            what[:, c] = S16[:, k] * (q - Z[:, k])
+            err = (w - what[:, c]) / U[c, c]
+            Eb[:, j] = err
+            Wb[:, j + 1:] -= np.outer(err, U[c, c + 1:b1])
+        W[:, b1:] -= Eb @ U[b0:b1, b1:]
+    return _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p)
+
+
+def gptq_obs(W: np.ndarray, Hd: np.ndarray, p: Params) -> Result:
+    """GPTQ through explicit OBS elimination (no Cholesky factor).
+
+    Before quantizing column c the inverse of the remaining block Hd[c:, c:] is formed
+    directly; the update of the remaining weights is
+    -(w_c - q(w_c)) / [H_F^-1]_cc * [H_F^-1]_{c, :}.
+    [GPTQ summary page, OBQ background: update all remaining weights after each
+     quantization, direction given by the inverse Hessian of the remaining weights;
+     "Innovation 1": one order shared by all rows]
+    O(d_col^4); tiny layers only.
+    """
+    W = np.array(W, dtype=np.float64, copy=True)
+    d_row, d_col = W.shape
+    g = p.group(d_col)
+    ng = _n_groups(d_col, p)
+    Q = np.zeros((d_row, d_col), dtype=np.int64)
+    S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    for c in range(d_col):
+        k = c // g
+        if c % g == 0:
+            S[:, k], S16[:, k], Z[:, k] = group_params(W[:, c:c + g], p)
+        Finv = np.linalg.inv(Hd[c:, c:])
+        w = W[:, c].copy()
+        w_at_q[:, c] = w
+        q = decide_codes(w, S16[:, k], Z[:, k], p)
+        Q[:, c] = q
+        what[:, c] = S16[:, k] * (q - Z[:, k])
+        W[:, c + 1:] -= np.outer((w - what[:, c]) / Finv[0, 0], Finv[0, 1:])
+    return _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p)
+
+
+def rtn(W: np.ndarray, p: Params) -> Result:
+    """Round-to-nearest: every weight quantized on its own group grid, no compensation.
+
+    [GPTQ summary page, results: the RTN baseline]
+    """
+    W = np.asarray(W, dtype=np.float64)
+    d_row, d_col = W.shape
+    g = p.group(d_col)
+    ng = _n_groups(d_col, p)
+    Q = np.zeros((d_row, d_col), dtype=np.int64)
+    S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    what = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    for k in range(ng):
+        c0, c1 = k * g, min((k + 1) * g, d_col)
+        S[:, k], S16[:, k], Z[:, k] = group_params(W[:, c0:c1], p)
+        for c in range(c0, c1):
+            Q[:, c] = decide_codes(W[:, c], S16[:, k], Z[:, k], p)
+            what[:, c] = S16[:, k] * (Q[:, c] - Z[:, k])
+    return _finish(Q, S, S16, Z, what, W.copy(), t_at_q, p)
+
+
+# ---------------------------------------------------------------------------
+# Storage format and dequantisation.
+
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Two codes per byte for bits <= 4: byte k = u[2k] | u[2k+1] << 4 (first value in
+    the low nibble); one code per byte for 8 bits.
+
+    [Quantization concepts guide, "Data types - int8 and int4": two int4 values packed
+     in one byte, the first in the low 4 bits and the second in the high 4 bits]
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    if bits == 8:
+        return codes.copy()
+    if codes.shape[-1] % 2:
+        raise ValueError("odd number of columns")
+    lo = codes[..., 0::2] & 0xF
+    hi = codes[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack(packed: np.ndarray, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    if bits == 8:
+        return packed.copy()
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def dequantize(codes: np.ndarray, scales16: np.ndarray, zeros: np.ndarray, group_size: int) -> np.ndarray:
+    """What = S16 * (u - z), evaluated in float32 (exact: an fp16 times a small integer).
+
+    [Quantization concepts guide, "Mapping values to fewer bits": x ~= S (q - Z)]
+    """
+    codes = np.asarray(codes)
+    d_col = codes.shape[1]
+    g = d_col if group_size == 0 else group_size
+    idx = np.arange(d_col) // g
+    s = np.asarray(scales16, dtype=np.float16).astype(np.float32)[:, idx]
+    z = np.asarray(zeros).astype(np.float32)[:, idx]
+    return (s * (codes.astype(np.float32) - z)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# The layer objective.
+
+def recon_error_x(x_chunks: Iterable[np.ndarray], W: np.ndarray, What: np.ndarray) -> float:
+    """||X (W - What)^T||_F^2 summed over calibration tokens.
+
+    [GPTQ summary page, layer-wise objective: make the layer output with What as
+     close as possible to the output with W]
+    """
+    D = (np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)).T
+    tot = 0.0
+    for x in x_chunks:
+        y = np.asarray(x, dtype=np.float64) @ D
+        tot += float(np.sum(y * y))
+    return tot
+
+
+def recon_error_h(H: np.ndarray, W: np.ndarray, What: np.ndarray, per_row: bool = False):
+    """The same objective from H: 1/2 * sum_r (W_r - What_r) H (W_r - What_r)^T."""
+    D = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    rows = 0.5 * np.einsum("ij,jk,ik->i", D, H, D)
+    return rows if per_row else float(np.sum(rows))
+
+
+def brute_force_row(w: np.ndarray, H: np.ndarray, S16: float, Z: int, p: Params):
+    """Exhaustive minimum of (w - what) H (w - what)^T over every code vector on the
+    grid {S16 * (q - Z) : qmin <= q <= qmax}^d.  Tiny d only."""
+    d = w.shape[0]
+    levels = np.arange(p.qmin, p.qmax + 1)
+    vals = S16 * (levels - Z)
+    best, best_q = np.inf, None
+    # enumerate in slabs over the first coordinate to bound memory
+    rest = np.array(list(itertools.product(range(len(levels)), repeat=d - 1)), dtype=np.int64) if d > 1 else np.zeros((1, 0), dtype=np.int64)
+    for i0 in range(len(levels)):
+        cand = np.empty((rest.shape[0], d))
+        cand[:, 0] = vals[i0]
+        cand[:, 1:] = vals[rest]
+        D = w[None, :] - cand
+        e = np.einsum("ij,jk,ik->i", D, H, D)
+        j = int(np.argmin(e))
+        if e[j] < best:
+            best = float(e[j])
+            best_q = np.concatenate([[levels[i0]], levels[rest[j]]])
+    return best, best_q
