@@ -1,0 +1,175 @@
+/*
+ * gptq.h - C ABI of the GPTQ layer quantizer for AMD Instinct MI355X (gfx950).
+ *
+ * One linear layer y = W x with W of shape d_row x d_col is quantized to
+ * int4 / int3 (or int8) codes with one fp16 scale and zero point per group of
+ * consecutive weights of a row, guided by the Hessian of the layer-wise
+ * reconstruction objective built from calibration activations X.
+ *
+ * Method: GPTQ paper summary page (azimuth.plus, "GPTQ: accurate post-training
+ * quantization for generative pre-trained transformers"): layer-wise objective,
+ * OBQ-style compensation through the inverse Hessian, one fixed column order
+ * shared by all rows ("Innovation 1"), lazy batched updates in blocks of 128
+ * columns ("Innovation 2"), Cholesky factor of the inverse Hessian computed once
+ * with a small dampening term ("Innovation 3").  Quantizer and storage format:
+ * Hugging Face Transformers "Quantization concepts" guide ("Mapping values to
+ * fewer bits", "Choose granularity", "Data types - int8 and int4").
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument named as a matrix or buffer is a DEVICE pointer
+ *    unless its comment says "host".  The caller owns every buffer; the library
+ *    never allocates or frees memory and keeps no state between calls.
+ *  - Matrices are row-major.  All work is enqueued asynchronously on `stream`
+ *    (a hipStream_t; NULL = the default stream); no call synchronizes.
+ *  - Argument errors (null pointers, bad sizes, unsupported settings, a
+ *    workspace that is too small) are detected on the host before anything is
+ *    enqueued and returned immediately; nothing is written then.
+ *  - Conditions that only the device can see are reported through `*info`
+ *    (device int32), readable after the stream is synchronized: 0 = success,
+ *    k > 0 = a matrix that must be positive definite is not (see
+ *    gptq_prepare_hinv), -1 = a non-finite input or a scale that is not a
+ *    normal fp16 number.  The call itself still returns GPTQ_OK.
+ *  - Calls on one stream are ordered; concurrent calls on different streams
+ *    must not share output or workspace buffers.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GPTQ_OK = 0,
+    GPTQ_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size */
+    GPTQ_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+    GPTQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    GPTQ_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+    GPTQ_ERR_NOT_PD = 5,        /* used by bindings to report info > 0 */
+    GPTQ_ERR_NONFINITE = 6      /* used by bindings to report info == -1 */
+} gptq_status;
+
+typedef enum {
+    GPTQ_F32 = 0,
+    GPTQ_BF16 = 1,
+    GPTQ_F16 = 2
+} gptq_dtype;
+
+/* Quantizer settings (host struct). */
+typedef struct {
+    int32_t bits;        /* 3 or 4 (codes packed two per byte) or 8 (one per byte) */
+    int32_t group_size;  /* weights per scale/zero group along a row; must divide
+                            block_size and d_col; 0 = one group per row */
+    int32_t sym;         /* 0: asymmetric grid [0, 2^bits-1], S = (max-min)/(2^bits-1),
+                               Z = -round(min/S16);
+                            1: symmetric grid +-(2^(bits-1)-1), S = absmax/(2^(bits-1)-1),
+                               stored codes shifted by 2^(bits-1), stored zero 2^(bits-1) */
+    int32_t block_size;  /* lazy-update block width; this build supports 128 */
+} gptq_params;
+
+/*
+ * H += 2 * X^T X   (Hessian of the layer objective ||X (W - What)^T||^2)
+ *
+ * Source: GPTQ summary page, statement of the one-layer procedure (H = 2 X X^T
+ * with the page's d_col x tokens X; the same matrix for the tokens x d_col X used
+ * here).  Call once per chunk of calibration tokens; zero H before the first call.
+ *
+ *  H        d_col x d_col fp32, read and written.  H is kept symmetric: both
+ *           triangles are written with the same values.
+ *  X        n_tokens x d_col, row stride ldx elements (ldx >= d_col), dtype x_dtype.
+ *           GPTQ_BF16 products are exact in fp32 and run on bf16 MFMA;
+ *           GPTQ_F32 and GPTQ_F16 run on fp32 MFMA.
+ *  ws       device workspace of at least gptq_hessian_workspace_size(n_tokens, d_col)
+ *           bytes (split-K partial sums and tile counters); contents on entry are
+ *           ignored.  May be NULL when the size is 0.
+ * The accumulation order is fixed, so results are bitwise reproducible.
+ * n_tokens == 0 or d_col == 0 is a no-op.
+ */
+size_t gptq_hessian_workspace_size(int64_t n_tokens, int64_t d_col);
+gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype,
+                                    int64_t n_tokens, int64_t d_col, int64_t ldx,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * U = upper Cholesky factor of (H + lambda I)^-1, lambda = percdamp * mean(diag H):
+ * (H + lambda I)^-1 = U^T U, U upper triangular with a positive diagonal.
+ *
+ * Source: GPTQ summary page, "Innovation 3" (Cholesky decomposition of the inverse
+ * Hessian computed once in advance, entries read row by row; dampening term
+ * lambda I for near-singular H).  Computed as U = T^-1 where H + lambda I = T T^T
+ * with T upper triangular (a Cholesky factorization that starts from the last
+ * column), in fp64, then rounded to fp32.
+ *
+ *  H        d_col x d_col fp32 (only the upper triangle is read).
+ *  U        d_col x d_col fp32 output; the strictly lower triangle is written as 0.
+ *  ws       at least gptq_prepare_hinv_workspace_size(d_col) bytes.
+ *  info     device int32: 0, or k > 0 when the trailing principal submatrix of
+ *           H + lambda I of order k is not positive definite (U is then undefined),
+ *           or -1 when diag(H) holds a non-finite value.
+ */
+size_t gptq_prepare_hinv_workspace_size(int64_t d_col);
+gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float percdamp,
+                              void* ws, size_t ws_bytes, int32_t* info, void* stream);
+
+/*
+ * Quantize W column by column in natural order with error compensation through U.
+ *
+ * Sources: GPTQ summary page (OBQ background; "Innovation 1" fixed order;
+ * "Innovation 2" lazy blocks of 128 columns; "Innovation 3" rows of U);
+ * Quantization concepts guide ("Mapping values to fewer bits", "Choose
+ * granularity", "Data types - int8 and int4").
+ *
+ * For every row r and column c = 0..d_col-1: at the first column of a group the
+ * group's scale S and zero point Z are computed from the group's current
+ * (compensated) values and S16 = fp16(S); then
+ *     q = clamp(rne(w / S16 + Z))  (fp32, IEEE division), what = S16 (q - Z),
+ *     err = (w - what) / U[c][c],  w[c+1:] -= err * U[c][c+1:].
+ * Updates stay inside the current 128-column block; the block's errors are applied
+ * to the later columns in one matrix product per block.
+ *
+ *  W          d_row x d_col, dtype w_dtype (read only).
+ *  U          d_col x d_col fp32 from gptq_prepare_hinv (upper triangle read; the
+ *             strictly lower triangle of each 128x128 diagonal block must be 0).
+ *  p          host pointer to the settings.
+ *  codes      bits <= 4: d_row x d_col/2 bytes, column 2k in the low nibble of byte k,
+ *             column 2k+1 in the high nibble (d_col must be even);
+ *             bits == 8: d_row x d_col bytes.  Codes are unsigned (see gptq_params).
+ *  scales_f16 d_row x n_groups fp16 bit patterns (S16); n_groups = d_col/group_size,
+ *             or 1 when group_size == 0.
+ *  zeros_f16  d_row x n_groups fp16 bit patterns of the stored (integer) zero point.
+ *  ws         at least gptq_quantize_workspace_size(d_row, d_col, p) bytes.
+ *  info       device int32: 0, or -1 when W holds a non-finite value or a scale is
+ *             not a normal fp16 number.
+ * Rows are independent given U; d_row == 0 is a no-op.
+ */
+size_t gptq_quantize_workspace_size(int64_t d_row, int64_t d_col, const gptq_params* p);
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col,
+                                const float* U, const gptq_params* p,
+                                uint8_t* codes, uint16_t* scales_f16, uint16_t* zeros_f16,
+                                void* ws, size_t ws_bytes, int32_t* info, void* stream);
+
+/*
+ * W_out = S16 * (u - z) for every weight (computed in fp32, exact, then rounded
+ * to out_dtype with round-to-nearest-even).
+ *
+ * Source: Quantization concepts guide, "Mapping values to fewer bits"
+ * (x ~= S (q - Z)) and "Data types - int8 and int4" (unpacking two codes per byte).
+ *
+ *  codes, scales_f16, zeros_f16   as written by gptq_quantize_layer.
+ *  W_out      d_row x d_col, dtype out_dtype.
+ */
+gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16,
+                            const uint16_t* zeros_f16, int64_t d_row, int64_t d_col,
+                            int32_t bits, int32_t group_size,
+                            void* W_out, gptq_dtype out_dtype, void* stream);
+
+/* Host: a static message for a status code. */
+const char* gptq_status_string(gptq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTQ_MI355X_H */

@@ -133,8 +133,9 @@ def group_params(vals: np.ndarray, p: Params):
     """Scale and zero point of one group for every row at once.
 
     ``vals`` is (rows, g): the current values of the group's columns.
-    Returns (S, S16, Z): pre-rounding scale (fp64), fp16-rounded scale (as fp64)
-    and the integer zero point on the signed/unsigned grid.
+    Returns (S, S16, Z, zt): pre-rounding scale (fp64), fp16-rounded scale (as fp64),
+    the integer zero point on the signed/unsigned grid, and the float32 value
+    fl32(min) / S16 whose rounding gave Z (0 for the symmetric grid).
 
     [Quantization concepts guide, "Mapping values to fewer bits" (asymmetric:
      literal min/max; symmetric: [-a, a], Z = 0) and "Choose granularity"
@@ -146,6 +147,7 @@ def group_params(vals: np.ndarray, p: Params):
         S = np.where(a > 0, a / qmax, 1.0)
         S16 = _fp16_round(S)
         Z = np.zeros(vals.shape[0], dtype=np.int64)
+        t = np.zeros(vals.shape[0], dtype=np.float32)
     else:
         mn = np.min(vals, axis=1)
         mx = np.max(vals, axis=1)
@@ -162,7 +164,7 @@ def group_params(vals: np.ndarray, p: Params):
         Z = (qmin - np.rint(t)).astype(np.int64)
     if not np.all(np.isfinite(S16)) or np.any(S16 < 2.0 ** -14):
         raise NonFinite("scale is not a normal fp16 number")
-    return S, S16, Z
+    return S, S16, Z, t
 
 
 def decide_codes(w: np.ndarray, S16: np.ndarray, Z: np.ndarray, p: Params) -> np.ndarray:
@@ -264,6 +266,7 @@ class Result:
     S: np.ndarray          # pre-rounding scales, d_row x n_groups (fp64)
     scales16: np.ndarray   # fp16 scales, d_row x n_groups (np.float16)
     zeros: np.ndarray      # stored zero points z, d_row x n_groups (int64)
+    z_t: np.ndarray        # fl32(min) / S16, the value rounded to get Z (float32), d_row x n_groups
     what: np.ndarray       # dequantized weights S16 * (q - Z), fp64
     w_at_q: np.ndarray     # the value each weight had when it was quantized (fp64)
     t_at_q: np.ndarray     # fl32(fl32(w) / S16) + Z, the pre-rounding code value (float32)
@@ -274,10 +277,10 @@ def _n_groups(d_col: int, p: Params) -> int:
     return (d_col + g - 1) // g
 
 
-def _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p) -> Result:
+def _finish(Q, S, S16, Z, ZT, what, w_at_q, t_at_q, p) -> Result:
     codes = (Q + p.zero_offset).astype(np.uint8)
     zeros = (Z + p.zero_offset).astype(np.int64) if not p.sym else np.full_like(Z, p.zero_offset)
-    return Result(q=Q, codes=codes, S=S, scales16=S16.astype(np.float16), zeros=zeros,
+    return Result(q=Q, codes=codes, S=S, scales16=S16.astype(np.float16), zeros=zeros, z_t=ZT,
                   what=what, w_at_q=w_at_q, t_at_q=t_at_q)
 
 
@@ -298,11 +301,12 @@ def gptq(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    ZT = np.zeros((d_row, ng), dtype=np.float32)
     what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
     for c in range(d_col):
         k = c // g
         if c % g == 0:
-            S[:, k], S16[:, k], Z[:, k] = group_params(W[:, c:c + g], p)
+            S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(W[:, c:c + g], p)
         w = W[:, c].copy()
         w_at_q[:, c] = w
         t_at_q[:, c] = ((_f32(w) / _f32(S16[:, k])).astype(np.float32) + Z[:, k].astype(np.float32)).astype(np.float32)
@@ -311,7 +315,7 @@ def gptq(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
         what[:, c] = S16[:, k] * (q - Z[:, k])
         err = (w - what[:, c]) / U[c, c]
         W[:, c + 1:] -= np.outer(err, U[c, c + 1:])
-    return _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p)
+    return _finish(Q, S, S16, Z, ZT, what, w_at_q, t_at_q, p)
 
 
 def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
@@ -335,6 +339,7 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    ZT = np.zeros((d_row, ng), dtype=np.float32)
     what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
     for b0 in range(0, d_col, B):
         b1 = min(b0 + B, d_col)
@@ -345,7 +350,7 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
             k = c // g
             if c % g == 0:
                 src = Wb[:, j:j + g] if g <= B else W[:, c:c + g]
-                S[:, k], S16[:, k], Z[:, k] = group_params(src, p)
+                S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(src, p)
             w = Wb[:, j].copy()
             w_at_q[:, c] = w
             t_at_q[:, c] = ((_f32(w) / _f32(S16[:, k])).astype(np.float32) + Z[:, k].astype(np.float32)).astype(np.float32)
@@ -356,7 +361,7 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
             Eb[:, j] = err
             Wb[:, j + 1:] -= np.outer(err, U[c, c + 1:b1])
         W[:, b1:] -= Eb @ U[b0:b1, b1:]
-    return _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p)
+    return _finish(Q, S, S16, Z, ZT, what, w_at_q, t_at_q, p)
 
 
 def gptq_obs(W: np.ndarray, Hd: np.ndarray, p: Params) -> Result:
@@ -376,11 +381,12 @@ def gptq_obs(W: np.ndarray, Hd: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    ZT = np.zeros((d_row, ng), dtype=np.float32)
     what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
     for c in range(d_col):
         k = c // g
         if c % g == 0:
-            S[:, k], S16[:, k], Z[:, k] = group_params(W[:, c:c + g], p)
+            S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(W[:, c:c + g], p)
         Finv = np.linalg.inv(Hd[c:, c:])
         w = W[:, c].copy()
         w_at_q[:, c] = w
@@ -388,7 +394,7 @@ def gptq_obs(W: np.ndarray, Hd: np.ndarray, p: Params) -> Result:
         Q[:, c] = q
         what[:, c] = S16[:, k] * (q - Z[:, k])
         W[:, c + 1:] -= np.outer((w - what[:, c]) / Finv[0, 0], Finv[0, 1:])
-    return _finish(Q, S, S16, Z, what, w_at_q, t_at_q, p)
+    return _finish(Q, S, S16, Z, ZT, what, w_at_q, t_at_q, p)
 
 
 def rtn(W: np.ndarray, p: Params) -> Result:
@@ -402,14 +408,15 @@ def rtn(W: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
+    ZT = np.zeros((d_row, ng), dtype=np.float32)
     what = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
     for k in range(ng):
         c0, c1 = k * g, min((k + 1) * g, d_col)
-        S[:, k], S16[:, k], Z[:, k] = group_params(W[:, c0:c1], p)
+        S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(W[:, c0:c1], p)
         for c in range(c0, c1):
             Q[:, c] = decide_codes(W[:, c], S16[:, k], Z[:, k], p)
             what[:, c] = S16[:, k] * (Q[:, c] - Z[:, k])
-    return _finish(Q, S, S16, Z, what, W.copy(), t_at_q, p)
+    return _finish(Q, S, S16, Z, ZT, what, W.copy(), t_at_q, p)
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,201 @@
+"""GPTQ layer quantizer for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libgptq.so`` (C ABI declared in ``include/gptq.h``).
+Every step of the computation runs in the library's HIP kernels; this module only
+checks tensor placement/dtypes, allocates caller-owned buffers with PyTorch and
+passes raw device pointers and the current HIP stream.  If the library is missing
+the import fails: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgptq.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NOT_PD, ERR_NONFINITE = range(7)
+F32, BF16, F16 = 0, 1, 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("sym", ctypes.c_int32), ("block_size", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python -m post_weight_quantization_25_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "gptq_hessian_workspace_size": (sz, [i64, i64]),
+        "gptq_hessian_accumulate": (ctypes.c_int, [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp]),
+        "gptq_prepare_hinv_workspace_size": (sz, [i64]),
+        "gptq_prepare_hinv": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp, sz, vp, vp]),
+        "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
+        "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
+                                               vp, vp, vp, vp, sz, vp, vp]),
+        "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
+        "gptq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(s: int) -> str:
+    return lib.gptq_status_string(s).decode()
+
+
+def _check(s: int, what: str):
+    if s != OK:
+        raise GptqError(s, f"{what}: {status_string(s)}")
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws
+
+
+# ---------------------------------------------------------------- Hessian
+
+def hessian_workspace_size(n_tokens: int, d_col: int) -> int:
+    return lib.gptq_hessian_workspace_size(n_tokens, d_col)
+
+
+def hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """H += 2 X^T X (X: tokens x d_col, rows may be strided). Returns H."""
+    _dev(H, "H")
+    if H.dtype != torch.float32 or H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be a square float32 matrix")
+    if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1 or X.dtype not in _DT:
+        raise ValueError("X must be a 2-D device tensor with unit column stride (f32/bf16/f16)")
+    n, d = X.shape
+    if d != H.shape[0]:
+        raise ValueError("X width must match H")
+    ws = _workspace(hessian_workspace_size(n, d), X.device, ws)
+    _check(lib.gptq_hessian_accumulate(H.data_ptr(), X.data_ptr(), _DT[X.dtype], n, d, X.stride(0),
+                                       ws.data_ptr() if ws is not None else None,
+                                       ws.numel() if ws is not None else 0, _stream(stream)),
+           "gptq_hessian_accumulate")
+    return H
+
+
+# ---------------------------------------------------------------- preparation
+
+def prepare_hinv_workspace_size(d_col: int) -> int:
+    return lib.gptq_prepare_hinv_workspace_size(d_col)
+
+
+def prepare_hinv(H: torch.Tensor, percdamp: float = 0.01, U: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None, info: torch.Tensor | None = None, stream=None):
+    """Upper Cholesky factor U of (H + percdamp*mean(diag H) I)^-1.  Returns (U, info)."""
+    _dev(H, "H")
+    d = H.shape[0]
+    if U is None:
+        U = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    if info is None:
+        info = torch.zeros(1, dtype=torch.int32, device=H.device)
+    ws = _workspace(prepare_hinv_workspace_size(d), H.device, ws)
+    _check(lib.gptq_prepare_hinv(H.data_ptr(), U.data_ptr(), d, float(percdamp),
+                                 ws.data_ptr() if ws is not None else None,
+                                 ws.numel() if ws is not None else 0, info.data_ptr(), _stream(stream)),
+           "gptq_prepare_hinv")
+    return U, info
+
+
+# ---------------------------------------------------------------- quantization
+
+@dataclass
+class Quantized:
+    codes: torch.Tensor      # uint8, d_row x d_col/2 (bits <= 4) or d_row x d_col
+    scales: torch.Tensor     # float16, d_row x n_groups
+    zeros: torch.Tensor      # float16, d_row x n_groups (integer values)
+    info: torch.Tensor       # int32 device scalar
+    bits: int
+    group_size: int
+    d_col: int
+
+
+def make_params(bits=4, group_size=128, sym=False, block_size=128) -> Params:
+    return Params(bits, group_size, int(bool(sym)), block_size)
+
+
+def quantize_workspace_size(d_row: int, d_col: int, p: Params) -> int:
+    return lib.gptq_quantize_workspace_size(d_row, d_col, ctypes.byref(p))
+
+
+def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: int = 128, sym: bool = False,
+                   block_size: int = 128, ws: torch.Tensor | None = None, out: Quantized | None = None,
+                   stream=None) -> Quantized:
+    _dev(W, "W"); _dev(U, "U")
+    if W.dtype not in _DT or U.dtype != torch.float32:
+        raise ValueError("W must be f32/bf16/f16 and U float32")
+    d_row, d_col = W.shape
+    p = make_params(bits, group_size, sym, block_size)
+    n_groups = 1 if group_size == 0 else max(1, d_col // group_size)
+    if out is None:
+        cb = d_col // 2 if bits <= 4 else d_col
+        out = Quantized(torch.empty((d_row, cb), dtype=torch.uint8, device=W.device),
+                        torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
+                        torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
+                        torch.zeros(1, dtype=torch.int32, device=W.device), bits, group_size, d_col)
+    ws = _workspace(quantize_workspace_size(d_row, d_col, p), W.device, ws)
+    _check(lib.gptq_quantize_layer(W.data_ptr(), _DT[W.dtype], d_row, d_col, U.data_ptr(), ctypes.byref(p),
+                                   out.codes.data_ptr(), out.scales.data_ptr(), out.zeros.data_ptr(),
+                                   ws.data_ptr() if ws is not None else None,
+                                   ws.numel() if ws is not None else 0, out.info.data_ptr(), _stream(stream)),
+           "gptq_quantize_layer")
+    return out
+
+
+def dequantize(q: Quantized, out_dtype=torch.float32, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    d_row = q.codes.shape[0]
+    if out is None:
+        out = torch.empty((d_row, q.d_col), dtype=out_dtype, device=q.codes.device)
+    _check(lib.gptq_dequantize(q.codes.data_ptr(), q.scales.data_ptr(), q.zeros.data_ptr(), d_row, q.d_col,
+                               q.bits, q.group_size, out.data_ptr(), _DT[out.dtype], _stream(stream)),
+           "gptq_dequantize")
+    return out
+
+
+def check_info(info: torch.Tensor, what: str = "gptq"):
+    """Synchronize on ``info`` and raise on a device-detected failure."""
+    v = int(info.item())
+    if v > 0:
+        raise GptqError(ERR_NOT_PD, f"{what}: trailing principal submatrix of order {v} of the damped "
+                                    "Hessian is not positive definite")
+    if v < 0:
+        raise GptqError(ERR_NONFINITE, f"{what}: {status_string(ERR_NONFINITE)}")

@@ -1,0 +1,103 @@
+// C ABI of the GPTQ layer quantizer: argument validation, workspace sizing and
+// dispatch to the gfx950 kernels.  See include/gptq.h for the contract.
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace gptq;
+
+static bool valid_dtype(gptq_dtype t) { return t == GPTQ_F32 || t == GPTQ_BF16 || t == GPTQ_F16; }
+
+static gptq_status check_params(const gptq_params* p, int64_t d_col) {
+    if (p == nullptr) return GPTQ_ERR_INVALID_ARG;
+    if (p->bits != 3 && p->bits != 4 && p->bits != 8) return GPTQ_ERR_UNSUPPORTED;
+    if (p->block_size != 128) return GPTQ_ERR_UNSUPPORTED;
+    if (p->group_size < 0) return GPTQ_ERR_INVALID_ARG;
+    if (p->group_size > 0) {
+        if (p->block_size % p->group_size != 0 || d_col % p->group_size != 0) return GPTQ_ERR_INVALID_ARG;
+        if (p->group_size != 32 && p->group_size != 64 && p->group_size != 128) return GPTQ_ERR_UNSUPPORTED;
+    }
+    if (p->bits <= 4 && (d_col & 1)) return GPTQ_ERR_INVALID_ARG;
+    return GPTQ_OK;
+}
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+size_t gptq_hessian_workspace_size(int64_t n_tokens, int64_t d_col) {
+    if (n_tokens <= 0 || d_col <= 0) return 0;
+    return hessian_ws_bytes(n_tokens, d_col);
+}
+
+gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype, int64_t n_tokens, int64_t d_col,
+                                    int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
+    if (n_tokens < 0 || d_col < 0) return GPTQ_ERR_INVALID_ARG;
+    if (!valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
+    if (n_tokens == 0 || d_col == 0) return GPTQ_OK;
+    if (H == nullptr || X == nullptr || ldx < d_col) return GPTQ_ERR_INVALID_ARG;
+    if (d_col > 65536) return GPTQ_ERR_UNSUPPORTED;
+    return hessian_launch(H, X, x_dtype, n_tokens, d_col, ldx, ws, ws_bytes, (hipStream_t)stream);
+}
+
+size_t gptq_prepare_hinv_workspace_size(int64_t d_col) {
+    if (d_col <= 0) return 0;
+    return prep_ws_bytes(d_col);
+}
+
+gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float percdamp, void* ws, size_t ws_bytes,
+                              int32_t* info, void* stream) {
+    if (d_col < 0 || !(percdamp >= 0.f)) return GPTQ_ERR_INVALID_ARG;
+    if (d_col == 0) return GPTQ_OK;
+    if (H == nullptr || U == nullptr || info == nullptr) return GPTQ_ERR_INVALID_ARG;
+    if (d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
+    return prep_launch(H, U, d_col, percdamp, ws, ws_bytes, info, (hipStream_t)stream);
+}
+
+size_t gptq_quantize_workspace_size(int64_t d_row, int64_t d_col, const gptq_params* p) {
+    (void)p;
+    if (d_row <= 0 || d_col <= 0) return 0;
+    return quant_ws_bytes(d_row, d_col);
+}
+
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
+                                const gptq_params* p, uint8_t* codes, uint16_t* scales_f16, uint16_t* zeros_f16,
+                                void* ws, size_t ws_bytes, int32_t* info, void* stream) {
+    if (d_row < 0 || d_col < 0 || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_params(p, d_col);
+    if (st != GPTQ_OK) return st;
+    if (d_row == 0 || d_col == 0) return GPTQ_OK;
+    if (!W || !U || !codes || !scales_f16 || !zeros_f16 || !info) return GPTQ_ERR_INVALID_ARG;
+    if (d_row > 2147483647LL / 64 || d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
+    return quant_launch(W, w_dtype, d_row, d_col, U, *p, codes, scales_f16, zeros_f16, ws, ws_bytes, info,
+                        (hipStream_t)stream);
+}
+
+gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* zeros_f16,
+                            int64_t d_row, int64_t d_col, int32_t bits, int32_t group_size, void* W_out,
+                            gptq_dtype out_dtype, void* stream) {
+    if (d_row < 0 || d_col < 0 || !valid_dtype(out_dtype) || group_size < 0) return GPTQ_ERR_INVALID_ARG;
+    if (bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_UNSUPPORTED;
+    if (group_size > 0 && d_col % group_size != 0) return GPTQ_ERR_INVALID_ARG;
+    if (bits <= 4 && (d_col & 1)) return GPTQ_ERR_INVALID_ARG;
+    if (d_row == 0 || d_col == 0) return GPTQ_OK;
+    if (!codes || !scales_f16 || !zeros_f16 || !W_out) return GPTQ_ERR_INVALID_ARG;
+    if (d_row > 65535) return GPTQ_ERR_UNSUPPORTED;
+    return dequant_launch(codes, scales_f16, zeros_f16, d_row, d_col, bits, group_size, W_out, out_dtype,
+                          (hipStream_t)stream);
+}
+
+const char* gptq_status_string(gptq_status s) {
+    switch (s) {
+        case GPTQ_OK: return "ok";
+        case GPTQ_ERR_INVALID_ARG: return "invalid argument";
+        case GPTQ_ERR_UNSUPPORTED: return "unsupported setting or size";
+        case GPTQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case GPTQ_ERR_HIP: return "HIP runtime error";
+        case GPTQ_ERR_NOT_PD: return "damped Hessian is not positive definite";
+        case GPTQ_ERR_NONFINITE: return "non-finite input or scale outside the fp16 normal range";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

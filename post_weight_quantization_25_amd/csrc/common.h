@@ -1,0 +1,67 @@
+// Device helpers shared by the GPTQ kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gptq.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define GPTQ_DEV __device__ __forceinline__
+
+// bf16 / fp16 bit patterns <-> fp32 (exact widening; narrowing rounds to nearest even).
+GPTQ_DEV float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+GPTQ_DEV uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+GPTQ_DEV float f16_bits_to_f32(uint16_t b) {
+    _Float16 h = __builtin_bit_cast(_Float16, b);
+    return (float)h;
+}
+
+GPTQ_DEV uint16_t f32_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+template <gptq_dtype DT>
+GPTQ_DEV float load_as_f32(const void* base, int64_t idx) {
+    if constexpr (DT == GPTQ_F32) return reinterpret_cast<const float*>(base)[idx];
+    else if constexpr (DT == GPTQ_BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+    else return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+}
+
+// DPP broadcast of lane `src` of each group of 4 lanes to the whole group.
+template <int SRC>
+GPTQ_DEV float quad_bcast(float v) {
+    constexpr int ctrl = SRC | (SRC << 2) | (SRC << 4) | (SRC << 6);  // quad_perm
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xf, 0xf, false));
+}
+
+// DPP quad_perm with an arbitrary pattern.
+template <int CTRL>
+GPTQ_DEV float quad_perm(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+GPTQ_DEV int quad_perm_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+// quad_perm encodings: lane i of the quad reads lane sel[i].
+constexpr int QP_XOR1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // [1,0,3,2]
+constexpr int QP_XOR2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // [2,3,0,1]
+
+// Launch-error helper for the host side.
+#define GPTQ_LAUNCH_CHECK()                                   \
+    do {                                                      \
+        if (hipGetLastError() != hipSuccess) return GPTQ_ERR_HIP; \
+    } while (0)

@@ -1,0 +1,29 @@
+// Host-side launchers of the GPTQ kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gptq.h"
+
+namespace gptq {
+
+void fill_i32(int32_t* p, int n, int v, hipStream_t s);
+
+size_t hessian_ws_bytes(int64_t n_tokens, int64_t d_col);
+gptq_status hessian_launch(float* H, const void* X, gptq_dtype dt, int64_t n, int64_t d, int64_t ldx,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+size_t prep_ws_bytes(int64_t d_col);
+gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, void* ws, size_t ws_bytes,
+                        int32_t* info, hipStream_t stream);
+
+size_t quant_ws_bytes(int64_t d_row, int64_t d_col);
+gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
+                         const gptq_params& p, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                         void* ws, size_t ws_bytes, int32_t* info, hipStream_t stream);
+
+gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
+                           int64_t d_col, int bits, int group_size, void* out, gptq_dtype out_dtype,
+                           hipStream_t stream);
+
+}  // namespace gptq

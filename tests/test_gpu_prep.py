@@ -1,0 +1,62 @@
+"""GPU parity of gptq_prepare_hinv against the oracle (same fp32 H on both sides)."""
+import numpy as np
+import pytest
+
+from gpu_helpers import log
+from oracle import gptq_oracle as o
+
+pytestmark = pytest.mark.gpu
+
+
+def _h(d, n, seed):
+    rng = np.random.default_rng([seed, d])
+    s = rng.lognormal(0.0, 1.0, size=d)
+    A = np.eye(d) + 0.5 * rng.standard_normal((d, d)) / np.sqrt(d)
+    x = (rng.standard_normal((n, d)) * s) @ A
+    return o.hessian([x]).astype(np.float32)
+
+
+def _gpu_u(H32, percdamp=0.01):
+    import torch
+    import post_weight_quantization_25_amd as g
+    Hd = torch.from_numpy(H32).cuda()
+    U, info = g.prepare_hinv(Hd, percdamp)
+    torch.cuda.synchronize()
+    return U.cpu().numpy(), int(info.item())
+
+
+@pytest.mark.parametrize("d", [1, 37, 64, 65, 130, 200, 520, 1024])
+def test_prep_parity(d):
+    log(f"prep parity d={d}")
+    H32 = _h(d, max(2 * d, 64), 3)
+    Uo, _ = o.prepare_u(H32.astype(np.float64), 0.01)
+    Ug, info = _gpu_u(H32)
+    assert info == 0
+    assert np.all(np.tril(Ug, -1) == 0.0)
+    # fp64 inside, fp32 output: the rounding of U dominates (2^-24 relative per entry)
+    rowmax = np.max(np.abs(Uo), axis=1, keepdims=True)
+    err = float(np.max(np.abs(Ug - Uo) / rowmax))
+    log(f"  max |dU| / rowmax = {err:.3e}")
+    assert err <= 1e-6
+
+
+@pytest.mark.parametrize("d,neg", [(4, 2), (200, 150), (200, 0), (129, 128)])
+def test_prep_not_positive_definite(d, neg):
+    H = np.diag(np.linspace(1.0, 2.0, d)).astype(np.float32)
+    H[neg, neg] = -1.0
+    want = o.trailing_not_pd_order(H.astype(np.float64), 0.0)
+    assert want == d - neg
+    _, info = _gpu_u(H, percdamp=0.0)
+    assert info == want
+
+
+def test_prep_zero_hessian_without_damping():
+    _, info = _gpu_u(np.zeros((10, 10), dtype=np.float32), percdamp=0.0)
+    assert info == o.trailing_not_pd_order(np.zeros((10, 10)), 0.0) == 1
+
+
+def test_prep_nonfinite_diagonal():
+    H = np.eye(70, dtype=np.float32)
+    H[5, 5] = np.nan
+    _, info = _gpu_u(H)
+    assert info == -1

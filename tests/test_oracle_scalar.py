@@ -36,7 +36,7 @@ def test_affine_example_through_group_params_unsigned_grid():
     g = _load("affine_int8_example.json")
     p = o.Params(bits=8, group_size=0, sym=False)
     vals = np.array([[g["vmin"], g["x"], 0.0, g["vmax"]]])
-    S, S16, Z = o.group_params(vals, p)
+    S, S16, Z, _ = o.group_params(vals, p)
     assert abs(S[0] - (g["vmax"] - g["vmin"]) / 255) < 1e-15
     assert Z[0] == g["Z"] + 128
     q = o.decide_codes(vals[0], S16, np.repeat(Z, 4), p)
@@ -53,7 +53,7 @@ def test_absmax_worked_example():
     assert list(q) == g["q"]
     # same result through the layer quantizer's symmetric group rule (fp16 scale)
     p = o.Params(bits=8, group_size=0, sym=True)
-    S, S16, Z = o.group_params(x[None, :], p)
+    S, S16, Z, _ = o.group_params(x[None, :], p)
     assert abs(S[0] - g["absmax"] / g["qmax"]) < 1e-15
     q2 = o.decide_codes(x, np.repeat(S16, x.size), np.repeat(Z, x.size), p)
     assert list(q2) == g["q"]
@@ -103,7 +103,7 @@ def test_dequantize_matches_definition():
 def test_group_params_degenerate_groups():
     p = o.Params(bits=4, group_size=0, sym=False)
     vals = np.array([[0.5, 0.5, 0.5], [0.0, 0.0, 0.0], [-0.25, -0.25, -0.25]])
-    S, S16, Z = o.group_params(vals, p)
+    S, S16, Z, _ = o.group_params(vals, p)
     for r in range(3):
         q = o.decide_codes(vals[r], np.repeat(S16[r], 3), np.repeat(Z[r], 3), p)
         # the constant lands on an end of the grid: exact up to the fp16 rounding of S
@@ -115,7 +115,7 @@ def test_group_params_symmetric_int3():
     p = o.Params(bits=3, group_size=0, sym=True)
     assert (p.qmin, p.qmax, p.zero_offset) == (-3, 3, 4)
     vals = np.array([[0.3, -0.9, 0.6, 0.1]])
-    S, S16, Z = o.group_params(vals, p)
+    S, S16, Z, _ = o.group_params(vals, p)
     assert abs(S[0] - 0.3) < 1e-15 and Z[0] == 0
     q = o.decide_codes(vals[0], np.repeat(S16, 4), np.repeat(Z, 4), p)
     assert list(q) == [1, -3, 2, 0]
