@@ -1,0 +1,225 @@
+"""Benchmark: one GPTQ layer quantization (int4, group 128) of a 4096 x 4096 layer on
+one MI355X.
+
+A step is one pass of the whole path on inputs already resident in HBM:
+zero H, H += 2 X^T X over 262144 calibration tokens (bf16), damping + Cholesky
+factor of the inverse (fp64), the blocked column sweep with trailing updates
+(int4 asymmetric, group 128, B = 128), and dequantization of the result.
+Prints one JSON line.  ``value`` = quantized weights per second.
+
+Options: --steps K --warmup W --gpus N (only 1 is supported: the path runs on one
+GPU) --no-cpu-baseline --calibrate-copy (adds one plain 1 GiB device copy after
+the timed region, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ quantized weights/sec + ms/layer (int4 g128) at 4096x4096, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0
+HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hess_bf16_c2_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(name: str) -> str:
+    with open(os.path.join(ROOT, "post_weight_quantization_25_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_alg: float):
+    """HBM bytes per Hessian launch from the committed rocprofv3 counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash("hessian.hip"):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(layer, sample_tokens: int, sample_rows: int):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to one layer."""
+    import numpy as np
+
+    import synth
+    from oracle import gptq_oracle as o
+
+    t0 = time.perf_counter()
+    scales = synth.channel_scales(layer)
+    chunks = [synth.x_as_f64(synth.x_chunk(layer, c, scales)) for c in range(sample_tokens // synth.CHUNK)]
+    t_gen = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Hs = o.hessian(chunks)
+    t_hess = time.perf_counter() - t0
+    H = Hs * (layer.n_tokens / sample_tokens)
+    t0 = time.perf_counter()
+    U, _ = o.prepare_u(H, 0.01)
+    t_prep = time.perf_counter() - t0
+    W = synth.w_as_f64(synth.weights(layer))[:sample_rows]
+    t0 = time.perf_counter()
+    o.gptq_blocked(W, U, o.Params(bits=4, group_size=128))
+    t_sweep = time.perf_counter() - t0
+    hess_full = t_hess * layer.n_tokens / sample_tokens
+    sweep_full = t_sweep * layer.d_row / sample_rows
+    total = hess_full + t_prep + sweep_full
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {
+        "value": layer.d_row * layer.d_col / total,
+        "unit": "weights/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: H on {sample_tokens} of {layer.n_tokens} tokens "
+                   f"({t_hess:.2f} s, scaled x{layer.n_tokens // sample_tokens}), full prep at d=4096 "
+                   f"({t_prep:.2f} s), blocked sweep on {sample_rows} of {layer.d_row} rows "
+                   f"({t_sweep:.2f} s, scaled x{layer.d_row // sample_rows}); "
+                   f"extrapolated {total:.1f} s per layer; input generation {t_gen:.1f} s not counted"),
+        "seconds_per_layer": total,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: the GPTQ layer quantizer runs on one GPU; only --gpus 1 is supported "
+              "(rows shard with no communication and H needs one all-reduce, which this build "
+              "does not implement)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_25_amd as g
+    import synth
+
+    layer = synth.config_layers(2)[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n, d, r = layer.n_tokens, layer.d_col, layer.d_row
+
+    # synthetic inputs, generated chunk by chunk on the host and kept resident in HBM
+    X = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+    for c, arr in enumerate(synth.x_chunks(layer)):
+        lo = c * synth.CHUNK
+        X[lo:lo + arr.shape[0]].copy_(torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16))
+    W = torch.from_numpy(synth.weights(layer).view(np.int16)).view(torch.bfloat16).to(dev)
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    ws_h = torch.empty(g.hessian_workspace_size(n, d), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(g.prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
+    U = torch.empty((d, d), dtype=torch.float32, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    p = g.make_params(4, 128)
+    ws_q = torch.empty(g.quantize_workspace_size(r, d, p), dtype=torch.uint8, device=dev)
+    q = g.Quantized(torch.empty((r, d // 2), dtype=torch.uint8, device=dev),
+                    torch.empty((r, d // 128), dtype=torch.float16, device=dev),
+                    torch.empty((r, d // 128), dtype=torch.float16, device=dev),
+                    torch.zeros(1, dtype=torch.int32, device=dev), 4, 128, d)
+    What = torch.empty((r, d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    phases = ["hess", "prep", "quant", "deq"]
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        H.zero_()
+        g.hessian_accumulate(H, X, ws=ws_h)
+        if ev: ev[1].record()
+        g.prepare_hinv(H, 0.01, U=U, ws=ws_p, info=info)
+        if ev: ev[2].record()
+        g.quantize_layer(W, U, 4, 128, ws=ws_q, out=q)
+        if ev: ev[3].record()
+        g.dequantize(q, out=What)
+        if ev: ev[4].record()
+
+    # the dominant kernel alone (Hessian SYRK), timed with events on the launch stream
+    def hess_only(ev):
+        ev[0].record()
+        g.hessian_accumulate(H, X, ws=ws_h)
+        ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    g.check_info(info, "prepare_hinv")
+    g.check_info(q.info, "quantize_layer")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1000.0 / args.steps
+    ph = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+          for i, nm in enumerate(phases)}
+
+    hev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        hess_only(hev[k])
+    torch.cuda.synchronize()
+    hess_launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in hev]))
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    flops_hess = float(n) * d * (d + 1)            # symmetric rank-n update, upper triangle incl. diagonal
+    achieved = flops_hess / (hess_launch_ms * 1e-3) / 1e12
+    ms_layer = ph["hess"] + ph["prep"] + ph["quant"]
+    rec = {
+        "metric": METRIC,
+        "value": r * d / (ms_step * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention projection 4096x4096: W bf16 ~N(0,0.02^2), X 262144x4096 bf16 "
+                               "(log-normal channel scales, 4 channels x50), int4 asym g128, B=128, damp 0.01",
+                   "d_row": r, "d_col": d, "n_tokens": n, "bits": 4, "group_size": 128, "block_size": 128,
+                   "arithmetic": "H: bf16 MFMA, fp32 accumulate; prep: fp64 MFMA; sweep: fp32; trailing: fp32 MFMA"},
+        "ms_per_layer": ms_layer,
+        "ms_per_layer_quantize_only": ph["prep"] + ph["quant"],
+        "phases_ms": ph,
+        "roofline": {"kernel": "hess_bf16_kernel", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(flops_hess),
+                     "launch_ms": hess_launch_ms,
+                     "algorithmic_flops_per_launch": flops_hess},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(layer, sample_tokens=4 * 8192, sample_rows=256)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

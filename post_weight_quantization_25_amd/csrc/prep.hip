@@ -9,14 +9,15 @@
 // and (H + lambda I)^-1 = (J L^-1 J)^T (J L^-1 J), so U = J L^-1 J: one
 // factorization and one triangular inverse, (2/3) d^3 flops in all.
 //
-// Both are done together by a recursive 2 x 2 block algorithm in fp64:
-//   [L11, X11] = cholinv(A11)
-//   L21 = A21 X11^T;  A22 -= L21 L21^T
-//   [L22, X22] = cholinv(A22)
-//   X21 = -X22 (L21 X11)
-// with X = L^-1.  The leaves (<= 64 columns) run in one workgroup in LDS; the
-// block products run on v_mfma_f64_16x16x4_f64, skipping tiles that are zero
+// Both in fp64: a right-looking blocked Cholesky with 64-column panels (the
+// diagonal block is factored and inverted in one workgroup, the panel below it is
+// multiplied by that inverse, the trailing matrix gets a rank-64 update), then
+// X = L^-1 from the inverted diagonal blocks by recursive doubling over block
+// pairs, X[q][p] = -X[q][q] (L[q][p] X[p][p]), each level one batched product.
+// The block products run on v_mfma_f64_16x16x4_f64 and skip tiles that are zero
 // because an operand is triangular.
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -74,73 +75,173 @@ __global__ void prep_output_kernel(const double* X, int64_t d, float* U) {
 }
 
 // --------------------------------------------------------------------------
-// Leaf: factor the n x n (n <= 64) block A[off.., off..] (lower part read) and
-// write its inverse factor X[off.., off..] (full block, zeros above the diagonal).
-// On a non-positive (or NaN) pivot j the leaf records j + 1 in *info if no earlier
-// failure was recorded; prep_fix_info_kernel then adds the block offset.
-__global__ __launch_bounds__(256) void prep_leaf_kernel(const double* A, double* X, int64_t d, int64_t off, int n,
+// Diagonal block k (n <= 64 columns at offset k0, fully updated by the earlier
+// panels): Cholesky A_kk = L_kk L_kk^T and X_kk = L_kk^-1 in one workgroup, in LDS.
+// Factorization by 8-column sub-panels: wave 0 factors the sub-panel with lane i
+// holding row i in registers and pivots / column entries broadcast with
+// v_readlane (no barriers inside the sub-panel); then all four waves apply the
+// rank-8 update to the rest of the block.  The inverse is built by recursive
+// doubling: 8 x 8 diagonal blocks by forward substitution, then levels of
+// X[q][p] = -X[q][q] (L[q][p] X[p][p]).  Writes X_kk (zeros above the diagonal).
+// On a non-positive (or NaN) pivot j the first failure is recorded as
+// info = k0 + j + 1 (the order of the trailing principal submatrix of H + lambda I
+// that is not positive definite).
+GPTQ_DEV double readlane_f64(double v, int lane) {
+    const int2 p = __builtin_bit_cast(int2, v);
+    int2 r;
+    r.x = __builtin_amdgcn_readlane(p.x, lane);
+    r.y = __builtin_amdgcn_readlane(p.y, lane);
+    return __builtin_bit_cast(double, r);
+}
+
+__global__ __launch_bounds__(256) void prep_diag_kernel(const double* A, double* X, int64_t d, int64_t k0, int n,
                                                       int32_t* info) {
-    __shared__ double a[PNB][PNB + 1];
-    __shared__ double x[PNB][PNB + 1];
-    __shared__ int fail;
-    const int tid = threadIdx.x;
+    constexpr int LD = PNB + 1;
+    __shared__ double a[PNB * LD];
+    __shared__ double xs[PNB * LD];
+    __shared__ double ts[PNB * 16];
+    __shared__ int fail_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int idx = tid; idx < PNB * PNB; idx += 256) {
-        const int i = idx / PNB, j = idx % PNB;
-        a[i][j] = (i < n && j <= i) ? A[(off + i) * d + off + j] : 0.0;
-        x[i][j] = 0.0;
+        const int i = idx >> 6, k = idx & 63;
+        double v = 0.0;
+        if (i < n && k <= i) v = A[(k0 + i) * d + k0 + k];
+        else if (i == k) v = 1.0;                      // identity padding of a short block
+        a[i * LD + k] = v;
+        xs[i * LD + k] = 0.0;
     }
-    if (tid == 0) fail = 0;
+    if (tid == 0) fail_s = 0;
     __syncthreads();
-    const int i = tid & 63;      // row owned in the column scaling / X row
-    const int part = tid >> 6;   // 0..3: column stripe in the trailing update
-    for (int j = 0; j < n; ++j) {
-        const double piv = a[j][j];
-        if (!(piv > 0.0)) {      // uniform across the WG
-            if (tid == 0) fail = j + 1;
-            break;
+
+    for (int c0 = 0; c0 < PNB; c0 += 8) {
+        if (wave == 0) {
+            double p[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) p[jj] = (lane >= c0 + jj) ? a[lane * LD + c0 + jj] : 0.0;
+            int f = 0;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int j = c0 + jj;
+                const double piv = readlane_f64(p[jj], j);
+                if (!(piv > 0.0)) { f = j + 1; break; }
+                const double l = sqrt(piv);
+                const double inv = 1.0 / l;
+                p[jj] = (lane == j) ? l : ((lane > j) ? p[jj] * inv : 0.0);
+#pragma unroll
+                for (int kk = jj + 1; kk < 8; ++kk) {
+                    const double lk = readlane_f64(p[jj], c0 + kk);
+                    if (lane >= c0 + kk) p[kk] -= p[jj] * lk;
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                if (lane >= c0 + jj) a[lane * LD + c0 + jj] = p[jj];
+            if (lane == 0 && f) fail_s = f;
         }
-        const double l = sqrt(piv);
         __syncthreads();
-        if (part == 0) {
-            if (i == j) a[j][j] = l;
-            else if (i > j && i < n) a[i][j] = a[i][j] / l;
-        }
-        __syncthreads();
-        // trailing update a[r][k] -= a[r][j] a[k][j] for j < k <= r, and X row j
+        if (fail_s) break;
+        // rank-8 update of the lower part of rows / columns >= c0 + 8
         for (int idx = tid; idx < PNB * PNB; idx += 256) {
             const int r = idx >> 6, k = idx & 63;
-            if (k > j && k <= r && r < n) a[r][k] -= a[r][j] * a[k][j];
-        }
-        // X[j][c] for c < j: -(sum_{k=c}^{j-1} L[j][k] X[k][c]) / L[j][j]; X[j][j] = 1/L[j][j]
-        if (part == 1 && i <= j) {
-            double v;
-            if (i == j) {
-                v = 1.0 / l;
-            } else {
-                double s = 0.0;
-                for (int k = i; k < j; ++k) s += a[j][k] * x[k][i];
-                v = -s / l;
+            if (k >= c0 + 8 && k <= r) {
+                double acc = 0.0;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) acc += a[r * LD + c0 + jj] * a[k * LD + c0 + jj];
+                a[r * LD + k] -= acc;
             }
-            x[j][i] = v;
         }
         __syncthreads();
     }
-    __syncthreads();
-    if (fail) {
-        if (tid == 0 && *info == 0) *info = fail;  // local index; host converts
+    if (fail_s) {
+        if (tid == 0 && fail_s <= n && *info == 0) *info = (int32_t)(k0 + fail_s);
         return;
+    }
+    // inverse of the eight 8 x 8 diagonal blocks: one thread per (block, column)
+    if (tid < 64) {
+        const int bl = tid >> 3, c = tid & 7, o = bl * 8;
+        double x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            double sacc = (i == c) ? 1.0 : 0.0;
+#pragma unroll
+            for (int k = 0; k < i; ++k) sacc -= a[(o + i) * LD + o + k] * x[k];
+            x[i] = (i >= c) ? sacc / a[(o + i) * LD + o + i] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs[(o + i) * LD + o + c] = x[i];
+    }
+    __syncthreads();
+    // recursive doubling: block pairs p = [2 m b, 2 m b + b), q = [2 m b + b, 2 m b + 2 b)
+    for (int b = 8; b < PNB; b *= 2) {
+        const int np = PNB / (2 * b);
+        // T_m = L[q][p] X[p][p]
+        for (int idx = tid; idx < np * b * b; idx += 256) {
+            const int m = idx / (b * b), rr = (idx / b) % b, cc = idx % b;
+            const int p0 = 2 * m * b, q0 = p0 + b;
+            double acc = 0.0;
+            for (int k = cc; k < b; ++k) acc += a[(q0 + rr) * LD + p0 + k] * xs[(p0 + k) * LD + p0 + cc];
+            ts[idx] = acc;
+        }
+        __syncthreads();
+        // X[q][p] = -X[q][q] T_m
+        for (int idx = tid; idx < np * b * b; idx += 256) {
+            const int m = idx / (b * b), rr = (idx / b) % b, cc = idx % b;
+            const int p0 = 2 * m * b, q0 = p0 + b;
+            double acc = 0.0;
+            for (int k = 0; k <= rr; ++k) acc += xs[(q0 + rr) * LD + q0 + k] * ts[m * b * b + k * b + cc];
+            xs[(q0 + rr) * LD + p0 + cc] = -acc;
+        }
+        __syncthreads();
     }
     for (int idx = tid; idx < n * n; idx += 256) {
         const int r = idx / n, c = idx % n;
-        X[(off + r) * d + off + c] = x[r][c];
+        X[(k0 + r) * d + k0 + c] = xs[r * LD + c];
     }
 }
 
-// Non-positive-pivot index conversion: the leaf writes its local j+1; the host
-// launches this right after to make it the global order of the failing trailing
-// submatrix of H + lambda I (= global pivot index + 1 in the reversed matrix).
-__global__ void prep_fix_info_kernel(int32_t* info, int32_t* seen, int64_t off) {
-    if (*info > 0 && *seen == 0) { *info = (int32_t)(off + *info); *seen = 1; }
+// Panel: L[k0+64:, k0:k0+64] = A[k0+64:, k0:k0+64] X_kk^T, in place (each workgroup
+// reads its 64 rows completely before writing them).  fp64 MFMA 16x16x4.
+__global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double* X, int64_t d, int64_t k0, int n) {
+    __shared__ double As[64][PNB + 1];
+    __shared__ double Xs[64][PNB + 1];
+    const int64_t r0 = k0 + PNB + (int64_t)blockIdx.x * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    for (int idx = tid; idx < 64 * PNB; idx += 256) {
+        const int i = idx / PNB, k = idx % PNB;
+        As[i][k] = (r0 + i < d && k < n) ? A[(r0 + i) * d + k0 + k] : 0.0;
+        Xs[i][k] = (i < n && k < n) ? X[(k0 + i) * d + k0 + k] : 0.0;
+    }
+    __syncthreads();
+    f64x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{};
+    // out[i][c] = sum_k As[i][k] Xs[c][k]   (X_kk^T)
+#pragma unroll 4
+    for (int kk = 0; kk < PNB; kk += 4) {
+        double fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[i] = As[wr * 32 + i * 16 + (lane & 15)][kk + (lane >> 4)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = Xs[wc * 32 + j * 16 + (lane & 15)][kk + (lane >> 4)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t gr = r0 + wr * 32 + i * 16 + 4 * e + (lane >> 4);
+                const int c = wc * 32 + j * 16 + (lane & 15);
+                if (gr < d && c < n) A[gr * d + k0 + c] = acc[i][j][e];
+            }
 }
 
 // --------------------------------------------------------------------------
@@ -155,11 +256,25 @@ struct GemmD {
     int M, N, K;
     double alpha, beta;
     int flags;
+    // batching over blockIdx.z: operand offsets advance by these element strides;
+    // the last batch entry may have fewer rows (M_last) and, for G_TRI_A, fewer k (= M_last)
+    int64_t sA, sB, sC; int M_last; int nbatch;
 };
 
 __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     __shared__ double As[GD_BM * GD_LD];
     __shared__ double Bs[GD_BM * GD_LD];
+    const int bz = blockIdx.z;
+    if (bz > 0) {
+        g.A += bz * g.sA; g.B += bz * g.sB; g.C += bz * g.sC;
+        if (bz == g.nbatch - 1) {
+            if (g.flags & G_TRI_A) g.K = g.M_last;
+            g.M = g.M_last;
+        }
+    } else if (g.nbatch == 1 && g.M_last > 0) {
+        if (g.flags & G_TRI_A) g.K = g.M_last;
+        g.M = g.M_last;
+    }
     const int mi = blockIdx.y, nj = blockIdx.x;
     const int m0 = mi * GD_BM, n0 = nj * GD_BM;
     if ((g.flags & G_LOWER_C) && n0 > m0 + GD_BM - 1) return;
@@ -228,70 +343,71 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
             }
 }
 
-__global__ void copy_f64_kernel(double* dst, int64_t ldd, const double* src, int64_t lds, int M, int N) {
-    const int64_t i = blockIdx.y;
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < N; j += gridDim.x * blockDim.x)
-        if (i < M) dst[i * ldd + j] = src[i * lds + j];
-}
-
 // --------------------------------------------------------------------------
 // Host side
 struct PrepCtx {
     double* A; double* X; double* T; int64_t d;
-    int32_t* info; int32_t* seen; hipStream_t s;
+    int32_t* info; hipStream_t s;
 };
 
 static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int64_t lda, const double* B,
-                        int64_t ldb, int M, int N, int K, double alpha, double beta, int flags) {
-    if (M <= 0 || N <= 0) return GPTQ_OK;
-    GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags};
-    dim3 grid((N + GD_BM - 1) / GD_BM, (M + GD_BM - 1) / GD_BM);
+                        int64_t ldb, int M, int N, int K, double alpha, double beta, int flags,
+                        int nbatch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, int M_last = 0) {
+    if (M <= 0 || N <= 0 || nbatch <= 0) return GPTQ_OK;
+    GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch};
+    dim3 grid((N + GD_BM - 1) / GD_BM, (M + GD_BM - 1) / GD_BM, nbatch);
     gemm_f64_kernel<<<grid, 256, 0, c.s>>>(g);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
 
-static gptq_status cholinv(PrepCtx& c, int64_t off, int64_t n) {
+// Right-looking blocked Cholesky of A (lower, reversed damped H) with the inverse of
+// every 64 x 64 diagonal block of L, then X = L^-1 by recursive doubling over
+// independent block pairs: X[q][p] = -X[q][q] (L[q][p] X[p][p]).
+static gptq_status cholinv(PrepCtx& c) {
     const int64_t d = c.d;
-    if (n <= PNB) {
-        prep_leaf_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, off, (int)n, c.info);
-        GPTQ_LAUNCH_CHECK();
-        prep_fix_info_kernel<<<1, 1, 0, c.s>>>(c.info, c.seen, off);
-        GPTQ_LAUNCH_CHECK();
-        return GPTQ_OK;
-    }
-    int64_t h = ((n / 2 + PNB - 1) / PNB) * PNB;
-    if (h >= n) h = n - PNB;
-    const int64_t n2 = n - h;
     gptq_status st;
-    if ((st = cholinv(c, off, h)) != GPTQ_OK) return st;
-    double* A21 = c.A + (off + h) * d + off;
-    double* A22 = c.A + (off + h) * d + off + h;
-    double* X11 = c.X + off * d + off;
-    double* X21 = c.X + (off + h) * d + off;
-    double* X22 = c.X + (off + h) * d + off + h;
-    // L21 = A21 X11^T  -> T (n2 x h)
-    if ((st = gemm(c, c.T, h, A21, d, X11, d, (int)n2, (int)h, (int)h, 1.0, 0.0, G_BT | G_TRI_B)) != GPTQ_OK) return st;
-    // A22 -= L21 L21^T (lower tiles)
-    if ((st = gemm(c, A22, d, c.T, h, c.T, h, (int)n2, (int)n2, (int)h, -1.0, 1.0, G_BT | G_LOWER_C)) != GPTQ_OK) return st;
-    // X21 <- L21 X11 (temporary, X21's own storage is untouched by the next call)
-    if ((st = gemm(c, X21, d, c.T, h, X11, d, (int)n2, (int)h, (int)h, 1.0, 0.0, G_TRI_B)) != GPTQ_OK) return st;
-    if ((st = cholinv(c, off + h, n2)) != GPTQ_OK) return st;
-    // X21 = -X22 (L21 X11)  via T
-    if ((st = gemm(c, c.T, h, X22, d, X21, d, (int)n2, (int)h, (int)n2, -1.0, 0.0, G_TRI_A)) != GPTQ_OK) return st;
-    dim3 grid(((int)h + 255) / 256 < 64 ? ((int)h + 255) / 256 : 64, (unsigned)n2);
-    copy_f64_kernel<<<grid, 256, 0, c.s>>>(X21, d, c.T, h, (int)n2, (int)h);
-    GPTQ_LAUNCH_CHECK();
+    for (int64_t k0 = 0; k0 < d; k0 += PNB) {
+        const int n = (int)std::min<int64_t>(PNB, d - k0);
+        prep_diag_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, k0, n, c.info);
+        GPTQ_LAUNCH_CHECK();
+        const int64_t rest = d - k0 - n;
+        if (rest <= 0) break;
+        prep_panel_kernel<<<(unsigned)((rest + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, k0, n);
+        GPTQ_LAUNCH_CHECK();
+        double* L21 = c.A + (k0 + n) * d + k0;
+        double* A22 = c.A + (k0 + n) * d + k0 + n;
+        if ((st = gemm(c, A22, d, L21, d, L21, d, (int)rest, (int)rest, n, -1.0, 1.0, G_BT | G_LOWER_C)) != GPTQ_OK)
+            return st;
+    }
+    for (int64_t b = PNB; b < d; b *= 2) {
+        // pairs p = [2 m b, (2 m + 1) b), q = [(2 m + 1) b, min((2 m + 2) b, d))
+        const int64_t npairs = (d - b + 2 * b - 1) / (2 * b);
+        const int64_t q_last = (2 * (npairs - 1) + 1) * b;
+        const int qn_last = (int)std::min<int64_t>(b, d - q_last);
+        const int64_t step = 2 * b * (d + 1);
+        const int bb = (int)b;
+        // T_m = L[q][p] X[p][p]   (b x b each, X[p][p] lower triangular)
+        if ((st = gemm(c, c.T, bb, c.A + b * d, d, c.X, d, bb, bb, bb, 1.0, 0.0, G_TRI_B,
+                       (int)npairs, step, step, (int64_t)b * b, qn_last)) != GPTQ_OK) return st;
+        // X[q][p] = -X[q][q] T_m   (X[q][q] lower triangular)
+        if ((st = gemm(c, c.X + b * d, d, c.X + b * d + b, d, c.T, bb, bb, bb, bb, -1.0, 0.0, G_TRI_A,
+                       (int)npairs, step, (int64_t)b * b, step, qn_last)) != GPTQ_OK) return st;
+    }
     return GPTQ_OK;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+static size_t t_bytes(int64_t d) {
+    // recursive-doubling scratch: npairs * b * b <= d * b / 2 + b * b with b < d
+    return (size_t)d * d * sizeof(double);
+}
+
 size_t prep_ws_bytes(int64_t d) {
     if (d <= 0) return 0;
     const size_t dd = (size_t)d * d * sizeof(double);
-    const size_t t = (size_t)(d / 2 + PNB) * (d / 2 + PNB) * sizeof(double);
-    return align256(dd) * 2 + align256(t) + 256;
+    return align256(dd) * 2 + align256(t_bytes(d)) + 256;
 }
 
 gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, void* ws, size_t ws_bytes,
@@ -303,19 +419,16 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     c.A = reinterpret_cast<double*>(p);
     c.X = reinterpret_cast<double*>(p + dd);
     c.T = reinterpret_cast<double*>(p + 2 * dd);
-    const size_t t = align256((size_t)(d / 2 + PNB) * (d / 2 + PNB) * sizeof(double));
+    const size_t t = align256(t_bytes(d));
     double* lam = reinterpret_cast<double*>(p + 2 * dd + t);
-    c.seen = reinterpret_cast<int32_t*>(p + 2 * dd + t + 8);
     c.d = d; c.info = info; c.s = s;
 
     prep_lambda_kernel<<<1, 1024, 0, s>>>(H, d, percdamp, lam, info);
     GPTQ_LAUNCH_CHECK();
-    fill_i32(c.seen, 1, 0, s);
-    GPTQ_LAUNCH_CHECK();
     dim3 gb((unsigned)((d + 255) / 256 < 64 ? (d + 255) / 256 : 64), (unsigned)d);
     prep_build_kernel<<<gb, 256, 0, s>>>(H, d, lam, c.A, c.X);
     GPTQ_LAUNCH_CHECK();
-    gptq_status st = cholinv(c, 0, d);
+    gptq_status st = cholinv(c);
     if (st != GPTQ_OK) return st;
     prep_output_kernel<<<gb, 256, 0, s>>>(c.X, d, U);
     GPTQ_LAUNCH_CHECK();

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import dev_tensor, log, parity_report, recon_rows, unpack_codes
+from gpu_helpers import check_recon, dev_tensor, log, parity_report, unpack_codes
 from oracle import gptq_oracle as o
 
 pytestmark = pytest.mark.gpu
@@ -73,10 +73,8 @@ def test_quantize_parity(d_row, d_col, bits, group, sym, wdt):
     expect = s16.astype(np.float32)[:, gi] * (codes.astype(np.float32) - z.astype(np.float32)[:, gi])
     wh = What.cpu().numpy()
     assert np.array_equal(wh, expect)
-    # layer objective within 1e-3 relative
-    e_g, e_o = recon_rows(H, Wf, wh).sum(), recon_rows(H, Wf, ref.what).sum()
-    log(f"  recon error gpu {e_g:.6e} oracle {e_o:.6e} rel {abs(e_g - e_o) / e_o:.2e}")
-    assert abs(e_g - e_o) <= 1e-3 * e_o
+    # layer objective
+    check_recon(H, Wf, wh, ref.what, rep["event_rows"], log)
 
 
 @pytest.mark.parametrize("bits,group,out", [(4, 128, "f32"), (3, 0, "bf16"), (4, 64, "f16"), (8, 128, "f32")])
