@@ -76,30 +76,23 @@ __global__ void prep_output_kernel(const double* X, int64_t d, float* U) {
 
 // --------------------------------------------------------------------------
 // Diagonal block k (n <= 64 columns at offset k0, fully updated by the earlier
-// panels): Cholesky A_kk = L_kk L_kk^T and X_kk = L_kk^-1 in one workgroup, in LDS.
-// Factorization by 8-column sub-panels: wave 0 factors the sub-panel with lane i
-// holding row i in registers and pivots / column entries broadcast with
-// v_readlane (no barriers inside the sub-panel); then all four waves apply the
-// rank-8 update to the rest of the block.  The inverse is built by recursive
-// doubling: 8 x 8 diagonal blocks by forward substitution, then levels of
-// X[q][p] = -X[q][q] (L[q][p] X[p][p]).  Writes X_kk (zeros above the diagonal).
+// panels): Cholesky A_kk = L_kk L_kk^T in place (lower part), one workgroup.
+// The block is processed in 8-column sub-panels.  For a sub-panel, every lane of
+// wave 0 factors the sub-panel's 8 x 8 top block redundantly in registers (no
+// cross-lane traffic) and then solves its own row of the sub-panel against it;
+// afterwards the four waves apply the rank-8 update to the rest of the block on
+// v_mfma_f64_16x16x4_f64.  Then X_kk = L_kk^-1 is built in LDS (8 x 8 diagonal
+// blocks by substitution, then recursive doubling).  Writes L_kk (lower) and X_kk.
 // On a non-positive (or NaN) pivot j the first failure is recorded as
-// info = k0 + j + 1 (the order of the trailing principal submatrix of H + lambda I
-// that is not positive definite).
-GPTQ_DEV double readlane_f64(double v, int lane) {
-    const int2 p = __builtin_bit_cast(int2, v);
-    int2 r;
-    r.x = __builtin_amdgcn_readlane(p.x, lane);
-    r.y = __builtin_amdgcn_readlane(p.y, lane);
-    return __builtin_bit_cast(double, r);
-}
+// info = k0 + j + 1, the order of the trailing principal submatrix of H + lambda I
+// that is not positive definite.
+constexpr int DLD = PNB + 1;
 
-__global__ __launch_bounds__(256) void prep_diag_kernel(const double* A, double* X, int64_t d, int64_t k0, int n,
+__global__ __launch_bounds__(256) void prep_diag_kernel(double* A, double* X, int64_t d, int64_t k0, int n,
                                                       int32_t* info) {
-    constexpr int LD = PNB + 1;
-    __shared__ double a[PNB * LD];
-    __shared__ double xs[PNB * LD];
-    __shared__ double ts[PNB * 16];
+    __shared__ double a[PNB * DLD];
+    __shared__ double xs[PNB * DLD];
+    __shared__ double ts[PNB * 32];
     __shared__ int fail_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int idx = tid; idx < PNB * PNB; idx += 256) {
@@ -107,47 +100,88 @@ __global__ __launch_bounds__(256) void prep_diag_kernel(const double* A, double*
         double v = 0.0;
         if (i < n && k <= i) v = A[(k0 + i) * d + k0 + k];
         else if (i == k) v = 1.0;                      // identity padding of a short block
-        a[i * LD + k] = v;
-        xs[i * LD + k] = 0.0;
+        a[i * DLD + k] = v;
     }
     if (tid == 0) fail_s = 0;
     __syncthreads();
 
     for (int c0 = 0; c0 < PNB; c0 += 8) {
         if (wave == 0) {
-            double p[8];
+            // Cholesky of the 8 x 8 top block, in every lane
+            double t[8][8];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) p[jj] = (lane >= c0 + jj) ? a[lane * LD + c0 + jj] : 0.0;
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int k = 0; k <= i; ++k) t[i][k] = a[(c0 + i) * DLD + c0 + k];
+            double rd[8];
             int f = 0;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int j = c0 + jj;
-                const double piv = readlane_f64(p[jj], j);
-                if (!(piv > 0.0)) { f = j + 1; break; }
-                const double l = sqrt(piv);
-                const double inv = 1.0 / l;
-                p[jj] = (lane == j) ? l : ((lane > j) ? p[jj] * inv : 0.0);
+            for (int k = 0; k < 8; ++k) {
+                double dk = t[k][k];
 #pragma unroll
-                for (int kk = jj + 1; kk < 8; ++kk) {
-                    const double lk = readlane_f64(p[jj], c0 + kk);
-                    if (lane >= c0 + kk) p[kk] -= p[jj] * lk;
+                for (int m = 0; m < k; ++m) dk -= t[k][m] * t[k][m];
+                if (!(dk > 0.0) && f == 0) f = c0 + k + 1;
+                rd[k] = rsqrt(dk > 0.0 ? dk : 1.0);
+                t[k][k] = (dk > 0.0 ? dk : 1.0) * rd[k];
+#pragma unroll
+                for (int i = k + 1; i < 8; ++i) {
+                    double v = t[i][k];
+#pragma unroll
+                    for (int m = 0; m < k; ++m) v -= t[i][m] * t[k][m];
+                    t[i][k] = v * rd[k];
                 }
             }
+            // this lane's row of the sub-panel
+            const int r = lane;
+            if (r >= c0 + 8) {
+                double x[8];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                if (lane >= c0 + jj) a[lane * LD + c0 + jj] = p[jj];
+                for (int k = 0; k < 8; ++k) {
+                    double v = a[r * DLD + c0 + k];
+#pragma unroll
+                    for (int m = 0; m < k; ++m) v -= t[k][m] * x[m];
+                    x[k] = v * rd[k];
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) a[r * DLD + c0 + k] = x[k];
+            } else if (r >= c0) {
+                const int i = r - c0;
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii)
+                    if (ii == i) {
+#pragma unroll
+                        for (int k = 0; k <= ii; ++k) a[r * DLD + c0 + k] = t[ii][k];
+                    }
+            }
             if (lane == 0 && f) fail_s = f;
         }
         __syncthreads();
         if (fail_s) break;
-        // rank-8 update of the lower part of rows / columns >= c0 + 8
-        for (int idx = tid; idx < PNB * PNB; idx += 256) {
-            const int r = idx >> 6, k = idx & 63;
-            if (k >= c0 + 8 && k <= r) {
-                double acc = 0.0;
+        // rank-8 update of the lower part of rows / columns >= c1 = c0 + 8, in 16 x 16 tiles
+        const int c1 = c0 + 8;
+        if (c1 < PNB) {
+            const int t0 = c1 >> 4;
+            const int nt = 4 - t0;                         // tiles per dimension still active
+            const int ntiles = nt * (nt + 1) / 2;
+            for (int tt = wave; tt < ntiles; tt += 4) {
+                int tr = 0, rem = tt;
+                while (rem > tr) { rem -= tr + 1; ++tr; }
+                const int tc = rem;                        // tc <= tr within the active tiles
+                const int R0 = (t0 + tr) * 16, C0 = (t0 + tc) * 16;
+                f64x4_t acc;
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) acc += a[r * LD + c0 + jj] * a[k * LD + c0 + jj];
-                a[r * LD + k] -= acc;
+                for (int e = 0; e < 4; ++e) acc[e] = a[(R0 + 4 * e + (lane >> 4)) * DLD + C0 + (lane & 15)];
+#pragma unroll
+                for (int kk = 0; kk < 8; kk += 4) {
+                    const double fa = -a[(R0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
+                    const double fb = a[(C0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = R0 + 4 * e + (lane >> 4), cc = C0 + (lane & 15);
+                    if (rr >= c1 && cc >= c1) a[rr * DLD + cc] = acc[e];
+                }
             }
         }
         __syncthreads();
@@ -156,61 +190,100 @@ __global__ __launch_bounds__(256) void prep_diag_kernel(const double* A, double*
         if (tid == 0 && fail_s <= n && *info == 0) *info = (int32_t)(k0 + fail_s);
         return;
     }
-    // inverse of the eight 8 x 8 diagonal blocks: one thread per (block, column)
+    // X_kk = L_kk^-1: inverses of the eight 8 x 8 diagonal blocks by forward
+    // substitution (one thread per block column), then recursive doubling
+    // X[q][p] = -X[q][q] (L[q][p] X[p][p]) for block sizes 8, 16, 32
+    for (int idx = tid; idx < PNB * PNB; idx += 256) xs[(idx >> 6) * DLD + (idx & 63)] = 0.0;
+    __syncthreads();
     if (tid < 64) {
         const int bl = tid >> 3, c = tid & 7, o = bl * 8;
         double x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            double sacc = (i == c) ? 1.0 : 0.0;
+            double v = (i == c) ? 1.0 : 0.0;
 #pragma unroll
-            for (int k = 0; k < i; ++k) sacc -= a[(o + i) * LD + o + k] * x[k];
-            x[i] = (i >= c) ? sacc / a[(o + i) * LD + o + i] : 0.0;
+            for (int k = 0; k < i; ++k) v -= a[(o + i) * DLD + o + k] * x[k];
+            x[i] = v / a[(o + i) * DLD + o + i];
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xs[(o + i) * LD + o + c] = x[i];
+        for (int i = 0; i < 8; ++i) xs[(o + i) * DLD + o + c] = (i >= c) ? x[i] : 0.0;
     }
     __syncthreads();
-    // recursive doubling: block pairs p = [2 m b, 2 m b + b), q = [2 m b + b, 2 m b + 2 b)
     for (int b = 8; b < PNB; b *= 2) {
         const int np = PNB / (2 * b);
-        // T_m = L[q][p] X[p][p]
-        for (int idx = tid; idx < np * b * b; idx += 256) {
-            const int m = idx / (b * b), rr = (idx / b) % b, cc = idx % b;
-            const int p0 = 2 * m * b, q0 = p0 + b;
-            double acc = 0.0;
-            for (int k = cc; k < b; ++k) acc += a[(q0 + rr) * LD + p0 + k] * xs[(p0 + k) * LD + p0 + cc];
-            ts[idx] = acc;
+        if (b == 8) {
+            // 8 x 8 products: one output element per thread
+            for (int idx = tid; idx < np * 64; idx += 256) {
+                const int m = idx >> 6, rr = (idx >> 3) & 7, cc = idx & 7, p0 = 16 * m, q0 = p0 + 8;
+                double acc = 0.0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc += a[(q0 + rr) * DLD + p0 + k] * xs[(p0 + k) * DLD + p0 + cc];
+                ts[idx] = acc;
+            }
+            __syncthreads();
+            for (int idx = tid; idx < np * 64; idx += 256) {
+                const int m = idx >> 6, rr = (idx >> 3) & 7, cc = idx & 7, p0 = 16 * m, q0 = p0 + 8;
+                double acc = 0.0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc += xs[(q0 + rr) * DLD + q0 + k] * ts[m * 64 + k * 8 + cc];
+                xs[(q0 + rr) * DLD + p0 + cc] = -acc;
+            }
+            __syncthreads();
+        } else {
+            // b = 16, 32: 16 x 16 output tiles on MFMA, one tile per wave at a time
+            const int tpb = b / 16, ntile = np * tpb * tpb;
+            for (int t = wave; t < ntile; t += 4) {           // T_m = L[q][p] X[p][p]
+                const int m = t / (tpb * tpb), ti = (t / tpb) % tpb, tj = t % tpb;
+                const int p0 = 2 * m * b, q0 = p0 + b;
+                f64x4_t acc = f64x4_t{0.0, 0.0, 0.0, 0.0};
+                for (int k = 0; k < b; k += 4) {
+                    const double fa = a[(q0 + ti * 16 + (lane & 15)) * DLD + p0 + k + (lane >> 4)];
+                    const double fb = xs[(p0 + k + (lane >> 4)) * DLD + p0 + tj * 16 + (lane & 15)];
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ts[(m * b + ti * 16 + 4 * e + (lane >> 4)) * 32 + tj * 16 + (lane & 15)] = acc[e];
+            }
+            __syncthreads();
+            for (int t = wave; t < ntile; t += 4) {           // X[q][p] = -X[q][q] T_m
+                const int m = t / (tpb * tpb), ti = (t / tpb) % tpb, tj = t % tpb;
+                const int p0 = 2 * m * b, q0 = p0 + b;
+                f64x4_t acc = f64x4_t{0.0, 0.0, 0.0, 0.0};
+                for (int k = 0; k < b; k += 4) {
+                    const double fa = -xs[(q0 + ti * 16 + (lane & 15)) * DLD + q0 + k + (lane >> 4)];
+                    const double fb = ts[(m * b + k + (lane >> 4)) * 32 + tj * 16 + (lane & 15)];
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xs[(q0 + ti * 16 + 4 * e + (lane >> 4)) * DLD + p0 + tj * 16 + (lane & 15)] = acc[e];
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        // X[q][p] = -X[q][q] T_m
-        for (int idx = tid; idx < np * b * b; idx += 256) {
-            const int m = idx / (b * b), rr = (idx / b) % b, cc = idx % b;
-            const int p0 = 2 * m * b, q0 = p0 + b;
-            double acc = 0.0;
-            for (int k = 0; k <= rr; ++k) acc += xs[(q0 + rr) * LD + q0 + k] * ts[m * b * b + k * b + cc];
-            xs[(q0 + rr) * LD + p0 + cc] = -acc;
-        }
-        __syncthreads();
     }
     for (int idx = tid; idx < n * n; idx += 256) {
         const int r = idx / n, c = idx % n;
-        X[(k0 + r) * d + k0 + c] = xs[r * LD + c];
+        if (c <= r) A[(k0 + r) * d + k0 + c] = a[r * DLD + c];
+        X[(k0 + r) * d + k0 + c] = xs[r * DLD + c];
     }
 }
 
 // Panel: L[k0+64:, k0:k0+64] = A[k0+64:, k0:k0+64] X_kk^T, in place (each workgroup
 // reads its 64 rows completely before writing them).  fp64 MFMA 16x16x4.
-__global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double* X, int64_t d, int64_t k0, int n) {
-    __shared__ double As[64][PNB + 1];
-    __shared__ double Xs[64][PNB + 1];
+__global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double* X, int64_t d, int64_t k0) {
+    __shared__ double As[64 * DLD];
+    __shared__ double Xs[64 * DLD];
     const int64_t r0 = k0 + PNB + (int64_t)blockIdx.x * 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    for (int idx = tid; idx < 64 * PNB; idx += 256) {
-        const int i = idx / PNB, k = idx % PNB;
-        As[i][k] = (r0 + i < d && k < n) ? A[(r0 + i) * d + k0 + k] : 0.0;
-        Xs[i][k] = (i < n && k < n) ? X[(k0 + i) * d + k0 + k] : 0.0;
+    for (int idx = tid; idx < 64 * PNB / 2; idx += 256) {
+        const int i = idx / (PNB / 2), k = 2 * (idx % (PNB / 2));
+        double2 va = double2{0.0, 0.0};
+        if (r0 + i < d) va = *reinterpret_cast<const double2*>(A + (r0 + i) * d + k0 + k);
+        const double2 vx = *reinterpret_cast<const double2*>(X + (k0 + i) * d + k0 + k);
+        As[i * DLD + k] = va.x; As[i * DLD + k + 1] = va.y;
+        Xs[i * DLD + k] = vx.x; Xs[i * DLD + k + 1] = vx.y;
     }
     __syncthreads();
     f64x4_t acc[2][2];
@@ -218,14 +291,13 @@ __global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{};
-    // out[i][c] = sum_k As[i][k] Xs[c][k]   (X_kk^T)
 #pragma unroll 4
     for (int kk = 0; kk < PNB; kk += 4) {
         double fa[2], fb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = As[wr * 32 + i * 16 + (lane & 15)][kk + (lane >> 4)];
+        for (int i = 0; i < 2; ++i) fa[i] = As[(wr * 32 + i * 16 + (lane & 15)) * DLD + kk + (lane >> 4)];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = Xs[wc * 32 + j * 16 + (lane & 15)][kk + (lane >> 4)];
+        for (int j = 0; j < 2; ++j) fb[j] = Xs[(wc * 32 + j * 16 + (lane & 15)) * DLD + kk + (lane >> 4)];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -240,7 +312,7 @@ __global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double
             for (int e = 0; e < 4; ++e) {
                 const int64_t gr = r0 + wr * 32 + i * 16 + 4 * e + (lane >> 4);
                 const int c = wc * 32 + j * 16 + (lane & 15);
-                if (gr < d && c < n) A[gr * d + k0 + c] = acc[i][j][e];
+                if (gr < d) A[gr * d + k0 + c] = acc[i][j][e];
             }
 }
 
@@ -373,7 +445,7 @@ static gptq_status cholinv(PrepCtx& c) {
         GPTQ_LAUNCH_CHECK();
         const int64_t rest = d - k0 - n;
         if (rest <= 0) break;
-        prep_panel_kernel<<<(unsigned)((rest + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, k0, n);
+        prep_panel_kernel<<<(unsigned)((rest + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, k0);
         GPTQ_LAUNCH_CHECK();
         double* L21 = c.A + (k0 + n) * d + k0;
         double* A22 = c.A + (k0 + n) * d + k0 + n;

@@ -12,186 +12,17 @@
 // "Choose granularity" (per-group scales along a row), "Data types - int8 and
 // int4" (two codes per byte, first in the low nibble).
 //
-// Sweep kernel layout: a workgroup owns 64 rows of the block; each row is held
-// by 4 lanes of one quad, lane q holding columns q, q+4, ..., q+124 in registers
-// (column-cyclic, so the triangular work stays balanced).  The block's diagonal
-// 128 x 128 part of U is staged in LDS, permuted so that a lane reads its four
-// next coefficients with one 16-byte LDS read.  The quantization error of column
-// j is broadcast inside the quad with a DPP quad_perm.  Group min/max use DPP
-// quad reductions.  The trailing update W[:, b1:] -= E U[b0:b1, b1:] runs on
-// v_mfma_f32_16x16x4_f32 (fp32 operands).
+// The in-block column sweep is in sweep.hip.  This file holds the per-row
+// scale/zero of group_size 0, the working-copy conversion, the trailing lazy
+// update W[:, b1:] -= E U[b0:b1, b1:] on v_mfma_f32_16x16x4_f32 (fp32 operands),
+// the host-side block loop, and dequantization.
 
-#include <utility>
-
-#include "common.h"
 #include "kernels.h"
+#include "quant_internal.h"
 
 namespace gptq {
 
-constexpr int QB = 128;
-constexpr int QROWS = 64;
-constexpr int QT = 256;
-
-template <int I, int N, typename F>
-GPTQ_DEV void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
 GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 65504.f; }
-
-struct SweepArgs {
-    const float* Wws; int64_t d_row, d_col;
-    const float* U;
-    int64_t b0; int nb;
-    float* E;                       // d_row x 128
-    uint8_t* codes; int64_t code_ld;
-    uint16_t* scales; uint16_t* zeros; int n_groups;
-    int32_t* info;
-    int group;                      // 32, 64, 128 (power of two), or 0 = per-row params precomputed
-    int qmin, qmax, zoff;           // grid and stored-code offset
-    int sym; int packed;            // packed: two codes per byte
-};
-
-__global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
-    __shared__ __attribute__((aligned(16))) float Up[QB][4][32];  // Up[j][q][i] = U[b0+j][b0+4i+q]
-    __shared__ uint8_t cl[QROWS][QB];
-    __shared__ int bad_any;
-
-    const int tid = threadIdx.x;
-    const int q = tid & 3;
-    const int rl = tid >> 2;
-    const int64_t row = (int64_t)blockIdx.x * QROWS + rl;
-    const bool rv = row < a.d_row;
-    const int nb = a.nb;
-    const int G = a.group;
-    const float fqmin = (float)a.qmin, fqmax = (float)a.qmax, fzoff = (float)a.zoff;
-    if (tid == 0) bad_any = 0;
-
-    for (int idx = tid; idx < QB * QB; idx += QT) {
-        const int j = idx >> 7, c = idx & 127;
-        Up[j][c & 3][c >> 2] = (j < nb && c < nb) ? a.U[(a.b0 + j) * a.d_col + a.b0 + c] : 0.f;
-    }
-    float w[32], e[32], uc[32];
-    const float* wrow = a.Wws + (rv ? row : 0) * a.d_col + a.b0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int c = 4 * i + q;
-        w[i] = (rv && c < nb) ? wrow[c] : 0.f;
-        e[i] = 0.f;
-    }
-    float s16f = 1.f, zf = 0.f;
-    bool bad = false;
-    if (G == 0 && rv) {
-        s16f = f16_bits_to_f32(a.scales[row * a.n_groups]);
-        zf = f16_bits_to_f32(a.zeros[row * a.n_groups]) - fzoff;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const f32x4_t u4 = *reinterpret_cast<const f32x4_t*>(&Up[0][q][4 * m]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) uc[4 * m + k] = u4[k];
-    }
-
-    static_for<0, QB>([&](auto JC) {
-        constexpr int j = decltype(JC)::value;
-        constexpr int qj = j & 3, ij = j >> 2;
-        constexpr int ijn = (j + 1) >> 2;
-        if (j >= nb) return;
-        // prefetch the coefficients of step j + 1 (slots >= its own slot)
-        float un[32];
-        if constexpr (j + 1 < QB) {
-#pragma unroll
-            for (int m = ijn >> 2; m < 8; ++m) {
-                const f32x4_t u4 = *reinterpret_cast<const f32x4_t*>(&Up[j + 1][q][4 * m]);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) un[4 * m + k] = u4[k];
-            }
-        }
-        if (G > 0 && (j & (G - 1)) == 0) {
-            // group scale/zero from the current values of columns j .. j+G-1
-            const int iend = (j + G) >> 2;
-            float s, mn = 0.f;
-            if (a.sym) {
-                float am = 0.f;
-#pragma unroll
-                for (int i = j / 4; i < 32; ++i) if (i < iend) am = fmaxf(am, fabsf(w[i]));
-                am = fmaxf(am, quad_perm<QP_XOR1>(am));
-                am = fmaxf(am, quad_perm<QP_XOR2>(am));
-                s = am > 0.f ? am / fqmax : 1.f;
-            } else {
-                float mx = w[j / 4];
-                mn = w[j / 4];
-#pragma unroll
-                for (int i = j / 4 + 1; i < 32; ++i)
-                    if (i < iend) { mn = fminf(mn, w[i]); mx = fmaxf(mx, w[i]); }
-                mn = fminf(mn, quad_perm<QP_XOR1>(mn));
-                mn = fminf(mn, quad_perm<QP_XOR2>(mn));
-                mx = fmaxf(mx, quad_perm<QP_XOR1>(mx));
-                mx = fmaxf(mx, quad_perm<QP_XOR2>(mx));
-                if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
-                s = (mx > mn) ? (mx - mn) / (fqmax - fqmin) : 1.f;
-            }
-            s16f = f16_bits_to_f32(f32_to_f16_bits(s));
-            if (!normal_f16_scale(s16f)) { bad = true; s16f = 1.f; }
-            zf = a.sym ? 0.f : fqmin - rintf(mn / s16f);
-            if (q == 0 && rv) {
-                const int64_t g = (a.b0 + j) / G;
-                a.scales[row * a.n_groups + g] = f32_to_f16_bits(s16f);
-                a.zeros[row * a.n_groups + g] = f32_to_f16_bits(zf + fzoff);
-            }
-        }
-        // quantize column j (its owner is lane qj of the quad, slot ij)
-        const float wv = w[ij];
-        const float t = wv / s16f;
-        const float qv = fminf(fmaxf(rintf(t + zf), fqmin), fqmax);
-        const float wq = s16f * (qv - zf);
-        const float err = (wv - wq) / uc[ij];
-        const float errb = quad_bcast<qj>(err);
-        if (q == qj) {
-            e[ij] = err;
-            cl[rl][j] = (uint8_t)((int)qv + a.zoff);
-            if (!(fabsf(err) <= 3.0e38f)) bad = true;
-        }
-        // compensate the later columns of the block; U is upper triangular, so the
-        // coefficients of earlier columns in slot ij are zero or hit finished columns
-#pragma unroll
-        for (int i = ij; i < 32; ++i) w[i] = fmaf(-errb, uc[i], w[i]);
-        if constexpr (j + 1 < QB) {
-#pragma unroll
-            for (int i = ijn; i < 32; ++i) uc[i] = un[i];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    });
-
-    if (rv) {
-        float* erow = a.E + row * QB;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int c = 4 * i + q;
-            if (c < nb) erow[c] = e[i];
-        }
-    }
-    if (bad && rv) atomicOr(&bad_any, 1);
-    __syncthreads();
-    if (tid == 0 && bad_any) *a.info = -1;
-
-    // pack the block's codes: two per byte (column 2k in the low nibble) or one per byte
-    const int per = a.packed ? 2 : 1;
-    const int nbytes = nb / per;
-    const int rowbytes = QB / per;
-    for (int idx = tid; idx < QROWS * rowbytes; idx += QT) {
-        const int r = idx / rowbytes, bidx = idx % rowbytes;
-        const int64_t grow = (int64_t)blockIdx.x * QROWS + r;
-        if (grow >= a.d_row || bidx >= nbytes) continue;
-        const uint8_t v = a.packed ? (uint8_t)((cl[r][2 * bidx] & 0xF) | ((cl[r][2 * bidx + 1] & 0xF) << 4))
-                                   : cl[r][bidx];
-        a.codes[grow * a.code_ld + a.b0 / per + bidx] = v;
-    }
-}
 
 // --------------------------------------------------------------------------
 // One scale/zero per row (group_size 0): from the original row, before any update.
@@ -248,50 +79,156 @@ __global__ void convert_kernel(const void* W, int64_t n, float* out, int32_t* in
 }
 
 // --------------------------------------------------------------------------
-// Trailing lazy update on fp32 MFMA: W[:, b1:] -= E[:, :nb] U[b0:b0+nb, b1:].
-constexpr int TB = 64, TK = 32, TLD = TB + 4;
+// Trailing lazy update: W[:, n_beg:n_end] -= E[:, :K] U[k0:k0+K, n_beg:n_end] on
+// bf16 MFMA (v_mfma_f32_32x32x16_bf16) with a three-term split of the fp32
+// operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi), and
+// E U ~= Ehi Uhi + Ehi Ulo + Elo Uhi (the dropped Elo Ulo and the residuals are
+// ~2^-16 relative per product), accumulated in fp32.
+// 128 x 128 output tiles, four waves of 64 x 64 (2 x 2 MFMA 32 x 32 tiles); K in
+// chunks of 32 staged in LDS as bf16: E row-major ([m][k], 8 consecutive k per
+// 16-byte read), U as it lies in memory ([k][n]) and read transposed with
+// ds_read_b64_tr_b16.  The next chunk is loaded into registers while the current
+// one is multiplied.
+constexpr int TB = 128, TK = 32;
+constexpr int TE_LD = TK + 8;       // E rows in LDS: 40 bf16 = 80 B (conflict-free 16 B reads)
+constexpr int TU_RS = TB + 16;      // U rows in LDS: 144 bf16 = 72 dwords (conflict-free transposed reads)
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 struct TrailArgs {
     float* Wws; int64_t d_row, d_col;
-    const float* E; const float* U;
-    int64_t b0, b1; int nb;
+    const float* E; int64_t lde;     // E block: d_row x K, row stride lde
+    const float* U; int64_t k0; int K;
+    int64_t n_beg, n_end;
 };
 
+struct TrailStage {
+    uint16_t ehi[TB * TE_LD], elo[TB * TE_LD];
+    uint16_t uhi[TK * TU_RS], ulo[TK * TU_RS];
+};
+
+GPTQ_DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16_bits(x);
+    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// Per thread and chunk: 4 x float4 of E (row m = tid / 2, k = 16 (tid & 1) .. +15) and
+// 4 x float4 of U (row k = tid / 8, n = 16 (tid & 7) .. +15).
+GPTQ_DEV void trail_load(const TrailArgs& a, int64_t m0, int64_t n0, int kc, int tid, f32x4_t (&re)[4],
+                         f32x4_t (&ru)[4]) {
+    const int me = tid >> 1, ke = (tid & 1) * 16;
+    const int64_t gm = m0 + me;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int k = kc + ke + 4 * v;
+        f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (gm < a.d_row) {
+            const float* src = a.E + gm * a.lde + k;
+            if (k + 4 <= a.K) x = *reinterpret_cast<const f32x4_t*>(src);
+            else for (int e = 0; e < 4; ++e) x[e] = (k + e < a.K) ? src[e] : 0.f;
+        }
+        re[v] = x;
+    }
+    const int ku = tid >> 3, nu = (tid & 7) * 16;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t gn = n0 + nu + 4 * v;
+        f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (kc + ku < a.K) {
+            const float* src = a.U + (a.k0 + kc + ku) * a.d_col + gn;
+            if (gn + 4 <= a.n_end && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) x = *reinterpret_cast<const f32x4_t*>(src);
+            else for (int e = 0; e < 4; ++e) x[e] = (gn + e < a.n_end) ? src[e] : 0.f;
+        }
+        ru[v] = x;
+    }
+}
+
+// Split 8 fp32 values into hi and lo bf16 and write both 16-byte groups.
+GPTQ_DEV void store_split8(uint16_t* hi_dst, uint16_t* lo_dst, const f32x4_t& x0, const f32x4_t& x1) {
+    u32x4_t H, L;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const f32x4_t& x = (e < 2) ? x0 : x1;
+        uint16_t h0, l0, h1, l1;
+        split_bf16(x[(2 * e) & 3], h0, l0);
+        split_bf16(x[(2 * e + 1) & 3], h1, l1);
+        H[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        L[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(hi_dst) = H;
+    *reinterpret_cast<u32x4_t*>(lo_dst) = L;
+}
+
+GPTQ_DEV void trail_store(TrailStage& st, int tid, const f32x4_t (&re)[4], const f32x4_t (&ru)[4]) {
+    const int me = tid >> 1, ke = (tid & 1) * 16;
+    store_split8(&st.ehi[me * TE_LD + ke], &st.elo[me * TE_LD + ke], re[0], re[1]);
+    store_split8(&st.ehi[me * TE_LD + ke + 8], &st.elo[me * TE_LD + ke + 8], re[2], re[3]);
+    const int ku = tid >> 3, nu = (tid & 7) * 16;
+    store_split8(&st.uhi[ku * TU_RS + nu], &st.ulo[ku * TU_RS + nu], ru[0], ru[1]);
+    store_split8(&st.uhi[ku * TU_RS + nu + 8], &st.ulo[ku * TU_RS + nu + 8], ru[2], ru[3]);
+}
+
+// B operand (32 columns n x 16 k) from the [k][n] tile with two transposed reads:
+// in each 16-lane group lane j addresses k = k0 + (j >> 2), n = n0 + 4 (j & 3) and lane
+// i receives column n0 + i at k0 .. k0 + 3.
+GPTQ_DEV bf16x8_t trail_bfrag(const uint16_t* tile, int nc0, int kk, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int n = nc0 + (g & 1) * 16 + 4 * (j & 3);
+    const int k = kk + (g >> 1) * 8 + (j >> 2);
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + k * TU_RS + n));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + (k + 4) * TU_RS + n));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+GPTQ_DEV void trail_mfma(const TrailStage& st, int wr, int wc, int lane, f32x16_t (&acc)[2][2]) {
+#pragma unroll
+    for (int kk = 0; kk < TK; kk += 16) {
+        bf16x8_t ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int m = wr * 64 + i * 32 + (lane & 31), k = kk + (lane >> 5) * 8;
+            ah[i] = *reinterpret_cast<const bf16x8_t*>(&st.ehi[m * TE_LD + k]);
+            al[i] = *reinterpret_cast<const bf16x8_t*>(&st.elo[m * TE_LD + k]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            bh[j] = trail_bfrag(st.uhi, wc * 64 + j * 32, kk, lane);
+            bl[j] = trail_bfrag(st.ulo, wc * 64 + j * 32, kk, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+            }
+    }
+}
+
 __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
-    __shared__ float Es[TK][TLD];
-    __shared__ float Us[TK][TLD];
+    __shared__ __attribute__((aligned(16))) TrailStage stg[2];
     const int64_t m0 = (int64_t)blockIdx.y * TB;
-    const int64_t n0 = a.b1 + (int64_t)blockIdx.x * TB;
+    const int64_t n0 = a.n_beg + (int64_t)blockIdx.x * TB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    f32x4_t acc[2][2];
+    f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{};
-    for (int k0 = 0; k0 < a.nb; k0 += TK) {
-        for (int idx = tid; idx < TB * TK; idx += 256) {
-            const int m = idx / TK, k = idx % TK;  // E rows, k contiguous
-            const int64_t gm = m0 + m;
-            Es[k][m] = (gm < a.d_row && k0 + k < a.nb) ? a.E[gm * QB + k0 + k] : 0.f;
-            const int kk = idx / TB, n = idx % TB;  // U rows, n contiguous
-            const int64_t gn = n0 + n;
-            Us[kk][n] = (gn < a.d_col && k0 + kk < a.nb) ? a.U[(a.b0 + k0 + kk) * a.d_col + gn] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < TK; kk += 4) {
-            float fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = Es[kk + (lane >> 4)][wr * 32 + i * 16 + (lane & 15)];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = Us[kk + (lane >> 4)][wc * 32 + j * 16 + (lane & 15)];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    const int nch = (a.K + TK - 1) / TK;
+    f32x4_t re[4], ru[4];
+    trail_load(a, m0, n0, 0, tid, re, ru);
+    trail_store(stg[0], tid, re, ru);
+    if (nch > 1) trail_load(a, m0, n0, TK, tid, re, ru);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        trail_mfma(stg[c & 1], wr, wc, lane, acc);
+        if (c + 1 < nch) trail_store(stg[(c + 1) & 1], tid, re, ru);
+        if (c + 2 < nch) trail_load(a, m0, n0, (c + 2) * TK, tid, re, ru);
         __syncthreads();
     }
 #pragma unroll
@@ -299,20 +236,34 @@ __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t gm = m0 + wr * 32 + i * 16 + 4 * (lane >> 4) + e;
-                const int64_t gn = n0 + wc * 32 + j * 16 + (lane & 15);
-                if (gm < a.d_row && gn < a.d_col) a.Wws[gm * a.d_col + gn] -= acc[i][j][e];
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gm = m0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t gn = n0 + wc * 64 + j * 32 + (lane & 31);
+                if (gm < a.d_row && gn < a.n_end) a.Wws[gm * a.d_col + gn] -= acc[i][j][e];
             }
+}
+
+static gptq_status trail(const TrailArgs& ta, hipStream_t s) {
+    if (ta.n_end <= ta.n_beg || ta.K <= 0 || ta.d_row <= 0) return GPTQ_OK;
+    dim3 grid((unsigned)((ta.n_end - ta.n_beg + TB - 1) / TB), (unsigned)((ta.d_row + TB - 1) / TB));
+    trail_kernel<<<grid, 256, 0, s>>>(ta);
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
 }
 
 // --------------------------------------------------------------------------
 // Host side
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Super-block width of the deferred trailing update: inside a super-block every
+// 128-column block updates only the rest of the super-block; the columns after it
+// get one product with K = QSB per super-block.  The regrouping of the rank-1
+// updates is exact in exact arithmetic, as for the 128-column lazy blocks.
+constexpr int QSB = 512;
+
 size_t quant_ws_bytes(int64_t d_row, int64_t d_col) {
     if (d_row <= 0 || d_col <= 0) return 0;
-    return align256((size_t)d_row * d_col * sizeof(float)) + align256((size_t)d_row * QB * sizeof(float));
+    return align256((size_t)d_row * d_col * sizeof(float)) + align256((size_t)d_row * QSB * sizeof(float));
 }
 
 static gptq_status launch_row_params(int bits, bool sym, const float* Wws, int64_t d_row, int64_t d_col,
@@ -361,19 +312,20 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     sa.qmin = sa.sym ? -((1 << (p.bits - 1)) - 1) : 0;
     sa.qmax = sa.sym ? ((1 << (p.bits - 1)) - 1) : (1 << p.bits) - 1;
     sa.zoff = sa.sym ? (1 << (p.bits - 1)) : 0;
-    const dim3 sgrid((unsigned)((d_row + QROWS - 1) / QROWS));
-    for (int64_t b0 = 0; b0 < d_col; b0 += QB) {
-        const int nb = (int)std::min<int64_t>(QB, d_col - b0);
-        sa.b0 = b0; sa.nb = nb;
-        sweep_kernel<<<sgrid, QT, 0, s>>>(sa);
-        GPTQ_LAUNCH_CHECK();
-        const int64_t b1 = b0 + nb;
-        if (b1 < d_col) {
-            TrailArgs ta{Wws, d_row, d_col, E, U, b0, b1, nb};
-            dim3 tgrid((unsigned)((d_col - b1 + TB - 1) / TB), (unsigned)((d_row + TB - 1) / TB));
-            trail_kernel<<<tgrid, 256, 0, s>>>(ta);
-            GPTQ_LAUNCH_CHECK();
+    for (int64_t s0 = 0; s0 < d_col; s0 += QSB) {
+        const int64_t s1 = std::min<int64_t>(s0 + QSB, d_col);
+        for (int64_t b0 = s0; b0 < s1; b0 += QB) {
+            const int nb = (int)std::min<int64_t>(QB, s1 - b0);
+            sa.b0 = b0; sa.nb = nb; sa.E = E + (b0 - s0); sa.lde = QSB;
+            st = sweep_launch(sa, s);
+            if (st != GPTQ_OK) return st;
+            // within the super-block
+            TrailArgs ta{Wws, d_row, d_col, E + (b0 - s0), QSB, U, b0, nb, b0 + nb, s1};
+            if ((st = trail(ta, s)) != GPTQ_OK) return st;
         }
+        // everything after the super-block, K = s1 - s0
+        TrailArgs tb{Wws, d_row, d_col, E, QSB, U, s0, (int)(s1 - s0), s1, d_col};
+        if ((st = trail(tb, s)) != GPTQ_OK) return st;
     }
     return GPTQ_OK;
 }

@@ -1,0 +1,223 @@
+// The GPTQ column sweep inside one 128-column block: fused group scale / zero
+// point, quantization, error compensation of the later columns of the block,
+// and the error block E for the lazy trailing update.
+//
+// GPTQ summary page: OBQ background (quantize one weight, then update the
+// remaining full-precision weights to compensate, in the direction given by the
+// inverse Hessian); "Innovation 1" (one column order for all rows); "Innovation
+// 2" (updates kept local to a block of B = 128 columns); "Innovation 3" (rows of
+// the Cholesky factor U of the inverse give the updates).  Quantization concepts
+// guide: "Mapping values to fewer bits", "Choose granularity".
+//
+// Layout: a workgroup owns 16 rows of the block; each row is held by the 16
+// lanes of one DPP row, lane q holding columns q, q+16, ..., q+112 in registers
+// (column-cyclic, so the triangular work stays balanced).  The block's diagonal
+// 128 x 128 part of U is staged in LDS, permuted so that a lane reads its eight
+// coefficients of the next step with two 16-byte LDS reads (prefetched one step
+// ahead).  The quantization error of column j is broadcast along the row with
+// DPP row_newbcast; group min/max use DPP butterfly reductions.
+
+#include <utility>
+
+#include "quant_internal.h"
+
+namespace gptq {
+
+template <int I, int N, typename F>
+GPTQ_DEV void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+constexpr int SSLOTS = QB / SL;     // columns per lane: q, q+16, ..., q+112
+
+GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 65504.f; }
+
+template <int SRC>
+GPTQ_DEV float row_bcast(float v) {  // DPP row_newbcast: lane SRC of each 16-lane row to the whole row
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + SRC, 0xf, 0xf, false));
+}
+template <int CTRL>
+GPTQ_DEV float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+GPTQ_DEV float row_min(float v) {
+    v = fminf(v, quad_perm<QP_XOR1>(v));
+    v = fminf(v, quad_perm<QP_XOR2>(v));
+    v = fminf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    return fminf(v, dpp_f<DPP_MIRROR>(v));
+}
+GPTQ_DEV float row_max(float v) {
+    v = fmaxf(v, quad_perm<QP_XOR1>(v));
+    v = fmaxf(v, quad_perm<QP_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    return fmaxf(v, dpp_f<DPP_MIRROR>(v));
+}
+
+__global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
+    __shared__ __attribute__((aligned(16))) float Up[QB][SL][SSLOTS];  // Up[j][q][i] = U[b0+j][b0+q+16i]
+    __shared__ float invd[QB];                                         // 1 / U[b0+j][b0+j]
+    __shared__ uint8_t cl[SROWS][QB];
+    __shared__ int bad_any;
+
+    const int tid = threadIdx.x;
+    const int q = tid & (SL - 1);
+    const int rl = tid >> 4;
+    const int64_t row = (int64_t)blockIdx.x * SROWS + rl;
+    const bool rv = row < a.d_row;
+    const int nb = a.nb;
+    const int G = a.group;
+    const float fqmin = (float)a.qmin, fqmax = (float)a.qmax, fzoff = (float)a.zoff;
+    if (tid == 0) bad_any = 0;
+
+    for (int idx = tid; idx < QB * QB; idx += QT) {
+        const int j = idx >> 7, c = idx & 127;
+        const float u = (j < nb && c < nb) ? a.U[(a.b0 + j) * a.d_col + a.b0 + c] : 0.f;
+        Up[j][c & (SL - 1)][c >> 4] = u;
+        if (c == j) invd[j] = (j < nb) ? 1.0f / u : 0.f;
+    }
+    float w[SSLOTS], e[SSLOTS], uc[SSLOTS];
+    int cv[SSLOTS];
+    const float* wrow = a.Wws + (rv ? row : 0) * a.d_col + a.b0;
+#pragma unroll
+    for (int i = 0; i < SSLOTS; ++i) {
+        const int c = SL * i + q;
+        w[i] = (rv && c < nb) ? wrow[c] : 0.f;
+        e[i] = 0.f;
+        cv[i] = 0;
+    }
+    float s16f = 1.f, zf = 0.f;
+    bool bad = false;
+    if (G == 0 && rv) {
+        s16f = f16_bits_to_f32(a.scales[row * a.n_groups]);
+        zf = f16_bits_to_f32(a.zeros[row * a.n_groups]) - fzoff;
+    }
+    __syncthreads();
+    {
+        const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Up[0][q][0]);
+        const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Up[0][q][4]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { uc[k] = u0[k]; uc[4 + k] = u1[k]; }
+    }
+    float idc = invd[0];
+
+    static_for<0, QB>([&](auto JC) {
+        constexpr int j = decltype(JC)::value;
+        constexpr int qj = j & (SL - 1), ij = j >> 4;
+        if (j >= nb) return;
+        // prefetch the coefficients of step j + 1
+        float un[SSLOTS];
+        float idn = 0.f;
+        if constexpr (j + 1 < QB) {
+            const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Up[j + 1][q][0]);
+            const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Up[j + 1][q][4]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { un[k] = u0[k]; un[4 + k] = u1[k]; }
+            idn = invd[j + 1];
+        }
+        // a group starts at a multiple of its size (32, 64 or 128), so only every 32nd
+        // step carries the group code
+        if constexpr ((j & 31) == 0) {
+            if (G > 0 && (j & (G - 1)) == 0) {
+                // group scale/zero from the current values of columns j .. j+G-1
+                const int iend = (j + G) >> 4;
+                float s, mn = 0.f;
+                if (a.sym) {
+                    float am = 0.f;
+#pragma unroll
+                    for (int i = ij; i < SSLOTS; ++i) if (i < iend) am = fmaxf(am, fabsf(w[i]));
+                    am = row_max(am);
+                    s = am > 0.f ? am / fqmax : 1.f;
+                } else {
+                    float mx = w[ij];
+                    mn = w[ij];
+#pragma unroll
+                    for (int i = ij + 1; i < SSLOTS; ++i)
+                        if (i < iend) { mn = fminf(mn, w[i]); mx = fmaxf(mx, w[i]); }
+                    mn = row_min(mn);
+                    mx = row_max(mx);
+                    if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
+                    s = (mx > mn) ? (mx - mn) / (fqmax - fqmin) : 1.f;
+                }
+                s16f = f16_bits_to_f32(f32_to_f16_bits(s));
+                if (!normal_f16_scale(s16f)) { bad = true; s16f = 1.f; }
+                zf = a.sym ? 0.f : fqmin - rintf(mn / s16f);
+                if (q == 0 && rv) {
+                    const int64_t g = (a.b0 + j) / G;
+                    a.scales[row * a.n_groups + g] = f32_to_f16_bits(s16f);
+                    a.zeros[row * a.n_groups + g] = f32_to_f16_bits(zf + fzoff);
+                }
+            }
+        }
+        // quantize column j (owner: lane qj of the row, slot ij); the code is decided
+        // with an IEEE fp32 division, the error is scaled by 1 / U[j][j]
+        const float wv = w[ij];
+        const float t = wv / s16f;
+        const float qv = fminf(fmaxf(rintf(t + zf), fqmin), fqmax);
+        const float wq = s16f * (qv - zf);
+        const float err = (wv - wq) * idc;
+        const float errb = row_bcast<qj>(err);
+        if (q == qj) {
+            e[ij] = err;
+            cv[ij] = (int)qv + a.zoff;
+            if (!(fabsf(err) <= 3.0e38f)) bad = true;
+        }
+        // compensate the later columns; U is upper triangular, so in slot ij the lanes
+        // holding columns <= j get a zero coefficient (or touch a finished column)
+        if constexpr (ij + 1 < SSLOTS || true) {
+            // the slot of the next column first: it is on the critical path
+            constexpr int in = ((j + 1) >> 4) < SSLOTS ? ((j + 1) >> 4) : SSLOTS - 1;
+            w[in] = fmaf(-errb, uc[in], w[in]);
+#pragma unroll
+            for (int i = ij; i < SSLOTS; ++i)
+                if (i != in) w[i] = fmaf(-errb, uc[i], w[i]);
+        }
+        if constexpr (j + 1 < QB) {
+#pragma unroll
+            for (int i = 0; i < SSLOTS; ++i) uc[i] = un[i];
+            idc = idn;
+        }
+        // bound the scheduling regions (compile time) while still letting the
+        // independent work of neighbouring steps overlap
+        if constexpr ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    });
+
+    if (rv) {
+        float* erow = a.E + row * a.lde;
+#pragma unroll
+        for (int i = 0; i < SSLOTS; ++i) {
+            const int c = SL * i + q;
+            if (c < nb) erow[c] = e[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SSLOTS; ++i) cl[rl][SL * i + q] = (uint8_t)cv[i];
+    if (bad && rv) atomicOr(&bad_any, 1);
+    __syncthreads();
+    if (tid == 0 && bad_any) *a.info = -1;
+
+    // pack the block's codes: two per byte (column 2k in the low nibble) or one per byte
+    const int per = a.packed ? 2 : 1;
+    const int nbytes = nb / per;
+    const int rowbytes = QB / per;
+    for (int idx = tid; idx < SROWS * rowbytes; idx += QT) {
+        const int r = idx / rowbytes, bidx = idx % rowbytes;
+        const int64_t grow = (int64_t)blockIdx.x * SROWS + r;
+        if (grow >= a.d_row || bidx >= nbytes) continue;
+        const uint8_t v = a.packed ? (uint8_t)((cl[r][2 * bidx] & 0xF) | ((cl[r][2 * bidx + 1] & 0xF) << 4))
+                                   : cl[r][bidx];
+        a.codes[grow * a.code_ld + a.b0 / per + bidx] = v;
+    }
+}
+
+gptq_status sweep_launch(const SweepArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.d_row + SROWS - 1) / SROWS));
+    sweep_kernel<<<grid, QT, 0, s>>>(a);
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
+}  // namespace gptq
