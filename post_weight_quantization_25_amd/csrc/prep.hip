@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double
 // --------------------------------------------------------------------------
 // fp64 GEMM on MFMA: C = beta C + alpha A op(B), 64 x 64 tiles, 4 waves (2 x 2 of 32 x 32).
 enum : int { G_BT = 1, G_TRI_A = 2, G_TRI_B = 4, G_LOWER_C = 8 };
-constexpr int GD_BM = 64, GD_BK = 16, GD_LD = GD_BK + 1;
+constexpr int GD_BM = 64, GD_BK = 32, GD_LD = GD_BK + 1;
 
 struct GemmD {
     double* C; int64_t ldc;
@@ -333,9 +333,55 @@ struct GemmD {
     int64_t sA, sB, sC; int M_last; int nbatch;
 };
 
+// Operand chunk of GD_BK columns of k: 64 rows (m or n) x 32 k, as 4 double2 per thread.
+template <bool KMAJOR>
+GPTQ_DEV void gd_load(const double* P, int64_t ld, int rows, int r0, int kc, int ke, int tid, double2 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i;            // 1024 double2 slots
+        double2 x = double2{0.0, 0.0};
+        if constexpr (!KMAJOR) {
+            // P[r][k] row-major with k contiguous: 16 double2 per row of 32 k
+            const int r = idx >> 4, k = kc + 2 * (idx & 15);
+            if (r0 + r < rows) {
+                const double* src = P + (int64_t)(r0 + r) * ld + k;
+                if (k + 1 < ke) x = *reinterpret_cast<const double2*>(src);
+                else if (k < ke) x.x = src[0];
+            }
+        } else {
+            // P[k][n] row-major with n contiguous: 32 double2 per k row of 64 n
+            const int k = kc + (idx >> 5), r = 2 * (idx & 31);
+            if (k < ke) {
+                const double* src = P + (int64_t)k * ld + r0 + r;
+                if (r0 + r + 1 < rows) x = *reinterpret_cast<const double2*>(src);
+                else if (r0 + r < rows) x.x = src[0];
+            }
+        }
+        v[i] = x;
+    }
+}
+
+template <bool KMAJOR>
+GPTQ_DEV void gd_store(double* S, int tid, const double2 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i;
+        if constexpr (!KMAJOR) {
+            const int r = idx >> 4, k = 2 * (idx & 15);
+            S[r * GD_LD + k] = v[i].x;
+            S[r * GD_LD + k + 1] = v[i].y;
+        } else {
+            const int k = idx >> 5, r = 2 * (idx & 31);
+            S[r * GD_LD + k] = v[i].x;
+            S[(r + 1) * GD_LD + k] = v[i].y;
+        }
+    }
+}
+
+template <bool BKMAJOR>
 __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
-    __shared__ double As[GD_BM * GD_LD];
-    __shared__ double Bs[GD_BM * GD_LD];
+    __shared__ double As[2][GD_BM * GD_LD];
+    __shared__ double Bs[2][GD_BM * GD_LD];
     const int bz = blockIdx.z;
     if (bz > 0) {
         g.A += bz * g.sA; g.B += bz * g.sB; g.C += bz * g.sC;
@@ -350,6 +396,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     const int mi = blockIdx.y, nj = blockIdx.x;
     const int m0 = mi * GD_BM, n0 = nj * GD_BM;
     if ((g.flags & G_LOWER_C) && n0 > m0 + GD_BM - 1) return;
+    if (m0 >= g.M) return;
     int kb = 0, ke = g.K;
     if (g.flags & G_TRI_A) ke = min(ke, m0 + GD_BM);           // A lower: A[m][k] = 0 for k > m
     if (g.flags & G_TRI_B) {
@@ -364,37 +411,42 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{};
 
-    for (int k0 = kb; k0 < ke; k0 += GD_BK) {
-        for (int idx = tid; idx < GD_BM * GD_BK; idx += 256) {
-            // A tile: m-major rows, k contiguous in memory
-            const int m = idx / GD_BK, k = idx % GD_BK;
-            const int gm = m0 + m, gk = k0 + k;
-            As[m * GD_LD + k] = (gm < g.M && gk < ke) ? g.A[(int64_t)gm * g.lda + gk] : 0.0;
-            double bv = 0.0;
-            if (g.flags & G_BT) {
-                const int gn = n0 + m;
-                if (gn < g.N && gk < ke) bv = g.B[(int64_t)gn * g.ldb + gk];
-                Bs[m * GD_LD + k] = bv;
-            } else {
-                const int kk = idx / GD_BM, n = idx % GD_BM;   // coalesced along n
-                const int gn = n0 + n, gk2 = k0 + kk;
-                if (gn < g.N && gk2 < ke) bv = g.B[(int64_t)gk2 * g.ldb + gn];
-                Bs[n * GD_LD + kk] = bv;
-            }
+    const int nch = (ke > kb) ? (ke - kb + GD_BK - 1) / GD_BK : 0;
+    double2 va[4], vb[4];
+    if (nch > 0) {
+        gd_load<false>(g.A, g.lda, g.M, m0, kb, ke, tid, va);
+        gd_load<BKMAJOR>(g.B, g.ldb, g.N, n0, kb, ke, tid, vb);
+        gd_store<false>(As[0], tid, va);
+        gd_store<BKMAJOR>(Bs[0], tid, vb);
+        if (nch > 1) {
+            gd_load<false>(g.A, g.lda, g.M, m0, kb + GD_BK, ke, tid, va);
+            gd_load<BKMAJOR>(g.B, g.ldb, g.N, n0, kb + GD_BK, ke, tid, vb);
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const double* as = As[c & 1];
+        const double* bs = Bs[c & 1];
 #pragma unroll
         for (int kk = 0; kk < GD_BK; kk += 4) {
             double fa[2], fb[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = As[(wr * 32 + i * 16 + (lane & 15)) * GD_LD + kk + (lane >> 4)];
+            for (int i = 0; i < 2; ++i) fa[i] = as[(wr * 32 + i * 16 + (lane & 15)) * GD_LD + kk + (lane >> 4)];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = Bs[(wc * 32 + j * 16 + (lane & 15)) * GD_LD + kk + (lane >> 4)];
+            for (int j = 0; j < 2; ++j) fb[j] = bs[(wc * 32 + j * 16 + (lane & 15)) * GD_LD + kk + (lane >> 4)];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (c + 1 < nch) {
+            gd_store<false>(As[(c + 1) & 1], tid, va);
+            gd_store<BKMAJOR>(Bs[(c + 1) & 1], tid, vb);
+        }
+        if (c + 2 < nch) {
+            gd_load<false>(g.A, g.lda, g.M, m0, kb + (c + 2) * GD_BK, ke, tid, va);
+            gd_load<BKMAJOR>(g.B, g.ldb, g.N, n0, kb + (c + 2) * GD_BK, ke, tid, vb);
         }
         __syncthreads();
     }
@@ -428,7 +480,8 @@ static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int
     if (M <= 0 || N <= 0 || nbatch <= 0) return GPTQ_OK;
     GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch};
     dim3 grid((N + GD_BM - 1) / GD_BM, (M + GD_BM - 1) / GD_BM, nbatch);
-    gemm_f64_kernel<<<grid, 256, 0, c.s>>>(g);
+    if (flags & G_BT) gemm_f64_kernel<false><<<grid, 256, 0, c.s>>>(g);
+    else gemm_f64_kernel<true><<<grid, 256, 0, c.s>>>(g);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
