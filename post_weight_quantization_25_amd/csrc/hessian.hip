@@ -7,16 +7,16 @@
 // on or above the diagonal are computed (256 x 256 output tiles, one workgroup of
 // eight waves per CU, each wave accumulating a 64 x 128 sub-tile in 8 MFMAs).  X is stored
 // token-major (channels contiguous), i.e. the contraction index is the strided
-// one.  Tiles are copied to LDS as they lie in memory (coalesced 16-byte loads,
-// conflict-free 16-byte LDS writes) and the MFMA operands, which need 8
-// consecutive tokens of one channel per lane, are read with the gfx950
-// transposing LDS read ds_read_b64_tr_b16.
-// Global loads run one 64-token stage ahead of the MFMAs, LDS is double
-// buffered.  The token range is split S ways; each XCD (workgroups are
-// dealt round-robin to the 8 XCDs) owns a compact range of tiles and walks the
-// splits in order, so all XCDs read the same token slab at about the same time.  Each work item writes its fp32
-// partial tile; the last work item of a tile to finish (tile counter) sums the
-// S partials in split order and updates H, so results are bitwise reproducible.
+// one.  Tiles are copied to LDS as they lie in memory by direct global -> LDS
+// loads (global_load_lds_dwordx4, no register staging) into a ring of four
+// 32-token stages, and the MFMA operands, which need 8 consecutive tokens of one
+// channel per lane, are read with the gfx950 transposing LDS read
+// ds_read_b64_tr_b16; the 16-byte chunks of a row are XOR-swizzled so that these
+// reads are free of bank conflicts.
+// The token range is split S ways; XCDs are grouped and each group owns a compact
+// run of tiles (see the work mapping in the kernel).  Each work item writes its
+// fp32 partial tile; a second kernel sums the S partials of every element in split
+// order and updates H, so results are bitwise reproducible.
 //
 // fp32 / fp16 X: exact-product path on v_mfma_f32_16x16x4_f32, one WG per
 // 64 x 64 upper tile over all tokens (no split).
@@ -56,128 +56,233 @@ __host__ __device__ inline void upper_tile(int idx, int nt, int& ti, int& tj) {
 // ----------------------------------------------------------------------------
 // bf16 path
 constexpr int HB_BM = 256;           // tile edge (channels)
-constexpr int HB_BK = 64;            // tokens per LDS stage
-constexpr int HB_RS = HB_BM + 16;    // LDS row = one token: 256 channels + pad (544 B = 136 dwords)
+constexpr int HB_BK = 32;            // tokens per LDS stage
+constexpr int HB_NSTG = 4;           // LDS ring depth (stages in flight: 3 loading, 1 computing)
 constexpr int HB_THREADS = 512;      // 8 waves: wave (wr, wc) owns rows wr*64.., columns wc*128..
-constexpr int HB_SLICE = 32;         // rows per LDS-staged slice of the final reduction
-constexpr int HB_TILE = HB_BK * HB_RS;  // bf16 elements of one operand stage
+constexpr int HB_OPE = HB_BK * HB_BM;  // bf16 elements of one operand stage (16 KB)
+constexpr int HB_STE = 2 * HB_OPE;     // bf16 elements of one stage (A then B)
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 struct HessBf16Args {
     const uint16_t* X; int64_t n; int d; int64_t ldx;
-    float* H; float* partials; int* counters;
+    float* H; float* partials;
     int nt; int T; int S; int64_t ks;  // tokens per split (multiple of HB_BK)
-    int tpx;                           // tiles per XCD
+    int tpg;                           // tiles per XCD group
+    int xpg;                           // XCDs per group (1, 2, 4 or 8)
 };
 
-// One thread's share of a stage: 8 chunks of 8 channels (16 B) from token rows
-// k = kr + 8 i of the stage, channel chunk cc (lanes consecutive in cc: 512 B per row).
-template <bool FULL>
-GPTQ_DEV void load_stage(const HessBf16Args& a, int64_t t0, int64_t t_end, int c, int kr, u32x4_t (&r)[8]) {
+// LDS layout of an operand stage: token rows of 256 channels (512 B, 32 chunks of
+// 16 B), chunk c of row k stored at chunk position c ^ 2 f(k mod 4), f = 0, 3, 5, 6.
+// A transposed fragment read touches 4 consecutive rows, 32 B per row for 16 lanes
+// and 64 B per row for 32 lanes; with this swizzle the 4 rows fall on distinct banks
+// both within 128 B (f mod 4 distinct) and within 256 B (f / 2 mod 4 distinct).
+GPTQ_DEV int swz(int k, int c) {
+    const int r = k & 3;
+    const int f = 2 * r + ((r ^ (r >> 1)) & 1);
+    return c ^ (f << 1);
+}
+
+// One direct global -> LDS load (global_load_lds_dwordx4, scalar-base form): lane i
+// reads 16 bytes at sbase + voff_i and they land at LDS byte address lds_base + 16 i
+// (sbase and lds_base wave-uniform; lds_base is passed in M0).  Written as inline asm:
+// the compiler counts the builtin's LDS write against every later LDS read of the
+// array and inserts a full vmcnt(0) wait before it, which would leave no load in
+// flight; here the waits are explicit (the asm has no register results, the data
+// goes to LDS only).
+GPTQ_DEV void dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+}
+
+GPTQ_DEV uint32_t lds_addr(const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// Per-wave constants of the stage copy.  Wave w issues loads 4w .. 4w+3 of 1 KB
+// each; load i (of the wave) covers operand w / 4 (0: the c0 channel block, 1: c1),
+// token rows kb + 2 i and kb + 2 i + 1 (kb = 8 (w % 4)), lane l writing chunk
+// position l % 32 of row kb + 2 i + l / 32, i.e. logical chunk swz(row, l % 32).  Only
+// two distinct per-lane byte offsets occur (the swizzle depends on the row mod 4).
+struct StageCopy {
+    uint32_t voff[2];      // per-lane byte offsets for even / odd i
+    int64_t row_elems;     // ldx
+    int cbase;             // channel base of this wave's operand (wave-uniform)
+    int wave_u;
+};
+
+GPTQ_DEV StageCopy stage_copy_setup(const HessBf16Args& a, int c0, int c1, int wave, int lane) {
+    StageCopy sc;
+    sc.wave_u = __builtin_amdgcn_readfirstlane(wave);
+    sc.cbase = (sc.wave_u >> 2) ? c1 : c0;
+    sc.row_elems = a.ldx;
+    const int kb = (wave & 3) * 8 + (lane >> 5), pc = lane & 31;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t t = t0 + kr + 8 * i;
-        if constexpr (FULL) {
-            r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.X + t * a.ldx + c));
-        } else {
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-            if (t < t_end) {
-                if (c + 8 <= a.d) {
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.X + t * a.ldx + c);
-                    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-                } else {
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t v = (c + e < a.d) ? (uint32_t)a.X[t * a.ldx + c + e] : 0u;
-                        w[e >> 1] |= v << (16 * (e & 1));
-                    }
-                }
-            }
-            r[i] = u32x4_t{w[0], w[1], w[2], w[3]};
-        }
+    for (int par = 0; par < 2; ++par)
+        sc.voff[par] = (uint32_t)(((int64_t)kb * a.ldx + 8 * swz(kb + 2 * par, pc)) * 2);
+    return sc;
+}
+
+// Direct global -> LDS copy of one stage (tokens t0 .. t0 + 31) into buf.
+GPTQ_DEV void issue_stage(const HessBf16Args& a, const StageCopy& sc, uint16_t* buf, int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint16_t* sbase = a.X + (t0 + 2 * i) * sc.row_elems + sc.cbase;
+        dma16(sc.voff[i & 1], sbase, lds_addr(buf) + (uint32_t)(sc.wave_u * 4 + i) * 1024u);
     }
 }
 
-// Store the chunks token-major (the layout they have in memory): conflict-free 16 B writes.
-GPTQ_DEV void store_stage(uint16_t* tile, int cc, int kr, const u32x4_t (&r)[8]) {
+// Register path for tiles at the matrix edge or a partial stage: zero-filled loads
+// written to the same swizzled layout.
+GPTQ_DEV void copy_stage_edge(const HessBf16Args& a, uint16_t* buf, int64_t t0, int64_t t_end, int c0, int c1, int tid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(tile + (kr + 8 * i) * HB_RS + cc * 8) = r[i];
+    for (int i = 0; i < 4; ++i) {
+        const int p = tid + 512 * i;
+        const int op = p >> 10, pos = p & 1023;
+        const int k = pos >> 5, pc = pos & 31;
+        const int c = swz(k, pc);
+        const int64_t t = t0 + k;
+        const int ch = (op ? c1 : c0) + 8 * c;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (t < t_end) {
+            if (ch + 8 <= a.d && ((reinterpret_cast<uintptr_t>(a.X + t * a.ldx + ch) & 15) == 0)) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.X + t * a.ldx + ch);
+                w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+            } else {
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t v = (ch + e < a.d) ? (uint32_t)a.X[t * a.ldx + ch + e] : 0u;
+                    w[e >> 1] |= v << (16 * (e & 1));
+                }
+            }
+        }
+        *reinterpret_cast<u32x4_t*>(buf + p * 8) = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
 }
 
 // MFMA operand fragment (32 channels x 16 tokens, lane l: channel l % 32, tokens
-// 8 (l / 32) .. +7) read from the token-major tile with two ds_read_b64_tr_b16.
-// Within each 16-lane group the instruction returns to lane i, element e, the
-// (i & 3)-th value of the 8-byte chunk addressed by lane (i >> 2) + 4 e; lane j
-// therefore addresses token k0 + (j >> 2), channels m0 + 4 (j & 3) .. +3, and lane i
-// receives channel m0 + i at tokens k0 .. k0 + 3.
-GPTQ_DEV bf16x8_t read_frag(const uint16_t* tile, int ch0, int kk, int lane) {
+// 8 (l / 32) .. +7) from a token-major swizzled operand stage, with two
+// ds_read_b64_tr_b16.  In each 16-lane group the instruction returns to lane i,
+// element e, the (i & 3)-th value of the 8-byte chunk addressed by lane (i >> 2) + 4 e;
+// lane j therefore addresses token k0 + (j >> 2), channels m0 + 4 (j & 3) .. +3, and
+// lane i receives channel m0 + i at tokens k0 .. k0 + 3.
+GPTQ_DEV bf16x8_t read_frag(const uint16_t* op, int ch0, int kk, int lane) {
     const int g = lane >> 4, j = lane & 15;
-    const int m0 = ch0 + (g & 1) * 16 + 4 * (j & 3);
+    const int m = ch0 + (g & 1) * 16 + 4 * (j & 3);
     const int k0 = kk + (g >> 1) * 8 + (j >> 2);
-    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + k0 * HB_RS + m0));
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + (k0 + 4) * HB_RS + m0));
+    const int c = m >> 3, half = (m >> 2) & 1;
+    const int k1 = k0 + 4;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(op + k0 * HB_BM + 8 * swz(k0, c) + 4 * half));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(op + k1 * HB_BM + 8 * swz(k1, c) + 4 * half));
     typedef short v8i16_t __attribute__((ext_vector_type(8)));
     const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// The MFMAs of one LDS stage for one wave: 2 x 4 tiles of 32 x 32, four k16 slices.
-GPTQ_DEV void mfma_stage(const uint16_t* A, const uint16_t* B, int wr, int wc, int lane, f32x16_t (&acc)[2][4]) {
+// One wave's operand fragments for one 16-token slice of a stage: 2 (rows) + 4
+// (columns) fragments of 32 channels.
+struct Frags { bf16x8_t a[2], b[4]; };
+
+GPTQ_DEV void read_slice(const uint16_t* stg, int kk, int wr, int wc, int lane, Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = read_frag(stg, wr * 64 + i * 32, kk, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = read_frag(stg + HB_OPE, wc * 128 + j * 32, kk, lane);
+}
+
+GPTQ_DEV void mfma_slice(const Frags& f, f32x16_t (&acc)[2][4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// The MFMAs of one LDS stage for one wave (both slices), used by the edge path.
+GPTQ_DEV void mfma_stage(const uint16_t* stg, int wr, int wc, int lane, f32x16_t (&acc)[2][4]) {
 #pragma unroll
     for (int kk = 0; kk < HB_BK; kk += 16) {
-        bf16x8_t fa[2], fb[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = read_frag(A, wr * 64 + i * 32, kk, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = read_frag(B, wc * 128 + j * 32, kk, lane);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        Frags f;
+        read_slice(stg, kk, wr, wc, lane, f);
+        mfma_slice(f, acc);
     }
 }
 
-// Main loop: stage st in LDS buffer st & 1; the registers hold stage st + 1.
-template <bool FULL>
-GPTQ_DEV void hess_main_loop(const HessBf16Args& a, uint16_t (*lds)[2][HB_TILE], int64_t t_beg, int64_t t_end,
-                             int64_t nst, int which, int cc, int kr, int lc, int wr, int wc, int lane,
-                             f32x16_t (&acc)[2][4]) {
-    u32x4_t r[8];
-    if (nst <= 0) return;
-    // a load past the last stage re-reads the last stage (in bounds, unused), so every
-    // iteration issues the same loads and the waits count them exactly
+// s_waitcnt vmcnt(8) lgkmcnt(0): the loads of the two stages issued after the one
+// about to be used may stay in flight; this wave's LDS reads are complete.
+GPTQ_DEV void wait_vm8_lgkm0() { __builtin_amdgcn_s_waitcnt(0x8 | (0x7 << 4)); }
+
+// Fast path: every stage full and the tile inside the matrix.  LDS ring of four
+// stages, DMA issued three stages ahead (re-loads of the last stage past the end
+// keep the number of loads in flight constant, so one wait count fits every step),
+// and the LDS reads software-pipelined by 16-token slices: the fragments of the
+// next slice are read while the MFMAs of the current one run.  Step u:
+//   read slice 1 of stage u | MFMAs of slice 0 | wait stage u+1, barrier |
+//   DMA stage u+4 into stage u's slot | read slice 0 of stage u+1 | MFMAs of slice 1.
+GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NSTG], int64_t t_beg, int64_t nst,
+                            int c0, int c1, int wr, int wc, int wave, int lane, f32x16_t (&acc)[2][4]) {
     auto t0 = [&](int64_t st) { return t_beg + (st < nst ? st : nst - 1) * HB_BK; };
-    load_stage<FULL>(a, t0(0), t_end, lc, kr, r);
-    store_stage(&lds[0][which][0], cc, kr, r);
-    load_stage<FULL>(a, t0(1), t_end, lc, kr, r);
+    const StageCopy sc = stage_copy_setup(a, c0, c1, wave, lane);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) issue_stage(a, sc, ring[i], t0(i));
+    wait_vm8_lgkm0();
     __syncthreads();
-    int64_t st = 0;
-    for (; st + 1 < nst; st += 2) {
-        mfma_stage(&lds[0][0][0], &lds[0][1][0], wr, wc, lane, acc);
-        store_stage(&lds[1][which][0], cc, kr, r);
-        load_stage<FULL>(a, t0(st + 2), t_end, lc, kr, r);
-        __syncthreads();
-        mfma_stage(&lds[1][0][0], &lds[1][1][0], wr, wc, lane, acc);
-        store_stage(&lds[0][which][0], cc, kr, r);
-        load_stage<FULL>(a, t0(st + 3), t_end, lc, kr, r);
-        __syncthreads();
+    issue_stage(a, sc, ring[3], t0(3));
+    Frags f0, f1;
+    read_slice(ring[0], 0, wr, wc, lane, f0);
+    for (int64_t st = 0; st < nst; st += HB_NSTG) {
+#pragma unroll
+        for (int u = 0; u < HB_NSTG; ++u) {
+            if (st + u < nst) {
+                read_slice(ring[u], 16, wr, wc, lane, f1);
+                mfma_slice(f0, acc);
+                __builtin_amdgcn_sched_barrier(0);   // keep the phases in this order
+                wait_vm8_lgkm0();
+                __syncthreads();
+                issue_stage(a, sc, ring[u], t0(st + u + 4));
+                if (st + u + 1 < nst) read_slice(ring[(u + 1) & 3], 0, wr, wc, lane, f0);
+                mfma_slice(f1, acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
-    if (st < nst) mfma_stage(&lds[0][0][0], &lds[0][1][0], wr, wc, lane, acc);
+    __builtin_amdgcn_s_waitcnt(0);   // drain the trailing re-loads before the LDS is reused
+    __syncthreads();
+}
+
+// Edge path: register copies, two LDS stages.
+GPTQ_DEV void hess_loop_edge(const HessBf16Args& a, uint16_t* const (&ring)[HB_NSTG], int64_t t_beg, int64_t t_end,
+                             int64_t nst, int c0, int c1, int wr, int wc, int tid, int lane, f32x16_t (&acc)[2][4]) {
+    for (int64_t st = 0; st < nst; st += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (st + u < nst) {
+                copy_stage_edge(a, ring[u], t_beg + (st + u) * HB_BK, t_end, c0, c1, tid);
+                __syncthreads();
+                mfma_stage(ring[u], wr, wc, lane, acc);
+            }
+        }
+    }
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][HB_TILE];  // 139264 B
-    __shared__ int last_flag;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_ring[HB_NSTG * HB_STE];  // 4 x 32 KB
+    uint16_t* const ring[HB_NSTG] = {lds_ring, lds_ring + HB_STE, lds_ring + 2 * HB_STE, lds_ring + 3 * HB_STE};
 
-    // XCD-aware work mapping: workgroup L runs on XCD L % 8.  Each XCD owns a
-    // contiguous range of tpx tiles and walks the splits in order, so at any time
-    // all XCDs read the same token slab (shared through the Infinity Cache) and the
-    // workgroups of one XCD share channel blocks through its L2.
+    // XCD-aware work mapping: workgroup L runs on XCD L % 8 (round-robin dispatch).
+    // The tiles, in super-tile order, are cut into 8 / xpg runs of tpg tiles; the xpg
+    // XCDs of a group share one run and take its token splits in turn, each XCD
+    // walking its splits in order.  The 32 CUs of an XCD thus work on one or two
+    // splits of one compact run of tiles, whose few distinct channel blocks are
+    // shared through that XCD's L2.
     const int L = blockIdx.x;
     const int xcd = L & 7, k = L >> 3;
-    const int s = k / a.tpx, tile = xcd * a.tpx + k % a.tpx;
+    const int grp = xcd / a.xpg, xi = xcd % a.xpg;
+    const int tig = k % a.tpg;
+    const int s = (k / a.tpg) * a.xpg + xi, tile = grp * a.tpg + tig;
     if (s >= a.S || tile >= a.T) return;
     int ti, tj;
     upper_tile(tile, a.nt, ti, tj);
@@ -189,12 +294,6 @@ __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
 
-    // loader role: 256 threads per operand; 32 channel chunks (fastest) x 8 token rows
-    const int which = tid >> 8;
-    const int u = tid & 255;
-    const int cc = u & 31, kr = u >> 5;
-    const int lc = (which ? c1 : c0) + cc * 8;
-
     f32x16_t acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -202,10 +301,15 @@ __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
     const int64_t nst = (t_end > t_beg) ? (t_end - t_beg + HB_BK - 1) / HB_BK : 0;
+    // the DMA path: whole tiles, whole stages, 16-byte aligned rows, per-lane offsets
+    // (up to 31 rows) within 32 bits
     const bool full = (c0 + HB_BM <= a.d) && (c1 + HB_BM <= a.d) && ((t_end - t_beg) % HB_BK == 0) &&
-                      ((reinterpret_cast<uintptr_t>(a.X) & 15) == 0) && ((a.ldx & 7) == 0);
-    if (full) hess_main_loop<true>(a, lds, t_beg, t_end, nst, which, cc, kr, lc, wr, wc, lane, acc);
-    else hess_main_loop<false>(a, lds, t_beg, t_end, nst, which, cc, kr, lc, wr, wc, lane, acc);
+                      ((reinterpret_cast<uintptr_t>(a.X) & 15) == 0) && ((a.ldx & 7) == 0) &&
+                      (a.ldx < ((int64_t)1 << 25));
+    if (nst > 0) {
+        if (full) hess_loop_dma(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
+        else hess_loop_edge(a, ring, t_beg, t_end, nst, c0, c1, wr, wc, tid, lane, acc);
+    }
 
     // this split's partial tile (row-major 256 x 256 fp32)
     float* P = a.partials + ((int64_t)s * a.T + tile) * (HB_BM * HB_BM);
@@ -219,42 +323,56 @@ __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a
                 const int nn = wc * 128 + j * 32 + (lane & 31);
                 P[m * HB_BM + nn] = acc[i][j][e];
             }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const int old = atomicAdd(&a.counters[tile], 1);
-        last_flag = (old == a.S - 1);
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
+}
 
-    // last arriver: sum the partials in split order, update the upper triangle of H,
-    // and mirror it into the lower triangle through an LDS-staged transpose
-    float* st_lds = reinterpret_cast<float*>(&lds[0][0][0]);  // HB_SLICE x (HB_BM + 1) fp32
-    constexpr int SLD = HB_BM + 1;
-    for (int m0 = 0; m0 < HB_BM; m0 += HB_SLICE) {
-        for (int idx = tid; idx < HB_SLICE * HB_BM; idx += HB_THREADS) {
-            const int ml = idx / HB_BM, nn = idx % HB_BM, m = m0 + ml;
-            const int gr = c0 + m, gc = c1 + nn;
+// Split reduction: H += 2 * (sum of the S partial tiles, in split order), on the upper
+// triangle, mirrored into the lower triangle.  One workgroup per 16 rows of a tile;
+// thread t sums 4 x 4 consecutive columns with 16-byte loads (columns 4 (t % 16) +
+// 64 q, row t / 16), so every partial is read once, coalesced, by the whole grid.
+constexpr int HR_ROWS = 16;
+
+__global__ __launch_bounds__(256) void hess_reduce_kernel(HessBf16Args a) {
+    __shared__ float st[HR_ROWS][HB_BM + 1];
+    const int tile = blockIdx.x / (HB_BM / HR_ROWS), rc = blockIdx.x % (HB_BM / HR_ROWS);
+    int ti, tj;
+    upper_tile(tile, a.nt, ti, tj);
+    const int c0 = ti * HB_BM, c1 = tj * HB_BM;
+    const int tid = threadIdx.x, ml = tid >> 4, m = rc * HR_ROWS + ml;
+    const int64_t tstride = (int64_t)a.T * HB_BM * HB_BM;
+    const float* P = a.partials + (int64_t)tile * (HB_BM * HB_BM) + m * HB_BM + 4 * (tid & 15);
+    f32x4_t v[4] = {};
+#pragma unroll 4
+    for (int ss = 0; ss < a.S; ++ss) {
+        f32x4_t x[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            x[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(P + ss * tstride + 64 * q));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += x[q];
+    }
+    const int gr = c0 + m;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int nn = 4 * (tid & 15) + 64 * q + e, gc = c1 + nn;
             if (gr < a.d && gc < a.d && gr <= gc) {
-                float v = 0.f;
-                for (int ss = 0; ss < a.S; ++ss)
-                    v += __builtin_nontemporal_load(a.partials + ((int64_t)ss * a.T + tile) * (HB_BM * HB_BM) + m * HB_BM + nn);
-                const float nv = a.H[(int64_t)gr * a.d + gc] + 2.f * v;
-                a.H[(int64_t)gr * a.d + gc] = nv;
-                st_lds[ml * SLD + nn] = nv;
+                float* h = a.H + (int64_t)gr * a.d + gc;
+                const float nv = *h + 2.f * v[q][e];
+                *h = nv;
+                st[ml][nn] = nv;
             }
         }
-        __syncthreads();
-        for (int idx = tid; idx < HB_SLICE * HB_BM; idx += HB_THREADS) {
-            const int nn = idx / HB_SLICE, ml = idx % HB_SLICE, m = m0 + ml;
-            const int gr = c0 + m, gc = c1 + nn;
-            if (gr < a.d && gc < a.d && gr < gc) a.H[(int64_t)gc * a.d + gr] = st_lds[ml * SLD + nn];
+    __syncthreads();
+    // mirror: thread t writes column c1 + t of the slice as row c1 + t of H
+    const int gc = c1 + tid;
+    if (gc < a.d) {
+#pragma unroll
+        for (int r = 0; r < HR_ROWS; ++r) {
+            const int g = c0 + rc * HR_ROWS + r;
+            if (g < a.d && g < gc) a.H[(int64_t)gc * a.d + g] = st[r][tid];
         }
-        __syncthreads();
     }
-    if (tid == 0) a.counters[tile] = 0;
 }
 
 __global__ void fill_i32_kernel(int* p, int n, int v) {
@@ -339,37 +457,47 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(const void* X, int64_t n,
 // ----------------------------------------------------------------------------
 // Host side
 
-static void bf16_plan(int64_t n, int64_t d, int& nt, int& T, int& S, int64_t& ks, int& tpx) {
-    nt = (int)((d + HB_BM - 1) / HB_BM);
-    T = nt * (nt + 1) / 2;
-    tpx = (T + 7) / 8;
+struct Bf16Plan {
+    int nt, T, S, tpg, xpg;
+    int64_t ks;
+    int grid() const { return 8 * tpg * ((S + xpg - 1) / xpg); }
+};
+
+static Bf16Plan bf16_plan(int64_t n, int64_t d) {
+    Bf16Plan p;
+    p.nt = (int)((d + HB_BM - 1) / HB_BM);
+    p.T = p.nt * (p.nt + 1) / 2;
+    // one run of tiles per XCD (8 groups); fewer, larger groups raise the L2 hit rate
+    // but were not faster at d = 4096 once the split reduction ran in parallel
+    const int G = 8;
+    p.xpg = 8 / G;
+    p.tpg = (p.T + G - 1) / G;
     const int64_t nst = (n + HB_BK - 1) / HB_BK;
-    // split count: whole rounds of the 256 workgroup slots (one per CU) with a small
-    // tail, while the partial tiles (S * T * 256 KB written and read back) stay a
-    // small fraction of the activation traffic
-    const int slots = 256;
+    // split count: whole rounds of the 32 workgroup slots of each XCD (one per CU)
+    // with a small tail, while the partial tiles (S * T * 256 KB written and read
+    // back) stay a small fraction of the activation traffic
+    const int slots_per_xcd = 32;
     int best = 1;
     double best_cost = 1e300;
     for (int sp = 1; sp <= 64; ++sp) {
         if (sp > 1 && (int64_t)sp > nst) break;
-        const double items = 8.0 * tpx * sp;
-        const double rounds = items / slots;
-        const double eff = ((double)T * sp / slots) / std::ceil(rounds);
+        const double items = (double)p.tpg * ((sp + p.xpg - 1) / p.xpg);   // per XCD
+        const double rounds = std::ceil(items / slots_per_xcd);
+        const double eff = ((double)p.T * sp / (8.0 * slots_per_xcd)) / rounds;
         const double x_bytes = (double)n * d * 2.0;
-        const double p_bytes = (double)sp * T * HB_BM * HB_BM * 4.0 * 2.0;
+        const double p_bytes = (double)sp * p.T * HB_BM * HB_BM * 4.0 * 2.0;
         const double cost = 1.0 / eff + 0.5 * p_bytes / (x_bytes + 1.0);
         if (cost < best_cost - 1e-9) { best_cost = cost; best = sp; }
     }
-    S = best;
-    ks = ((nst + S - 1) / S) * HB_BK;
+    p.S = best;
+    p.ks = ((nst + p.S - 1) / p.S) * HB_BK;
+    return p;
 }
 
 size_t hessian_ws_bytes(int64_t n, int64_t d) {
     if (n <= 0 || d <= 0) return 0;
-    int nt, T, S, tpx; int64_t ks;
-    bf16_plan(n, d, nt, T, S, ks, tpx);
-    const size_t cnt = ((size_t)T * sizeof(int) + 255) & ~(size_t)255;
-    return cnt + (size_t)T * S * HB_BM * HB_BM * sizeof(float);
+    const Bf16Plan p = bf16_plan(n, d);
+    return (size_t)p.T * p.S * HB_BM * HB_BM * sizeof(float);
 }
 
 gptq_status hessian_launch(float* H, const void* X, gptq_dtype dt, int64_t n, int64_t d, int64_t ldx,
@@ -377,17 +505,15 @@ gptq_status hessian_launch(float* H, const void* X, gptq_dtype dt, int64_t n, in
     const bool aligned = ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && ((ldx & 7) == 0);
     if (dt == GPTQ_BF16 && aligned) {
         HessBf16Args a;
-        int nt, T, S, tpx; int64_t ks;
-        bf16_plan(n, d, nt, T, S, ks, tpx);
+        const Bf16Plan p = bf16_plan(n, d);
         if (ws_bytes < hessian_ws_bytes(n, d) || ws == nullptr) return GPTQ_ERR_WORKSPACE;
-        const size_t cnt = ((size_t)T * sizeof(int) + 255) & ~(size_t)255;
         a.X = reinterpret_cast<const uint16_t*>(X); a.n = n; a.d = (int)d; a.ldx = ldx;
-        a.H = H; a.counters = reinterpret_cast<int*>(ws);
-        a.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + cnt);
-        a.nt = nt; a.T = T; a.S = S; a.ks = ks; a.tpx = tpx;
-        fill_i32(a.counters, T, 0, stream);
+        a.H = H;
+        a.partials = reinterpret_cast<float*>(ws);
+        a.nt = p.nt; a.T = p.T; a.S = p.S; a.ks = p.ks; a.tpg = p.tpg; a.xpg = p.xpg;
+        hess_bf16_kernel<<<p.grid(), HB_THREADS, 0, stream>>>(a);
         GPTQ_LAUNCH_CHECK();
-        hess_bf16_kernel<<<8 * S * tpx, HB_THREADS, 0, stream>>>(a);
+        hess_reduce_kernel<<<p.T * (HB_BM / HR_ROWS), 256, 0, stream>>>(a);
         GPTQ_LAUNCH_CHECK();
         return GPTQ_OK;
     }
