@@ -8,8 +8,9 @@ factor of the inverse (fp64), the blocked column sweep with trailing updates
 Prints one JSON line.  ``value`` = quantized weights per second.
 
 Options: --steps K --warmup W --gpus N (only 1 is supported: the path runs on one
-GPU) --no-cpu-baseline --calibrate-copy (adds one plain 1 GiB device copy after
-the timed region, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters).
+GPU) --no-cpu-baseline --calibrate-copy (adds, after the timed region, one plain
+elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 multiply by 1), used to
+scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
 """
 from __future__ import annotations
 
@@ -181,9 +182,10 @@ def main():
     hess_launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in hev]))
 
     if args.calibrate_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.cuda.synchronize()
+        torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
     flops_hess = float(n) * d * (d + 1)            # symmetric rank-n update, upper triangle incl. diagonal
@@ -209,7 +211,8 @@ def main():
         "ms_per_layer": ms_layer,
         "ms_per_layer_quantize_only": ph["prep"] + ph["quant"],
         "phases_ms": ph,
-        "roofline": {"kernel": "hess_bf16_kernel", "bound": "mfma",
+        "roofline": {"kernel": "hess_bf16_kernel + hess_reduce_kernel (one gptq_hessian_accumulate call)",
+                     "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(flops_hess),

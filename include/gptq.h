@@ -83,7 +83,7 @@ typedef struct {
  *           GPTQ_BF16 products are exact in fp32 and run on bf16 MFMA;
  *           GPTQ_F32 and GPTQ_F16 run on fp32 MFMA.
  *  ws       device workspace of at least gptq_hessian_workspace_size(n_tokens, d_col)
- *           bytes (split-K partial sums and tile counters); contents on entry are
+ *           bytes (the fp32 partial sums of the token splits); contents on entry are
  *           ignored.  May be NULL when the size is 0.
  * The accumulation order is fixed, so results are bitwise reproducible.
  * n_tokens == 0 or d_col == 0 is a no-op.

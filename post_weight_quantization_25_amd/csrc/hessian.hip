@@ -473,21 +473,22 @@ static Bf16Plan bf16_plan(int64_t n, int64_t d) {
     p.xpg = 8 / G;
     p.tpg = (p.T + G - 1) / G;
     const int64_t nst = (n + HB_BK - 1) / HB_BK;
-    // split count: whole rounds of the 32 workgroup slots of each XCD (one per CU)
-    // with a small tail, while the partial tiles (S * T * 256 KB written and read
-    // back) stay a small fraction of the activation traffic
+    // split count: minimize the estimated time = rounds of the 32 workgroup slots of
+    // an XCD (one per CU) x stages per item x time of one 32-token stage of a
+    // 256 x 256 tile (about 0.75 us), plus writing and reading back the S partial
+    // tiles of 256 KB each (about 4 TB/s)
     const int slots_per_xcd = 32;
+    const double t_stage = 0.75e-6, bw = 4.0e12;
     int best = 1;
     double best_cost = 1e300;
     for (int sp = 1; sp <= 64; ++sp) {
         if (sp > 1 && (int64_t)sp > nst) break;
         const double items = (double)p.tpg * ((sp + p.xpg - 1) / p.xpg);   // per XCD
         const double rounds = std::ceil(items / slots_per_xcd);
-        const double eff = ((double)p.T * sp / (8.0 * slots_per_xcd)) / rounds;
-        const double x_bytes = (double)n * d * 2.0;
+        const double stages = (double)((nst + sp - 1) / sp);
         const double p_bytes = (double)sp * p.T * HB_BM * HB_BM * 4.0 * 2.0;
-        const double cost = 1.0 / eff + 0.5 * p_bytes / (x_bytes + 1.0);
-        if (cost < best_cost - 1e-9) { best_cost = cost; best = sp; }
+        const double cost = rounds * stages * t_stage + p_bytes / bw;
+        if (cost < best_cost - 1e-12) { best_cost = cost; best = sp; }
     }
     p.S = best;
     p.ks = ((nst + p.S - 1) / p.S) * HB_BK;
