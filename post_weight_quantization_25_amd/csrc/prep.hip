@@ -88,22 +88,17 @@ __global__ void prep_output_kernel(const double* X, int64_t d, float* U) {
 // that is not positive definite.
 constexpr int DLD = PNB + 1;
 
-__global__ __launch_bounds__(256) void prep_diag_kernel(double* A, double* X, int64_t d, int64_t k0, int n,
-                                                      int32_t* info) {
-    __shared__ double a[PNB * DLD];
-    __shared__ double xs[PNB * DLD];
-    __shared__ double ts[PNB * 32];
-    __shared__ int fail_s;
+// LDS of the diagonal routine: the block (padded rows), its inverse, and the
+// recursive-doubling temporaries (at most one 32 x 32 product, or two 16 x 16).
+constexpr int DIAG_TS = 32 * 32;
+constexpr int DIAG_LDS_DOUBLES = 2 * PNB * DLD + DIAG_TS;
+
+// The block is in a[] (lower part, identity padding past n).  All 256 threads of
+// the workgroup call this.
+GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double* A, double* X, int64_t d,
+                         int64_t k0, int n, int32_t* info) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int idx = tid; idx < PNB * PNB; idx += 256) {
-        const int i = idx >> 6, k = idx & 63;
-        double v = 0.0;
-        if (i < n && k <= i) v = A[(k0 + i) * d + k0 + k];
-        else if (i == k) v = 1.0;                      // identity padding of a short block
-        a[i * DLD + k] = v;
-    }
-    if (tid == 0) fail_s = 0;
-    __syncthreads();
+    int& fail_s = *fail_p;
 
     for (int c0 = 0; c0 < PNB; c0 += 8) {
         if (wave == 0) {
@@ -269,6 +264,29 @@ __global__ __launch_bounds__(256) void prep_diag_kernel(double* A, double* X, in
     }
 }
 
+// Load the lower part of diagonal block k (identity padding past n) into a[].
+GPTQ_DEV void diag_load(double* a, const double* A, int64_t d, int64_t k0, int n) {
+    for (int idx = threadIdx.x; idx < PNB * PNB; idx += 256) {
+        const int i = idx >> 6, k = idx & 63;
+        double v = 0.0;
+        if (i < n && k <= i) v = A[(k0 + i) * d + k0 + k];
+        else if (i == k) v = 1.0;
+        a[i * DLD + k] = v;
+    }
+}
+
+// Diagonal block 0 on its own (every later block is factored by the panel kernel
+// of the step before it).
+__global__ __launch_bounds__(256) void prep_diag_kernel(double* A, double* X, int64_t d, int64_t k0, int n,
+                                                      int32_t* info) {
+    __shared__ double lds[DIAG_LDS_DOUBLES];
+    __shared__ int fail_s;
+    if (threadIdx.x == 0) fail_s = 0;
+    diag_load(lds, A, d, k0, n);
+    __syncthreads();
+    diag_block(lds, lds + PNB * DLD, lds + 2 * PNB * DLD, &fail_s, A, X, d, k0, n, info);
+}
+
 // Panel: L[k0+64:, k0:k0+64] = A[k0+64:, k0:k0+64] X_kk^T, in place (each workgroup
 // reads its 64 rows completely before writing them).  fp64 MFMA 16x16x4.
 __global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double* X, int64_t d, int64_t k0) {
@@ -318,7 +336,7 @@ __global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double
 
 // --------------------------------------------------------------------------
 // fp64 GEMM on MFMA: C = beta C + alpha A op(B), 64 x 64 tiles, 4 waves (2 x 2 of 32 x 32).
-enum : int { G_BT = 1, G_TRI_A = 2, G_TRI_B = 4, G_LOWER_C = 8 };
+enum : int { G_BT = 1, G_TRI_A = 2, G_TRI_B = 4, G_LOWER_C = 8, G_DIAG0 = 16 };
 constexpr int GD_BM = 64, GD_BK = 32, GD_LD = GD_BK + 1;
 
 struct GemmD {
@@ -331,6 +349,10 @@ struct GemmD {
     // batching over blockIdx.z: operand offsets advance by these element strides;
     // the last batch entry may have fewer rows (M_last) and, for G_TRI_A, fewer k (= M_last)
     int64_t sA, sB, sC; int M_last; int nbatch;
+    // G_DIAG0: tile (0, 0) of C is the next diagonal block (rows / columns k1 ..
+    // k1 + n1 of the factored matrix fA, inverse blocks in fX); its workgroup
+    // factors it after the update instead of storing it
+    double* fA; double* fX; int64_t fd, k1; int n1; int32_t* info;
 };
 
 // Operand chunk of GD_BK columns of k: 64 rows (m or n) x 32 k, as 4 double2 per thread.
@@ -378,10 +400,16 @@ GPTQ_DEV void gd_store(double* S, int tid, const double2 (&v)[4]) {
     }
 }
 
+constexpr int GD_TILE = GD_BM * GD_LD;
+constexpr int GD_LDS = (4 * GD_TILE > DIAG_LDS_DOUBLES) ? 4 * GD_TILE : DIAG_LDS_DOUBLES;
+
 template <bool BKMAJOR>
 __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
-    __shared__ double As[2][GD_BM * GD_LD];
-    __shared__ double Bs[2][GD_BM * GD_LD];
+    // operand double buffers; the diagonal routine's buffers in the G_DIAG0 workgroup
+    __shared__ double lds[GD_LDS];
+    __shared__ int fail_s;
+    auto As = [&](int b) { return lds + b * GD_TILE; };
+    auto Bs = [&](int b) { return lds + (2 + b) * GD_TILE; };
     const int bz = blockIdx.z;
     if (bz > 0) {
         g.A += bz * g.sA; g.B += bz * g.sB; g.C += bz * g.sC;
@@ -396,6 +424,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     const int mi = blockIdx.y, nj = blockIdx.x;
     const int m0 = mi * GD_BM, n0 = nj * GD_BM;
     if ((g.flags & G_LOWER_C) && n0 > m0 + GD_BM - 1) return;
+    const bool diag0 = (g.flags & G_DIAG0) && mi == 0 && nj == 0 && bz == 0;
     if (m0 >= g.M) return;
     int kb = 0, ke = g.K;
     if (g.flags & G_TRI_A) ke = min(ke, m0 + GD_BM);           // A lower: A[m][k] = 0 for k > m
@@ -416,8 +445,8 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     if (nch > 0) {
         gd_load<false>(g.A, g.lda, g.M, m0, kb, ke, tid, va);
         gd_load<BKMAJOR>(g.B, g.ldb, g.N, n0, kb, ke, tid, vb);
-        gd_store<false>(As[0], tid, va);
-        gd_store<BKMAJOR>(Bs[0], tid, vb);
+        gd_store<false>(As(0), tid, va);
+        gd_store<BKMAJOR>(Bs(0), tid, vb);
         if (nch > 1) {
             gd_load<false>(g.A, g.lda, g.M, m0, kb + GD_BK, ke, tid, va);
             gd_load<BKMAJOR>(g.B, g.ldb, g.N, n0, kb + GD_BK, ke, tid, vb);
@@ -425,8 +454,8 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     }
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        const double* as = As[c & 1];
-        const double* bs = Bs[c & 1];
+        const double* as = As(c & 1);
+        const double* bs = Bs(c & 1);
 #pragma unroll
         for (int kk = 0; kk < GD_BK; kk += 4) {
             double fa[2], fb[2];
@@ -441,14 +470,34 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
                     acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
         if (c + 1 < nch) {
-            gd_store<false>(As[(c + 1) & 1], tid, va);
-            gd_store<BKMAJOR>(Bs[(c + 1) & 1], tid, vb);
+            gd_store<false>(As((c + 1) & 1), tid, va);
+            gd_store<BKMAJOR>(Bs((c + 1) & 1), tid, vb);
         }
         if (c + 2 < nch) {
             gd_load<false>(g.A, g.lda, g.M, m0, kb + (c + 2) * GD_BK, ke, tid, va);
             gd_load<BKMAJOR>(g.B, g.ldb, g.N, n0, kb + (c + 2) * GD_BK, ke, tid, vb);
         }
         __syncthreads();
+    }
+    if (diag0) {
+        // updated diagonal block -> a[] (lower part; upper 0, identity padding), factor
+        double* a = lds;
+        if (tid == 0) fail_s = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = wr * 32 + i * 16 + 4 * e + (lane >> 4);
+                    const int cc = wc * 32 + j * 16 + (lane & 15);
+                    double v = (r == cc) ? 1.0 : 0.0;
+                    if (r < g.n1 && cc <= r) v = g.beta * g.C[(int64_t)r * g.ldc + cc] + g.alpha * acc[i][j][e];
+                    a[r * DLD + cc] = v;
+                }
+        __syncthreads();
+        diag_block(a, a + PNB * DLD, a + 2 * PNB * DLD, &fail_s, g.fA, g.fX, g.fd, g.k1, g.n1, g.info);
+        return;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -476,9 +525,11 @@ struct PrepCtx {
 
 static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int64_t lda, const double* B,
                         int64_t ldb, int M, int N, int K, double alpha, double beta, int flags,
-                        int nbatch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, int M_last = 0) {
+                        int nbatch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, int M_last = 0,
+                        int64_t k1 = 0, int n1 = 0) {
     if (M <= 0 || N <= 0 || nbatch <= 0) return GPTQ_OK;
-    GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch};
+    GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch,
+            c.A, c.X, c.d, k1, n1, c.info};
     dim3 grid((N + GD_BM - 1) / GD_BM, (M + GD_BM - 1) / GD_BM, nbatch);
     if (flags & G_BT) gemm_f64_kernel<false><<<grid, 256, 0, c.s>>>(g);
     else gemm_f64_kernel<true><<<grid, 256, 0, c.s>>>(g);
@@ -492,17 +543,20 @@ static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int
 static gptq_status cholinv(PrepCtx& c) {
     const int64_t d = c.d;
     gptq_status st;
+    prep_diag_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, 0, (int)std::min<int64_t>(PNB, d), c.info);
+    GPTQ_LAUNCH_CHECK();
     for (int64_t k0 = 0; k0 < d; k0 += PNB) {
         const int n = (int)std::min<int64_t>(PNB, d - k0);
-        prep_diag_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, k0, n, c.info);
-        GPTQ_LAUNCH_CHECK();
         const int64_t rest = d - k0 - n;
         if (rest <= 0) break;
         prep_panel_kernel<<<(unsigned)((rest + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, k0);
         GPTQ_LAUNCH_CHECK();
+        // trailing update; its workgroup of tile (0, 0) also factors diagonal block k+1
         double* L21 = c.A + (k0 + n) * d + k0;
         double* A22 = c.A + (k0 + n) * d + k0 + n;
-        if ((st = gemm(c, A22, d, L21, d, L21, d, (int)rest, (int)rest, n, -1.0, 1.0, G_BT | G_LOWER_C)) != GPTQ_OK)
+        if ((st = gemm(c, A22, d, L21, d, L21, d, (int)rest, (int)rest, n, -1.0, 1.0,
+                       G_BT | G_LOWER_C | G_DIAG0, 1, 0, 0, 0, 0, k0 + n,
+                       (int)std::min<int64_t>(PNB, rest))) != GPTQ_OK)
             return st;
     }
     for (int64_t b = PNB; b < d; b *= 2) {
