@@ -351,15 +351,24 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(HessBf16Args a) {
         for (int q = 0; q < 4; ++q) v[q] += x[q];
     }
     const int gr = c0 + m;
+    // all loads of H first, then the stores (a load after a store to the same array
+    // would otherwise wait for that store's round trip)
+    float h0[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int gc = c1 + 4 * (tid & 15) + 64 * q + e;
+            h0[q][e] = (gr < a.d && gc < a.d && gr <= gc) ? a.H[(int64_t)gr * a.d + gc] : 0.f;
+        }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int nn = 4 * (tid & 15) + 64 * q + e, gc = c1 + nn;
             if (gr < a.d && gc < a.d && gr <= gc) {
-                float* h = a.H + (int64_t)gr * a.d + gc;
-                const float nv = *h + 2.f * v[q][e];
-                *h = nv;
+                const float nv = h0[q][e] + 2.f * v[q][e];
+                a.H[(int64_t)gr * a.d + gc] = nv;
                 st[ml][nn] = nv;
             }
         }

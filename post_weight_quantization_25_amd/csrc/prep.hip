@@ -499,21 +499,47 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
         diag_block(a, a + PNB * DLD, a + 2 * PNB * DLD, &fail_s, g.fA, g.fX, g.fd, g.k1, g.n1, g.info);
         return;
     }
+    // C = beta C + alpha acc: all loads of C first, then all stores (a load after a
+    // store to the same array would otherwise wait for that store's round trip)
+    // v_mfma_f64_16x16x4_f64 result layout: element e of lane l is row 4 e + l / 16
+    const bool full = (m0 + GD_BM <= g.M) && (n0 + GD_BM <= g.N);
+    double* cbase = g.C + (int64_t)(m0 + wr * 32 + (lane >> 4)) * g.ldc + n0 + wc * 32 + (lane & 15);
+    auto off = [&](int i, int j, int e) { return (int64_t)(i * 16 + 4 * e) * g.ldc + j * 16; };
+    if (full) {
+        double cold[2][2][4];
+        if (g.beta != 0.0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // v_mfma_f64_16x16x4_f64 result layout: element e of lane l is row 4 e + l / 16
-                const int gm = m0 + wr * 32 + i * 16 + 4 * e + (lane >> 4);
-                const int gn = n0 + wc * 32 + j * 16 + (lane & 15);
-                if (gm < g.M && gn < g.N) {
-                    double* c = g.C + (int64_t)gm * g.ldc + gn;
+                    for (int e = 0; e < 4; ++e) cold[i][j][e] = cbase[off(i, j, e)];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
                     const double v = g.alpha * acc[i][j][e];
-                    *c = (g.beta == 0.0) ? v : g.beta * *c + v;
+                    cbase[off(i, j, e)] = (g.beta == 0.0) ? v : g.beta * cold[i][j][e] + v;
                 }
-            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int gm = m0 + wr * 32 + i * 16 + 4 * e + (lane >> 4);
+                    const int gn = n0 + wc * 32 + j * 16 + (lane & 15);
+                    if (gm < g.M && gn < g.N) {
+                        double* c = g.C + (int64_t)gm * g.ldc + gn;
+                        const double v = g.alpha * acc[i][j][e];
+                        *c = (g.beta == 0.0) ? v : g.beta * *c + v;
+                    }
+                }
+    }
 }
 
 // --------------------------------------------------------------------------

@@ -231,16 +231,35 @@ __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
         if (c + 2 < nch) trail_load(a, m0, n0, (c + 2) * TK, tid, re, ru);
         __syncthreads();
     }
+    // W -= acc: all loads first, then all stores (a load after a store to the same
+    // array would otherwise wait for that store's round trip)
+    const bool full = (m0 + TB <= a.d_row) && (n0 + TB <= a.n_end);
+    float* wbase = a.Wws + (m0 + wr * 64 + 4 * (lane >> 5)) * a.d_col + n0 + wc * 64 + (lane & 31);
+    auto off = [&](int i, int j, int e) { return (int64_t)(i * 32 + 8 * (e >> 2) + (e & 3)) * a.d_col + j * 32; };
+    if (full) {
+        // one accumulator tile (16 values per lane) at a time keeps the register count low
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j) {
+                float old[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t gm = m0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int64_t gn = n0 + wc * 64 + j * 32 + (lane & 31);
-                if (gm < a.d_row && gn < a.n_end) a.Wws[gm * a.d_col + gn] -= acc[i][j][e];
+                for (int e = 0; e < 16; ++e) old[e] = wbase[off(i, j, e)];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) wbase[off(i, j, e)] = old[e] - acc[i][j][e];
             }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t gm = m0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    const int64_t gn = n0 + wc * 64 + j * 32 + (lane & 31);
+                    if (gm < a.d_row && gn < a.n_end) a.Wws[gm * a.d_col + gn] -= acc[i][j][e];
+                }
+    }
 }
 
 static gptq_status trail(const TrailArgs& ta, hipStream_t s) {
