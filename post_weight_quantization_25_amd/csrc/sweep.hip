@@ -79,7 +79,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         Up[j][c & (SL - 1)][c >> 4] = u;
         if (c == j) invd[j] = (j < nb) ? 1.0f / u : 0.f;
     }
-    float w[SSLOTS], e[SSLOTS], uc[SSLOTS];
+    float w[SSLOTS], e[SSLOTS];
     int cv[SSLOTS];
     const float* wrow = a.Wws + (rv ? row : 0) * a.d_col + a.b0;
 #pragma unroll
@@ -89,33 +89,53 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         e[i] = 0.f;
         cv[i] = 0;
     }
-    float s16f = 1.f, zf = 0.f;
+    float s16f = 1.f, r16f = 1.f, zf = 0.f;
     bool bad = false;
     if (G == 0 && rv) {
         s16f = f16_bits_to_f32(a.scales[row * a.n_groups]);
+        r16f = 1.0f / s16f;
         zf = f16_bits_to_f32(a.zeros[row * a.n_groups]) - fzoff;
     }
     __syncthreads();
+    // U coefficients of the current and the next step, alternating by step parity
+    float ucA[SSLOTS], ucB[SSLOTS];
     {
         const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Up[0][q][0]);
         const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Up[0][q][4]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) { uc[k] = u0[k]; uc[4 + k] = u1[k]; }
+        for (int k = 0; k < 4; ++k) { ucA[k] = u0[k]; ucA[4 + k] = u1[k]; }
     }
     float idc = invd[0];
 
+    // All 128 steps run: past nb (the last block of a width that is not a multiple of
+    // 128) the weights, U and 1 / U[j][j] are 0, so those steps change nothing.
     static_for<0, QB>([&](auto JC) {
         constexpr int j = decltype(JC)::value;
         constexpr int qj = j & (SL - 1), ij = j >> 4;
-        if (j >= nb) return;
-        // prefetch the coefficients of step j + 1
-        float un[SSLOTS];
+        float* uc = (j & 1) ? ucB : ucA;
+        float* un = (j & 1) ? ucA : ucB;
+        // prefetch the coefficients of step j + 1, only the slots it uses (a loaded
+        // value left unused lets the compiler reuse its register while the load is in
+        // flight, which costs a wait every step)
         float idn = 0.f;
         if constexpr (j + 1 < QB) {
-            const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Up[j + 1][q][0]);
-            const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Up[j + 1][q][4]);
+            constexpr int i1 = (j + 1) >> 4;
+            if constexpr (i1 == 0) {
+                const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Up[j + 1][q][0]);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) { un[k] = u0[k]; un[4 + k] = u1[k]; }
+                for (int k = 0; k < 4; ++k) un[k] = u0[k];
+            } else {
+#pragma unroll
+                for (int k = i1; k < 4; ++k) un[k] = Up[j + 1][q][k];
+            }
+            if constexpr (i1 <= 4) {
+                const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Up[j + 1][q][4]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) un[4 + k] = u1[k];
+            } else {
+#pragma unroll
+                for (int k = i1; k < SSLOTS; ++k) un[k] = Up[j + 1][q][k];
+            }
             idn = invd[j + 1];
         }
         // a group starts at a multiple of its size (32, 64 or 128), so only every 32nd
@@ -124,13 +144,13 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
             if (G > 0 && (j & (G - 1)) == 0) {
                 // group scale/zero from the current values of columns j .. j+G-1
                 const int iend = (j + G) >> 4;
-                float s, mn = 0.f;
+                float sc, mn = 0.f;
                 if (a.sym) {
                     float am = 0.f;
 #pragma unroll
                     for (int i = ij; i < SSLOTS; ++i) if (i < iend) am = fmaxf(am, fabsf(w[i]));
                     am = row_max(am);
-                    s = am > 0.f ? am / fqmax : 1.f;
+                    sc = am > 0.f ? am / fqmax : 1.f;
                 } else {
                     float mx = w[ij];
                     mn = w[ij];
@@ -140,46 +160,42 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                     mn = row_min(mn);
                     mx = row_max(mx);
                     if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
-                    s = (mx > mn) ? (mx - mn) / (fqmax - fqmin) : 1.f;
+                    sc = (mx > mn) ? (mx - mn) / (fqmax - fqmin) : 1.f;
                 }
-                s16f = f16_bits_to_f32(f32_to_f16_bits(s));
+                s16f = f16_bits_to_f32(f32_to_f16_bits(sc));
                 if (!normal_f16_scale(s16f)) { bad = true; s16f = 1.f; }
+                r16f = 1.0f / s16f;
                 zf = a.sym ? 0.f : fqmin - rintf(mn / s16f);
-                if (q == 0 && rv) {
+                if (q == 0 && rv && a.b0 + j < a.d_col) {
                     const int64_t g = (a.b0 + j) / G;
                     a.scales[row * a.n_groups + g] = f32_to_f16_bits(s16f);
                     a.zeros[row * a.n_groups + g] = f32_to_f16_bits(zf + fzoff);
                 }
             }
         }
-        // quantize column j (owner: lane qj of the row, slot ij); the code is decided
-        // with an IEEE fp32 division, the error is scaled by 1 / U[j][j]
+        // quantize column j (owner: lane qj of the row, slot ij).  t = w / S16 correctly
+        // rounded: q0 = w r with r = 1 / S16 correctly rounded, then one correction with
+        // the exact residual w - q0 S16 (Markstein); equal to the IEEE quotient
         const float wv = w[ij];
-        const float t = wv / s16f;
+        const float q0 = wv * r16f;
+        const float t = fmaf(fmaf(-q0, s16f, wv), r16f, q0);
         const float qv = fminf(fmaxf(rintf(t + zf), fqmin), fqmax);
         const float wq = s16f * (qv - zf);
         const float err = (wv - wq) * idc;
         const float errb = row_bcast<qj>(err);
-        if (q == qj) {
-            e[ij] = err;
-            cv[ij] = (int)qv + a.zoff;
-            if (!(fabsf(err) <= 3.0e38f)) bad = true;
-        }
+        const bool own = (q == qj);
+        e[ij] = own ? err : e[ij];
+        cv[ij] = own ? (int)qv + a.zoff : cv[ij];
+        bad = bad || (own && !(fabsf(err) <= 3.0e38f));
         // compensate the later columns; U is upper triangular, so in slot ij the lanes
-        // holding columns <= j get a zero coefficient (or touch a finished column)
-        if constexpr (ij + 1 < SSLOTS || true) {
-            // the slot of the next column first: it is on the critical path
-            constexpr int in = ((j + 1) >> 4) < SSLOTS ? ((j + 1) >> 4) : SSLOTS - 1;
-            w[in] = fmaf(-errb, uc[in], w[in]);
+        // holding columns <= j get a zero coefficient (or touch a finished column).
+        // The slot of the next column first: it is on the critical path.
+        constexpr int in = ((j + 1) >> 4) < SSLOTS ? ((j + 1) >> 4) : SSLOTS - 1;
+        w[in] = fmaf(-errb, uc[in], w[in]);
 #pragma unroll
-            for (int i = ij; i < SSLOTS; ++i)
-                if (i != in) w[i] = fmaf(-errb, uc[i], w[i]);
-        }
-        if constexpr (j + 1 < QB) {
-#pragma unroll
-            for (int i = 0; i < SSLOTS; ++i) uc[i] = un[i];
-            idc = idn;
-        }
+        for (int i = ij; i < SSLOTS; ++i)
+            if (i != in) w[i] = fmaf(-errb, uc[i], w[i]);
+        idc = idn;
         // bound the scheduling regions (compile time) while still letting the
         // independent work of neighbouring steps overlap
         if constexpr ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
