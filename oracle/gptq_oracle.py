@@ -35,8 +35,9 @@ listing were lost in extraction; the readings used here are:
 * asymmetric grid [0, 2^b - 1] with S = (max - min) / (2^b - 1),
   Z = -round(min / S16); symmetric grid +-(2^(b-1) - 1) with S = absmax / (2^(b-1) - 1),
   Z = 0; S16 = fp16(S) is the scale used for quantizing and stored;
-* a code is decided in float32: q = clamp(rne(fl32(fl32(w) / S16) + Z)), as the
-  GPU does, so both sides round the same value; everything else is fp64;
+* a code is decided from the float32 quotient: q = clamp(rne(fl32(fl32(w) / S16)) + Z),
+  as the GPU does, so both sides round the same value; adding the integer Z is
+  exact (rne(t + Z) = rne(t) + Z); everything else is fp64;
 * stored codes are unsigned: u = q (asymmetric) or q + 2^(b-1) (symmetric), stored
   zero z = Z or 2^(b-1); dequantisation is fl32(S16) * fl32(u - z).
 """
@@ -168,14 +169,20 @@ def group_params(vals: np.ndarray, p: Params):
 
 
 def decide_codes(w: np.ndarray, S16: np.ndarray, Z: np.ndarray, p: Params) -> np.ndarray:
-    """q = clamp(round(w / S16 + Z)) on the signed (or unsigned) grid, decided in float32.
+    """q = clamp(round(w / S16 + Z)) on the signed (or unsigned) grid.
 
+    The quotient t = fl32(w / S16) is decided in float32; Z is an integer, so the
+    sum t + Z and its rounding are exact: round(t + Z) = round(t) + Z.
     [Quantization concepts guide, "Mapping values to fewer bits": quantize formula;
      the clamp keeps compensated values that left the group's range on the grid]
     """
     t = (_f32(w) / _f32(S16)).astype(np.float32)
-    u = (t + Z.astype(np.float32)).astype(np.float32)
-    return np.clip(np.rint(u), p.qmin, p.qmax).astype(np.int64)
+    return np.clip(np.rint(t.astype(np.float64)) + Z, p.qmin, p.qmax).astype(np.int64)
+
+
+def code_value(w: np.ndarray, S16: np.ndarray, Z: np.ndarray) -> np.ndarray:
+    """The pre-rounding code value fl32(w / S16) + Z (the sum exact, in fp64)."""
+    return (_f32(w) / _f32(S16)).astype(np.float32).astype(np.float64) + Z
 
 
 # ---------------------------------------------------------------------------
@@ -269,7 +276,7 @@ class Result:
     z_t: np.ndarray        # fl32(min) / S16, the value rounded to get Z (float32), d_row x n_groups
     what: np.ndarray       # dequantized weights S16 * (q - Z), fp64
     w_at_q: np.ndarray     # the value each weight had when it was quantized (fp64)
-    t_at_q: np.ndarray     # fl32(fl32(w) / S16) + Z, the pre-rounding code value (float32)
+    t_at_q: np.ndarray     # fl32(fl32(w) / S16) + Z, the pre-rounding code value (exact sum, fp64)
 
 
 def _n_groups(d_col: int, p: Params) -> int:
@@ -302,14 +309,14 @@ def gptq(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
     ZT = np.zeros((d_row, ng), dtype=np.float32)
-    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for c in range(d_col):
         k = c // g
         if c % g == 0:
             S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(W[:, c:c + g], p)
         w = W[:, c].copy()
         w_at_q[:, c] = w
-        t_at_q[:, c] = ((_f32(w) / _f32(S16[:, k])).astype(np.float32) + Z[:, k].astype(np.float32)).astype(np.float32)
+        t_at_q[:, c] = code_value(w, S16[:, k], Z[:, k])
         q = decide_codes(w, S16[:, k], Z[:, k], p)
         Q[:, c] = q
         what[:, c] = S16[:, k] * (q - Z[:, k])
@@ -340,7 +347,7 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
     ZT = np.zeros((d_row, ng), dtype=np.float32)
-    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for b0 in range(0, d_col, B):
         b1 = min(b0 + B, d_col)
         Wb = W[:, b0:b1].copy()
@@ -353,7 +360,7 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
                 S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(src, p)
             w = Wb[:, j].copy()
             w_at_q[:, c] = w
-            t_at_q[:, c] = ((_f32(w) / _f32(S16[:, k])).astype(np.float32) + Z[:, k].astype(np.float32)).astype(np.float32)
+            t_at_q[:, c] = code_value(w, S16[:, k], Z[:, k])
             q = decide_codes(w, S16[:, k], Z[:, k], p)
             Q[:, c] = q
             what[:, c] = S16[:, k] * (q - Z[:, k])
@@ -382,7 +389,7 @@ def gptq_obs(W: np.ndarray, Hd: np.ndarray, p: Params) -> Result:
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
     ZT = np.zeros((d_row, ng), dtype=np.float32)
-    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for c in range(d_col):
         k = c // g
         if c % g == 0:
@@ -409,7 +416,7 @@ def rtn(W: np.ndarray, p: Params) -> Result:
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
     ZT = np.zeros((d_row, ng), dtype=np.float32)
-    what = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float32)
+    what = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for k in range(ng):
         c0, c1 = k * g, min((k + 1) * g, d_col)
         S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(W[:, c0:c1], p)

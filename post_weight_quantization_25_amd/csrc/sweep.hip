@@ -73,11 +73,38 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     const float fqmin = (float)a.qmin, fqmax = (float)a.qmax, fzoff = (float)a.zoff;
     if (tid == 0) bad_any = 0;
 
-    for (int idx = tid; idx < QB * QB; idx += QT) {
-        const int j = idx >> 7, c = idx & 127;
-        const float u = (j < nb && c < nb) ? a.U[(a.b0 + j) * a.d_col + a.b0 + c] : 0.f;
-        Up[j][c & (SL - 1)][c >> 4] = u;
-        if (c == j) invd[j] = (j < nb) ? 1.0f / u : 0.f;
+    // stage U's diagonal block: all loads of a thread first (16-byte loads when rows
+    // are 16-byte aligned), then the permuted LDS stores
+    constexpr int NV = QB * QB / 4 / QT;   // float4 per thread
+    f32x4_t uv[NV];
+    const bool vec = nb == QB && ((a.d_col & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.U) & 15) == 0);
+    if (vec) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + QT * v;       // float4 index: 32 per row of 128
+            const int j = idx >> 5, c4 = (idx & 31) * 4;
+            uv[v] = *reinterpret_cast<const f32x4_t*>(a.U + (a.b0 + j) * a.d_col + a.b0 + c4);
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + QT * v;
+            const int j = idx >> 5, c4 = (idx & 31) * 4;
+            const float* src = a.U + (a.b0 + j) * a.d_col + a.b0 + c4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uv[v][e] = (j < nb && c4 + e < nb) ? src[e] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int idx = tid + QT * v;
+        const int j = idx >> 5, c4 = (idx & 31) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = c4 + e;
+            Up[j][c & (SL - 1)][c >> 4] = uv[v][e];
+            if (c == j) invd[j] = (j < nb) ? 1.0f / uv[v][e] : 0.f;
+        }
     }
     float w[SSLOTS], e[SSLOTS];
     int cv[SSLOTS];
@@ -89,6 +116,8 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         e[i] = 0.f;
         cv[i] = 0;
     }
+    // s16f, r16f = 1 / s16f and the zero point zf of the current group; the code is
+    // rne(t) + zf clamped to [qmin, qmax], i.e. rne(t) clamped to [lo, hi]
     float s16f = 1.f, r16f = 1.f, zf = 0.f;
     bool bad = false;
     if (G == 0 && rv) {
@@ -96,6 +125,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         r16f = 1.0f / s16f;
         zf = f16_bits_to_f32(a.zeros[row * a.n_groups]) - fzoff;
     }
+    float lo = fqmin - zf, hi = fqmax - zf;
     __syncthreads();
     // U coefficients of the current and the next step, alternating by step parity
     float ucA[SSLOTS], ucB[SSLOTS];
@@ -138,6 +168,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
             }
             idn = invd[j + 1];
         }
+        __builtin_amdgcn_sched_barrier(0);   // issue the prefetch at the top of the step
         // a group starts at a multiple of its size (32, 64 or 128), so only every 32nd
         // step carries the group code
         if constexpr ((j & 31) == 0) {
@@ -166,6 +197,8 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                 if (!normal_f16_scale(s16f)) { bad = true; s16f = 1.f; }
                 r16f = 1.0f / s16f;
                 zf = a.sym ? 0.f : fqmin - rintf(mn / s16f);
+                lo = fqmin - zf;
+                hi = fqmax - zf;
                 if (q == 0 && rv && a.b0 + j < a.d_col) {
                     const int64_t g = (a.b0 + j) / G;
                     a.scales[row * a.n_groups + g] = f32_to_f16_bits(s16f);
@@ -175,18 +208,17 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         }
         // quantize column j (owner: lane qj of the row, slot ij).  t = w / S16 correctly
         // rounded: q0 = w r with r = 1 / S16 correctly rounded, then one correction with
-        // the exact residual w - q0 S16 (Markstein); equal to the IEEE quotient
+        // the exact residual w - q0 S16 (Markstein); equal to the IEEE quotient.  The code
+        // is rne(t) + zf clamped to the grid (zf is an integer, so this is exact).
         const float wv = w[ij];
         const float q0 = wv * r16f;
         const float t = fmaf(fmaf(-q0, s16f, wv), r16f, q0);
-        const float qv = fminf(fmaxf(rintf(t + zf), fqmin), fqmax);
-        const float wq = s16f * (qv - zf);
-        const float err = (wv - wq) * idc;
+        const float qd = __builtin_amdgcn_fmed3f(rintf(t), lo, hi);
+        const float err = fmaf(-s16f, qd, wv) * idc;
         const float errb = row_bcast<qj>(err);
         const bool own = (q == qj);
         e[ij] = own ? err : e[ij];
-        cv[ij] = own ? (int)qv + a.zoff : cv[ij];
-        bad = bad || (own && !(fabsf(err) <= 3.0e38f));
+        cv[ij] = own ? (int)(qd + zf) + a.zoff : cv[ij];
         // compensate the later columns; U is upper triangular, so in slot ij the lanes
         // holding columns <= j get a zero coefficient (or touch a finished column).
         // The slot of the next column first: it is on the critical path.
@@ -196,11 +228,11 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         for (int i = ij; i < SSLOTS; ++i)
             if (i != in) w[i] = fmaf(-errb, uc[i], w[i]);
         idc = idn;
-        // bound the scheduling regions (compile time) while still letting the
-        // independent work of neighbouring steps overlap
-        if constexpr ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     });
 
+    // a non-finite weight, scale or error shows up in the block's errors
+#pragma unroll
+    for (int i = 0; i < SSLOTS; ++i) bad = bad || !(fabsf(e[i]) <= 3.0e38f);
     if (rv) {
         float* erow = a.E + row * a.lde;
 #pragma unroll
