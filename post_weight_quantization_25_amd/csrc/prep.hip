@@ -266,12 +266,20 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
 
 // Load the lower part of diagonal block k (identity padding past n) into a[].
 GPTQ_DEV void diag_load(double* a, const double* A, int64_t d, int64_t k0, int n) {
-    for (int idx = threadIdx.x; idx < PNB * PNB; idx += 256) {
+    constexpr int NV = PNB * PNB / 256;
+    double v[NV];
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {            // all loads first
+        const int idx = threadIdx.x + 256 * t;
         const int i = idx >> 6, k = idx & 63;
-        double v = 0.0;
-        if (i < n && k <= i) v = A[(k0 + i) * d + k0 + k];
-        else if (i == k) v = 1.0;
-        a[i * DLD + k] = v;
+        // unconditional load from a clamped (in-bounds) address, then the selection
+        const double x = A[(k0 + (i < n ? i : n - 1)) * d + k0 + (k < n ? k : n - 1)];
+        v[t] = (i < n && k <= i) ? x : ((i == k) ? 1.0 : 0.0);
+    }
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+        const int idx = threadIdx.x + 256 * t;
+        a[(idx >> 6) * DLD + (idx & 63)] = v[t];
     }
 }
 
@@ -295,13 +303,22 @@ __global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double
     const int64_t r0 = k0 + PNB + (int64_t)blockIdx.x * 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    for (int idx = tid; idx < 64 * PNB / 2; idx += 256) {
+    // all loads of a thread first, then the LDS stores
+    constexpr int PV = 64 * PNB / 2 / 256;      // double2 per thread and operand
+    double2 va[PV], vx[PV];
+#pragma unroll
+    for (int v = 0; v < PV; ++v) {
+        const int idx = tid + 256 * v;
         const int i = idx / (PNB / 2), k = 2 * (idx % (PNB / 2));
-        double2 va = double2{0.0, 0.0};
-        if (r0 + i < d) va = *reinterpret_cast<const double2*>(A + (r0 + i) * d + k0 + k);
-        const double2 vx = *reinterpret_cast<const double2*>(X + (k0 + i) * d + k0 + k);
-        As[i * DLD + k] = va.x; As[i * DLD + k + 1] = va.y;
-        Xs[i * DLD + k] = vx.x; Xs[i * DLD + k + 1] = vx.y;
+        va[v] = (r0 + i < d) ? *reinterpret_cast<const double2*>(A + (r0 + i) * d + k0 + k) : double2{0.0, 0.0};
+        vx[v] = *reinterpret_cast<const double2*>(X + (k0 + i) * d + k0 + k);
+    }
+#pragma unroll
+    for (int v = 0; v < PV; ++v) {
+        const int idx = tid + 256 * v;
+        const int i = idx / (PNB / 2), k = 2 * (idx % (PNB / 2));
+        As[i * DLD + k] = va[v].x; As[i * DLD + k + 1] = va[v].y;
+        Xs[i * DLD + k] = vx[v].x; Xs[i * DLD + k + 1] = vx[v].y;
     }
     __syncthreads();
     f64x4_t acc[2][2];

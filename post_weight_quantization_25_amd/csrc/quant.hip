@@ -117,9 +117,20 @@ GPTQ_DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
 // Per thread and chunk: 4 x float4 of E (row m = tid / 2, k = 16 (tid & 1) .. +15) and
 // 4 x float4 of U (row k = tid / 8, n = 16 (tid & 7) .. +15).
 GPTQ_DEV void trail_load(const TrailArgs& a, int64_t m0, int64_t n0, int kc, int tid, f32x4_t (&re)[4],
-                         f32x4_t (&ru)[4]) {
+                         f32x4_t (&ru)[4], bool full) {
     const int me = tid >> 1, ke = (tid & 1) * 16;
     const int64_t gm = m0 + me;
+    const int ku = tid >> 3, nu = (tid & 7) * 16;
+    if (full) {
+        // whole chunk in bounds, rows 16-byte aligned: unconditional 16-byte loads
+        const float* se = a.E + gm * a.lde + kc + ke;
+        const float* su = a.U + (a.k0 + kc + ku) * a.d_col + n0 + nu;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) re[v] = *reinterpret_cast<const f32x4_t*>(se + 4 * v);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ru[v] = *reinterpret_cast<const f32x4_t*>(su + 4 * v);
+        return;
+    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int k = kc + ke + 4 * v;
@@ -131,7 +142,6 @@ GPTQ_DEV void trail_load(const TrailArgs& a, int64_t m0, int64_t n0, int kc, int
         }
         re[v] = x;
     }
-    const int ku = tid >> 3, nu = (tid & 7) * 16;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int64_t gn = n0 + nu + 4 * v;
@@ -220,15 +230,19 @@ __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
     const int nch = (a.K + TK - 1) / TK;
+    // fast loads: the tile inside W, whole chunks of k, 16-byte aligned rows
+    const bool fl = (m0 + TB <= a.d_row) && (n0 + TB <= a.n_end) && (a.K % TK == 0) && ((a.lde & 3) == 0) &&
+                    ((a.d_col & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.E) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.U + a.k0 * a.d_col + n0) & 15) == 0);
     f32x4_t re[4], ru[4];
-    trail_load(a, m0, n0, 0, tid, re, ru);
+    trail_load(a, m0, n0, 0, tid, re, ru, fl);
     trail_store(stg[0], tid, re, ru);
-    if (nch > 1) trail_load(a, m0, n0, TK, tid, re, ru);
+    if (nch > 1) trail_load(a, m0, n0, TK, tid, re, ru, fl);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         trail_mfma(stg[c & 1], wr, wc, lane, acc);
         if (c + 1 < nch) trail_store(stg[(c + 1) & 1], tid, re, ru);
-        if (c + 2 < nch) trail_load(a, m0, n0, (c + 2) * TK, tid, re, ru);
+        if (c + 2 < nch) trail_load(a, m0, n0, (c + 2) * TK, tid, re, ru, fl);
         __syncthreads();
     }
     // W -= acc: all loads first, then all stores (a load after a store to the same
