@@ -370,6 +370,7 @@ struct GemmD {
     // k1 + n1 of the factored matrix fA, inverse blocks in fX); its workgroup
     // factors it after the update instead of storing it
     double* fA; double* fX; int64_t fd, k1; int n1; int32_t* info;
+    int ntm, ntn;   // tiles along M (of a full batch entry) and N
 };
 
 // Operand chunk of GD_BK columns of k: 64 rows (m or n) x 32 k, as 4 double2 per thread.
@@ -438,9 +439,28 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
         if (g.flags & G_TRI_A) g.K = g.M_last;
         g.M = g.M_last;
     }
-    const int mi = blockIdx.y, nj = blockIdx.x;
+    // tile order of the 1-D grid: longest k ranges first where they differ (a lower-
+    // triangular operand), so the long tiles do not finish last; only the lower tiles
+    // of a lower-triangular C are enumerated
+    const int bid = blockIdx.x;
+    int mi, nj;
+    if (g.flags & G_LOWER_C) {
+        mi = (int)((sqrtf(8.f * bid + 1.f) - 1.f) * 0.5f);
+        while ((mi + 1) * (mi + 2) / 2 <= bid) ++mi;
+        while (mi * (mi + 1) / 2 > bid) --mi;
+        nj = bid - mi * (mi + 1) / 2;
+    } else if (g.flags & G_TRI_B) {          // k >= n0 (B lower) or k < n0 + 64 (B^T lower)
+        const int q = bid / g.ntm;
+        nj = (g.flags & G_BT) ? g.ntn - 1 - q : q;
+        mi = bid % g.ntm;
+    } else if (g.flags & G_TRI_A) {          // k < m0 + 64
+        mi = g.ntm - 1 - bid / g.ntn;
+        nj = bid % g.ntn;
+    } else {
+        mi = bid / g.ntn;
+        nj = bid % g.ntn;
+    }
     const int m0 = mi * GD_BM, n0 = nj * GD_BM;
-    if ((g.flags & G_LOWER_C) && n0 > m0 + GD_BM - 1) return;
     const bool diag0 = (g.flags & G_DIAG0) && mi == 0 && nj == 0 && bz == 0;
     if (m0 >= g.M) return;
     int kb = 0, ke = g.K;
@@ -571,9 +591,11 @@ static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int
                         int nbatch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, int M_last = 0,
                         int64_t k1 = 0, int n1 = 0) {
     if (M <= 0 || N <= 0 || nbatch <= 0) return GPTQ_OK;
+    const int ntm = (M + GD_BM - 1) / GD_BM, ntn = (N + GD_BM - 1) / GD_BM;
     GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch,
-            c.A, c.X, c.d, k1, n1, c.info};
-    dim3 grid((N + GD_BM - 1) / GD_BM, (M + GD_BM - 1) / GD_BM, nbatch);
+            c.A, c.X, c.d, k1, n1, c.info, ntm, ntn};
+    const int ntiles = (flags & G_LOWER_C) ? ntm * (ntm + 1) / 2 : ntm * ntn;
+    dim3 grid((unsigned)ntiles, 1, nbatch);
     if (flags & G_BT) gemm_f64_kernel<false><<<grid, 256, 0, c.s>>>(g);
     else gemm_f64_kernel<true><<<grid, 256, 0, c.s>>>(g);
     GPTQ_LAUNCH_CHECK();
