@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <utility>
 
 #include "gptq.h"
 
@@ -59,6 +60,15 @@ GPTQ_DEV int quad_perm_i(int v) {
 // quad_perm encodings: lane i of the quad reads lane sel[i].
 constexpr int QP_XOR1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // [1,0,3,2]
 constexpr int QP_XOR2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // [2,3,0,1]
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. N-1.
+template <int I, int N, typename F>
+GPTQ_DEV void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 // Launch-error helper for the host side.
 #define GPTQ_LAUNCH_CHECK()                                   \

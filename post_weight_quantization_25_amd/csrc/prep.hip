@@ -100,7 +100,11 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int& fail_s = *fail_p;
 
-    for (int c0 = 0; c0 < PNB; c0 += 8) {
+    // eight rounds of 8 columns, unrolled (compile-time addresses and tile lists); a
+    // failed pivot skips the remaining rounds
+    static_for<0, PNB / 8>([&](auto P) {
+        constexpr int c0 = decltype(P)::value * 8;
+        if (fail_s) return;
         if (wave == 0) {
             // Cholesky of the 8 x 8 top block, in every lane
             double t[8][8];
@@ -126,61 +130,58 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
                     t[i][k] = v * rd[k];
                 }
             }
-            // this lane's row of the sub-panel
+            // every lane at or below the sub-panel solves its row; for a row of the top
+            // block this reproduces that row of the factor bit for bit (same operands,
+            // same order), and the entries right of its diagonal are never read
             const int r = lane;
-            if (r >= c0 + 8) {
-                double x[8];
+            double x[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    double v = a[r * DLD + c0 + k];
+            for (int k = 0; k < 8; ++k) {
+                double v = a[r * DLD + c0 + k];
 #pragma unroll
-                    for (int m = 0; m < k; ++m) v -= t[k][m] * x[m];
-                    x[k] = v * rd[k];
-                }
+                for (int m = 0; m < k; ++m) v -= t[k][m] * x[m];
+                x[k] = v * rd[k];
+            }
+            if (r >= c0) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) a[r * DLD + c0 + k] = x[k];
-            } else if (r >= c0) {
-                const int i = r - c0;
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii)
-                    if (ii == i) {
-#pragma unroll
-                        for (int k = 0; k <= ii; ++k) a[r * DLD + c0 + k] = t[ii][k];
-                    }
             }
             if (lane == 0 && f) fail_s = f;
         }
         __syncthreads();
-        if (fail_s) break;
+        if (fail_s) return;
         // rank-8 update of the lower part of rows / columns >= c1 = c0 + 8, in 16 x 16 tiles
-        const int c1 = c0 + 8;
-        if (c1 < PNB) {
-            const int t0 = c1 >> 4;
-            const int nt = 4 - t0;                         // tiles per dimension still active
-            const int ntiles = nt * (nt + 1) / 2;
-            for (int tt = wave; tt < ntiles; tt += 4) {
-                int tr = 0, rem = tt;
-                while (rem > tr) { rem -= tr + 1; ++tr; }
-                const int tc = rem;                        // tc <= tr within the active tiles
-                const int R0 = (t0 + tr) * 16, C0 = (t0 + tc) * 16;
-                f64x4_t acc;
+        constexpr int c1 = c0 + 8;
+        if constexpr (c1 < PNB) {
+            constexpr int t0 = c1 >> 4;
+            constexpr int nt = 4 - t0;                     // tiles per dimension still active
+            constexpr int ntiles = nt * (nt + 1) / 2;
+            static_for<0, (ntiles + 3) / 4>([&](auto R) {
+                const int tt = wave + 4 * decltype(R)::value;
+                if (tt < ntiles) {
+                    int tr = 0, rem = tt;
+                    while (rem > tr) { rem -= tr + 1; ++tr; }
+                    const int tc = rem;                    // tc <= tr within the active tiles
+                    const int R0 = (t0 + tr) * 16, C0 = (t0 + tc) * 16;
+                    f64x4_t acc;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = a[(R0 + 4 * e + (lane >> 4)) * DLD + C0 + (lane & 15)];
+                    for (int e = 0; e < 4; ++e) acc[e] = a[(R0 + 4 * e + (lane >> 4)) * DLD + C0 + (lane & 15)];
 #pragma unroll
-                for (int kk = 0; kk < 8; kk += 4) {
-                    const double fa = -a[(R0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
-                    const double fb = a[(C0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
-                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
+                    for (int kk = 0; kk < 8; kk += 4) {
+                        const double fa = -a[(R0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
+                        const double fb = a[(C0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
+                        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rr = R0 + 4 * e + (lane >> 4), cc = C0 + (lane & 15);
+                        if (rr >= c1 && cc >= c1) a[rr * DLD + cc] = acc[e];
+                    }
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int rr = R0 + 4 * e + (lane >> 4), cc = C0 + (lane & 15);
-                    if (rr >= c1 && cc >= c1) a[rr * DLD + cc] = acc[e];
-                }
-            }
+            });
         }
         __syncthreads();
-    }
+    });
     if (fail_s) {
         if (tid == 0 && fail_s <= n && *info == 0) *info = (int32_t)(k0 + fail_s);
         return;

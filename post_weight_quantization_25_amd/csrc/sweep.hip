@@ -23,14 +23,6 @@
 
 namespace gptq {
 
-template <int I, int N, typename F>
-GPTQ_DEV void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
 constexpr int SSLOTS = QB / SL;     // columns per lane: q, q+16, ..., q+112
 
 GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 65504.f; }
