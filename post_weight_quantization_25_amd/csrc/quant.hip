@@ -99,8 +99,9 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 struct TrailArgs {
     float* Wws; int64_t d_row, d_col;
-    const float* E; int64_t lde;     // E block: d_row x K, row stride lde
-    const float* U; int64_t k0; int K;
+    const uint16_t* Ehi; const uint16_t* Elo; int64_t lde;   // E block (bf16 hi + lo): d_row x K
+    const uint16_t* Uhi; const uint16_t* Ulo;                // U (bf16 hi + lo), d_col x d_col
+    int64_t k0; int K;
     int64_t n_beg, n_end;
 };
 
@@ -109,75 +110,56 @@ struct TrailStage {
     uint16_t uhi[TK * TU_RS], ulo[TK * TU_RS];
 };
 
-GPTQ_DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
-    hi = f32_to_bf16_bits(x);
-    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+// Per thread and chunk: E rows m = tid / 2, k = 16 (tid & 1) .. +15 and U rows
+// k = tid / 8, n = 16 (tid & 7) .. +15, each as hi and lo: 8 x 16 bytes.
+struct TrailRegs { u32x4_t e[2][2], u[2][2]; };   // [hi/lo][first/second 8 values]
+
+GPTQ_DEV u32x4_t ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+GPTQ_DEV u32x4_t ld8_edge(const uint16_t* p, int valid) {   // 8 bf16, zero past `valid`
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int e = 0; e < 8; ++e)
+        if (e < valid) w[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+    return u32x4_t{w[0], w[1], w[2], w[3]};
 }
 
-// Per thread and chunk: 4 x float4 of E (row m = tid / 2, k = 16 (tid & 1) .. +15) and
-// 4 x float4 of U (row k = tid / 8, n = 16 (tid & 7) .. +15).
-GPTQ_DEV void trail_load(const TrailArgs& a, int64_t m0, int64_t n0, int kc, int tid, f32x4_t (&re)[4],
-                         f32x4_t (&ru)[4], bool full) {
+GPTQ_DEV void trail_load(const TrailArgs& a, int64_t m0, int64_t n0, int kc, int tid, TrailRegs& r, bool full) {
     const int me = tid >> 1, ke = (tid & 1) * 16;
-    const int64_t gm = m0 + me;
     const int ku = tid >> 3, nu = (tid & 7) * 16;
+    const int64_t gm = m0 + me;
+    const int64_t eo = gm * a.lde + kc + ke;
+    const int64_t uo = (a.k0 + kc + ku) * a.d_col + n0 + nu;
     if (full) {
-        // whole chunk in bounds, rows 16-byte aligned: unconditional 16-byte loads
-        const float* se = a.E + gm * a.lde + kc + ke;
-        const float* su = a.U + (a.k0 + kc + ku) * a.d_col + n0 + nu;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) re[v] = *reinterpret_cast<const f32x4_t*>(se + 4 * v);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) ru[v] = *reinterpret_cast<const f32x4_t*>(su + 4 * v);
+        for (int h = 0; h < 2; ++h) {
+            r.e[0][h] = ld16(a.Ehi + eo + 8 * h);
+            r.e[1][h] = ld16(a.Elo + eo + 8 * h);
+            r.u[0][h] = ld16(a.Uhi + uo + 8 * h);
+            r.u[1][h] = ld16(a.Ulo + uo + 8 * h);
+        }
         return;
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int k = kc + ke + 4 * v;
-        f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (gm < a.d_row) {
-            const float* src = a.E + gm * a.lde + k;
-            if (k + 4 <= a.K) x = *reinterpret_cast<const f32x4_t*>(src);
-            else for (int e = 0; e < 4; ++e) x[e] = (k + e < a.K) ? src[e] : 0.f;
-        }
-        re[v] = x;
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int64_t gn = n0 + nu + 4 * v;
-        f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kc + ku < a.K) {
-            const float* src = a.U + (a.k0 + kc + ku) * a.d_col + gn;
-            if (gn + 4 <= a.n_end && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) x = *reinterpret_cast<const f32x4_t*>(src);
-            else for (int e = 0; e < 4; ++e) x[e] = (gn + e < a.n_end) ? src[e] : 0.f;
-        }
-        ru[v] = x;
+    for (int h = 0; h < 2; ++h) {
+        const int ve = (gm < a.d_row) ? a.K - (kc + ke + 8 * h) : 0;
+        const int vu = (kc + ku < a.K) ? (int)(a.n_end - (n0 + nu + 8 * h)) : 0;
+        r.e[0][h] = ld8_edge(a.Ehi + eo + 8 * h, ve);
+        r.e[1][h] = ld8_edge(a.Elo + eo + 8 * h, ve);
+        r.u[0][h] = ld8_edge(a.Uhi + uo + 8 * h, vu);
+        r.u[1][h] = ld8_edge(a.Ulo + uo + 8 * h, vu);
     }
 }
 
-// Split 8 fp32 values into hi and lo bf16 and write both 16-byte groups.
-GPTQ_DEV void store_split8(uint16_t* hi_dst, uint16_t* lo_dst, const f32x4_t& x0, const f32x4_t& x1) {
-    u32x4_t H, L;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const f32x4_t& x = (e < 2) ? x0 : x1;
-        uint16_t h0, l0, h1, l1;
-        split_bf16(x[(2 * e) & 3], h0, l0);
-        split_bf16(x[(2 * e + 1) & 3], h1, l1);
-        H[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        L[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-    *reinterpret_cast<u32x4_t*>(hi_dst) = H;
-    *reinterpret_cast<u32x4_t*>(lo_dst) = L;
-}
-
-GPTQ_DEV void trail_store(TrailStage& st, int tid, const f32x4_t (&re)[4], const f32x4_t (&ru)[4]) {
+GPTQ_DEV void trail_store(TrailStage& st, int tid, const TrailRegs& r) {
     const int me = tid >> 1, ke = (tid & 1) * 16;
-    store_split8(&st.ehi[me * TE_LD + ke], &st.elo[me * TE_LD + ke], re[0], re[1]);
-    store_split8(&st.ehi[me * TE_LD + ke + 8], &st.elo[me * TE_LD + ke + 8], re[2], re[3]);
     const int ku = tid >> 3, nu = (tid & 7) * 16;
-    store_split8(&st.uhi[ku * TU_RS + nu], &st.ulo[ku * TU_RS + nu], ru[0], ru[1]);
-    store_split8(&st.uhi[ku * TU_RS + nu + 8], &st.ulo[ku * TU_RS + nu + 8], ru[2], ru[3]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        *reinterpret_cast<u32x4_t*>(&st.ehi[me * TE_LD + ke + 8 * h]) = r.e[0][h];
+        *reinterpret_cast<u32x4_t*>(&st.elo[me * TE_LD + ke + 8 * h]) = r.e[1][h];
+        *reinterpret_cast<u32x4_t*>(&st.uhi[ku * TU_RS + nu + 8 * h]) = r.u[0][h];
+        *reinterpret_cast<u32x4_t*>(&st.ulo[ku * TU_RS + nu + 8 * h]) = r.u[1][h];
+    }
 }
 
 // B operand (32 columns n x 16 k) from the [k][n] tile with two transposed reads:
@@ -231,18 +213,20 @@ __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
     const int nch = (a.K + TK - 1) / TK;
     // fast loads: the tile inside W, whole chunks of k, 16-byte aligned rows
-    const bool fl = (m0 + TB <= a.d_row) && (n0 + TB <= a.n_end) && (a.K % TK == 0) && ((a.lde & 3) == 0) &&
-                    ((a.d_col & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.E) & 15) == 0) &&
-                    ((reinterpret_cast<uintptr_t>(a.U + a.k0 * a.d_col + n0) & 15) == 0);
-    f32x4_t re[4], ru[4];
-    trail_load(a, m0, n0, 0, tid, re, ru, fl);
-    trail_store(stg[0], tid, re, ru);
-    if (nch > 1) trail_load(a, m0, n0, TK, tid, re, ru, fl);
+    const bool fl = (m0 + TB <= a.d_row) && (n0 + TB <= a.n_end) && (a.K % TK == 0) && ((a.lde & 7) == 0) &&
+                    ((a.d_col & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.Ehi) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.Elo) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.Uhi + a.k0 * a.d_col + n0) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.Ulo + a.k0 * a.d_col + n0) & 15) == 0);
+    TrailRegs rg;
+    trail_load(a, m0, n0, 0, tid, rg, fl);
+    trail_store(stg[0], tid, rg);
+    if (nch > 1) trail_load(a, m0, n0, TK, tid, rg, fl);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         trail_mfma(stg[c & 1], wr, wc, lane, acc);
-        if (c + 1 < nch) trail_store(stg[(c + 1) & 1], tid, re, ru);
-        if (c + 2 < nch) trail_load(a, m0, n0, (c + 2) * TK, tid, re, ru, fl);
+        if (c + 1 < nch) trail_store(stg[(c + 1) & 1], tid, rg);
+        if (c + 2 < nch) trail_load(a, m0, n0, (c + 2) * TK, tid, rg, fl);
         __syncthreads();
     }
     // W -= acc: all loads first, then all stores (a load after a store to the same
@@ -294,9 +278,23 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // updates is exact in exact arithmetic, as for the 128-column lazy blocks.
 constexpr int QSB = 512;
 
+// Workspace: fp32 working copy of W | E hi | E lo (bf16, d_row x QSB) | U hi | U lo
+// (bf16, d_col x d_col).
 size_t quant_ws_bytes(int64_t d_row, int64_t d_col) {
     if (d_row <= 0 || d_col <= 0) return 0;
-    return align256((size_t)d_row * d_col * sizeof(float)) + align256((size_t)d_row * QSB * sizeof(float));
+    return align256((size_t)d_row * d_col * sizeof(float)) + 2 * align256((size_t)d_row * QSB * 2) +
+           2 * align256((size_t)d_col * d_col * 2);
+}
+
+// U -> bf16 hi + lo (hi = bf16(u), lo = bf16(u - hi)), once per call: every workgroup
+// of the trailing products reads the split instead of forming it again.
+__global__ void split_u_kernel(const float* U, int64_t n, uint16_t* hi, uint16_t* lo) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const float u = U[i];
+        const uint16_t h = f32_to_bf16_bits(u);
+        hi[i] = h;
+        lo[i] = f32_to_bf16_bits(u - bf16_bits_to_f32(h));
+    }
 }
 
 static gptq_status launch_row_params(int bits, bool sym, const float* Wws, int64_t d_row, int64_t d_col,
@@ -317,7 +315,14 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
                          void* ws, size_t ws_bytes, int32_t* info, hipStream_t s) {
     if (ws == nullptr || ws_bytes < quant_ws_bytes(d_row, d_col)) return GPTQ_ERR_WORKSPACE;
     float* Wws = reinterpret_cast<float*>(ws);
-    float* E = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)d_row * d_col * sizeof(float)));
+    char* wp = reinterpret_cast<char*>(ws) + align256((size_t)d_row * d_col * sizeof(float));
+    uint16_t* Ehi = reinterpret_cast<uint16_t*>(wp);
+    wp += align256((size_t)d_row * QSB * 2);
+    uint16_t* Elo = reinterpret_cast<uint16_t*>(wp);
+    wp += align256((size_t)d_row * QSB * 2);
+    uint16_t* Uhi = reinterpret_cast<uint16_t*>(wp);
+    wp += align256((size_t)d_col * d_col * 2);
+    uint16_t* Ulo = reinterpret_cast<uint16_t*>(wp);
     const int G = p.group_size;
     const int n_groups = (G == 0) ? 1 : (int)(d_col / G);
 
@@ -338,7 +343,13 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         if (st != GPTQ_OK) return st;
     }
     SweepArgs sa;
-    sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U; sa.E = E;
+    {
+        const int64_t nu = d_col * d_col;
+        const unsigned ug = (unsigned)std::min<int64_t>((nu + 255) / 256, 8192);
+        split_u_kernel<<<ug, 256, 0, s>>>(U, nu, Uhi, Ulo);
+        GPTQ_LAUNCH_CHECK();
+    }
+    sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U;
     sa.codes = codes; sa.code_ld = (p.bits <= 4) ? d_col / 2 : d_col;
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
     sa.group = G; sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
@@ -349,15 +360,15 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         const int64_t s1 = std::min<int64_t>(s0 + QSB, d_col);
         for (int64_t b0 = s0; b0 < s1; b0 += QB) {
             const int nb = (int)std::min<int64_t>(QB, s1 - b0);
-            sa.b0 = b0; sa.nb = nb; sa.E = E + (b0 - s0); sa.lde = QSB;
+            sa.b0 = b0; sa.nb = nb; sa.Ehi = Ehi + (b0 - s0); sa.Elo = Elo + (b0 - s0); sa.lde = QSB;
             st = sweep_launch(sa, s);
             if (st != GPTQ_OK) return st;
             // within the super-block
-            TrailArgs ta{Wws, d_row, d_col, E + (b0 - s0), QSB, U, b0, nb, b0 + nb, s1};
+            TrailArgs ta{Wws, d_row, d_col, Ehi + (b0 - s0), Elo + (b0 - s0), QSB, Uhi, Ulo, b0, nb, b0 + nb, s1};
             if ((st = trail(ta, s)) != GPTQ_OK) return st;
         }
         // everything after the super-block, K = s1 - s0
-        TrailArgs tb{Wws, d_row, d_col, E, QSB, U, s0, (int)(s1 - s0), s1, d_col};
+        TrailArgs tb{Wws, d_row, d_col, Ehi, Elo, QSB, Uhi, Ulo, s0, (int)(s1 - s0), s1, d_col};
         if ((st = trail(tb, s)) != GPTQ_OK) return st;
     }
     return GPTQ_OK;

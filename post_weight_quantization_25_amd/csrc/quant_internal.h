@@ -13,7 +13,8 @@ struct SweepArgs {
     const float* Wws; int64_t d_row, d_col;
     const float* U;
     int64_t b0; int nb;
-    float* E; int64_t lde;          // error block of this block: d_row x 128, row stride lde
+    uint16_t* Ehi; uint16_t* Elo;   // error block of this block as bf16 hi + lo (hi = bf16(e),
+    int64_t lde;                    // lo = bf16(e - hi)): d_row x 128, row stride lde
     uint8_t* codes; int64_t code_ld;
     uint16_t* scales; uint16_t* zeros; int n_groups;
     int32_t* info;

@@ -226,11 +226,16 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) bad = bad || !(fabsf(e[i]) <= 3.0e38f);
     if (rv) {
-        float* erow = a.E + row * a.lde;
+        uint16_t* hrow = a.Ehi + row * a.lde;
+        uint16_t* lrow = a.Elo + row * a.lde;
 #pragma unroll
         for (int i = 0; i < SSLOTS; ++i) {
             const int c = SL * i + q;
-            if (c < nb) erow[c] = e[i];
+            // the trailing update multiplies on bf16 MFMA with a three-term split:
+            // store the split here once instead of in every workgroup of the product
+            const uint16_t h = f32_to_bf16_bits(e[i]);
+            const uint16_t l = f32_to_bf16_bits(e[i] - bf16_bits_to_f32(h));
+            if (c < nb) { hrow[c] = h; lrow[c] = l; }
         }
     }
 #pragma unroll
