@@ -58,7 +58,13 @@ __host__ __device__ inline void upper_tile(int idx, int nt, int& ti, int& tj) {
 constexpr int HB_BM = 256;           // tile edge (channels)
 constexpr int HB_BK = 32;            // tokens per LDS stage
 constexpr int HB_NSTG = 4;           // LDS ring depth (stages in flight: 3 loading, 1 computing)
-constexpr int HB_THREADS = 512;      // 8 waves: wave (wr, wc) owns rows wr*64.., columns wc*128..
+constexpr int HB_WAVES = 8;          // waves per workgroup, two per SIMD
+constexpr int HB_WN = 128;           // columns per wave
+constexpr int HB_WM = HB_BM * (HB_BM / HB_WN) / HB_WAVES;   // rows per wave (waves: rows x 2 columns)
+constexpr int HB_THREADS = 64 * HB_WAVES;
+constexpr int HB_FA = HB_WM / 32;    // 32 x 32 MFMA tiles per wave: HB_FA x HB_FB
+constexpr int HB_FB = HB_WN / 32;
+constexpr int HB_DMA = 32 / HB_WAVES;  // 1 KB direct-to-LDS loads per wave and stage
 constexpr int HB_OPE = HB_BK * HB_BM;  // bf16 elements of one operand stage (16 KB)
 constexpr int HB_STE = 2 * HB_OPE;     // bf16 elements of one stage (A then B)
 
@@ -91,54 +97,68 @@ GPTQ_DEV int swz(int k, int c) {
 // array and inserts a full vmcnt(0) wait before it, which would leave no load in
 // flight; here the waits are explicit (the asm has no register results, the data
 // goes to LDS only).
-GPTQ_DEV void dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+// One direct global -> LDS load (global_load_lds_dwordx4, scalar-base form): lane i
+// reads 16 bytes at sbase + voff_i and they land at LDS byte address m0base + MOFF +
+// 16 i (M0 is formed in the asm from one wave-uniform register and a compile-time
+// offset, so no register per slot and load stays live).
+template <uint32_t MOFF>
+GPTQ_DEV void dma16(uint32_t voff, const void* sbase, uint32_t m0base) {
+    // the base and M0 are wave-uniform; readfirstlane makes that visible to the
+    // compiler, which must place them in scalar registers
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t mu = __builtin_amdgcn_readfirstlane(m0base);
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(bu), "s"(mu), "i"(MOFF) : "memory", "scc");
 }
 
 GPTQ_DEV uint32_t lds_addr(const uint16_t* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
 }
 
-// Per-wave constants of the stage copy.  Wave w issues loads 4w .. 4w+3 of 1 KB
-// each; load i (of the wave) covers operand w / 4 (0: the c0 channel block, 1: c1),
-// token rows kb + 2 i and kb + 2 i + 1 (kb = 8 (w % 4)), lane l writing chunk
-// position l % 32 of row kb + 2 i + l / 32, i.e. logical chunk swz(row, l % 32).  Only
-// two distinct per-lane byte offsets occur (the swizzle depends on the row mod 4).
+// Per-wave constants of the stage copy.  Wave w issues loads HB_DMA w .. HB_DMA w +
+// HB_DMA - 1 of 1 KB each; load i (of the wave) covers operand (HB_DMA w) / 16 (0: the
+// c0 channel block, 1: c1), token rows kb + 2 i and kb + 2 i + 1 (kb = 2 ((HB_DMA w) mod
+// 16)), lane l writing chunk position l % 32 of row kb + 2 i + l / 32, i.e. logical
+// chunk swz(row, l % 32).  The per-lane byte offset of load i carries its row.
 struct StageCopy {
-    uint32_t voff[2];      // per-lane byte offsets for even / odd i
-    int64_t row_elems;     // ldx
-    int cbase;             // channel base of this wave's operand (wave-uniform)
-    int wave_u;
+    uint32_t voff[HB_DMA];  // per-lane byte offsets of the wave's loads
+    int64_t row_elems;      // ldx
+    int cbase;              // channel base of this wave's operand (wave-uniform)
+    uint32_t m0base;        // LDS byte address of the wave's first block in slot 0
 };
 
-GPTQ_DEV StageCopy stage_copy_setup(const HessBf16Args& a, int c0, int c1, int wave, int lane) {
+GPTQ_DEV StageCopy stage_copy_setup(const HessBf16Args& a, const uint16_t* ring0, int c0, int c1, int wave,
+                                    int lane) {
     StageCopy sc;
-    sc.wave_u = __builtin_amdgcn_readfirstlane(wave);
-    sc.cbase = (sc.wave_u >> 2) ? c1 : c0;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    sc.cbase = ((wave_u * HB_DMA) >> 4) ? c1 : c0;
     sc.row_elems = a.ldx;
-    const int kb = (wave & 3) * 8 + (lane >> 5), pc = lane & 31;
+    sc.m0base = lds_addr(ring0) + (uint32_t)(wave_u * HB_DMA) * 1024u;
+    const int kb = ((wave * HB_DMA) & 15) * 2 + (lane >> 5), pc = lane & 31;
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-        sc.voff[par] = (uint32_t)(((int64_t)kb * a.ldx + 8 * swz(kb + 2 * par, pc)) * 2);
+    for (int i = 0; i < HB_DMA; ++i)
+        sc.voff[i] = (uint32_t)(((int64_t)(kb + 2 * i) * a.ldx + 8 * swz(kb + 2 * i, pc)) * 2);
     return sc;
 }
 
-// Direct global -> LDS copy of one stage (tokens t0 .. t0 + 31) into buf.
-GPTQ_DEV void issue_stage(const HessBf16Args& a, const StageCopy& sc, uint16_t* buf, int64_t t0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint16_t* sbase = a.X + (t0 + 2 * i) * sc.row_elems + sc.cbase;
-        dma16(sc.voff[i & 1], sbase, lds_addr(buf) + (uint32_t)(sc.wave_u * 4 + i) * 1024u);
-    }
+// Direct global -> LDS copy of one stage (tokens t0 .. t0 + 31) into ring slot SLOT.
+template <int SLOT>
+GPTQ_DEV void issue_stage(const HessBf16Args& a, const StageCopy& sc, int64_t t0) {
+    const uint16_t* sbase = a.X + t0 * sc.row_elems + sc.cbase;
+    static_for<0, HB_DMA>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        dma16<(uint32_t)(SLOT * HB_STE * 2 + i * 1024)>(sc.voff[i], sbase, sc.m0base);
+    });
 }
 
 // Register path for tiles at the matrix edge or a partial stage: zero-filled loads
 // written to the same swizzled layout.
 GPTQ_DEV void copy_stage_edge(const HessBf16Args& a, uint16_t* buf, int64_t t0, int64_t t_end, int c0, int c1, int tid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = tid + 512 * i;
+    for (int i = 0; i < 2048 / HB_THREADS; ++i) {
+        const int p = tid + HB_THREADS * i;
         const int op = p >> 10, pos = p & 1023;
         const int k = pos >> 5, pc = pos & 31;
         const int c = swz(k, pc);
@@ -183,25 +203,25 @@ GPTQ_DEV bf16x8_t read_frag(const uint16_t* op, int ch0, int kk, int lane) {
 
 // One wave's operand fragments for one 16-token slice of a stage: 2 (rows) + 4
 // (columns) fragments of 32 channels.
-struct Frags { bf16x8_t a[2], b[4]; };
+struct Frags { bf16x8_t a[HB_FA], b[HB_FB]; };
 
 GPTQ_DEV void read_slice(const uint16_t* stg, int kk, int wr, int wc, int lane, Frags& f) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[i] = read_frag(stg, wr * 64 + i * 32, kk, lane);
+    for (int i = 0; i < HB_FA; ++i) f.a[i] = read_frag(stg, wr * HB_WM + i * 32, kk, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = read_frag(stg + HB_OPE, wc * 128 + j * 32, kk, lane);
+    for (int j = 0; j < HB_FB; ++j) f.b[j] = read_frag(stg + HB_OPE, wc * HB_WN + j * 32, kk, lane);
 }
 
-GPTQ_DEV void mfma_slice(const Frags& f, f32x16_t (&acc)[2][4]) {
+GPTQ_DEV void mfma_slice(const Frags& f, f32x16_t (&acc)[HB_FA][HB_FB]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < HB_FA; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < HB_FB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // The MFMAs of one LDS stage for one wave (both slices), used by the edge path.
-GPTQ_DEV void mfma_stage(const uint16_t* stg, int wr, int wc, int lane, f32x16_t (&acc)[2][4]) {
+GPTQ_DEV void mfma_stage(const uint16_t* stg, int wr, int wc, int lane, f32x16_t (&acc)[HB_FA][HB_FB]) {
 #pragma unroll
     for (int kk = 0; kk < HB_BK; kk += 16) {
         Frags f;
@@ -212,7 +232,9 @@ GPTQ_DEV void mfma_stage(const uint16_t* stg, int wr, int wc, int lane, f32x16_t
 
 // s_waitcnt vmcnt(8) lgkmcnt(0): the loads of the two stages issued after the one
 // about to be used may stay in flight; this wave's LDS reads are complete.
-GPTQ_DEV void wait_vm8_lgkm0() { __builtin_amdgcn_s_waitcnt(0x8 | (0x7 << 4)); }
+constexpr int HB_VM = 2 * HB_DMA;    // loads of two stages
+static_assert(HB_VM < 64, "vmcnt field");
+GPTQ_DEV void wait_vm8_lgkm0() { __builtin_amdgcn_s_waitcnt((HB_VM & 15) | (0x7 << 4) | ((HB_VM >> 4) << 14)); }
 
 // Fast path: every stage full and the tile inside the matrix.  LDS ring of four
 // stages, DMA issued three stages ahead (re-loads of the last stage past the end
@@ -222,31 +244,32 @@ GPTQ_DEV void wait_vm8_lgkm0() { __builtin_amdgcn_s_waitcnt(0x8 | (0x7 << 4)); }
 //   read slice 1 of stage u | MFMAs of slice 0 | wait stage u+1, barrier |
 //   DMA stage u+4 into stage u's slot | read slice 0 of stage u+1 | MFMAs of slice 1.
 GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NSTG], int64_t t_beg, int64_t nst,
-                            int c0, int c1, int wr, int wc, int wave, int lane, f32x16_t (&acc)[2][4]) {
+                            int c0, int c1, int wr, int wc, int wave, int lane, f32x16_t (&acc)[HB_FA][HB_FB]) {
     auto t0 = [&](int64_t st) { return t_beg + (st < nst ? st : nst - 1) * HB_BK; };
-    const StageCopy sc = stage_copy_setup(a, c0, c1, wave, lane);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) issue_stage(a, sc, ring[i], t0(i));
+    const StageCopy sc = stage_copy_setup(a, ring[0], c0, c1, wave, lane);
+    issue_stage<0>(a, sc, t0(0));
+    issue_stage<1>(a, sc, t0(1));
+    issue_stage<2>(a, sc, t0(2));
     wait_vm8_lgkm0();
     __syncthreads();
-    issue_stage(a, sc, ring[3], t0(3));
+    issue_stage<3>(a, sc, t0(3));
     Frags f0, f1;
     read_slice(ring[0], 0, wr, wc, lane, f0);
     for (int64_t st = 0; st < nst; st += HB_NSTG) {
-#pragma unroll
-        for (int u = 0; u < HB_NSTG; ++u) {
+        static_for<0, HB_NSTG>([&](auto U) {
+            constexpr int u = decltype(U)::value;
             if (st + u < nst) {
                 read_slice(ring[u], 16, wr, wc, lane, f1);
                 mfma_slice(f0, acc);
                 __builtin_amdgcn_sched_barrier(0);   // keep the phases in this order
                 wait_vm8_lgkm0();
                 __syncthreads();
-                issue_stage(a, sc, ring[u], t0(st + u + 4));
+                issue_stage<u>(a, sc, t0(st + u + 4));
                 if (st + u + 1 < nst) read_slice(ring[(u + 1) & 3], 0, wr, wc, lane, f0);
                 mfma_slice(f1, acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        });
     }
     __builtin_amdgcn_s_waitcnt(0);   // drain the trailing re-loads before the LDS is reused
     __syncthreads();
@@ -254,7 +277,7 @@ GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NS
 
 // Edge path: register copies, two LDS stages.
 GPTQ_DEV void hess_loop_edge(const HessBf16Args& a, uint16_t* const (&ring)[HB_NSTG], int64_t t_beg, int64_t t_end,
-                             int64_t nst, int c0, int c1, int wr, int wc, int tid, int lane, f32x16_t (&acc)[2][4]) {
+                             int64_t nst, int c0, int c1, int wr, int wc, int tid, int lane, f32x16_t (&acc)[HB_FA][HB_FB]) {
     for (int64_t st = 0; st < nst; st += 2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -294,11 +317,11 @@ __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[HB_FA][HB_FB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < HB_FA; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+        for (int j = 0; j < HB_FB; ++j) acc[i][j] = f32x16_t{};
 
     const int64_t nst = (t_end > t_beg) ? (t_end - t_beg + HB_BK - 1) / HB_BK : 0;
     // the DMA path: whole tiles, whole stages, 16-byte aligned rows, per-lane offsets
@@ -314,13 +337,13 @@ __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a
     // this split's partial tile (row-major 256 x 256 fp32)
     float* P = a.partials + ((int64_t)s * a.T + tile) * (HB_BM * HB_BM);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < HB_FA; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < HB_FB; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int m = wr * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int nn = wc * 128 + j * 32 + (lane & 31);
+                const int m = wr * HB_WM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int nn = wc * HB_WN + j * 32 + (lane & 31);
                 P[m * HB_BM + nn] = acc[i][j][e];
             }
 }
