@@ -207,7 +207,7 @@ def main():
         "config": {"workload": "attention projection 4096x4096: W bf16 ~N(0,0.02^2), X 262144x4096 bf16 "
                                "(log-normal channel scales, 4 channels x50), int4 asym g128, B=128, damp 0.01",
                    "d_row": r, "d_col": d, "n_tokens": n, "bits": 4, "group_size": 128, "block_size": 128,
-                   "arithmetic": "H: bf16 MFMA, fp32 accumulate; prep: fp64 MFMA; sweep: fp32; trailing: fp32 MFMA"},
+                   "arithmetic": "H: bf16 MFMA, fp32 accumulate; prep: fp64 MFMA; sweep: fp32; trailing: bf16 hi/lo split (three products) on bf16 MFMA, fp32 accumulate"},
         "ms_per_layer": ms_layer,
         "ms_per_layer_quantize_only": ph["prep"] + ph["quant"],
         "phases_ms": ph,
