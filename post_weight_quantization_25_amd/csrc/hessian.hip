@@ -127,6 +127,7 @@ struct StageCopy {
     int64_t row_elems;      // ldx
     int cbase;              // channel base of this wave's operand (wave-uniform)
     uint32_t m0base;        // LDS byte address of the wave's first block in slot 0
+    bool skip;              // diagonal tile: the wave's operand is the other one, not loaded
 };
 
 GPTQ_DEV StageCopy stage_copy_setup(const HessBf16Args& a, const uint16_t* ring0, int c0, int c1, int wave,
@@ -136,6 +137,7 @@ GPTQ_DEV StageCopy stage_copy_setup(const HessBf16Args& a, const uint16_t* ring0
     sc.cbase = ((wave_u * HB_DMA) >> 4) ? c1 : c0;
     sc.row_elems = a.ldx;
     sc.m0base = lds_addr(ring0) + (uint32_t)(wave_u * HB_DMA) * 1024u;
+    sc.skip = (c0 == c1) && ((wave_u * HB_DMA) >> 4);
     const int kb = ((wave * HB_DMA) & 15) * 2 + (lane >> 5), pc = lane & 31;
 #pragma unroll
     for (int i = 0; i < HB_DMA; ++i)
@@ -146,6 +148,7 @@ GPTQ_DEV StageCopy stage_copy_setup(const HessBf16Args& a, const uint16_t* ring0
 // Direct global -> LDS copy of one stage (tokens t0 .. t0 + 31) into ring slot SLOT.
 template <int SLOT>
 GPTQ_DEV void issue_stage(const HessBf16Args& a, const StageCopy& sc, int64_t t0) {
+    if (sc.skip) return;
     const uint16_t* sbase = a.X + t0 * sc.row_elems + sc.cbase;
     static_for<0, HB_DMA>([&](auto I) {
         constexpr int i = decltype(I)::value;
@@ -205,11 +208,13 @@ GPTQ_DEV bf16x8_t read_frag(const uint16_t* op, int ch0, int kk, int lane) {
 // (columns) fragments of 32 channels.
 struct Frags { bf16x8_t a[HB_FA], b[HB_FB]; };
 
+// On a diagonal tile both operands are the same channel block, loaded once (DIAG).
+template <bool DIAG = false>
 GPTQ_DEV void read_slice(const uint16_t* stg, int kk, int wr, int wc, int lane, Frags& f) {
 #pragma unroll
     for (int i = 0; i < HB_FA; ++i) f.a[i] = read_frag(stg, wr * HB_WM + i * 32, kk, lane);
 #pragma unroll
-    for (int j = 0; j < HB_FB; ++j) f.b[j] = read_frag(stg + HB_OPE, wc * HB_WN + j * 32, kk, lane);
+    for (int j = 0; j < HB_FB; ++j) f.b[j] = read_frag(stg + (DIAG ? 0 : HB_OPE), wc * HB_WN + j * 32, kk, lane);
 }
 
 GPTQ_DEV void mfma_slice(const Frags& f, f32x16_t (&acc)[HB_FA][HB_FB]) {
@@ -218,6 +223,22 @@ GPTQ_DEV void mfma_slice(const Frags& f, f32x16_t (&acc)[HB_FA][HB_FB]) {
 #pragma unroll
         for (int j = 0; j < HB_FB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling hint for one region of the pipelined loop, which holds the 12 LDS reads
+// of the next slice and the 8 MFMAs of the current one: issue them interleaved (one
+// read per MFMA, then two), so that the LDS port and the matrix core work at the
+// same time instead of in bursts.
+GPTQ_DEV void interleave_reads_mfma() {
+    static_assert(HB_FA * HB_FB == 8 && 2 * (HB_FA + HB_FB) == 12, "pattern assumes 8 MFMAs, 12 reads");
+    static_for<0, 4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    });
+    static_for<0, 4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
 }
 
 // The MFMAs of one LDS stage for one wave (both slices), used by the edge path.
@@ -243,8 +264,23 @@ GPTQ_DEV void wait_vm8_lgkm0() { __builtin_amdgcn_s_waitcnt((HB_VM & 15) | (0x7 
 // next slice are read while the MFMAs of the current one run.  Step u:
 //   read slice 1 of stage u | MFMAs of slice 0 | wait stage u+1, barrier |
 //   DMA stage u+4 into stage u's slot | read slice 0 of stage u+1 | MFMAs of slice 1.
+// The reads of the next stage are issued also after the last stage (of a slot that
+// stays inside the ring, results unused), so that each region is one basic block
+// and the reads can be interleaved with the MFMAs.
+// Whether wave w's sub-tile of a diagonal tile lies strictly below the diagonal (its
+// first row after its last column).  Wave-uniform by construction.
+GPTQ_DEV bool below_diagonal(int wave) {
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    return (w >> 1) * HB_WM > (w & 1) * HB_WN + HB_WN - 1;
+}
+
+// DIAG: a diagonal tile (c0 == c1).  One operand is loaded, and the waves whose
+// sub-tile lies strictly below the diagonal (never read by the reduction) only take
+// part in the loads and barriers.
+template <bool DIAG>
 GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NSTG], int64_t t_beg, int64_t nst,
                             int c0, int c1, int wr, int wc, int wave, int lane, f32x16_t (&acc)[HB_FA][HB_FB]) {
+    const bool work = !DIAG || !below_diagonal(wave);
     auto t0 = [&](int64_t st) { return t_beg + (st < nst ? st : nst - 1) * HB_BK; };
     const StageCopy sc = stage_copy_setup(a, ring[0], c0, c1, wave, lane);
     issue_stage<0>(a, sc, t0(0));
@@ -254,19 +290,25 @@ GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NS
     __syncthreads();
     issue_stage<3>(a, sc, t0(3));
     Frags f0, f1;
-    read_slice(ring[0], 0, wr, wc, lane, f0);
+    if (work) read_slice<DIAG>(ring[0], 0, wr, wc, lane, f0);
     for (int64_t st = 0; st < nst; st += HB_NSTG) {
         static_for<0, HB_NSTG>([&](auto U) {
             constexpr int u = decltype(U)::value;
             if (st + u < nst) {
-                read_slice(ring[u], 16, wr, wc, lane, f1);
-                mfma_slice(f0, acc);
+                if (work) {
+                    read_slice<DIAG>(ring[u], 16, wr, wc, lane, f1);
+                    mfma_slice(f0, acc);
+                    interleave_reads_mfma();
+                }
                 __builtin_amdgcn_sched_barrier(0);   // keep the phases in this order
                 wait_vm8_lgkm0();
                 __syncthreads();
                 issue_stage<u>(a, sc, t0(st + u + 4));
-                if (st + u + 1 < nst) read_slice(ring[(u + 1) & 3], 0, wr, wc, lane, f0);
-                mfma_slice(f1, acc);
+                if (work) {
+                    read_slice<DIAG>(ring[(u + 1) & 3], 0, wr, wc, lane, f0);
+                    mfma_slice(f1, acc);
+                    interleave_reads_mfma();
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -330,11 +372,14 @@ __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a
                       ((reinterpret_cast<uintptr_t>(a.X) & 15) == 0) && ((a.ldx & 7) == 0) &&
                       (a.ldx < ((int64_t)1 << 25));
     if (nst > 0) {
-        if (full) hess_loop_dma(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
+        if (full && c0 == c1) hess_loop_dma<true>(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
+        else if (full) hess_loop_dma<false>(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
         else hess_loop_edge(a, ring, t_beg, t_end, nst, c0, c1, wr, wc, tid, lane, acc);
     }
 
-    // this split's partial tile (row-major 256 x 256 fp32)
+    // this split's partial tile (row-major 256 x 256 fp32); the reduction reads no
+    // element below the diagonal of a diagonal tile
+    if (c0 == c1 && below_diagonal(wave)) return;
     float* P = a.partials + ((int64_t)s * a.T + tile) * (HB_BM * HB_BM);
 #pragma unroll
     for (int i = 0; i < HB_FA; ++i)
