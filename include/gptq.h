@@ -28,7 +28,8 @@
  *    (device int32), readable after the stream is synchronized: 0 = success,
  *    k > 0 = a matrix that must be positive definite is not (see
  *    gptq_prepare_hinv), -1 = a non-finite input or a scale that is not a
- *    normal fp16 number.  The call itself still returns GPTQ_OK.
+ *    normal fp16 number, -2 = a bounded wait between workgroups expired (see
+ *    gptq_prepare_hinv).  The call itself still returns GPTQ_OK.
  *  - Calls on one stream are ordered; concurrent calls on different streams
  *    must not share output or workspace buffers.
  */
@@ -108,7 +109,10 @@ gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype,
  *  ws       at least gptq_prepare_hinv_workspace_size(d_col) bytes.
  *  info     device int32: 0, or k > 0 when the trailing principal submatrix of
  *           H + lambda I of order k is not positive definite (U is then undefined),
- *           or -1 when diag(H) holds a non-finite value.
+ *           or -1 when diag(H) holds a non-finite value, or -2 when a workgroup of
+ *           the factorization waited longer than its bound (about 2 s) for the
+ *           diagonal block that another workgroup of the same launch publishes
+ *           (U is then undefined; not expected on an idle device).
  */
 size_t gptq_prepare_hinv_workspace_size(int64_t d_col);
 gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float percdamp,

@@ -197,5 +197,8 @@ def check_info(info: torch.Tensor, what: str = "gptq"):
     if v > 0:
         raise GptqError(ERR_NOT_PD, f"{what}: trailing principal submatrix of order {v} of the damped "
                                     "Hessian is not positive definite")
+    if v == -2:
+        raise GptqError(ERR_HIP, f"{what}: a bounded wait between workgroups of the factorization "
+                                 "expired (device overloaded or preempted); results are undefined")
     if v < 0:
         raise GptqError(ERR_NONFINITE, f"{what}: {status_string(ERR_NONFINITE)}")

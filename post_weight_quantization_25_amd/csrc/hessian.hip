@@ -58,6 +58,7 @@ __host__ __device__ inline void upper_tile(int idx, int nt, int& ti, int& tj) {
 constexpr int HB_BM = 256;           // tile edge (channels)
 constexpr int HB_BK = 32;            // tokens per LDS stage
 constexpr int HB_NSTG = 4;           // LDS ring depth (stages in flight: 3 loading, 1 computing)
+static_assert(HB_NSTG * 32 * 1024 <= 160 * 1024, "LDS ring exceeds the workgroup's LDS");
 constexpr int HB_WAVES = 8;          // waves per workgroup, two per SIMD
 constexpr int HB_WN = 128;           // columns per wave
 constexpr int HB_WM = HB_BM * (HB_BM / HB_WN) / HB_WAVES;   // rows per wave (waves: rows x 2 columns)
@@ -251,19 +252,19 @@ GPTQ_DEV void mfma_stage(const uint16_t* stg, int wr, int wc, int lane, f32x16_t
     }
 }
 
-// s_waitcnt vmcnt(8) lgkmcnt(0): the loads of the two stages issued after the one
-// about to be used may stay in flight; this wave's LDS reads are complete.
-constexpr int HB_VM = 2 * HB_DMA;    // loads of two stages
+// s_waitcnt vmcnt(HB_VM) lgkmcnt(0): the loads of the HB_NSTG - 2 stages issued after
+// the one about to be used may stay in flight; this wave's LDS reads are complete.
+constexpr int HB_VM = (HB_NSTG - 2) * HB_DMA;
 static_assert(HB_VM < 64, "vmcnt field");
 GPTQ_DEV void wait_vm8_lgkm0() { __builtin_amdgcn_s_waitcnt((HB_VM & 15) | (0x7 << 4) | ((HB_VM >> 4) << 14)); }
 
-// Fast path: every stage full and the tile inside the matrix.  LDS ring of four
-// stages, DMA issued three stages ahead (re-loads of the last stage past the end
+// Fast path: every stage full and the tile inside the matrix.  LDS ring of HB_NSTG
+// stages, DMA issued HB_NSTG - 1 stages ahead (re-loads of the last stage past the end
 // keep the number of loads in flight constant, so one wait count fits every step),
 // and the LDS reads software-pipelined by 16-token slices: the fragments of the
 // next slice are read while the MFMAs of the current one run.  Step u:
 //   read slice 1 of stage u | MFMAs of slice 0 | wait stage u+1, barrier |
-//   DMA stage u+4 into stage u's slot | read slice 0 of stage u+1 | MFMAs of slice 1.
+//   DMA stage u+HB_NSTG into stage u's slot | read slice 0 of stage u+1 | MFMAs of slice 1.
 // The reads of the next stage are issued also after the last stage (of a slot that
 // stays inside the ring, results unused), so that each region is one basic block
 // and the reads can be interleaved with the MFMAs.
@@ -283,12 +284,10 @@ GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NS
     const bool work = !DIAG || !below_diagonal(wave);
     auto t0 = [&](int64_t st) { return t_beg + (st < nst ? st : nst - 1) * HB_BK; };
     const StageCopy sc = stage_copy_setup(a, ring[0], c0, c1, wave, lane);
-    issue_stage<0>(a, sc, t0(0));
-    issue_stage<1>(a, sc, t0(1));
-    issue_stage<2>(a, sc, t0(2));
+    static_for<0, HB_NSTG - 1>([&](auto I) { issue_stage<decltype(I)::value>(a, sc, t0(decltype(I)::value)); });
     wait_vm8_lgkm0();
     __syncthreads();
-    issue_stage<3>(a, sc, t0(3));
+    issue_stage<HB_NSTG - 1>(a, sc, t0(HB_NSTG - 1));
     Frags f0, f1;
     if (work) read_slice<DIAG>(ring[0], 0, wr, wc, lane, f0);
     for (int64_t st = 0; st < nst; st += HB_NSTG) {
@@ -303,9 +302,9 @@ GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NS
                 __builtin_amdgcn_sched_barrier(0);   // keep the phases in this order
                 wait_vm8_lgkm0();
                 __syncthreads();
-                issue_stage<u>(a, sc, t0(st + u + 4));
+                issue_stage<u>(a, sc, t0(st + u + HB_NSTG));
                 if (work) {
-                    read_slice<DIAG>(ring[(u + 1) & 3], 0, wr, wc, lane, f0);
+                    read_slice<DIAG>(ring[(u + 1) % HB_NSTG], 0, wr, wc, lane, f0);
                     mfma_slice(f1, acc);
                     interleave_reads_mfma();
                 }
@@ -334,8 +333,9 @@ GPTQ_DEV void hess_loop_edge(const HessBf16Args& a, uint16_t* const (&ring)[HB_N
 }
 
 __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds_ring[HB_NSTG * HB_STE];  // 4 x 32 KB
-    uint16_t* const ring[HB_NSTG] = {lds_ring, lds_ring + HB_STE, lds_ring + 2 * HB_STE, lds_ring + 3 * HB_STE};
+    __shared__ __attribute__((aligned(16))) uint16_t lds_ring[HB_NSTG * HB_STE];  // HB_NSTG x 32 KB
+    uint16_t* ring[HB_NSTG];
+    static_for<0, HB_NSTG>([&](auto I) { ring[decltype(I)::value] = lds_ring + decltype(I)::value * HB_STE; });
 
     // XCD-aware work mapping: workgroup L runs on XCD L % 8 (round-robin dispatch).
     // The tiles, in super-tile order, are cut into 8 / xpg runs of tpg tiles; the xpg

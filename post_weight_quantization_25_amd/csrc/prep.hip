@@ -28,7 +28,7 @@ constexpr int PNB = 64;  // leaf size
 
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void prep_lambda_kernel(const float* H, int64_t d, float percdamp,
-                                                         double* lam_out, int32_t* info) {
+                                                         double* lam_out, int32_t* info, int* flag) {
     __shared__ double red[1024];
     __shared__ int bad;
     if (threadIdx.x == 0) bad = 0;
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(1024) void prep_lambda_kernel(const float* H, int64
     if (threadIdx.x == 0) {
         *lam_out = (double)percdamp * (red[0] / (double)d);
         *info = bad ? -1 : 0;
+        *flag = 0;    // no diagonal block published yet in this call
     }
 }
 
@@ -284,8 +285,8 @@ GPTQ_DEV void diag_load(double* a, const double* A, int64_t d, int64_t k0, int n
     }
 }
 
-// Diagonal block 0 on its own (every later block is factored by the panel kernel
-// of the step before it).
+// Diagonal block 0 on its own (every later block is factored inside the trailing
+// update of the step before it).
 __global__ __launch_bounds__(256) void prep_diag_kernel(double* A, double* X, int64_t d, int64_t k0, int n,
                                                       int32_t* info) {
     __shared__ double lds[DIAG_LDS_DOUBLES];
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(256) void prep_panel_kernel(double* A, const double
 
 // --------------------------------------------------------------------------
 // fp64 GEMM on MFMA: C = beta C + alpha A op(B), 64 x 64 tiles, 4 waves (2 x 2 of 32 x 32).
-enum : int { G_BT = 1, G_TRI_A = 2, G_TRI_B = 4, G_LOWER_C = 8, G_DIAG0 = 16 };
+enum : int { G_BT = 1, G_TRI_A = 2, G_TRI_B = 4, G_LOWER_C = 8, G_DIAG0 = 16, G_PANEL1 = 32 };
 constexpr int GD_BM = 64, GD_BK = 32, GD_LD = GD_BK + 1;
 
 struct GemmD {
@@ -372,7 +373,15 @@ struct GemmD {
     // factors it after the update instead of storing it
     double* fA; double* fX; int64_t fd, k1; int n1; int32_t* info;
     int ntm, ntn;   // tiles along M (of a full batch entry) and N
+    // G_PANEL1: the tiles of block column 0 below tile (0, 0) are the next panel; their
+    // workgroups multiply the updated tile by the transposed inverse of the next
+    // diagonal block once the G_DIAG0 workgroup has published it (*flag >= step)
+    int* flag; int step;
 };
+
+// Bound of the wait for the next diagonal block (s_sleep 2 = 128 clocks per poll:
+// about 2 s at 2 GHz; the factorization of one block takes microseconds).
+constexpr int PANEL_SPIN_LIMIT = 1 << 25;
 
 // Operand chunk of GD_BK columns of k: 64 rows (m or n) x 32 k, as 4 double2 per thread.
 template <bool KMAJOR>
@@ -445,11 +454,22 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     // of a lower-triangular C are enumerated
     const int bid = blockIdx.x;
     int mi, nj;
-    if (g.flags & G_LOWER_C) {
-        mi = (int)((sqrtf(8.f * bid + 1.f) - 1.f) * 0.5f);
-        while ((mi + 1) * (mi + 2) / 2 <= bid) ++mi;
-        while (mi * (mi + 1) / 2 > bid) --mi;
-        nj = bid - mi * (mi + 1) / 2;
+    auto tri = [](int t, int& r, int& c) {   // t-th entry of a lower triangle, row-major
+        r = (int)((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
+        while ((r + 1) * (r + 2) / 2 <= t) ++r;
+        while (r * (r + 1) / 2 > t) --r;
+        c = t - r * (r + 1) / 2;
+    };
+    if (g.flags & G_PANEL1) {
+        // tile (0, 0) first (the next diagonal block), then the tiles right of block
+        // column 0, then block column 0 (the next panel, which waits for the block): in
+        // a large update those workgroups start after the block is published
+        const int inner = (g.ntm - 1) * g.ntm / 2;
+        if (bid == 0) { mi = 0; nj = 0; }
+        else if (bid <= inner) { tri(bid - 1, mi, nj); ++mi; ++nj; }
+        else { mi = bid - inner; nj = 0; }
+    } else if (g.flags & G_LOWER_C) {
+        tri(bid, mi, nj);
     } else if (g.flags & G_TRI_B) {          // k >= n0 (B lower) or k < n0 + 64 (B^T lower)
         const int q = bid / g.ntm;
         nj = (g.flags & G_BT) ? g.ntn - 1 - q : q;
@@ -477,6 +497,16 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{};
+
+    const bool full = (m0 + GD_BM <= g.M) && (n0 + GD_BM <= g.N);
+    const bool panel = (g.flags & G_PANEL1) && nj == 0 && mi > 0 && bz == 0;
+    // v_mfma_f64_16x16x4_f64 result layout: element e of lane l is row 4 e + l / 16
+    double* cbase = g.C + (int64_t)(m0 + wr * 32 + (lane >> 4)) * g.ldc + n0 + wc * 32 + (lane & 15);
+    auto off = [&](int i, int j, int e) { return (int64_t)(i * 16 + 4 * e) * g.ldc + j * 16; };
+    // C of a whole tile, loaded after the products (loading it before them measured
+    // slower: it competes with the operand loads of the first chunks)
+    double cold[2][2][4];
+    const bool pre = full && g.beta != 0.0;
 
     const int nch = (ke > kb) ? (ke - kb + GD_BK - 1) / GD_BK : 0;
     double2 va[4], vb[4];
@@ -517,6 +547,14 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
         }
         __syncthreads();
     }
+    if (pre) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cold[i][j][e] = cbase[off(i, j, e)];
+    }
     if (diag0) {
         // updated diagonal block -> a[] (lower part; upper 0, identity padding), factor
         double* a = lds;
@@ -530,28 +568,89 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
                     const int r = wr * 32 + i * 16 + 4 * e + (lane >> 4);
                     const int cc = wc * 32 + j * 16 + (lane & 15);
                     double v = (r == cc) ? 1.0 : 0.0;
-                    if (r < g.n1 && cc <= r) v = g.beta * g.C[(int64_t)r * g.ldc + cc] + g.alpha * acc[i][j][e];
+                    if (r < g.n1 && cc <= r) {
+                        const double c = pre ? cold[i][j][e] : g.C[(int64_t)r * g.ldc + cc];
+                        v = g.beta * c + g.alpha * acc[i][j][e];
+                    }
                     a[r * DLD + cc] = v;
                 }
         __syncthreads();
         diag_block(a, a + PNB * DLD, a + 2 * PNB * DLD, &fail_s, g.fA, g.fX, g.fd, g.k1, g.n1, g.info);
+        if (g.flags & G_PANEL1) {
+            // publish the factored block and its inverse (also after a failed pivot, so
+            // that no panel workgroup waits in vain; info then already holds the failure)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(g.flag, g.step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
         return;
     }
-    // C = beta C + alpha acc: all loads of C first, then all stores (a load after a
-    // store to the same array would otherwise wait for that store's round trip)
-    // v_mfma_f64_16x16x4_f64 result layout: element e of lane l is row 4 e + l / 16
-    const bool full = (m0 + GD_BM <= g.M) && (n0 + GD_BM <= g.N);
-    double* cbase = g.C + (int64_t)(m0 + wr * 32 + (lane >> 4)) * g.ldc + n0 + wc * 32 + (lane & 15);
-    auto off = [&](int i, int j, int e) { return (int64_t)(i * 16 + 4 * e) * g.ldc + j * 16; };
-    if (full) {
-        double cold[2][2][4];
-        if (g.beta != 0.0) {
+    if (panel) {
+        // updated tile (rows past M as zeros) -> LDS; the operand buffers are free after
+        // the last barrier of the product loop
+        double* pa = lds;
+        double* px = lds + PNB * DLD;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = wr * 32 + i * 16 + 4 * e + (lane >> 4);
+                    const int cc = wc * 32 + j * 16 + (lane & 15);
+                    double v = 0.0;
+                    if (m0 + r < g.M) {
+                        const double c = pre ? cold[i][j][e] : g.C[(int64_t)(m0 + r) * g.ldc + cc];
+                        v = g.beta * c + g.alpha * acc[i][j][e];
+                    }
+                    pa[r * DLD + cc] = v;
+                }
+        // wait (bounded) until the inverse of the next diagonal block is published
+        if (tid == 0) {
+            int spins = 0;
+            while (__hip_atomic_load(g.flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < g.step) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins == PANEL_SPIN_LIMIT) {
+                    atomicCAS(g.info, 0, -2);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        constexpr int PV = 64 * PNB / 2 / 256;      // double2 per thread
+        double2 vx[PV];
+#pragma unroll
+        for (int v = 0; v < PV; ++v) {
+            const int idx = tid + 256 * v;
+            const int i = idx / (PNB / 2), k = 2 * (idx % (PNB / 2));
+            vx[v] = *reinterpret_cast<const double2*>(g.fX + (g.k1 + i) * g.fd + g.k1 + k);
+        }
+#pragma unroll
+        for (int v = 0; v < PV; ++v) {
+            const int idx = tid + 256 * v;
+            const int i = idx / (PNB / 2), k = 2 * (idx % (PNB / 2));
+            px[i * DLD + k] = vx[v].x; px[i * DLD + k + 1] = vx[v].y;
+        }
+        __syncthreads();
+        // L[rows][k1 : k1 + 64] = (updated tile) X_kk^T, in the panel kernel's order
+        f64x4_t pacc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pacc[i][j] = f64x4_t{};
+#pragma unroll 4
+        for (int kk = 0; kk < PNB; kk += 4) {
+            double fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = pa[(wr * 32 + i * 16 + (lane & 15)) * DLD + kk + (lane >> 4)];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) fb[j] = px[(wc * 32 + j * 16 + (lane & 15)) * DLD + kk + (lane >> 4)];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cold[i][j][e] = cbase[off(i, j, e)];
+                    pacc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[i], fb[j], pacc[i][j], 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -559,8 +658,22 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
+                    const int r = wr * 32 + i * 16 + 4 * e + (lane >> 4);
+                    if (m0 + r < g.M) cbase[off(i, j, e)] = pacc[i][j][e];
+                }
+        return;
+    }
+    // C = beta C + alpha acc: all loads of C first (above), then all stores (a load
+    // after a store to the same array would otherwise wait for that store's round trip)
+    if (full) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
                     const double v = g.alpha * acc[i][j][e];
-                    cbase[off(i, j, e)] = (g.beta == 0.0) ? v : g.beta * cold[i][j][e] + v;
+                    cbase[off(i, j, e)] = pre ? g.beta * cold[i][j][e] + v : v;
                 }
     } else {
 #pragma unroll
@@ -584,17 +697,17 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
 // Host side
 struct PrepCtx {
     double* A; double* X; double* T; int64_t d;
-    int32_t* info; hipStream_t s;
+    int32_t* info; int* flag; hipStream_t s;
 };
 
 static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int64_t lda, const double* B,
                         int64_t ldb, int M, int N, int K, double alpha, double beta, int flags,
                         int nbatch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, int M_last = 0,
-                        int64_t k1 = 0, int n1 = 0) {
+                        int64_t k1 = 0, int n1 = 0, int step = 0) {
     if (M <= 0 || N <= 0 || nbatch <= 0) return GPTQ_OK;
     const int ntm = (M + GD_BM - 1) / GD_BM, ntn = (N + GD_BM - 1) / GD_BM;
     GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch,
-            c.A, c.X, c.d, k1, n1, c.info, ntm, ntn};
+            c.A, c.X, c.d, k1, n1, c.info, ntm, ntn, c.flag, step};
     const int ntiles = (flags & G_LOWER_C) ? ntm * (ntm + 1) / 2 : ntm * ntn;
     dim3 grid((unsigned)ntiles, 1, nbatch);
     if (flags & G_BT) gemm_f64_kernel<false><<<grid, 256, 0, c.s>>>(g);
@@ -606,23 +719,30 @@ static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int
 // Right-looking blocked Cholesky of A (lower, reversed damped H) with the inverse of
 // every 64 x 64 diagonal block of L, then X = L^-1 by recursive doubling over
 // independent block pairs: X[q][p] = -X[q][q] (L[q][p] X[p][p]).
+// Block 0 and its panel have launches of their own; every later diagonal block and
+// its panel are finished inside the trailing update of the step before (tile (0, 0)
+// factors the block, the tiles below it apply its inverse), so each step of the
+// chain is one launch.
 static gptq_status cholinv(PrepCtx& c) {
     const int64_t d = c.d;
     gptq_status st;
     prep_diag_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, 0, (int)std::min<int64_t>(PNB, d), c.info);
     GPTQ_LAUNCH_CHECK();
+    if (d > PNB) {
+        prep_panel_kernel<<<(unsigned)((d - PNB + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, 0);
+        GPTQ_LAUNCH_CHECK();
+    }
     for (int64_t k0 = 0; k0 < d; k0 += PNB) {
         const int n = (int)std::min<int64_t>(PNB, d - k0);
         const int64_t rest = d - k0 - n;
         if (rest <= 0) break;
-        prep_panel_kernel<<<(unsigned)((rest + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, k0);
-        GPTQ_LAUNCH_CHECK();
-        // trailing update; its workgroup of tile (0, 0) also factors diagonal block k+1
+        // trailing update; tile (0, 0) factors diagonal block k+1, the tiles below it
+        // form panel k+1
         double* L21 = c.A + (k0 + n) * d + k0;
         double* A22 = c.A + (k0 + n) * d + k0 + n;
         if ((st = gemm(c, A22, d, L21, d, L21, d, (int)rest, (int)rest, n, -1.0, 1.0,
-                       G_BT | G_LOWER_C | G_DIAG0, 1, 0, 0, 0, 0, k0 + n,
-                       (int)std::min<int64_t>(PNB, rest))) != GPTQ_OK)
+                       G_BT | G_LOWER_C | G_DIAG0 | G_PANEL1, 1, 0, 0, 0, 0, k0 + n,
+                       (int)std::min<int64_t>(PNB, rest), (int)(k0 / PNB) + 1)) != GPTQ_OK)
             return st;
     }
     for (int64_t b = PNB; b < d; b *= 2) {
@@ -667,8 +787,9 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     const size_t t = align256(t_bytes(d));
     double* lam = reinterpret_cast<double*>(p + 2 * dd + t);
     c.d = d; c.info = info; c.s = s;
+    c.flag = reinterpret_cast<int*>(lam + 1);    // inside the 256 reserved bytes
 
-    prep_lambda_kernel<<<1, 1024, 0, s>>>(H, d, percdamp, lam, info);
+    prep_lambda_kernel<<<1, 1024, 0, s>>>(H, d, percdamp, lam, info, c.flag);
     GPTQ_LAUNCH_CHECK();
     dim3 gb((unsigned)((d + 255) / 256 < 64 ? (d + 255) / 256 : 64), (unsigned)d);
     prep_build_kernel<<<gb, 256, 0, s>>>(H, d, lam, c.A, c.X);
