@@ -94,8 +94,48 @@ constexpr int DLD = PNB + 1;
 constexpr int DIAG_TS = 32 * 32;
 constexpr int DIAG_LDS_DOUBLES = 2 * PNB * DLD + DIAG_TS;
 
+// Inverse of the 8 x 8 lower block of L at rows / columns o .. o + 7 into xs, by
+// forward substitution; lane c < 8 computes column c.
+GPTQ_DEV void diag_inv8(const double* a, double* xs, int o, int c) {
+    double x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        double v = (i == c) ? 1.0 : 0.0;
+#pragma unroll
+        for (int k = 0; k < i; ++k) v -= a[(o + i) * DLD + o + k] * x[k];
+        x[i] = v / a[(o + i) * DLD + o + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs[(o + i) * DLD + o + c] = (i >= c) ? x[i] : 0.0;
+}
+
+// One 16 x 16 tile of a rank-8 update on MFMA: a[R0.., C0..] -= L[R0.., cL..cL+7]
+// L[C0.., cL..cL+7]^T, stored where row and column are >= cmask.
+GPTQ_DEV void diag_upd_tile(double* a, int R0, int C0, int cL, int cmask, int lane) {
+    f64x4_t acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = a[(R0 + 4 * e + (lane >> 4)) * DLD + C0 + (lane & 15)];
+#pragma unroll
+    for (int kk = 0; kk < 8; kk += 4) {
+        const double fa = -a[(R0 + (lane & 15)) * DLD + cL + kk + (lane >> 4)];
+        const double fb = a[(C0 + (lane & 15)) * DLD + cL + kk + (lane >> 4)];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int rr = R0 + 4 * e + (lane >> 4), cc = C0 + (lane & 15);
+        if (rr >= cmask && cc >= cmask) a[rr * DLD + cc] = acc[e];
+    }
+}
+
 // The block is in a[] (lower part, identity padding past n).  All 256 threads of
 // the workgroup call this.
+//
+// Look-ahead: the rank-8 update of round P is split into the 16-column tile strip
+// holding the next sub-panel (done by all waves right after round P's factor step)
+// and the tile columns right of it, which waves 2 and 3 apply while wave 0 factors
+// round P + 1 (those columns are disjoint from the sub-panel being factored).  Every
+// element receives the same updates in the same order as with whole-round updates.
 GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double* A, double* X, int64_t d,
                          int64_t k0, int n, int32_t* info) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -148,38 +188,36 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
                 for (int k = 0; k < 8; ++k) a[r * DLD + c0 + k] = x[k];
             }
             if (lane == 0 && f) fail_s = f;
+        } else if constexpr (c0 == 0) {
+            // meanwhile: the inverse starts as zero (the other three waves)
+            for (int idx = tid - 64; idx < PNB * DLD; idx += 192) xs[idx] = 0.0;
+        } else if (wave == 1) {
+            // meanwhile: the inverse of the previous sub-panel's 8 x 8 diagonal block (its
+            // divisions stay off the critical path of wave 0)
+            if (lane < 8) diag_inv8(a, xs, c0 - 8, lane);
+        } else {
+            // meanwhile: the rest of the previous round's update, tile columns right of
+            // the strip it updated (the strip holding column c0), on waves 2 and 3
+            constexpr int tp = c0 >> 4;
+            constexpr int nr = 3 - tp;                     // tile columns left to update
+            constexpr int nrt = nr * (nr + 1) / 2;         // their lower tiles
+            static_for<0, (nrt + 1) / 2>([&](auto R) {
+                const int tt = (wave - 2) + 2 * decltype(R)::value;
+                if (tt < nrt) {
+                    int tc = tp + 1, rem = tt;
+                    while (rem >= 4 - tc) { rem -= 4 - tc; ++tc; }
+                    diag_upd_tile(a, (tc + rem) * 16, tc * 16, c0 - 8, c0, lane);
+                }
+            });
         }
         __syncthreads();
         if (fail_s) return;
-        // rank-8 update of the lower part of rows / columns >= c1 = c0 + 8, in 16 x 16 tiles
+        // this round's update of the strip holding the next sub-panel (columns c1 ..),
+        // rows >= c1: at most four tiles, one per wave
         constexpr int c1 = c0 + 8;
         if constexpr (c1 < PNB) {
-            constexpr int t0 = c1 >> 4;
-            constexpr int nt = 4 - t0;                     // tiles per dimension still active
-            constexpr int ntiles = nt * (nt + 1) / 2;
-            static_for<0, (ntiles + 3) / 4>([&](auto R) {
-                const int tt = wave + 4 * decltype(R)::value;
-                if (tt < ntiles) {
-                    int tr = 0, rem = tt;
-                    while (rem > tr) { rem -= tr + 1; ++tr; }
-                    const int tc = rem;                    // tc <= tr within the active tiles
-                    const int R0 = (t0 + tr) * 16, C0 = (t0 + tc) * 16;
-                    f64x4_t acc;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = a[(R0 + 4 * e + (lane >> 4)) * DLD + C0 + (lane & 15)];
-#pragma unroll
-                    for (int kk = 0; kk < 8; kk += 4) {
-                        const double fa = -a[(R0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
-                        const double fb = a[(C0 + (lane & 15)) * DLD + c0 + kk + (lane >> 4)];
-                        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int rr = R0 + 4 * e + (lane >> 4), cc = C0 + (lane & 15);
-                        if (rr >= c1 && cc >= c1) a[rr * DLD + cc] = acc[e];
-                    }
-                }
-            });
+            constexpr int tn = c1 >> 4;
+            if (wave < 4 - tn) diag_upd_tile(a, (tn + wave) * 16, tn * 16, c0, c1, lane);
         }
         __syncthreads();
     });
@@ -187,24 +225,10 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
         if (tid == 0 && fail_s <= n && *info == 0) *info = (int32_t)(k0 + fail_s);
         return;
     }
-    // X_kk = L_kk^-1: inverses of the eight 8 x 8 diagonal blocks by forward
-    // substitution (one thread per block column), then recursive doubling
+    // X_kk = L_kk^-1: the inverses of the eight 8 x 8 diagonal blocks (the first seven
+    // were formed during the rounds), then recursive doubling
     // X[q][p] = -X[q][q] (L[q][p] X[p][p]) for block sizes 8, 16, 32
-    for (int idx = tid; idx < PNB * PNB; idx += 256) xs[(idx >> 6) * DLD + (idx & 63)] = 0.0;
-    __syncthreads();
-    if (tid < 64) {
-        const int bl = tid >> 3, c = tid & 7, o = bl * 8;
-        double x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            double v = (i == c) ? 1.0 : 0.0;
-#pragma unroll
-            for (int k = 0; k < i; ++k) v -= a[(o + i) * DLD + o + k] * x[k];
-            x[i] = v / a[(o + i) * DLD + o + i];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xs[(o + i) * DLD + o + c] = (i >= c) ? x[i] : 0.0;
-    }
+    if (wave == 1 && lane < 8) diag_inv8(a, xs, PNB - 8, lane);
     __syncthreads();
     for (int b = 8; b < PNB; b *= 2) {
         const int np = PNB / (2 * b);
@@ -259,10 +283,28 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
             __syncthreads();
         }
     }
-    for (int idx = tid; idx < n * n; idx += 256) {
-        const int r = idx / n, c = idx % n;
-        if (c <= r) A[(k0 + r) * d + k0 + c] = a[r * DLD + c];
-        X[(k0 + r) * d + k0 + c] = xs[r * DLD + c];
+    if (n == PNB && (d & 1) == 0) {
+        // 16-byte stores, 32 threads per row (whole rows per instruction); the strictly
+        // upper part of L's block is written as 0 (it is never read)
+        double2 vl[8], vx[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = (tid >> 5) + 8 * q, c = 2 * (tid & 31);
+            vl[q] = double2{c <= r ? a[r * DLD + c] : 0.0, c + 1 <= r ? a[r * DLD + c + 1] : 0.0};
+            vx[q] = double2{xs[r * DLD + c], xs[r * DLD + c + 1]};
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = (tid >> 5) + 8 * q, c = 2 * (tid & 31);
+            *reinterpret_cast<double2*>(A + (k0 + r) * d + k0 + c) = vl[q];
+            *reinterpret_cast<double2*>(X + (k0 + r) * d + k0 + c) = vx[q];
+        }
+    } else {
+        for (int idx = tid; idx < n * n; idx += 256) {
+            const int r = idx / n, c = idx % n;
+            if (c <= r) A[(k0 + r) * d + k0 + c] = a[r * DLD + c];
+            X[(k0 + r) * d + k0 + c] = xs[r * DLD + c];
+        }
     }
 }
 
