@@ -18,7 +18,10 @@
  * Conventions shared by every entry point
  *  - Every pointer argument named as a matrix or buffer is a DEVICE pointer
  *    unless its comment says "host".  The caller owns every buffer; the library
- *    never allocates or frees memory and keeps no state between calls.
+ *    never allocates or frees memory.  It keeps no state between calls, except
+ *    that gptq_prepare_hinv creates, at its first call on a device (the current
+ *    device), one auxiliary HIP stream of default priority and two events, and
+ *    keeps them until the process ends (see gptq_prepare_hinv).
  *  - Matrices are row-major.  All work is enqueued asynchronously on `stream`
  *    (a hipStream_t; NULL = the default stream); no call synchronizes.
  *  - Argument errors (null pointers, bad sizes, unsupported settings, a
@@ -107,6 +110,12 @@ gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype,
  *  H        d_col x d_col fp32 (only the upper triangle is read).
  *  U        d_col x d_col fp32 output; the strictly lower triangle is written as 0.
  *  ws       at least gptq_prepare_hinv_workspace_size(d_col) bytes.
+ * Part of the work (the inverse of the leading block) runs on the library's
+ * auxiliary stream of the current device, ordered after the earlier work of
+ * `stream` and joined back into `stream` by events, so `stream` sees the call as
+ * one ordered operation (also under stream capture).  `stream` must belong to the
+ * current device.
+ *
  *  info     device int32: 0, or k > 0 when the trailing principal submatrix of
  *           H + lambda I of order k is not positive definite (U is then undefined),
  *           or -1 when diag(H) holds a non-finite value, or -2 when a workgroup of

@@ -18,6 +18,7 @@
 // because an operand is triangular.
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -419,6 +420,9 @@ struct GemmD {
     // workgroups multiply the updated tile by the transposed inverse of the next
     // diagonal block once the G_DIAG0 workgroup has published it (*flag >= step)
     int* flag; int step;
+    // capped grid (0: one workgroup per tile): vtiles = tiles per batch entry (tpb) x
+    // entries, taken by the workgroups in turn
+    int vtiles, tpb;
 };
 
 // Bound of the wait for the next diagonal block (s_sleep 2 = 128 clocks per poll:
@@ -473,14 +477,13 @@ GPTQ_DEV void gd_store(double* S, int tid, const double2 (&v)[4]) {
 constexpr int GD_TILE = GD_BM * GD_LD;
 constexpr int GD_LDS = (4 * GD_TILE > DIAG_LDS_DOUBLES) ? 4 * GD_TILE : DIAG_LDS_DOUBLES;
 
-template <bool BKMAJOR>
-__global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
-    // operand double buffers; the diagonal routine's buffers in the G_DIAG0 workgroup
-    __shared__ double lds[GD_LDS];
-    __shared__ int fail_s;
+// One output tile (bid within batch entry bz).  lds: the operand double buffers, and
+// the diagonal routine's buffers in the G_DIAG0 workgroup.  FUSED: the G_DIAG0 /
+// G_PANEL1 paths are compiled in.
+template <bool BKMAJOR, bool FUSED>
+GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, int& fail_s) {
     auto As = [&](int b) { return lds + b * GD_TILE; };
     auto Bs = [&](int b) { return lds + (2 + b) * GD_TILE; };
-    const int bz = blockIdx.z;
     if (bz > 0) {
         g.A += bz * g.sA; g.B += bz * g.sB; g.C += bz * g.sC;
         if (bz == g.nbatch - 1) {
@@ -494,7 +497,6 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     // tile order of the 1-D grid: longest k ranges first where they differ (a lower-
     // triangular operand), so the long tiles do not finish last; only the lower tiles
     // of a lower-triangular C are enumerated
-    const int bid = blockIdx.x;
     int mi, nj;
     auto tri = [](int t, int& r, int& c) {   // t-th entry of a lower triangle, row-major
         r = (int)((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
         nj = bid % g.ntn;
     }
     const int m0 = mi * GD_BM, n0 = nj * GD_BM;
-    const bool diag0 = (g.flags & G_DIAG0) && mi == 0 && nj == 0 && bz == 0;
+    const bool diag0 = FUSED && (g.flags & G_DIAG0) && mi == 0 && nj == 0 && bz == 0;
     if (m0 >= g.M) return;
     int kb = 0, ke = g.K;
     if (g.flags & G_TRI_A) ke = min(ke, m0 + GD_BM);           // A lower: A[m][k] = 0 for k > m
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{};
 
     const bool full = (m0 + GD_BM <= g.M) && (n0 + GD_BM <= g.N);
-    const bool panel = (g.flags & G_PANEL1) && nj == 0 && mi > 0 && bz == 0;
+    const bool panel = FUSED && (g.flags & G_PANEL1) && nj == 0 && mi > 0 && bz == 0;
     // v_mfma_f64_16x16x4_f64 result layout: element e of lane l is row 4 e + l / 16
     double* cbase = g.C + (int64_t)(m0 + wr * 32 + (lane >> 4)) * g.ldc + n0 + wc * 32 + (lane & 15);
     auto off = [&](int i, int j, int e) { return (int64_t)(i * 16 + 4 * e) * g.ldc + j * 16; };
@@ -597,7 +599,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) cold[i][j][e] = cbase[off(i, j, e)];
     }
-    if (diag0) {
+    if constexpr (FUSED) if (diag0) {
         // updated diagonal block -> a[] (lower part; upper 0, identity padding), factor
         double* a = lds;
         if (tid == 0) fail_s = 0;
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
         }
         return;
     }
-    if (panel) {
+    if constexpr (FUSED) if (panel) {
         // updated tile (rows past M as zeros) -> LDS; the operand buffers are free after
         // the last barrier of the product loop
         double* pa = lds;
@@ -735,6 +737,25 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
     }
 }
 
+template <bool BKMAJOR>
+__global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
+    __shared__ double lds[GD_LDS];
+    __shared__ int fail_s;
+    gemm_f64_tile<BKMAJOR, true>(g, blockIdx.x, blockIdx.z, lds, fail_s);
+}
+
+// Capped grid: workgroup w takes the tiles w, w + gridDim.x, ... (batch-major); no
+// G_DIAG0 / G_PANEL1 work.
+template <bool BKMAJOR>
+__global__ __launch_bounds__(256) void gemm_f64_capped_kernel(GemmD g) {
+    __shared__ double lds[4 * GD_TILE];
+    __shared__ int fail_s;
+    for (int vt = blockIdx.x; vt < g.vtiles; vt += gridDim.x) {
+        __syncthreads();   // the previous tile's last LDS reads are done
+        gemm_f64_tile<BKMAJOR, false>(g, vt % g.tpb, vt / g.tpb, lds, fail_s);
+    }
+}
+
 // --------------------------------------------------------------------------
 // Host side
 struct PrepCtx {
@@ -745,35 +766,133 @@ struct PrepCtx {
 static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int64_t lda, const double* B,
                         int64_t ldb, int M, int N, int K, double alpha, double beta, int flags,
                         int nbatch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, int M_last = 0,
-                        int64_t k1 = 0, int n1 = 0, int step = 0) {
+                        int64_t k1 = 0, int n1 = 0, int step = 0, int max_wg = 0) {
     if (M <= 0 || N <= 0 || nbatch <= 0) return GPTQ_OK;
     const int ntm = (M + GD_BM - 1) / GD_BM, ntn = (N + GD_BM - 1) / GD_BM;
     GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch,
-            c.A, c.X, c.d, k1, n1, c.info, ntm, ntn, c.flag, step};
+            c.A, c.X, c.d, k1, n1, c.info, ntm, ntn, c.flag, step, 0, 0};
     const int ntiles = (flags & G_LOWER_C) ? ntm * (ntm + 1) / 2 : ntm * ntn;
     dim3 grid((unsigned)ntiles, 1, nbatch);
+    if (max_wg > 0 && (int64_t)ntiles * nbatch > max_wg && !(flags & (G_DIAG0 | G_PANEL1))) {
+        g.vtiles = ntiles * nbatch;
+        g.tpb = ntiles;
+        if (flags & G_BT) gemm_f64_capped_kernel<false><<<max_wg, 256, 0, c.s>>>(g);
+        else gemm_f64_capped_kernel<true><<<max_wg, 256, 0, c.s>>>(g);
+        GPTQ_LAUNCH_CHECK();
+        return GPTQ_OK;
+    }
     if (flags & G_BT) gemm_f64_kernel<false><<<grid, 256, 0, c.s>>>(g);
     else gemm_f64_kernel<true><<<grid, 256, 0, c.s>>>(g);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
 
+// X = L^-1 on the diagonal block [off, off + m) by recursive doubling of the inverted
+// 64 x 64 diagonal blocks over independent block pairs, X[q][p] = -X[q][q] (L[q][p]
+// X[p][p]), block sizes 64, 128, .. < m, each level two batched products; T is
+// scratch for the products (at most m * m doubles).
+static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, int max_wg = 0) {
+    const int64_t d = c.d;
+    gptq_status st;
+    for (int64_t b = PNB; b < m; b *= 2) {
+        // pairs p = off + [2 j b, (2 j + 1) b), q = off + [(2 j + 1) b, min((2 j + 2) b, m))
+        const int64_t npairs = (m - b + 2 * b - 1) / (2 * b);
+        const int64_t q_last = (2 * (npairs - 1) + 1) * b;
+        const int qn_last = (int)std::min<int64_t>(b, m - q_last);
+        const int64_t step = 2 * b * (d + 1);
+        const int bb = (int)b;
+        double* Ab = c.A + (off + b) * d + off;       // L[q][p] of the first pair
+        double* Xp = c.X + off * d + off;             // X[p][p]
+        double* Xq = c.X + (off + b) * d + off;       // X[q][p]
+        // T_j = L[q][p] X[p][p]   (b x b each, X[p][p] lower triangular)
+        if ((st = gemm(c, T, bb, Ab, d, Xp, d, bb, bb, bb, 1.0, 0.0, G_TRI_B,
+                       (int)npairs, step, step, (int64_t)b * b, qn_last, 0, 0, 0, max_wg)) != GPTQ_OK) return st;
+        // X[q][p] = -X[q][q] T_j   (X[q][q] lower triangular)
+        if ((st = gemm(c, Xq, d, Xq + b, d, T, bb, bb, bb, bb, -1.0, 0.0, G_TRI_A,
+                       (int)npairs, step, (int64_t)b * b, step, qn_last, 0, 0, 0, max_wg)) != GPTQ_OK) return st;
+    }
+    return GPTQ_OK;
+}
+
+// The auxiliary work starts once the trailing matrix is down to AUX_FORK_REST columns
+// (or later, when the leading block is final only then), and its products take at
+// most AUX_MAX_WG workgroups at a time, so that the factorization steps beside it
+// still find free slots.
+#ifndef AUX_FORK_REST
+#define AUX_FORK_REST 2048
+#endif
+#ifndef AUX_MAX_WG
+#define AUX_MAX_WG 256
+#endif
+
+// One auxiliary stream and two events per device, created on first use and kept
+// until the process ends; enqueueing is serialized so that concurrent calls do not
+// interleave their fork / join records.
+struct AuxStream { hipStream_t s = nullptr; hipEvent_t fork = nullptr, join = nullptr; };
+static std::mutex aux_mu;
+static AuxStream aux_dev[64];
+
+static gptq_status aux_stream(AuxStream*& out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GPTQ_ERR_HIP;
+    AuxStream& a = aux_dev[dev];
+    if (a.s == nullptr) {
+        if (hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) != hipSuccess) { a.s = nullptr; return GPTQ_ERR_HIP; }
+        if (hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess)
+            return GPTQ_ERR_HIP;
+    }
+    out = &a;
+    return GPTQ_OK;
+}
+
 // Right-looking blocked Cholesky of A (lower, reversed damped H) with the inverse of
-// every 64 x 64 diagonal block of L, then X = L^-1 by recursive doubling over
-// independent block pairs: X[q][p] = -X[q][q] (L[q][p] X[p][p]).
+// every 64 x 64 diagonal block of L, then X = L^-1.
 // Block 0 and its panel have launches of their own; every later diagonal block and
 // its panel are finished inside the trailing update of the step before (tile (0, 0)
 // factors the block, the tiles below it apply its inverse), so each step of the
 // chain is one launch.
+// The inverse is split at h, the largest 64 * 2^i below d: as soon as the first h
+// columns of L are final, the inverse X11 of the leading h x h block and the product
+// T = L21 X11 run on the auxiliary stream, beside the remaining (latency-bound)
+// factorization steps; afterwards the trailing block is inverted and
+// X21 = -X22 T closes the last doubling level.
 static gptq_status cholinv(PrepCtx& c) {
     const int64_t d = c.d;
     gptq_status st;
     prep_diag_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, 0, (int)std::min<int64_t>(PNB, d), c.info);
     GPTQ_LAUNCH_CHECK();
-    if (d > PNB) {
-        prep_panel_kernel<<<(unsigned)((d - PNB + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, 0);
-        GPTQ_LAUNCH_CHECK();
-    }
+    if (d <= PNB) return GPTQ_OK;
+    prep_panel_kernel<<<(unsigned)((d - PNB + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, 0);
+    GPTQ_LAUNCH_CHECK();
+
+    int64_t h = PNB;
+    while (2 * h < d) h *= 2;
+    const int64_t m = d - h;                 // 0 < m <= h
+    double* T11 = c.T;                       // h * h doubles: X11's levels, then T (m x h)
+    double* T22 = c.T + h * h;               // m * m doubles: X22's levels
+
+    AuxStream* aux = nullptr;
+    if ((st = aux_stream(aux)) != GPTQ_OK) return st;
+    PrepCtx ca = c;
+    ca.s = aux->s;
+    // columns [0, h) of L and the inverted diagonal blocks below h are final once the
+    // step that forms panel h / 64 - 1 has been enqueued (step h / 64 - 2; before the
+    // loop when h = 64)
+    const int64_t fork_step = std::max<int64_t>(h / PNB - 2, (d - AUX_FORK_REST) / PNB);
+    auto fork = [&]() -> gptq_status {
+        if (hipEventRecord(aux->fork, c.s) != hipSuccess || hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess)
+            return GPTQ_ERR_HIP;
+        gptq_status s2;
+        if ((s2 = trtri_block(ca, 0, h, T11, AUX_MAX_WG)) != GPTQ_OK) return s2;
+        // T = L21 X11   (m x h, X11 lower triangular)
+        if ((s2 = gemm(ca, T11, h, c.A + h * d, d, c.X, d, (int)m, (int)h, (int)h, 1.0, 0.0, G_TRI_B, 1, 0, 0, 0,
+                       0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+            return s2;
+        if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
+        return GPTQ_OK;
+    };
+    if (fork_step < 0 && (st = fork()) != GPTQ_OK) return st;
     for (int64_t k0 = 0; k0 < d; k0 += PNB) {
         const int n = (int)std::min<int64_t>(PNB, d - k0);
         const int64_t rest = d - k0 - n;
@@ -786,28 +905,19 @@ static gptq_status cholinv(PrepCtx& c) {
                        G_BT | G_LOWER_C | G_DIAG0 | G_PANEL1, 1, 0, 0, 0, 0, k0 + n,
                        (int)std::min<int64_t>(PNB, rest), (int)(k0 / PNB) + 1)) != GPTQ_OK)
             return st;
+        if (k0 / PNB == fork_step && (st = fork()) != GPTQ_OK) return st;
     }
-    for (int64_t b = PNB; b < d; b *= 2) {
-        // pairs p = [2 m b, (2 m + 1) b), q = [(2 m + 1) b, min((2 m + 2) b, d))
-        const int64_t npairs = (d - b + 2 * b - 1) / (2 * b);
-        const int64_t q_last = (2 * (npairs - 1) + 1) * b;
-        const int qn_last = (int)std::min<int64_t>(b, d - q_last);
-        const int64_t step = 2 * b * (d + 1);
-        const int bb = (int)b;
-        // T_m = L[q][p] X[p][p]   (b x b each, X[p][p] lower triangular)
-        if ((st = gemm(c, c.T, bb, c.A + b * d, d, c.X, d, bb, bb, bb, 1.0, 0.0, G_TRI_B,
-                       (int)npairs, step, step, (int64_t)b * b, qn_last)) != GPTQ_OK) return st;
-        // X[q][p] = -X[q][q] T_m   (X[q][q] lower triangular)
-        if ((st = gemm(c, c.X + b * d, d, c.X + b * d + b, d, c.T, bb, bb, bb, bb, -1.0, 0.0, G_TRI_A,
-                       (int)npairs, step, (int64_t)b * b, step, qn_last)) != GPTQ_OK) return st;
-    }
-    return GPTQ_OK;
+    if ((st = trtri_block(c, h, m, T22)) != GPTQ_OK) return st;
+    if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
+    // X21 = -X22 T   (X22 lower triangular)
+    return gemm(c, c.X + h * d, d, c.X + h * d + h, d, T11, h, (int)m, (int)h, (int)m, -1.0, 0.0, G_TRI_A);
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static size_t t_bytes(int64_t d) {
-    // recursive-doubling scratch: npairs * b * b <= d * b / 2 + b * b with b < d
+    // product scratch: h * h doubles for the leading block's levels and T (m x h), then
+    // m * m for the trailing block's levels (m = d - h <= h), h * h + m * m <= d * d
     return (size_t)d * d * sizeof(double);
 }
 
@@ -836,7 +946,11 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     dim3 gb((unsigned)((d + 255) / 256 < 64 ? (d + 255) / 256 : 64), (unsigned)d);
     prep_build_kernel<<<gb, 256, 0, s>>>(H, d, lam, c.A, c.X);
     GPTQ_LAUNCH_CHECK();
-    gptq_status st = cholinv(c);
+    gptq_status st;
+    {
+        std::lock_guard<std::mutex> g(aux_mu);
+        st = cholinv(c);
+    }
     if (st != GPTQ_OK) return st;
     prep_output_kernel<<<gb, 256, 0, s>>>(c.X, d, U);
     GPTQ_LAUNCH_CHECK();
