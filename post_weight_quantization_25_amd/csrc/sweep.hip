@@ -52,7 +52,8 @@ GPTQ_DEV float row_max(float v) {
 __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     __shared__ __attribute__((aligned(16))) float Up[QB][SL][SSLOTS];  // Up[j][q][i] = U[b0+j][b0+q+16i]
     __shared__ float invd[QB];                                         // 1 / U[b0+j][b0+j]
-    __shared__ uint8_t cl[SROWS][QB];
+    __shared__ __attribute__((aligned(16))) uint8_t cl[SROWS][QB];
+    __shared__ __attribute__((aligned(16))) uint16_t ehs[SROWS][QB], els[SROWS][QB];   // E split, staged
     __shared__ int bad_any;
 
     const int tid = threadIdx.x;
@@ -65,6 +66,16 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     const float fqmin = (float)a.qmin, fqmax = (float)a.qmax, fzoff = (float)a.zoff;
     if (tid == 0) bad_any = 0;
 
+    float w[SSLOTS], e[SSLOTS];
+    int cv[SSLOTS];
+    const float* wrow = a.Wws + (rv ? row : 0) * a.d_col + a.b0;
+#pragma unroll
+    for (int i = 0; i < SSLOTS; ++i) {
+        const int c = SL * i + q;
+        w[i] = (rv && c < nb) ? wrow[c] : 0.f;
+        e[i] = 0.f;
+        cv[i] = 0;
+    }
     // stage U's diagonal block: all loads of a thread first (16-byte loads when rows
     // are 16-byte aligned), then the permuted LDS stores
     constexpr int NV = QB * QB / 4 / QT;   // float4 per thread
@@ -87,6 +98,8 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
             for (int e = 0; e < 4; ++e) uv[v][e] = (j < nb && c4 + e < nb) ? src[e] : 0.f;
         }
     }
+    // the reciprocal pivots: one division in each of the first 128 threads
+    const float udiag = (tid < nb) ? a.U[(a.b0 + tid) * a.d_col + a.b0 + tid] : 0.f;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int idx = tid + QT * v;
@@ -95,19 +108,9 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         for (int e = 0; e < 4; ++e) {
             const int c = c4 + e;
             Up[j][c & (SL - 1)][c >> 4] = uv[v][e];
-            if (c == j) invd[j] = (j < nb) ? 1.0f / uv[v][e] : 0.f;
         }
     }
-    float w[SSLOTS], e[SSLOTS];
-    int cv[SSLOTS];
-    const float* wrow = a.Wws + (rv ? row : 0) * a.d_col + a.b0;
-#pragma unroll
-    for (int i = 0; i < SSLOTS; ++i) {
-        const int c = SL * i + q;
-        w[i] = (rv && c < nb) ? wrow[c] : 0.f;
-        e[i] = 0.f;
-        cv[i] = 0;
-    }
+    if (tid < QB) invd[tid] = (tid < nb) ? 1.0f / udiag : 0.f;
     // s16f, r16f = 1 / s16f and the zero point zf of the current group; the code is
     // rne(t) + zf clamped to [qmin, qmax], i.e. rne(t) clamped to [lo, hi]
     float s16f = 1.f, r16f = 1.f, zf = 0.f;
@@ -225,36 +228,61 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     // a non-finite weight, scale or error shows up in the block's errors
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) bad = bad || !(fabsf(e[i]) <= 3.0e38f);
-    if (rv) {
-        uint16_t* hrow = a.Ehi + row * a.lde;
-        uint16_t* lrow = a.Elo + row * a.lde;
+    // the trailing update multiplies on bf16 MFMA with a three-term split: the split
+    // is formed here once (hi = bf16(e), lo = bf16(e - hi)) instead of in every
+    // workgroup of the product; it and the codes are staged in LDS and written as
+    // whole 16- / 4-byte pieces
 #pragma unroll
-        for (int i = 0; i < SSLOTS; ++i) {
-            const int c = SL * i + q;
-            // the trailing update multiplies on bf16 MFMA with a three-term split:
-            // store the split here once instead of in every workgroup of the product
-            const uint16_t h = f32_to_bf16_bits(e[i]);
-            const uint16_t l = f32_to_bf16_bits(e[i] - bf16_bits_to_f32(h));
-            if (c < nb) { hrow[c] = h; lrow[c] = l; }
-        }
+    for (int i = 0; i < SSLOTS; ++i) {
+        const int c = SL * i + q;
+        const uint16_t h = f32_to_bf16_bits(e[i]);
+        ehs[rl][c] = h;
+        els[rl][c] = f32_to_bf16_bits(e[i] - bf16_bits_to_f32(h));
+        cl[rl][c] = (uint8_t)cv[i];
     }
-#pragma unroll
-    for (int i = 0; i < SSLOTS; ++i) cl[rl][SL * i + q] = (uint8_t)cv[i];
     if (bad && rv) atomicOr(&bad_any, 1);
-    __syncthreads();
+    // LDS only: the global stores above and below need not have landed
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
     if (tid == 0 && bad_any) *a.info = -1;
 
-    // pack the block's codes: two per byte (column 2k in the low nibble) or one per byte
     const int per = a.packed ? 2 : 1;
-    const int nbytes = nb / per;
-    const int rowbytes = QB / per;
-    for (int idx = tid; idx < SROWS * rowbytes; idx += QT) {
-        const int r = idx / rowbytes, bidx = idx % rowbytes;
+    {
+        // E: thread t writes 8 columns of row t / 16
+        const int r = tid >> 4, c8 = (tid & 15) * 8;
         const int64_t grow = (int64_t)blockIdx.x * SROWS + r;
-        if (grow >= a.d_row || bidx >= nbytes) continue;
-        const uint8_t v = a.packed ? (uint8_t)((cl[r][2 * bidx] & 0xF) | ((cl[r][2 * bidx + 1] & 0xF) << 4))
-                                   : cl[r][bidx];
-        a.codes[grow * a.code_ld + a.b0 / per + bidx] = v;
+        if (grow < a.d_row) {
+            uint16_t* hrow = a.Ehi + grow * a.lde;
+            uint16_t* lrow = a.Elo + grow * a.lde;
+            if (nb == QB && (a.lde & 7) == 0 && ((reinterpret_cast<uintptr_t>(a.Ehi) & 15) == 0) &&
+                ((reinterpret_cast<uintptr_t>(a.Elo) & 15) == 0)) {
+                *reinterpret_cast<u32x4_t*>(hrow + c8) = *reinterpret_cast<const u32x4_t*>(&ehs[r][c8]);
+                *reinterpret_cast<u32x4_t*>(lrow + c8) = *reinterpret_cast<const u32x4_t*>(&els[r][c8]);
+            } else {
+                for (int c = c8; c < c8 + 8 && c < nb; ++c) { hrow[c] = ehs[r][c]; lrow[c] = els[r][c]; }
+            }
+        }
+        // codes: two per byte (column 2k in the low nibble) or one per byte; thread t
+        // writes 8 columns of row t / 16
+        if (grow < a.d_row) {
+            uint8_t* crow = a.codes + grow * a.code_ld + a.b0 / per;
+            const bool whole = nb == QB && ((reinterpret_cast<uintptr_t>(crow) & (a.packed ? 3 : 7)) == 0);
+            if (a.packed) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    v |= (uint32_t)((cl[r][c8 + 2 * k] & 0xF) | ((cl[r][c8 + 2 * k + 1] & 0xF) << 4)) << (8 * k);
+                if (whole) *reinterpret_cast<uint32_t*>(crow + c8 / 2) = v;
+                else
+                    for (int k = 0; k < 4 && c8 + 2 * k < nb; ++k) crow[c8 / 2 + k] = (uint8_t)(v >> (8 * k));
+            } else {
+                if (whole) {
+                    *reinterpret_cast<uint2*>(crow + c8) = *reinterpret_cast<const uint2*>(&cl[r][c8]);
+                } else {
+                    for (int k = 0; k < 8 && c8 + k < nb; ++k) crow[c8 + k] = cl[r][c8 + k];
+                }
+            }
+        }
     }
 }
 
