@@ -14,8 +14,9 @@
 //
 // The in-block column sweep is in sweep.hip.  This file holds the per-row
 // scale/zero of group_size 0, the working-copy conversion, the trailing lazy
-// update W[:, b1:] -= E U[b0:b1, b1:] on v_mfma_f32_16x16x4_f32 (fp32 operands),
-// the host-side block loop, and dequantization.
+// update W[:, b1:] -= E U[b0:b1, b1:] on v_mfma_f32_32x32x16_bf16 with both
+// operands split into bf16 hi + lo (three products, fp32 accumulation), the
+// host-side block loop, and dequantization.
 
 #include "kernels.h"
 #include "quant_internal.h"
