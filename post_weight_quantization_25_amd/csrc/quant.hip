@@ -273,11 +273,11 @@ static gptq_status trail(const TrailArgs& ta, hipStream_t s) {
 // Host side
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Super-block width of the deferred trailing update: inside a super-block every
-// 128-column block updates only the rest of the super-block; the columns after it
-// get one product with K = QSB per super-block.  The regrouping of the rank-1
-// updates is exact in exact arithmetic, as for the 128-column lazy blocks.
-constexpr int QSB = 512;
+// Super-blocks (QSB columns) of the deferred trailing update: inside a super-block
+// every 128-column block updates only the rest of the super-block (in the sweep
+// kernel); the columns after it get one product with K = QSB per super-block.  The
+// regrouping of the rank-1 updates is exact in exact arithmetic, as for the
+// 128-column lazy blocks.
 
 // Workspace: fp32 working copy of W | E hi | E lo (bf16, d_row x QSB) | U hi | U lo
 // (bf16, d_col x d_col).
@@ -350,7 +350,7 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         split_u_kernel<<<ug, 256, 0, s>>>(U, nu, Uhi, Ulo);
         GPTQ_LAUNCH_CHECK();
     }
-    sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U;
+    sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U; sa.Uhi = Uhi; sa.Ulo = Ulo;
     sa.codes = codes; sa.code_ld = (p.bits <= 4) ? d_col / 2 : d_col;
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
     sa.group = G; sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
@@ -359,15 +359,11 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     sa.zoff = sa.sym ? (1 << (p.bits - 1)) : 0;
     for (int64_t s0 = 0; s0 < d_col; s0 += QSB) {
         const int64_t s1 = std::min<int64_t>(s0 + QSB, d_col);
-        for (int64_t b0 = s0; b0 < s1; b0 += QB) {
-            const int nb = (int)std::min<int64_t>(QB, s1 - b0);
-            sa.b0 = b0; sa.nb = nb; sa.Ehi = Ehi + (b0 - s0); sa.Elo = Elo + (b0 - s0); sa.lde = QSB;
-            st = sweep_launch(sa, s);
-            if (st != GPTQ_OK) return st;
-            // within the super-block
-            TrailArgs ta{Wws, d_row, d_col, Ehi + (b0 - s0), Elo + (b0 - s0), QSB, Uhi, Ulo, b0, nb, b0 + nb, s1};
-            if ((st = trail(ta, s)) != GPTQ_OK) return st;
-        }
+        // the super-block's blocks, each followed by the update of the rest of the
+        // super-block, in one launch
+        sa.s0 = s0; sa.s1 = s1; sa.Ehi = Ehi; sa.Elo = Elo; sa.lde = QSB;
+        st = sweep_launch(sa, s);
+        if (st != GPTQ_OK) return st;
         // everything after the super-block, K = s1 - s0
         TrailArgs tb{Wws, d_row, d_col, Ehi, Elo, QSB, Uhi, Ulo, s0, (int)(s1 - s0), s1, d_col};
         if ((st = trail(tb, s)) != GPTQ_OK) return st;

@@ -8,13 +8,17 @@ constexpr int QB = 128;             // lazy-update block width (columns)
 constexpr int QT = 256;             // threads per sweep workgroup
 constexpr int SL = 16;              // lanes per row in the sweep (one DPP row)
 constexpr int SROWS = QT / SL;      // rows per sweep workgroup
+// Super-block of the deferred trailing update: the sweep of its blocks and the updates
+// inside it run in one launch; the columns after it get one product with K = QSB.
+constexpr int QSB = 512;
 
 struct SweepArgs {
     const float* Wws; int64_t d_row, d_col;
-    const float* U;
-    int64_t b0; int nb;
-    uint16_t* Ehi; uint16_t* Elo;   // error block of this block as bf16 hi + lo (hi = bf16(e),
-    int64_t lde;                    // lo = bf16(e - hi)): d_row x 128, row stride lde
+    const float* U;                 // fp32 U (the diagonal blocks for the sweep)
+    const uint16_t* Uhi; const uint16_t* Ulo;   // U split into bf16 hi + lo (the updates)
+    int64_t s0, s1;                 // the super-block: columns s0 .. s1 - 1 (s1 - s0 <= QSB)
+    uint16_t* Ehi; uint16_t* Elo;   // the super-block's errors as bf16 hi + lo (hi = bf16(e),
+    int64_t lde;                    // lo = bf16(e - hi)): d_row x QSB, row stride lde
     uint8_t* codes; int64_t code_ld;
     uint16_t* scales; uint16_t* zeros; int n_groups;
     int32_t* info;

@@ -1,6 +1,7 @@
-// The GPTQ column sweep inside one 128-column block: fused group scale / zero
-// point, quantization, error compensation of the later columns of the block,
-// and the error block E for the lazy trailing update.
+// The GPTQ column sweep over one super-block of up to four 128-column blocks: fused
+// group scale / zero point, quantization, error compensation of the later columns of
+// the block, the error block E for the lazy trailing update, and, after each block,
+// that block's update of the rest of the super-block.
 //
 // GPTQ summary page: OBQ background (quantize one weight, then update the
 // remaining full-precision weights to compensate, in the direction given by the
@@ -9,13 +10,20 @@
 // the Cholesky factor U of the inverse give the updates).  Quantization concepts
 // guide: "Mapping values to fewer bits", "Choose granularity".
 //
-// Layout: a workgroup owns 16 rows of the block; each row is held by the 16
-// lanes of one DPP row, lane q holding columns q, q+16, ..., q+112 in registers
-// (column-cyclic, so the triangular work stays balanced).  The block's diagonal
+// Layout: a workgroup owns 16 rows; their values in the super-block's columns stay in
+// LDS for the whole launch.  In a block each row is held by the 16 lanes of one DPP
+// row, lane q holding columns q, q+16, ..., q+112 in registers (column-cyclic, so
+// the triangular work stays balanced).  The block's diagonal
 // 128 x 128 part of U is staged in LDS, permuted so that a lane reads its eight
 // coefficients of the next step with two 16-byte LDS reads (prefetched one step
 // ahead).  The quantization error of column j is broadcast along the row with
 // DPP row_newbcast; group min/max use DPP butterfly reductions.
+// After a block, its errors E (16 x 128, bf16 hi + lo, staged in LDS) update the rest
+// of the super-block in LDS, W[:, later] -= E U[block, later], on
+// v_mfma_f32_16x16x32_bf16 with three products (hi hi + hi lo + lo hi, fp32
+// accumulation), U staged 64 columns at a time in the LDS of the U block (free after
+// the steps) and read with transposing LDS reads.  Rows are independent, so no other
+// workgroup is involved.
 
 #include <utility>
 
@@ -24,6 +32,24 @@
 namespace gptq {
 
 constexpr int SSLOTS = QB / SL;     // columns per lane: q, q+16, ..., q+112
+constexpr int WL_LD = QSB + 4;      // LDS row pitch of the super-block's W (floats)
+constexpr int UT_N = 64;            // columns of U per update chunk
+constexpr int UT_RS = UT_N + 8;     // LDS row pitch of a U chunk (bf16): conflict-free transposed reads
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// B operand of v_mfma_f32_16x16x32_bf16 (32 k x 16 columns: lane l holds column
+// n0 + l % 16 at k = k0 + 8 (l / 16) .. + 7) from a [k][n] chunk, with two transposing
+// reads: in each 16-lane group lane j addresses k = k0 + 8 g + (j >> 2), columns
+// n0 + 4 (j & 3) .. + 3, and lane i receives column n0 + i at four consecutive k.
+GPTQ_DEV bf16x8_t ut_bfrag(const uint16_t* ut, int n0, int k0, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int k = k0 + 8 * g + (j >> 2), n = n0 + 4 * (j & 3);
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(ut + k * UT_RS + n));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(ut + (k + 4) * UT_RS + n));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 65504.f; }
 
@@ -49,30 +75,101 @@ GPTQ_DEV float row_max(float v) {
     return fmaxf(v, dpp_f<DPP_MIRROR>(v));
 }
 
+// One U chunk of an in-super-block update: rows b0 .. b0 + 127 (k), columns n0 .. n0 +
+// 63, hi and lo, into registers (thread t: rows (t + 256 m) / 8, 8 columns each); zero
+// past the super-block or past U.
+constexpr int NU = QB * UT_N / 8 / QT;   // 16-byte pieces per thread and half
+struct UChunk { u32x4_t h[NU], l[NU]; };
+
+GPTQ_DEV void load_uchunk(const SweepArgs& a, int64_t b0, int64_t n0, int tid, UChunk& u) {
+    const bool fast = (b0 + QB <= a.d_col) && (n0 + UT_N <= a.s1) && ((a.d_col & 7) == 0) &&
+                      ((reinterpret_cast<uintptr_t>(a.Uhi) & 15) == 0) &&
+                      ((reinterpret_cast<uintptr_t>(a.Ulo) & 15) == 0) && ((n0 & 7) == 0);
+#pragma unroll
+    for (int m = 0; m < NU; ++m) {
+        const int idx = tid + QT * m;
+        const int k = idx >> 3, c8 = (idx & 7) * 8;
+        const int64_t off = (b0 + k) * a.d_col + n0 + c8;
+        if (fast) {
+            u.h[m] = *reinterpret_cast<const u32x4_t*>(a.Uhi + off);
+            u.l[m] = *reinterpret_cast<const u32x4_t*>(a.Ulo + off);
+        } else {
+            uint32_t th[4] = {0u, 0u, 0u, 0u}, tl[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e) {
+                if (b0 + k < a.d_col && n0 + c8 + e < a.s1) {
+                    th[e >> 1] |= (uint32_t)a.Uhi[off + e] << (16 * (e & 1));
+                    tl[e >> 1] |= (uint32_t)a.Ulo[off + e] << (16 * (e & 1));
+                }
+            }
+            u.h[m] = u32x4_t{th[0], th[1], th[2], th[3]};
+            u.l[m] = u32x4_t{tl[0], tl[1], tl[2], tl[3]};
+        }
+    }
+}
+
 __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
-    __shared__ __attribute__((aligned(16))) float Up[QB][SL][SSLOTS];  // Up[j][q][i] = U[b0+j][b0+q+16i]
+    // Up[j][q][i] = U[b0+j][b0+q+16i] during the steps; a U chunk (hi, lo) during the updates
+    __shared__ __attribute__((aligned(16))) float Up[QB][SL][SSLOTS];
     __shared__ float invd[QB];                                         // 1 / U[b0+j][b0+j]
+    __shared__ __attribute__((aligned(16))) float Wl[SROWS][WL_LD];    // the super-block's W
     __shared__ __attribute__((aligned(16))) uint8_t cl[SROWS][QB];
     __shared__ __attribute__((aligned(16))) uint16_t ehs[SROWS][QB], els[SROWS][QB];   // E split, staged
     __shared__ int bad_any;
+    static_assert(2 * QB * UT_RS * 2 <= (int)sizeof(Up), "a U chunk fits in the U block's LDS");
+    uint16_t* const uth = reinterpret_cast<uint16_t*>(&Up[0][0][0]);
+    uint16_t* const utl = uth + QB * UT_RS;
 
     const int tid = threadIdx.x;
     const int q = tid & (SL - 1);
     const int rl = tid >> 4;
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t row = (int64_t)blockIdx.x * SROWS + rl;
     const bool rv = row < a.d_row;
-    const int nb = a.nb;
+    const int nsb = (int)(a.s1 - a.s0);
     const int G = a.group;
     const float fqmin = (float)a.qmin, fqmax = (float)a.qmax, fzoff = (float)a.zoff;
     if (tid == 0) bad_any = 0;
 
+    // the super-block's W for the workgroup's rows: thread t loads row t / 16,
+    // columns 4 (t % 16) + 64 m (16-byte loads when rows are aligned)
+    {
+        constexpr int NW = QSB / 64;
+        const float* src = a.Wws + (rv ? row : 0) * a.d_col + a.s0;
+        const bool vec = nsb == QSB && ((a.d_col & 3) == 0) && ((a.s0 & 3) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(a.Wws) & 15) == 0);
+        f32x4_t v[NW];
+#pragma unroll
+        for (int m = 0; m < NW; ++m) {
+            const int c = 4 * q + 64 * m;
+            if (vec) {
+                v[m] = rv ? *reinterpret_cast<const f32x4_t*>(src + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[m][e] = (rv && c + e < nsb) ? src[c + e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NW; ++m) *reinterpret_cast<f32x4_t*>(&Wl[rl][4 * q + 64 * m]) = v[m];
+    }
+
+    // s16f, r16f = 1 / s16f and the zero point zf of the current group; the code is
+    // rne(t) + zf clamped to [qmin, qmax], i.e. rne(t) clamped to [lo, hi]
+    float s16f = 1.f, r16f = 1.f, zf = 0.f;
+    bool bad = false;
+    if (G == 0 && rv) {
+        s16f = f16_bits_to_f32(a.scales[row * a.n_groups]);
+        r16f = 1.0f / s16f;
+        zf = f16_bits_to_f32(a.zeros[row * a.n_groups]) - fzoff;
+    }
+    float lo = fqmin - zf, hi = fqmax - zf;
+
+    for (int64_t b0 = a.s0; b0 < a.s1; b0 += QB) {
+    const int nb = (int)((a.s1 - b0) < QB ? (a.s1 - b0) : QB);
+    const int cb = (int)(b0 - a.s0);       // the block's first column in Wl
     float w[SSLOTS], e[SSLOTS];
     int cv[SSLOTS];
-    const float* wrow = a.Wws + (rv ? row : 0) * a.d_col + a.b0;
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) {
-        const int c = SL * i + q;
-        w[i] = (rv && c < nb) ? wrow[c] : 0.f;
         e[i] = 0.f;
         cv[i] = 0;
     }
@@ -86,20 +183,20 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         for (int v = 0; v < NV; ++v) {
             const int idx = tid + QT * v;       // float4 index: 32 per row of 128
             const int j = idx >> 5, c4 = (idx & 31) * 4;
-            uv[v] = *reinterpret_cast<const f32x4_t*>(a.U + (a.b0 + j) * a.d_col + a.b0 + c4);
+            uv[v] = *reinterpret_cast<const f32x4_t*>(a.U + (b0 + j) * a.d_col + b0 + c4);
         }
     } else {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int idx = tid + QT * v;
             const int j = idx >> 5, c4 = (idx & 31) * 4;
-            const float* src = a.U + (a.b0 + j) * a.d_col + a.b0 + c4;
+            const float* src = a.U + (b0 + j) * a.d_col + b0 + c4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) uv[v][e] = (j < nb && c4 + e < nb) ? src[e] : 0.f;
         }
     }
     // the reciprocal pivots: one division in each of the first 128 threads
-    const float udiag = (tid < nb) ? a.U[(a.b0 + tid) * a.d_col + a.b0 + tid] : 0.f;
+    const float udiag = (tid < nb) ? a.U[(b0 + tid) * a.d_col + b0 + tid] : 0.f;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int idx = tid + QT * v;
@@ -111,16 +208,17 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         }
     }
     if (tid < QB) invd[tid] = (tid < nb) ? 1.0f / udiag : 0.f;
-    // s16f, r16f = 1 / s16f and the zero point zf of the current group; the code is
-    // rne(t) + zf clamped to [qmin, qmax], i.e. rne(t) clamped to [lo, hi]
-    float s16f = 1.f, r16f = 1.f, zf = 0.f;
-    bool bad = false;
-    if (G == 0 && rv) {
-        s16f = f16_bits_to_f32(a.scales[row * a.n_groups]);
-        r16f = 1.0f / s16f;
-        zf = f16_bits_to_f32(a.zeros[row * a.n_groups]) - fzoff;
+    // the first U chunk of this block's update, in flight during the steps
+    UChunk uc;
+    if (b0 + QB < a.s1) load_uchunk(a, b0, b0 + QB, tid, uc);
+    // the block's W from LDS (updated by the earlier blocks of the super-block); the
+    // barrier before the U staging of the first block orders the W stores above
+    if (b0 == a.s0) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SSLOTS; ++i) {
+        const int c = SL * i + q;
+        w[i] = (c < nb) ? Wl[rl][cb + c] : 0.f;
     }
-    float lo = fqmin - zf, hi = fqmax - zf;
     __syncthreads();
     // U coefficients of the current and the next step, alternating by step parity
     float ucA[SSLOTS], ucB[SSLOTS];
@@ -194,8 +292,8 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                 zf = a.sym ? 0.f : fqmin - rintf(mn / s16f);
                 lo = fqmin - zf;
                 hi = fqmax - zf;
-                if (q == 0 && rv && a.b0 + j < a.d_col) {
-                    const int64_t g = (a.b0 + j) / G;
+                if (q == 0 && rv && b0 + j < a.d_col) {
+                    const int64_t g = (b0 + j) / G;
                     a.scales[row * a.n_groups + g] = f32_to_f16_bits(s16f);
                     a.zeros[row * a.n_groups + g] = f32_to_f16_bits(zf + fzoff);
                 }
@@ -252,10 +350,10 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         const int r = tid >> 4, c8 = (tid & 15) * 8;
         const int64_t grow = (int64_t)blockIdx.x * SROWS + r;
         if (grow < a.d_row) {
-            uint16_t* hrow = a.Ehi + grow * a.lde;
-            uint16_t* lrow = a.Elo + grow * a.lde;
-            if (nb == QB && (a.lde & 7) == 0 && ((reinterpret_cast<uintptr_t>(a.Ehi) & 15) == 0) &&
-                ((reinterpret_cast<uintptr_t>(a.Elo) & 15) == 0)) {
+            uint16_t* hrow = a.Ehi + grow * a.lde + cb;
+            uint16_t* lrow = a.Elo + grow * a.lde + cb;
+            if (nb == QB && (a.lde & 7) == 0 && ((reinterpret_cast<uintptr_t>(hrow) & 15) == 0) &&
+                ((reinterpret_cast<uintptr_t>(lrow) & 15) == 0)) {
                 *reinterpret_cast<u32x4_t*>(hrow + c8) = *reinterpret_cast<const u32x4_t*>(&ehs[r][c8]);
                 *reinterpret_cast<u32x4_t*>(lrow + c8) = *reinterpret_cast<const u32x4_t*>(&els[r][c8]);
             } else {
@@ -265,7 +363,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         // codes: two per byte (column 2k in the low nibble) or one per byte; thread t
         // writes 8 columns of row t / 16
         if (grow < a.d_row) {
-            uint8_t* crow = a.codes + grow * a.code_ld + a.b0 / per;
+            uint8_t* crow = a.codes + grow * a.code_ld + b0 / per;
             const bool whole = nb == QB && ((reinterpret_cast<uintptr_t>(crow) & (a.packed ? 3 : 7)) == 0);
             if (a.packed) {
                 uint32_t v = 0;
@@ -284,6 +382,39 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
             }
         }
     }
+
+    // the rest of the super-block: W[:, n0 ..] -= E U[b0 .. b0 + 127, n0 ..], 64 columns of
+    // U at a time; wave w updates 16 rows x 16 columns of each chunk
+    for (int64_t n0 = b0 + QB; n0 < a.s1; n0 += UT_N) {
+#pragma unroll
+        for (int m = 0; m < NU; ++m) {
+            const int idx = tid + QT * m;
+            const int k = idx >> 3, c8 = (idx & 7) * 8;
+            *reinterpret_cast<u32x4_t*>(uth + k * UT_RS + c8) = uc.h[m];
+            *reinterpret_cast<u32x4_t*>(utl + k * UT_RS + c8) = uc.l[m];
+        }
+        __syncthreads();
+        // the next chunk, in flight during this one's products
+        if (n0 + UT_N < a.s1) load_uchunk(a, b0, n0 + UT_N, tid, uc);
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < QB; kk += 32) {
+            const int mr = lane & 15, ka = kk + 8 * (lane >> 4);
+            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&ehs[mr][ka]);
+            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&els[mr][ka]);
+            const bf16x8_t bh = ut_bfrag(uth, 16 * wave, kk, lane);
+            const bf16x8_t bl = ut_bfrag(utl, 16 * wave, kk, lane);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        }
+        // D layout: lane l holds column l % 16, rows 4 (l / 16) .. + 3
+        const int nc = (int)(n0 - a.s0) + 16 * wave + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Wl[4 * (lane >> 4) + r][nc] -= acc[r];
+        __syncthreads();
+    }
+    }   // blocks of the super-block
 }
 
 gptq_status sweep_launch(const SweepArgs& a, hipStream_t s) {
