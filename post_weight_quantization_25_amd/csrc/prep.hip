@@ -869,8 +869,15 @@ static gptq_status cholinv(PrepCtx& c) {
     int64_t h = PNB;
     while (2 * h < d) h *= 2;
     const int64_t m = d - h;                 // 0 < m <= h
+    // the trailing block [h, d) is split the same way at h + h2 when it is larger than
+    // one diagonal block: its leading part's inverse and T2 = L[h + h2 ..][h .. h + h2)
+    // X[h .. h + h2) also run on the auxiliary stream
+    int64_t h2 = 0;
+    if (m > PNB) { h2 = PNB; while (2 * h2 < m) h2 *= 2; }
+    const int64_t m2 = m - h2;               // 0 < m2 <= h2 when h2 > 0
     double* T11 = c.T;                       // h * h doubles: X11's levels, then T (m x h)
-    double* T22 = c.T + h * h;               // m * m doubles: X22's levels
+    double* T2b = c.T + h * h;               // h2 * h2: the levels of [h, h + h2), then T2 (m2 x h2)
+    double* T22 = T2b + h2 * h2;             // m2 * m2 (or m * m): the levels of the last block
 
     AuxStream* aux = nullptr;
     if ((st = aux_stream(aux)) != GPTQ_OK) return st;
@@ -892,6 +899,20 @@ static gptq_status cholinv(PrepCtx& c) {
         if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
         return GPTQ_OK;
     };
+    const int64_t s2 = h + h2;
+    const int64_t fork_step2 = std::max<int64_t>(s2 / PNB - 2, fork_step);
+    auto fork2 = [&]() -> gptq_status {
+        if (hipEventRecord(aux->fork, c.s) != hipSuccess || hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess)
+            return GPTQ_ERR_HIP;
+        gptq_status s3;
+        if ((s3 = trtri_block(ca, h, h2, T2b, AUX_MAX_WG)) != GPTQ_OK) return s3;
+        // T2 = L[s2 ..][h .. s2) X[h .. s2)   (m2 x h2, lower triangular X block)
+        if ((s3 = gemm(ca, T2b, h2, c.A + s2 * d + h, d, c.X + h * d + h, d, (int)m2, (int)h2, (int)h2, 1.0, 0.0,
+                       G_TRI_B, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+            return s3;
+        if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
+        return GPTQ_OK;
+    };
     if (fork_step < 0 && (st = fork()) != GPTQ_OK) return st;
     for (int64_t k0 = 0; k0 < d; k0 += PNB) {
         const int n = (int)std::min<int64_t>(PNB, d - k0);
@@ -906,9 +927,19 @@ static gptq_status cholinv(PrepCtx& c) {
                        (int)std::min<int64_t>(PNB, rest), (int)(k0 / PNB) + 1)) != GPTQ_OK)
             return st;
         if (k0 / PNB == fork_step && (st = fork()) != GPTQ_OK) return st;
+        if (h2 > 0 && k0 / PNB == fork_step2 && (st = fork2()) != GPTQ_OK) return st;
     }
-    if ((st = trtri_block(c, h, m, T22)) != GPTQ_OK) return st;
-    if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
+    if (h2 > 0) {
+        // the last block [s2, d), then X[s2 ..][h .. s2) = -X[s2 ..][s2 ..] T2
+        if ((st = trtri_block(c, s2, m2, T22)) != GPTQ_OK) return st;
+        if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
+        if ((st = gemm(c, c.X + s2 * d + h, d, c.X + s2 * d + s2, d, T2b, h2, (int)m2, (int)h2, (int)m2, -1.0, 0.0,
+                       G_TRI_A)) != GPTQ_OK)
+            return st;
+    } else {
+        if ((st = trtri_block(c, h, m, T22)) != GPTQ_OK) return st;
+        if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
+    }
     // X21 = -X22 T   (X22 lower triangular)
     return gemm(c, c.X + h * d, d, c.X + h * d + h, d, T11, h, (int)m, (int)h, (int)m, -1.0, 0.0, G_TRI_A);
 }
@@ -916,8 +947,9 @@ static gptq_status cholinv(PrepCtx& c) {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static size_t t_bytes(int64_t d) {
-    // product scratch: h * h doubles for the leading block's levels and T (m x h), then
-    // m * m for the trailing block's levels (m = d - h <= h), h * h + m * m <= d * d
+    // product scratch: h * h doubles for the leading block's levels and T (m x h), h2 * h2
+    // for the trailing block's leading part and T2, m2 * m2 for its last part
+    // (h2 + m2 = m = d - h <= h), h * h + h2 * h2 + m2 * m2 <= h * h + m * m <= d * d
     return (size_t)d * d * sizeof(double);
 }
 
