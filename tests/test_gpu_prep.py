@@ -25,7 +25,10 @@ def _gpu_u(H32, percdamp=0.01):
     return U.cpu().numpy(), int(info.item())
 
 
-@pytest.mark.parametrize("d", [1, 37, 64, 65, 130, 200, 520, 1024])
+# sizes: one block, ragged single split (65, 130, 520), the trailing block split again
+# (200, 1024), and 3000 (a ragged trailing block, and products large enough for the
+# capped grid of the overlapped inverse)
+@pytest.mark.parametrize("d", [1, 37, 64, 65, 130, 200, 520, 1024, 3000])
 def test_prep_parity(d):
     log(f"prep parity d={d}")
     H32 = _h(d, max(2 * d, 64), 3)
