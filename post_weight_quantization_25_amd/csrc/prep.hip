@@ -55,17 +55,18 @@ __global__ __launch_bounds__(1024) void prep_lambda_kernel(const float* H, int64
     }
 }
 
-// A[i][j] = H[d-1-i][d-1-j] + lambda [i == j] for j <= i; X = 0.
-__global__ void prep_build_kernel(const float* H, int64_t d, const double* lam, double* A, double* X) {
+// A[i][j] = H[d-1-i][d-1-j] + lambda [i == j] for j <= i.  Neither triangle above the
+// diagonal is ever read: the diagonal 64 x 64 blocks of L and X are written whole (zeros
+// above the diagonal) by the diagonal routine, the products clip their k ranges to
+// those blocks and the ones below, and the output reads the lower part of X only; so X
+// needs no initialization.
+__global__ void prep_build_kernel(const float* H, int64_t d, const double* lam, double* A) {
     const int64_t i = blockIdx.y;
     const double l = *lam;
-    for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j < d; j += (int64_t)gridDim.x * blockDim.x) {
-        X[i * d + j] = 0.0;
-        if (j <= i) {
-            double v = (double)H[(d - 1 - i) * d + (d - 1 - j)];
-            if (i == j) v += l;
-            A[i * d + j] = v;
-        }
+    for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j <= i; j += (int64_t)gridDim.x * blockDim.x) {
+        double v = (double)H[(d - 1 - i) * d + (d - 1 - j)];
+        if (i == j) v += l;
+        A[i * d + j] = v;
     }
 }
 
@@ -976,7 +977,7 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     prep_lambda_kernel<<<1, 1024, 0, s>>>(H, d, percdamp, lam, info, c.flag);
     GPTQ_LAUNCH_CHECK();
     dim3 gb((unsigned)((d + 255) / 256 < 64 ? (d + 255) / 256 : 64), (unsigned)d);
-    prep_build_kernel<<<gb, 256, 0, s>>>(H, d, lam, c.A, c.X);
+    prep_build_kernel<<<gb, 256, 0, s>>>(H, d, lam, c.A);
     GPTQ_LAUNCH_CHECK();
     gptq_status st;
     {

@@ -98,3 +98,23 @@ def test_hessian_empty_is_noop():
     g.hessian_accumulate(H, torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()
     assert torch.all(H == 3.0)
+
+
+@pytest.mark.parametrize("n,d", [(20000, 512), (4096, 1000)])
+def test_hessian_ignores_workspace_contents(n, d):
+    """The split partials' workspace holds all-ones bytes (NaN floats) before the call:
+    the reduction stores only what the main kernel wrote (the sub-tiles below the
+    diagonal of a diagonal tile are never written and never stored), so H is finite and
+    matches."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    x, xf = _x(n, d, "bf16", 11)
+    Ho = o.hessian([xf])
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    ws = torch.full((g.hessian_workspace_size(n, d),), 255, dtype=torch.uint8, device="cuda")
+    g.hessian_accumulate(H, dev_tensor(x, "bf16"), ws=ws)
+    torch.cuda.synchronize()
+    Hg = H.cpu().numpy()
+    assert np.all(np.isfinite(Hg))
+    assert np.array_equal(Hg, Hg.T)
+    assert _err(Hg, Ho) <= _tol(n, "bf16")
