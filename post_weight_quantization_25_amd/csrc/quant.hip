@@ -373,6 +373,9 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
 
 // --------------------------------------------------------------------------
 // Dequantization: W_out = S16 (u - z).
+// Fast path (8 consecutive columns per thread, one group): one 4-byte (two codes per
+// byte) or 8-byte load of codes, one scale / zero pair, 16-byte stores; it needs d_col
+// and the group size to be multiples of 8 and aligned rows.  Otherwise element by element.
 template <int BITS, gptq_dtype OT>
 __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
                                int64_t d_col, int G, void* out) {
@@ -380,9 +383,45 @@ __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, con
     const int64_t chunks = (d_col + 7) / 8;
     const int64_t code_ld = (BITS <= 4) ? d_col / 2 : d_col;
     const int n_groups = (G == 0) ? 1 : (int)(d_col / G);
+    constexpr int OB = (OT == GPTQ_F32) ? 4 : 2;     // output bytes per value
+    const bool fast = (d_col % 8 == 0) && (G % 8 == 0) &&
+                      ((reinterpret_cast<uintptr_t>(codes) & 7) == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0) &&
+                      ((code_ld * row) % ((BITS <= 4) ? 4 : 8) == 0) && ((d_col * OB) % 16 == 0);
     for (int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ch < chunks; ch += (int64_t)gridDim.x * blockDim.x) {
         const int64_t c0 = ch * 8;
         float v[8];
+        if (fast) {
+            uint32_t u[8];
+            if constexpr (BITS <= 4) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + row * code_ld + c0 / 2);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] = (w >> (4 * e)) & 0xFu;
+            } else {
+                const uint2 w = *reinterpret_cast<const uint2*>(codes + row * code_ld + c0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { u[e] = (w.x >> (8 * e)) & 0xFFu; u[4 + e] = (w.y >> (8 * e)) & 0xFFu; }
+            }
+            const int g = (G == 0) ? 0 : (int)(c0 / G);
+            const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
+            const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = sc * ((float)u[e] - z);
+            if constexpr (OT == GPTQ_F32) {
+                f32x4_t* o = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + row * d_col + c0);
+                o[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+                o[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+            } else {
+                uint32_t p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = (OT == GPTQ_BF16) ? f32_to_bf16_bits(v[2 * e]) : f32_to_f16_bits(v[2 * e]);
+                    const uint32_t hi = (OT == GPTQ_BF16) ? f32_to_bf16_bits(v[2 * e + 1]) : f32_to_f16_bits(v[2 * e + 1]);
+                    p[e] = lo | (hi << 16);
+                }
+                *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + row * d_col + c0) = u32x4_t{p[0], p[1], p[2], p[3]};
+            }
+            continue;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int64_t c = c0 + e;
@@ -395,9 +434,9 @@ __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, con
                 u = codes[row * code_ld + c];
             }
             const int g = (G == 0) ? 0 : (int)(c / G);
-            const float s = f16_bits_to_f32(scales[row * n_groups + g]);
+            const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
             const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
-            v[e] = s * ((float)u - z);
+            v[e] = sc * ((float)u - z);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
