@@ -67,11 +67,37 @@ __global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64
     zeros[row] = f32_to_f16_bits(zf + (float)ZOFF);
 }
 
-// W (any dtype) -> fp32 working copy; flags non-finite values.
+// W (any dtype) -> fp32 working copy; flags non-finite values.  Eight values per
+// thread and step with 16-byte accesses when both arrays are 16-byte aligned; the
+// rest (or everything, unaligned) one value at a time.
 template <gptq_dtype DT>
 __global__ void convert_kernel(const void* W, int64_t n, float* out, int32_t* info) {
     int bad = 0;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nth = (int64_t)gridDim.x * blockDim.x;
+    const bool vec = ((reinterpret_cast<uintptr_t>(W) & 15) == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+    const int64_t n8 = vec ? n / 8 : 0;
+    for (int64_t i = tid; i < n8; i += nth) {
+        float v[8];
+        if constexpr (DT == GPTQ_F32) {
+            const f32x4_t a = reinterpret_cast<const f32x4_t*>(W)[2 * i], b = reinterpret_cast<const f32x4_t*>(W)[2 * i + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+        } else {
+            const u32x4_t h = reinterpret_cast<const u32x4_t*>(W)[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t lo = (uint16_t)(h[e] & 0xFFFFu), hi = (uint16_t)(h[e] >> 16);
+                v[2 * e] = (DT == GPTQ_BF16) ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
+                v[2 * e + 1] = (DT == GPTQ_BF16) ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bad |= !isfinite(v[e]);
+        f32x4_t* o = reinterpret_cast<f32x4_t*>(out) + 2 * i;
+        o[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+        o[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+    }
+    for (int64_t i = 8 * n8 + tid; i < n; i += nth) {
         const float v = load_as_f32<DT>(W, i);
         if (!isfinite(v)) bad = 1;
         out[i] = v;
@@ -288,9 +314,29 @@ size_t quant_ws_bytes(int64_t d_row, int64_t d_col) {
 }
 
 // U -> bf16 hi + lo (hi = bf16(u), lo = bf16(u - hi)), once per call: every workgroup
-// of the trailing products reads the split instead of forming it again.
+// of the trailing products reads the split instead of forming it again.  Eight values
+// per thread and step with 16-byte accesses when the arrays are aligned.
 __global__ void split_u_kernel(const float* U, int64_t n, uint16_t* hi, uint16_t* lo) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nth = (int64_t)gridDim.x * blockDim.x;
+    const bool vec = ((reinterpret_cast<uintptr_t>(U) & 15) == 0) && ((reinterpret_cast<uintptr_t>(hi) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(lo) & 15) == 0);
+    const int64_t n8 = vec ? n / 8 : 0;
+    for (int64_t i = tid; i < n8; i += nth) {
+        const f32x4_t a = reinterpret_cast<const f32x4_t*>(U)[2 * i], b = reinterpret_cast<const f32x4_t*>(U)[2 * i + 1];
+        const float u[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint16_t h0 = f32_to_bf16_bits(u[2 * e]), h1 = f32_to_bf16_bits(u[2 * e + 1]);
+            const uint16_t l0 = f32_to_bf16_bits(u[2 * e] - bf16_bits_to_f32(h0));
+            const uint16_t l1 = f32_to_bf16_bits(u[2 * e + 1] - bf16_bits_to_f32(h1));
+            ph[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            pl[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        reinterpret_cast<u32x4_t*>(hi)[i] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+        reinterpret_cast<u32x4_t*>(lo)[i] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+    }
+    for (int64_t i = 8 * n8 + tid; i < n; i += nth) {
         const float u = U[i];
         const uint16_t h = f32_to_bf16_bits(u);
         hi[i] = h;
@@ -330,7 +376,7 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     fill_i32(info, 1, 0, s);
     GPTQ_LAUNCH_CHECK();
     const int64_t n = d_row * d_col;
-    const unsigned cgrid = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+    const unsigned cgrid = (unsigned)std::min<int64_t>((n / 8 + 255) / 256 + 1, 4096);
     switch (w_dtype) {
         case GPTQ_F32: convert_kernel<GPTQ_F32><<<cgrid, 256, 0, s>>>(W, n, Wws, info); break;
         case GPTQ_BF16: convert_kernel<GPTQ_BF16><<<cgrid, 256, 0, s>>>(W, n, Wws, info); break;
@@ -346,7 +392,7 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     SweepArgs sa;
     {
         const int64_t nu = d_col * d_col;
-        const unsigned ug = (unsigned)std::min<int64_t>((nu + 255) / 256, 8192);
+        const unsigned ug = (unsigned)std::min<int64_t>((nu / 8 + 255) / 256 + 1, 4096);
         split_u_kernel<<<ug, 256, 0, s>>>(U, nu, Uhi, Ulo);
         GPTQ_LAUNCH_CHECK();
     }
