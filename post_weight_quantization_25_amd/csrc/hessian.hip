@@ -226,20 +226,28 @@ GPTQ_DEV void mfma_slice(const Frags& f, f32x16_t (&acc)[HB_FA][HB_FB]) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Scheduling hint for one region of the pipelined loop, which holds the 12 LDS reads
-// of the next slice and the 8 MFMAs of the current one: issue them interleaved (one
-// read per MFMA, then two), so that the LDS port and the matrix core work at the
-// same time instead of in bursts.
+// Scheduling hint for one region of the pipelined loop, which holds the LDS reads of
+// the next slice and the MFMAs of the current one (12 and 8 with eight waves, 16 and
+// 16 with four): issue them interleaved, so that the LDS port and the matrix core work
+// at the same time instead of in bursts.
 GPTQ_DEV void interleave_reads_mfma() {
-    static_assert(HB_FA * HB_FB == 8 && 2 * (HB_FA + HB_FB) == 12, "pattern assumes 8 MFMAs, 12 reads");
-    static_for<0, 4>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    });
-    static_for<0, 4>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    });
+    constexpr int NR = 2 * (HB_FA + HB_FB), NM = HB_FA * HB_FB;   // LDS reads, MFMAs
+    static_assert((NR == 12 && NM == 8) || NR == NM, "interleave pattern for this wave layout");
+    if constexpr (NR == 12 && NM == 8) {
+        static_for<0, 4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        });
+        static_for<0, 4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        });
+    } else {
+        static_for<0, NM>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        });
+    }
 }
 
 // The MFMAs of one LDS stage for one wave (both slices), used by the edge path.
