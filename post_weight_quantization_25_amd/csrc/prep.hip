@@ -147,8 +147,18 @@ GPTQ_DEV double rsqrt_pos(double x) {
 // and the tile columns right of it, which waves 2 and 3 apply while wave 0 factors
 // round P + 1 (those columns are disjoint from the sub-panel being factored).  Every
 // element receives the same updates in the same order as with whole-round updates.
+// flag (may be null): once X_kk is stored it is published for other workgroups of
+// the launch (release fence, then *flag = step with an agent-scope store), before L_kk
+// is stored; after a failed pivot it is published too (info then holds the failure).
+GPTQ_DEV void publish_block(int* flag, int step) {
+    if (flag == nullptr) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double* A, double* X, int64_t d,
-                         int64_t k0, int n, int32_t* info) {
+                         int64_t k0, int n, int32_t* info, int* flag = nullptr, int step = 0) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int& fail_s = *fail_p;
 
@@ -234,6 +244,7 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
     });
     if (fail_s) {
         if (tid == 0 && fail_s <= n && *info == 0) *info = (int32_t)(k0 + fail_s);
+        publish_block(flag, step);
         return;
     }
     // X_kk = L_kk^-1: the inverses of the eight 8 x 8 diagonal blocks (the first seven
@@ -252,7 +263,8 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
                 for (int k = 0; k < 8; ++k) acc += a[(q0 + rr) * DLD + p0 + k] * xs[(p0 + k) * DLD + p0 + cc];
                 ts[idx] = acc;
             }
-            __syncthreads();
+            // pair m = idx / 64 = wave: the same wave reads its T (LDS is in order per wave)
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             for (int idx = tid; idx < np * 64; idx += 256) {
                 const int m = idx >> 6, rr = (idx >> 3) & 7, cc = idx & 7, p0 = 16 * m, q0 = p0 + 8;
                 double acc = 0.0;
@@ -277,7 +289,9 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
                 for (int e = 0; e < 4; ++e)
                     ts[(m * b + ti * 16 + 4 * e + (lane >> 4)) * 32 + tj * 16 + (lane & 15)] = acc[e];
             }
-            __syncthreads();
+            // b = 16: one tile per pair, the same wave reads it; b = 32: tiles are shared
+            if (tpb == 1) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            else __syncthreads();
             for (int t = wave; t < ntile; t += 4) {           // X[q][p] = -X[q][q] T_m
                 const int m = t / (tpb * tpb), ti = (t / tpb) % tpb, tj = t % tpb;
                 const int p0 = 2 * m * b, q0 = p0 + b;
@@ -294,27 +308,45 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
             __syncthreads();
         }
     }
-    if (n == PNB && (d & 1) == 0) {
-        // 16-byte stores, 32 threads per row (whole rows per instruction); the strictly
-        // upper part of L's block is written as 0 (it is never read)
-        double2 vl[8], vx[8];
+    // X_kk first (the workgroups waiting for this block read only X_kk), published, then
+    // L_kk; 16-byte stores of whole rows (32 threads per row) for a full block.  The
+    // strictly upper part of L's block is written as 0 (it is never read).
+    const bool vec = n == PNB && (d & 1) == 0;
+    if (vec) {
+        double2 vx[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int r = (tid >> 5) + 8 * q, c = 2 * (tid & 31);
-            vl[q] = double2{c <= r ? a[r * DLD + c] : 0.0, c + 1 <= r ? a[r * DLD + c + 1] : 0.0};
             vx[q] = double2{xs[r * DLD + c], xs[r * DLD + c + 1]};
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int r = (tid >> 5) + 8 * q, c = 2 * (tid & 31);
-            *reinterpret_cast<double2*>(A + (k0 + r) * d + k0 + c) = vl[q];
             *reinterpret_cast<double2*>(X + (k0 + r) * d + k0 + c) = vx[q];
         }
     } else {
         for (int idx = tid; idx < n * n; idx += 256) {
             const int r = idx / n, c = idx % n;
-            if (c <= r) A[(k0 + r) * d + k0 + c] = a[r * DLD + c];
             X[(k0 + r) * d + k0 + c] = xs[r * DLD + c];
+        }
+    }
+    publish_block(flag, step);
+    if (vec) {
+        double2 vl[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = (tid >> 5) + 8 * q, c = 2 * (tid & 31);
+            vl[q] = double2{c <= r ? a[r * DLD + c] : 0.0, c + 1 <= r ? a[r * DLD + c + 1] : 0.0};
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = (tid >> 5) + 8 * q, c = 2 * (tid & 31);
+            *reinterpret_cast<double2*>(A + (k0 + r) * d + k0 + c) = vl[q];
+        }
+    } else {
+        for (int idx = tid; idx < n * n; idx += 256) {
+            const int r = idx / n, c = idx % n;
+            if (c <= r) A[(k0 + r) * d + k0 + c] = a[r * DLD + c];
         }
     }
 }
@@ -629,14 +661,10 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
                     a[r * DLD + cc] = v;
                 }
         __syncthreads();
-        diag_block(a, a + PNB * DLD, a + 2 * PNB * DLD, &fail_s, g.fA, g.fX, g.fd, g.k1, g.n1, g.info);
-        if (g.flags & G_PANEL1) {
-            // publish the factored block and its inverse (also after a failed pivot, so
-            // that no panel workgroup waits in vain; info then already holds the failure)
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __syncthreads();
-            if (tid == 0) __hip_atomic_store(g.flag, g.step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        // the routine publishes the block's inverse to the panel workgroups (also after a
+        // failed pivot, so that none waits in vain; info then holds the failure)
+        diag_block(a, a + PNB * DLD, a + 2 * PNB * DLD, &fail_s, g.fA, g.fX, g.fd, g.k1, g.n1, g.info,
+                   (g.flags & G_PANEL1) ? g.flag : nullptr, g.step);
         return;
     }
     if constexpr (FUSED) if (panel) {
