@@ -208,6 +208,22 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
 #pragma unroll
                 for (int k = 0; k < 8; ++k) a[r * DLD + c0 + k] = x[k];
             }
+            if constexpr (c0 == PNB - 8) {
+                // the last sub-panel's 8 x 8 inverse, from the factor and reciprocal pivots
+                // in registers (lane c < 8: column c); the earlier ones are formed by wave 1
+                if (lane < 8) {
+                    double y[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        double v = (i == lane) ? 1.0 : 0.0;
+#pragma unroll
+                        for (int k = 0; k < i; ++k) v -= t[i][k] * y[k];
+                        y[i] = v * rd[i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xs[(c0 + i) * DLD + c0 + lane] = (i >= lane) ? y[i] : 0.0;
+                }
+            }
             if (lane == 0 && f) fail_s = f;
         } else if constexpr (c0 == 0) {
             // meanwhile: the inverse starts as zero (the other three waves)
@@ -247,11 +263,9 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
         publish_block(flag, step);
         return;
     }
-    // X_kk = L_kk^-1: the inverses of the eight 8 x 8 diagonal blocks (the first seven
-    // were formed during the rounds), then recursive doubling
-    // X[q][p] = -X[q][q] (L[q][p] X[p][p]) for block sizes 8, 16, 32
-    if (wave == 1 && lane < 8) diag_inv8(a, xs, PNB - 8, lane);
-    __syncthreads();
+    // X_kk = L_kk^-1: the inverses of the eight 8 x 8 diagonal blocks were formed during
+    // the rounds; recursive doubling X[q][p] = -X[q][q] (L[q][p] X[p][p]) for block
+    // sizes 8, 16, 32
     for (int b = 8; b < PNB; b *= 2) {
         const int np = PNB / (2 * b);
         if (b == 8) {
