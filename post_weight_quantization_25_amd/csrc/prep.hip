@@ -584,6 +584,9 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
     const int m0 = mi * GD_BM, n0 = nj * GD_BM;
     const bool diag0 = FUSED && (g.flags & G_DIAG0) && mi == 0 && nj == 0 && bz == 0;
     if (m0 >= g.M) return;
+    // the next diagonal block heads the factorization chain: its waves take issue
+    // priority over the update tiles that share their compute unit
+    if (diag0) __builtin_amdgcn_s_setprio(3);
     int kb = 0, ke = g.K;
     if (g.flags & G_TRI_A) ke = min(ke, m0 + GD_BM);           // A lower: A[m][k] = 0 for k > m
     if (g.flags & G_TRI_B) {
@@ -604,9 +607,19 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
     double* cbase = g.C + (int64_t)(m0 + wr * 32 + (lane >> 4)) * g.ldc + n0 + wc * 32 + (lane & 15);
     auto off = [&](int i, int j, int e) { return (int64_t)(i * 16 + 4 * e) * g.ldc + j * 16; };
     // C of a whole tile, loaded after the products (loading it before them measured
-    // slower: it competes with the operand loads of the first chunks)
+    // slower: it competes with the operand loads of the first chunks), except for the
+    // next diagonal block, whose load latency would add to the chain
     double cold[2][2][4];
     const bool pre = full && g.beta != 0.0;
+    auto load_c = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cold[i][j][e] = cbase[off(i, j, e)];
+    };
+    if (pre && diag0) load_c();
 
     const int nch = (ke > kb) ? (ke - kb + GD_BK - 1) / GD_BK : 0;
     double2 va[4], vb[4];
@@ -647,14 +660,7 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
         }
         __syncthreads();
     }
-    if (pre) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) cold[i][j][e] = cbase[off(i, j, e)];
-    }
+    if (pre && !diag0) load_c();
     if constexpr (FUSED) if (diag0) {
         // updated diagonal block -> a[] (lower part; upper 0, identity padding), factor
         double* a = lds;
@@ -714,6 +720,7 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
         }
         __syncthreads();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __builtin_amdgcn_s_setprio(2);   // from here the panel is on the chain
         constexpr int PV = 64 * PNB / 2 / 256;      // double2 per thread
         double2 vx[PV];
 #pragma unroll
@@ -823,6 +830,7 @@ static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int
     const int ntm = (M + GD_BM - 1) / GD_BM, ntn = (N + GD_BM - 1) / GD_BM;
     GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch,
             c.A, c.X, c.d, k1, n1, c.info, ntm, ntn, c.flag, step, 0, 0};
+    if ((flags & G_LOWER_C) && N != M) return GPTQ_ERR_INVALID_ARG;
     const int ntiles = (flags & G_LOWER_C) ? ntm * (ntm + 1) / 2 : ntm * ntn;
     dim3 grid((unsigned)ntiles, 1, nbatch);
     if (max_wg > 0 && (int64_t)ntiles * nbatch > max_wg && !(flags & (G_DIAG0 | G_PANEL1))) {
@@ -903,7 +911,9 @@ static gptq_status aux_stream(AuxStream*& out) {
 // Block 0 and its panel have launches of their own; every later diagonal block and
 // its panel are finished inside the trailing update of the step before (tile (0, 0)
 // factors the block, the tiles below it apply its inverse), so each step of the
-// chain is one launch.
+// chain is one launch.  (Deferring the trailing update to blocks of 256 columns, so
+// that each step inside a block updates only the rest of that block, measured
+// slower: the rank-256 update then lies on the chain.)
 // The inverse is split at h, the largest 64 * 2^i below d: as soon as the first h
 // columns of L are final, the inverse X11 of the leading h x h block and the product
 // T = L21 X11 run on the auxiliary stream, beside the remaining (latency-bound)
