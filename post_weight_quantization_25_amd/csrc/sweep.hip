@@ -81,8 +81,9 @@ GPTQ_DEV float row_max(float v) {
 constexpr int NU = QB * UT_N / 8 / QT;   // 16-byte pieces per thread and half
 struct UChunk { u32x4_t h[NU], l[NU]; };
 
+template <bool FULL>
 GPTQ_DEV void load_uchunk(const SweepArgs& a, int64_t b0, int64_t n0, int tid, UChunk& u) {
-    const bool fast = (b0 + QB <= a.d_col) && (n0 + UT_N <= a.s1) && ((a.d_col & 7) == 0) &&
+    const bool fast = FULL || (b0 + QB <= a.d_col) && (n0 + UT_N <= a.s1) && ((a.d_col & 7) == 0) &&
                       ((reinterpret_cast<uintptr_t>(a.Uhi) & 15) == 0) &&
                       ((reinterpret_cast<uintptr_t>(a.Ulo) & 15) == 0) && ((n0 & 7) == 0);
 #pragma unroll
@@ -107,13 +108,50 @@ GPTQ_DEV void load_uchunk(const SweepArgs& a, int64_t b0, int64_t n0, int tid, U
     }
 }
 
+// Workgroup barrier that orders LDS accesses only (every barrier of the sweep guards
+// LDS data): global loads issued before it stay in flight across it.
+GPTQ_DEV void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A block's diagonal 128 x 128 part of U into registers, in the order of its LDS copy:
+// thread t holds the (row j, lane q) pairs p = t + QT m, each as the eight values
+// U[b0 + j][b0 + q + 16 i] that lane q uses in step j (zero past nb), and, in the first
+// 128 threads, the pivot U[b0 + t][b0 + t].
+constexpr int NPAIR = QB * SL / QT;
+struct UDiag { float v[NPAIR][SSLOTS]; float piv; };
+
+template <bool FULL>
+GPTQ_DEV void load_udiag(const SweepArgs& a, int64_t b0, int nb, int tid, UDiag& u) {
+#pragma unroll
+    for (int m = 0; m < NPAIR; ++m) {
+        const int pr = tid + QT * m;
+        const int j = pr >> 4, qq = pr & (SL - 1);
+        const float* src = a.U + (b0 + j) * a.d_col + b0 + qq;
+#pragma unroll
+        for (int i = 0; i < SSLOTS; ++i) u.v[m][i] = (FULL || (j < nb && qq + SL * i < nb)) ? src[SL * i] : 0.f;
+    }
+    u.piv = (tid < nb) ? a.U[(b0 + tid) * a.d_col + b0 + tid] : 0.f;
+}
+
+// U chunks of one block's update of the rest of the super-block (at most QSB - QB columns)
+constexpr int NCH = (QSB - QB) / UT_N;
+
+// FULL: a whole super-block with every row, block and pointer aligned for 16-byte
+// accesses (checked on the host), so that every load and store takes its vector form
+// with no edge code around it.
+template <bool FULL>
 __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     // Up[j][q][i] = U[b0+j][b0+q+16i] during the steps; a U chunk (hi, lo) during the updates
     __shared__ __attribute__((aligned(16))) float Up[QB][SL][SSLOTS];
     __shared__ float invd[QB];                                         // 1 / U[b0+j][b0+j]
     __shared__ __attribute__((aligned(16))) float Wl[SROWS][WL_LD];    // the super-block's W
     __shared__ __attribute__((aligned(16))) uint8_t cl[SROWS][QB];
-    __shared__ __attribute__((aligned(16))) uint16_t ehs[SROWS][QB], els[SROWS][QB];   // E split, staged
+    // E split, staged; rows padded by 16 bytes so that the 16 rows of an operand read
+    // fall on distinct banks
+    __shared__ __attribute__((aligned(16))) uint16_t ehs[SROWS][QB + 8], els[SROWS][QB + 8];
     __shared__ int bad_any;
     static_assert(2 * QB * UT_RS * 2 <= (int)sizeof(Up), "a U chunk fits in the U block's LDS");
     uint16_t* const uth = reinterpret_cast<uint16_t*>(&Up[0][0][0]);
@@ -135,7 +173,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     {
         constexpr int NW = QSB / 64;
         const float* src = a.Wws + (rv ? row : 0) * a.d_col + a.s0;
-        const bool vec = nsb == QSB && ((a.d_col & 3) == 0) && ((a.s0 & 3) == 0) &&
+        const bool vec = FULL || nsb == QSB && ((a.d_col & 3) == 0) && ((a.s0 & 3) == 0) &&
                          ((reinterpret_cast<uintptr_t>(a.Wws) & 15) == 0);
         f32x4_t v[NW];
 #pragma unroll
@@ -163,6 +201,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     }
     float lo = fqmin - zf, hi = fqmax - zf;
 
+    UDiag ud;
     for (int64_t b0 = a.s0; b0 < a.s1; b0 += QB) {
     const int nb = (int)((a.s1 - b0) < QB ? (a.s1 - b0) : QB);
     const int cb = (int)(b0 - a.s0);       // the block's first column in Wl
@@ -173,53 +212,32 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         e[i] = 0.f;
         cv[i] = 0;
     }
-    // stage U's diagonal block: all loads of a thread first (16-byte loads when rows
-    // are 16-byte aligned), then the permuted LDS stores
-    constexpr int NV = QB * QB / 4 / QT;   // float4 per thread
-    f32x4_t uv[NV];
-    const bool vec = nb == QB && ((a.d_col & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.U) & 15) == 0);
-    if (vec) {
+    // stage U's diagonal block (loaded ahead, during the previous block, except for
+    // the first block) permuted into Up, and the reciprocal pivots
+    if (b0 == a.s0) load_udiag<FULL>(a, b0, nb, tid, ud);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int idx = tid + QT * v;       // float4 index: 32 per row of 128
-            const int j = idx >> 5, c4 = (idx & 31) * 4;
-            uv[v] = *reinterpret_cast<const f32x4_t*>(a.U + (b0 + j) * a.d_col + b0 + c4);
-        }
-    } else {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int idx = tid + QT * v;
-            const int j = idx >> 5, c4 = (idx & 31) * 4;
-            const float* src = a.U + (b0 + j) * a.d_col + b0 + c4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) uv[v][e] = (j < nb && c4 + e < nb) ? src[e] : 0.f;
-        }
+    for (int m = 0; m < NPAIR; ++m) {
+        const int pr = tid + QT * m;
+        const int j = pr >> 4, qq = pr & (SL - 1);
+        *reinterpret_cast<f32x4_t*>(&Up[j][qq][0]) = f32x4_t{ud.v[m][0], ud.v[m][1], ud.v[m][2], ud.v[m][3]};
+        *reinterpret_cast<f32x4_t*>(&Up[j][qq][4]) = f32x4_t{ud.v[m][4], ud.v[m][5], ud.v[m][6], ud.v[m][7]};
     }
-    // the reciprocal pivots: one division in each of the first 128 threads
-    const float udiag = (tid < nb) ? a.U[(b0 + tid) * a.d_col + b0 + tid] : 0.f;
+    if (tid < QB) invd[tid] = (tid < nb) ? 1.0f / ud.piv : 0.f;
+    // every U chunk of this block's update: the loads are in flight during the steps
+    const int64_t bn = b0 + QB;                       // the next block
+    UChunk uch[NCH];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int idx = tid + QT * v;
-        const int j = idx >> 5, c4 = (idx & 31) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = c4 + e;
-            Up[j][c & (SL - 1)][c >> 4] = uv[v][e];
-        }
-    }
-    if (tid < QB) invd[tid] = (tid < nb) ? 1.0f / udiag : 0.f;
-    // the first U chunk of this block's update, in flight during the steps
-    UChunk uc;
-    if (b0 + QB < a.s1) load_uchunk(a, b0, b0 + QB, tid, uc);
+    for (int ch = 0; ch < NCH; ++ch)
+        if (bn + UT_N * ch < a.s1) load_uchunk<FULL>(a, b0, bn + UT_N * ch, tid, uch[ch]);
     // the block's W from LDS (updated by the earlier blocks of the super-block); the
     // barrier before the U staging of the first block orders the W stores above
-    if (b0 == a.s0) __syncthreads();
+    if (b0 == a.s0) lds_barrier();
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) {
         const int c = SL * i + q;
         w[i] = (c < nb) ? Wl[rl][cb + c] : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     // U coefficients of the current and the next step, alternating by step parity
     float ucA[SSLOTS], ucB[SSLOTS];
     {
@@ -312,6 +330,10 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         const bool own = (q == qj);
         e[ij] = own ? err : e[ij];
         cv[ij] = own ? (int)(qd + zf) + a.zoff : cv[ij];
+        // keep both selects in this step (left alone, the compiler moves every step's
+        // selects after the last step, holding 128 values live and putting that work on
+        // the block's path)
+        asm volatile("" : "+v"(e[ij]), "+v"(cv[ij]));
         // compensate the later columns; U is upper triangular, so in slot ij the lanes
         // holding columns <= j get a zero coefficient (or touch a finished column).
         // The slot of the next column first: it is on the critical path.
@@ -323,6 +345,9 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         idc = idn;
     });
 
+    // the next block's diagonal U: the loads are in flight during the error staging and
+    // this block's update of the rest of the super-block
+    if (bn < a.s1) load_udiag<FULL>(a, bn, (int)((a.s1 - bn) < QB ? (a.s1 - bn) : QB), tid, ud);
     // a non-finite weight, scale or error shows up in the block's errors
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) bad = bad || !(fabsf(e[i]) <= 3.0e38f);
@@ -339,9 +364,8 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         cl[rl][c] = (uint8_t)cv[i];
     }
     if (bad && rv) atomicOr(&bad_any, 1);
-    // LDS only: the global stores above and below need not have landed
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
+    // the global stores above and below need not have landed
+    lds_barrier();
     if (tid == 0 && bad_any) *a.info = -1;
 
     const int per = a.packed ? 2 : 1;
@@ -352,7 +376,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         if (grow < a.d_row) {
             uint16_t* hrow = a.Ehi + grow * a.lde + cb;
             uint16_t* lrow = a.Elo + grow * a.lde + cb;
-            if (nb == QB && (a.lde & 7) == 0 && ((reinterpret_cast<uintptr_t>(hrow) & 15) == 0) &&
+            if (FULL || nb == QB && (a.lde & 7) == 0 && ((reinterpret_cast<uintptr_t>(hrow) & 15) == 0) &&
                 ((reinterpret_cast<uintptr_t>(lrow) & 15) == 0)) {
                 *reinterpret_cast<u32x4_t*>(hrow + c8) = *reinterpret_cast<const u32x4_t*>(&ehs[r][c8]);
                 *reinterpret_cast<u32x4_t*>(lrow + c8) = *reinterpret_cast<const u32x4_t*>(&els[r][c8]);
@@ -364,7 +388,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         // writes 8 columns of row t / 16
         if (grow < a.d_row) {
             uint8_t* crow = a.codes + grow * a.code_ld + b0 / per;
-            const bool whole = nb == QB && ((reinterpret_cast<uintptr_t>(crow) & (a.packed ? 3 : 7)) == 0);
+            const bool whole = FULL || nb == QB && ((reinterpret_cast<uintptr_t>(crow) & (a.packed ? 3 : 7)) == 0);
             if (a.packed) {
                 uint32_t v = 0;
 #pragma unroll
@@ -384,18 +408,20 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     }
 
     // the rest of the super-block: W[:, n0 ..] -= E U[b0 .. b0 + 127, n0 ..], 64 columns of
-    // U at a time; wave w updates 16 rows x 16 columns of each chunk
-    for (int64_t n0 = b0 + QB; n0 < a.s1; n0 += UT_N) {
+    // U at a time (in registers since the steps); wave w updates 16 rows x 16 columns of
+    // each chunk
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int64_t n0 = b0 + QB + UT_N * ch;
+        if (n0 >= a.s1) break;
 #pragma unroll
         for (int m = 0; m < NU; ++m) {
             const int idx = tid + QT * m;
             const int k = idx >> 3, c8 = (idx & 7) * 8;
-            *reinterpret_cast<u32x4_t*>(uth + k * UT_RS + c8) = uc.h[m];
-            *reinterpret_cast<u32x4_t*>(utl + k * UT_RS + c8) = uc.l[m];
+            *reinterpret_cast<u32x4_t*>(uth + k * UT_RS + c8) = uch[ch].h[m];
+            *reinterpret_cast<u32x4_t*>(utl + k * UT_RS + c8) = uch[ch].l[m];
         }
-        __syncthreads();
-        // the next chunk, in flight during this one's products
-        if (n0 + UT_N < a.s1) load_uchunk(a, b0, n0 + UT_N, tid, uc);
+        lds_barrier();
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < QB; kk += 32) {
@@ -412,14 +438,19 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         const int nc = (int)(n0 - a.s0) + 16 * wave + (lane & 15);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Wl[4 * (lane >> 4) + r][nc] -= acc[r];
-        __syncthreads();
+        lds_barrier();
     }
     }   // blocks of the super-block
 }
 
 gptq_status sweep_launch(const SweepArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.d_row + SROWS - 1) / SROWS));
-    sweep_kernel<<<grid, QT, 0, s>>>(a);
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool full = a.s1 - a.s0 == QSB && (a.d_col & 15) == 0 && (a.lde & 7) == 0 && (a.code_ld & 7) == 0 &&
+                      al16(a.Wws) && al16(a.U) && al16(a.Uhi) && al16(a.Ulo) && al16(a.Ehi) && al16(a.Elo) &&
+                      al16(a.codes);
+    if (full) sweep_kernel<true><<<grid, QT, 0, s>>>(a);
+    else sweep_kernel<false><<<grid, QT, 0, s>>>(a);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
