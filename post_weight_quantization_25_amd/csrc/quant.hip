@@ -306,11 +306,56 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // 128-column lazy blocks.
 
 // Workspace: fp32 working copy of W | E hi | E lo (bf16, d_row x QSB) | U hi | U lo
-// (bf16, d_col x d_col).
+// (bf16, d_col x d_col) | Ut hi | Ut lo (bf16, one transposed QSB x QSB diagonal block
+// of U per super-block).
+static size_t ut_bytes(int64_t d_col) { return (size_t)((d_col + QSB - 1) / QSB) * QSB * QSB * 2; }
+
 size_t quant_ws_bytes(int64_t d_row, int64_t d_col) {
     if (d_row <= 0 || d_col <= 0) return 0;
     return align256((size_t)d_row * d_col * sizeof(float)) + 2 * align256((size_t)d_row * QSB * 2) +
-           2 * align256((size_t)d_col * d_col * 2);
+           2 * align256((size_t)d_col * d_col * 2) + 2 * align256(ut_bytes(d_col));
+}
+
+// The diagonal QSB x QSB blocks of U, split into bf16 hi + lo, zero past d, in the
+// order in which the updates inside a super-block read them as MFMA B operands: for
+// column group g = n / 16 and k step s = k / 32, a 1 KB piece holds, for lane l =
+// n % 16 + 16 ((k % 32) / 8), the eight values k = 32 s + 8 (l / 16) .. + 7 of column
+// n, so that a wave reads each operand with one contiguous 16-byte-per-lane load.
+// One workgroup per 64 x 64 tile, transposed through LDS.
+__global__ __launch_bounds__(256) void udt_kernel(const float* U, int64_t d, uint16_t* th, uint16_t* tl) {
+    __shared__ float t[64][65];
+    const int b = blockIdx.y, tk = blockIdx.x / (QSB / 64), tn = blockIdx.x % (QSB / 64);
+    const int64_t k0 = (int64_t)b * QSB + tk * 64, n0 = (int64_t)b * QSB + tn * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 4 * (tid & 15) + e;
+            t[r][c] = (k0 + r < d && n0 + c < d) ? U[(k0 + r) * d + n0 + c] : 0.f;
+        }
+    }
+    __syncthreads();
+    const int n = tid >> 2, kb = 16 * (tid & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int nb = tn * 64 + n, k = tk * 64 + kb + 8 * h;   // within the block
+        const int64_t o = (int64_t)b * QSB * QSB +
+                          ((int64_t)((nb >> 4) * (QSB / 32) + (k >> 5)) * 64 + (nb & 15) + 16 * ((k & 31) >> 3)) * 8;
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float u0 = t[kb + 8 * h + 2 * e][n], u1 = t[kb + 8 * h + 2 * e + 1][n];
+            const uint16_t h0 = f32_to_bf16_bits(u0), h1 = f32_to_bf16_bits(u1);
+            const uint16_t l0 = f32_to_bf16_bits(u0 - bf16_bits_to_f32(h0));
+            const uint16_t l1 = f32_to_bf16_bits(u1 - bf16_bits_to_f32(h1));
+            ph[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            pl[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        *reinterpret_cast<u32x4_t*>(th + o) = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+        *reinterpret_cast<u32x4_t*>(tl + o) = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+    }
 }
 
 // U -> bf16 hi + lo (hi = bf16(u), lo = bf16(u - hi)), once per call: every workgroup
@@ -370,6 +415,10 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     uint16_t* Uhi = reinterpret_cast<uint16_t*>(wp);
     wp += align256((size_t)d_col * d_col * 2);
     uint16_t* Ulo = reinterpret_cast<uint16_t*>(wp);
+    wp += align256((size_t)d_col * d_col * 2);
+    uint16_t* Uthi = reinterpret_cast<uint16_t*>(wp);
+    wp += align256(ut_bytes(d_col));
+    uint16_t* Utlo = reinterpret_cast<uint16_t*>(wp);
     const int G = p.group_size;
     const int n_groups = (G == 0) ? 1 : (int)(d_col / G);
 
@@ -395,8 +444,11 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         const unsigned ug = (unsigned)std::min<int64_t>((nu / 8 + 255) / 256 + 1, 4096);
         split_u_kernel<<<ug, 256, 0, s>>>(U, nu, Uhi, Ulo);
         GPTQ_LAUNCH_CHECK();
+        udt_kernel<<<dim3((QSB / 64) * (QSB / 64), (unsigned)((d_col + QSB - 1) / QSB)), 256, 0, s>>>(U, d_col, Uthi,
+                                                                                                    Utlo);
+        GPTQ_LAUNCH_CHECK();
     }
-    sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U; sa.Uhi = Uhi; sa.Ulo = Ulo;
+    sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U;
     sa.codes = codes; sa.code_ld = (p.bits <= 4) ? d_col / 2 : d_col;
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
     sa.group = G; sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
@@ -408,6 +460,8 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         // the super-block's blocks, each followed by the update of the rest of the
         // super-block, in one launch
         sa.s0 = s0; sa.s1 = s1; sa.Ehi = Ehi; sa.Elo = Elo; sa.lde = QSB;
+        sa.Uthi = Uthi + (s0 / QSB) * QSB * QSB;
+        sa.Utlo = Utlo + (s0 / QSB) * QSB * QSB;
         st = sweep_launch(sa, s);
         if (st != GPTQ_OK) return st;
         // everything after the super-block, K = s1 - s0

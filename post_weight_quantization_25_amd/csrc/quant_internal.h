@@ -15,7 +15,9 @@ constexpr int QSB = 512;
 struct SweepArgs {
     const float* Wws; int64_t d_row, d_col;
     const float* U;                 // fp32 U (the diagonal blocks for the sweep)
-    const uint16_t* Uhi; const uint16_t* Ulo;   // U split into bf16 hi + lo (the updates)
+    // this super-block's diagonal QSB x QSB part of U split into bf16 hi + lo, zero past
+    // d_col, in MFMA B-operand order (the updates inside the super-block)
+    const uint16_t* Uthi; const uint16_t* Utlo;
     int64_t s0, s1;                 // the super-block: columns s0 .. s1 - 1 (s1 - s0 <= QSB)
     uint16_t* Ehi; uint16_t* Elo;   // the super-block's errors as bf16 hi + lo (hi = bf16(e),
     int64_t lde;                    // lo = bf16(e - hi)): d_row x QSB, row stride lde

@@ -18,12 +18,13 @@
 // coefficients of the next step with two 16-byte LDS reads (prefetched one step
 // ahead).  The quantization error of column j is broadcast along the row with
 // DPP row_newbcast; group min/max use DPP butterfly reductions.
-// After a block, its errors E (16 x 128, bf16 hi + lo, staged in LDS) update the rest
-// of the super-block in LDS, W[:, later] -= E U[block, later], on
-// v_mfma_f32_16x16x32_bf16 with three products (hi hi + hi lo + lo hi, fp32
-// accumulation), U staged 64 columns at a time in the LDS of the U block (free after
-// the steps) and read with transposing LDS reads.  Rows are independent, so no other
-// workgroup is involved.
+// After a block, its errors E (16 x 128, bf16 hi + lo, staged in LDS, then held in
+// registers) update the rest of the super-block in LDS, W[:, later] -= E U[block,
+// later], on v_mfma_f32_16x16x32_bf16 with three products (hi hi + hi lo + lo hi, fp32
+// accumulation); the U operands come straight from global memory in registers, from
+// the transposed bf16 copy of the super-block's diagonal block of U (eight consecutive
+// k of one column per 16-byte load), loaded while the block's steps run.  Rows are
+// independent, so no other workgroup is involved.
 
 #include <utility>
 
@@ -34,22 +35,6 @@ namespace gptq {
 constexpr int SSLOTS = QB / SL;     // columns per lane: q, q+16, ..., q+112
 constexpr int WL_LD = QSB + 4;      // LDS row pitch of the super-block's W (floats)
 constexpr int UT_N = 64;            // columns of U per update chunk
-constexpr int UT_RS = UT_N + 8;     // LDS row pitch of a U chunk (bf16): conflict-free transposed reads
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-// B operand of v_mfma_f32_16x16x32_bf16 (32 k x 16 columns: lane l holds column
-// n0 + l % 16 at k = k0 + 8 (l / 16) .. + 7) from a [k][n] chunk, with two transposing
-// reads: in each 16-lane group lane j addresses k = k0 + 8 g + (j >> 2), columns
-// n0 + 4 (j & 3) .. + 3, and lane i receives column n0 + i at four consecutive k.
-GPTQ_DEV bf16x8_t ut_bfrag(const uint16_t* ut, int n0, int k0, int lane) {
-    const int g = lane >> 4, j = lane & 15;
-    const int k = k0 + 8 * g + (j >> 2), n = n0 + 4 * (j & 3);
-    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(ut + k * UT_RS + n));
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(ut + (k + 4) * UT_RS + n));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
 
 GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 65504.f; }
 
@@ -75,36 +60,20 @@ GPTQ_DEV float row_max(float v) {
     return fmaxf(v, dpp_f<DPP_MIRROR>(v));
 }
 
-// One U chunk of an in-super-block update: rows b0 .. b0 + 127 (k), columns n0 .. n0 +
-// 63, hi and lo, into registers (thread t: rows (t + 256 m) / 8, 8 columns each); zero
-// past the super-block or past U.
-constexpr int NU = QB * UT_N / 8 / QT;   // 16-byte pieces per thread and half
-struct UChunk { u32x4_t h[NU], l[NU]; };
+// The U operands of one 64-column chunk of a block's update for this lane (wave w:
+// columns n0 + 16 w .. + 15): for each 32-k step, lane l holds column n0 + 16 w + l % 16
+// at k = b0 + 32 kk + 8 (l / 16) .. + 7, hi and lo, from the operand-ordered copy of
+// the diagonal block (always QSB x QSB, zero past d_col, so no bounds checks): one
+// contiguous 1 KB piece per wave and operand.
+constexpr int NKK = QB / 32;
+struct UChunk { bf16x8_t h[NKK], l[NKK]; };
 
-template <bool FULL>
-GPTQ_DEV void load_uchunk(const SweepArgs& a, int64_t b0, int64_t n0, int tid, UChunk& u) {
-    const bool fast = FULL || (b0 + QB <= a.d_col) && (n0 + UT_N <= a.s1) && ((a.d_col & 7) == 0) &&
-                      ((reinterpret_cast<uintptr_t>(a.Uhi) & 15) == 0) &&
-                      ((reinterpret_cast<uintptr_t>(a.Ulo) & 15) == 0) && ((n0 & 7) == 0);
+GPTQ_DEV void load_uchunk(const SweepArgs& a, int64_t b0, int64_t n0, int wave, int lane, UChunk& u) {
+    const int64_t o = ((((n0 - a.s0) >> 4) + wave) * (QSB / 32) + ((b0 - a.s0) >> 5)) * 512 + 8 * lane;
 #pragma unroll
-    for (int m = 0; m < NU; ++m) {
-        const int idx = tid + QT * m;
-        const int k = idx >> 3, c8 = (idx & 7) * 8;
-        const int64_t off = (b0 + k) * a.d_col + n0 + c8;
-        if (fast) {
-            u.h[m] = *reinterpret_cast<const u32x4_t*>(a.Uhi + off);
-            u.l[m] = *reinterpret_cast<const u32x4_t*>(a.Ulo + off);
-        } else {
-            uint32_t th[4] = {0u, 0u, 0u, 0u}, tl[4] = {0u, 0u, 0u, 0u};
-            for (int e = 0; e < 8; ++e) {
-                if (b0 + k < a.d_col && n0 + c8 + e < a.s1) {
-                    th[e >> 1] |= (uint32_t)a.Uhi[off + e] << (16 * (e & 1));
-                    tl[e >> 1] |= (uint32_t)a.Ulo[off + e] << (16 * (e & 1));
-                }
-            }
-            u.h[m] = u32x4_t{th[0], th[1], th[2], th[3]};
-            u.l[m] = u32x4_t{tl[0], tl[1], tl[2], tl[3]};
-        }
+    for (int kk = 0; kk < NKK; ++kk) {
+        u.h[kk] = *reinterpret_cast<const bf16x8_t*>(a.Uthi + o + 512 * kk);
+        u.l[kk] = *reinterpret_cast<const bf16x8_t*>(a.Utlo + o + 512 * kk);
     }
 }
 
@@ -144,7 +113,7 @@ constexpr int NCH = (QSB - QB) / UT_N;
 // with no edge code around it.
 template <bool FULL>
 __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
-    // Up[j][q][i] = U[b0+j][b0+q+16i] during the steps; a U chunk (hi, lo) during the updates
+    // Up[j][q][i] = U[b0+j][b0+q+16i]
     __shared__ __attribute__((aligned(16))) float Up[QB][SL][SSLOTS];
     __shared__ float invd[QB];                                         // 1 / U[b0+j][b0+j]
     __shared__ __attribute__((aligned(16))) float Wl[SROWS][WL_LD];    // the super-block's W
@@ -153,9 +122,6 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     // fall on distinct banks
     __shared__ __attribute__((aligned(16))) uint16_t ehs[SROWS][QB + 8], els[SROWS][QB + 8];
     __shared__ int bad_any;
-    static_assert(2 * QB * UT_RS * 2 <= (int)sizeof(Up), "a U chunk fits in the U block's LDS");
-    uint16_t* const uth = reinterpret_cast<uint16_t*>(&Up[0][0][0]);
-    uint16_t* const utl = uth + QB * UT_RS;
 
     const int tid = threadIdx.x;
     const int q = tid & (SL - 1);
@@ -228,7 +194,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     UChunk uch[NCH];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
-        if (bn + UT_N * ch < a.s1) load_uchunk<FULL>(a, b0, bn + UT_N * ch, tid, uch[ch]);
+        if (bn + UT_N * ch < a.s1) load_uchunk(a, b0, bn + UT_N * ch, wave, lane, uch[ch]);
     // the block's W from LDS (updated by the earlier blocks of the super-block); the
     // barrier before the U staging of the first block orders the W stores above
     if (b0 == a.s0) lds_barrier();
@@ -408,37 +374,33 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     }
 
     // the rest of the super-block: W[:, n0 ..] -= E U[b0 .. b0 + 127, n0 ..], 64 columns of
-    // U at a time (in registers since the steps); wave w updates 16 rows x 16 columns of
-    // each chunk
+    // U at a time; wave w updates 16 rows x 16 columns of each chunk (its own columns of
+    // Wl, so the chunks need no barrier between them)
+    if (bn < a.s1) {
+        bf16x8_t eh[NKK], el[NKK];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-        const int64_t n0 = b0 + QB + UT_N * ch;
-        if (n0 >= a.s1) break;
-#pragma unroll
-        for (int m = 0; m < NU; ++m) {
-            const int idx = tid + QT * m;
-            const int k = idx >> 3, c8 = (idx & 7) * 8;
-            *reinterpret_cast<u32x4_t*>(uth + k * UT_RS + c8) = uch[ch].h[m];
-            *reinterpret_cast<u32x4_t*>(utl + k * UT_RS + c8) = uch[ch].l[m];
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int mr = lane & 15, ka = 32 * kk + 8 * (lane >> 4);
+            eh[kk] = *reinterpret_cast<const bf16x8_t*>(&ehs[mr][ka]);
+            el[kk] = *reinterpret_cast<const bf16x8_t*>(&els[mr][ka]);
         }
-        lds_barrier();
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < QB; kk += 32) {
-            const int mr = lane & 15, ka = kk + 8 * (lane >> 4);
-            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&ehs[mr][ka]);
-            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&els[mr][ka]);
-            const bf16x8_t bh = ut_bfrag(uth, 16 * wave, kk, lane);
-            const bf16x8_t bl = ut_bfrag(utl, 16 * wave, kk, lane);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        for (int ch = 0; ch < NCH; ++ch) {
+            const int64_t n0 = bn + UT_N * ch;
+            if (n0 >= a.s1) break;
+            f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eh[kk], uch[ch].h[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eh[kk], uch[ch].l[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(el[kk], uch[ch].h[kk], acc, 0, 0, 0);
+            }
+            // D layout: lane l holds column l % 16, rows 4 (l / 16) .. + 3
+            const int nc = (int)(n0 - a.s0) + 16 * wave + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wl[4 * (lane >> 4) + r][nc] -= acc[r];
         }
-        // D layout: lane l holds column l % 16, rows 4 (l / 16) .. + 3
-        const int nc = (int)(n0 - a.s0) + 16 * wave + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Wl[4 * (lane >> 4) + r][nc] -= acc[r];
-        lds_barrier();
+        lds_barrier();   // the next block reads these columns of Wl
     }
     }   // blocks of the super-block
 }
@@ -447,7 +409,7 @@ gptq_status sweep_launch(const SweepArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.d_row + SROWS - 1) / SROWS));
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const bool full = a.s1 - a.s0 == QSB && (a.d_col & 15) == 0 && (a.lde & 7) == 0 && (a.code_ld & 7) == 0 &&
-                      al16(a.Wws) && al16(a.U) && al16(a.Uhi) && al16(a.Ulo) && al16(a.Ehi) && al16(a.Elo) &&
+                      al16(a.Wws) && al16(a.U) && al16(a.Ehi) && al16(a.Elo) &&
                       al16(a.codes);
     if (full) sweep_kernel<true><<<grid, QT, 0, s>>>(a);
     else sweep_kernel<false><<<grid, QT, 0, s>>>(a);
