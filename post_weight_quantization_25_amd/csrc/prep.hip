@@ -918,7 +918,11 @@ static gptq_status aux_stream(AuxStream*& out) {
 // columns of L are final, the inverse X11 of the leading h x h block and the product
 // T = L21 X11 run on the auxiliary stream, beside the remaining (latency-bound)
 // factorization steps; afterwards the trailing block is inverted and
-// X21 = -X22 T closes the last doubling level.
+// X21 = -X22 T closes the last doubling level.  When the trailing block is split once
+// more (at s2 = h + h2), the blocks P = [0, h), Q = [h, s2), R = [s2, d) give
+// X[Q][P] = -X[Q][Q] L[Q][P] X[P][P] and X[R][P] = -X[R][R] (L[R][P] X[P][P] +
+// L[R][Q] X[Q][P]); everything but the products with X[R][R] then runs on the
+// auxiliary stream before the last steps end.
 static gptq_status cholinv(PrepCtx& c) {
     const int64_t d = c.d;
     gptq_status st;
@@ -972,6 +976,16 @@ static gptq_status cholinv(PrepCtx& c) {
         if ((s3 = gemm(ca, T2b, h2, c.A + s2 * d + h, d, c.X + h * d + h, d, (int)m2, (int)h2, (int)h2, 1.0, 0.0,
                        G_TRI_B, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
             return s3;
+        // with Q = [h, s2), R = [s2, d) and P = [0, h): X[Q][P] = -X[Q][Q] T[Q], T[Q] =
+        // L[Q][P] X[P][P] the first h2 rows of T (h2 x h, lower triangular X block) ...
+        if ((s3 = gemm(ca, c.X + h * d, d, c.X + h * d + h, d, T11, h, (int)h2, (int)h, (int)h2, -1.0, 0.0, G_TRI_A,
+                       1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+            return s3;
+        // ... and V = L[R][P] X[P][P] + L[R][Q] X[Q][P] in place of T's last m2 rows, so
+        // that X[R][P] = -X[R][R] V needs only the last block's inverse
+        if ((s3 = gemm(ca, T11 + h2 * h, h, c.A + s2 * d + h, d, c.X + h * d, d, (int)m2, (int)h, (int)h2, 1.0, 1.0, 0,
+                       1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+            return s3;
         if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
         return GPTQ_OK;
     };
@@ -992,16 +1006,17 @@ static gptq_status cholinv(PrepCtx& c) {
         if (h2 > 0 && k0 / PNB == fork_step2 && (st = fork2()) != GPTQ_OK) return st;
     }
     if (h2 > 0) {
-        // the last block [s2, d), then X[s2 ..][h .. s2) = -X[s2 ..][s2 ..] T2
+        // the last block R = [s2, d), then X[R][Q] = -X[R][R] T2 and X[R][P] = -X[R][R] V
         if ((st = trtri_block(c, s2, m2, T22)) != GPTQ_OK) return st;
         if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
         if ((st = gemm(c, c.X + s2 * d + h, d, c.X + s2 * d + s2, d, T2b, h2, (int)m2, (int)h2, (int)m2, -1.0, 0.0,
                        G_TRI_A)) != GPTQ_OK)
             return st;
-    } else {
-        if ((st = trtri_block(c, h, m, T22)) != GPTQ_OK) return st;
-        if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
+        return gemm(c, c.X + s2 * d, d, c.X + s2 * d + s2, d, T11 + h2 * h, h, (int)m2, (int)h, (int)m2, -1.0, 0.0,
+                    G_TRI_A);
     }
+    if ((st = trtri_block(c, h, m, T22)) != GPTQ_OK) return st;
+    if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
     // X21 = -X22 T   (X22 lower triangular)
     return gemm(c, c.X + h * d, d, c.X + h * d + h, d, T11, h, (int)m, (int)h, (int)m, -1.0, 0.0, G_TRI_A);
 }
