@@ -941,9 +941,15 @@ static gptq_status cholinv(PrepCtx& c) {
     int64_t h2 = 0;
     if (m > PNB) { h2 = PNB; while (2 * h2 < m) h2 *= 2; }
     const int64_t m2 = m - h2;               // 0 < m2 <= h2 when h2 > 0
-    double* T11 = c.T;                       // h * h doubles: X11's levels, then T (m x h)
-    double* T2b = c.T + h * h;               // h2 * h2: the levels of [h, h + h2), then T2 (m2 x h2)
-    double* T22 = T2b + h2 * h2;             // m2 * m2 (or m * m): the levels of the last block
+    // T11: X11's levels (h x h), then T (m x h, row pitch ldt); with the second split its
+    // last m2 rows also hold T2 in columns h .. s2, beside V, so that the two final
+    // products with the last block's inverse are one
+    const int64_t s2 = h + h2;
+    const int64_t ldt = (h2 > 0) ? s2 : h;
+    double* T11 = c.T;
+    double* T2b = c.T + std::max(h * h, m * ldt);   // h2 * h2: the levels of [h, s2)
+    double* T22 = T2b + h2 * h2;                     // m2 * m2 (or m * m): the levels of the last block
+    double* T2 = T11 + h2 * ldt + h;                 // m2 x h2, row pitch ldt
 
     AuxStream* aux = nullptr;
     if ((st = aux_stream(aux)) != GPTQ_OK) return st;
@@ -956,36 +962,35 @@ static gptq_status cholinv(PrepCtx& c) {
     auto fork = [&]() -> gptq_status {
         if (hipEventRecord(aux->fork, c.s) != hipSuccess || hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess)
             return GPTQ_ERR_HIP;
-        gptq_status s2;
-        if ((s2 = trtri_block(ca, 0, h, T11, AUX_MAX_WG)) != GPTQ_OK) return s2;
+        gptq_status r;
+        if ((r = trtri_block(ca, 0, h, T11, AUX_MAX_WG)) != GPTQ_OK) return r;
         // T = L21 X11   (m x h, X11 lower triangular)
-        if ((s2 = gemm(ca, T11, h, c.A + h * d, d, c.X, d, (int)m, (int)h, (int)h, 1.0, 0.0, G_TRI_B, 1, 0, 0, 0,
+        if ((r = gemm(ca, T11, ldt, c.A + h * d, d, c.X, d, (int)m, (int)h, (int)h, 1.0, 0.0, G_TRI_B, 1, 0, 0, 0,
                        0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
-            return s2;
+            return r;
         if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
         return GPTQ_OK;
     };
-    const int64_t s2 = h + h2;
     const int64_t fork_step2 = std::max<int64_t>(s2 / PNB - 2, fork_step);
     auto fork2 = [&]() -> gptq_status {
         if (hipEventRecord(aux->fork, c.s) != hipSuccess || hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess)
             return GPTQ_ERR_HIP;
-        gptq_status s3;
-        if ((s3 = trtri_block(ca, h, h2, T2b, AUX_MAX_WG)) != GPTQ_OK) return s3;
+        gptq_status r;
+        if ((r = trtri_block(ca, h, h2, T2b, AUX_MAX_WG)) != GPTQ_OK) return r;
         // T2 = L[s2 ..][h .. s2) X[h .. s2)   (m2 x h2, lower triangular X block)
-        if ((s3 = gemm(ca, T2b, h2, c.A + s2 * d + h, d, c.X + h * d + h, d, (int)m2, (int)h2, (int)h2, 1.0, 0.0,
+        if ((r = gemm(ca, T2, ldt, c.A + s2 * d + h, d, c.X + h * d + h, d, (int)m2, (int)h2, (int)h2, 1.0, 0.0,
                        G_TRI_B, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
-            return s3;
+            return r;
         // with Q = [h, s2), R = [s2, d) and P = [0, h): X[Q][P] = -X[Q][Q] T[Q], T[Q] =
         // L[Q][P] X[P][P] the first h2 rows of T (h2 x h, lower triangular X block) ...
-        if ((s3 = gemm(ca, c.X + h * d, d, c.X + h * d + h, d, T11, h, (int)h2, (int)h, (int)h2, -1.0, 0.0, G_TRI_A,
+        if ((r = gemm(ca, c.X + h * d, d, c.X + h * d + h, d, T11, ldt, (int)h2, (int)h, (int)h2, -1.0, 0.0, G_TRI_A,
                        1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
-            return s3;
+            return r;
         // ... and V = L[R][P] X[P][P] + L[R][Q] X[Q][P] in place of T's last m2 rows, so
         // that X[R][P] = -X[R][R] V needs only the last block's inverse
-        if ((s3 = gemm(ca, T11 + h2 * h, h, c.A + s2 * d + h, d, c.X + h * d, d, (int)m2, (int)h, (int)h2, 1.0, 1.0, 0,
+        if ((r = gemm(ca, T11 + h2 * ldt, ldt, c.A + s2 * d + h, d, c.X + h * d, d, (int)m2, (int)h, (int)h2, 1.0, 1.0, 0,
                        1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
-            return s3;
+            return r;
         if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
         return GPTQ_OK;
     };
@@ -1006,27 +1011,25 @@ static gptq_status cholinv(PrepCtx& c) {
         if (h2 > 0 && k0 / PNB == fork_step2 && (st = fork2()) != GPTQ_OK) return st;
     }
     if (h2 > 0) {
-        // the last block R = [s2, d), then X[R][Q] = -X[R][R] T2 and X[R][P] = -X[R][R] V
+        // the last block R = [s2, d), then [X[R][P] X[R][Q]] = -X[R][R] [V T2]
         if ((st = trtri_block(c, s2, m2, T22)) != GPTQ_OK) return st;
         if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
-        if ((st = gemm(c, c.X + s2 * d + h, d, c.X + s2 * d + s2, d, T2b, h2, (int)m2, (int)h2, (int)m2, -1.0, 0.0,
-                       G_TRI_A)) != GPTQ_OK)
-            return st;
-        return gemm(c, c.X + s2 * d, d, c.X + s2 * d + s2, d, T11 + h2 * h, h, (int)m2, (int)h, (int)m2, -1.0, 0.0,
-                    G_TRI_A);
+        return gemm(c, c.X + s2 * d, d, c.X + s2 * d + s2, d, T11 + h2 * ldt, ldt, (int)m2, (int)s2, (int)m2, -1.0,
+                    0.0, G_TRI_A);
     }
     if ((st = trtri_block(c, h, m, T22)) != GPTQ_OK) return st;
     if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
     // X21 = -X22 T   (X22 lower triangular)
-    return gemm(c, c.X + h * d, d, c.X + h * d + h, d, T11, h, (int)m, (int)h, (int)m, -1.0, 0.0, G_TRI_A);
+    return gemm(c, c.X + h * d, d, c.X + h * d + h, d, T11, ldt, (int)m, (int)h, (int)m, -1.0, 0.0, G_TRI_A);
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static size_t t_bytes(int64_t d) {
-    // product scratch: h * h doubles for the leading block's levels and T (m x h), h2 * h2
-    // for the trailing block's leading part and T2, m2 * m2 for its last part
-    // (h2 + m2 = m = d - h <= h), h * h + h2 * h2 + m2 * m2 <= h * h + m * m <= d * d
+    // product scratch: max(h * h, m * s2) doubles for the leading block's levels and T
+    // (m x h) beside T2 (m2 x h2), h2 * h2 for the levels of the trailing block's leading
+    // part, m2 * m2 for its last part; with h2 + m2 = m = d - h <= h and s2 <= d:
+    // max(h * h, m * d) + m * m <= d * d
     return (size_t)d * d * sizeof(double);
 }
 
