@@ -882,7 +882,7 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 #define AUX_FORK_REST 2048
 #endif
 #ifndef AUX_MAX_WG
-#define AUX_MAX_WG 256
+#define AUX_MAX_WG 384
 #endif
 
 // One auxiliary stream and two events per device, created on first use and kept
