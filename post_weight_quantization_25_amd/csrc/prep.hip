@@ -60,20 +60,59 @@ __global__ __launch_bounds__(1024) void prep_lambda_kernel(const float* H, int64
 // above the diagonal) by the diagonal routine, the products clip their k ranges to
 // those blocks and the ones below, and the output reads the lower part of X only; so X
 // needs no initialization.
+// VEC (d a multiple of 4, H 16-byte aligned): each thread moves four columns, one
+// 16-byte load of H (the four values in reverse order) and two 16-byte stores of A.
+template <bool VEC>
 __global__ void prep_build_kernel(const float* H, int64_t d, const double* lam, double* A) {
     const int64_t i = blockIdx.y;
     const double l = *lam;
-    for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j <= i; j += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    if constexpr (VEC) {
+        const float* hrow = H + (d - 1 - i) * d;
+        for (int64_t j = 4 * (blockIdx.x * blockDim.x + threadIdx.x); j <= i; j += 4 * nth) {
+            const f32x4_t h = *reinterpret_cast<const f32x4_t*>(hrow + (d - 4 - j));   // columns d-4-j .. d-1-j
+            double v[4] = {(double)h[3], (double)h[2], (double)h[1], (double)h[0]};  // A columns j .. j+3
+            if (j + 3 <= i) {
+                if (i - j < 4) v[i - j] += l;
+                *reinterpret_cast<double2*>(A + i * d + j) = double2{v[0], v[1]};
+                *reinterpret_cast<double2*>(A + i * d + j + 2) = double2{v[2], v[3]};
+            } else {
+                for (int e = 0; e < 4 && j + e <= i; ++e) A[i * d + j + e] = v[e] + ((j + e == i) ? l : 0.0);
+            }
+        }
+        return;
+    }
+    for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j <= i; j += nth) {
         double v = (double)H[(d - 1 - i) * d + (d - 1 - j)];
         if (i == j) v += l;
         A[i * d + j] = v;
     }
 }
 
-// U[i][j] = X[d-1-i][d-1-j] for j >= i, 0 below the diagonal.
+// U[i][j] = X[d-1-i][d-1-j] for j >= i, 0 below the diagonal.  VEC (d a multiple of
+// 4, U 16-byte aligned): each thread writes four columns with one 16-byte store (from
+// two 16-byte loads of X where any of the four lies on or above the diagonal; the
+// values read from X's unwritten upper part are discarded).
+template <bool VEC>
 __global__ void prep_output_kernel(const double* X, int64_t d, float* U) {
     const int64_t i = blockIdx.y;
-    for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j < d; j += (int64_t)gridDim.x * blockDim.x)
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    if constexpr (VEC) {
+        const double* xrow = X + (d - 1 - i) * d;
+        for (int64_t j = 4 * (blockIdx.x * blockDim.x + threadIdx.x); j < d; j += 4 * nth) {
+            f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+            if (j + 3 >= i) {
+                const double2 a = *reinterpret_cast<const double2*>(xrow + (d - 4 - j));   // X columns d-4-j, d-3-j
+                const double2 b = *reinterpret_cast<const double2*>(xrow + (d - 2 - j));   // d-2-j, d-1-j
+                const double v[4] = {b.y, b.x, a.y, a.x};                                  // U columns j .. j+3
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u[e] = (j + e >= i) ? (float)v[e] : 0.f;
+            }
+            *reinterpret_cast<f32x4_t*>(U + i * d + j) = u;
+        }
+        return;
+    }
+    for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j < d; j += nth)
         U[i * d + j] = (j >= i) ? (float)X[(d - 1 - i) * d + (d - 1 - j)] : 0.0f;
 }
 
@@ -1056,7 +1095,9 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     prep_lambda_kernel<<<1, 1024, 0, s>>>(H, d, percdamp, lam, info, c.flag);
     GPTQ_LAUNCH_CHECK();
     dim3 gb((unsigned)((d + 255) / 256 < 64 ? (d + 255) / 256 : 64), (unsigned)d);
-    prep_build_kernel<<<gb, 256, 0, s>>>(H, d, lam, c.A);
+    dim3 gb4((unsigned)((d + 1023) / 1024 < 64 ? (d + 1023) / 1024 : 64), (unsigned)d);
+    if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0) prep_build_kernel<true><<<gb4, 256, 0, s>>>(H, d, lam, c.A);
+    else prep_build_kernel<false><<<gb, 256, 0, s>>>(H, d, lam, c.A);
     GPTQ_LAUNCH_CHECK();
     gptq_status st;
     {
@@ -1064,7 +1105,8 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
         st = cholinv(c);
     }
     if (st != GPTQ_OK) return st;
-    prep_output_kernel<<<gb, 256, 0, s>>>(c.X, d, U);
+    if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0) prep_output_kernel<true><<<gb4, 256, 0, s>>>(c.X, d, U);
+    else prep_output_kernel<false><<<gb, 256, 0, s>>>(c.X, d, U);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
