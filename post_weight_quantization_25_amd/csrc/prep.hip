@@ -917,9 +917,6 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // (or later, when the leading block is final only then), and its products take at
 // most AUX_MAX_WG workgroups at a time, so that the factorization steps beside it
 // still find free slots.
-#ifndef AUX_FORK_REST
-#define AUX_FORK_REST 2048
-#endif
 #ifndef AUX_MAX_WG
 #define AUX_MAX_WG 384
 #endif
@@ -953,15 +950,28 @@ static gptq_status aux_stream(AuxStream*& out) {
 // chain is one launch.  (Deferring the trailing update to blocks of 256 columns, so
 // that each step inside a block updates only the rest of that block, measured
 // slower: the rank-256 update then lies on the chain.)
-// The inverse is split at h, the largest 64 * 2^i below d: as soon as the first h
-// columns of L are final, the inverse X11 of the leading h x h block and the product
-// T = L21 X11 run on the auxiliary stream, beside the remaining (latency-bound)
-// factorization steps; afterwards the trailing block is inverted and
-// X21 = -X22 T closes the last doubling level.  When the trailing block is split once
-// more (at s2 = h + h2), the blocks P = [0, h), Q = [h, s2), R = [s2, d) give
-// X[Q][P] = -X[Q][Q] L[Q][P] X[P][P] and X[R][P] = -X[R][R] (L[R][P] X[P][P] +
-// L[R][Q] X[Q][P]); everything but the products with X[R][R] then runs on the
-// auxiliary stream before the last steps end.
+//
+// The inverse is assembled by row blocks B_0, B_1, .., B_last: B_0 = [0, h) with h
+// the largest 64 * 2^i below d, and each next block the largest 64 * 2^i below what
+// remains, until at most INV_LAST columns are left (the last block).  With P_i =
+// [0, s_i) the columns before B_i and Trest[r][P_i] = L[r][P_i] X[P_i][P_i] for the
+// rows r after B_{i-1}:
+//   X[B_i][P_i] = -X[B_i][B_i] Trest[B_i][P_i],
+//   Trest[r][P_i] += L[r][B_i] X[B_i][P_i] and Trest[r][B_i] = L[r][B_i] X[B_i][B_i]
+//   for the rows r after B_i.
+// As soon as the columns of B_i are final (and for B_0 no earlier than AUX_FORK_REST
+// columns before the end), its inverse X[B_i][B_i] (recursive doubling) and these
+// products run on the auxiliary stream, beside the remaining (latency-bound)
+// factorization steps.  After the loop only the last block's inverse and one product
+// remain on the caller's stream.  (A last block of 512 or 256 columns at d = 4096
+// measured slower than 1024: the auxiliary stream then still works on the blocks
+// before it when the loop ends.)
+#ifndef AUX_FORK_REST
+#define AUX_FORK_REST 2048
+#endif
+#ifndef INV_LAST
+#define INV_LAST 1024
+#endif
 static gptq_status cholinv(PrepCtx& c) {
     const int64_t d = c.d;
     gptq_status st;
@@ -971,69 +981,64 @@ static gptq_status cholinv(PrepCtx& c) {
     prep_panel_kernel<<<(unsigned)((d - PNB + 63) / 64), 256, 0, c.s>>>(c.A, c.X, d, 0);
     GPTQ_LAUNCH_CHECK();
 
-    int64_t h = PNB;
-    while (2 * h < d) h *= 2;
-    const int64_t m = d - h;                 // 0 < m <= h
-    // the trailing block [h, d) is split the same way at h + h2 when it is larger than
-    // one diagonal block: its leading part's inverse and T2 = L[h + h2 ..][h .. h + h2)
-    // X[h .. h + h2) also run on the auxiliary stream
-    int64_t h2 = 0;
-    if (m > PNB) { h2 = PNB; while (2 * h2 < m) h2 *= 2; }
-    const int64_t m2 = m - h2;               // 0 < m2 <= h2 when h2 > 0
-    // T11: X11's levels (h x h), then T (m x h, row pitch ldt); with the second split its
-    // last m2 rows also hold T2 in columns h .. s2, beside V, so that the two final
-    // products with the last block's inverse are one
-    const int64_t s2 = h + h2;
-    const int64_t ldt = (h2 > 0) ? s2 : h;
-    double* T11 = c.T;
-    double* T2b = c.T + std::max(h * h, m * ldt);   // h2 * h2: the levels of [h, s2)
-    double* T22 = T2b + h2 * h2;                     // m2 * m2 (or m * m): the levels of the last block
-    double* T2 = T11 + h2 * ldt + h;                 // m2 x h2, row pitch ldt
+    // row blocks: B_i = [bs[i], bs[i + 1]) for i < nb, the last block [bs[nb], d)
+    int64_t bs[64];
+    int nb = 0;
+    for (int64_t s0 = 0;;) {
+        const int64_t r = d - s0;
+        if (r <= PNB || (nb > 0 && r <= INV_LAST)) { bs[nb] = s0; break; }
+        int64_t b = PNB;
+        while (2 * b < r) b *= 2;
+        bs[nb++] = s0;
+        s0 += b;
+    }
+    const int64_t h = bs[1], sl = bs[nb], nl = d - sl;
+    // product scratch (doubles): the auxiliary levels (h * h), Trest (rows h .. d, row
+    // pitch sl, columns 0 .. sl), the last block's levels (nl * nl); with m = d - h <= h:
+    // h * h + m * sl + nl * nl <= h * h + m * d + m * m <= d * d
+    double* Saux = c.T;
+    double* Trest = c.T + h * h;
+    double* Smain = Trest + (d - h) * sl;
+    auto trow = [&](int64_t r) { return Trest + (r - h) * sl; };
 
     AuxStream* aux = nullptr;
     if ((st = aux_stream(aux)) != GPTQ_OK) return st;
     PrepCtx ca = c;
     ca.s = aux->s;
-    // columns [0, h) of L and the inverted diagonal blocks below h are final once the
-    // step that forms panel h / 64 - 1 has been enqueued (step h / 64 - 2; before the
-    // loop when h = 64)
-    const int64_t fork_step = std::max<int64_t>(h / PNB - 2, (d - AUX_FORK_REST) / PNB);
-    auto fork = [&]() -> gptq_status {
+    // block i's columns are final once the step that forms the panel of its last 64
+    // columns has been enqueued (step bs[i + 1] / 64 - 2; before the loop when negative)
+    int64_t fork_step[64];
+    for (int i = 0; i < nb; ++i) {
+        fork_step[i] = bs[i + 1] / PNB - 2;
+        if (i == 0) fork_step[i] = std::max<int64_t>(fork_step[i], (d - AUX_FORK_REST) / PNB);
+        else fork_step[i] = std::max(fork_step[i], fork_step[i - 1]);
+    }
+    auto fork = [&](int i) -> gptq_status {
         if (hipEventRecord(aux->fork, c.s) != hipSuccess || hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess)
             return GPTQ_ERR_HIP;
+        const int64_t b0 = bs[i], b1 = bs[i + 1], len = b1 - b0, below = d - b1;
         gptq_status r;
-        if ((r = trtri_block(ca, 0, h, T11, AUX_MAX_WG)) != GPTQ_OK) return r;
-        // T = L21 X11   (m x h, X11 lower triangular)
-        if ((r = gemm(ca, T11, ldt, c.A + h * d, d, c.X, d, (int)m, (int)h, (int)h, 1.0, 0.0, G_TRI_B, 1, 0, 0, 0,
-                       0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+        if ((r = trtri_block(ca, b0, len, Saux, AUX_MAX_WG)) != GPTQ_OK) return r;
+        if (i > 0) {
+            // X[B_i][P_i] = -X[B_i][B_i] Trest[B_i][P_i]   (lower triangular X block)
+            if ((r = gemm(ca, c.X + b0 * d, d, c.X + b0 * d + b0, d, trow(b0), sl, (int)len, (int)b0, (int)len, -1.0,
+                          0.0, G_TRI_A, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+                return r;
+            // Trest[after B_i][P_i] += L[after B_i][B_i] X[B_i][P_i]
+            if ((r = gemm(ca, trow(b1), sl, c.A + b1 * d + b0, d, c.X + b0 * d, d, (int)below, (int)b0, (int)len, 1.0,
+                          1.0, 0, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+                return r;
+        }
+        // Trest[after B_i][B_i] = L[after B_i][B_i] X[B_i][B_i]   (lower triangular X block)
+        if ((r = gemm(ca, trow(b1) + b0, sl, c.A + b1 * d + b0, d, c.X + b0 * d + b0, d, (int)below, (int)len, (int)len,
+                      1.0, 0.0, G_TRI_B, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
             return r;
         if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
         return GPTQ_OK;
     };
-    const int64_t fork_step2 = std::max<int64_t>(s2 / PNB - 2, fork_step);
-    auto fork2 = [&]() -> gptq_status {
-        if (hipEventRecord(aux->fork, c.s) != hipSuccess || hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess)
-            return GPTQ_ERR_HIP;
-        gptq_status r;
-        if ((r = trtri_block(ca, h, h2, T2b, AUX_MAX_WG)) != GPTQ_OK) return r;
-        // T2 = L[s2 ..][h .. s2) X[h .. s2)   (m2 x h2, lower triangular X block)
-        if ((r = gemm(ca, T2, ldt, c.A + s2 * d + h, d, c.X + h * d + h, d, (int)m2, (int)h2, (int)h2, 1.0, 0.0,
-                       G_TRI_B, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
-            return r;
-        // with Q = [h, s2), R = [s2, d) and P = [0, h): X[Q][P] = -X[Q][Q] T[Q], T[Q] =
-        // L[Q][P] X[P][P] the first h2 rows of T (h2 x h, lower triangular X block) ...
-        if ((r = gemm(ca, c.X + h * d, d, c.X + h * d + h, d, T11, ldt, (int)h2, (int)h, (int)h2, -1.0, 0.0, G_TRI_A,
-                       1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
-            return r;
-        // ... and V = L[R][P] X[P][P] + L[R][Q] X[Q][P] in place of T's last m2 rows, so
-        // that X[R][P] = -X[R][R] V needs only the last block's inverse
-        if ((r = gemm(ca, T11 + h2 * ldt, ldt, c.A + s2 * d + h, d, c.X + h * d, d, (int)m2, (int)h, (int)h2, 1.0, 1.0, 0,
-                       1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
-            return r;
-        if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
-        return GPTQ_OK;
-    };
-    if (fork_step < 0 && (st = fork()) != GPTQ_OK) return st;
+    int nf = 0;   // blocks handed to the auxiliary stream
+    while (nf < nb && fork_step[nf] < 0)
+        if ((st = fork(nf++)) != GPTQ_OK) return st;
     for (int64_t k0 = 0; k0 < d; k0 += PNB) {
         const int n = (int)std::min<int64_t>(PNB, d - k0);
         const int64_t rest = d - k0 - n;
@@ -1046,29 +1051,22 @@ static gptq_status cholinv(PrepCtx& c) {
                        G_BT | G_LOWER_C | G_DIAG0 | G_PANEL1, 1, 0, 0, 0, 0, k0 + n,
                        (int)std::min<int64_t>(PNB, rest), (int)(k0 / PNB) + 1)) != GPTQ_OK)
             return st;
-        if (k0 / PNB == fork_step && (st = fork()) != GPTQ_OK) return st;
-        if (h2 > 0 && k0 / PNB == fork_step2 && (st = fork2()) != GPTQ_OK) return st;
+        while (nf < nb && fork_step[nf] == k0 / PNB)
+            if ((st = fork(nf++)) != GPTQ_OK) return st;
     }
-    if (h2 > 0) {
-        // the last block R = [s2, d), then [X[R][P] X[R][Q]] = -X[R][R] [V T2]
-        if ((st = trtri_block(c, s2, m2, T22)) != GPTQ_OK) return st;
-        if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
-        return gemm(c, c.X + s2 * d, d, c.X + s2 * d + s2, d, T11 + h2 * ldt, ldt, (int)m2, (int)s2, (int)m2, -1.0,
-                    0.0, G_TRI_A);
-    }
-    if ((st = trtri_block(c, h, m, T22)) != GPTQ_OK) return st;
+    while (nf < nb)
+        if ((st = fork(nf++)) != GPTQ_OK) return st;
+    // the last block's inverse, then X[last][P] = -X[last][last] Trest[last][P]
+    if ((st = trtri_block(c, sl, nl, Smain)) != GPTQ_OK) return st;
     if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
-    // X21 = -X22 T   (X22 lower triangular)
-    return gemm(c, c.X + h * d, d, c.X + h * d + h, d, T11, ldt, (int)m, (int)h, (int)m, -1.0, 0.0, G_TRI_A);
+    return gemm(c, c.X + sl * d, d, c.X + sl * d + sl, d, trow(sl), sl, (int)nl, (int)sl, (int)nl, -1.0, 0.0, G_TRI_A);
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static size_t t_bytes(int64_t d) {
-    // product scratch: max(h * h, m * s2) doubles for the leading block's levels and T
-    // (m x h) beside T2 (m2 x h2), h2 * h2 for the levels of the trailing block's leading
-    // part, m2 * m2 for its last part; with h2 + m2 = m = d - h <= h and s2 <= d:
-    // max(h * h, m * d) + m * m <= d * d
+    // product scratch: h * h doubles for the auxiliary levels, (d - h) * sl for Trest,
+    // nl * nl for the last block's levels; at most d * d (see cholinv)
     return (size_t)d * d * sizeof(double);
 }
 
