@@ -70,6 +70,37 @@ GPTQ_DEV void static_for(F&& f) {
     }
 }
 
+// One direct global -> LDS load (global_load_lds_dwordx4, scalar-base form): lane i
+// reads 16 bytes at sbase + voff_i and they land at LDS byte address m0base + MOFF +
+// 16 i (M0 is formed in the asm from one wave-uniform register and a compile-time
+// offset, so no register per slot and load stays live).
+// (Written as inline asm: the compiler counts the builtin's LDS write against every
+// later LDS read of the array and inserts a full vmcnt(0) wait before it, which would
+// leave no load in flight; the callers place the waits explicitly, and the asm has no
+// register results, the data going to LDS only.)
+template <uint32_t MOFF>
+GPTQ_DEV void dma16(uint32_t voff, const void* sbase, uint32_t m0base) {
+    // the base and M0 are wave-uniform; readfirstlane makes that visible to the
+    // compiler, which must place them in scalar registers
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t mu = __builtin_amdgcn_readfirstlane(m0base);
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(bu), "s"(mu), "i"(MOFF) : "memory", "scc");
+}
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0), expcnt not waited for.
+template <int VM>
+GPTQ_DEV void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (0x7 << 4) | ((VM >> 4) << 14));
+}
+
+GPTQ_DEV uint32_t lds_addr(const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
 // Launch-error helper for the host side.
 #define GPTQ_LAUNCH_CHECK()                                   \
     do {                                                      \

@@ -91,33 +91,6 @@ GPTQ_DEV int swz(int k, int c) {
     return c ^ (f << 1);
 }
 
-// One direct global -> LDS load (global_load_lds_dwordx4, scalar-base form): lane i
-// reads 16 bytes at sbase + voff_i and they land at LDS byte address lds_base + 16 i
-// (sbase and lds_base wave-uniform; lds_base is passed in M0).  Written as inline asm:
-// the compiler counts the builtin's LDS write against every later LDS read of the
-// array and inserts a full vmcnt(0) wait before it, which would leave no load in
-// flight; here the waits are explicit (the asm has no register results, the data
-// goes to LDS only).
-// One direct global -> LDS load (global_load_lds_dwordx4, scalar-base form): lane i
-// reads 16 bytes at sbase + voff_i and they land at LDS byte address m0base + MOFF +
-// 16 i (M0 is formed in the asm from one wave-uniform register and a compile-time
-// offset, so no register per slot and load stays live).
-template <uint32_t MOFF>
-GPTQ_DEV void dma16(uint32_t voff, const void* sbase, uint32_t m0base) {
-    // the base and M0 are wave-uniform; readfirstlane makes that visible to the
-    // compiler, which must place them in scalar registers
-    const uint64_t b = (uint64_t)(uintptr_t)sbase;
-    const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t mu = __builtin_amdgcn_readfirstlane(m0base);
-    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(bu), "s"(mu), "i"(MOFF) : "memory", "scc");
-}
-
-GPTQ_DEV uint32_t lds_addr(const uint16_t* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
-}
-
 // Per-wave constants of the stage copy.  Wave w issues loads HB_DMA w .. HB_DMA w +
 // HB_DMA - 1 of 1 KB each; load i (of the wave) covers operand (HB_DMA w) / 16 (0: the
 // c0 channel block, 1: c1), token rows kb + 2 i and kb + 2 i + 1 (kb = 2 ((HB_DMA w) mod

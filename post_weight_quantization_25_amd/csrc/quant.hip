@@ -130,6 +130,7 @@ struct TrailArgs {
     const uint16_t* Uhi; const uint16_t* Ulo;                // U (bf16 hi + lo), d_col x d_col
     int64_t k0; int K;
     int64_t n_beg, n_end;
+    int64_t m_beg;                                           // first row of the launch's tiles
 };
 
 struct TrailStage {
@@ -229,7 +230,7 @@ GPTQ_DEV void trail_mfma(const TrailStage& st, int wr, int wc, int lane, f32x16_
 
 __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
     __shared__ __attribute__((aligned(16))) TrailStage stg[2];
-    const int64_t m0 = (int64_t)blockIdx.y * TB;
+    const int64_t m0 = a.m_beg + (int64_t)blockIdx.y * TB;
     const int64_t n0 = a.n_beg + (int64_t)blockIdx.x * TB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
@@ -287,12 +288,211 @@ __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
     }
 }
 
+// --------------------------------------------------------------------------
+// Whole 128 x 128 tiles: the same product with the operands copied to LDS by direct
+// global -> LDS loads (global_load_lds_dwordx4) into a ring of four 32-deep stages,
+// issued three stages ahead, and the fragment reads of the next 16-deep slice
+// overlapped with the MFMAs of the current one.  A stage holds E hi, E lo, U hi, U lo
+// (8 KB each); wave w copies operand w.  E rows (64 bytes, four 16-byte chunks) are
+// stored with chunk q at q ^ eswz(row) and read with 16-byte reads; U rows (256 bytes)
+// with chunk c at tswz(row, c) and read with ds_read_b64_tr_b16; both are free of bank
+// conflicts for 8- and 16-lane groups.
+constexpr int TD_NSTG = 4;
+constexpr int TD_OPE = TK * TB;                  // bf16 elements of one operand tile
+constexpr int TD_STE = 4 * TD_OPE;               // one stage
+constexpr int TD_DMA = TD_OPE * 2 / 1024;        // 1 KB loads per wave and stage
+constexpr int TD_VM = (TD_NSTG - 2) * TD_DMA;    // loads left in flight at a stage wait
+static_assert(TD_NSTG * TD_STE * 2 <= 160 * 1024, "LDS ring exceeds the workgroup's LDS");
+
+GPTQ_DEV int eswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+GPTQ_DEV int tswz(int k, int c) {
+    const int r = k & 3;
+    const int f = 2 * r + ((r ^ (r >> 1)) & 1);
+    return c ^ (f << 1);
+}
+
+struct TrailCopy {
+    uint32_t voff[TD_DMA];   // per-lane byte offsets of the wave's loads (row and chunk)
+    const uint16_t* base;    // the wave's operand at stage 0 (wave-uniform)
+    int64_t sstride;         // elements between stages
+    uint32_t m0base;         // LDS byte address of the wave's operand tile in slot 0
+};
+
+GPTQ_DEV TrailCopy trail_copy_setup(const TrailArgs& a, const uint16_t* ring0, int64_t m0, int64_t n0, int wave,
+                                    int lane) {
+    TrailCopy tc;
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    tc.m0base = lds_addr(ring0) + (uint32_t)(w * TD_OPE * 2);
+    if (w < 2) {   // E hi / lo: load i covers rows 16 i .. 16 i + 15, lane l row 16 i + l / 4
+        tc.base = (w ? a.Elo : a.Ehi) + m0 * a.lde;
+        tc.sstride = TK;
+#pragma unroll
+        for (int i = 0; i < TD_DMA; ++i) {
+            const int r = 16 * i + (lane >> 2), q = (lane & 3) ^ eswz(r);
+            tc.voff[i] = (uint32_t)(((int64_t)r * a.lde + 8 * q) * 2);
+        }
+    } else {       // U hi / lo: load i covers rows 4 i .. 4 i + 3, lane l row 4 i + l / 16
+        tc.base = (w == 2 ? a.Uhi : a.Ulo) + a.k0 * a.d_col + n0;
+        tc.sstride = (int64_t)TK * a.d_col;
+#pragma unroll
+        for (int i = 0; i < TD_DMA; ++i) {
+            const int r = 4 * i + (lane >> 4), c = tswz(r, lane & 15);
+            tc.voff[i] = (uint32_t)(((int64_t)r * a.d_col + 8 * c) * 2);
+        }
+    }
+    return tc;
+}
+
+template <int SLOT>
+GPTQ_DEV void trail_issue(const TrailCopy& tc, int st) {
+    const uint16_t* sbase = tc.base + st * tc.sstride;
+    static_for<0, TD_DMA>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        dma16<(uint32_t)(SLOT * TD_STE * 2 + i * 1024)>(tc.voff[i], sbase, tc.m0base);
+    });
+}
+
+struct TdFrags { bf16x8_t ah[2], al[2], bh[2], bl[2]; };
+
+// B operand from a swizzled U tile (as trail_bfrag, with the chunk swizzle)
+GPTQ_DEV bf16x8_t td_bfrag(const uint16_t* tile, int nc0, int kk, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int n = nc0 + (g & 1) * 16 + 4 * (j & 3);
+    const int k = kk + (g >> 1) * 8 + (j >> 2);
+    const int c = n >> 3, half = (n >> 2) & 1;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(tile + k * TB + 8 * tswz(k, c) + 4 * half));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(tile + (k + 4) * TB + 8 * tswz(k + 4, c) + 4 * half));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// one wave's fragments for the 16-deep slice kk of a stage: A (rows wr * 64 + 32 i +
+// lane % 32, k = kk + 8 (lane / 32) .. + 7) with 16-byte reads, B transposed
+GPTQ_DEV void td_read(const uint16_t* stg, int kk, int wr, int wc, int lane, TdFrags& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = wr * 64 + i * 32 + (lane & 31), q = (kk >> 3) + (lane >> 5);
+        const int o = m * TK + 8 * (q ^ eswz(m));
+        f.ah[i] = *reinterpret_cast<const bf16x8_t*>(stg + o);
+        f.al[i] = *reinterpret_cast<const bf16x8_t*>(stg + TD_OPE + o);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        f.bh[j] = td_bfrag(stg + 2 * TD_OPE, wc * 64 + j * 32, kk, lane);
+        f.bl[j] = td_bfrag(stg + 3 * TD_OPE, wc * 64 + j * 32, kk, lane);
+    }
+}
+
+// the three products, product-major (the four accumulators take turns)
+GPTQ_DEV void td_mfma(const TdFrags& f, f32x16_t (&acc)[2][2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[i], f.bh[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[i], f.bl[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.al[i], f.bh[j], acc[i][j], 0, 0, 0);
+    // 12 fragment reads of the next slice against 12 MFMAs: one each, in turn
+    static_for<0, 12>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
+}
+
+__global__ __launch_bounds__(256, 1) void trail_dma_kernel(TrailArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds_ring[TD_NSTG * TD_STE];
+    const uint16_t* ring[TD_NSTG];
+    static_for<0, TD_NSTG>([&](auto I) { ring[decltype(I)::value] = lds_ring + decltype(I)::value * TD_STE; });
+    const int64_t m0 = a.m_beg + (int64_t)blockIdx.y * TB;
+    const int64_t n0 = a.n_beg + (int64_t)blockIdx.x * TB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    const int nst = a.K / TK;
+    // loads of stages past the last re-load the last one (addresses stay inside the
+    // operands), so that every step leaves the same number of loads in flight
+    auto t0 = [&](int st) { return st < nst ? st : nst - 1; };
+    const TrailCopy tc = trail_copy_setup(a, lds_ring, m0, n0, wave, lane);
+    static_for<0, TD_NSTG - 1>([&](auto I) { trail_issue<decltype(I)::value>(tc, t0(decltype(I)::value)); });
+    wait_vm_lgkm0<TD_VM>();
+    __syncthreads();
+    trail_issue<TD_NSTG - 1>(tc, t0(TD_NSTG - 1));
+    TdFrags f0, f1;
+    td_read(ring[0], 0, wr, wc, lane, f0);
+    for (int st = 0; st < nst; st += TD_NSTG) {
+        static_for<0, TD_NSTG>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if (st + u < nst) {
+                td_read(ring[u], 16, wr, wc, lane, f1);
+                td_mfma(f0, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_lgkm0<TD_VM>();
+                __syncthreads();
+                trail_issue<u>(tc, t0(st + u + TD_NSTG));
+                td_read(ring[(u + 1) % TD_NSTG], 0, wr, wc, lane, f0);
+                td_mfma(f1, acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the trailing re-loads land before the workgroup ends
+    // W -= acc (whole tile): all loads first, then all stores
+    float* wbase = a.Wws + (m0 + wr * 64 + 4 * (lane >> 5)) * a.d_col + n0 + wc * 64 + (lane & 31);
+    auto off = [&](int i, int j, int e) { return (int64_t)(i * 32 + 8 * (e >> 2) + (e & 3)) * a.d_col + j * 32; };
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float old[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) old[e] = wbase[off(i, j, e)];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) wbase[off(i, j, e)] = old[e] - acc[i][j][e];
+        }
+}
+
+// Whole tiles on the direct-load kernel when the operands allow 16-byte loads at every
+// row (K a multiple of 32, row pitches multiples of 8 elements, aligned arrays); the
+// partial last row and column of tiles (and everything otherwise) on trail_kernel.
 static gptq_status trail(const TrailArgs& ta, hipStream_t s) {
     if (ta.n_end <= ta.n_beg || ta.K <= 0 || ta.d_row <= 0) return GPTQ_OK;
-    dim3 grid((unsigned)((ta.n_end - ta.n_beg + TB - 1) / TB), (unsigned)((ta.d_row + TB - 1) / TB));
-    trail_kernel<<<grid, 256, 0, s>>>(ta);
-    GPTQ_LAUNCH_CHECK();
-    return GPTQ_OK;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool dma = ta.K % TK == 0 && (ta.lde & 7) == 0 && (ta.d_col & 7) == 0 && (ta.n_beg & 7) == 0 &&
+                     ta.d_col < ((int64_t)1 << 25) && ta.lde < ((int64_t)1 << 20) && al16(ta.Ehi) && al16(ta.Elo) &&
+                     al16(ta.Uhi) && al16(ta.Ulo);
+    const int64_t mf = dma ? (ta.d_row / TB) * TB : 0;                             // rows of whole tiles
+    const int64_t nf = dma ? ta.n_beg + ((ta.n_end - ta.n_beg) / TB) * TB : ta.n_beg;   // columns of whole tiles
+    if (mf > 0 && nf > ta.n_beg) {
+        TrailArgs t = ta;
+        t.m_beg = 0;
+        trail_dma_kernel<<<dim3((unsigned)((nf - ta.n_beg) / TB), (unsigned)(mf / TB)), 256, 0, s>>>(t);
+        GPTQ_LAUNCH_CHECK();
+    }
+    auto edge = [&](int64_t m_beg, int64_t m_end, int64_t n_beg, int64_t n_end) -> gptq_status {
+        if (m_end <= m_beg || n_end <= n_beg) return GPTQ_OK;
+        TrailArgs t = ta;
+        t.m_beg = m_beg; t.d_row = m_end; t.n_beg = n_beg; t.n_end = n_end;
+        trail_kernel<<<dim3((unsigned)((n_end - n_beg + TB - 1) / TB), (unsigned)((m_end - m_beg + TB - 1) / TB)), 256,
+                       0, s>>>(t);
+        GPTQ_LAUNCH_CHECK();
+        return GPTQ_OK;
+    };
+    gptq_status st;
+    if (mf > 0 && nf > ta.n_beg) {
+        if ((st = edge(0, mf, nf, ta.n_end)) != GPTQ_OK) return st;      // last column of tiles
+        return edge(mf, ta.d_row, ta.n_beg, ta.n_end);                    // last row of tiles
+    }
+    return edge(0, ta.d_row, ta.n_beg, ta.n_end);
 }
 
 // --------------------------------------------------------------------------
@@ -465,7 +665,7 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         st = sweep_launch(sa, s);
         if (st != GPTQ_OK) return st;
         // everything after the super-block, K = s1 - s0
-        TrailArgs tb{Wws, d_row, d_col, Ehi, Elo, QSB, Uhi, Ulo, s0, (int)(s1 - s0), s1, d_col};
+        TrailArgs tb{Wws, d_row, d_col, Ehi, Elo, QSB, Uhi, Ulo, s0, (int)(s1 - s0), s1, d_col, 0};
         if ((st = trail(tb, s)) != GPTQ_OK) return st;
     }
     return GPTQ_OK;
