@@ -470,6 +470,19 @@ def dequantize(codes: np.ndarray, scales16: np.ndarray, zeros: np.ndarray, group
     return (s * (codes.astype(np.float32) - z)).astype(np.float32)
 
 
+def linear(x: np.ndarray, codes: np.ndarray, scales16: np.ndarray, zeros: np.ndarray,
+           group_size: int) -> np.ndarray:
+    """y = x What^T in fp64, What = dequantize(codes, scales16, zeros, group_size): the
+    layer's output on its quantized weights, for activations stored tokens x d_col.
+
+    [GPTQ summary page, layer-wise objective (the layer computes W X; here X is tokens
+     x d_col, so the output is X W^T) and its results on inference with the packed
+     weights]
+    """
+    What = dequantize(codes, scales16, zeros, group_size).astype(np.float64)
+    return np.asarray(x, dtype=np.float64) @ What.T
+
+
 # ---------------------------------------------------------------------------
 # The layer objective.
 
