@@ -11,6 +11,11 @@ Options: --steps K --warmup W --gpus N (only 1 is supported: the path runs on on
 GPU) --no-cpu-baseline --calibrate-copy (adds, after the timed region, one plain
 elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 multiply by 1), used to
 scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
+
+--linear measures, instead of the layer step, the product of the quantized layer with
+activations read from the stored format (gptq_quantized_linear) for 1, 4 and 16
+tokens, beside torch's bf16 product with the unquantized weights, and prints its own
+JSON line.
 """
 from __future__ import annotations
 
@@ -37,6 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--linear", action="store_true")
     return ap.parse_args()
 
 
@@ -96,6 +102,60 @@ def cpu_baseline(layer, sample_tokens: int, sample_rows: int):
                    f"extrapolated {total:.1f} s per layer; input generation {t_gen:.1f} s not counted"),
         "seconds_per_layer": total,
     }
+
+
+def linear_bench(args, g, q, W, r, d):
+    """Time gptq_quantized_linear on the quantized metric layer for 1, 4 and 16 bf16
+    tokens, and torch's bf16 product with the unquantized weights on the same
+    activations.  Each is captured as a graph of 100 back-to-back calls (so that host
+    launch overhead does not hide the kernel time) and replayed: HIP events around 5
+    replays after 2 warm-up replays, mean per call."""
+    import torch
+    reps = 100
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(reps):
+                f()
+        for _ in range(2):
+            gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / (5 * reps)
+
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    per = {}
+    for nt in (1, 4, 16):
+        x = torch.randn((nt, d), generator=gen, device="cuda").to(torch.bfloat16)
+        y = torch.empty((nt, r), dtype=torch.bfloat16, device="cuda")
+        yb = torch.empty((nt, r), dtype=torch.bfloat16, device="cuda")
+        us_q = timed(lambda: g.linear(q, x, out=y))
+        us_b = timed(lambda: torch.matmul(x, W.t(), out=yb))
+        # algorithmic bytes: codes, scales and zeros once, activations in, outputs out
+        byt = r * d // 2 + 2 * 2 * r * (d // 128) + 2 * nt * d + 2 * nt * r
+        per[str(nt)] = {"us": us_q, "bf16_matmul_us": us_b, "speedup": us_b / us_q,
+                        "algorithmic_bytes": byt, "GBps": byt / (us_q * 1e-6) / 1e9}
+    one = per["1"]
+    rec = {
+        "metric": "quantized linear (int4 g128 codes read directly) time per call, 1 token, 4096x4096",
+        "value": one["us"], "unit": "us", "n_gpus": 1, "steps": 5 * reps, "warmup": 2 * reps,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "the quantized attention projection of the layer step (4096x4096, int4 asym g128), "
+                               "bf16 activations of 1, 4 and 16 tokens, bf16 output", "d_row": r, "d_col": d},
+        "per_tokens": per,
+        "roofline": {"kernel": "linear_kernel (1 token)", "bound": "hbm", "achieved": one["GBps"],
+                     "peak": HBM_GBS, "unit": "GB/s", "frac": one["GBps"] / HBM_GBS, "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -163,6 +223,9 @@ def main():
     torch.cuda.synchronize()
     g.check_info(info, "prepare_hinv")
     g.check_info(q.info, "quantize_layer")
+    if args.linear:
+        linear_bench(args, g, q, W, r, d)
+        return
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()

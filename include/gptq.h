@@ -179,6 +179,32 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16,
                             int32_t bits, int32_t group_size,
                             void* W_out, gptq_dtype out_dtype, void* stream);
 
+/*
+ * The layer's product on its quantized weights, read from the stored format:
+ *   y[t][r] = sum_c x[t][c] * What[r][c],  What[r][c] = S16[r][g] * (u[r][c] - z[r][g]),
+ * accumulated in fp32 (per 32-column piece of one group: sum of x * (u - z), then
+ * times S16), rounded once to y_dtype.
+ *
+ * Sources: GPTQ summary page, layer-wise objective (the layer computes W X; with
+ * activations stored tokens x d_col the output is X W^T) and its results on
+ * inference with the packed weights; Quantization concepts guide, "Mapping values to
+ * fewer bits" (x ~= S (q - Z)) and "Data types - int8 and int4".
+ *
+ *  codes, scales_f16, zeros_f16   as written by gptq_quantize_layer (bits, group_size
+ *             as there: 3 or 4 two per byte, 8 one per byte; group 0 = per row).
+ *  x          n_tokens x d_col, row pitch ldx >= d_col elements, dtype x_dtype.
+ *  y          n_tokens x d_row (row pitch d_row), dtype y_dtype; written, not read.
+ * Any even d_col works; d_col a multiple of 32 with 16-byte aligned code rows and x
+ * rows takes the fast kernel (codes streamed once per four tokens).
+ * Errors: negative sizes, bad dtypes or group width -> GPTQ_ERR_INVALID_ARG; bits not
+ * 3/4/8 -> GPTQ_ERR_UNSUPPORTED; zero sizes are a no-op.
+ */
+gptq_status gptq_quantized_linear(const uint8_t* codes, const uint16_t* scales_f16,
+                                  const uint16_t* zeros_f16, int64_t d_row, int64_t d_col,
+                                  int32_t bits, int32_t group_size,
+                                  const void* x, gptq_dtype x_dtype, int64_t n_tokens, int64_t ldx,
+                                  void* y, gptq_dtype y_dtype, void* stream);
+
 /* Host: a static message for a status code. */
 const char* gptq_status_string(gptq_status s);
 

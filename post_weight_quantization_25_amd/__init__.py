@@ -48,6 +48,8 @@ def _load():
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
+        "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
+                                                 vp, ctypes.c_int, vp]),
         "gptq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -188,6 +190,26 @@ def dequantize(q: Quantized, out_dtype=torch.float32, out: torch.Tensor | None =
     _check(lib.gptq_dequantize(q.codes.data_ptr(), q.scales.data_ptr(), q.zeros.data_ptr(), d_row, q.d_col,
                                q.bits, q.group_size, out.data_ptr(), _DT[out.dtype], _stream(stream)),
            "gptq_dequantize")
+    return out
+
+
+def linear(q: Quantized, x: torch.Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """y = x What^T on the stored format (What as ``dequantize`` defines it), fp32 accumulation.
+    x may be a row-strided view (its row pitch is passed as ldx)."""
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if x.dtype not in _DT or x.dim() != 2 or x.shape[1] != q.d_col or (x.shape[0] > 0 and x.stride(1) != 1):
+        raise ValueError("x must be a (n_tokens, d_col) f32/bf16/f16 tensor with unit column stride")
+    d_row, n = q.codes.shape[0], x.shape[0]
+    if out is None:
+        out = torch.empty((n, d_row), dtype=out_dtype, device=x.device)
+    if not out.is_contiguous() or tuple(out.shape) != (n, d_row):
+        raise ValueError("out must be a contiguous (n_tokens, d_row) tensor")
+    _check(lib.gptq_quantized_linear(q.codes.data_ptr(), q.scales.data_ptr(), q.zeros.data_ptr(), d_row, q.d_col,
+                                     q.bits, q.group_size, x.data_ptr(), _DT[x.dtype], n, max(x.stride(0), q.d_col),
+                                     out.data_ptr(), _DT[out.dtype], _stream(stream)),
+           "gptq_quantized_linear")
     return out
 
 

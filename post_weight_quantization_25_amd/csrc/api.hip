@@ -86,6 +86,22 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, co
                           (hipStream_t)stream);
 }
 
+gptq_status gptq_quantized_linear(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* zeros_f16,
+                                  int64_t d_row, int64_t d_col, int32_t bits, int32_t group_size, const void* x,
+                                  gptq_dtype x_dtype, int64_t n_tokens, int64_t ldx, void* y, gptq_dtype y_dtype,
+                                  void* stream) {
+    if (d_row < 0 || d_col < 0 || n_tokens < 0 || group_size < 0) return GPTQ_ERR_INVALID_ARG;
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return GPTQ_ERR_INVALID_ARG;
+    if (bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_UNSUPPORTED;
+    if (group_size > 0 && d_col % group_size != 0) return GPTQ_ERR_INVALID_ARG;
+    if (bits <= 4 && (d_col & 1)) return GPTQ_ERR_INVALID_ARG;
+    if (d_row == 0 || d_col == 0 || n_tokens == 0) return GPTQ_OK;
+    if (!codes || !scales_f16 || !zeros_f16 || !x || !y || ldx < d_col) return GPTQ_ERR_INVALID_ARG;
+    if (d_row > 2147483647LL / 64 || d_col > 2147483647LL / 64) return GPTQ_ERR_UNSUPPORTED;
+    return linear_launch(codes, scales_f16, zeros_f16, d_row, d_col, bits, group_size, x, x_dtype, n_tokens, ldx, y,
+                         y_dtype, (hipStream_t)stream);
+}
+
 const char* gptq_status_string(gptq_status s) {
     switch (s) {
         case GPTQ_OK: return "ok";

@@ -26,4 +26,8 @@ gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const u
                            int64_t d_col, int bits, int group_size, void* out, gptq_dtype out_dtype,
                            hipStream_t stream);
 
+gptq_status linear_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
+                          int64_t d_col, int bits, int group_size, const void* x, gptq_dtype x_dtype, int64_t n_tok,
+                          int64_t ldx, void* y, gptq_dtype y_dtype, hipStream_t stream);
+
 }  // namespace gptq

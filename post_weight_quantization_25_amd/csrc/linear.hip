@@ -1,0 +1,241 @@
+// The layer's product on its quantized weights, read straight from the stored format:
+// y[t][r] = sum_c x[t][c] What[r][c], What[r][c] = S16[r][g] (u[r][c] - z[r][g]), with
+// fp32 accumulation.
+//
+// GPTQ summary page, layer-wise objective (the layer computes W X; with activations
+// stored tokens x d_col the output is X W^T) and its results on inference with the
+// packed weights; Quantization concepts guide, "Mapping values to fewer bits"
+// (x ~= S (q - Z)) and "Data types - int8 and int4" (two int4 values per byte, the
+// first in the low nibble).
+//
+// Decode-shaped (few tokens): the product streams the codes once and is bound by
+// their bytes.  A workgroup of four waves owns 16 rows (four per wave); the 64 lanes
+// of a wave take 32-column chunks in turn (lane l: chunks l, l + 64, ..), so each
+// wave reads a row's codes as contiguous 1 KB pieces.  Per chunk the group's scale
+// and zero are loaded once; the 32 products x (u - z) are summed in fp32 and scaled
+// by S once (the sum of a group's products is exact up to its fp32 roundings; S is
+// factored out of the chunk).  The lanes' partial sums of a row are added with a
+// butterfly over the wave.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gptq {
+
+struct LinArgs {
+    const uint8_t* codes; int64_t code_ld;            // bytes per row
+    const uint16_t* scales; const uint16_t* zeros;    // fp16, d_row x n_groups
+    int n_groups; int64_t G;                          // group width in columns (d_col when per row)
+    const void* x; int64_t ldx; int64_t n_tok;
+    void* y; int64_t ldy;
+    int64_t d_row, d_col;
+};
+
+#ifndef LIN_ROWS
+#define LIN_ROWS 2
+#endif
+constexpr int LROWS = LIN_ROWS;              // rows per wave
+#ifndef LIN_WAVES
+#define LIN_WAVES 4
+#endif
+constexpr int LWAVES = LIN_WAVES;
+constexpr int LCH = 32;                      // columns per chunk
+
+template <gptq_dtype DT>
+GPTQ_DEV void load_x8(const void* base, int64_t idx, float (&v)[8]) {   // 8 values, 16-byte aligned
+    if constexpr (DT == GPTQ_F32) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(base) + idx);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(base) + idx + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+    } else {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint16_t lo = (uint16_t)(w[e] & 0xffffu), hi = (uint16_t)(w[e] >> 16);
+            if constexpr (DT == GPTQ_BF16) { v[2 * e] = bf16_bits_to_f32(lo); v[2 * e + 1] = bf16_bits_to_f32(hi); }
+            else { v[2 * e] = f16_bits_to_f32(lo); v[2 * e + 1] = f16_bits_to_f32(hi); }
+        }
+    }
+}
+
+template <gptq_dtype YT>
+GPTQ_DEV void store_y(void* y, int64_t idx, float v) {
+    if constexpr (YT == GPTQ_F32) reinterpret_cast<float*>(y)[idx] = v;
+    else if constexpr (YT == GPTQ_BF16) reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16_bits(v);
+    else reinterpret_cast<uint16_t*>(y)[idx] = f32_to_f16_bits(v);
+}
+
+GPTQ_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Fast path: d_col a multiple of 32, rows of codes and x 16-byte aligned.  NT tokens per
+// pass; PACKED: two codes per byte (16 bytes per chunk), else one per byte (32 bytes).
+template <bool PACKED, int NT, gptq_dtype XT, gptq_dtype YT>
+__global__ __launch_bounds__(64 * LWAVES) void linear_kernel(LinArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = ((int64_t)blockIdx.x * LWAVES + wave) * LROWS;
+    const int nch = (int)(a.d_col / LCH);
+    for (int64_t t0 = 0; t0 < a.n_tok; t0 += NT) {
+        float acc[LROWS][NT];
+#pragma unroll
+        for (int i = 0; i < LROWS; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[i][t] = 0.f;
+        for (int j = lane; j < nch; j += 64) {
+            const int64_t c0 = (int64_t)j * LCH;
+            float xv[NT][LCH];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int64_t tt = (t0 + t < a.n_tok) ? t0 + t : a.n_tok - 1;   // a repeated token past the end
+#pragma unroll
+                for (int q = 0; q < LCH / 8; ++q) {
+                    float v8[8];
+                    load_x8<XT>(a.x, tt * a.ldx + c0 + 8 * q, v8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xv[t][8 * q + e] = v8[e];
+                }
+            }
+            const int g = (int)(c0 / a.G);
+            // every row's codes, scale and zero first (rows past the end re-read the last
+            // row; their sums are not stored), so the loads are in flight together
+            uint32_t cw[LROWS][8];
+            float S[LROWS], z[LROWS];
+#pragma unroll
+            for (int i = 0; i < LROWS; ++i) {
+                const int64_t r = (r0 + i < a.d_row) ? r0 + i : a.d_row - 1;
+                const uint8_t* crow = a.codes + r * a.code_ld;
+                if constexpr (PACKED) {
+                    // nibbles 0, 2, 4, .. and 1, 3, 5, .. of a word as bytes
+                    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(crow + c0 / 2);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        cw[i][2 * e] = w[e] & 0x0F0F0F0Fu;
+                        cw[i][2 * e + 1] = (w[e] >> 4) & 0x0F0F0F0Fu;
+                    }
+                } else {
+                    const u32x4_t w0 = *reinterpret_cast<const u32x4_t*>(crow + c0);
+                    const u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(crow + c0 + 16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { cw[i][e] = w0[e]; cw[i][4 + e] = w1[e]; }
+                }
+                S[i] = f16_bits_to_f32(a.scales[r * a.n_groups + g]);
+                z[i] = f16_bits_to_f32(a.zeros[r * a.n_groups + g]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep every load above the arithmetic
+#pragma unroll
+            for (int i = 0; i < LROWS; ++i) {
+                float s[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) s[t] = 0.f;
+#pragma unroll
+                for (int e = 0; e < LCH; ++e) {
+                    // code of column c0 + e: packed, word e / 8 holds columns 8 (e / 8) .. + 7 with
+                    // the even ones in the bytes of cw[.][2 (e / 8)] and the odd ones in
+                    // cw[.][2 (e / 8) + 1]; one code per byte otherwise
+                    const uint32_t word = PACKED ? cw[i][2 * (e >> 3) + (e & 1)] : cw[i][e >> 2];
+                    const int byte = PACKED ? ((e & 7) >> 1) : (e & 3);
+                    const float d = (float)((word >> (8 * byte)) & 0xFFu) - z[i];   // exact: small integers
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) s[t] = fmaf(xv[t][e], d, s[t]);
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[i][t] = fmaf(S[i], s[t], acc[i][t]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < LROWS; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float v = wave_sum(acc[i][t]);
+                const int64_t r = r0 + i;
+                if (lane == 0 && r < a.d_row && t0 + t < a.n_tok) store_y<YT>(a.y, (t0 + t) * a.ldy + r, v);
+            }
+    }
+}
+
+// General path (any even d_col, any alignment): one thread per (row, token), columns in
+// order; the same arithmetic per group.
+template <bool PACKED, gptq_dtype XT, gptq_dtype YT>
+__global__ __launch_bounds__(256) void linear_any_kernel(LinArgs a) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= a.d_row) return;
+    const uint8_t* crow = a.codes + r * a.code_ld;
+    for (int64_t t = blockIdx.y; t < a.n_tok; t += gridDim.y) {
+        float acc = 0.f;
+        for (int64_t c0 = 0; c0 < a.d_col; c0 += a.G) {
+            const int g = (int)(c0 / a.G);
+            const float S = f16_bits_to_f32(a.scales[r * a.n_groups + g]);
+            const float z = f16_bits_to_f32(a.zeros[r * a.n_groups + g]);
+            const int64_t c1 = (c0 + a.G < a.d_col) ? c0 + a.G : a.d_col;
+            float s = 0.f;
+            for (int64_t c = c0; c < c1; ++c) {
+                const uint32_t u = PACKED ? (crow[c >> 1] >> (4 * (c & 1))) & 0xFu : crow[c];
+                s = fmaf(load_as_f32<XT>(a.x, t * a.ldx + c), (float)u - z, s);
+            }
+            acc = fmaf(S, s, acc);
+        }
+        store_y<YT>(a.y, t * a.ldy + r, acc);
+    }
+}
+
+template <bool PACKED, gptq_dtype XT, gptq_dtype YT>
+static gptq_status launch3(const LinArgs& a, bool fast, hipStream_t s) {
+    if (!fast) {
+        const unsigned ty = (unsigned)(a.n_tok < 65535 ? a.n_tok : 65535);
+        linear_any_kernel<PACKED, XT, YT><<<dim3((unsigned)((a.d_row + 255) / 256), ty), 256, 0, s>>>(a);
+        GPTQ_LAUNCH_CHECK();
+        return GPTQ_OK;
+    }
+    const dim3 grid((unsigned)((a.d_row + LWAVES * LROWS - 1) / (LWAVES * LROWS)));
+    if (a.n_tok == 1) linear_kernel<PACKED, 1, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
+    else if (a.n_tok == 2) linear_kernel<PACKED, 2, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
+    else linear_kernel<PACKED, 4, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
+template <bool PACKED, gptq_dtype XT>
+static gptq_status launch2(const LinArgs& a, gptq_dtype yt, bool fast, hipStream_t s) {
+    switch (yt) {
+        case GPTQ_F32: return launch3<PACKED, XT, GPTQ_F32>(a, fast, s);
+        case GPTQ_BF16: return launch3<PACKED, XT, GPTQ_BF16>(a, fast, s);
+        case GPTQ_F16: return launch3<PACKED, XT, GPTQ_F16>(a, fast, s);
+    }
+    return GPTQ_ERR_UNSUPPORTED;
+}
+
+template <bool PACKED>
+static gptq_status launch1(const LinArgs& a, gptq_dtype xt, gptq_dtype yt, bool fast, hipStream_t s) {
+    switch (xt) {
+        case GPTQ_F32: return launch2<PACKED, GPTQ_F32>(a, yt, fast, s);
+        case GPTQ_BF16: return launch2<PACKED, GPTQ_BF16>(a, yt, fast, s);
+        case GPTQ_F16: return launch2<PACKED, GPTQ_F16>(a, yt, fast, s);
+    }
+    return GPTQ_ERR_UNSUPPORTED;
+}
+
+gptq_status linear_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
+                          int64_t d_col, int bits, int group_size, const void* x, gptq_dtype x_dtype, int64_t n_tok,
+                          int64_t ldx, void* y, gptq_dtype y_dtype, hipStream_t s) {
+    LinArgs a;
+    const bool packed = bits <= 4;
+    a.codes = codes; a.code_ld = packed ? d_col / 2 : d_col;
+    a.scales = scales; a.zeros = zeros;
+    a.G = group_size == 0 ? d_col : group_size;
+    a.n_groups = (int)(d_col / a.G);
+    a.x = x; a.ldx = ldx; a.n_tok = n_tok;
+    a.y = y; a.ldy = d_row;
+    a.d_row = d_row; a.d_col = d_col;
+    const size_t xsz = x_dtype == GPTQ_F32 ? 4 : 2;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    // whole 32-column chunks inside one group, every chunk of codes and of x 16-byte aligned
+    const bool fast = d_col % LCH == 0 && a.G % LCH == 0 && (a.code_ld % 16) == 0 && al16(codes) && al16(x) &&
+                      ((size_t)ldx * xsz) % 16 == 0;
+    return packed ? launch1<true>(a, x_dtype, y_dtype, fast, s) : launch1<false>(a, x_dtype, y_dtype, fast, s);
+}
+
+}  // namespace gptq

@@ -45,6 +45,8 @@ def lib():
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
+        "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
+                                                 vp, ctypes.c_int, vp]),
         "gptq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -58,7 +60,7 @@ def test_header_declares_the_boundary():
         "gptq_hessian_workspace_size", "gptq_hessian_accumulate",
         "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
         "gptq_quantize_workspace_size", "gptq_quantize_layer",
-        "gptq_dequantize", "gptq_status_string"])
+        "gptq_dequantize", "gptq_quantized_linear", "gptq_status_string"])
 
 
 def test_library_exports_exactly_the_declared_functions(lib):
@@ -138,3 +140,21 @@ def test_dequantize_argument_errors(lib):
     assert f(FAKE, FAKE, FAKE, 4, 256, 4, 128, FAKE, 7, None) == INVALID_ARG
     assert f(None, FAKE, FAKE, 4, 256, 4, 128, FAKE, F32, None) == INVALID_ARG
     assert f(None, None, None, 0, 256, 4, 128, None, F32, None) == OK
+
+
+def test_linear_argument_errors(lib):
+    f = lib.gptq_quantized_linear
+
+    def call(d_row=4, d_col=256, bits=4, G=128, xt=BF16, n=2, ldx=256, yt=F32, codes=FAKE, x=FAKE, y=FAKE):
+        return f(codes, FAKE, FAKE, d_row, d_col, bits, G, x, xt, n, ldx, y, yt, None)
+
+    assert call(bits=5) == UNSUPPORTED
+    assert call(G=100) == INVALID_ARG                  # group does not divide d_col
+    assert call(d_col=255, G=0, ldx=255) == INVALID_ARG   # odd width with nibble packing
+    assert call(xt=7) == INVALID_ARG
+    assert call(yt=7) == INVALID_ARG
+    assert call(ldx=128) == INVALID_ARG                # ldx < d_col
+    assert call(n=-1) == INVALID_ARG
+    assert call(codes=None) == INVALID_ARG
+    assert call(y=None) == INVALID_ARG
+    assert call(n=0, codes=None, x=None, y=None) == OK   # no tokens: no work

@@ -1,0 +1,92 @@
+"""Parity of gptq_quantized_linear (y = x What^T on the stored format) with the oracle,
+element by element, on seeded synthetic codes, scales, zeros and activations.
+
+Tolerance (derived from the arithmetic): the kernel forms, per 32-column piece of a
+group, s = sum x (u - z) with fp32 fused multiply-adds, then acc += S16 s; per element
+at most d_col + 64 fp32 roundings touch the result, so
+|y - y_exact| <= (d_col + 64) 2^-24 sum_c |x_c What_rc|, plus the final rounding to a
+16-bit output type (2^-8 relative for bf16, 2^-11 for f16)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import gptq_oracle as o
+from gpu_helpers import log
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(d_row, d_col, bits, G, n, seed):
+    rng = np.random.default_rng([seed, d_row, d_col, bits, G, n])
+    if bits == 8:
+        packed = rng.integers(0, 256, size=(d_row, d_col), dtype=np.uint8)
+    else:
+        mask = 0xFF if bits == 4 else 0x77
+        packed = (rng.integers(0, 256, size=(d_row, d_col // 2), dtype=np.uint8) & mask).astype(np.uint8)
+    ng = 1 if G == 0 else d_col // G
+    scales = (rng.random((d_row, ng)) * 0.05 + 0.001).astype(np.float16)
+    zeros = rng.integers(0, 2 ** bits, size=(d_row, ng)).astype(np.float16)
+    x = rng.standard_normal((n, d_col)).astype(np.float32)
+    return packed, scales, zeros, x
+
+
+def gpu_linear(packed, scales, zeros, x, bits, G, x_dtype, y_dtype, ldx_pad=0):
+    import post_weight_quantization_25_amd as g
+    d_row = packed.shape[0]
+    d_col = x.shape[1]
+    q = g.Quantized(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda(),
+                    torch.zeros(1, dtype=torch.int32, device="cuda"), bits, G, d_col)
+    xt = torch.from_numpy(x).cuda().to(x_dtype)
+    if ldx_pad:
+        buf = torch.zeros((x.shape[0], d_col + ldx_pad), dtype=x_dtype, device="cuda")
+        buf[:, :d_col] = xt
+        xt = buf[:, :d_col]
+    y = g.linear(q, xt, out_dtype=y_dtype)
+    torch.cuda.synchronize()
+    x_used = xt.float().cpu().numpy().astype(np.float64)   # the activations as the kernel read them
+    return y.float().cpu().numpy().astype(np.float64), x_used
+
+
+CASES = [
+    # d_row, d_col, bits, G, n, x dtype, y dtype, ldx pad
+    (4096, 4096, 4, 128, 1, torch.bfloat16, torch.float32, 0),     # the decode shape of the metric layer
+    (4096, 4096, 4, 128, 4, torch.bfloat16, torch.bfloat16, 0),
+    (300, 512, 4, 128, 3, torch.bfloat16, torch.float32, 0),       # ragged rows, a partial token pass
+    (333, 1024, 4, 64, 9, torch.float16, torch.float32, 0),        # three passes, the last partial
+    (64, 256, 3, 32, 2, torch.float32, torch.float32, 0),
+    (128, 256, 8, 64, 7, torch.float16, torch.bfloat16, 0),        # one code per byte
+    (100, 250, 4, 0, 5, torch.bfloat16, torch.float32, 0),         # width not a multiple of 32: general kernel
+    (96, 512, 4, 128, 2, torch.bfloat16, torch.float16, 3),        # x rows not 16-byte aligned: general kernel
+    (17, 64, 4, 0, 1, torch.bfloat16, torch.float32, 0),           # per-row group, tiny
+]
+
+
+@pytest.mark.parametrize("d_row,d_col,bits,G,n,xt,yt,pad", CASES)
+def test_linear_parity(d_row, d_col, bits, G, n, xt, yt, pad):
+    log(f"linear parity {d_row}x{d_col} bits={bits} G={G} n={n} x={xt} y={yt} pad={pad}")
+    packed, scales, zeros, x = make_case(d_row, d_col, bits, G, n, 11)
+    y, xu = gpu_linear(packed, scales, zeros, x, bits, G, xt, yt, pad)
+    codes = o.unpack(packed, bits)
+    ref = o.linear(xu, codes, scales, zeros, G)
+    What = o.dequantize(codes, scales, zeros, G).astype(np.float64)
+    mag = np.abs(xu) @ np.abs(What).T
+    bound = (d_col + 64) * 2.0 ** -24 * mag
+    if yt == torch.bfloat16:
+        bound = bound + 2.0 ** -8 * np.abs(ref) + 1e-30
+    elif yt == torch.float16:
+        bound = bound + 2.0 ** -11 * np.abs(ref) + 6e-8
+    err = np.abs(y - ref)
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    log(f"  max |err| / bound = {worst:.3f}")
+    assert y.shape == ref.shape
+    assert np.all(err <= bound)
+
+
+def test_linear_no_tokens_is_a_no_op():
+    import post_weight_quantization_25_amd as g
+    packed, scales, zeros, _ = make_case(32, 64, 4, 32, 1, 3)
+    q = g.Quantized(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda(),
+                    torch.zeros(1, dtype=torch.int32, device="cuda"), 4, 32, 64)
+    y = g.linear(q, torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"))
+    assert tuple(y.shape) == (0, 32)
