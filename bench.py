@@ -13,7 +13,7 @@ elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 multiply by 1), used 
 scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
 
 --linear measures, instead of the layer step, the product of the quantized layer with
-activations read from the stored format (gptq_quantized_linear) for 1, 4 and 16
+activations read from the stored format (gptq_quantized_linear) for 1, 4, 16 and 64
 tokens, beside torch's bf16 product with the unquantized weights, and prints its own
 JSON line.
 """
@@ -105,7 +105,7 @@ def cpu_baseline(layer, sample_tokens: int, sample_rows: int):
 
 
 def linear_bench(args, g, q, W, r, d):
-    """Time gptq_quantized_linear on the quantized metric layer for 1, 4 and 16 bf16
+    """Time gptq_quantized_linear on the quantized metric layer for 1, 4, 16 and 64 bf16
     tokens, and torch's bf16 product with the unquantized weights on the same
     activations.  Each is captured as a graph of 100 back-to-back calls (so that host
     launch overhead does not hide the kernel time) and replayed: HIP events around 5
@@ -133,7 +133,7 @@ def linear_bench(args, g, q, W, r, d):
 
     gen = torch.Generator(device="cuda").manual_seed(5)
     per = {}
-    for nt in (1, 4, 16):
+    for nt in (1, 4, 16, 64):
         x = torch.randn((nt, d), generator=gen, device="cuda").to(torch.bfloat16)
         y = torch.empty((nt, r), dtype=torch.bfloat16, device="cuda")
         yb = torch.empty((nt, r), dtype=torch.bfloat16, device="cuda")
@@ -150,7 +150,7 @@ def linear_bench(args, g, q, W, r, d):
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "the quantized attention projection of the layer step (4096x4096, int4 asym g128), "
-                               "bf16 activations of 1, 4 and 16 tokens, bf16 output", "d_row": r, "d_col": d},
+                               "bf16 activations of 1, 4, 16 and 64 tokens, bf16 output", "d_row": r, "d_col": d},
         "per_tokens": per,
         "roofline": {"kernel": "linear_kernel (1 token)", "bound": "hbm", "achieved": one["GBps"],
                      "peak": HBM_GBS, "unit": "GB/s", "frac": one["GBps"] / HBM_GBS, "traffic": None},

@@ -182,8 +182,8 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16,
 /*
  * The layer's product on its quantized weights, read from the stored format:
  *   y[t][r] = sum_c x[t][c] * What[r][c],  What[r][c] = S16[r][g] * (u[r][c] - z[r][g]),
- * accumulated in fp32 (per 32-column piece of one group: sum of x * (u - z), then
- * times S16), rounded once to y_dtype.
+ * accumulated in fp32 (per piece of one group: sum of x * (u - z), then times S16),
+ * rounded once to y_dtype.
  *
  * Sources: GPTQ summary page, layer-wise objective (the layer computes W X; with
  * activations stored tokens x d_col the output is X W^T) and its results on
@@ -195,7 +195,11 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16,
  *  x          n_tokens x d_col, row pitch ldx >= d_col elements, dtype x_dtype.
  *  y          n_tokens x d_row (row pitch d_row), dtype y_dtype; written, not read.
  * Any even d_col works; d_col a multiple of 32 with 16-byte aligned code rows and x
- * rows takes the fast kernel (codes streamed once per four tokens).
+ * rows takes the fast kernels: a single token streams the codes with fp32 multiply-adds;
+ * from two tokens on, packed codes with bf16/f16 x and d_col and the group width
+ * multiples of 128 go to the matrix cores (u - z decoded once per 16 tokens, exact in
+ * x's 16-bit type for integer zeros, else completed by a second product of the
+ * remainder), otherwise the codes are streamed once per four tokens.
  * Errors: negative sizes, bad dtypes or group width -> GPTQ_ERR_INVALID_ARG; bits not
  * 3/4/8 -> GPTQ_ERR_UNSUPPORTED; zero sizes are a no-op.
  */

@@ -8,14 +8,23 @@
 // (x ~= S (q - Z)) and "Data types - int8 and int4" (two int4 values per byte, the
 // first in the low nibble).
 //
-// Decode-shaped (few tokens): the product streams the codes once and is bound by
-// their bytes.  A workgroup of four waves owns 16 rows (four per wave); the 64 lanes
-// of a wave take 32-column chunks in turn (lane l: chunks l, l + 64, ..), so each
-// wave reads a row's codes as contiguous 1 KB pieces.  Per chunk the group's scale
-// and zero are loaded once; the 32 products x (u - z) are summed in fp32 and scaled
-// by S once (the sum of a group's products is exact up to its fp32 roundings; S is
-// factored out of the chunk).  The lanes' partial sums of a row are added with a
-// butterfly over the wave.
+// Decode-shaped (one to a few tokens, linear_kernel): the product streams the codes
+// once and is bound by their bytes.  A workgroup of four waves owns 4 LROWS rows
+// (LROWS per wave); the 64 lanes of a wave take 32-column chunks in turn (lane l:
+// chunks l, l + 64, ..), so each wave reads a row's codes as contiguous 1 KB pieces.
+// Per chunk the group's scale and zero are loaded once; the 32 products x (u - z) are
+// summed in fp32 and scaled by S once (S is factored out of the chunk).  The lanes'
+// partial sums of a row are added with a butterfly over the wave.
+//
+// Batched tokens (linear_mfma_kernel): per token the decode kernel spends an fp32
+// multiply-add per weight, so beyond a few tokens the products move to the matrix
+// cores (v_mfma_f32_16x16x32 in the activations' own 16-bit type): the activations
+// are the A operand (16 tokens), the codes, decoded to u - z in that type, the B
+// operand (16 rows), so the decoding is paid once per weight for all the tokens of a
+// tile.  u - z is exact in bf16 (f16) when the zero is an integer of magnitude at most
+// 240 (2032); otherwise the remainder d - bf16(d) goes through a second product.
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -40,6 +49,9 @@ constexpr int LROWS = LIN_ROWS;              // rows per wave
 #endif
 constexpr int LWAVES = LIN_WAVES;
 constexpr int LCH = 32;                      // columns per chunk
+#ifndef LIN_MFMA_MIN_TOK
+#define LIN_MFMA_MIN_TOK 2                   // fewest tokens taken by the batched kernel
+#endif
 
 template <gptq_dtype DT>
 GPTQ_DEV void load_x8(const void* base, int64_t idx, float (&v)[8]) {   // 8 values, 16-byte aligned
@@ -182,8 +194,163 @@ __global__ __launch_bounds__(256) void linear_any_kernel(LinArgs a) {
     }
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+#ifndef LIN_MW
+#define LIN_MW 8
+#endif
+#ifndef LIN_CPW1
+#define LIN_CPW1 4
+#endif
+#ifndef LIN_CPW2
+#define LIN_CPW2 2
+#endif
+#ifndef LIN_CPW4
+#define LIN_CPW4 1
+#endif
+#ifndef LIN_NTT_MAX
+#define LIN_NTT_MAX 4
+#endif
+constexpr int MW = LIN_MW;   // waves per workgroup of the batched kernel, each a share of the chunks
+constexpr int MCK = 128;     // columns per chunk: four 32-deep products, one scale
+
+// Batched kernel: a workgroup owns 16 rows and 16 NTT tokens; its waves take the row's
+// 128-column chunks in turn (wave w: chunks w, w + 8, ..).  Within a chunk lane l reads
+// the 16 code bytes 16 (l / 16) .. + 15 of row l % 16 (columns 32 (l / 16) .. + 31) and
+// the same 32 columns of token l % 16 of each token tile; product t of the chunk takes
+// columns 32 (l / 16) + 8 t .. + 7 from every lane, so over its four products the
+// chunk's 128 columns each enter once (the order of a sum's terms is the only thing
+// this changes).  Requires packed codes, 16-bit activations, d_col and the group width
+// multiples of 128, 16-byte aligned code and activation rows.
+template <int NTT, gptq_dtype XT, gptq_dtype YT>
+__global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
+    typedef std::conditional_t<XT == GPTQ_BF16, bf16x8_t, f16x8_t> frag_t;
+    typedef std::conditional_t<XT == GPTQ_BF16, __bf16, _Float16> elem_t;
+    constexpr float ZMAX = XT == GPTQ_BF16 ? 240.f : 2032.f;   // |u - z| <= 255 (2047): exact
+    constexpr int CPW = NTT == 1 ? LIN_CPW1 : NTT == 2 ? LIN_CPW2 : LIN_CPW4;  // chunks per wave per pass
+    __shared__ float red[MW][NTT][4][64];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n16 = lane & 15, q = lane >> 4;
+    const int64_t row = (int64_t)blockIdx.x * 16 + n16;
+    const int64_t rr = row < a.d_row ? row : a.d_row - 1;       // rows past the end re-read the last
+    const int64_t tok0 = (int64_t)blockIdx.y * 16 * NTT;
+    const uint8_t* crow = a.codes + rr * a.code_ld + 16 * q;
+    const uint16_t* xrow[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+        int64_t t = tok0 + 16 * tt + n16;
+        t = t < a.n_tok ? t : a.n_tok - 1;                      // a repeated token past the end
+        xrow[tt] = reinterpret_cast<const uint16_t*>(a.x) + t * a.ldx + 32 * q;
+    }
+    const int nck = (int)(a.d_col / MCK);
+    const int cpg = (int)(a.G / MCK);
+    f32x4_t acc[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = wave; c0 < nck; c0 += MW * CPW) {
+        u32x4_t cw[CPW], xw[CPW][NTT][4];
+        float S[CPW], z[CPW];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            const int c = c0 + MW * j < nck ? c0 + MW * j : c0;  // chunks past the end re-read c0
+            cw[j] = *reinterpret_cast<const u32x4_t*>(crow + (int64_t)c * (MCK / 2));
+            const int64_t gi = rr * a.n_groups + c / cpg;
+            S[j] = f16_bits_to_f32(a.scales[gi]);
+            z[j] = f16_bits_to_f32(a.zeros[gi]);
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    xw[j][tt][t] = *reinterpret_cast<const u32x4_t*>(xrow[tt] + (int64_t)c * MCK + 8 * t);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep every load above the arithmetic
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            if (c0 + MW * j >= nck) break;   // wave-uniform
+            const bool exact = z[j] == rintf(z[j]) && fabsf(z[j]) <= ZMAX;
+            const bool need_lo = __ballot(!exact) != 0;
+            f32x4_t cs[NTT];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) cs[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                // element e of the operand is column 8 t + e of the lane's 32: the low
+                // nibble of byte e / 2 for even e, the high nibble for odd e
+                const uint32_t w = cw[j][t];
+                const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+                float d[8];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    d[2 * b] = (float)((lo >> (8 * b)) & 0xFFu) - z[j];
+                    d[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu) - z[j];
+                }
+                frag_t bh;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bh[e] = (elem_t)d[e];
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) {
+                    const frag_t xa = __builtin_bit_cast(frag_t, xw[j][tt][t]);
+                    if constexpr (XT == GPTQ_BF16) cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, cs[tt], 0, 0, 0);
+                    else cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bh, cs[tt], 0, 0, 0);
+                }
+                if (need_lo) {
+                    frag_t bl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bl[e] = (elem_t)(d[e] - (float)bh[e]);
+#pragma unroll
+                    for (int tt = 0; tt < NTT; ++tt) {
+                        const frag_t xa = __builtin_bit_cast(frag_t, xw[j][tt][t]);
+                        if constexpr (XT == GPTQ_BF16) cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, cs[tt], 0, 0, 0);
+                        else cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bl, cs[tt], 0, 0, 0);
+                    }
+                }
+            }
+            // lane l holds the sums of row l % 16 (its own row) for tokens 4 (l / 16) + i
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[tt][i] = fmaf(S[j], cs[tt][i], acc[tt][i]);
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][tt][i][lane] = acc[tt][i];
+    __syncthreads();
+    // output o: token tile o / 256, token m = (o / 16) % 16 of the tile, row n = o % 16;
+    // its partial sums sit in lane n + 16 (m / 4), register m % 4, of every wave
+    for (int o = threadIdx.x; o < NTT * 256; o += 64 * MW) {
+        const int tt = o >> 8, m = (o >> 4) & 15, n = o & 15;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) v += red[w][tt][m & 3][n + 16 * (m >> 2)];
+        const int64_t t = tok0 + 16 * tt + m, r = (int64_t)blockIdx.x * 16 + n;
+        if (t < a.n_tok && r < a.d_row) store_y<YT>(a.y, t * a.ldy + r, v);
+    }
+}
+
+template <gptq_dtype XT, gptq_dtype YT>
+static void launch_mfma(const LinArgs& a, hipStream_t s) {
+    const unsigned gx = (unsigned)((a.d_row + 15) / 16);
+    if (a.n_tok <= 16 || LIN_NTT_MAX == 1)
+        linear_mfma_kernel<1, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
+    else if (a.n_tok <= 32 || LIN_NTT_MAX == 2)
+        linear_mfma_kernel<2, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 31) / 32)), 64 * MW, 0, s>>>(a);
+    else linear_mfma_kernel<4, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 63) / 64)), 64 * MW, 0, s>>>(a);
+}
+
 template <bool PACKED, gptq_dtype XT, gptq_dtype YT>
-static gptq_status launch3(const LinArgs& a, bool fast, hipStream_t s) {
+static gptq_status launch3(const LinArgs& a, int path, hipStream_t s) {
+    if constexpr (PACKED && XT != GPTQ_F32) {
+        if (path == 2) {
+            launch_mfma<XT, YT>(a, s);
+            GPTQ_LAUNCH_CHECK();
+            return GPTQ_OK;
+        }
+    }
+    const bool fast = path >= 1;
     if (!fast) {
         const unsigned ty = (unsigned)(a.n_tok < 65535 ? a.n_tok : 65535);
         linear_any_kernel<PACKED, XT, YT><<<dim3((unsigned)((a.d_row + 255) / 256), ty), 256, 0, s>>>(a);
@@ -199,21 +366,21 @@ static gptq_status launch3(const LinArgs& a, bool fast, hipStream_t s) {
 }
 
 template <bool PACKED, gptq_dtype XT>
-static gptq_status launch2(const LinArgs& a, gptq_dtype yt, bool fast, hipStream_t s) {
+static gptq_status launch2(const LinArgs& a, gptq_dtype yt, int path, hipStream_t s) {
     switch (yt) {
-        case GPTQ_F32: return launch3<PACKED, XT, GPTQ_F32>(a, fast, s);
-        case GPTQ_BF16: return launch3<PACKED, XT, GPTQ_BF16>(a, fast, s);
-        case GPTQ_F16: return launch3<PACKED, XT, GPTQ_F16>(a, fast, s);
+        case GPTQ_F32: return launch3<PACKED, XT, GPTQ_F32>(a, path, s);
+        case GPTQ_BF16: return launch3<PACKED, XT, GPTQ_BF16>(a, path, s);
+        case GPTQ_F16: return launch3<PACKED, XT, GPTQ_F16>(a, path, s);
     }
     return GPTQ_ERR_UNSUPPORTED;
 }
 
 template <bool PACKED>
-static gptq_status launch1(const LinArgs& a, gptq_dtype xt, gptq_dtype yt, bool fast, hipStream_t s) {
+static gptq_status launch1(const LinArgs& a, gptq_dtype xt, gptq_dtype yt, int path, hipStream_t s) {
     switch (xt) {
-        case GPTQ_F32: return launch2<PACKED, GPTQ_F32>(a, yt, fast, s);
-        case GPTQ_BF16: return launch2<PACKED, GPTQ_BF16>(a, yt, fast, s);
-        case GPTQ_F16: return launch2<PACKED, GPTQ_F16>(a, yt, fast, s);
+        case GPTQ_F32: return launch2<PACKED, GPTQ_F32>(a, yt, path, s);
+        case GPTQ_BF16: return launch2<PACKED, GPTQ_BF16>(a, yt, path, s);
+        case GPTQ_F16: return launch2<PACKED, GPTQ_F16>(a, yt, path, s);
     }
     return GPTQ_ERR_UNSUPPORTED;
 }
@@ -235,7 +402,12 @@ gptq_status linear_launch(const uint8_t* codes, const uint16_t* scales, const ui
     // whole 32-column chunks inside one group, every chunk of codes and of x 16-byte aligned
     const bool fast = d_col % LCH == 0 && a.G % LCH == 0 && (a.code_ld % 16) == 0 && al16(codes) && al16(x) &&
                       ((size_t)ldx * xsz) % 16 == 0;
-    return packed ? launch1<true>(a, x_dtype, y_dtype, fast, s) : launch1<false>(a, x_dtype, y_dtype, fast, s);
+    // batched tokens on the matrix cores: packed codes, 16-bit activations, whole 128-column
+    // chunks inside one group
+    const bool mfma = fast && packed && x_dtype != GPTQ_F32 && n_tok >= LIN_MFMA_MIN_TOK && d_col % MCK == 0 &&
+                      a.G % MCK == 0;
+    const int path = mfma ? 2 : fast ? 1 : 0;
+    return packed ? launch1<true>(a, x_dtype, y_dtype, path, s) : launch1<false>(a, x_dtype, y_dtype, path, s);
 }
 
 }  // namespace gptq

@@ -1,11 +1,16 @@
 """Parity of gptq_quantized_linear (y = x What^T on the stored format) with the oracle,
 element by element, on seeded synthetic codes, scales, zeros and activations.
 
-Tolerance (derived from the arithmetic): the kernel forms, per 32-column piece of a
-group, s = sum x (u - z) with fp32 fused multiply-adds, then acc += S16 s; per element
-at most d_col + 64 fp32 roundings touch the result, so
-|y - y_exact| <= (d_col + 64) 2^-24 sum_c |x_c What_rc|, plus the final rounding to a
-16-bit output type (2^-8 relative for bf16, 2^-11 for f16)."""
+Tolerance (derived from the arithmetic).  The decode kernel forms, per 32-column piece
+of a group, s = sum x (u - z) with fp32 fused multiply-adds, then acc += S16 s; the
+batched kernel forms the same sums on the matrix cores per 128-column piece (products
+of 16-bit values are exact in fp32) and then acc += S16 s.  Per element at most
+d_col + 64 fp32 additions touch the result; they are taken at one unit in the last
+place each (2^-23, so the bound does not assume the matrix cores round to nearest).
+When a zero is not a small integer the batched kernel splits d = u - z into
+hi = 16-bit(d) and lo = 16-bit(d - hi), |hi + lo - d| <= 2^-18 |d|.  So
+|y - y_exact| <= ((d_col + 64) 2^-23 + 2^-18) sum_c |x_c What_rc|, plus the final
+rounding to a 16-bit output type (2^-8 relative for bf16, 2^-11 for f16)."""
 import numpy as np
 import pytest
 
@@ -17,7 +22,7 @@ from gpu_helpers import log
 pytestmark = pytest.mark.gpu
 
 
-def make_case(d_row, d_col, bits, G, n, seed):
+def make_case(d_row, d_col, bits, G, n, seed, frac_zeros=False):
     rng = np.random.default_rng([seed, d_row, d_col, bits, G, n])
     if bits == 8:
         packed = rng.integers(0, 256, size=(d_row, d_col), dtype=np.uint8)
@@ -27,11 +32,17 @@ def make_case(d_row, d_col, bits, G, n, seed):
     ng = 1 if G == 0 else d_col // G
     scales = (rng.random((d_row, ng)) * 0.05 + 0.001).astype(np.float16)
     zeros = rng.integers(0, 2 ** bits, size=(d_row, ng)).astype(np.float16)
+    if frac_zeros:
+        # zeros that are not integers, and a few far outside the code range, so that
+        # u - z is not exact in a 16-bit type
+        zeros = (rng.random((d_row, ng)) * (2 ** bits)).astype(np.float16)
+        far = rng.random((d_row, ng)) < 0.05
+        zeros[far] = np.float16(300.0)
     x = rng.standard_normal((n, d_col)).astype(np.float32)
     return packed, scales, zeros, x
 
 
-def gpu_linear(packed, scales, zeros, x, bits, G, x_dtype, y_dtype, ldx_pad=0):
+def gpu_linear(packed, scales, zeros, x, bits, G, x_dtype, y_dtype, ldx_pad=0, repeat=2):
     import post_weight_quantization_25_amd as g
     d_row = packed.shape[0]
     d_col = x.shape[1]
@@ -42,8 +53,11 @@ def gpu_linear(packed, scales, zeros, x, bits, G, x_dtype, y_dtype, ldx_pad=0):
         buf = torch.zeros((x.shape[0], d_col + ldx_pad), dtype=x_dtype, device="cuda")
         buf[:, :d_col] = xt
         xt = buf[:, :d_col]
-    y = g.linear(q, xt, out_dtype=y_dtype)
+    ys = [g.linear(q, xt, out_dtype=y_dtype) for _ in range(repeat)]
     torch.cuda.synchronize()
+    y = ys[0]
+    for other in ys[1:]:   # the same sums in the same order on every call
+        assert torch.equal(other, y)
     x_used = xt.float().cpu().numpy().astype(np.float64)   # the activations as the kernel read them
     return y.float().cpu().numpy().astype(np.float64), x_used
 
@@ -59,6 +73,13 @@ CASES = [
     (100, 250, 4, 0, 5, torch.bfloat16, torch.float32, 0),         # width not a multiple of 32: general kernel
     (96, 512, 4, 128, 2, torch.bfloat16, torch.float16, 3),        # x rows not 16-byte aligned: general kernel
     (17, 64, 4, 0, 1, torch.bfloat16, torch.float32, 0),           # per-row group, tiny
+    # batched kernel (packed codes, 16-bit x, two or more tokens, 128-column chunks)
+    (4096, 4096, 4, 128, 16, torch.bfloat16, torch.bfloat16, 0),   # one full token tile, metric layer shape
+    (512, 1024, 4, 128, 5, torch.bfloat16, torch.float32, 0),      # a partial token tile
+    (272, 512, 4, 256, 20, torch.float16, torch.float32, 0),       # two token tiles, 17 row tiles, two chunks a group
+    (200, 384, 3, 128, 70, torch.bfloat16, torch.float32, 0),      # two tile rows of 64 tokens, ragged rows, 3 chunks
+    (160, 2048, 4, 0, 2, torch.float16, torch.float16, 0),         # per-row group over 16 chunks
+    (64, 1280, 4, 128, 33, torch.bfloat16, torch.float32, 8),      # padded x rows (16-byte aligned)
 ]
 
 
@@ -71,7 +92,7 @@ def test_linear_parity(d_row, d_col, bits, G, n, xt, yt, pad):
     ref = o.linear(xu, codes, scales, zeros, G)
     What = o.dequantize(codes, scales, zeros, G).astype(np.float64)
     mag = np.abs(xu) @ np.abs(What).T
-    bound = (d_col + 64) * 2.0 ** -24 * mag
+    bound = ((d_col + 64) * 2.0 ** -23 + 2.0 ** -18) * mag
     if yt == torch.bfloat16:
         bound = bound + 2.0 ** -8 * np.abs(ref) + 1e-30
     elif yt == torch.float16:
@@ -80,6 +101,42 @@ def test_linear_parity(d_row, d_col, bits, G, n, xt, yt, pad):
     worst = float(np.max(err / np.maximum(bound, 1e-300)))
     log(f"  max |err| / bound = {worst:.3f}")
     assert y.shape == ref.shape
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("xt", [torch.bfloat16, torch.float16])
+def test_linear_batched_inexact_zeros(xt):
+    """Zeros that are not small integers take the batched kernel's second product."""
+    log(f"linear batched, fractional zeros, x={xt}")
+    packed, scales, zeros, x = make_case(256, 1024, 4, 128, 12, 5, frac_zeros=True)
+    y, xu = gpu_linear(packed, scales, zeros, x, 4, 128, xt, torch.float32)
+    codes = o.unpack(packed, 4)
+    ref = o.linear(xu, codes, scales, zeros, 128)
+    What = o.dequantize(codes, scales, zeros, 128).astype(np.float64)
+    mag = np.abs(xu) @ np.abs(What).T
+    bound = ((1024 + 64) * 2.0 ** -23 + 2.0 ** -18) * mag
+    err = np.abs(y - ref)
+    log(f"  max |err| / bound = {float(np.max(err / np.maximum(bound, 1e-300))):.3f}")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("xt", [torch.bfloat16, torch.float16])
+def test_linear_batched_inexact_zeros_coherent(xt):
+    """Every code 5, every zero 0.3, activations >= 0: u - z = 4.7 is not a 16-bit value
+    (bf16 rounds it to 4.6875, f16 to 4.69921875), and the rounding errors all have one
+    sign, so a product of the rounded value alone misses by 2.6e-3 (bf16) or 1.6e-4
+    (f16) of |y|, above the bound of ((d_col + 64) 2^-23 + 2^-18) |y| = 1.3e-4 |y|."""
+    log(f"linear batched, coherent fractional zeros, x={xt}")
+    d_row, d_col, n = 64, 1024, 4
+    packed = np.full((d_row, d_col // 2), 0x55, dtype=np.uint8)
+    scales = np.full((d_row, d_col // 128), 0.01, dtype=np.float16)
+    zeros = np.full((d_row, d_col // 128), 0.3, dtype=np.float16)
+    x = np.abs(np.random.default_rng(9).standard_normal((n, d_col))).astype(np.float32)
+    y, xu = gpu_linear(packed, scales, zeros, x, 4, 128, xt, torch.float32)
+    ref = o.linear(xu, o.unpack(packed, 4), scales, zeros, 128)
+    bound = ((d_col + 64) * 2.0 ** -23 + 2.0 ** -18) * np.abs(ref)
+    err = np.abs(y - ref)
+    log(f"  max |err| / bound = {float(np.max(err / bound)):.3f}")
     assert np.all(err <= bound)
 
 
