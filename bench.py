@@ -33,6 +33,7 @@ METRIC = "GPTQ quantized weights/sec + ms/layer (int4 g128) at 4096x4096, 1 MI35
 PEAK_BF16_TFLOPS = 2500.0
 HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hess_bf16_c2_traffic.json")
+LINEAR_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "linear_int4_g128_1tok_traffic.json")
 
 
 def parse():
@@ -51,17 +52,28 @@ def source_hash(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes_alg: float):
-    """HBM bytes per Hessian launch from the committed rocprofv3 counter summary,
-    or None when the kernel source changed since the counters were taken."""
+def measured_traffic(launch_bytes_alg: float = 0.0, path: str | None = None, source: str = "hessian.hip"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (the Hessian's by
+    default), or None when the kernel source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != source_hash("hessian.hip"):
+    if t.get("source_sha256_16") != source_hash(source):
         return None
     return t.get("bytes_per_launch")
+
+
+def calibrate_copy(dev):
+    """One plain elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 times 1): the
+    known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(layer, sample_tokens: int, sample_rows: int):
@@ -153,7 +165,8 @@ def linear_bench(args, g, q, W, r, d):
                                "bf16 activations of 1, 4, 16 and 64 tokens, bf16 output", "d_row": r, "d_col": d},
         "per_tokens": per,
         "roofline": {"kernel": "linear_kernel (1 token)", "bound": "hbm", "achieved": one["GBps"],
-                     "peak": HBM_GBS, "unit": "GB/s", "frac": one["GBps"] / HBM_GBS, "traffic": None},
+                     "peak": HBM_GBS, "unit": "GB/s", "frac": one["GBps"] / HBM_GBS,
+                     "traffic": measured_traffic(path=LINEAR_TRAFFIC_FILE, source="linear.hip")},
     }
     print(json.dumps(rec), flush=True)
 
@@ -225,6 +238,8 @@ def main():
     g.check_info(q.info, "quantize_layer")
     if args.linear:
         linear_bench(args, g, q, W, r, d)
+        if args.calibrate_copy:
+            calibrate_copy(dev)
         return
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -245,11 +260,7 @@ def main():
     hess_launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in hev]))
 
     if args.calibrate_copy:
-        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        torch.mul(a, 1.0, out=b)
-        torch.cuda.synchronize()
+        calibrate_copy(dev)
 
     flops_hess = float(n) * d * (d + 1)            # symmetric rank-n update, upper triangle incl. diagonal
     achieved = flops_hess / (hess_launch_ms * 1e-3) / 1e12
