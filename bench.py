@@ -12,6 +12,11 @@ GPU) --no-cpu-baseline --calibrate-copy (adds, after the timed region, one plain
 elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 multiply by 1), used to
 scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
 
+--config N (1..5; default 2, the line above) instead times every layer of workload N
+(1: 256x512; 3: MLP up/down pair at int4 and int3; 4: a decoder block of 7 linears;
+5: the 49152/12288 fc pair) with the same step, and prints one JSON line with
+ms/layer and the phase breakdown per layer.
+
 --linear measures, instead of the layer step, the product of the quantized layer with
 activations read from the stored format (gptq_quantized_linear) for 1, 4, 16 and 64
 tokens, beside torch's bf16 product with the unquantized weights, and prints its own
@@ -44,6 +49,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--linear", action="store_true")
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     return ap.parse_args()
 
 
@@ -171,6 +177,116 @@ def linear_bench(args, g, q, W, r, d):
     print(json.dumps(rec), flush=True)
 
 
+CONFIG_WORKLOADS = {
+    1: "single linear layer 256x512: W fp32 ~N(0,0.02^2), X 2048x512 fp32 N(0,1) with 4 channels x20; int4 asym g128",
+    2: "attention projection 4096x4096: W bf16 ~N(0,0.02^2), X 262144x4096 bf16 (log-normal channel scales, "
+       "4 channels x50); int4 asym g128",
+    3: "MLP pair: up 11008x4096 and down 4096x11008, bf16 ~N(0,0.02^2), X 131072 tokens Student-t(4); "
+       "int4 g128 and int3 g128 asym",
+    4: "decoder block of 7 linears (q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008), bf16 "
+       "~N(0,0.02^2), each its own X of 65536 bf16 N(0,1) tokens; int3 per-channel symmetric",
+    5: "large layers: fc1 49152x12288 and fc2 12288x49152, bf16 ~N(0,0.01^2), X 262144 bf16 N(0,1) tokens "
+       "with 0.1% channels x30; int4 asym g128",
+}
+
+
+def _upload(L, dev):
+    """The layer's synthetic X and W (the seeded generator's chunks) resident on the device."""
+    import numpy as np
+    import torch
+
+    import synth
+    dt = torch.bfloat16 if L.x_dtype == "bf16" else torch.float32
+    X = torch.empty((L.n_tokens, L.d_col), dtype=dt, device=dev)
+    for c, arr in enumerate(synth.x_chunks(L)):
+        lo = c * synth.CHUNK
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if arr.dtype == np.uint16 else torch.from_numpy(arr)
+        X[lo:lo + arr.shape[0]].copy_(t)
+    w = synth.weights(L)
+    W = (torch.from_numpy(w.view(np.int16)).view(torch.bfloat16) if w.dtype == np.uint16 else torch.from_numpy(w)).to(dev)
+    return X, W
+
+
+def layer_bench(g, L, dev, steps: int, warmup: int, damp: float = 0.01):
+    """One layer's step (zero H, Hessian, prep, quantize, dequantize) with inputs resident:
+    warm-up steps, then the mean per phase over timed steps (HIP events on the stream)."""
+    import numpy as np
+    import torch
+    t0 = time.perf_counter()
+    X, W = _upload(L, dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t0
+    n, d, r = L.n_tokens, L.d_col, L.d_row
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    ws_h = torch.empty(g.hessian_workspace_size(n, d), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(g.prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
+    U = torch.empty((d, d), dtype=torch.float32, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    p = g.make_params(L.bits, L.group_size, L.sym)
+    ws_q = torch.empty(g.quantize_workspace_size(r, d, p), dtype=torch.uint8, device=dev)
+    ng = 1 if L.group_size == 0 else d // L.group_size
+    q = g.Quantized(torch.empty((r, d // 2 if L.bits <= 4 else d), dtype=torch.uint8, device=dev),
+                    torch.empty((r, ng), dtype=torch.float16, device=dev),
+                    torch.empty((r, ng), dtype=torch.float16, device=dev),
+                    torch.zeros(1, dtype=torch.int32, device=dev), L.bits, L.group_size, d)
+    What = torch.empty((r, d), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        H.zero_()
+        g.hessian_accumulate(H, X, ws=ws_h)
+        if ev: ev[1].record()
+        g.prepare_hinv(H, damp, U=U, ws=ws_p, info=info)
+        if ev: ev[2].record()
+        g.quantize_layer(W, U, L.bits, L.group_size, L.sym, ws=ws_q, out=q)
+        if ev: ev[3].record()
+        g.dequantize(q, out=What)
+        if ev: ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    g.check_info(info, "prepare_hinv")
+    g.check_info(q.info, "quantize_layer")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ph = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+          for i, nm in enumerate(["hess", "prep", "quant", "deq"])}
+    ms_layer = ph["hess"] + ph["prep"] + ph["quant"]
+    return {"name": L.name, "d_row": r, "d_col": d, "n_tokens": n, "bits": L.bits, "group_size": L.group_size,
+            "sym": bool(L.sym), "phases_ms": ph, "ms_per_layer": ms_layer,
+            "ms_per_layer_quantize_only": ph["prep"] + ph["quant"],
+            "weights_per_s": r * d / (ms_layer * 1e-3), "input_generation_s": t_gen}
+
+
+def config_bench(args, cfg: int):
+    """ms/layer and weights/s for every layer of one workload, printed as one JSON line."""
+    import torch
+
+    import post_weight_quantization_25_amd as g
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = []
+    for L in synth.config_layers(cfg):
+        print(f"[config {cfg}] {L.name} {L.d_row}x{L.d_col} n={L.n_tokens}: start", file=sys.stderr, flush=True)
+        res = layer_bench(g, L, dev, args.steps, args.warmup)
+        print(f"[config {cfg}] {L.name}: {res['ms_per_layer']:.3f} ms/layer "
+              f"(inputs {res['input_generation_s']:.1f} s)", file=sys.stderr, flush=True)
+        layers.append(res)
+        torch.cuda.empty_cache()
+    tot_w = sum(x["d_row"] * x["d_col"] for x in layers)
+    tot_ms = sum(x["ms_per_layer"] for x in layers)
+    rec = {"metric": METRIC, "value": tot_w / (tot_ms * 1e-3), "unit": "weights/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if cfg != 1 else "f32", "data": "synthetic",
+           "config": {"workload": CONFIG_WORKLOADS[cfg], "index": cfg, "damp": 0.01, "block_size": 128},
+           "layers": layers, "ms_all_layers": tot_ms}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -179,6 +295,10 @@ def main():
               "(rows shard with no communication and H needs one all-reduce, which this build "
               "does not implement)", file=sys.stderr)
         sys.exit(2)
+
+    if args.config != 2:
+        config_bench(args, args.config)
+        return
 
     import numpy as np
     import torch
