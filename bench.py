@@ -261,6 +261,38 @@ def layer_bench(g, L, dev, steps: int, warmup: int, damp: float = 0.01):
             "weights_per_s": r * d / (ms_layer * 1e-3), "input_generation_s": t_gen}
 
 
+def block_bench(g, layers, dev, steps: int, warmup: int, shared: bool):
+    """The whole decoder block through gptq_quantize_layers (Hessians, factorizations and
+    sweeps of different layers overlapped) for 1, 2 and 3 slots: HIP events around the
+    call on the caller's stream, mean over the timed calls.  shared: q, k, v read q's
+    inputs and gate, up read gate's (one H and one U per group), else every layer its own."""
+    import torch
+    data = [_upload(L, dev) for L in layers]
+    if shared:
+        src = {"c4_k": 0, "c4_v": 0, "c4_up": 4}
+        data = [(data[src[L.name]][0] if L.name in src else X, W) for L, (X, W) in zip(layers, data)]
+    L0 = layers[0]
+    out = {}
+    for slots in (1, 2, 3):
+        ws = torch.empty(g.quantize_layers_workspace_size(data, slots), dtype=torch.uint8, device=dev)
+        res, info = g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws)
+        for _ in range(max(0, warmup - 1)):
+            g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws, outs=res, info=info)
+        torch.cuda.synchronize()
+        if info.cpu().any():
+            raise RuntimeError(f"gptq_quantize_layers: status {info.cpu().tolist()}")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(steps):
+            ev[k][0].record()
+            g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws, outs=res, info=info)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        out[str(slots)] = float(sum(e[0].elapsed_time(e[1]) for e in ev) / steps)
+        del ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def config_bench(args, cfg: int):
     """ms/layer and weights/s for every layer of one workload, printed as one JSON line."""
     import torch
@@ -284,6 +316,19 @@ def config_bench(args, cfg: int):
            "vs_baseline": None, "dtype": "bf16" if cfg != 1 else "f32", "data": "synthetic",
            "config": {"workload": CONFIG_WORKLOADS[cfg], "index": cfg, "damp": 0.01, "block_size": 128},
            "layers": layers, "ms_all_layers": tot_ms}
+    if cfg == 4:
+        # the block in one call (phases of different layers overlapped), each layer with its
+        # own inputs as above, and with q/k/v and gate/up sharing theirs as in a real block
+        Ls = synth.config_layers(cfg)
+        for shared in (False, True):
+            key = "block_shared_inputs_ms" if shared else "block_ms"
+            print(f"[config {cfg}] block in one call, shared inputs={shared}", file=sys.stderr, flush=True)
+            rec[key] = block_bench(g, Ls, dev, args.steps, args.warmup, shared)
+            torch.cuda.empty_cache()
+        best = min(rec["block_ms"].values())
+        rec["block_weights_per_s"] = tot_w / (best * 1e-3)
+        rec["value"] = rec["block_weights_per_s"]
+        rec["value_note"] = "block of 7 layers in one gptq_quantize_layers call, best slot count, own inputs per layer"
     print(json.dumps(rec), flush=True)
 
 

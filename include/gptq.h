@@ -165,6 +165,52 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row
                                 void* ws, size_t ws_bytes, int32_t* info, void* stream);
 
 /*
+ * Several layers in one call, with the phases of different layers overlapped: for
+ * every layer, H = 2 X^T X over its own calibration inputs, U as gptq_prepare_hinv
+ * makes it, and codes, scales and zeros as gptq_quantize_layer writes them; each
+ * layer's outputs are bit-identical to those three calls'.  Consecutive layers with
+ * the same inputs (X, x_dtype, n_tokens, ldx, d_col all equal: a block's q, k and v,
+ * or gate and up) share one H and one U.
+ *
+ * Source: GPTQ summary page, the statement of the procedure (the model is quantized
+ * layer by layer, each layer from the inputs it receives; H depends only on a layer's
+ * inputs) and "Innovation 3" (the factorization is computed once per H).
+ *
+ * Schedule: groups start widest first (ties in the given order; no layer's result
+ * depends on the order); their Hessians run one after another on one library stream;
+ * the k-th started group's factorization and sweeps run on slot stream k mod n_slots,
+ * so the next group's Hessian overlaps the running factorizations and sweeps, and
+ * the factorizations of up to n_slots groups overlap each other.  The call is ordered
+ * after the work already queued on `stream`, and later work on `stream` after it.
+ *
+ *  layers     host array of n_layers descriptors (device pointers inside); the
+ *             quantizer settings p apply to every layer (group size dividing each d_col).
+ *  n_slots    1 .. GPTQ_LAYERS_MAX_SLOTS: groups in flight at once (memory grows with it).
+ *  ws         at least gptq_quantize_layers_workspace_size(layers, n_layers, n_slots)
+ *             bytes, 256-byte aligned: n_slots x (H, U, factorization and sweep
+ *             workspaces of the largest layer) + one Hessian workspace.
+ *  info       device int32[2 * n_layers], set to 0 first: info[2l] = the factorization's
+ *             status for layer l's group (on the group's first layer; as
+ *             gptq_prepare_hinv), info[2l + 1] = layer l's sweep status (as
+ *             gptq_quantize_layer).
+ * Errors (checked for every layer before anything is queued): as the per-phase calls;
+ * n_tokens < 1, d_row < 1 or d_col < 1 -> GPTQ_ERR_INVALID_ARG; n_slots out of range
+ * -> GPTQ_ERR_INVALID_ARG.  n_layers = 0 is a no-op.  Calls that overlap in time (from
+ * several host threads) are queued one after the other; their device work may
+ * interleave only through different workspaces.
+ */
+#define GPTQ_LAYERS_MAX_SLOTS 4
+typedef struct gptq_layer {
+    const void* X; gptq_dtype x_dtype; int64_t n_tokens; int64_t ldx;   /* n_tokens x d_col inputs */
+    const void* W; gptq_dtype w_dtype; int64_t d_row; int64_t d_col;    /* d_row x d_col weights */
+    uint8_t* codes; uint16_t* scales_f16; uint16_t* zeros_f16;          /* outputs, as gptq_quantize_layer */
+} gptq_layer;
+size_t gptq_quantize_layers_workspace_size(const gptq_layer* layers, int32_t n_layers, int32_t n_slots);  /* reads shapes only */
+gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, float percdamp,
+                                 const gptq_params* p, int32_t n_slots, void* ws, size_t ws_bytes,
+                                 int32_t* info, void* stream);
+
+/*
  * W_out = S16 * (u - z) for every weight (computed in fp32, exact, then rounded
  * to out_dtype with round-to-nearest-even).
  *

@@ -33,6 +33,17 @@ class Params(ctypes.Structure):
                 ("sym", ctypes.c_int32), ("block_size", ctypes.c_int32)]
 
 
+class LayerDesc(ctypes.Structure):
+    """gptq_layer: one layer's inputs, weights and outputs (device pointers)."""
+    _fields_ = [("X", ctypes.c_void_p), ("x_dtype", ctypes.c_int), ("n_tokens", ctypes.c_int64),
+                ("ldx", ctypes.c_int64), ("W", ctypes.c_void_p), ("w_dtype", ctypes.c_int),
+                ("d_row", ctypes.c_int64), ("d_col", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales_f16", ctypes.c_void_p), ("zeros_f16", ctypes.c_void_p)]
+
+
+LAYERS_MAX_SLOTS = 4
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -47,6 +58,9 @@ def _load():
         "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
+        "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
+        "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
+                                                ctypes.POINTER(Params), i32, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
         "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
                                                  vp, ctypes.c_int, vp]),
@@ -181,6 +195,67 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: 
                                    ws.numel() if ws is not None else 0, out.info.data_ptr(), _stream(stream)),
            "gptq_quantize_layer")
     return out
+
+
+def _layer_descs(pairs, outs):
+    arr = (LayerDesc * len(pairs))()
+    for k, ((X, W), q) in enumerate(zip(pairs, outs)):
+        arr[k] = LayerDesc(X.data_ptr(), _DT[X.dtype], X.shape[0], max(X.stride(0), X.shape[1]), W.data_ptr(),
+                           _DT[W.dtype], W.shape[0], W.shape[1], q.codes.data_ptr(), q.scales.data_ptr(),
+                           q.zeros.data_ptr())
+    return arr
+
+
+def _layer_descs_shapes(pairs):
+    """Descriptors with shapes only (the workspace size reads no pointer)."""
+    arr = (LayerDesc * len(pairs))()
+    for k, (X, W) in enumerate(pairs):
+        arr[k] = LayerDesc(X.data_ptr(), _DT[X.dtype], X.shape[0], max(X.stride(0), X.shape[1]), None,
+                           _DT[W.dtype], W.shape[0], W.shape[1], None, None, None)
+    return arr
+
+
+def quantize_layers_workspace_size(pairs, n_slots: int = 2) -> int:
+    """Bytes of workspace for ``quantize_layers`` on these (X, W) pairs."""
+    return int(lib.gptq_quantize_layers_workspace_size(_layer_descs_shapes(pairs), len(pairs), n_slots))
+
+
+def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = False, percdamp: float = 0.01,
+                    n_slots: int = 2, ws: torch.Tensor | None = None, outs: list | None = None,
+                    info: torch.Tensor | None = None, stream=None):
+    """Quantize several layers in one call (gptq_quantize_layers): ``pairs`` is a list of
+    (X, W) device tensors, X tokens x d_col (rows may be strided), W d_row x d_col.
+    Consecutive pairs with the same X tensor share one H and one U.  Returns (outs, info):
+    one Quantized per layer and the device int32[2 n] status array."""
+    if not pairs:
+        return [], info
+    for X, W in pairs:
+        _dev(W, "W")
+        if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1 or X.dtype not in _DT or W.dtype not in _DT:
+            raise ValueError("X must be 2-D with unit column stride and f32/bf16/f16, W f32/bf16/f16")
+        if X.shape[1] != W.shape[1]:
+            raise ValueError("X and W must have the same d_col")
+    dev = pairs[0][1].device
+    p = make_params(bits, group_size, sym)
+    if outs is None:
+        outs = []
+        for _, W in pairs:
+            d_row, d_col = W.shape
+            n_groups = 1 if group_size == 0 else max(1, d_col // group_size)
+            outs.append(Quantized(torch.empty((d_row, d_col // 2 if bits <= 4 else d_col), dtype=torch.uint8, device=dev),
+                                  torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),
+                                  torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),
+                                  torch.zeros(1, dtype=torch.int32, device=dev), bits, group_size, d_col))
+    if info is None:
+        info = torch.empty(2 * len(pairs), dtype=torch.int32, device=dev)
+    need = int(lib.gptq_quantize_layers_workspace_size(_layer_descs_shapes(pairs), len(pairs), n_slots))
+    ws = _workspace(need, dev, ws)
+    descs = _layer_descs(pairs, outs)
+    _check(lib.gptq_quantize_layers(descs, len(pairs), percdamp, ctypes.byref(p), n_slots,
+                                    ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                                    info.data_ptr(), _stream(stream)),
+           "gptq_quantize_layers")
+    return outs, info
 
 
 def dequantize(q: Quantized, out_dtype=torch.float32, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

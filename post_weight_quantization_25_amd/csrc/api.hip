@@ -72,6 +72,39 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row
                         (hipStream_t)stream);
 }
 
+// p == nullptr: shapes only (the workspace size), no settings and no pointers checked.
+static gptq_status check_layers(const gptq_layer* L, int32_t n, const gptq_params* p, int32_t n_slots) {
+    if (n < 0 || (n > 0 && L == nullptr)) return GPTQ_ERR_INVALID_ARG;
+    if (n_slots < 1 || n_slots > GPTQ_LAYERS_MAX_SLOTS) return GPTQ_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+        const gptq_layer& l = L[i];
+        if (l.n_tokens < 1 || l.d_row < 1 || l.d_col < 1 || l.ldx < l.d_col) return GPTQ_ERR_INVALID_ARG;
+        if (!valid_dtype(l.x_dtype) || !valid_dtype(l.w_dtype)) return GPTQ_ERR_INVALID_ARG;
+        if (p) {
+            if (!l.X || !l.W || !l.codes || !l.scales_f16 || !l.zeros_f16) return GPTQ_ERR_INVALID_ARG;
+            const gptq_status st = check_params(p, l.d_col);
+            if (st != GPTQ_OK) return st;
+        }
+        if (l.d_row > 2147483647LL / 64 || l.d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
+    }
+    return GPTQ_OK;
+}
+
+size_t gptq_quantize_layers_workspace_size(const gptq_layer* layers, int32_t n_layers, int32_t n_slots) {
+    if (check_layers(layers, n_layers, nullptr, n_slots) != GPTQ_OK || n_layers == 0) return 0;
+    return layers_ws_bytes(layers, n_layers, n_slots);
+}
+
+gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, float percdamp, const gptq_params* p,
+                                 int32_t n_slots, void* ws, size_t ws_bytes, int32_t* info, void* stream) {
+    if (p == nullptr || !(percdamp >= 0.f)) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_layers(layers, n_layers, p, n_slots);
+    if (st != GPTQ_OK) return st;
+    if (n_layers == 0) return GPTQ_OK;
+    if (info == nullptr) return GPTQ_ERR_INVALID_ARG;
+    return layers_launch(layers, n_layers, percdamp, *p, n_slots, ws, ws_bytes, info, (hipStream_t)stream);
+}
+
 gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* zeros_f16,
                             int64_t d_row, int64_t d_col, int32_t bits, int32_t group_size, void* W_out,
                             gptq_dtype out_dtype, void* stream) {

@@ -1,0 +1,174 @@
+// Quantization of a list of layers (a transformer block's linears) with the phases of
+// different layers overlapped.
+//
+// GPTQ summary page, the statement of the procedure: the model is quantized one layer
+// at a time, each layer from its own calibration inputs, and layers that read the same
+// inputs (a block's q, k and v; gate and up) need only one H = 2 X X^T and one
+// factorization between them.  Every layer goes through the same kernels as the
+// one-call-per-phase entry points (Hessian, factorization of the damped inverse,
+// blocked sweep), so its codes, scales and zeros are bit-identical to theirs.
+//
+// Schedule.  Consecutive layers with the same inputs form a group.  Groups are started
+// widest first (the factorization grows as d_col^3, so the longest chain starts first
+// and the rest fits beside it; ties keep the caller's order); a layer's result does
+// not depend on the order.  The groups' Hessians run one after another on one library
+// stream; the k-th started group's factorization and its layers' sweeps run on slot
+// stream k mod n_slots, each slot with its own H, U and workspaces and its own
+// auxiliary stream for the factorization's inverse.  So the next group's Hessian
+// (matrix-core bound) runs beside the current groups' factorizations (latency-bound
+// chains of 64-column steps) and sweeps, and the factorizations of up to n_slots groups
+// overlap one another.  A group's Hessian waits until its slot's previous group has
+// finished with H and U.  Events order the whole call after the work already on the
+// caller's stream, and the caller's stream after it.
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gptq {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__global__ void zero_f32_kernel(float* p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+void zero_f32(float* p, int64_t n, hipStream_t s) {
+    const int64_t blocks = (n + 255) / 256;
+    zero_f32_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>(p, n);
+}
+
+struct LayersSlot {
+    hipStream_t s = nullptr;
+    PrepAux aux;
+    hipEvent_t hdone = nullptr, free = nullptr;
+};
+
+struct LayersDev {
+    bool ready = false;
+    hipStream_t hs = nullptr;          // the Hessians
+    hipEvent_t start = nullptr, hs_done = nullptr;
+    LayersSlot slot[GPTQ_LAYERS_MAX_SLOTS];
+};
+
+// Streams and events are made once per device and kept until the process ends (all at
+// the default priority); enqueueing is serialized so that concurrent calls do not
+// interleave their event records.
+static std::mutex layers_mu;
+static LayersDev layers_dev[64];
+
+static gptq_status layers_resources(LayersDev*& out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GPTQ_ERR_HIP;
+    LayersDev& L = layers_dev[dev];
+    if (!L.ready) {
+        auto ev = [](hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess; };
+        auto st = [](hipStream_t* s) { return hipStreamCreateWithFlags(s, hipStreamNonBlocking) == hipSuccess; };
+        if (!st(&L.hs) || !ev(&L.start) || !ev(&L.hs_done)) return GPTQ_ERR_HIP;
+        for (auto& sl : L.slot)
+            if (!st(&sl.s) || !st(&sl.aux.s) || !ev(&sl.aux.fork) || !ev(&sl.aux.join) || !ev(&sl.hdone) ||
+                !ev(&sl.free))
+                return GPTQ_ERR_HIP;
+        L.ready = true;
+    }
+    out = &L;
+    return GPTQ_OK;
+}
+
+static bool same_inputs(const gptq_layer& a, const gptq_layer& b) {
+    return a.X == b.X && a.x_dtype == b.x_dtype && a.n_tokens == b.n_tokens && a.ldx == b.ldx && a.d_col == b.d_col;
+}
+
+// Workspace: n_slots x (H, U, factorization workspace, sweep workspace), each sized for
+// the largest layer, then one Hessian workspace (the Hessians run one at a time).
+struct LayersPlan {
+    size_t h_bytes = 0, p_bytes = 0, q_bytes = 0, hw_bytes = 0, slot_bytes = 0, total = 0;
+};
+
+static LayersPlan layers_plan(const gptq_layer* L, int n, int n_slots) {
+    LayersPlan p;
+    for (int i = 0; i < n; ++i) {
+        const int64_t d = L[i].d_col;
+        p.h_bytes = std::max(p.h_bytes, align256((size_t)d * d * sizeof(float)));
+        p.p_bytes = std::max(p.p_bytes, align256(prep_ws_bytes(d)));
+        p.q_bytes = std::max(p.q_bytes, align256(quant_ws_bytes(L[i].d_row, d)));
+        p.hw_bytes = std::max(p.hw_bytes, align256(hessian_ws_bytes(L[i].n_tokens, d)));
+    }
+    p.slot_bytes = 2 * p.h_bytes + p.p_bytes + p.q_bytes;
+    p.total = n > 0 ? (size_t)n_slots * p.slot_bytes + p.hw_bytes : 0;
+    return p;
+}
+
+size_t layers_ws_bytes(const gptq_layer* L, int n, int n_slots) { return layers_plan(L, n, n_slots).total; }
+
+gptq_status layers_launch(const gptq_layer* L, int n, float percdamp, const gptq_params& prm, int n_slots,
+                          void* ws, size_t ws_bytes, int32_t* info, hipStream_t caller) {
+    const LayersPlan plan = layers_plan(L, n, n_slots);
+    if (ws == nullptr || ws_bytes < plan.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return GPTQ_ERR_WORKSPACE;
+    LayersDev* R = nullptr;
+    gptq_status st;
+    std::lock_guard<std::mutex> g(layers_mu);
+    if ((st = layers_resources(R)) != GPTQ_OK) return st;
+    char* base = reinterpret_cast<char*>(ws);
+    void* hws = base + (size_t)n_slots * plan.slot_bytes;
+    auto slot_ptr = [&](int s, size_t off) { return base + (size_t)s * plan.slot_bytes + off; };
+
+    fill_i32(info, 2 * n, 0, caller);
+    GPTQ_LAUNCH_CHECK();
+    if (hipEventRecord(R->start, caller) != hipSuccess || hipStreamWaitEvent(R->hs, R->start, 0) != hipSuccess)
+        return GPTQ_ERR_HIP;
+    for (int s = 0; s < n_slots; ++s)
+        if (hipStreamWaitEvent(R->slot[s].s, R->start, 0) != hipSuccess) return GPTQ_ERR_HIP;
+
+    // groups [first, end) of consecutive layers with the same inputs, widest first
+    std::vector<std::pair<int, int>> grp;
+    for (int i = 0; i < n;) {
+        int j = i + 1;
+        while (j < n && same_inputs(L[i], L[j])) ++j;
+        grp.push_back({i, j});
+        i = j;
+    }
+    std::stable_sort(grp.begin(), grp.end(), [&](const std::pair<int, int>& a, const std::pair<int, int>& b) {
+        return L[a.first].d_col > L[b.first].d_col;
+    });
+    int groups = 0;
+    for (const auto& gr : grp) {
+        const int i = gr.first, j = gr.second;
+        const int s = groups % n_slots;
+        LayersSlot& sl = R->slot[s];
+        const int64_t d = L[i].d_col;
+        float* H = reinterpret_cast<float*>(slot_ptr(s, 0));
+        float* U = reinterpret_cast<float*>(slot_ptr(s, plan.h_bytes));
+        void* pws = slot_ptr(s, 2 * plan.h_bytes);
+        void* qws = slot_ptr(s, 2 * plan.h_bytes + plan.p_bytes);
+        // H and U of this slot are free once its previous group's sweeps are done
+        if (groups >= n_slots && hipStreamWaitEvent(R->hs, sl.free, 0) != hipSuccess) return GPTQ_ERR_HIP;
+        zero_f32(H, d * d, R->hs);
+        GPTQ_LAUNCH_CHECK();
+        if ((st = hessian_launch(H, L[i].X, L[i].x_dtype, L[i].n_tokens, d, L[i].ldx, hws, plan.hw_bytes, R->hs)) !=
+            GPTQ_OK)
+            return st;
+        if (hipEventRecord(sl.hdone, R->hs) != hipSuccess || hipStreamWaitEvent(sl.s, sl.hdone, 0) != hipSuccess)
+            return GPTQ_ERR_HIP;
+        if ((st = prep_launch(H, U, d, percdamp, pws, plan.p_bytes, info + 2 * i, sl.s, &sl.aux)) != GPTQ_OK)
+            return st;
+        for (int l = i; l < j; ++l)
+            if ((st = quant_launch(L[l].W, L[l].w_dtype, L[l].d_row, d, U, prm, L[l].codes, L[l].scales_f16,
+                                   L[l].zeros_f16, qws, plan.q_bytes, info + 2 * l + 1, sl.s)) != GPTQ_OK)
+                return st;
+        if (hipEventRecord(sl.free, sl.s) != hipSuccess) return GPTQ_ERR_HIP;
+        ++groups;
+    }
+    // the caller's stream resumes after every slot and the Hessian stream
+    for (int s = 0; s < n_slots && s < groups; ++s)
+        if (hipStreamWaitEvent(caller, R->slot[s].free, 0) != hipSuccess) return GPTQ_ERR_HIP;
+    if (hipEventRecord(R->hs_done, R->hs) != hipSuccess || hipStreamWaitEvent(caller, R->hs_done, 0) != hipSuccess)
+        return GPTQ_ERR_HIP;
+    return GPTQ_OK;
+}
+
+}  // namespace gptq

@@ -924,7 +924,7 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // One auxiliary stream and two events per device, created on first use and kept
 // until the process ends; enqueueing is serialized so that concurrent calls do not
 // interleave their fork / join records.
-struct AuxStream { hipStream_t s = nullptr; hipEvent_t fork = nullptr, join = nullptr; };
+typedef PrepAux AuxStream;
 static std::mutex aux_mu;
 static AuxStream aux_dev[64];
 
@@ -972,7 +972,7 @@ static gptq_status aux_stream(AuxStream*& out) {
 #ifndef INV_LAST
 #define INV_LAST 1024
 #endif
-static gptq_status cholinv(PrepCtx& c) {
+static gptq_status cholinv(PrepCtx& c, AuxStream* own_aux) {
     const int64_t d = c.d;
     gptq_status st;
     prep_diag_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, 0, (int)std::min<int64_t>(PNB, d), c.info);
@@ -1001,8 +1001,8 @@ static gptq_status cholinv(PrepCtx& c) {
     double* Smain = Trest + (d - h) * sl;
     auto trow = [&](int64_t r) { return Trest + (r - h) * sl; };
 
-    AuxStream* aux = nullptr;
-    if ((st = aux_stream(aux)) != GPTQ_OK) return st;
+    AuxStream* aux = own_aux;
+    if (aux == nullptr && (st = aux_stream(aux)) != GPTQ_OK) return st;
     PrepCtx ca = c;
     ca.s = aux->s;
     // block i's columns are final once the step that forms the panel of its last 64
@@ -1077,7 +1077,7 @@ size_t prep_ws_bytes(int64_t d) {
 }
 
 gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, void* ws, size_t ws_bytes,
-                        int32_t* info, hipStream_t s) {
+                        int32_t* info, hipStream_t s, PrepAux* own_aux) {
     if (ws == nullptr || ws_bytes < prep_ws_bytes(d)) return GPTQ_ERR_WORKSPACE;
     char* p = reinterpret_cast<char*>(ws);
     const size_t dd = align256((size_t)d * d * sizeof(double));
@@ -1098,9 +1098,11 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     else prep_build_kernel<false><<<gb, 256, 0, s>>>(H, d, lam, c.A);
     GPTQ_LAUNCH_CHECK();
     gptq_status st;
-    {
+    if (own_aux) {
+        st = cholinv(c, own_aux);   // the caller's auxiliary stream and events
+    } else {
         std::lock_guard<std::mutex> g(aux_mu);
-        st = cholinv(c);
+        st = cholinv(c, nullptr);
     }
     if (st != GPTQ_OK) return st;
     if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0) prep_output_kernel<true><<<gb4, 256, 0, s>>>(c.X, d, U);

@@ -35,7 +35,13 @@ def lib():
     class Params(ctypes.Structure):
         _fields_ = [("bits", i32), ("group_size", i32), ("sym", i32), ("block_size", i32)]
 
+    class LayerDesc(ctypes.Structure):
+        _fields_ = [("X", vp), ("x_dtype", ctypes.c_int), ("n_tokens", i64), ("ldx", i64), ("W", vp),
+                    ("w_dtype", ctypes.c_int), ("d_row", i64), ("d_col", i64), ("codes", vp),
+                    ("scales_f16", vp), ("zeros_f16", vp)]
+
     L.Params = Params
+    L.LayerDesc = LayerDesc
     sig = {
         "gptq_hessian_workspace_size": (sz, [i64, i64]),
         "gptq_hessian_accumulate": (ctypes.c_int, [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp]),
@@ -44,6 +50,9 @@ def lib():
         "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
+        "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
+        "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
+                                                ctypes.POINTER(Params), i32, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
         "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
                                                  vp, ctypes.c_int, vp]),
@@ -60,6 +69,7 @@ def test_header_declares_the_boundary():
         "gptq_hessian_workspace_size", "gptq_hessian_accumulate",
         "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
         "gptq_quantize_workspace_size", "gptq_quantize_layer",
+        "gptq_quantize_layers_workspace_size", "gptq_quantize_layers",
         "gptq_dequantize", "gptq_quantized_linear", "gptq_status_string"])
 
 
@@ -158,3 +168,53 @@ def test_linear_argument_errors(lib):
     assert call(codes=None) == INVALID_ARG
     assert call(y=None) == INVALID_ARG
     assert call(n=0, codes=None, x=None, y=None) == OK   # no tokens: no work
+
+
+def _layers(lib, specs, ptr=FAKE):
+    """gptq_layer descriptors: (X id, n_tokens, d_row, d_col) each; equal X ids share inputs."""
+    arr = (lib.LayerDesc * len(specs))()
+    for k, (xid, n, r, c) in enumerate(specs):
+        arr[k] = lib.LayerDesc(0x100000 * (xid + 1), BF16, n, c, ptr, BF16, r, c, ptr, ptr, ptr)
+    return arr
+
+
+def test_layers_workspace_size(lib):
+    """n_slots x (H, U, factorization and sweep workspaces of the largest layer) + one
+    Hessian workspace, each 256-byte aligned; inputs shared or not, the size is the same."""
+    f = lib.gptq_quantize_layers_workspace_size
+    a256 = lambda x: (x + 255) // 256 * 256
+    specs = [(0, 4096, 256, 512), (0, 4096, 384, 512), (1, 2048, 512, 1024)]
+    h = a256(1024 * 1024 * 4)
+    pw = a256(lib.gptq_prepare_hinv_workspace_size(1024))
+    qw = max(a256(lib.gptq_quantize_workspace_size(r, c, None)) for _, _, r, c in specs)
+    hw = max(a256(lib.gptq_hessian_workspace_size(n, c)) for _, n, _, c in specs)
+    for slots in (1, 2, 3):
+        assert f(_layers(lib, specs), 3, slots) == slots * (2 * h + pw + qw) + hw
+    assert f(_layers(lib, specs), 0, 2) == 0
+    assert f(_layers(lib, specs), 3, 0) == 0        # slots out of range
+    assert f(_layers(lib, specs), 3, 5) == 0
+    assert f(_layers(lib, [(0, 0, 256, 512)]), 1, 1) == 0   # no tokens
+
+
+def test_layers_argument_errors(lib):
+    f = lib.gptq_quantize_layers
+    p = lib.Params(4, 128, 0, 128)
+    good = _layers(lib, [(0, 4096, 256, 512), (1, 4096, 256, 512)])
+    need = lib.gptq_quantize_layers_workspace_size(good, 2, 2)
+    ws = ctypes.c_void_p(0x10000000)
+    call = lambda layers, n=2, slots=2, prm=ctypes.byref(p), damp=0.01, w=ws, wb=need, info=FAKE: \
+        f(layers, n, damp, prm, slots, w, wb, info, None)
+    assert call(good, slots=0) == INVALID_ARG
+    assert call(good, slots=5) == INVALID_ARG
+    assert call(None, n=1) == INVALID_ARG
+    assert call(good, prm=None) == INVALID_ARG
+    assert call(good, damp=-1.0) == INVALID_ARG
+    assert call(good, info=None) == INVALID_ARG
+    assert call(_layers(lib, [(0, 0, 256, 512)]), n=1) == INVALID_ARG          # no tokens
+    assert call(_layers(lib, [(0, 4096, 256, 512)], ptr=None), n=1) == INVALID_ARG   # null W / outputs
+    bad = lib.Params(5, 128, 0, 128)
+    assert call(good, prm=ctypes.byref(bad)) == UNSUPPORTED
+    assert call(_layers(lib, [(0, 4096, 256, 500)]), n=1) == INVALID_ARG     # group does not divide d_col
+    assert call(good, wb=need - 1) == WORKSPACE
+    assert call(good, w=ctypes.c_void_p(0x10000010)) == WORKSPACE         # not 256-byte aligned
+    assert call(good, n=0) == OK
