@@ -98,7 +98,7 @@ def symmetric_quantize(x, absmax: float, qmax: int):
 @dataclasses.dataclass(frozen=True)
 class Params:
     bits: int = 4
-    group_size: int = 128      # 0 = one group per row (per-channel)
+    group_size: int = 128      # 0 = one group per row (per-channel); -1 = one range for the whole matrix (per-tensor)
     sym: bool = False
     block_size: int = 128
     percdamp: float = 0.01
@@ -117,7 +117,7 @@ class Params:
         return 2 ** (self.bits - 1) if self.sym else 0
 
     def group(self, d_col: int) -> int:
-        return d_col if self.group_size == 0 else self.group_size
+        return d_col if self.group_size <= 0 else self.group_size
 
 
 def _f32(x):
@@ -142,6 +142,13 @@ def group_params(vals: np.ndarray, p: Params):
      literal min/max; symmetric: [-a, a], Z = 0) and "Choose granularity"
      (one scale per group of consecutive weights of a row)]
     """
+    if p.group_size < 0:
+        # Per-tensor: one range over the values of every row, the same S and Z for all
+        # rows.  Callers pass the whole matrix before any column is quantized.
+        # ["Choose granularity": per-tensor, a single scale for the whole tensor]
+        S, S16, Z, t = group_params(np.asarray(vals).reshape(1, -1), dataclasses.replace(p, group_size=0))
+        n = vals.shape[0]
+        return np.repeat(S, n), np.repeat(S16, n), np.repeat(Z, n), np.repeat(t, n)
     qmin, qmax = p.qmin, p.qmax
     if p.sym:
         a = np.max(np.abs(vals), axis=1)
@@ -341,7 +348,7 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     d_row, d_col = W.shape
     g = p.group(d_col)
     B = p.block_size
-    if not (p.group_size == 0 or B % g == 0):
+    if not (p.group_size <= 0 or B % g == 0):
         raise ValueError("group must not straddle a block")
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
@@ -463,7 +470,7 @@ def dequantize(codes: np.ndarray, scales16: np.ndarray, zeros: np.ndarray, group
     """
     codes = np.asarray(codes)
     d_col = codes.shape[1]
-    g = d_col if group_size == 0 else group_size
+    g = d_col if group_size <= 0 else group_size
     idx = np.arange(d_col) // g
     s = np.asarray(scales16, dtype=np.float16).astype(np.float32)[:, idx]
     z = np.asarray(zeros).astype(np.float32)[:, idx]
