@@ -66,7 +66,11 @@ typedef enum {
 typedef struct {
     int32_t bits;        /* 3 or 4 (codes packed two per byte) or 8 (one per byte) */
     int32_t group_size;  /* weights per scale/zero group along a row; must divide
-                            block_size and d_col; 0 = one group per row */
+                            block_size and d_col; 0 = one group per row; -1 = one range
+                            for the whole matrix (per tensor: every row stores the same
+                            S16 and zero, laid out as one group per row; dequantize and
+                            the quantized linear take -1 or 0 for it).  Quantization
+                            concepts guide, "Choose granularity". */
     int32_t sym;         /* 0: asymmetric grid [0, 2^bits-1], S = (max-min)/(2^bits-1),
                                Z = -round(min/S16);
                             1: symmetric grid +-(2^(bits-1)-1), S = absmax/(2^(bits-1)-1),
@@ -151,7 +155,7 @@ gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float per
  *             column 2k+1 in the high nibble (d_col must be even);
  *             bits == 8: d_row x d_col bytes.  Codes are unsigned (see gptq_params).
  *  scales_f16 d_row x n_groups fp16 bit patterns (S16); n_groups = d_col/group_size,
- *             or 1 when group_size == 0.
+ *             or 1 when group_size is 0 or -1.
  *  zeros_f16  d_row x n_groups fp16 bit patterns of the stored (integer) zero point.
  *  ws         at least gptq_quantize_workspace_size(d_row, d_col, p) bytes.
  *  info       device int32: 0, or -1 when W holds a non-finite value or a scale is

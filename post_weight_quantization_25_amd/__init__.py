@@ -181,7 +181,7 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: 
         raise ValueError("W must be f32/bf16/f16 and U float32")
     d_row, d_col = W.shape
     p = make_params(bits, group_size, sym, block_size)
-    n_groups = 1 if group_size == 0 else max(1, d_col // group_size)
+    n_groups = 1 if group_size <= 0 else max(1, d_col // group_size)
     if out is None:
         cb = d_col // 2 if bits <= 4 else d_col
         out = Quantized(torch.empty((d_row, cb), dtype=torch.uint8, device=W.device),
@@ -241,7 +241,7 @@ def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = Fal
         outs = []
         for _, W in pairs:
             d_row, d_col = W.shape
-            n_groups = 1 if group_size == 0 else max(1, d_col // group_size)
+            n_groups = 1 if group_size <= 0 else max(1, d_col // group_size)
             outs.append(Quantized(torch.empty((d_row, d_col // 2 if bits <= 4 else d_col), dtype=torch.uint8, device=dev),
                                   torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),
                                   torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),

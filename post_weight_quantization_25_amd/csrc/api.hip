@@ -12,7 +12,7 @@ static gptq_status check_params(const gptq_params* p, int64_t d_col) {
     if (p == nullptr) return GPTQ_ERR_INVALID_ARG;
     if (p->bits != 3 && p->bits != 4 && p->bits != 8) return GPTQ_ERR_UNSUPPORTED;
     if (p->block_size != 128) return GPTQ_ERR_UNSUPPORTED;
-    if (p->group_size < 0) return GPTQ_ERR_INVALID_ARG;
+    if (p->group_size < -1) return GPTQ_ERR_INVALID_ARG;   // -1: per tensor, 0: per row
     if (p->group_size > 0) {
         if (p->block_size % p->group_size != 0 || d_col % p->group_size != 0) return GPTQ_ERR_INVALID_ARG;
         if (p->group_size != 32 && p->group_size != 64 && p->group_size != 128) return GPTQ_ERR_UNSUPPORTED;
@@ -108,6 +108,7 @@ gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, flo
 gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* zeros_f16,
                             int64_t d_row, int64_t d_col, int32_t bits, int32_t group_size, void* W_out,
                             gptq_dtype out_dtype, void* stream) {
+    if (group_size == -1) group_size = 0;   // per tensor is stored as one (equal) group per row
     if (d_row < 0 || d_col < 0 || !valid_dtype(out_dtype) || group_size < 0) return GPTQ_ERR_INVALID_ARG;
     if (bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_UNSUPPORTED;
     if (group_size > 0 && d_col % group_size != 0) return GPTQ_ERR_INVALID_ARG;
@@ -123,6 +124,7 @@ gptq_status gptq_quantized_linear(const uint8_t* codes, const uint16_t* scales_f
                                   int64_t d_row, int64_t d_col, int32_t bits, int32_t group_size, const void* x,
                                   gptq_dtype x_dtype, int64_t n_tokens, int64_t ldx, void* y, gptq_dtype y_dtype,
                                   void* stream) {
+    if (group_size == -1) group_size = 0;   // per tensor is stored as one (equal) group per row
     if (d_row < 0 || d_col < 0 || n_tokens < 0 || group_size < 0) return GPTQ_ERR_INVALID_ARG;
     if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return GPTQ_ERR_INVALID_ARG;
     if (bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_UNSUPPORTED;

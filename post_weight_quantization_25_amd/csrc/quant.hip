@@ -27,12 +27,32 @@ GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 6
 
 // --------------------------------------------------------------------------
 // One scale/zero per row (group_size 0): from the original row, before any update.
+// S16 and the stored zero of one range: [mn, mx] (asymmetric; a constant range is
+// widened to include 0) or its absolute maximum (symmetric); *info = -1 when the scale
+// is not a normal fp16 number.
 template <int BITS, bool SYM>
-__global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64_t d_col, uint16_t* scales,
-                                                         uint16_t* zeros, int32_t* info) {
+GPTQ_DEV void range_params(float mn, float mx, int32_t* info, uint16_t& s_out, uint16_t& z_out) {
     constexpr int QMIN = SYM ? -((1 << (BITS - 1)) - 1) : 0;
     constexpr int QMAX = SYM ? ((1 << (BITS - 1)) - 1) : (1 << BITS) - 1;
     constexpr int ZOFF = SYM ? (1 << (BITS - 1)) : 0;
+    float s, zf = 0.f;
+    if (SYM) {
+        const float am = fmaxf(fabsf(mn), fabsf(mx));
+        s = am > 0.f ? am / (float)QMAX : 1.f;
+    } else {
+        if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
+        s = (mx > mn) ? (mx - mn) / (float)(QMAX - QMIN) : 1.f;
+    }
+    float s16f = f16_bits_to_f32(f32_to_f16_bits(s));
+    if (!normal_f16_scale(s16f)) { *info = -1; s16f = 1.f; }
+    if (!SYM) zf = (float)QMIN - rintf(mn / s16f);
+    s_out = f32_to_f16_bits(s16f);
+    z_out = f32_to_f16_bits(zf + (float)ZOFF);
+}
+
+template <int BITS, bool SYM>
+__global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64_t d_col, uint16_t* scales,
+                                                         uint16_t* zeros, int32_t* info) {
     __shared__ float smn[256], smx[256];
     const int64_t row = blockIdx.x;
     const float* w = Wws + row * d_col;
@@ -51,20 +71,52 @@ __global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64
         __syncthreads();
     }
     if (threadIdx.x != 0) return;
-    mn = smn[0]; mx = smx[0];
-    float s, zf = 0.f;
-    if (SYM) {
-        const float am = fmaxf(fabsf(mn), fabsf(mx));
-        s = am > 0.f ? am / (float)QMAX : 1.f;
-    } else {
-        if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
-        s = (mx > mn) ? (mx - mn) / (float)(QMAX - QMIN) : 1.f;
+    range_params<BITS, SYM>(smn[0], smx[0], info, scales[row], zeros[row]);
+}
+
+// Per-tensor granularity (one range for the whole matrix; Quantization concepts
+// guide, "Choose granularity"): min and max of every block's share of the working
+// copy, then one block reduces the partial ranges and gives every row the same S16
+// and zero.
+__global__ __launch_bounds__(256) void tensor_minmax_kernel(const float* Wws, int64_t n, float* part) {
+    __shared__ float smn[256], smx[256];
+    float mn = INFINITY, mx = -INFINITY;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const float v = Wws[i];
+        mn = fminf(mn, v); mx = fmaxf(mx, v);
     }
-    float s16f = f16_bits_to_f32(f32_to_f16_bits(s));
-    if (!normal_f16_scale(s16f)) { *info = -1; s16f = 1.f; }
-    if (!SYM) zf = (float)QMIN - rintf(mn / s16f);
-    scales[row] = f32_to_f16_bits(s16f);
-    zeros[row] = f32_to_f16_bits(zf + (float)ZOFF);
+    smn[threadIdx.x] = mn; smx[threadIdx.x] = mx;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+        if ((int)threadIdx.x < st) {
+            smn[threadIdx.x] = fminf(smn[threadIdx.x], smn[threadIdx.x + st]);
+            smx[threadIdx.x] = fmaxf(smx[threadIdx.x], smx[threadIdx.x + st]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) { part[2 * blockIdx.x] = smn[0]; part[2 * blockIdx.x + 1] = smx[0]; }
+}
+
+template <int BITS, bool SYM>
+__global__ __launch_bounds__(256) void tensor_params_kernel(const float* part, int nb, int64_t d_row,
+                                                            uint16_t* scales, uint16_t* zeros, int32_t* info) {
+    __shared__ float smn[256], smx[256];
+    __shared__ uint16_t sz[2];
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = threadIdx.x; i < nb; i += 256) { mn = fminf(mn, part[2 * i]); mx = fmaxf(mx, part[2 * i + 1]); }
+    smn[threadIdx.x] = mn; smx[threadIdx.x] = mx;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+        if ((int)threadIdx.x < st) {
+            smn[threadIdx.x] = fminf(smn[threadIdx.x], smn[threadIdx.x + st]);
+            smx[threadIdx.x] = fmaxf(smx[threadIdx.x], smx[threadIdx.x + st]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) range_params<BITS, SYM>(smn[0], smx[0], info, sz[0], sz[1]);
+    __syncthreads();
+    for (int64_t r = threadIdx.x; r < d_row; r += 256) { scales[r] = sz[0]; zeros[r] = sz[1]; }
 }
 
 // W (any dtype) -> fp32 working copy; flags non-finite values.  Eight values per
@@ -602,6 +654,23 @@ static gptq_status launch_row_params(int bits, bool sym, const float* Wws, int64
     return GPTQ_OK;
 }
 
+// Per-tensor: partial ranges of up to 1024 blocks (in the E area of the workspace, which
+// the sweep only uses later on the same stream), then one block for S16 and the zero.
+static gptq_status launch_tensor_params(int bits, bool sym, const float* Wws, int64_t d_row, int64_t d_col,
+                                        float* part, int nb, uint16_t* scales, uint16_t* zeros, int32_t* info,
+                                        hipStream_t s) {
+    tensor_minmax_kernel<<<nb, 256, 0, s>>>(Wws, d_row * d_col, part);
+    GPTQ_LAUNCH_CHECK();
+#define TP(B, S) tensor_params_kernel<B, S><<<1, 256, 0, s>>>(part, nb, d_row, scales, zeros, info)
+    if (bits == 4) { if (sym) TP(4, true); else TP(4, false); }
+    else if (bits == 3) { if (sym) TP(3, true); else TP(3, false); }
+    else if (bits == 8) { if (sym) TP(8, true); else TP(8, false); }
+    else return GPTQ_ERR_UNSUPPORTED;
+#undef TP
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
 gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
                          const gptq_params& p, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
                          void* ws, size_t ws_bytes, int32_t* info, hipStream_t s) {
@@ -619,8 +688,8 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     uint16_t* Uthi = reinterpret_cast<uint16_t*>(wp);
     wp += align256(ut_bytes(d_col));
     uint16_t* Utlo = reinterpret_cast<uint16_t*>(wp);
-    const int G = p.group_size;
-    const int n_groups = (G == 0) ? 1 : (int)(d_col / G);
+    const int G = p.group_size;                 // -1: per tensor, 0: per row
+    const int n_groups = (G <= 0) ? 1 : (int)(d_col / G);
 
     fill_i32(info, 1, 0, s);
     GPTQ_LAUNCH_CHECK();
@@ -637,6 +706,12 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     if (G == 0) {
         st = launch_row_params(p.bits, p.sym != 0, Wws, d_row, d_col, scales, zeros, info, s);
         if (st != GPTQ_OK) return st;
+    } else if (G < 0) {
+        // E holds d_row x QSB bf16 values: room for 64 d_row partial ranges
+        const int nb = (int)std::min<int64_t>(1024, 64 * d_row);
+        st = launch_tensor_params(p.bits, p.sym != 0, Wws, d_row, d_col, reinterpret_cast<float*>(Ehi), nb, scales,
+                                  zeros, info, s);
+        if (st != GPTQ_OK) return st;
     }
     SweepArgs sa;
     {
@@ -651,7 +726,8 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U;
     sa.codes = codes; sa.code_ld = (p.bits <= 4) ? d_col / 2 : d_col;
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
-    sa.group = G; sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
+    sa.group = G < 0 ? 0 : G;   // per tensor: every row's parameters are set, as per row
+    sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
     sa.qmin = sa.sym ? -((1 << (p.bits - 1)) - 1) : 0;
     sa.qmax = sa.sym ? ((1 << (p.bits - 1)) - 1) : (1 << p.bits) - 1;
     sa.zoff = sa.sym ? (1 << (p.bits - 1)) : 0;

@@ -42,6 +42,11 @@ CASES = [
     (65, 256, 8, 128, False, "f32"),
     (90, 320, 4, 64, False, "f32"),     # blocks 128, 128, 64
     (1, 256, 4, 128, False, "f32"),
+    # per tensor (group -1): one range for the whole matrix, stored as one group per row
+    (300, 512, 4, -1, False, "f32"),
+    (200, 384, 3, -1, True, "bf16"),
+    (65, 256, 8, -1, False, "f32"),
+    (17, 200, 4, -1, False, "f32"),     # ragged last block, few rows
 ]
 
 
@@ -60,7 +65,9 @@ def test_quantize_parity(d_row, d_col, bits, group, sym, wdt):
     codes = unpack_codes(q.codes.cpu().numpy(), bits)
     s16 = q.scales.cpu().numpy()
     z = q.zeros.cpu().numpy().astype(np.int64)
-    rep = parity_report(codes, s16, z, ref, group, tie_window=1e-3)
+    if group < 0:   # per tensor: every row holds the same scale and zero
+        assert np.all(s16 == s16[0, 0]) and np.all(z == z[0, 0])
+    rep = parity_report(codes, s16, z, ref, max(group, 0), tie_window=1e-3)
     log(f"  codes {rep['code_match']:.6f} groups {rep['group_match']:.6f} rows with events "
         f"{rep['rows_with_events']} unjustified {rep['unjustified'][:3]}")
     assert rep["code_match"] >= 0.999
@@ -69,7 +76,7 @@ def test_quantize_parity(d_row, d_col, bits, group, sym, wdt):
     clean = np.all(codes == ref.codes, axis=1)
     assert np.array_equal(q.codes.cpu().numpy()[clean], o.pack(ref.codes, bits)[clean])
     # dequantization of the kernel's own codes: S16 (u - z) exactly, in fp32
-    gi = np.arange(d_col) // (d_col if group == 0 else group)
+    gi = np.arange(d_col) // (d_col if group <= 0 else group)
     expect = s16.astype(np.float32)[:, gi] * (codes.astype(np.float32) - z.astype(np.float32)[:, gi])
     wh = What.cpu().numpy()
     assert np.array_equal(wh, expect)
