@@ -411,6 +411,61 @@ def gptq_obs(W: np.ndarray, Hd: np.ndarray, p: Params) -> Result:
     return _finish(Q, S, S16, Z, ZT, what, w_at_q, t_at_q, p)
 
 
+def obq_step(w: np.ndarray, Finv: np.ndarray, live: np.ndarray, S16: float, Z: int, p: Params):
+    """One OBQ step on one row: of the remaining weights (mask ``live``), quantize the
+    one whose quantization adds the least error, (w_j - q(w_j))^2 / [Finv]_jj (ties to
+    the lowest index); move the other remaining weights by the OBS update
+    -(w_j - q(w_j)) / [Finv]_jj * Finv[:, j]; remove j from the inverse Hessian of the
+    remaining weights, Finv - Finv[:, j] Finv[j, :] / [Finv]_jj.  Returns
+    (j, q_j, what_j, w, Finv, live), the arrays updated copies.
+
+    [GPTQ summary page, OBQ background: greedy order by the smallest added error, the
+     update of the remaining weights through the inverse Hessian, and the removal of
+     the quantized weight from that inverse]
+    """
+    w = w.copy(); Finv = Finv.copy(); live = live.copy()
+    q = decide_codes(w, np.full(w.shape, S16), np.full(w.shape, Z, dtype=np.int64), p)
+    wh = S16 * (q - Z)
+    score = np.where(live, (w - wh) ** 2 / np.where(live, np.diag(Finv), 1.0), np.inf)
+    j = int(np.argmin(score))
+    err = (w[j] - wh[j]) / Finv[j, j]
+    col = Finv[:, j].copy()
+    upd = live.copy(); upd[j] = False
+    w[upd] -= err * col[upd]
+    Finv -= np.outer(col, col) / col[j]
+    live[j] = False
+    Finv[j, :] = 0.0; Finv[:, j] = 0.0
+    return j, int(q[j]), float(wh[j]), w, Finv, live
+
+
+def obq(W: np.ndarray, Hd: np.ndarray, p: Params) -> tuple[Result, np.ndarray]:
+    """OBQ: every row on its own, its weights quantized in a greedy order (``obq_step``
+    until none remain), starting from the inverse of the damped Hessian.  The row's grid
+    (one group per row) is fixed first from its original values.  O(d_row d_col^3).
+    Returns the result and each row's order of quantization.
+
+    [GPTQ summary page, OBQ background (the method GPTQ is compared with: per-row
+     greedy order, inverse Hessian updated after every weight)]
+    """
+    if p.group_size != 0:
+        raise ValueError("OBQ here uses one group per row")
+    W = np.array(W, dtype=np.float64, copy=True)
+    d_row, d_col = W.shape
+    Hinv = np.linalg.inv(Hd)
+    S, S16, Z, ZT = group_params(W, p)
+    Q = np.zeros((d_row, d_col), dtype=np.int64)
+    what = np.zeros_like(W)
+    order = np.zeros((d_row, d_col), dtype=np.int64)
+    for r in range(d_row):
+        w, Finv, live = W[r].copy(), Hinv.copy(), np.ones(d_col, dtype=bool)
+        for k in range(d_col):
+            j, qj, whj, w, Finv, live = obq_step(w, Finv, live, S16[r], int(Z[r]), p)
+            Q[r, j], what[r, j], order[r, k] = qj, whj, j
+    res = _finish(Q, S[:, None], S16[:, None], Z[:, None], ZT[:, None], what, np.zeros_like(W),
+                  np.zeros_like(W), p)
+    return res, order
+
+
 def rtn(W: np.ndarray, p: Params) -> Result:
     """Round-to-nearest: every weight quantized on its own group grid, no compensation.
 
