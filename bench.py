@@ -17,6 +17,9 @@ scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
 5: the 49152/12288 fc pair) with the same step, and prints one JSON line with
 ms/layer and the phase breakdown per layer.
 
+--obq times GPTQ against OBQ (gptq_obq_layer, the per-row greedy method) on the same
+layers from the same U and prints their runtime ratio.
+
 --linear measures, instead of the layer step, the product of the quantized layer with
 activations read from the stored format (gptq_quantized_linear) for 1, 4, 16 and 64
 tokens, beside torch's bf16 product with the unquantized weights, and prints its own
@@ -50,6 +53,7 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--linear", action="store_true")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--obq", action="store_true")
     return ap.parse_args()
 
 
@@ -293,6 +297,54 @@ def block_bench(g, layers, dev, steps: int, warmup: int, shared: bool):
     return out
 
 
+def obq_bench(args):
+    """GPTQ against OBQ (the per-row greedy method the pages compare with) on the same
+    layer from the same U: the 256 x 512 layer of workload 1 and a 1024 x 1024 layer of
+    workload 2's recipe (8192 tokens), int4 asymmetric, one group per row (the grid OBQ
+    uses here).  HIP events around each call, mean over the timed calls."""
+    import torch
+
+    import post_weight_quantization_25_amd as g
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sizes = [synth.config_layers(1)[0], synth.scaled(synth.config_layers(2)[0], 1024, 1024, 8192)]
+    rows = []
+    for L in sizes:
+        X, W = _upload(L, dev)
+        d = L.d_col
+        H = torch.zeros((d, d), dtype=torch.float32, device=dev)
+        g.hessian_accumulate(H, X)
+        U, info = g.prepare_hinv(H, 0.01)
+        ws_q = torch.empty(g.quantize_workspace_size(L.d_row, d, g.make_params(4, 0)), dtype=torch.uint8, device=dev)
+        ws_o = torch.empty(int(g.lib.gptq_obq_workspace_size(L.d_row, d)), dtype=torch.uint8, device=dev)
+
+        def timed(f, n):
+            f()
+            torch.cuda.synchronize()
+            e = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+            for k in range(n):
+                e[k][0].record(); f(); e[k][1].record()
+            torch.cuda.synchronize()
+            return float(sum(a.elapsed_time(b) for a, b in e) / n)
+
+        qg = g.quantize_layer(W, U, 4, 0, False, ws=ws_q)
+        qo = g.obq_layer(W, U, 4, False, ws=ws_o)
+        ms_g = timed(lambda: g.quantize_layer(W, U, 4, 0, False, ws=ws_q, out=qg), max(args.steps, 3))
+        print(f"[obq] {L.d_row}x{d}: GPTQ {ms_g:.3f} ms", file=sys.stderr, flush=True)
+        ms_o = timed(lambda: g.obq_layer(W, U, 4, False, ws=ws_o, out=qo), 2)
+        print(f"[obq] {L.d_row}x{d}: OBQ {ms_o:.3f} ms", file=sys.stderr, flush=True)
+        g.check_info(info, "prepare_hinv"); g.check_info(qg.info, "quantize_layer"); g.check_info(qo.info, "obq")
+        rows.append({"d_row": L.d_row, "d_col": d, "gptq_ms": ms_g, "obq_ms": ms_o, "ratio": ms_o / ms_g})
+        del X, W, H, U, ws_q, ws_o
+        torch.cuda.empty_cache()
+    rec = {"metric": "OBQ / GPTQ runtime ratio on the same layer from the same U (int4 asym, one group per row)",
+           "value": rows[-1]["ratio"], "unit": "x", "n_gpus": 1, "higher_is_better": True, "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic", "config": {"workload": "256x512 (workload 1) and 1024x1024 "
+                                                          "(workload 2 recipe, 8192 tokens)"}, "layers": rows}
+    print(json.dumps(rec), flush=True)
+
+
 def config_bench(args, cfg: int):
     """ms/layer and weights/s for every layer of one workload, printed as one JSON line."""
     import torch
@@ -341,6 +393,9 @@ def main():
               "does not implement)", file=sys.stderr)
         sys.exit(2)
 
+    if args.obq:
+        obq_bench(args)
+        return
     if args.config != 2:
         config_bench(args, args.config)
         return

@@ -215,6 +215,33 @@ gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, flo
                                  int32_t* info, void* stream);
 
 /*
+ * OBQ, the method GPTQ is compared with: every row on its own, its weights quantized
+ * in a greedy order (next: the remaining weight whose quantization adds the least
+ * error, (w_j - q(w_j))^2 / [F]_jj), each followed by the update of the row's other
+ * remaining weights and the removal of that weight from F, the inverse Hessian of the
+ * remaining weights (starting from (H + lambda I)^-1 = U^T U).  The row's grid is
+ * fixed first from its original values (one group per row).  O(d_row d_col^3); a
+ * baseline for timing, not a production path.
+ *
+ * Source: GPTQ summary page, OBQ background (greedy order, update of the remaining
+ * weights and of the inverse Hessian after each weight) and the runtime comparison
+ * with GPTQ.
+ *
+ *  W, U, p, codes, scales_f16, zeros_f16, info   as for gptq_quantize_layer; p must have
+ *             group_size 0 (else GPTQ_ERR_UNSUPPORTED).
+ *  ws         at least gptq_obq_workspace_size(d_row, d_col) bytes: H^-1 and one
+ *             d_col x d_col copy per row in flight (at most 256).
+ * Errors as gptq_quantize_layer; d_col > 2048 -> GPTQ_ERR_UNSUPPORTED.  Arithmetic is
+ * fp32, so where two candidates' added errors are nearly equal the order can differ
+ * from an fp64 evaluation.
+ */
+size_t gptq_obq_workspace_size(int64_t d_row, int64_t d_col);
+gptq_status gptq_obq_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col,
+                           const float* U, const gptq_params* p,
+                           uint8_t* codes, uint16_t* scales_f16, uint16_t* zeros_f16,
+                           void* ws, size_t ws_bytes, int32_t* info, void* stream);
+
+/*
  * W_out = S16 * (u - z) for every weight (computed in fp32, exact, then rounded
  * to out_dtype with round-to-nearest-even).
  *

@@ -61,6 +61,9 @@ def _load():
         "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
         "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
                                                 ctypes.POINTER(Params), i32, vp, sz, vp, vp]),
+        "gptq_obq_workspace_size": (sz, [i64, i64]),
+        "gptq_obq_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
+                                          vp, vp, vp, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
         "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
                                                  vp, ctypes.c_int, vp]),
@@ -194,6 +197,26 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: 
                                    ws.data_ptr() if ws is not None else None,
                                    ws.numel() if ws is not None else 0, out.info.data_ptr(), _stream(stream)),
            "gptq_quantize_layer")
+    return out
+
+
+def obq_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, sym: bool = False, ws: torch.Tensor | None = None,
+              out: Quantized | None = None, stream=None) -> Quantized:
+    """OBQ (gptq_obq_layer): per-row greedy order, one group per row; a timing baseline."""
+    _dev(W, "W"); _dev(U, "U")
+    d_row, d_col = W.shape
+    p = make_params(bits, 0, sym)
+    if out is None:
+        out = Quantized(torch.empty((d_row, d_col // 2 if bits <= 4 else d_col), dtype=torch.uint8, device=W.device),
+                        torch.empty((d_row, 1), dtype=torch.float16, device=W.device),
+                        torch.empty((d_row, 1), dtype=torch.float16, device=W.device),
+                        torch.zeros(1, dtype=torch.int32, device=W.device), bits, 0, d_col)
+    ws = _workspace(int(lib.gptq_obq_workspace_size(d_row, d_col)), W.device, ws)
+    _check(lib.gptq_obq_layer(W.data_ptr(), _DT[W.dtype], d_row, d_col, U.data_ptr(), ctypes.byref(p),
+                              out.codes.data_ptr(), out.scales.data_ptr(), out.zeros.data_ptr(),
+                              ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                              out.info.data_ptr(), _stream(stream)),
+           "gptq_obq_layer")
     return out
 
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgptq.so")
-SOURCES = ["api.hip", "hessian.hip", "prep.hip", "quant.hip", "sweep.hip", "linear.hip", "layers.hip"]
+SOURCES = ["api.hip", "hessian.hip", "prep.hip", "quant.hip", "sweep.hip", "linear.hip", "layers.hip", "obq.hip"]
 ARCH = "gfx950"
 
 

@@ -105,6 +105,25 @@ gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, flo
     return layers_launch(layers, n_layers, percdamp, *p, n_slots, ws, ws_bytes, info, (hipStream_t)stream);
 }
 
+size_t gptq_obq_workspace_size(int64_t d_row, int64_t d_col) {
+    if (d_row <= 0 || d_col <= 0 || d_col > OBQ_MAXD) return 0;
+    return obq_ws_bytes(d_row, d_col);
+}
+
+gptq_status gptq_obq_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
+                           const gptq_params* p, uint8_t* codes, uint16_t* scales_f16, uint16_t* zeros_f16,
+                           void* ws, size_t ws_bytes, int32_t* info, void* stream) {
+    if (d_row < 0 || d_col < 0 || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_params(p, d_col);
+    if (st != GPTQ_OK) return st;
+    if (p->group_size != 0) return GPTQ_ERR_UNSUPPORTED;   // one group per row
+    if (d_row == 0 || d_col == 0) return GPTQ_OK;
+    if (!W || !U || !codes || !scales_f16 || !zeros_f16 || !info) return GPTQ_ERR_INVALID_ARG;
+    if (d_col > OBQ_MAXD || d_row > 2147483647LL / 64) return GPTQ_ERR_UNSUPPORTED;
+    return obq_launch(W, w_dtype, d_row, d_col, U, *p, codes, scales_f16, zeros_f16, ws, ws_bytes, info,
+                      (hipStream_t)stream);
+}
+
 gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* zeros_f16,
                             int64_t d_row, int64_t d_col, int32_t bits, int32_t group_size, void* W_out,
                             gptq_dtype out_dtype, void* stream) {

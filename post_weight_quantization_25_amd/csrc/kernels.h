@@ -34,6 +34,12 @@ size_t layers_ws_bytes(const gptq_layer* layers, int n, int n_slots);
 gptq_status layers_launch(const gptq_layer* layers, int n, float percdamp, const gptq_params& p, int n_slots,
                           void* ws, size_t ws_bytes, int32_t* info, hipStream_t stream);
 
+constexpr int OBQ_MAXD = 2048;   // widest row the OBQ kernel keeps in LDS
+size_t obq_ws_bytes(int64_t d_row, int64_t d_col);
+gptq_status obq_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
+                       const gptq_params& p, uint8_t* codes, uint16_t* scales, uint16_t* zeros, void* ws,
+                       size_t ws_bytes, int32_t* info, hipStream_t stream);
+
 gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
                            int64_t d_col, int bits, int group_size, void* out, gptq_dtype out_dtype,
                            hipStream_t stream);

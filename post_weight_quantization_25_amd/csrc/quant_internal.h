@@ -4,6 +4,33 @@
 
 namespace gptq {
 
+// A scale is usable when fp16 holds it as a normal number.
+GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 65504.f; }
+
+// S16 and the stored zero of one range: [mn, mx] (asymmetric; a constant range is
+// widened to include 0) or its absolute maximum (symmetric); *info = -1 when the scale
+// is not a normal fp16 number.
+template <int BITS, bool SYM>
+GPTQ_DEV void range_params(float mn, float mx, int32_t* info, uint16_t& s_out, uint16_t& z_out) {
+    constexpr int QMIN = SYM ? -((1 << (BITS - 1)) - 1) : 0;
+    constexpr int QMAX = SYM ? ((1 << (BITS - 1)) - 1) : (1 << BITS) - 1;
+    constexpr int ZOFF = SYM ? (1 << (BITS - 1)) : 0;
+    float s, zf = 0.f;
+    if (SYM) {
+        const float am = fmaxf(fabsf(mn), fabsf(mx));
+        s = am > 0.f ? am / (float)QMAX : 1.f;
+    } else {
+        if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
+        s = (mx > mn) ? (mx - mn) / (float)(QMAX - QMIN) : 1.f;
+    }
+    float s16f = f16_bits_to_f32(f32_to_f16_bits(s));
+    if (!normal_f16_scale(s16f)) { *info = -1; s16f = 1.f; }
+    if (!SYM) zf = (float)QMIN - rintf(mn / s16f);
+    s_out = f32_to_f16_bits(s16f);
+    z_out = f32_to_f16_bits(zf + (float)ZOFF);
+}
+
+
 constexpr int QB = 128;             // lazy-update block width (columns)
 constexpr int QT = 256;             // threads per sweep workgroup
 constexpr int SL = 16;              // lanes per row in the sweep (one DPP row)

@@ -36,7 +36,6 @@ constexpr int SSLOTS = QB / SL;     // columns per lane: q, q+16, ..., q+112
 constexpr int WL_LD = QSB + 4;      // LDS row pitch of the super-block's W (floats)
 constexpr int UT_N = 64;            // columns of U per update chunk
 
-GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 65504.f; }
 
 template <int SRC>
 GPTQ_DEV float row_bcast(float v) {  // DPP row_newbcast: lane SRC of each 16-lane row to the whole row

@@ -53,6 +53,9 @@ def lib():
         "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
         "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
                                                 ctypes.POINTER(Params), i32, vp, sz, vp, vp]),
+        "gptq_obq_workspace_size": (sz, [i64, i64]),
+        "gptq_obq_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
+                                          vp, vp, vp, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
         "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
                                                  vp, ctypes.c_int, vp]),
@@ -70,6 +73,7 @@ def test_header_declares_the_boundary():
         "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
         "gptq_quantize_workspace_size", "gptq_quantize_layer",
         "gptq_quantize_layers_workspace_size", "gptq_quantize_layers",
+        "gptq_obq_workspace_size", "gptq_obq_layer",
         "gptq_dequantize", "gptq_quantized_linear", "gptq_status_string"])
 
 
@@ -218,3 +222,20 @@ def test_layers_argument_errors(lib):
     assert call(good, wb=need - 1) == WORKSPACE
     assert call(good, w=ctypes.c_void_p(0x10000010)) == WORKSPACE         # not 256-byte aligned
     assert call(good, n=0) == OK
+
+
+def test_obq_workspace_and_errors(lib):
+    """H^-1 plus one d_col x d_col copy per row in flight (at most 256 rows)."""
+    assert lib.gptq_obq_workspace_size(256, 512) == 257 * 512 * 512 * 4
+    assert lib.gptq_obq_workspace_size(10, 512) == 11 * 512 * 512 * 4
+    assert lib.gptq_obq_workspace_size(10, 4096) == 0          # wider than the kernel keeps in LDS
+    f = lib.gptq_obq_layer
+    p0 = lib.Params(4, 0, 0, 128)
+    pg = lib.Params(4, 128, 0, 128)
+    call = lambda prm, d_col=512, w=FAKE, wsb=1 << 40: f(w, BF16, 16, d_col, FAKE, ctypes.byref(prm), FAKE, FAKE,
+                                                          FAKE, FAKE, wsb, FAKE, None)
+    assert call(pg) == UNSUPPORTED          # grouped grids: OBQ here uses one group per row
+    assert call(p0, d_col=4096) == UNSUPPORTED
+    assert call(p0, w=None) == INVALID_ARG
+    assert call(p0, wsb=100) == WORKSPACE
+    assert f(None, BF16, 0, 512, None, ctypes.byref(p0), None, None, None, None, 0, None, None) == OK
