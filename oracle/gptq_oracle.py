@@ -102,6 +102,7 @@ class Params:
     sym: bool = False
     block_size: int = 128
     percdamp: float = 0.01
+    fp4: bool = False          # E2M1 grid with one fp16 scale per group (bits must be 4)
 
     @property
     def qmin(self) -> int:
@@ -118,6 +119,22 @@ class Params:
 
     def group(self, d_col: int) -> int:
         return d_col if self.group_size <= 0 else self.group_size
+
+
+# FP4 E2M1: 1 sign, 2 exponent, 1 mantissa bit; magnitudes by code index 0 .. 7.
+# [Quantization concepts guide, "FP4 with block scales"]
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_round(t: np.ndarray) -> np.ndarray:
+    """Index (0 .. 7) of the E2M1 magnitude nearest |t|; a tie between two neighbours
+    goes to the even index (the even mantissa bit); beyond 6 the largest, 6."""
+    a = np.abs(np.asarray(t, dtype=np.float64))
+    d = np.abs(a[..., None] - E2M1_VALUES)
+    i = np.argmin(d, axis=-1)
+    nxt = np.minimum(i + 1, 7)
+    tie = (np.take_along_axis(d, nxt[..., None], -1)[..., 0] == np.take_along_axis(d, i[..., None], -1)[..., 0]) & (nxt != i)
+    return np.where(tie & (i % 2 == 1), nxt, i)
 
 
 def _f32(x):
@@ -142,6 +159,21 @@ def group_params(vals: np.ndarray, p: Params):
      literal min/max; symmetric: [-a, a], Z = 0) and "Choose granularity"
      (one scale per group of consecutive weights of a row)]
     """
+    if p.fp4:
+        # E2M1: the group's largest magnitude goes to 6; the returned "S16" is the step
+        # S16 / 2 of the half-unit codes q = 2 * (+-E2M1 value), so that What = step * q
+        # as for the integer grids, with Z = 0  ["FP4 with block scales": one scale per
+        # small block]
+        if p.group_size < 0:
+            S, S16, Z, t = group_params(np.asarray(vals).reshape(1, -1), dataclasses.replace(p, group_size=0))
+            n = vals.shape[0]
+            return np.repeat(S, n), np.repeat(S16, n), np.repeat(Z, n), np.repeat(t, n)
+        a = np.max(np.abs(vals), axis=1)
+        S = np.where(a > 0, a / 6.0, 1.0)
+        S16 = _fp16_round(S)
+        if not np.all(np.isfinite(S16)) or np.any(S16 < 2.0 ** -14):
+            raise NonFinite("scale is not a normal fp16 number")
+        return S, S16 / 2.0, np.zeros(vals.shape[0], dtype=np.int64), np.zeros(vals.shape[0], dtype=np.float32)
     if p.group_size < 0:
         # Per-tensor: one range over the values of every row, the same S and Z for all
         # rows.  Callers pass the whole matrix before any column is quantized.
@@ -183,6 +215,10 @@ def decide_codes(w: np.ndarray, S16: np.ndarray, Z: np.ndarray, p: Params) -> np
     [Quantization concepts guide, "Mapping values to fewer bits": quantize formula;
      the clamp keeps compensated values that left the group's range on the grid]
     """
+    if p.fp4:
+        # E2M1: S16 here is the half-unit step; the quotient is by the stored scale 2 step
+        t = (_f32(w) / _f32(2.0 * np.asarray(S16))).astype(np.float32).astype(np.float64)
+        return (np.sign(t) * 2.0 * E2M1_VALUES[e2m1_round(t)]).astype(np.int64)
     t = (_f32(w) / _f32(S16)).astype(np.float32)
     return np.clip(np.rint(t.astype(np.float64)) + Z, p.qmin, p.qmax).astype(np.int64)
 
@@ -291,7 +327,17 @@ def _n_groups(d_col: int, p: Params) -> int:
     return (d_col + g - 1) // g
 
 
+def e2m1_codes(Q: np.ndarray) -> np.ndarray:
+    """Stored FP4 code of half-unit values Q = 2 * (+-E2M1 value): sign bit 8 (for a
+    nonzero negative value) | magnitude index."""
+    idx = np.searchsorted(E2M1_VALUES, np.abs(Q) / 2.0)
+    return (idx + np.where(Q < 0, 8, 0)).astype(np.uint8)
+
+
 def _finish(Q, S, S16, Z, ZT, what, w_at_q, t_at_q, p) -> Result:
+    if p.fp4:
+        return Result(q=Q, codes=e2m1_codes(Q), S=S, scales16=(2.0 * S16).astype(np.float16),
+                      zeros=np.zeros_like(Z), z_t=ZT, what=what, w_at_q=w_at_q, t_at_q=t_at_q)
     codes = (Q + p.zero_offset).astype(np.uint8)
     zeros = (Z + p.zero_offset).astype(np.int64) if not p.sym else np.full_like(Z, p.zero_offset)
     return Result(q=Q, codes=codes, S=S, scales16=S16.astype(np.float16), zeros=zeros, z_t=ZT,
@@ -516,6 +562,18 @@ def unpack(packed: np.ndarray, bits: int) -> np.ndarray:
     out[..., 0::2] = packed & 0xF
     out[..., 1::2] = packed >> 4
     return out
+
+
+def dequantize_e2m1(codes: np.ndarray, scales16: np.ndarray, group_size: int) -> np.ndarray:
+    """What = S16 * (+-E2M1 value of the code), in float32 (exact).
+    [Quantization concepts guide, "FP4 with block scales"]"""
+    codes = np.asarray(codes).astype(np.int64)
+    d_col = codes.shape[1]
+    g = d_col if group_size <= 0 else group_size
+    idx = np.arange(d_col) // g
+    s = np.asarray(scales16, dtype=np.float16).astype(np.float32)[:, idx]
+    v = np.where(codes >= 8, -1.0, 1.0) * E2M1_VALUES[codes & 7]
+    return (s * v.astype(np.float32)).astype(np.float32)
 
 
 def dequantize(codes: np.ndarray, scales16: np.ndarray, zeros: np.ndarray, group_size: int) -> np.ndarray:
