@@ -74,7 +74,12 @@ typedef struct {
     int32_t sym;         /* 0: asymmetric grid [0, 2^bits-1], S = (max-min)/(2^bits-1),
                                Z = -round(min/S16);
                             1: symmetric grid +-(2^(bits-1)-1), S = absmax/(2^(bits-1)-1),
-                               stored codes shifted by 2^(bits-1), stored zero 2^(bits-1) */
+                               stored codes shifted by 2^(bits-1), stored zero 2^(bits-1)
+                         2: FP4 E2M1 grid (bits 4): values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6},
+                            S = absmax / 6 per group, nearest value with ties to the even
+                            mantissa, code = sign bit 8 | magnitude index, stored zero 0;
+                            dequantize with gptq_dequantize_e2m1.  Quantization concepts
+                            guide, "FP4 with block scales". */
     int32_t block_size;  /* lazy-update block width; this build supports 128 */
 } gptq_params;
 
@@ -257,6 +262,17 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16,
                             void* W_out, gptq_dtype out_dtype, void* stream);
 
 /*
+ * W_out = S16 * e2m1(u) for every weight of a layer quantized on the FP4 E2M1 grid
+ * (gptq_params.sym = 2): e2m1(u) = +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}[u & 7], negative when
+ * u & 8.  Same layout and errors as gptq_dequantize (no zero array: the grid has none).
+ *
+ * Source: Quantization concepts guide, "FP4 with block scales".
+ */
+gptq_status gptq_dequantize_e2m1(const uint8_t* codes, const uint16_t* scales_f16, int64_t d_row,
+                                 int64_t d_col, int32_t group_size, void* W_out, gptq_dtype out_dtype,
+                                 void* stream);
+
+/*
  * The layer's product on its quantized weights, read from the stored format:
  *   y[t][r] = sum_c x[t][c] * What[r][c],  What[r][c] = S16[r][g] * (u[r][c] - z[r][g]),
  * accumulated in fp32 (per piece of one group: sum of x * (u - z), then times S16),
@@ -277,6 +293,7 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16,
  * multiples of 128 go to the matrix cores (u - z decoded once per 16 tokens, exact in
  * x's 16-bit type for integer zeros, else completed by a second product of the
  * remainder), otherwise the codes are streamed once per four tokens.
+ * Integer grids only (a layer on the E2M1 grid is dequantized with gptq_dequantize_e2m1).
  * Errors: negative sizes, bad dtypes or group width -> GPTQ_ERR_INVALID_ARG; bits not
  * 3/4/8 -> GPTQ_ERR_UNSUPPORTED; zero sizes are a no-op.
  */

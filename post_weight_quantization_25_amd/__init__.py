@@ -65,6 +65,7 @@ def _load():
         "gptq_obq_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                           vp, vp, vp, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
+        "gptq_dequantize_e2m1": (ctypes.c_int, [vp, vp, i64, i64, i32, vp, ctypes.c_int, vp]),
         "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
                                                  vp, ctypes.c_int, vp]),
         "gptq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -166,10 +167,12 @@ class Quantized:
     bits: int
     group_size: int
     d_col: int
+    fp4: bool = False        # codes on the E2M1 grid (sign bit 8 | magnitude index)
 
 
-def make_params(bits=4, group_size=128, sym=False, block_size=128) -> Params:
-    return Params(bits, group_size, int(bool(sym)), block_size)
+def make_params(bits=4, group_size=128, sym=False, block_size=128, fp4=False) -> Params:
+    """sym: symmetric integer grid; fp4: the E2M1 grid (bits 4)."""
+    return Params(bits, group_size, 2 if fp4 else int(bool(sym)), block_size)
 
 
 def quantize_workspace_size(d_row: int, d_col: int, p: Params) -> int:
@@ -178,19 +181,19 @@ def quantize_workspace_size(d_row: int, d_col: int, p: Params) -> int:
 
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: int = 128, sym: bool = False,
                    block_size: int = 128, ws: torch.Tensor | None = None, out: Quantized | None = None,
-                   stream=None) -> Quantized:
+                   stream=None, fp4: bool = False) -> Quantized:
     _dev(W, "W"); _dev(U, "U")
     if W.dtype not in _DT or U.dtype != torch.float32:
         raise ValueError("W must be f32/bf16/f16 and U float32")
     d_row, d_col = W.shape
-    p = make_params(bits, group_size, sym, block_size)
+    p = make_params(bits, group_size, sym, block_size, fp4)
     n_groups = 1 if group_size <= 0 else max(1, d_col // group_size)
     if out is None:
         cb = d_col // 2 if bits <= 4 else d_col
         out = Quantized(torch.empty((d_row, cb), dtype=torch.uint8, device=W.device),
                         torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
                         torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
-                        torch.zeros(1, dtype=torch.int32, device=W.device), bits, group_size, d_col)
+                        torch.zeros(1, dtype=torch.int32, device=W.device), bits, group_size, d_col, fp4)
     ws = _workspace(quantize_workspace_size(d_row, d_col, p), W.device, ws)
     _check(lib.gptq_quantize_layer(W.data_ptr(), _DT[W.dtype], d_row, d_col, U.data_ptr(), ctypes.byref(p),
                                    out.codes.data_ptr(), out.scales.data_ptr(), out.zeros.data_ptr(),
@@ -285,6 +288,10 @@ def dequantize(q: Quantized, out_dtype=torch.float32, out: torch.Tensor | None =
     d_row = q.codes.shape[0]
     if out is None:
         out = torch.empty((d_row, q.d_col), dtype=out_dtype, device=q.codes.device)
+    if q.fp4:
+        _check(lib.gptq_dequantize_e2m1(q.codes.data_ptr(), q.scales.data_ptr(), d_row, q.d_col, q.group_size,
+                                        out.data_ptr(), _DT[out.dtype], _stream(stream)), "gptq_dequantize_e2m1")
+        return out
     _check(lib.gptq_dequantize(q.codes.data_ptr(), q.scales.data_ptr(), q.zeros.data_ptr(), d_row, q.d_col,
                                q.bits, q.group_size, out.data_ptr(), _DT[out.dtype], _stream(stream)),
            "gptq_dequantize")

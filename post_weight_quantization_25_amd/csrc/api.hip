@@ -12,6 +12,8 @@ static gptq_status check_params(const gptq_params* p, int64_t d_col) {
     if (p == nullptr) return GPTQ_ERR_INVALID_ARG;
     if (p->bits != 3 && p->bits != 4 && p->bits != 8) return GPTQ_ERR_UNSUPPORTED;
     if (p->block_size != 128) return GPTQ_ERR_UNSUPPORTED;
+    if (p->sym < 0 || p->sym > 2) return GPTQ_ERR_INVALID_ARG;
+    if (p->sym == 2 && p->bits != 4) return GPTQ_ERR_UNSUPPORTED;   // E2M1 is a 4-bit grid
     if (p->group_size < -1) return GPTQ_ERR_INVALID_ARG;   // -1: per tensor, 0: per row
     if (p->group_size > 0) {
         if (p->block_size % p->group_size != 0 || d_col % p->group_size != 0) return GPTQ_ERR_INVALID_ARG;
@@ -137,6 +139,19 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, co
     if (d_row > 65535) return GPTQ_ERR_UNSUPPORTED;
     return dequant_launch(codes, scales_f16, zeros_f16, d_row, d_col, bits, group_size, W_out, out_dtype,
                           (hipStream_t)stream);
+}
+
+gptq_status gptq_dequantize_e2m1(const uint8_t* codes, const uint16_t* scales_f16, int64_t d_row, int64_t d_col,
+                                 int32_t group_size, void* W_out, gptq_dtype out_dtype, void* stream) {
+    if (group_size == -1) group_size = 0;
+    if (d_row < 0 || d_col < 0 || !valid_dtype(out_dtype) || group_size < 0 || (d_col & 1)) return GPTQ_ERR_INVALID_ARG;
+    if (group_size > 0 && d_col % group_size != 0) return GPTQ_ERR_INVALID_ARG;
+    if (d_row == 0 || d_col == 0) return GPTQ_OK;
+    if (!codes || !scales_f16 || !W_out) return GPTQ_ERR_INVALID_ARG;
+    if (d_row > 65535) return GPTQ_ERR_UNSUPPORTED;
+    // the zero array is not read on this grid: pass the scales in its place
+    return dequant_launch(codes, scales_f16, scales_f16, d_row, d_col, 4, group_size, W_out, out_dtype,
+                          (hipStream_t)stream, true);
 }
 
 gptq_status gptq_quantized_linear(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* zeros_f16,

@@ -42,7 +42,7 @@ gptq_status obq_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t
 
 gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
                            int64_t d_col, int bits, int group_size, void* out, gptq_dtype out_dtype,
-                           hipStream_t stream);
+                           hipStream_t stream, bool fp4 = false);
 
 gptq_status linear_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
                           int64_t d_col, int bits, int group_size, const void* x, gptq_dtype x_dtype, int64_t n_tok,

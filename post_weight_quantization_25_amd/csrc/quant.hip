@@ -26,7 +26,7 @@ namespace gptq {
 
 // --------------------------------------------------------------------------
 // One scale/zero per row (group_size 0): from the original row, before any update.
-template <int BITS, bool SYM>
+template <int BITS, bool SYM, bool FP4>
 __global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64_t d_col, uint16_t* scales,
                                                          uint16_t* zeros, int32_t* info) {
     __shared__ float smn[256], smx[256];
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64
         __syncthreads();
     }
     if (threadIdx.x != 0) return;
-    range_params<BITS, SYM>(smn[0], smx[0], info, scales[row], zeros[row]);
+    range_params<BITS, SYM, FP4>(smn[0], smx[0], info, scales[row], zeros[row]);
 }
 
 // Per-tensor granularity (one range for the whole matrix; Quantization concepts
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void tensor_minmax_kernel(const float* Wws, in
     if (threadIdx.x == 0) { part[2 * blockIdx.x] = smn[0]; part[2 * blockIdx.x + 1] = smx[0]; }
 }
 
-template <int BITS, bool SYM>
+template <int BITS, bool SYM, bool FP4>
 __global__ __launch_bounds__(256) void tensor_params_kernel(const float* part, int nb, int64_t d_row,
                                                             uint16_t* scales, uint16_t* zeros, int32_t* info) {
     __shared__ float smn[256], smx[256];
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void tensor_params_kernel(const float* part, i
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) range_params<BITS, SYM>(smn[0], smx[0], info, sz[0], sz[1]);
+    if (threadIdx.x == 0) range_params<BITS, SYM, FP4>(smn[0], smx[0], info, sz[0], sz[1]);
     __syncthreads();
     for (int64_t r = threadIdx.x; r < d_row; r += 256) { scales[r] = sz[0]; zeros[r] = sz[1]; }
 }
@@ -617,11 +617,12 @@ __global__ void split_u_kernel(const float* U, int64_t n, uint16_t* hi, uint16_t
     }
 }
 
-static gptq_status launch_row_params(int bits, bool sym, const float* Wws, int64_t d_row, int64_t d_col,
+static gptq_status launch_row_params(int bits, bool sym, bool fp4, const float* Wws, int64_t d_row, int64_t d_col,
                                      uint16_t* scales, uint16_t* zeros, int32_t* info, hipStream_t s) {
     dim3 grid((unsigned)d_row);
-#define RP(B, S) row_params_kernel<B, S><<<grid, 256, 0, s>>>(Wws, d_col, scales, zeros, info)
-    if (bits == 4) { if (sym) RP(4, true); else RP(4, false); }
+#define RP(B, S) row_params_kernel<B, S, false><<<grid, 256, 0, s>>>(Wws, d_col, scales, zeros, info)
+    if (fp4) row_params_kernel<4, true, true><<<grid, 256, 0, s>>>(Wws, d_col, scales, zeros, info);
+    else if (bits == 4) { if (sym) RP(4, true); else RP(4, false); }
     else if (bits == 3) { if (sym) RP(3, true); else RP(3, false); }
     else if (bits == 8) { if (sym) RP(8, true); else RP(8, false); }
     else return GPTQ_ERR_UNSUPPORTED;
@@ -632,13 +633,14 @@ static gptq_status launch_row_params(int bits, bool sym, const float* Wws, int64
 
 // Per-tensor: partial ranges of up to 1024 blocks (in the E area of the workspace, which
 // the sweep only uses later on the same stream), then one block for S16 and the zero.
-static gptq_status launch_tensor_params(int bits, bool sym, const float* Wws, int64_t d_row, int64_t d_col,
+static gptq_status launch_tensor_params(int bits, bool sym, bool fp4, const float* Wws, int64_t d_row, int64_t d_col,
                                         float* part, int nb, uint16_t* scales, uint16_t* zeros, int32_t* info,
                                         hipStream_t s) {
     tensor_minmax_kernel<<<nb, 256, 0, s>>>(Wws, d_row * d_col, part);
     GPTQ_LAUNCH_CHECK();
-#define TP(B, S) tensor_params_kernel<B, S><<<1, 256, 0, s>>>(part, nb, d_row, scales, zeros, info)
-    if (bits == 4) { if (sym) TP(4, true); else TP(4, false); }
+#define TP(B, S) tensor_params_kernel<B, S, false><<<1, 256, 0, s>>>(part, nb, d_row, scales, zeros, info)
+    if (fp4) tensor_params_kernel<4, true, true><<<1, 256, 0, s>>>(part, nb, d_row, scales, zeros, info);
+    else if (bits == 4) { if (sym) TP(4, true); else TP(4, false); }
     else if (bits == 3) { if (sym) TP(3, true); else TP(3, false); }
     else if (bits == 8) { if (sym) TP(8, true); else TP(8, false); }
     else return GPTQ_ERR_UNSUPPORTED;
@@ -680,12 +682,12 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     GPTQ_LAUNCH_CHECK();
     gptq_status st;
     if (G == 0) {
-        st = launch_row_params(p.bits, p.sym != 0, Wws, d_row, d_col, scales, zeros, info, s);
+        st = launch_row_params(p.bits, p.sym != 0, p.sym == 2, Wws, d_row, d_col, scales, zeros, info, s);
         if (st != GPTQ_OK) return st;
     } else if (G < 0) {
         // E holds d_row x QSB bf16 values: room for 64 d_row partial ranges
         const int nb = (int)std::min<int64_t>(1024, 64 * d_row);
-        st = launch_tensor_params(p.bits, p.sym != 0, Wws, d_row, d_col, reinterpret_cast<float*>(Ehi), nb, scales,
+        st = launch_tensor_params(p.bits, p.sym != 0, p.sym == 2, Wws, d_row, d_col, reinterpret_cast<float*>(Ehi), nb, scales,
                                   zeros, info, s);
         if (st != GPTQ_OK) return st;
     }
@@ -704,9 +706,10 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
     sa.group = G < 0 ? 0 : G;   // per tensor: every row's parameters are set, as per row
     sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
+    sa.fp4 = p.sym == 2;
     sa.qmin = sa.sym ? -((1 << (p.bits - 1)) - 1) : 0;
-    sa.qmax = sa.sym ? ((1 << (p.bits - 1)) - 1) : (1 << p.bits) - 1;
-    sa.zoff = sa.sym ? (1 << (p.bits - 1)) : 0;
+    sa.qmax = sa.fp4 ? 6 : sa.sym ? ((1 << (p.bits - 1)) - 1) : (1 << p.bits) - 1;
+    sa.zoff = (sa.sym && !sa.fp4) ? (1 << (p.bits - 1)) : 0;
     for (int64_t s0 = 0; s0 < d_col; s0 += QSB) {
         const int64_t s1 = std::min<int64_t>(s0 + QSB, d_col);
         // the super-block's blocks, each followed by the update of the rest of the
@@ -728,7 +731,14 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
 // Fast path (8 consecutive columns per thread, one group): one 4-byte (two codes per
 // byte) or 8-byte load of codes, one scale / zero pair, 16-byte stores; it needs d_col
 // and the group size to be multiples of 8 and aligned rows.  Otherwise element by element.
-template <int BITS, gptq_dtype OT>
+// E2M1 magnitude of a code's low 3 bits, negated when bit 3 is set.
+GPTQ_DEV float e2m1_value(uint32_t u) {
+    const uint32_t m = u & 7u;
+    const float v = m < 4u ? 0.5f * (float)m : (m < 6u ? (float)(m - 2u) : 2.f * (float)(m - 4u));
+    return (u & 8u) ? -v : v;
+}
+
+template <int BITS, gptq_dtype OT, bool FP4 = false>
 __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
                                int64_t d_col, int G, void* out) {
     const int64_t row = blockIdx.y;
@@ -757,7 +767,7 @@ __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, con
             const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
             const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = sc * ((float)u[e] - z);
+            for (int e = 0; e < 8; ++e) v[e] = FP4 ? sc * e2m1_value(u[e]) : sc * ((float)u[e] - z);
             if constexpr (OT == GPTQ_F32) {
                 f32x4_t* o = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + row * d_col + c0);
                 o[0] = f32x4_t{v[0], v[1], v[2], v[3]};
@@ -788,7 +798,7 @@ __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, con
             const int g = (G == 0) ? 0 : (int)(c / G);
             const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
             const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
-            v[e] = sc * ((float)u - z);
+            v[e] = FP4 ? sc * e2m1_value(u) : sc * ((float)u - z);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -801,13 +811,13 @@ __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, con
     }
 }
 
-template <int BITS>
+template <int BITS, bool FP4 = false>
 static gptq_status dq_dt(gptq_dtype ot, dim3 grid, hipStream_t s, const uint8_t* codes, const uint16_t* scales,
                          const uint16_t* zeros, int64_t d_row, int64_t d_col, int G, void* out) {
     switch (ot) {
-        case GPTQ_F32: dequant_kernel<BITS, GPTQ_F32><<<grid, 256, 0, s>>>(codes, scales, zeros, d_row, d_col, G, out); break;
-        case GPTQ_BF16: dequant_kernel<BITS, GPTQ_BF16><<<grid, 256, 0, s>>>(codes, scales, zeros, d_row, d_col, G, out); break;
-        case GPTQ_F16: dequant_kernel<BITS, GPTQ_F16><<<grid, 256, 0, s>>>(codes, scales, zeros, d_row, d_col, G, out); break;
+        case GPTQ_F32: dequant_kernel<BITS, GPTQ_F32, FP4><<<grid, 256, 0, s>>>(codes, scales, zeros, d_row, d_col, G, out); break;
+        case GPTQ_BF16: dequant_kernel<BITS, GPTQ_BF16, FP4><<<grid, 256, 0, s>>>(codes, scales, zeros, d_row, d_col, G, out); break;
+        case GPTQ_F16: dequant_kernel<BITS, GPTQ_F16, FP4><<<grid, 256, 0, s>>>(codes, scales, zeros, d_row, d_col, G, out); break;
         default: return GPTQ_ERR_UNSUPPORTED;
     }
     GPTQ_LAUNCH_CHECK();
@@ -816,9 +826,10 @@ static gptq_status dq_dt(gptq_dtype ot, dim3 grid, hipStream_t s, const uint8_t*
 
 gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
                            int64_t d_col, int bits, int group_size, void* out, gptq_dtype out_dtype,
-                           hipStream_t s) {
+                           hipStream_t s, bool fp4) {
     const int64_t chunks = (d_col + 7) / 8;
     dim3 grid((unsigned)std::min<int64_t>((chunks + 255) / 256, 64), (unsigned)d_row);
+    if (fp4) return dq_dt<4, true>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     if (bits <= 4) return dq_dt<4>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     return dq_dt<8>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
 }

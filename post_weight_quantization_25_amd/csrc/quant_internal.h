@@ -10,13 +10,14 @@ GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 6
 // S16 and the stored zero of one range: [mn, mx] (asymmetric; a constant range is
 // widened to include 0) or its absolute maximum (symmetric); *info = -1 when the scale
 // is not a normal fp16 number.
-template <int BITS, bool SYM>
+// FP4: the E2M1 grid (largest magnitude 6), one scale, stored zero 0.
+template <int BITS, bool SYM, bool FP4 = false>
 GPTQ_DEV void range_params(float mn, float mx, int32_t* info, uint16_t& s_out, uint16_t& z_out) {
     constexpr int QMIN = SYM ? -((1 << (BITS - 1)) - 1) : 0;
-    constexpr int QMAX = SYM ? ((1 << (BITS - 1)) - 1) : (1 << BITS) - 1;
-    constexpr int ZOFF = SYM ? (1 << (BITS - 1)) : 0;
+    constexpr int QMAX = FP4 ? 6 : SYM ? ((1 << (BITS - 1)) - 1) : (1 << BITS) - 1;
+    constexpr int ZOFF = (SYM && !FP4) ? (1 << (BITS - 1)) : 0;
     float s, zf = 0.f;
-    if (SYM) {
+    if (SYM || FP4) {
         const float am = fmaxf(fabsf(mn), fabsf(mx));
         s = am > 0.f ? am / (float)QMAX : 1.f;
     } else {
@@ -25,7 +26,7 @@ GPTQ_DEV void range_params(float mn, float mx, int32_t* info, uint16_t& s_out, u
     }
     float s16f = f16_bits_to_f32(f32_to_f16_bits(s));
     if (!normal_f16_scale(s16f)) { *info = -1; s16f = 1.f; }
-    if (!SYM) zf = (float)QMIN - rintf(mn / s16f);
+    if (!SYM && !FP4) zf = (float)QMIN - rintf(mn / s16f);
     s_out = f32_to_f16_bits(s16f);
     z_out = f32_to_f16_bits(zf + (float)ZOFF);
 }
@@ -54,6 +55,7 @@ struct SweepArgs {
     int group;                      // 32, 64, 128 (power of two), or 0 = per-row params precomputed
     int qmin, qmax, zoff;           // grid and stored-code offset
     int sym; int packed;            // packed: two codes per byte
+    int fp4;                        // E2M1 grid (sign bit 8 | magnitude index), zero 0
 };
 
 gptq_status sweep_launch(const SweepArgs& a, hipStream_t s);

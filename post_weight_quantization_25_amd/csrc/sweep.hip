@@ -110,7 +110,7 @@ constexpr int NCH = (QSB - QB) / UT_N;
 // FULL: a whole super-block with every row, block and pointer aligned for 16-byte
 // accesses (checked on the host), so that every load and store takes its vector form
 // with no edge code around it.
-template <bool FULL>
+template <bool FULL, bool FP4>
 __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     // Up[j][q][i] = U[b0+j][b0+q+16i]
     __shared__ __attribute__((aligned(16))) float Up[QB][SL][SSLOTS];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                 // group scale/zero from the current values of columns j .. j+G-1
                 const int iend = (j + G) >> 4;
                 float sc, mn = 0.f;
-                if (a.sym) {
+                if (FP4 || a.sym) {
                     float am = 0.f;
 #pragma unroll
                     for (int i = ij; i < SSLOTS; ++i) if (i < iend) am = fmaxf(am, fabsf(w[i]));
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                 s16f = f16_bits_to_f32(f32_to_f16_bits(sc));
                 if (!normal_f16_scale(s16f)) { bad = true; s16f = 1.f; }
                 r16f = 1.0f / s16f;
-                zf = a.sym ? 0.f : fqmin - rintf(mn / s16f);
+                zf = (FP4 || a.sym) ? 0.f : fqmin - rintf(mn / s16f);
                 lo = fqmin - zf;
                 hi = fqmax - zf;
                 if (q == 0 && rv && b0 + j < a.d_col) {
@@ -289,12 +289,25 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         const float wv = w[ij];
         const float q0 = wv * r16f;
         const float t = fmaf(fmaf(-q0, s16f, wv), r16f, q0);
-        const float qd = __builtin_amdgcn_fmed3f(rintf(t), lo, hi);
+        float qd;
+        int code;
+        if constexpr (FP4) {
+            // nearest E2M1 value (ties to the even mantissa, 6 beyond): steps of 0.5
+            // below 2, of 1 below 4, of 2 above; code = sign bit 8 | magnitude index
+            const float m = fabsf(t);
+            const float v = m < 2.f ? 0.5f * rintf(2.f * m) : (m < 4.f ? rintf(m) : fminf(2.f * rintf(0.5f * m), 6.f));
+            qd = copysignf(v, t);
+            const int idx = v < 2.f ? (int)(2.f * v) : (v < 4.f ? (int)v + 2 : (int)(0.5f * v) + 4);
+            code = idx + ((t < 0.f && v > 0.f) ? 8 : 0);
+        } else {
+            qd = __builtin_amdgcn_fmed3f(rintf(t), lo, hi);
+            code = (int)(qd + zf) + a.zoff;
+        }
         const float err = fmaf(-s16f, qd, wv) * idc;
         const float errb = row_bcast<qj>(err);
         const bool own = (q == qj);
         e[ij] = own ? err : e[ij];
-        cv[ij] = own ? (int)(qd + zf) + a.zoff : cv[ij];
+        cv[ij] = own ? code : cv[ij];
         // keep both selects in this step (left alone, the compiler moves every step's
         // selects after the last step, holding 128 values live and putting that work on
         // the block's path)
@@ -410,8 +423,13 @@ gptq_status sweep_launch(const SweepArgs& a, hipStream_t s) {
     const bool full = a.s1 - a.s0 == QSB && (a.d_col & 15) == 0 && (a.lde & 7) == 0 && (a.code_ld & 7) == 0 &&
                       al16(a.Wws) && al16(a.U) && al16(a.Ehi) && al16(a.Elo) &&
                       al16(a.codes);
-    if (full) sweep_kernel<true><<<grid, QT, 0, s>>>(a);
-    else sweep_kernel<false><<<grid, QT, 0, s>>>(a);
+    if (a.fp4) {
+        if (full) sweep_kernel<true, true><<<grid, QT, 0, s>>>(a);
+        else sweep_kernel<false, true><<<grid, QT, 0, s>>>(a);
+    } else {
+        if (full) sweep_kernel<true, false><<<grid, QT, 0, s>>>(a);
+        else sweep_kernel<false, false><<<grid, QT, 0, s>>>(a);
+    }
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }

@@ -57,6 +57,7 @@ def lib():
         "gptq_obq_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                           vp, vp, vp, vp, sz, vp, vp]),
         "gptq_dequantize": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]),
+        "gptq_dequantize_e2m1": (ctypes.c_int, [vp, vp, i64, i64, i32, vp, ctypes.c_int, vp]),
         "gptq_quantized_linear": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64,
                                                  vp, ctypes.c_int, vp]),
         "gptq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -73,7 +74,7 @@ def test_header_declares_the_boundary():
         "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
         "gptq_quantize_workspace_size", "gptq_quantize_layer",
         "gptq_quantize_layers_workspace_size", "gptq_quantize_layers",
-        "gptq_obq_workspace_size", "gptq_obq_layer",
+        "gptq_obq_workspace_size", "gptq_obq_layer", "gptq_dequantize_e2m1",
         "gptq_dequantize", "gptq_quantized_linear", "gptq_status_string"])
 
 
@@ -239,3 +240,17 @@ def test_obq_workspace_and_errors(lib):
     assert call(p0, w=None) == INVALID_ARG
     assert call(p0, wsb=100) == WORKSPACE
     assert f(None, BF16, 0, 512, None, ctypes.byref(p0), None, None, None, None, 0, None, None) == OK
+
+
+def test_e2m1_argument_errors(lib):
+    """The E2M1 grid is 4-bit; its dequantization validates like gptq_dequantize."""
+    f = lib.gptq_quantize_layer
+    ws = ctypes.c_void_p(0x10000000)
+    q = lambda prm: f(FAKE, BF16, 16, 256, FAKE, ctypes.byref(prm), FAKE, FAKE, FAKE, ws, 1 << 40, FAKE, None)
+    assert q(lib.Params(3, 128, 2, 128)) == UNSUPPORTED
+    assert q(lib.Params(4, 128, 3, 128)) == INVALID_ARG
+    d = lib.gptq_dequantize_e2m1
+    assert d(FAKE, FAKE, 4, 255, 0, FAKE, F32, None) == INVALID_ARG        # odd width
+    assert d(FAKE, FAKE, 4, 256, 100, FAKE, F32, None) == INVALID_ARG      # group does not divide
+    assert d(None, FAKE, 4, 256, 128, FAKE, F32, None) == INVALID_ARG
+    assert d(None, None, 0, 256, 128, None, F32, None) == OK

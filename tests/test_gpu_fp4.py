@@ -1,0 +1,58 @@
+"""GPU parity of the FP4 E2M1 grid in the sweep (gptq_params.sym = 2) and of its
+dequantization (gptq_dequantize_e2m1) against the oracle.  As in the integer-grid
+test, the sweep gets the oracle's U rounded to fp32 and the oracle runs on the same
+values.  Codes are compared element by element (a code can differ only where the
+fp32 and fp64 paths land on opposite sides of a rounding midpoint, or where the fp16
+group scale, fp32 on the GPU and fp64 in the oracle, rounds differently)."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import log, unpack_codes
+from oracle import gptq_oracle as o
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(d_row, d_col, seed):
+    base = synth.config_layers(2)[0]
+    L = synth.scaled(base, d_row, d_col, max(4 * d_col, 512), seed_offset=seed)
+    L = dataclasses.replace(L, w_dtype="f32")
+    Wf = synth.w_as_f64(synth.weights(L))
+    X = np.concatenate([synth.x_as_f64(c) for c in synth.x_chunks(L)])
+    H = o.hessian([X])
+    U, _ = o.prepare_u(H, 0.01)
+    return Wf, H, np.ascontiguousarray(U, dtype=np.float32)
+
+
+@pytest.mark.parametrize("d_row,d_col,group", [(300, 512, 128), (200, 384, 0), (65, 256, -1), (130, 256, 32),
+                                               (33, 320, 64)])
+def test_fp4_quantize_parity(d_row, d_col, group):
+    import torch
+    import post_weight_quantization_25_amd as g
+    log(f"fp4 parity {d_row}x{d_col} g{group}")
+    Wf, H, U32 = _problem(d_row, d_col, 900 + d_col + group)
+    p = o.Params(bits=4, group_size=group, fp4=True)
+    ref = o.gptq_blocked(Wf, U32.astype(np.float64), p)
+    q = g.quantize_layer(torch.from_numpy(Wf.astype(np.float32)).cuda(), torch.from_numpy(U32).cuda(), bits=4,
+                         group_size=group, fp4=True)
+    What = g.dequantize(q)
+    torch.cuda.synchronize()
+    assert int(q.info.item()) == 0
+    codes = unpack_codes(q.codes.cpu().numpy(), 4)
+    s16 = q.scales.cpu().numpy()
+    match = float(np.mean(codes == ref.codes))
+    smatch = float(np.mean(s16 == ref.scales16))
+    log(f"  codes {match:.6f} scales {smatch:.6f}")
+    assert match >= 0.999 and smatch >= 0.999
+    assert not q.zeros.cpu().numpy().astype(np.float64).any()
+    # dequantization of the kernel's own codes, bit-exact
+    expect = o.dequantize_e2m1(codes, s16, group)
+    assert np.array_equal(What.cpu().numpy(), expect)
+    # layer objective close to the oracle's
+    e_g = np.einsum("ij,jk,ik->", Wf - expect, H, Wf - expect)
+    e_o = np.einsum("ij,jk,ik->", Wf - ref.what, H, Wf - ref.what)
+    log(f"  objective gpu {e_g:.6e} oracle {e_o:.6e}")
+    assert e_g <= 1.01 * e_o
