@@ -254,3 +254,18 @@ def test_e2m1_argument_errors(lib):
     assert d(FAKE, FAKE, 4, 256, 100, FAKE, F32, None) == INVALID_ARG      # group does not divide
     assert d(None, FAKE, 4, 256, 128, FAKE, F32, None) == INVALID_ARG
     assert d(None, None, 0, 256, 128, None, F32, None) == OK
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    """include/gptq.h is a C ABI: it must compile as strict C99 and as C++."""
+    import shutil
+    if shutil.which("gcc") is None or shutil.which("g++") is None:
+        pytest.skip("gcc/g++ not installed")
+    src = tmp_path / "use.c"
+    src.write_text('#include "gptq.h"\nint main(void) { gptq_layer l; gptq_params p; (void)l; (void)p; '
+                   'return GPTQ_LAYERS_MAX_SLOTS; }\n')
+    inc = os.path.dirname(HEADER)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{inc}", "-fsyntax-only",
+                    str(src)], check=True)
+    subprocess.run(["g++", "-std=c++11", "-Wall", "-Werror", f"-I{inc}", "-fsyntax-only", "-x", "c++", str(src)],
+                   check=True)
