@@ -103,6 +103,7 @@ class Params:
     block_size: int = 128
     percdamp: float = 0.01
     fp4: bool = False          # E2M1 grid with one fp16 scale per group (bits must be 4)
+    mx: bool = False           # with fp4: the scale is a power of two (MXFP4)
 
     @property
     def qmin(self) -> int:
@@ -170,6 +171,12 @@ def group_params(vals: np.ndarray, p: Params):
             return np.repeat(S, n), np.repeat(S16, n), np.repeat(Z, n), np.repeat(t, n)
         a = np.max(np.abs(vals), axis=1)
         S = np.where(a > 0, a / 6.0, 1.0)
+        if p.mx:
+            # MXFP4: the smallest power of two not below absmax / 6 (frexp: x = m 2^e,
+            # m in [0.5, 1); exactly 2^(e-1) when m = 0.5)  ["FP4 with block scales":
+            # MXFP4's scale is a power of two]
+            m, e = np.frexp(S)
+            S = np.ldexp(1.0, np.where(m == 0.5, e - 1, e)).astype(np.float64)
         S16 = _fp16_round(S)
         if not np.all(np.isfinite(S16)) or np.any(S16 < 2.0 ** -14):
             raise NonFinite("scale is not a normal fp16 number")

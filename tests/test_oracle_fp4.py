@@ -55,3 +55,29 @@ def test_e2m1_identity_hessian_and_blocking():
     a, b = o.gptq_blocked(W, U, p), o.gptq(W, U, p)
     assert np.array_equal(a.scales16, b.scales16)
     assert np.mean(a.codes == b.codes) >= 0.999
+
+
+def test_mxfp4_scale_is_the_power_of_two_above_absmax_over_6():
+    """MXFP4 ("FP4 with block scales": a power-of-two scale): S = 2^ceil(log2(absmax/6)),
+    so absmax / 6 <= S < absmax / 3 and the largest magnitude lands in (3, 6]."""
+    rng = np.random.default_rng(12)
+    W = rng.standard_normal((40, 128)) * 0.02
+    W[0, :] = 0.0
+    W[0, 5] = 0.75            # absmax / 6 = 0.125 exactly: S = 0.125, the value lands on 6
+    W[1, 7] = -0.6            # absmax / 6 = 0.1 -> S = 0.125, -0.6 / 0.125 = -4.8 -> -4
+    p = o.Params(bits=4, group_size=0, fp4=True, mx=True)
+    r = o.rtn(W, p)
+    S = r.scales16.astype(np.float64)[:, 0]
+    a = np.max(np.abs(W), axis=1)
+    assert np.all(np.exp2(np.round(np.log2(S))) == S)
+    assert np.all(a / 6 <= S) and np.all(S < a / 3)
+    assert S[0] == 0.125 and r.codes[0, 5] == 7
+    assert S[1] == 0.125 and r.codes[1, 7] == 8 + 6
+    a2 = o.gptq_blocked(W, np.eye(128), dataclasses_replace(p, group_size=32))
+    b2 = o.rtn(W, dataclasses_replace(p, group_size=32))
+    assert np.array_equal(a2.codes, b2.codes) and np.array_equal(a2.scales16, b2.scales16)
+
+
+def dataclasses_replace(p, **kw):
+    import dataclasses
+    return dataclasses.replace(p, **kw)
