@@ -78,8 +78,9 @@ typedef struct {
                          2: FP4 E2M1 grid (bits 4): values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6},
                             S = absmax / 6 per group, nearest value with ties to the even
                             mantissa, code = sign bit 8 | magnitude index, stored zero 0;
-                            dequantize with gptq_dequantize_e2m1.  Quantization concepts
-                            guide, "FP4 with block scales". */
+                            dequantize with gptq_dequantize_e2m1;
+                         3: as 2 with S rounded up to a power of two (MXFP4).
+                            Quantization concepts guide, "FP4 with block scales". */
     int32_t block_size;  /* lazy-update block width; this build supports 128 */
 } gptq_params;
 

@@ -170,9 +170,10 @@ class Quantized:
     fp4: bool = False        # codes on the E2M1 grid (sign bit 8 | magnitude index)
 
 
-def make_params(bits=4, group_size=128, sym=False, block_size=128, fp4=False) -> Params:
-    """sym: symmetric integer grid; fp4: the E2M1 grid (bits 4)."""
-    return Params(bits, group_size, 2 if fp4 else int(bool(sym)), block_size)
+def make_params(bits=4, group_size=128, sym=False, block_size=128, fp4=False, mx=False) -> Params:
+    """sym: symmetric integer grid; fp4: the E2M1 grid (bits 4); mx: with fp4, power-of-two
+    group scales (MXFP4)."""
+    return Params(bits, group_size, (3 if mx else 2) if fp4 else int(bool(sym)), block_size)
 
 
 def quantize_workspace_size(d_row: int, d_col: int, p: Params) -> int:
@@ -181,12 +182,12 @@ def quantize_workspace_size(d_row: int, d_col: int, p: Params) -> int:
 
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: int = 128, sym: bool = False,
                    block_size: int = 128, ws: torch.Tensor | None = None, out: Quantized | None = None,
-                   stream=None, fp4: bool = False) -> Quantized:
+                   stream=None, fp4: bool = False, mx: bool = False) -> Quantized:
     _dev(W, "W"); _dev(U, "U")
     if W.dtype not in _DT or U.dtype != torch.float32:
         raise ValueError("W must be f32/bf16/f16 and U float32")
     d_row, d_col = W.shape
-    p = make_params(bits, group_size, sym, block_size, fp4)
+    p = make_params(bits, group_size, sym, block_size, fp4, mx)
     n_groups = 1 if group_size <= 0 else max(1, d_col // group_size)
     if out is None:
         cb = d_col // 2 if bits <= 4 else d_col

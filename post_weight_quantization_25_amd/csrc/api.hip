@@ -12,8 +12,8 @@ static gptq_status check_params(const gptq_params* p, int64_t d_col) {
     if (p == nullptr) return GPTQ_ERR_INVALID_ARG;
     if (p->bits != 3 && p->bits != 4 && p->bits != 8) return GPTQ_ERR_UNSUPPORTED;
     if (p->block_size != 128) return GPTQ_ERR_UNSUPPORTED;
-    if (p->sym < 0 || p->sym > 2) return GPTQ_ERR_INVALID_ARG;
-    if (p->sym == 2 && p->bits != 4) return GPTQ_ERR_UNSUPPORTED;   // E2M1 is a 4-bit grid
+    if (p->sym < 0 || p->sym > 3) return GPTQ_ERR_INVALID_ARG;
+    if (p->sym >= 2 && p->bits != 4) return GPTQ_ERR_UNSUPPORTED;   // E2M1 is a 4-bit grid
     if (p->group_size < -1) return GPTQ_ERR_INVALID_ARG;   // -1: per tensor, 0: per row
     if (p->group_size > 0) {
         if (p->block_size % p->group_size != 0 || d_col % p->group_size != 0) return GPTQ_ERR_INVALID_ARG;

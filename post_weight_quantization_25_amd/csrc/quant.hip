@@ -28,7 +28,7 @@ namespace gptq {
 // One scale/zero per row (group_size 0): from the original row, before any update.
 template <int BITS, bool SYM, bool FP4>
 __global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64_t d_col, uint16_t* scales,
-                                                         uint16_t* zeros, int32_t* info) {
+                                                         uint16_t* zeros, int32_t* info, int pow2 = 0) {
     __shared__ float smn[256], smx[256];
     const int64_t row = blockIdx.x;
     const float* w = Wws + row * d_col;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void row_params_kernel(const float* Wws, int64
         __syncthreads();
     }
     if (threadIdx.x != 0) return;
-    range_params<BITS, SYM, FP4>(smn[0], smx[0], info, scales[row], zeros[row]);
+    range_params<BITS, SYM, FP4>(smn[0], smx[0], info, scales[row], zeros[row], pow2 != 0);
 }
 
 // Per-tensor granularity (one range for the whole matrix; Quantization concepts
@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256) void tensor_minmax_kernel(const float* Wws, in
 
 template <int BITS, bool SYM, bool FP4>
 __global__ __launch_bounds__(256) void tensor_params_kernel(const float* part, int nb, int64_t d_row,
-                                                            uint16_t* scales, uint16_t* zeros, int32_t* info) {
+                                                            uint16_t* scales, uint16_t* zeros, int32_t* info,
+                                                            int pow2 = 0) {
     __shared__ float smn[256], smx[256];
     __shared__ uint16_t sz[2];
     float mn = INFINITY, mx = -INFINITY;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void tensor_params_kernel(const float* part, i
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) range_params<BITS, SYM, FP4>(smn[0], smx[0], info, sz[0], sz[1]);
+    if (threadIdx.x == 0) range_params<BITS, SYM, FP4>(smn[0], smx[0], info, sz[0], sz[1], pow2 != 0);
     __syncthreads();
     for (int64_t r = threadIdx.x; r < d_row; r += 256) { scales[r] = sz[0]; zeros[r] = sz[1]; }
 }
@@ -617,11 +618,11 @@ __global__ void split_u_kernel(const float* U, int64_t n, uint16_t* hi, uint16_t
     }
 }
 
-static gptq_status launch_row_params(int bits, bool sym, bool fp4, const float* Wws, int64_t d_row, int64_t d_col,
+static gptq_status launch_row_params(int bits, bool sym, bool fp4, bool mx, const float* Wws, int64_t d_row, int64_t d_col,
                                      uint16_t* scales, uint16_t* zeros, int32_t* info, hipStream_t s) {
     dim3 grid((unsigned)d_row);
 #define RP(B, S) row_params_kernel<B, S, false><<<grid, 256, 0, s>>>(Wws, d_col, scales, zeros, info)
-    if (fp4) row_params_kernel<4, true, true><<<grid, 256, 0, s>>>(Wws, d_col, scales, zeros, info);
+    if (fp4) row_params_kernel<4, true, true><<<grid, 256, 0, s>>>(Wws, d_col, scales, zeros, info, mx ? 1 : 0);
     else if (bits == 4) { if (sym) RP(4, true); else RP(4, false); }
     else if (bits == 3) { if (sym) RP(3, true); else RP(3, false); }
     else if (bits == 8) { if (sym) RP(8, true); else RP(8, false); }
@@ -633,13 +634,13 @@ static gptq_status launch_row_params(int bits, bool sym, bool fp4, const float* 
 
 // Per-tensor: partial ranges of up to 1024 blocks (in the E area of the workspace, which
 // the sweep only uses later on the same stream), then one block for S16 and the zero.
-static gptq_status launch_tensor_params(int bits, bool sym, bool fp4, const float* Wws, int64_t d_row, int64_t d_col,
+static gptq_status launch_tensor_params(int bits, bool sym, bool fp4, bool mx, const float* Wws, int64_t d_row, int64_t d_col,
                                         float* part, int nb, uint16_t* scales, uint16_t* zeros, int32_t* info,
                                         hipStream_t s) {
     tensor_minmax_kernel<<<nb, 256, 0, s>>>(Wws, d_row * d_col, part);
     GPTQ_LAUNCH_CHECK();
 #define TP(B, S) tensor_params_kernel<B, S, false><<<1, 256, 0, s>>>(part, nb, d_row, scales, zeros, info)
-    if (fp4) tensor_params_kernel<4, true, true><<<1, 256, 0, s>>>(part, nb, d_row, scales, zeros, info);
+    if (fp4) tensor_params_kernel<4, true, true><<<1, 256, 0, s>>>(part, nb, d_row, scales, zeros, info, mx ? 1 : 0);
     else if (bits == 4) { if (sym) TP(4, true); else TP(4, false); }
     else if (bits == 3) { if (sym) TP(3, true); else TP(3, false); }
     else if (bits == 8) { if (sym) TP(8, true); else TP(8, false); }
@@ -682,12 +683,12 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     GPTQ_LAUNCH_CHECK();
     gptq_status st;
     if (G == 0) {
-        st = launch_row_params(p.bits, p.sym != 0, p.sym == 2, Wws, d_row, d_col, scales, zeros, info, s);
+        st = launch_row_params(p.bits, p.sym != 0, p.sym >= 2, p.sym == 3, Wws, d_row, d_col, scales, zeros, info, s);
         if (st != GPTQ_OK) return st;
     } else if (G < 0) {
         // E holds d_row x QSB bf16 values: room for 64 d_row partial ranges
         const int nb = (int)std::min<int64_t>(1024, 64 * d_row);
-        st = launch_tensor_params(p.bits, p.sym != 0, p.sym == 2, Wws, d_row, d_col, reinterpret_cast<float*>(Ehi), nb, scales,
+        st = launch_tensor_params(p.bits, p.sym != 0, p.sym >= 2, p.sym == 3, Wws, d_row, d_col, reinterpret_cast<float*>(Ehi), nb, scales,
                                   zeros, info, s);
         if (st != GPTQ_OK) return st;
     }
@@ -706,7 +707,8 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
     sa.group = G < 0 ? 0 : G;   // per tensor: every row's parameters are set, as per row
     sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
-    sa.fp4 = p.sym == 2;
+    sa.fp4 = p.sym >= 2;
+    sa.mx = p.sym == 3;
     sa.qmin = sa.sym ? -((1 << (p.bits - 1)) - 1) : 0;
     sa.qmax = sa.fp4 ? 6 : sa.sym ? ((1 << (p.bits - 1)) - 1) : (1 << p.bits) - 1;
     sa.zoff = (sa.sym && !sa.fp4) ? (1 << (p.bits - 1)) : 0;

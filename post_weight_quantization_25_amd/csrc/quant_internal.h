@@ -10,9 +10,17 @@ GPTQ_DEV bool normal_f16_scale(float s) { return s >= 6.103515625e-05f && s <= 6
 // S16 and the stored zero of one range: [mn, mx] (asymmetric; a constant range is
 // widened to include 0) or its absolute maximum (symmetric); *info = -1 when the scale
 // is not a normal fp16 number.
-// FP4: the E2M1 grid (largest magnitude 6), one scale, stored zero 0.
+// The smallest power of two not below x > 0 (exact: from the exponent of x).
+GPTQ_DEV float pow2_ceil(float x) {
+    int e;
+    const float m = frexpf(x, &e);   // x = m 2^e, m in [0.5, 1)
+    return ldexpf(1.f, m == 0.5f ? e - 1 : e);
+}
+
+// FP4: the E2M1 grid (largest magnitude 6), one scale, stored zero 0; pow2: the scale
+// rounded up to a power of two (MXFP4).
 template <int BITS, bool SYM, bool FP4 = false>
-GPTQ_DEV void range_params(float mn, float mx, int32_t* info, uint16_t& s_out, uint16_t& z_out) {
+GPTQ_DEV void range_params(float mn, float mx, int32_t* info, uint16_t& s_out, uint16_t& z_out, bool pow2 = false) {
     constexpr int QMIN = SYM ? -((1 << (BITS - 1)) - 1) : 0;
     constexpr int QMAX = FP4 ? 6 : SYM ? ((1 << (BITS - 1)) - 1) : (1 << BITS) - 1;
     constexpr int ZOFF = (SYM && !FP4) ? (1 << (BITS - 1)) : 0;
@@ -24,6 +32,7 @@ GPTQ_DEV void range_params(float mn, float mx, int32_t* info, uint16_t& s_out, u
         if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
         s = (mx > mn) ? (mx - mn) / (float)(QMAX - QMIN) : 1.f;
     }
+    if (FP4 && pow2) s = pow2_ceil(s);
     float s16f = f16_bits_to_f32(f32_to_f16_bits(s));
     if (!normal_f16_scale(s16f)) { *info = -1; s16f = 1.f; }
     if (!SYM && !FP4) zf = (float)QMIN - rintf(mn / s16f);
@@ -56,6 +65,7 @@ struct SweepArgs {
     int qmin, qmax, zoff;           // grid and stored-code offset
     int sym; int packed;            // packed: two codes per byte
     int fp4;                        // E2M1 grid (sign bit 8 | magnitude index), zero 0
+    int mx;                         // with fp4: power-of-two group scales (MXFP4)
 };
 
 gptq_status sweep_launch(const SweepArgs& a, hipStream_t s);

@@ -258,6 +258,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                     for (int i = ij; i < SSLOTS; ++i) if (i < iend) am = fmaxf(am, fabsf(w[i]));
                     am = row_max(am);
                     sc = am > 0.f ? am / fqmax : 1.f;
+                    if (FP4 && a.mx) sc = pow2_ceil(sc);
                 } else {
                     float mx = w[ij];
                     mn = w[ij];

@@ -248,7 +248,8 @@ def test_e2m1_argument_errors(lib):
     ws = ctypes.c_void_p(0x10000000)
     q = lambda prm: f(FAKE, BF16, 16, 256, FAKE, ctypes.byref(prm), FAKE, FAKE, FAKE, ws, 1 << 40, FAKE, None)
     assert q(lib.Params(3, 128, 2, 128)) == UNSUPPORTED
-    assert q(lib.Params(4, 128, 3, 128)) == INVALID_ARG
+    assert q(lib.Params(4, 128, 4, 128)) == INVALID_ARG      # grids are 0 .. 3
+    assert q(lib.Params(8, 128, 3, 128)) == UNSUPPORTED      # MXFP4 is 4-bit too
     d = lib.gptq_dequantize_e2m1
     assert d(FAKE, FAKE, 4, 255, 0, FAKE, F32, None) == INVALID_ARG        # odd width
     assert d(FAKE, FAKE, 4, 256, 100, FAKE, F32, None) == INVALID_ARG      # group does not divide

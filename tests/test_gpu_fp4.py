@@ -27,17 +27,18 @@ def _problem(d_row, d_col, seed):
     return Wf, H, np.ascontiguousarray(U, dtype=np.float32)
 
 
-@pytest.mark.parametrize("d_row,d_col,group", [(300, 512, 128), (200, 384, 0), (65, 256, -1), (130, 256, 32),
-                                               (33, 320, 64)])
-def test_fp4_quantize_parity(d_row, d_col, group):
+@pytest.mark.parametrize("d_row,d_col,group,mx", [(300, 512, 128, False), (200, 384, 0, False), (65, 256, -1, False),
+                                                  (130, 256, 32, False), (33, 320, 64, False),
+                                                  (130, 256, 32, True), (200, 384, 0, True)])
+def test_fp4_quantize_parity(d_row, d_col, group, mx):
     import torch
     import post_weight_quantization_25_amd as g
-    log(f"fp4 parity {d_row}x{d_col} g{group}")
+    log(f"fp4 parity {d_row}x{d_col} g{group} mx={mx}")
     Wf, H, U32 = _problem(d_row, d_col, 900 + d_col + group)
-    p = o.Params(bits=4, group_size=group, fp4=True)
+    p = o.Params(bits=4, group_size=group, fp4=True, mx=mx)
     ref = o.gptq_blocked(Wf, U32.astype(np.float64), p)
     q = g.quantize_layer(torch.from_numpy(Wf.astype(np.float32)).cuda(), torch.from_numpy(U32).cuda(), bits=4,
-                         group_size=group, fp4=True)
+                         group_size=group, fp4=True, mx=mx)
     What = g.dequantize(q)
     torch.cuda.synchronize()
     assert int(q.info.item()) == 0
@@ -48,6 +49,9 @@ def test_fp4_quantize_parity(d_row, d_col, group):
     log(f"  codes {match:.6f} scales {smatch:.6f}")
     assert match >= 0.999 and smatch >= 0.999
     assert not q.zeros.cpu().numpy().astype(np.float64).any()
+    if mx:   # MXFP4: every scale a power of two
+        sf = s16.astype(np.float64)
+        assert np.all(np.exp2(np.round(np.log2(sf))) == sf)
     # dequantization of the kernel's own codes, bit-exact
     expect = o.dequantize_e2m1(codes, s16, group)
     assert np.array_equal(What.cpu().numpy(), expect)
