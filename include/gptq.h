@@ -234,7 +234,7 @@ gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, flo
  * with GPTQ.
  *
  *  W, U, p, codes, scales_f16, zeros_f16, info   as for gptq_quantize_layer; p must have
- *             group_size 0 (else GPTQ_ERR_UNSUPPORTED).
+ *             group_size 0 and an integer grid, sym 0 or 1 (else GPTQ_ERR_UNSUPPORTED).
  *  ws         at least gptq_obq_workspace_size(d_row, d_col) bytes: H^-1 and one
  *             d_col x d_col copy per row in flight (at most 256).
  * Errors as gptq_quantize_layer; d_col > 2048 -> GPTQ_ERR_UNSUPPORTED.  Arithmetic is

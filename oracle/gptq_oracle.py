@@ -35,9 +35,10 @@ listing were lost in extraction; the readings used here are:
 * asymmetric grid [0, 2^b - 1] with S = (max - min) / (2^b - 1),
   Z = -round(min / S16); symmetric grid +-(2^(b-1) - 1) with S = absmax / (2^(b-1) - 1),
   Z = 0; S16 = fp16(S) is the scale used for quantizing and stored;
-* a code is decided from the float32 quotient: q = clamp(rne(fl32(fl32(w) / S16)) + Z),
-  as the GPU does, so both sides round the same value; adding the integer Z is
-  exact (rne(t + Z) = rne(t) + Z); everything else is fp64;
+* a code is decided as the guide writes it, q = clamp(rne(w / S16 + Z)), with the
+  quotient and the sum in fp64 (round half to even; the pages name no precision,
+  so the decision is taken as close to exact arithmetic as fp64 allows); the
+  zero point likewise, Z = qmin - rne(min / S16) in fp64;
 * stored codes are unsigned: u = q (asymmetric) or q + 2^(b-1) (symmetric), stored
   zero z = Z or 2^(b-1); dequantisation is fl32(S16) * fl32(u - z).
 """
@@ -138,10 +139,6 @@ def e2m1_round(t: np.ndarray) -> np.ndarray:
     return np.where(tie & (i % 2 == 1), nxt, i)
 
 
-def _f32(x):
-    return np.asarray(x, dtype=np.float64).astype(np.float32)
-
-
 def _fp16_round(S: np.ndarray) -> np.ndarray:
     """Round the (fp64) scale to fp16 (nearest even); returned as fp64 values."""
     with np.errstate(over="ignore"):
@@ -153,8 +150,8 @@ def group_params(vals: np.ndarray, p: Params):
 
     ``vals`` is (rows, g): the current values of the group's columns.
     Returns (S, S16, Z, zt): pre-rounding scale (fp64), fp16-rounded scale (as fp64),
-    the integer zero point on the signed/unsigned grid, and the float32 value
-    fl32(min) / S16 whose rounding gave Z (0 for the symmetric grid).
+    the integer zero point on the signed/unsigned grid, and the fp64 value
+    min / S16 whose rounding gave Z (0 for the symmetric grid).
 
     [Quantization concepts guide, "Mapping values to fewer bits" (asymmetric:
      literal min/max; symmetric: [-a, a], Z = 0) and "Choose granularity"
@@ -171,6 +168,7 @@ def group_params(vals: np.ndarray, p: Params):
             return np.repeat(S, n), np.repeat(S16, n), np.repeat(Z, n), np.repeat(t, n)
         a = np.max(np.abs(vals), axis=1)
         S = np.where(a > 0, a / 6.0, 1.0)
+        S_pre = S   # returned as the pre-rounding scale
         if p.mx:
             # MXFP4: the smallest power of two not below absmax / 6 (frexp: x = m 2^e,
             # m in [0.5, 1); exactly 2^(e-1) when m = 0.5)  ["FP4 with block scales":
@@ -180,7 +178,7 @@ def group_params(vals: np.ndarray, p: Params):
         S16 = _fp16_round(S)
         if not np.all(np.isfinite(S16)) or np.any(S16 < 2.0 ** -14):
             raise NonFinite("scale is not a normal fp16 number")
-        return S, S16 / 2.0, np.zeros(vals.shape[0], dtype=np.int64), np.zeros(vals.shape[0], dtype=np.float32)
+        return S_pre, S16 / 2.0, np.zeros(vals.shape[0], dtype=np.int64), np.zeros(vals.shape[0])
     if p.group_size < 0:
         # Per-tensor: one range over the values of every row, the same S and Z for all
         # rows.  Callers pass the whole matrix before any column is quantized.
@@ -194,7 +192,7 @@ def group_params(vals: np.ndarray, p: Params):
         S = np.where(a > 0, a / qmax, 1.0)
         S16 = _fp16_round(S)
         Z = np.zeros(vals.shape[0], dtype=np.int64)
-        t = np.zeros(vals.shape[0], dtype=np.float32)
+        t = np.zeros(vals.shape[0])
     else:
         mn = np.min(vals, axis=1)
         mx = np.max(vals, axis=1)
@@ -206,8 +204,8 @@ def group_params(vals: np.ndarray, p: Params):
         mx = np.where(flat, np.maximum(mx, 0.0), mx)
         S = np.where(mx > mn, (mx - mn) / (qmax - qmin), 1.0)
         S16 = _fp16_round(S)
-        # Z = qmin - round(min / S16), decided in float32 (same precision as the GPU)
-        t = (_f32(mn) / _f32(S16)).astype(np.float32)
+        # Z = qmin - round(min / S16)  ["Mapping values to fewer bits": zero point]
+        t = mn / S16
         Z = (qmin - np.rint(t)).astype(np.int64)
     if not np.all(np.isfinite(S16)) or np.any(S16 < 2.0 ** -14):
         raise NonFinite("scale is not a normal fp16 number")
@@ -215,24 +213,22 @@ def group_params(vals: np.ndarray, p: Params):
 
 
 def decide_codes(w: np.ndarray, S16: np.ndarray, Z: np.ndarray, p: Params) -> np.ndarray:
-    """q = clamp(round(w / S16 + Z)) on the signed (or unsigned) grid.
+    """q = clamp(round(w / S16 + Z)) on the signed (or unsigned) grid, round half to
+    even, the quotient and the sum in fp64.
 
-    The quotient t = fl32(w / S16) is decided in float32; Z is an integer, so the
-    sum t + Z and its rounding are exact: round(t + Z) = round(t) + Z.
     [Quantization concepts guide, "Mapping values to fewer bits": quantize formula;
      the clamp keeps compensated values that left the group's range on the grid]
     """
     if p.fp4:
         # E2M1: S16 here is the half-unit step; the quotient is by the stored scale 2 step
-        t = (_f32(w) / _f32(2.0 * np.asarray(S16))).astype(np.float32).astype(np.float64)
+        t = np.asarray(w, dtype=np.float64) / (2.0 * np.asarray(S16, dtype=np.float64))
         return (np.sign(t) * 2.0 * E2M1_VALUES[e2m1_round(t)]).astype(np.int64)
-    t = (_f32(w) / _f32(S16)).astype(np.float32)
-    return np.clip(np.rint(t.astype(np.float64)) + Z, p.qmin, p.qmax).astype(np.int64)
+    return np.clip(np.rint(code_value(w, S16, Z)), p.qmin, p.qmax).astype(np.int64)
 
 
 def code_value(w: np.ndarray, S16: np.ndarray, Z: np.ndarray) -> np.ndarray:
-    """The pre-rounding code value fl32(w / S16) + Z (the sum exact, in fp64)."""
-    return (_f32(w) / _f32(S16)).astype(np.float32).astype(np.float64) + Z
+    """The pre-rounding code value w / S16 + Z in fp64 (what ``decide_codes`` rounds)."""
+    return np.asarray(w, dtype=np.float64) / np.asarray(S16, dtype=np.float64) + np.asarray(Z, dtype=np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -323,10 +319,10 @@ class Result:
     S: np.ndarray          # pre-rounding scales, d_row x n_groups (fp64)
     scales16: np.ndarray   # fp16 scales, d_row x n_groups (np.float16)
     zeros: np.ndarray      # stored zero points z, d_row x n_groups (int64)
-    z_t: np.ndarray        # fl32(min) / S16, the value rounded to get Z (float32), d_row x n_groups
+    z_t: np.ndarray        # min / S16, the value rounded to get Z (fp64), d_row x n_groups
     what: np.ndarray       # dequantized weights S16 * (q - Z), fp64
     w_at_q: np.ndarray     # the value each weight had when it was quantized (fp64)
-    t_at_q: np.ndarray     # fl32(fl32(w) / S16) + Z, the pre-rounding code value (exact sum, fp64)
+    t_at_q: np.ndarray     # w / S16 + Z, the pre-rounding code value (fp64)
 
 
 def _n_groups(d_col: int, p: Params) -> int:
@@ -368,7 +364,7 @@ def gptq(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
-    ZT = np.zeros((d_row, ng), dtype=np.float32)
+    ZT = np.zeros((d_row, ng))
     what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for c in range(d_col):
         k = c // g
@@ -385,7 +381,21 @@ def gptq(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     return _finish(Q, S, S16, Z, ZT, what, w_at_q, t_at_q, p)
 
 
-def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
+def _forced_index(forced):
+    """{("q", r, c): q} and {("g", r, k): (S16, Z)} -> per column / per group lists."""
+    by_col, by_grp = {}, {}
+    for key, val in (forced or {}).items():
+        kind, r, i = key
+        if kind == "q":
+            by_col.setdefault(i, []).append((r, val))
+        elif kind == "g":
+            by_grp.setdefault(i, []).append((r, val))
+        else:
+            raise ValueError(key)
+    return by_col, by_grp
+
+
+def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params, forced: dict | None = None) -> Result:
     """GPTQ with lazy batched updates in blocks of B columns.
 
     Inside a block the updates stay local to the block; the error block E
@@ -396,7 +406,15 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     Needs the group to lie inside one block (block_size % group_size == 0) or one
     group per row; otherwise a group's first column would see values that lack
     this block's pending updates.
+
+    ``forced`` optionally fixes decisions that another computation took on the other
+    side of a rounding tie (both sides of a tie follow the rule): ("q", r, c) -> q sets
+    row r's code at column c (signed grid, or half-units for E2M1), and
+    ("g", r, k) -> (S16, Z) sets row r's scale and zero point of group k.  Everything
+    else, including the compensation that follows a fixed decision, is computed as
+    without it.
     """
+    f_col, f_grp = _forced_index(forced)
     W = np.array(W, dtype=np.float64, copy=True)
     d_row, d_col = W.shape
     g = p.group(d_col)
@@ -406,7 +424,7 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
-    ZT = np.zeros((d_row, ng), dtype=np.float32)
+    ZT = np.zeros((d_row, ng))
     what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for b0 in range(0, d_col, B):
         b1 = min(b0 + B, d_col)
@@ -418,10 +436,14 @@ def gptq_blocked(W: np.ndarray, U: np.ndarray, p: Params) -> Result:
             if c % g == 0:
                 src = Wb[:, j:j + g] if g <= B else W[:, c:c + g]
                 S[:, k], S16[:, k], Z[:, k], ZT[:, k] = group_params(src, p)
+                for r, (s16, z) in f_grp.get(k, ()):
+                    S16[r, k], Z[r, k] = s16, z
             w = Wb[:, j].copy()
             w_at_q[:, c] = w
             t_at_q[:, c] = code_value(w, S16[:, k], Z[:, k])
             q = decide_codes(w, S16[:, k], Z[:, k], p)
+            for r, qf in f_col.get(c, ()):
+                q[r] = qf
             Q[:, c] = q
             what[:, c] = S16[:, k] * (q - Z[:, k])
             err = (w - what[:, c]) / U[c, c]
@@ -448,7 +470,7 @@ def gptq_obs(W: np.ndarray, Hd: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
-    ZT = np.zeros((d_row, ng), dtype=np.float32)
+    ZT = np.zeros((d_row, ng))
     what = np.zeros_like(W); w_at_q = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for c in range(d_col):
         k = c // g
@@ -530,7 +552,7 @@ def rtn(W: np.ndarray, p: Params) -> Result:
     ng = _n_groups(d_col, p)
     Q = np.zeros((d_row, d_col), dtype=np.int64)
     S = np.zeros((d_row, ng)); S16 = np.zeros((d_row, ng)); Z = np.zeros((d_row, ng), dtype=np.int64)
-    ZT = np.zeros((d_row, ng), dtype=np.float32)
+    ZT = np.zeros((d_row, ng))
     what = np.zeros_like(W); t_at_q = np.zeros((d_row, d_col), dtype=np.float64)
     for k in range(ng):
         c0, c1 = k * g, min((k + 1) * g, d_col)

@@ -303,6 +303,8 @@ def linear(q: Quantized, x: torch.Tensor, out_dtype=torch.float32, out: torch.Te
            stream=None) -> torch.Tensor:
     """y = x What^T on the stored format (What as ``dequantize`` defines it), fp32 accumulation.
     x may be a row-strided view (its row pitch is passed as ldx)."""
+    if q.fp4:
+        raise ValueError("linear reads integer-grid codes; a layer on the E2M1 grid is dequantized with dequantize")
     if not x.is_cuda:
         raise ValueError("x must be a device tensor")
     if x.dtype not in _DT or x.dim() != 2 or x.shape[1] != q.d_col or (x.shape[0] > 0 and x.stride(1) != 1):

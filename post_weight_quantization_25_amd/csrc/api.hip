@@ -119,6 +119,7 @@ gptq_status gptq_obq_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int
     gptq_status st = check_params(p, d_col);
     if (st != GPTQ_OK) return st;
     if (p->group_size != 0) return GPTQ_ERR_UNSUPPORTED;   // one group per row
+    if (p->sym >= 2) return GPTQ_ERR_UNSUPPORTED;          // integer grids only (no E2M1)
     if (d_row == 0 || d_col == 0) return GPTQ_OK;
     if (!W || !U || !codes || !scales_f16 || !zeros_f16 || !info) return GPTQ_ERR_INVALID_ARG;
     if (d_col > OBQ_MAXD || d_row > 2147483647LL / 64) return GPTQ_ERR_UNSUPPORTED;

@@ -236,6 +236,8 @@ def test_obq_workspace_and_errors(lib):
     call = lambda prm, d_col=512, w=FAKE, wsb=1 << 40: f(w, BF16, 16, d_col, FAKE, ctypes.byref(prm), FAKE, FAKE,
                                                           FAKE, FAKE, wsb, FAKE, None)
     assert call(pg) == UNSUPPORTED          # grouped grids: OBQ here uses one group per row
+    assert call(lib.Params(4, 0, 2, 128)) == UNSUPPORTED    # the E2M1 grid: OBQ takes integer grids only
+    assert call(lib.Params(4, 0, 3, 128)) == UNSUPPORTED    # MXFP4 likewise
     assert call(p0, d_col=4096) == UNSUPPORTED
     assert call(p0, w=None) == INVALID_ARG
     assert call(p0, wsb=100) == WORKSPACE

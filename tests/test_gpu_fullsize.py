@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import check_recon, log, parity_report, unpack_codes
+from gpu_helpers import assert_parity, check_recon, log, tie_consistent_parity, unpack_codes
 from oracle import gptq_oracle as o
 
 pytestmark = pytest.mark.gpu
@@ -90,15 +90,15 @@ def test_fullsize_quant_rows(c2):
     rng = np.random.default_rng(7)
     rows = np.array(sorted(set([0, 1, 4095]) | set(rng.choice(W.shape[0], 93, replace=False).tolist())))
     Wf = synth.w_as_f64(W[rows])
-    ref = o.gptq_blocked(Wf, U.astype(np.float64), o.Params(bits=4, group_size=128))
+    p = o.Params(bits=4, group_size=128)
+    U64 = U.astype(np.float64)
+    ref = o.gptq_blocked(Wf, U64, p)
     codes, s16, z = c2["codes"][rows], c2["s16"][rows], c2["z"][rows].astype(np.int64)
-    rep = parity_report(codes, s16, z, ref, 128, tie_window=1e-3)
-    log(f"  {rows.size} rows: codes {rep['code_match']:.6f} groups {rep['group_match']:.6f} "
-        f"rows w/ events {rep['rows_with_events']} unjustified {rep['unjustified'][:2]}")
-    assert rep["code_match"] >= 0.999
-    assert not rep["unjustified"]
+    rep = tie_consistent_parity(codes, s16, z, Wf, U64, p, tie_window=1e-3, ref=ref)
+    log(f"  {rows.size} sampled rows:")
+    assert_parity(rep, log)
     # dequantized rows: fp32(S16) * (u - z), bit for bit
     g = np.repeat(np.arange(W.shape[1] // 128), 128)
     deq = s16.astype(np.float32)[:, g] * (codes.astype(np.float32) - z.astype(np.float32)[:, g])
     assert np.array_equal(c2["What"][rows], deq)
-    check_recon(H.astype(np.float64), Wf, c2["What"][rows], ref.what, rep["event_rows"], log)
+    check_recon(H.astype(np.float64), Wf, c2["What"][rows], rep, log)

@@ -5,12 +5,12 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import dev_tensor, layer_x, log, parity_report, unpack_codes
+from gpu_helpers import assert_parity, dev_tensor, layer_x, log, tie_consistent_parity, unpack_codes
 from oracle import gptq_oracle as o
 
 pytestmark = pytest.mark.gpu
 
-CHAIN_TIE = 0.02   # as in the end-to-end chain test: the GPU Hessian is accumulated in fp32
+CHAIN_TIE = 1e-3   # as in the end-to-end chain test
 
 
 def _mini_block():
@@ -68,8 +68,7 @@ def test_layers_match_per_phase_calls(bits, group, sym):
     for (LX, LW), q in zip(spec[:3], outs):
         Wf = synth.w_as_f64(synth.weights(LW))
         r = o.gptq_blocked(Wf, Uo, p)
-        rep = parity_report(unpack_codes(q.codes.cpu().numpy(), bits), q.scales.cpu().numpy(),
-                            q.zeros.cpu().numpy().astype(np.int64), r, group, tie_window=CHAIN_TIE)
-        log(f"  {LW.name}: codes {rep['code_match']:.6f} unjustified {len(rep['unjustified'])}")
-        assert rep["code_match"] >= 0.999
-        assert not rep["unjustified"]
+        rep = tie_consistent_parity(unpack_codes(q.codes.cpu().numpy(), bits), q.scales.cpu().numpy(),
+                                    q.zeros.cpu().numpy().astype(np.int64), Wf, Uo, p, tie_window=CHAIN_TIE, ref=r)
+        log(f"  {LW.name}:")
+        assert_parity(rep, log)

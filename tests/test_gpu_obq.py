@@ -3,14 +3,14 @@ Hessian) against the oracle's OBQ.  The GPU decides the order in fp32 and the or
 fp64, so where two candidates' added errors are nearly equal the two may take different
 (equally valid) paths: rows whose oracle path has no near-tie (best and second-best
 added error apart by more than 1e-3 relative at every step) must match code for code;
-the others must hold valid codes with the same grid and a layer objective close to the
+the others must hold valid codes on the same grid with a row objective within 5% of the
 oracle's.  With a diagonal H every order gives round-to-nearest, which pins the
 bookkeeping (grid, codes, packing) on every row."""
 import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import dev_tensor, log, unpack_codes
+from gpu_helpers import _fp16_boundary_rel, dev_tensor, log, tie_distance, unpack_codes
 from oracle import gptq_oracle as o
 
 pytestmark = pytest.mark.gpu
@@ -55,9 +55,15 @@ def test_obq_parity(d_row, d_col, bits, sym):
     codes = unpack_codes(q.codes.cpu().numpy(), bits)
     s16 = q.scales.cpu().numpy().astype(np.float64)
     z = q.zeros.cpu().numpy().astype(np.int64)
-    assert np.allclose(s16, ref.scales16.astype(np.float64), rtol=1e-3, atol=0)
-    same_grid = (z == ref.zeros).all(axis=1)
-    assert same_grid.mean() >= 0.95
+    # the same grid on every row: scale and zero equal, unless the oracle's own value sits
+    # on a rounding tie (scale within 1e-5 of an fp16 boundary, min / S16 within 1e-3 of
+    # a half-integer)
+    s_eq = s16[:, 0] == ref.scales16.astype(np.float64)[:, 0]
+    z_eq = z[:, 0] == ref.zeros[:, 0]
+    s_tie = _fp16_boundary_rel(ref.S[:, 0]) < 1e-5
+    z_tie = tie_distance(ref.z_t[:, 0], o.Params(bits=8)) < 1e-3
+    assert np.all(s_eq | s_tie) and np.all(z_eq | (s_eq & z_tie))
+    same_grid = s_eq & z_eq
     gaps = _min_gap(W, Hd, p)
     clean = (gaps > 1e-3) & same_grid
     exact = np.all(codes == ref.codes, axis=1)
@@ -71,7 +77,7 @@ def test_obq_parity(d_row, d_col, bits, sym):
     for r in range(d_row):
         e_g = (W[r] - what[r]) @ Hd @ (W[r] - what[r])
         e_o = (W[r] - ref.what[r]) @ Hd @ (W[r] - ref.what[r])
-        assert e_g <= 1.25 * e_o + 1e-12, (r, e_g, e_o)
+        assert e_g <= 1.05 * e_o + 1e-12, (r, e_g, e_o)
 
 
 def test_obq_diagonal_hessian_is_round_to_nearest():

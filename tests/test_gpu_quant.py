@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import check_recon, dev_tensor, log, parity_report, unpack_codes
+from gpu_helpers import assert_parity, check_recon, dev_tensor, log, tie_consistent_parity, unpack_codes
 from oracle import gptq_oracle as o
 
 pytestmark = pytest.mark.gpu
@@ -67,21 +67,18 @@ def test_quantize_parity(d_row, d_col, bits, group, sym, wdt):
     z = q.zeros.cpu().numpy().astype(np.int64)
     if group < 0:   # per tensor: every row holds the same scale and zero
         assert np.all(s16 == s16[0, 0]) and np.all(z == z[0, 0])
-    rep = parity_report(codes, s16, z, ref, max(group, 0), tie_window=1e-3)
-    log(f"  codes {rep['code_match']:.6f} groups {rep['group_match']:.6f} rows with events "
-        f"{rep['rows_with_events']} unjustified {rep['unjustified'][:3]}")
-    assert rep["code_match"] >= 0.999
-    assert not rep["unjustified"]
-    # packing: rows without any event must be byte-identical to the oracle's packing
-    clean = np.all(codes == ref.codes, axis=1)
-    assert np.array_equal(q.codes.cpu().numpy()[clean], o.pack(ref.codes, bits)[clean])
+    U64 = U32.astype(np.float64)
+    rep = tie_consistent_parity(codes, s16, z, Wf, U64, p, tie_window=1e-3, ref=ref)
+    assert_parity(rep, log)
+    # packing: byte-identical to the oracle's packing of the (tie-consistent) codes
+    assert np.array_equal(q.codes.cpu().numpy(), o.pack(rep["codes"].astype(np.uint8), bits))
     # dequantization of the kernel's own codes: S16 (u - z) exactly, in fp32
     gi = np.arange(d_col) // (d_col if group <= 0 else group)
     expect = s16.astype(np.float32)[:, gi] * (codes.astype(np.float32) - z.astype(np.float32)[:, gi])
     wh = What.cpu().numpy()
     assert np.array_equal(wh, expect)
     # layer objective
-    check_recon(H, Wf, wh, ref.what, rep["event_rows"], log)
+    check_recon(H, Wf, wh, rep, log)
 
 
 # 8-column vector path (width and group multiples of 8) and the element-wise path

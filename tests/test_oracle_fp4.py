@@ -73,6 +73,8 @@ def test_mxfp4_scale_is_the_power_of_two_above_absmax_over_6():
     assert np.all(a / 6 <= S) and np.all(S < a / 3)
     assert S[0] == 0.125 and r.codes[0, 5] == 7
     assert S[1] == 0.125 and r.codes[1, 7] == 8 + 6
+    # the pre-rounding scale is absmax / 6, before the power of two
+    assert r.S[0, 0] == 0.125 and r.S[1, 0] == 0.6 / 6
     a2 = o.gptq_blocked(W, np.eye(128), dataclasses_replace(p, group_size=32))
     b2 = o.rtn(W, dataclasses_replace(p, group_size=32))
     assert np.array_equal(a2.codes, b2.codes) and np.array_equal(a2.scales16, b2.scales16)

@@ -249,3 +249,48 @@ def test_gptq_beats_rtn_on_first_workload():
     r = o.recon_error_h(H, W, o.rtn(W, p).what)
     # channels are nearly uncorrelated here, so the gain over RTN is modest (about 8%)
     assert g < 0.97 * r
+
+
+def test_forced_decisions_keep_the_compensation_exact():
+    """A decision fixed from outside (another computation's side of a rounding tie) is
+    followed by the same compensation: at every column the value being quantized is
+    still the exact minimizer of the damped objective given the (fixed) earlier weights
+    (direct solve, no Cholesky); the fixed codes and group parameters are the ones used;
+    every decision not fixed is still round(w / S16 + Z) of its own value."""
+    p = o.Params(bits=4, group_size=8, block_size=16)
+    W, X, H, U = _layer(21, 9, 48, n=200, p=p)
+    Hd, _ = o.damp(H, p.percdamp)
+    plain = o.gptq_blocked(W, U, p)
+    # fixing the oracle's own decisions changes nothing
+    same = {("q", r, c): int(plain.q[r, c]) for r, c in [(0, 3), (4, 20), (8, 47)]}
+    same[("g", 2, 1)] = (float(plain.scales16[2, 1]), int(plain.zeros[2, 1]))
+    r0 = o.gptq_blocked(W, U, p, forced=same)
+    assert np.array_equal(r0.codes, plain.codes) and np.array_equal(r0.what, plain.what)
+    # the other side: codes one step off, and one group's scale and zero replaced
+    forced = {}
+    for r, c in [(0, 3), (1, 17), (4, 20), (8, 47), (5, 8)]:
+        qf = int(plain.q[r, c]) + (1 if plain.q[r, c] < p.qmax else -1)
+        forced[("q", r, c)] = qf
+    g_s16, g_z = float(np.float16(plain.scales16[3, 2]) * np.float16(1.0009765625)), int(plain.zeros[3, 2]) + 1
+    forced[("g", 3, 2)] = (g_s16, g_z)
+    r = o.gptq_blocked(W, U, p, forced=forced)
+    for (kind, row, i), v in forced.items():
+        if kind == "q":
+            assert r.q[row, i] == v
+        else:
+            assert (float(r.scales16[row, i]), int(r.zeros[row, i])) == v
+    for c in range(1, 48):
+        Q, F = slice(0, c), slice(c, 48)
+        dQ = W[:, Q] - r.what[:, Q]
+        wF = W[:, F] + np.linalg.solve(Hd[F, F], (dQ @ Hd[Q, F]).T).T
+        assert np.allclose(r.w_at_q[:, c], wF[:, 0], rtol=1e-9, atol=1e-13)
+    gi = np.arange(48) // 8
+    s16 = r.scales16.astype(np.float64)[:, gi]
+    z = r.zeros[:, gi]
+    free = np.ones((W.shape[0], 48), dtype=bool)
+    for kind, row, i in forced:
+        if kind == "q":
+            free[row, i] = False
+    own = np.clip(np.rint(r.w_at_q / s16 + z), p.qmin, p.qmax)
+    assert np.array_equal(own[free], r.q[free])
+    assert not np.array_equal(r.codes, plain.codes)

@@ -119,3 +119,62 @@ def test_group_params_symmetric_int3():
     assert abs(S[0] - 0.3) < 1e-15 and Z[0] == 0
     q = o.decide_codes(vals[0], np.repeat(S16, 4), np.repeat(Z, 4), p)
     assert list(q) == [1, -3, 2, 0]
+
+
+# Hand-computed decisions q = clamp(round(w / S16 + Z)) with round half to even, from the
+# quotient and sum in exact arithmetic (Quantization concepts guide, "Mapping values to
+# fewer bits": quantize formula).  S16 = 0.25 is exact in fp16, so every expected value
+# below is worked out by hand.  Near-midpoint cases sit 2^-30 off a tie: closer than half
+# a float32 step of w (2^-26 at 0.375), so a float32 quotient would land on the tie itself.
+NEAR_MIDPOINTS = [
+    # w,                  Z, code value w/S16 + Z,      q
+    (0.375,               0, 1.5,                      2),    # exact tie -> even
+    (0.625,               0, 2.5,                      2),    # exact tie -> even
+    (0.375,               3, 4.5,                      4),    # the tie is decided after adding Z (not rne(1.5) + 3 = 5)
+    (0.375 - 2.0 ** -30,  0, 1.5 - 2.0 ** -28,         1),    # just below the tie
+    (0.375 + 2.0 ** -30,  0, 1.5 + 2.0 ** -28,         2),    # just above the tie
+    (0.625 + 2.0 ** -30,  0, 2.5 + 2.0 ** -28,         3),    # just above an even-down tie
+    (-0.125,              5, 4.5,                      4),
+    (-0.125 - 2.0 ** -30, 5, 4.5 - 2.0 ** -28,         4),
+    (-0.125 + 2.0 ** -30, 5, 4.5 + 2.0 ** -28,         5),
+    (4.0,                 3, 19.0,                     15),   # clamped to qmax
+    (-2.0,                2, -6.0,                     0),    # clamped to qmin
+]
+
+
+def test_code_value_and_decide_codes_near_midpoints():
+    p = o.Params(bits=4, group_size=0, sym=False)
+    w = np.array([c[0] for c in NEAR_MIDPOINTS])
+    Z = np.array([c[1] for c in NEAR_MIDPOINTS], dtype=np.int64)
+    S16 = np.full(w.size, 0.25)
+    t = o.code_value(w, S16, Z)
+    assert np.array_equal(t, np.array([c[2] for c in NEAR_MIDPOINTS]))
+    assert list(o.decide_codes(w, S16, Z, p)) == [c[3] for c in NEAR_MIDPOINTS]
+    # the reading is the exact quotient: a float32 quotient would put the case just
+    # below the tie on the tie itself (and round it up to 2)
+    assert np.float32(NEAR_MIDPOINTS[3][0]) / np.float32(0.25) == np.float32(1.5)
+
+
+def test_decide_codes_symmetric_near_midpoints():
+    """Symmetric grid (Z = 0, codes in +-3 for int3): -1.5 and 2.5 are ties (-> -2, 2);
+    2^-30 off them the exact quotient decides."""
+    p = o.Params(bits=3, group_size=0, sym=True)
+    w = np.array([-0.375, -0.375 + 2.0 ** -30, 0.625, 0.625 - 2.0 ** -30, 1.0])
+    q = o.decide_codes(w, np.full(5, 0.25), np.zeros(5, dtype=np.int64), p)
+    assert list(q) == [-2, -1, 2, 2, 3]
+
+
+def test_zero_point_decided_from_the_exact_quotient():
+    """Z = qmin - round(min / S16): for a group with range 3.75 at int4 (S = S16 = 0.25)
+    and min = -0.625 - 2^-30, min / S16 = -2.5 - 2^-28 rounds to -3, so Z = 3 (a float32
+    quotient, -2.5, would round to -2 and give Z = 2)."""
+    p = o.Params(bits=4, group_size=0, sym=False)
+    mn = -0.625 - 2.0 ** -30
+    vals = np.array([[mn, 0.1, mn + 3.75]])
+    S, S16, Z, zt = o.group_params(vals, p)
+    assert S[0] == 0.25 and S16[0] == 0.25
+    assert zt[0] == -2.5 - 2.0 ** -28
+    assert Z[0] == 3
+    # exactly on the tie, -2.5 goes to the even -2: Z = 2
+    S, S16, Z, zt = o.group_params(np.array([[-0.625, 0.0, 3.125]]), p)
+    assert zt[0] == -2.5 and Z[0] == 2
