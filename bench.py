@@ -234,13 +234,14 @@ def layer_bench(g, L, dev, steps: int, warmup: int, damp: float = 0.01):
                     torch.empty((r, ng), dtype=torch.float16, device=dev),
                     torch.zeros(1, dtype=torch.int32, device=dev), L.bits, L.group_size, d)
     What = torch.empty((r, d), dtype=torch.bfloat16, device=dev)
+    ctx = g.Context(1)
 
     def step(ev=None):
         if ev: ev[0].record()
         H.zero_()
         g.hessian_accumulate(H, X, ws=ws_h)
         if ev: ev[1].record()
-        g.prepare_hinv(H, damp, U=U, ws=ws_p, info=info)
+        g.prepare_hinv(H, damp, U=U, ws=ws_p, info=info, ctx=ctx)
         if ev: ev[2].record()
         g.quantize_layer(W, U, L.bits, L.group_size, L.sym, ws=ws_q, out=q)
         if ev: ev[3].record()
@@ -277,18 +278,19 @@ def block_bench(g, layers, dev, steps: int, warmup: int, shared: bool):
         data = [(data[src[L.name]][0] if L.name in src else X, W) for L, (X, W) in zip(layers, data)]
     L0 = layers[0]
     out = {}
+    ctx = g.Context(3)
     for slots in (1, 2, 3):
         ws = torch.empty(g.quantize_layers_workspace_size(data, slots), dtype=torch.uint8, device=dev)
-        res, info = g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws)
+        res, info = g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws, ctx=ctx)
         for _ in range(max(0, warmup - 1)):
-            g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws, outs=res, info=info)
+            g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws, outs=res, info=info, ctx=ctx)
         torch.cuda.synchronize()
         if info.cpu().any():
             raise RuntimeError(f"gptq_quantize_layers: status {info.cpu().tolist()}")
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for k in range(steps):
             ev[k][0].record()
-            g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws, outs=res, info=info)
+            g.quantize_layers(data, L0.bits, L0.group_size, L0.sym, 0.01, slots, ws=ws, outs=res, info=info, ctx=ctx)
             ev[k][1].record()
         torch.cuda.synchronize()
         out[str(slots)] = float(sum(e[0].elapsed_time(e[1]) for e in ev) / steps)
@@ -429,6 +431,7 @@ def main():
                     torch.empty((r, d // 128), dtype=torch.float16, device=dev),
                     torch.zeros(1, dtype=torch.int32, device=dev), 4, 128, d)
     What = torch.empty((r, d), dtype=torch.bfloat16, device=dev)
+    ctx = g.Context(1)
     torch.cuda.synchronize()
 
     phases = ["hess", "prep", "quant", "deq"]
@@ -438,7 +441,7 @@ def main():
         H.zero_()
         g.hessian_accumulate(H, X, ws=ws_h)
         if ev: ev[1].record()
-        g.prepare_hinv(H, 0.01, U=U, ws=ws_p, info=info)
+        g.prepare_hinv(H, 0.01, U=U, ws=ws_p, info=info, ctx=ctx)
         if ev: ev[2].record()
         g.quantize_layer(W, U, 4, 128, ws=ws_q, out=q)
         if ev: ev[3].record()

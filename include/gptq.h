@@ -18,10 +18,10 @@
  * Conventions shared by every entry point
  *  - Every pointer argument named as a matrix or buffer is a DEVICE pointer
  *    unless its comment says "host".  The caller owns every buffer; the library
- *    never allocates or frees memory.  It keeps no state between calls, except
- *    that gptq_prepare_hinv creates, at its first call on a device (the current
- *    device), one auxiliary HIP stream of default priority and two events, and
- *    keeps them until the process ends (see gptq_prepare_hinv).
+ *    never allocates or frees device memory.  It keeps no state between calls:
+ *    the extra HIP streams and events with which gptq_prepare_hinv and
+ *    gptq_quantize_layers overlap their own phases live in a gptq_context that the
+ *    caller creates, passes and destroys (NULL: everything runs on `stream`).
  *  - Matrices are row-major.  All work is enqueued asynchronously on `stream`
  *    (a hipStream_t; NULL = the default stream); no call synchronizes.
  *  - Argument errors (null pointers, bad sizes, unsupported settings, a
@@ -34,7 +34,7 @@
  *    normal fp16 number, -2 = a bounded wait between workgroups expired (see
  *    gptq_prepare_hinv).  The call itself still returns GPTQ_OK.
  *  - Calls on one stream are ordered; concurrent calls on different streams
- *    must not share output or workspace buffers.
+ *    must not share output or workspace buffers, nor a gptq_context.
  */
 #ifndef GPTQ_MI355X_H
 #define GPTQ_MI355X_H
@@ -61,6 +61,29 @@ typedef enum {
     GPTQ_BF16 = 1,
     GPTQ_F16 = 2
 } gptq_dtype;
+
+/*
+ * Execution context (host object owned by the caller): HIP streams and events, all at
+ * the default priority, with which one call overlaps its own phases -- an auxiliary
+ * stream for the factorization's triangular inverse, and for gptq_quantize_layers a
+ * Hessian stream plus n_slots slot streams, each with its own auxiliary stream.
+ * gptq_context_create makes them on the current device; gptq_context_destroy waits for
+ * the work already queued on them and releases them (with that device made current for
+ * the call).  A context serves one call at a time: calls that share one must not
+ * overlap on the host.  Different contexts are independent, so calls from several host
+ * threads, each with its own context and stream, run concurrently.
+ *
+ *  n_slots   1 .. GPTQ_LAYERS_MAX_SLOTS: the most slots a gptq_quantize_layers call with
+ *            this context may use.
+ *  ctx       host pointer that receives the context.
+ * Errors: n_slots out of range or ctx NULL -> GPTQ_ERR_INVALID_ARG (nothing is made);
+ * a failing HIP call -> GPTQ_ERR_HIP (what was made is released).  Destroying NULL is a
+ * no-op.
+ */
+#define GPTQ_LAYERS_MAX_SLOTS 4
+typedef struct gptq_context gptq_context;
+gptq_status gptq_context_create(int32_t n_slots, gptq_context** ctx);
+gptq_status gptq_context_destroy(gptq_context* ctx);
 
 /* Quantizer settings (host struct). */
 typedef struct {
@@ -120,11 +143,13 @@ gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype,
  *  H        d_col x d_col fp32 (only the upper triangle is read).
  *  U        d_col x d_col fp32 output; the strictly lower triangle is written as 0.
  *  ws       at least gptq_prepare_hinv_workspace_size(d_col) bytes.
- * Part of the work (the inverse of the leading block) runs on the library's
- * auxiliary stream of the current device, ordered after the earlier work of
- * `stream` and joined back into `stream` by events, so `stream` sees the call as
- * one ordered operation (also under stream capture).  `stream` must belong to the
- * current device.
+ *  ctx      NULL: every kernel runs on `stream`.  Otherwise a context made on the
+ *           current device: the inverse of the leading row blocks then runs on its
+ *           auxiliary stream beside the factorization's chain, ordered after the
+ *           earlier work of `stream` and joined back into `stream` by its events, so
+ *           `stream` sees the call as one ordered operation (also under stream
+ *           capture).  The result is bit-identical either way.
+ * `stream` must belong to the current device.
  *
  *  info     device int32: 0, or k > 0 when the trailing principal submatrix of
  *           H + lambda I of order k is not positive definite (U is then undefined),
@@ -135,7 +160,7 @@ gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype,
  */
 size_t gptq_prepare_hinv_workspace_size(int64_t d_col);
 gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float percdamp,
-                              void* ws, size_t ws_bytes, int32_t* info, void* stream);
+                              void* ws, size_t ws_bytes, int32_t* info, gptq_context* ctx, void* stream);
 
 /*
  * Quantize W column by column in natural order with error compensation through U.
@@ -187,15 +212,18 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row
  * inputs) and "Innovation 3" (the factorization is computed once per H).
  *
  * Schedule: groups start widest first (ties in the given order; no layer's result
- * depends on the order); their Hessians run one after another on one library stream;
- * the k-th started group's factorization and sweeps run on slot stream k mod n_slots,
- * so the next group's Hessian overlaps the running factorizations and sweeps, and
- * the factorizations of up to n_slots groups overlap each other.  The call is ordered
- * after the work already queued on `stream`, and later work on `stream` after it.
+ * depends on the order).  With a context, their Hessians run one after another on the
+ * context's Hessian stream and the k-th started group's factorization and sweeps on
+ * slot stream k mod n_slots, so the next group's Hessian overlaps the running
+ * factorizations and sweeps, and the factorizations of up to n_slots groups overlap
+ * each other; the call is ordered after the work already queued on `stream`, and later
+ * work on `stream` after it.  With ctx NULL every group runs on `stream`, one after
+ * another.
  *
  *  layers     host array of n_layers descriptors (device pointers inside); the
  *             quantizer settings p apply to every layer (group size dividing each d_col).
- *  n_slots    1 .. GPTQ_LAYERS_MAX_SLOTS: groups in flight at once (memory grows with it).
+ *  n_slots    1 .. GPTQ_LAYERS_MAX_SLOTS, and at most the context's: groups in flight at
+ *             once (memory grows with it; without a context 1 is enough).
  *  ws         at least gptq_quantize_layers_workspace_size(layers, n_layers, n_slots)
  *             bytes, 256-byte aligned: n_slots x (H, U, factorization and sweep
  *             workspaces of the largest layer) + one Hessian workspace.
@@ -205,11 +233,8 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row
  *             gptq_quantize_layer).
  * Errors (checked for every layer before anything is queued): as the per-phase calls;
  * n_tokens < 1, d_row < 1 or d_col < 1 -> GPTQ_ERR_INVALID_ARG; n_slots out of range
- * -> GPTQ_ERR_INVALID_ARG.  n_layers = 0 is a no-op.  Calls that overlap in time (from
- * several host threads) are queued one after the other; their device work may
- * interleave only through different workspaces.
+ * (or above the context's) -> GPTQ_ERR_INVALID_ARG.  n_layers = 0 is a no-op.
  */
-#define GPTQ_LAYERS_MAX_SLOTS 4
 typedef struct gptq_layer {
     const void* X; gptq_dtype x_dtype; int64_t n_tokens; int64_t ldx;   /* n_tokens x d_col inputs */
     const void* W; gptq_dtype w_dtype; int64_t d_row; int64_t d_col;    /* d_row x d_col weights */
@@ -218,7 +243,7 @@ typedef struct gptq_layer {
 size_t gptq_quantize_layers_workspace_size(const gptq_layer* layers, int32_t n_layers, int32_t n_slots);  /* reads shapes only */
 gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, float percdamp,
                                  const gptq_params* p, int32_t n_slots, void* ws, size_t ws_bytes,
-                                 int32_t* info, void* stream);
+                                 int32_t* info, gptq_context* ctx, void* stream);
 
 /*
  * OBQ, the method GPTQ is compared with: every row on its own, its weights quantized

@@ -54,13 +54,15 @@ def _load():
         "gptq_hessian_workspace_size": (sz, [i64, i64]),
         "gptq_hessian_accumulate": (ctypes.c_int, [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp]),
         "gptq_prepare_hinv_workspace_size": (sz, [i64]),
-        "gptq_prepare_hinv": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp, sz, vp, vp]),
+        "gptq_context_create": (ctypes.c_int, [i32, ctypes.POINTER(vp)]),
+        "gptq_context_destroy": (ctypes.c_int, [vp]),
+        "gptq_prepare_hinv": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp, sz, vp, vp, vp]),
         "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
         "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
         "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
-                                                ctypes.POINTER(Params), i32, vp, sz, vp, vp]),
+                                                ctypes.POINTER(Params), i32, vp, sz, vp, vp, vp]),
         "gptq_obq_workspace_size": (sz, [i64, i64]),
         "gptq_obq_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                           vp, vp, vp, vp, sz, vp, vp]),
@@ -109,6 +111,50 @@ def _workspace(nbytes: int, device, ws):
     return ws
 
 
+# ---------------------------------------------------------------- context
+
+class Context:
+    """A gptq_context: HIP streams and events, owned by this object, with which
+    ``prepare_hinv`` and ``quantize_layers`` overlap their own phases.  Made on the
+    current device (or ``device``); ``close()`` (or garbage collection) waits for the
+    work queued on them and releases them.  One context serves one call at a time."""
+
+    def __init__(self, n_slots: int = LAYERS_MAX_SLOTS, device=None):
+        self.device = torch.cuda.current_device() if device is None else torch.device(device).index
+        self.n_slots = n_slots
+        ptr = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib.gptq_context_create(n_slots, ctypes.byref(ptr)), "gptq_context_create")
+        self._ptr = ptr.value
+
+    @property
+    def ptr(self):
+        if not self._ptr:
+            raise ValueError("context is closed")
+        return self._ptr
+
+    def close(self):
+        if self._ptr:
+            p, self._ptr = self._ptr, None
+            _check(lib.gptq_context_destroy(p), "gptq_context_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ctx_ptr(ctx):
+    return None if ctx is None else ctx.ptr
+
+
 # ---------------------------------------------------------------- Hessian
 
 def hessian_workspace_size(n_tokens: int, d_col: int) -> int:
@@ -140,8 +186,11 @@ def prepare_hinv_workspace_size(d_col: int) -> int:
 
 
 def prepare_hinv(H: torch.Tensor, percdamp: float = 0.01, U: torch.Tensor | None = None,
-                 ws: torch.Tensor | None = None, info: torch.Tensor | None = None, stream=None):
-    """Upper Cholesky factor U of (H + percdamp*mean(diag H) I)^-1.  Returns (U, info)."""
+                 ws: torch.Tensor | None = None, info: torch.Tensor | None = None, stream=None,
+                 ctx: Context | None = None):
+    """Upper Cholesky factor U of (H + percdamp*mean(diag H) I)^-1.  Returns (U, info).
+    With a Context the triangular inverse overlaps the factorization on its auxiliary
+    stream; without one every kernel runs on ``stream`` (the same U either way)."""
     _dev(H, "H")
     d = H.shape[0]
     if U is None:
@@ -151,7 +200,8 @@ def prepare_hinv(H: torch.Tensor, percdamp: float = 0.01, U: torch.Tensor | None
     ws = _workspace(prepare_hinv_workspace_size(d), H.device, ws)
     _check(lib.gptq_prepare_hinv(H.data_ptr(), U.data_ptr(), d, float(percdamp),
                                  ws.data_ptr() if ws is not None else None,
-                                 ws.numel() if ws is not None else 0, info.data_ptr(), _stream(stream)),
+                                 ws.numel() if ws is not None else 0, info.data_ptr(), _ctx_ptr(ctx),
+                                 _stream(stream)),
            "gptq_prepare_hinv")
     return U, info
 
@@ -249,11 +299,13 @@ def quantize_layers_workspace_size(pairs, n_slots: int = 2) -> int:
 
 def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = False, percdamp: float = 0.01,
                     n_slots: int = 2, ws: torch.Tensor | None = None, outs: list | None = None,
-                    info: torch.Tensor | None = None, stream=None):
+                    info: torch.Tensor | None = None, stream=None, ctx: Context | None = None):
     """Quantize several layers in one call (gptq_quantize_layers): ``pairs`` is a list of
     (X, W) device tensors, X tokens x d_col (rows may be strided), W d_row x d_col.
-    Consecutive pairs with the same X tensor share one H and one U.  Returns (outs, info):
-    one Quantized per layer and the device int32[2 n] status array."""
+    Consecutive pairs with the same X tensor share one H and one U.  With a Context the
+    groups' phases overlap on its streams (``n_slots`` groups in flight); without one
+    they run on ``stream`` one after another.  Returns (outs, info): one Quantized per
+    layer and the device int32[2 n] status array."""
     if not pairs:
         return [], info
     for X, W in pairs:
@@ -280,7 +332,7 @@ def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = Fal
     descs = _layer_descs(pairs, outs)
     _check(lib.gptq_quantize_layers(descs, len(pairs), percdamp, ctypes.byref(p), n_slots,
                                     ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
-                                    info.data_ptr(), _stream(stream)),
+                                    info.data_ptr(), _ctx_ptr(ctx), _stream(stream)),
            "gptq_quantize_layers")
     return outs, info
 

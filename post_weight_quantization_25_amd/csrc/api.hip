@@ -46,13 +46,31 @@ size_t gptq_prepare_hinv_workspace_size(int64_t d_col) {
     return prep_ws_bytes(d_col);
 }
 
+gptq_status gptq_context_create(int32_t n_slots, gptq_context** ctx) {
+    if (ctx == nullptr || n_slots < 1 || n_slots > GPTQ_LAYERS_MAX_SLOTS) return GPTQ_ERR_INVALID_ARG;
+    return context_create(n_slots, ctx);
+}
+
+gptq_status gptq_context_destroy(gptq_context* ctx) { return context_destroy(ctx); }
+
+// A context serves the device it was made on.
+static gptq_status check_context(const gptq_context* ctx) {
+    if (ctx == nullptr) return GPTQ_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GPTQ_ERR_HIP;
+    return dev == ctx->device ? GPTQ_OK : GPTQ_ERR_INVALID_ARG;
+}
+
 gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float percdamp, void* ws, size_t ws_bytes,
-                              int32_t* info, void* stream) {
+                              int32_t* info, gptq_context* ctx, void* stream) {
     if (d_col < 0 || !(percdamp >= 0.f)) return GPTQ_ERR_INVALID_ARG;
     if (d_col == 0) return GPTQ_OK;
     if (H == nullptr || U == nullptr || info == nullptr) return GPTQ_ERR_INVALID_ARG;
     if (d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
-    return prep_launch(H, U, d_col, percdamp, ws, ws_bytes, info, (hipStream_t)stream);
+    if (ws == nullptr || ws_bytes < prep_ws_bytes(d_col)) return GPTQ_ERR_WORKSPACE;
+    const gptq_status st = check_context(ctx);
+    if (st != GPTQ_OK) return st;
+    return prep_launch(H, U, d_col, percdamp, ws, ws_bytes, info, (hipStream_t)stream, ctx ? &ctx->prep : nullptr);
 }
 
 size_t gptq_quantize_workspace_size(int64_t d_row, int64_t d_col, const gptq_params* p) {
@@ -98,13 +116,16 @@ size_t gptq_quantize_layers_workspace_size(const gptq_layer* layers, int32_t n_l
 }
 
 gptq_status gptq_quantize_layers(const gptq_layer* layers, int32_t n_layers, float percdamp, const gptq_params* p,
-                                 int32_t n_slots, void* ws, size_t ws_bytes, int32_t* info, void* stream) {
+                                 int32_t n_slots, void* ws, size_t ws_bytes, int32_t* info, gptq_context* ctx,
+                                 void* stream) {
     if (p == nullptr || !(percdamp >= 0.f)) return GPTQ_ERR_INVALID_ARG;
     gptq_status st = check_layers(layers, n_layers, p, n_slots);
     if (st != GPTQ_OK) return st;
+    if (ctx && n_slots > ctx->n_slots) return GPTQ_ERR_INVALID_ARG;
     if (n_layers == 0) return GPTQ_OK;
     if (info == nullptr) return GPTQ_ERR_INVALID_ARG;
-    return layers_launch(layers, n_layers, percdamp, *p, n_slots, ws, ws_bytes, info, (hipStream_t)stream);
+    if ((st = check_context(ctx)) != GPTQ_OK) return st;
+    return layers_launch(layers, n_layers, percdamp, *p, n_slots, ws, ws_bytes, info, ctx, (hipStream_t)stream);
 }
 
 size_t gptq_obq_workspace_size(int64_t d_row, int64_t d_col) {

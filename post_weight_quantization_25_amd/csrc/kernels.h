@@ -18,10 +18,10 @@ gptq_status hessian_launch(float* H, const void* X, gptq_dtype dt, int64_t n, in
 struct PrepAux { hipStream_t s = nullptr; hipEvent_t fork = nullptr, join = nullptr; };
 
 size_t prep_ws_bytes(int64_t d_col);
-// own_aux: the caller's auxiliary stream and events, used by this call alone (the caller
-// serializes calls that share them); nullptr: the device's own, under a lock.
+// aux: an auxiliary stream and its events, used by this call alone (from a caller-owned
+// context); nullptr: every kernel on `stream`.
 gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, void* ws, size_t ws_bytes,
-                        int32_t* info, hipStream_t stream, PrepAux* own_aux = nullptr);
+                        int32_t* info, hipStream_t stream, const PrepAux* aux);
 
 void zero_f32(float* p, int64_t n, hipStream_t s);
 
@@ -32,7 +32,9 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
 
 size_t layers_ws_bytes(const gptq_layer* layers, int n, int n_slots);
 gptq_status layers_launch(const gptq_layer* layers, int n, float percdamp, const gptq_params& p, int n_slots,
-                          void* ws, size_t ws_bytes, int32_t* info, hipStream_t stream);
+                          void* ws, size_t ws_bytes, int32_t* info, gptq_context* ctx, hipStream_t stream);
+gptq_status context_create(int n_slots, gptq_context** out);
+gptq_status context_destroy(gptq_context* ctx);
 
 constexpr int OBQ_MAXD = 2048;   // widest row the OBQ kernel keeps in LDS
 size_t obq_ws_bytes(int64_t d_row, int64_t d_col);
@@ -49,3 +51,19 @@ gptq_status linear_launch(const uint8_t* codes, const uint16_t* scales, const ui
                           int64_t ldx, void* y, gptq_dtype y_dtype, hipStream_t stream);
 
 }  // namespace gptq
+
+// The caller-owned execution context (opaque in the C header): the streams and events
+// that let one call overlap its own phases.  Made by gptq_context_create on one device,
+// freed by gptq_context_destroy; the library keeps no other state between calls.
+struct gptq_context {
+    int device = -1;
+    int n_slots = 0;
+    gptq::PrepAux prep;                          // gptq_prepare_hinv's auxiliary stream
+    hipStream_t hs = nullptr;                    // gptq_quantize_layers: the Hessians
+    hipEvent_t start = nullptr, hs_done = nullptr;
+    struct Slot {
+        hipStream_t s = nullptr;                 // factorization and sweeps of a group
+        gptq::PrepAux aux;                       // that factorization's auxiliary stream
+        hipEvent_t hdone = nullptr, free = nullptr;
+    } slot[GPTQ_LAYERS_MAX_SLOTS];
+};

@@ -18,7 +18,6 @@
 // because an operand is triangular.
 
 #include <algorithm>
-#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -921,27 +920,6 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 #define AUX_MAX_WG 384
 #endif
 
-// One auxiliary stream and two events per device, created on first use and kept
-// until the process ends; enqueueing is serialized so that concurrent calls do not
-// interleave their fork / join records.
-typedef PrepAux AuxStream;
-static std::mutex aux_mu;
-static AuxStream aux_dev[64];
-
-static gptq_status aux_stream(AuxStream*& out) {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GPTQ_ERR_HIP;
-    AuxStream& a = aux_dev[dev];
-    if (a.s == nullptr) {
-        if (hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) != hipSuccess) { a.s = nullptr; return GPTQ_ERR_HIP; }
-        if (hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess)
-            return GPTQ_ERR_HIP;
-    }
-    out = &a;
-    return GPTQ_OK;
-}
-
 // Right-looking blocked Cholesky of A (lower, reversed damped H) with the inverse of
 // every 64 x 64 diagonal block of L, then X = L^-1.
 // Block 0 and its panel have launches of their own; every later diagonal block and
@@ -972,7 +950,7 @@ static gptq_status aux_stream(AuxStream*& out) {
 #ifndef INV_LAST
 #define INV_LAST 1024
 #endif
-static gptq_status cholinv(PrepCtx& c, AuxStream* own_aux) {
+static gptq_status cholinv(PrepCtx& c, const PrepAux* aux) {
     const int64_t d = c.d;
     gptq_status st;
     prep_diag_kernel<<<1, 256, 0, c.s>>>(c.A, c.X, d, 0, (int)std::min<int64_t>(PNB, d), c.info);
@@ -1001,10 +979,11 @@ static gptq_status cholinv(PrepCtx& c, AuxStream* own_aux) {
     double* Smain = Trest + (d - h) * sl;
     auto trow = [&](int64_t r) { return Trest + (r - h) * sl; };
 
-    AuxStream* aux = own_aux;
-    if (aux == nullptr && (st = aux_stream(aux)) != GPTQ_OK) return st;
+    // Without an auxiliary stream the same work is queued on the caller's stream at the
+    // same points (stream order then gives every dependency) with an uncapped grid.
     PrepCtx ca = c;
-    ca.s = aux->s;
+    if (aux) ca.s = aux->s;
+    const int aux_wg = aux ? AUX_MAX_WG : 0;
     // block i's columns are final once the step that forms the panel of its last 64
     // columns has been enqueued (step bs[i + 1] / 64 - 2; before the loop when negative)
     int64_t fork_step[64];
@@ -1014,26 +993,27 @@ static gptq_status cholinv(PrepCtx& c, AuxStream* own_aux) {
         else fork_step[i] = std::max(fork_step[i], fork_step[i - 1]);
     }
     auto fork = [&](int i) -> gptq_status {
-        if (hipEventRecord(aux->fork, c.s) != hipSuccess || hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess)
+        if (aux && (hipEventRecord(aux->fork, c.s) != hipSuccess ||
+                    hipStreamWaitEvent(ca.s, aux->fork, 0) != hipSuccess))
             return GPTQ_ERR_HIP;
         const int64_t b0 = bs[i], b1 = bs[i + 1], len = b1 - b0, below = d - b1;
         gptq_status r;
-        if ((r = trtri_block(ca, b0, len, Saux, AUX_MAX_WG)) != GPTQ_OK) return r;
+        if ((r = trtri_block(ca, b0, len, Saux, aux_wg)) != GPTQ_OK) return r;
         if (i > 0) {
             // X[B_i][P_i] = -X[B_i][B_i] Trest[B_i][P_i]   (lower triangular X block)
             if ((r = gemm(ca, c.X + b0 * d, d, c.X + b0 * d + b0, d, trow(b0), sl, (int)len, (int)b0, (int)len, -1.0,
-                          0.0, G_TRI_A, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+                          0.0, G_TRI_A, 1, 0, 0, 0, 0, 0, 0, 0, aux_wg)) != GPTQ_OK)
                 return r;
             // Trest[after B_i][P_i] += L[after B_i][B_i] X[B_i][P_i]
             if ((r = gemm(ca, trow(b1), sl, c.A + b1 * d + b0, d, c.X + b0 * d, d, (int)below, (int)b0, (int)len, 1.0,
-                          1.0, 0, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+                          1.0, 0, 1, 0, 0, 0, 0, 0, 0, 0, aux_wg)) != GPTQ_OK)
                 return r;
         }
         // Trest[after B_i][B_i] = L[after B_i][B_i] X[B_i][B_i]   (lower triangular X block)
         if ((r = gemm(ca, trow(b1) + b0, sl, c.A + b1 * d + b0, d, c.X + b0 * d + b0, d, (int)below, (int)len, (int)len,
-                      1.0, 0.0, G_TRI_B, 1, 0, 0, 0, 0, 0, 0, 0, AUX_MAX_WG)) != GPTQ_OK)
+                      1.0, 0.0, G_TRI_B, 1, 0, 0, 0, 0, 0, 0, 0, aux_wg)) != GPTQ_OK)
             return r;
-        if (hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
+        if (aux && hipEventRecord(aux->join, ca.s) != hipSuccess) return GPTQ_ERR_HIP;
         return GPTQ_OK;
     };
     int nf = 0;   // blocks handed to the auxiliary stream
@@ -1058,7 +1038,7 @@ static gptq_status cholinv(PrepCtx& c, AuxStream* own_aux) {
         if ((st = fork(nf++)) != GPTQ_OK) return st;
     // the last block's inverse, then X[last][P] = -X[last][last] Trest[last][P]
     if ((st = trtri_block(c, sl, nl, Smain)) != GPTQ_OK) return st;
-    if (hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
+    if (aux && hipStreamWaitEvent(c.s, aux->join, 0) != hipSuccess) return GPTQ_ERR_HIP;
     return gemm(c, c.X + sl * d, d, c.X + sl * d + sl, d, trow(sl), sl, (int)nl, (int)sl, (int)nl, -1.0, 0.0, G_TRI_A);
 }
 
@@ -1077,7 +1057,7 @@ size_t prep_ws_bytes(int64_t d) {
 }
 
 gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, void* ws, size_t ws_bytes,
-                        int32_t* info, hipStream_t s, PrepAux* own_aux) {
+                        int32_t* info, hipStream_t s, const PrepAux* aux) {
     if (ws == nullptr || ws_bytes < prep_ws_bytes(d)) return GPTQ_ERR_WORKSPACE;
     char* p = reinterpret_cast<char*>(ws);
     const size_t dd = align256((size_t)d * d * sizeof(double));
@@ -1098,12 +1078,7 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     else prep_build_kernel<false><<<gb, 256, 0, s>>>(H, d, lam, c.A);
     GPTQ_LAUNCH_CHECK();
     gptq_status st;
-    if (own_aux) {
-        st = cholinv(c, own_aux);   // the caller's auxiliary stream and events
-    } else {
-        std::lock_guard<std::mutex> g(aux_mu);
-        st = cholinv(c, nullptr);
-    }
+    st = cholinv(c, aux);
     if (st != GPTQ_OK) return st;
     if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0) prep_output_kernel<true><<<gb4, 256, 0, s>>>(c.X, d, U);
     else prep_output_kernel<false><<<gb, 256, 0, s>>>(c.X, d, U);

@@ -46,13 +46,15 @@ def lib():
         "gptq_hessian_workspace_size": (sz, [i64, i64]),
         "gptq_hessian_accumulate": (ctypes.c_int, [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp]),
         "gptq_prepare_hinv_workspace_size": (sz, [i64]),
-        "gptq_prepare_hinv": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp, sz, vp, vp]),
+        "gptq_context_create": (ctypes.c_int, [i32, ctypes.POINTER(vp)]),
+        "gptq_context_destroy": (ctypes.c_int, [vp]),
+        "gptq_prepare_hinv": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp, sz, vp, vp, vp]),
         "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
         "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
         "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
-                                                ctypes.POINTER(Params), i32, vp, sz, vp, vp]),
+                                                ctypes.POINTER(Params), i32, vp, sz, vp, vp, vp]),
         "gptq_obq_workspace_size": (sz, [i64, i64]),
         "gptq_obq_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                           vp, vp, vp, vp, sz, vp, vp]),
@@ -70,6 +72,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
+        "gptq_context_create", "gptq_context_destroy",
         "gptq_hessian_workspace_size", "gptq_hessian_accumulate",
         "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
         "gptq_quantize_workspace_size", "gptq_quantize_layer",
@@ -121,11 +124,24 @@ def test_hessian_argument_errors(lib):
 
 def test_prepare_argument_errors(lib):
     f = lib.gptq_prepare_hinv
-    assert f(FAKE, FAKE, 16, -0.5, FAKE, 1 << 20, FAKE, None) == INVALID_ARG
-    assert f(FAKE, FAKE, 16, float("nan"), FAKE, 1 << 20, FAKE, None) == INVALID_ARG
-    assert f(FAKE, FAKE, 16, 0.01, FAKE, 1 << 20, None, None) == INVALID_ARG  # null info
-    assert f(FAKE, None, 16, 0.01, FAKE, 1 << 20, FAKE, None) == INVALID_ARG  # null U
-    assert f(None, None, 0, 0.01, None, 0, None, None) == OK                   # empty
+    assert f(FAKE, FAKE, 16, -0.5, FAKE, 1 << 20, FAKE, None, None) == INVALID_ARG
+    assert f(FAKE, FAKE, 16, float("nan"), FAKE, 1 << 20, FAKE, None, None) == INVALID_ARG
+    assert f(FAKE, FAKE, 16, 0.01, FAKE, 1 << 20, None, None, None) == INVALID_ARG  # null info
+    assert f(FAKE, None, 16, 0.01, FAKE, 1 << 20, FAKE, None, None) == INVALID_ARG  # null U
+    assert f(FAKE, FAKE, 16, 0.01, FAKE, 100, FAKE, None, None) == WORKSPACE        # too small
+    assert f(FAKE, FAKE, 16, 0.01, None, 1 << 20, FAKE, None, None) == WORKSPACE    # missing
+    assert f(None, None, 0, 0.01, None, 0, None, None, None) == OK                   # empty
+
+
+def test_context_argument_errors(lib):
+    """Slot counts outside 1 .. GPTQ_LAYERS_MAX_SLOTS and a null out-pointer are refused
+    before any HIP call; destroying NULL is a no-op."""
+    out = ctypes.c_void_p()
+    assert lib.gptq_context_create(0, ctypes.byref(out)) == INVALID_ARG
+    assert lib.gptq_context_create(5, ctypes.byref(out)) == INVALID_ARG
+    assert lib.gptq_context_create(2, None) == INVALID_ARG
+    assert out.value is None
+    assert lib.gptq_context_destroy(None) == OK
 
 
 def test_quantize_argument_errors(lib):
@@ -208,7 +224,7 @@ def test_layers_argument_errors(lib):
     need = lib.gptq_quantize_layers_workspace_size(good, 2, 2)
     ws = ctypes.c_void_p(0x10000000)
     call = lambda layers, n=2, slots=2, prm=ctypes.byref(p), damp=0.01, w=ws, wb=need, info=FAKE: \
-        f(layers, n, damp, prm, slots, w, wb, info, None)
+        f(layers, n, damp, prm, slots, w, wb, info, None, None)
     assert call(good, slots=0) == INVALID_ARG
     assert call(good, slots=5) == INVALID_ARG
     assert call(None, n=1) == INVALID_ARG

@@ -1,6 +1,7 @@
-"""gptq_quantize_layers (a block's linears in one call, phases overlapped on library
-streams) against one call per phase and layer, bit for bit, for 1, 2 and 3 slots and
-twice in a row; the group that shares one input (q, k, v) also against the oracle."""
+"""gptq_quantize_layers (a block's linears in one call, phases overlapped on the streams
+of a caller-owned context, or on one stream without it) against one call per phase and
+layer, bit for bit, for 1, 2 and 3 slots and twice in a row; the group that shares one
+input (q, k, v) also against the oracle."""
 import numpy as np
 import pytest
 
@@ -48,22 +49,25 @@ def test_layers_match_per_phase_calls(bits, group, sym):
         torch.cuda.synchronize()
         assert int(info.item()) == 0 and int(q.info.item()) == 0
         ref.append((q.codes.cpu(), q.scales.cpu(), q.zeros.cpu(), U))
-    for slots in (1, 2, 3, 2):
-        outs, info = g.quantize_layers(pairs, bits=bits, group_size=group, sym=sym, n_slots=slots)
+    ctx = g.Context(3)
+    for slots, c_ in ((1, ctx), (2, ctx), (3, ctx), (2, ctx), (1, None)):
+        outs, info = g.quantize_layers(pairs, bits=bits, group_size=group, sym=sym, n_slots=slots, ctx=c_)
         torch.cuda.synchronize()
         assert not info.cpu().any(), info.cpu()
         for k, (q, (c, s, z, _)) in enumerate(zip(outs, ref)):
             assert torch.equal(q.codes.cpu(), c), (slots, k)
             assert torch.equal(q.scales.cpu(), s), (slots, k)
             assert torch.equal(q.zeros.cpu(), z), (slots, k)
-        log(f"  {slots} slot(s): all {len(pairs)} layers bit-identical")
+        log(f"  {slots} slot(s){' (no context: one stream)' if c_ is None else ''}: all {len(pairs)} layers bit-identical")
+    with pytest.raises(g.GptqError):      # more slots than the context holds
+        g.quantize_layers(pairs, bits=bits, group_size=group, sym=sym, n_slots=4, ctx=ctx)
 
     # the shared-input group (q, k, v) against the oracle: one H, one U, three sweeps
     Xh = xs[spec[0][0].name][1]
     Ho = o.hessian([synth.x_as_f64(Xh)])
     Uo, _ = o.prepare_u(Ho, 0.01)
     p = o.Params(bits=bits, group_size=group, sym=sym)
-    outs, _ = g.quantize_layers(pairs[:3], bits=bits, group_size=group, sym=sym, n_slots=2)
+    outs, _ = g.quantize_layers(pairs[:3], bits=bits, group_size=group, sym=sym, n_slots=2, ctx=ctx)
     torch.cuda.synchronize()
     for (LX, LW), q in zip(spec[:3], outs):
         Wf = synth.w_as_f64(synth.weights(LW))

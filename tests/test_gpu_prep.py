@@ -81,3 +81,24 @@ def test_prep_ignores_workspace_contents(d):
     assert np.all(np.isfinite(Ug))
     rowmax = np.max(np.abs(Uo), axis=1, keepdims=True)
     assert float(np.max(np.abs(Ug - Uo) / rowmax)) <= 1e-6
+
+
+@pytest.mark.parametrize("d", [520, 3000, 4096])
+def test_prep_with_context_is_bit_identical(d):
+    """With a caller-owned context the inverse's row blocks run on its auxiliary stream
+    beside the factorization; U is the same bit for bit as with every kernel on one
+    stream (the same sums in the same order), and matches the oracle."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    H32 = _h(d, 2 * d, 7)
+    Hd = torch.from_numpy(H32).cuda()
+    U1, i1 = g.prepare_hinv(Hd, 0.01)
+    with g.Context(1) as ctx:
+        U2, i2 = g.prepare_hinv(Hd, 0.01, ctx=ctx)
+        U3, i3 = g.prepare_hinv(Hd, 0.01, ctx=ctx)      # the context again, right after
+        torch.cuda.synchronize()
+    assert int(i1.item()) == int(i2.item()) == int(i3.item()) == 0
+    assert torch.equal(U1, U2) and torch.equal(U1, U3)
+    Uo, _ = o.prepare_u(H32.astype(np.float64), 0.01)
+    rowmax = np.max(np.abs(Uo), axis=1, keepdims=True)
+    assert float(np.max(np.abs(U2.cpu().numpy() - Uo) / rowmax)) <= 1e-6
