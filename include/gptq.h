@@ -200,6 +200,29 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row
                                 void* ws, size_t ws_bytes, int32_t* info, void* stream);
 
 /*
+ * gptq_quantize_layer without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  It computes exactly what gptq_quantize_layer computes (the same
+ * kernels), with the library's own scratch in place of `ws`: a fixed array of
+ * GPTQ_NOALLOC_SCRATCH_BYTES in each GPU's memory, held from the library's first use of
+ * that GPU until the process ends.  The call allocates and frees nothing.
+ *
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
+ * (different streams, or several host threads) race and must be serialized by the
+ * caller; calls ordered on one stream are fine.
+ *
+ *  W, U, p, codes, scales_f16, zeros_f16, info, stream   as for gptq_quantize_layer.
+ * Errors as gptq_quantize_layer, and GPTQ_ERR_UNSUPPORTED when the layer needs more than
+ * the scratch holds (gptq_quantize_workspace_size(d_row, d_col, p) >
+ * GPTQ_NOALLOC_SCRATCH_BYTES: up to 4096 x 4096 fits), decided before anything is queued.
+ */
+#define GPTQ_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+gptq_status gptq_quantize_layer_noalloc(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col,
+                                        const float* U, const gptq_params* p,
+                                        uint8_t* codes, uint16_t* scales_f16, uint16_t* zeros_f16,
+                                        int32_t* info, void* stream);
+
+/*
  * Several layers in one call, with the phases of different layers overlapped: for
  * every layer, H = 2 X^T X over its own calibration inputs, U as gptq_prepare_hinv
  * makes it, and codes, scales and zeros as gptq_quantize_layer writes them; each

@@ -60,6 +60,8 @@ def _load():
         "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
+        "gptq_quantize_layer_noalloc": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
+                                                       vp, vp, vp, vp, vp]),
         "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
         "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
                                                 ctypes.POINTER(Params), i32, vp, sz, vp, vp, vp]),
@@ -251,6 +253,26 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: 
                                    ws.data_ptr() if ws is not None else None,
                                    ws.numel() if ws is not None else 0, out.info.data_ptr(), _stream(stream)),
            "gptq_quantize_layer")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # GPTQ_NOALLOC_SCRATCH_BYTES
+
+
+def quantize_layer_noalloc(W: torch.Tensor, U: torch.Tensor, out: Quantized, bits: int = 4, group_size: int = 128,
+                           sym: bool = False, stream=None, fp4: bool = False, mx: bool = False) -> Quantized:
+    """gptq_quantize_layer_noalloc: as quantize_layer, with the library's per-device scratch
+    in place of a workspace, into caller-allocated outputs (nothing is allocated here, so
+    it can be captured in a graph).  Calls that overlap on one GPU race on the scratch."""
+    _dev(W, "W"); _dev(U, "U")
+    if W.dtype not in _DT or U.dtype != torch.float32:
+        raise ValueError("W must be f32/bf16/f16 and U float32")
+    d_row, d_col = W.shape
+    p = make_params(bits, group_size, sym, 128, fp4, mx)
+    _check(lib.gptq_quantize_layer_noalloc(W.data_ptr(), _DT[W.dtype], d_row, d_col, U.data_ptr(), ctypes.byref(p),
+                                           out.codes.data_ptr(), out.scales.data_ptr(), out.zeros.data_ptr(),
+                                           out.info.data_ptr(), _stream(stream)),
+           "gptq_quantize_layer_noalloc")
     return out
 
 

@@ -92,6 +92,20 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row
                         (hipStream_t)stream);
 }
 
+gptq_status gptq_quantize_layer_noalloc(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col,
+                                        const float* U, const gptq_params* p, uint8_t* codes, uint16_t* scales_f16,
+                                        uint16_t* zeros_f16, int32_t* info, void* stream) {
+    if (d_row < 0 || d_col < 0 || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_params(p, d_col);
+    if (st != GPTQ_OK) return st;
+    if (d_row == 0 || d_col == 0) return GPTQ_OK;
+    if (!W || !U || !codes || !scales_f16 || !zeros_f16 || !info) return GPTQ_ERR_INVALID_ARG;
+    if (d_row > 2147483647LL / 64 || d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
+    if (quant_ws_bytes(d_row, d_col) > GPTQ_NOALLOC_SCRATCH_BYTES) return GPTQ_ERR_UNSUPPORTED;
+    return quant_launch_noalloc(W, w_dtype, d_row, d_col, U, *p, codes, scales_f16, zeros_f16, info,
+                                (hipStream_t)stream);
+}
+
 // p == nullptr: shapes only (the workspace size), no settings and no pointers checked.
 static gptq_status check_layers(const gptq_layer* L, int32_t n, const gptq_params* p, int32_t n_slots) {
     if (n < 0 || (n > 0 && L == nullptr)) return GPTQ_ERR_INVALID_ARG;

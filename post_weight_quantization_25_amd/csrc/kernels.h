@@ -30,6 +30,11 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
                          const gptq_params& p, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
                          void* ws, size_t ws_bytes, int32_t* info, hipStream_t stream);
 
+// gptq_quantize_layer with the library's own per-device scratch in place of a workspace
+gptq_status quant_launch_noalloc(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
+                                 const gptq_params& p, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                 int32_t* info, hipStream_t stream);
+
 size_t layers_ws_bytes(const gptq_layer* layers, int n, int n_slots);
 gptq_status layers_launch(const gptq_layer* layers, int n, float percdamp, const gptq_params& p, int n_slots,
                           void* ws, size_t ws_bytes, int32_t* info, gptq_context* ctx, hipStream_t stream);

@@ -18,6 +18,8 @@
 // operands split into bf16 hi + lo (three products, fp32 accumulation), the
 // host-side block loop, and dequantization.
 
+#include <mutex>
+
 #include "kernels.h"
 #include "quant_internal.h"
 
@@ -834,6 +836,46 @@ gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const u
     if (fp4) return dq_dt<4, true>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     if (bits <= 4) return dq_dt<4>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     return dq_dt<8>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
+}
+
+// --------------------------------------------------------------------------
+// Scratch of gptq_quantize_layer_noalloc, for callers that cannot allocate (code under
+// HIP graph capture, tight serving loops): a file-scope device array of fixed size in
+// place of the caller's workspace.  Each GPU the library runs on holds its own copy
+// until the process ends, and every call on that GPU shares it, keeping the last
+// call's contents (nothing in it needs to start at zero: every value a kernel reads is
+// written earlier in the same call).  Calls that overlap on one GPU race.  Host code
+// never passes the array's name (a host-side stand-in): its device address is looked up
+// once per device, with that device current, and that address is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[GPTQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::once_flag scratch_once[SCRATCH_MAX_DEVICES];
+static void* scratch_dev_ptr[SCRATCH_MAX_DEVICES];
+static hipError_t scratch_err[SCRATCH_MAX_DEVICES];
+
+static gptq_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return GPTQ_ERR_HIP;
+    std::call_once(scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        scratch_dev_ptr[dev] = scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (scratch_err[dev] != hipSuccess || scratch_dev_ptr[dev] == nullptr) return GPTQ_ERR_HIP;
+    *out = scratch_dev_ptr[dev];
+    return GPTQ_OK;
+}
+
+gptq_status quant_launch_noalloc(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
+                                 const gptq_params& p, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                 int32_t* info, hipStream_t s) {
+    if (quant_ws_bytes(d_row, d_col) > GPTQ_NOALLOC_SCRATCH_BYTES) return GPTQ_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    const gptq_status st = scratch_address(&ws);
+    if (st != GPTQ_OK) return st;
+    return quant_launch(W, w_dtype, d_row, d_col, U, p, codes, scales, zeros, ws, GPTQ_NOALLOC_SCRATCH_BYTES, info,
+                        s);
 }
 
 }  // namespace gptq

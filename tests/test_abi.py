@@ -52,6 +52,8 @@ def lib():
         "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
                                                vp, vp, vp, vp, sz, vp, vp]),
+        "gptq_quantize_layer_noalloc": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
+                                                       vp, vp, vp, vp, vp]),
         "gptq_quantize_layers_workspace_size": (sz, [ctypes.POINTER(LayerDesc), i32, i32]),
         "gptq_quantize_layers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), i32, ctypes.c_float,
                                                 ctypes.POINTER(Params), i32, vp, sz, vp, vp, vp]),
@@ -75,7 +77,7 @@ def test_header_declares_the_boundary():
         "gptq_context_create", "gptq_context_destroy",
         "gptq_hessian_workspace_size", "gptq_hessian_accumulate",
         "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
-        "gptq_quantize_workspace_size", "gptq_quantize_layer",
+        "gptq_quantize_workspace_size", "gptq_quantize_layer", "gptq_quantize_layer_noalloc",
         "gptq_quantize_layers_workspace_size", "gptq_quantize_layers",
         "gptq_obq_workspace_size", "gptq_obq_layer", "gptq_dequantize_e2m1",
         "gptq_dequantize", "gptq_quantized_linear", "gptq_status_string"])
@@ -288,3 +290,19 @@ def test_header_compiles_as_c_and_cpp(tmp_path):
                     str(src)], check=True)
     subprocess.run(["g++", "-std=c++11", "-Wall", "-Werror", f"-I{inc}", "-fsyntax-only", "-x", "c++", str(src)],
                    check=True)
+
+
+def test_noalloc_argument_errors(lib):
+    """The allocation-free variant validates like gptq_quantize_layer and refuses, before
+    any device work, a layer whose workspace would exceed its fixed scratch."""
+    f = lib.gptq_quantize_layer_noalloc
+    p = lib.Params(4, 128, 0, 128)
+    call = lambda d_row, d_col, prm=p, w=FAKE: f(w, BF16, d_row, d_col, FAKE, ctypes.byref(prm), FAKE, FAKE, FAKE,
+                                                 FAKE, None)
+    assert lib.gptq_quantize_workspace_size(4096, 4096, None) <= 256 << 20
+    assert lib.gptq_quantize_workspace_size(8192, 8192, None) > 256 << 20
+    assert call(8192, 8192) == UNSUPPORTED
+    assert call(64, 256, prm=lib.Params(5, 128, 0, 128)) == UNSUPPORTED
+    assert call(64, 250) == INVALID_ARG                 # group does not divide d_col
+    assert call(64, 256, w=None) == INVALID_ARG
+    assert f(None, BF16, 0, 256, None, ctypes.byref(p), None, None, None, None, None) == OK
