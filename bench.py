@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--linear", action="store_true")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--obq", action="store_true")
+    ap.add_argument("--no-kernel-split", action="store_true",
+                    help="skip the profiled step that splits the quantize phase by kernel")
     return ap.parse_args()
 
 
@@ -75,6 +77,47 @@ def measured_traffic(launch_bytes_alg: float = 0.0, path: str | None = None, sou
     return t.get("bytes_per_launch")
 
 
+MFMA_BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy_c2.json")
+
+
+def measured_mfma_busy():
+    """MFMA-busy fraction of the Hessian and trailing-update kernels from a committed
+    rocprofv3 counter summary, or None when either source changed since it was taken."""
+    try:
+        with open(MFMA_BUSY_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for src, h in t.get("source_sha256_16", {}).items():
+        if source_hash(src) != h:
+            return None
+    return t.get("mfma_busy")
+
+
+def phase_rooflines(split, r, d):
+    """Algorithmic rates of the sweep (HBM) and the trailing update (16-bit MFMA) from the
+    per-phase kernel times.  Sweep bytes per layer: the fp32 working copy read once (4 B),
+    the scaled fp16 error pair written (4 B), half a byte of codes per weight, a scale and
+    a zero per group, the diagonal blocks of U (d x 128 fp32).  Trailing-kernel flops: the
+    products after each 512-column super-block, 2 r sum_s 512 (d - s1) (the updates
+    inside a super-block run in the sweep kernel)."""
+    out = {}
+    sweep_ms, trail_ms = split.get("sweep"), split.get("trail")
+    if sweep_ms:
+        byt = r * d * (4 + 4 + 0.5) + r * (d // 128) * 4 + d * 128 * 4
+        gbs = byt / (sweep_ms * 1e-3) / 1e9
+        out["sweep"] = {"bound": "hbm", "algorithmic_bytes": byt, "ms": sweep_ms, "achieved": gbs,
+                        "unit": "GB/s", "peak": HBM_GBS, "frac": gbs / HBM_GBS}
+    if trail_ms:
+        fl = 2.0 * r * sum(min(512, d - s0) * (d - min(s0 + 512, d)) for s0 in range(0, d, 512))
+        tf = fl / (trail_ms * 1e-3) / 1e12
+        out["trail"] = {"bound": "mfma", "algorithmic_flops": fl, "ms": trail_ms, "achieved": tf,
+                        "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS,
+                        "note": "products after each super-block (the updates inside a super-block run in "
+                                "the sweep kernel); three fp16 products are issued per algorithmic one"}
+    return out
+
+
 def calibrate_copy(dev):
     """One plain elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 times 1): the
     known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -84,6 +127,38 @@ def calibrate_copy(dev):
     torch.cuda.synchronize()
     torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
+
+
+# kernel name -> phase of the step (kernels of the library; torch's own fills go to "other")
+KERNEL_PHASES = [("hess_", "hess"), ("prep_", "prep"), ("gemm_f64", "prep"), ("sweep_kernel", "sweep"),
+                 ("trail_", "trail"), ("convert_kernel", "quant_setup"), ("split_u_kernel", "quant_setup"),
+                 ("udt_kernel", "quant_setup"), ("row_params", "quant_setup"), ("tensor_", "quant_setup"),
+                 ("dequant_kernel", "deq")]
+
+
+def kernel_split(step, steps: int = 2):
+    """Per-phase kernel time of ``steps`` steps (mean per step, ms), from torch's profiler,
+    which records every kernel the process launches (the library's included), by kernel
+    name.  The quantize phase splits into the sweep, the trailing update and its set-up
+    kernels; kernels on two streams (the factorization's inverse) may overlap, so the
+    prep sum can exceed its wall time."""
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+    out, per_kernel = {}, {}
+    for e in prof.events():
+        dt = getattr(e, "device_time", None)
+        if dt is None:
+            dt = getattr(e, "cuda_time", 0.0)
+        if not dt or str(getattr(e, "device_type", "")).find("CUDA") < 0:
+            continue
+        ph = next((v for k, v in KERNEL_PHASES if k in e.name), "other")
+        out[ph] = out.get(ph, 0.0) + dt / 1000.0 / steps
+        per_kernel[e.name] = per_kernel.get(e.name, 0.0) + dt / 1000.0 / steps
+    return out, per_kernel
 
 
 def cpu_baseline(layer, sample_tokens: int, sample_rows: int):
@@ -484,6 +559,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(dev)
+    split = None
+    if not args.no_kernel_split:
+        split, _ = kernel_split(step)
 
     flops_hess = float(n) * d * (d + 1)            # symmetric rank-n update, upper triangle incl. diagonal
     achieved = flops_hess / (hess_launch_ms * 1e-3) / 1e12
@@ -504,7 +582,7 @@ def main():
         "config": {"workload": "attention projection 4096x4096: W bf16 ~N(0,0.02^2), X 262144x4096 bf16 "
                                "(log-normal channel scales, 4 channels x50), int4 asym g128, B=128, damp 0.01",
                    "d_row": r, "d_col": d, "n_tokens": n, "bits": 4, "group_size": 128, "block_size": 128,
-                   "arithmetic": "H: bf16 MFMA, fp32 accumulate; prep: fp64 MFMA; sweep: fp32; trailing: bf16 hi/lo split (three products) on bf16 MFMA, fp32 accumulate"},
+                   "arithmetic": "H: bf16 MFMA, fp32 accumulate; prep: fp64 MFMA; sweep: fp32; trailing: fp16 hi/lo split of power-of-two-scaled operands (three products) on fp16 MFMA, fp32 accumulate"},
         "ms_per_layer": ms_layer,
         "ms_per_layer_quantize_only": ph["prep"] + ph["quant"],
         "phases_ms": ph,
@@ -516,6 +594,12 @@ def main():
                      "launch_ms": hess_launch_ms,
                      "algorithmic_flops_per_launch": flops_hess},
     }
+    mb = measured_mfma_busy()
+    if mb is not None:
+        rec["roofline"]["mfma_busy"] = mb
+    if split is not None:
+        rec["kernel_ms"] = split
+        rec["phase_rooflines"] = phase_rooflines(split, r, d)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(layer, sample_tokens=4 * 8192, sample_rows=256)
     print(json.dumps(rec), flush=True)

@@ -98,23 +98,34 @@ __global__ __launch_bounds__(256) void tensor_params_kernel(const float* part, i
     for (int64_t r = threadIdx.x; r < d_row; r += 256) { scales[r] = sz[0]; zeros[r] = sz[1]; }
 }
 
-// W (any dtype) -> fp32 working copy; flags non-finite values.  Eight values per
-// thread and step with 16-byte accesses when both arrays are 16-byte aligned; the
-// rest (or everything, unaligned) one value at a time.
+// W (any dtype) -> fp32 working copy, one workgroup per row; flags non-finite values and
+// writes the row's error scale es_r = 2^(17 - e), |W[r][:]| < 2^e (frexp of the row's
+// largest magnitude): the scaled errors E[r][k] es_r / us_k of the trailing update then
+// stay well inside fp16's normal range (|E| / us_k is about |err| max_j |U[k][j]| /
+// U[k][k] 2^-13.5, and the errors are a fraction of the row's magnitude).  Eight values
+// per thread and step with 16-byte accesses when the rows are 16-byte aligned; otherwise
+// one value at a time.
 template <gptq_dtype DT>
-__global__ void convert_kernel(const void* W, int64_t n, float* out, int32_t* info) {
+__global__ __launch_bounds__(256) void convert_kernel(const void* W, int64_t d_col, float* out, float* es,
+                                                      int32_t* info) {
+    __shared__ float red[4];
+    constexpr int EB = (DT == GPTQ_F32) ? 4 : 2;
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const char* src = reinterpret_cast<const char*>(W) + row * d_col * EB;
+    float* dst = out + row * d_col;
+    const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0);
+    const int64_t n8 = vec ? d_col / 8 : 0;
     int bad = 0;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nth = (int64_t)gridDim.x * blockDim.x;
-    const bool vec = ((reinterpret_cast<uintptr_t>(W) & 15) == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
-    const int64_t n8 = vec ? n / 8 : 0;
-    for (int64_t i = tid; i < n8; i += nth) {
+    float m = 0.f;
+    for (int64_t i = tid; i < n8; i += 256) {
         float v[8];
         if constexpr (DT == GPTQ_F32) {
-            const f32x4_t a = reinterpret_cast<const f32x4_t*>(W)[2 * i], b = reinterpret_cast<const f32x4_t*>(W)[2 * i + 1];
+            const f32x4_t a = reinterpret_cast<const f32x4_t*>(src)[2 * i], b = reinterpret_cast<const f32x4_t*>(src)[2 * i + 1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
         } else {
-            const u32x4_t h = reinterpret_cast<const u32x4_t*>(W)[i];
+            const u32x4_t h = reinterpret_cast<const u32x4_t*>(src)[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint16_t lo = (uint16_t)(h[e] & 0xFFFFu), hi = (uint16_t)(h[e] >> 16);
@@ -123,25 +134,41 @@ __global__ void convert_kernel(const void* W, int64_t n, float* out, int32_t* in
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bad |= !isfinite(v[e]);
-        f32x4_t* o = reinterpret_cast<f32x4_t*>(out) + 2 * i;
+        for (int e = 0; e < 8; ++e) { bad |= !isfinite(v[e]); m = fmaxf(m, fabsf(v[e])); }
+        f32x4_t* o = reinterpret_cast<f32x4_t*>(dst) + 2 * i;
         o[0] = f32x4_t{v[0], v[1], v[2], v[3]};
         o[1] = f32x4_t{v[4], v[5], v[6], v[7]};
     }
-    for (int64_t i = 8 * n8 + tid; i < n; i += nth) {
-        const float v = load_as_f32<DT>(W, i);
-        if (!isfinite(v)) bad = 1;
-        out[i] = v;
+    for (int64_t c = 8 * n8 + tid; c < d_col; c += 256) {
+        const float v = load_as_f32<DT>(W, row * d_col + c);
+        bad |= !isfinite(v);
+        m = fmaxf(m, fabsf(v));
+        dst[c] = v;
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
     if (bad) *info = -1;
+    __syncthreads();
+    if (tid == 0) {
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        int e = 0;
+        (void)frexpf(m, &e);
+        es[row] = (m > 0.f && m <= 3.0e38f) ? ldexpf(1.f, 17 - e) : 1.f;
+    }
 }
 
 // --------------------------------------------------------------------------
 // Trailing lazy update: W[:, n_beg:n_end] -= E[:, :K] U[k0:k0+K, n_beg:n_end] on
-// bf16 MFMA (v_mfma_f32_32x32x16_bf16) with a three-term split of the fp32
-// operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi), and
+// fp16 MFMA (v_mfma_f32_32x32x16_f16) with a three-term split of scaled fp32
+// operands: x = hi + lo with hi = fp16(x), lo = fp16(x - hi), and
 // E U ~= Ehi Uhi + Ehi Ulo + Elo Uhi (the dropped Elo Ulo and the residuals are
-// ~2^-16 relative per product), accumulated in fp32.
+// ~2^-22 relative per product), accumulated in fp32.  fp16 keeps 11 bits where bf16
+// keeps 8, but not its range, so both operands are scaled by exact powers of two that
+// cancel: row k of U by us_k (its largest magnitude into [2^13, 2^14)), E[r][k] by
+// es_r / us_k (es_r from row r's largest weight), and the product of row r by 1 / es_r.
+// With bf16 (hi + lo) the per-product error was ~2^-17, which moved the values the
+// codes are decided from by ~1e-6 of a step on the widest layers.
 // 128 x 128 output tiles, four waves of 64 x 64 (2 x 2 MFMA 32 x 32 tiles); K in
 // chunks of 32 staged in LDS as bf16: E row-major ([m][k], 8 consecutive k per
 // 16-byte read), U as it lies in memory ([k][n]) and read transposed with
@@ -157,8 +184,9 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 struct TrailArgs {
     float* Wws; int64_t d_row, d_col;
-    const uint16_t* Ehi; const uint16_t* Elo; int64_t lde;   // E block (bf16 hi + lo): d_row x K
-    const uint16_t* Uhi; const uint16_t* Ulo;                // U (bf16 hi + lo), d_col x d_col
+    const uint16_t* Ehi; const uint16_t* Elo; int64_t lde;   // scaled E block (fp16 hi + lo): d_row x K
+    const uint16_t* Uhi; const uint16_t* Ulo;                // scaled U (fp16 hi + lo), d_col x d_col
+    const float* erow;                                       // es_r per row (the product is divided by it)
     int64_t k0; int K;
     int64_t n_beg, n_end;
     int64_t m_beg;                                           // first row of the launch's tiles
@@ -224,24 +252,24 @@ GPTQ_DEV void trail_store(TrailStage& st, int tid, const TrailRegs& r) {
 // B operand (32 columns n x 16 k) from the [k][n] tile with two transposed reads:
 // in each 16-lane group lane j addresses k = k0 + (j >> 2), n = n0 + 4 (j & 3) and lane
 // i receives column n0 + i at k0 .. k0 + 3.
-GPTQ_DEV bf16x8_t trail_bfrag(const uint16_t* tile, int nc0, int kk, int lane) {
+GPTQ_DEV f16x8_t trail_bfrag(const uint16_t* tile, int nc0, int kk, int lane) {
     const int g = lane >> 4, j = lane & 15;
     const int n = nc0 + (g & 1) * 16 + 4 * (j & 3);
     const int k = kk + (g >> 1) * 8 + (j >> 2);
     const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + k * TU_RS + n));
     const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + (k + 4) * TU_RS + n));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 GPTQ_DEV void trail_mfma(const TrailStage& st, int wr, int wc, int lane, f32x16_t (&acc)[2][2]) {
 #pragma unroll
     for (int kk = 0; kk < TK; kk += 16) {
-        bf16x8_t ah[2], al[2], bh[2], bl[2];
+        f16x8_t ah[2], al[2], bh[2], bl[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int m = wr * 64 + i * 32 + (lane & 31), k = kk + (lane >> 5) * 8;
-            ah[i] = *reinterpret_cast<const bf16x8_t*>(&st.ehi[m * TE_LD + k]);
-            al[i] = *reinterpret_cast<const bf16x8_t*>(&st.elo[m * TE_LD + k]);
+            ah[i] = *reinterpret_cast<const f16x8_t*>(&st.ehi[m * TE_LD + k]);
+            al[i] = *reinterpret_cast<const f16x8_t*>(&st.elo[m * TE_LD + k]);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -252,9 +280,9 @@ GPTQ_DEV void trail_mfma(const TrailStage& st, int wr, int wc, int lane, f32x16_
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bh[j], acc[i][j], 0, 0, 0);
             }
     }
 }
@@ -288,23 +316,28 @@ __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
         if (c + 2 < nch) trail_load(a, m0, n0, (c + 2) * TK, tid, rg, fl);
         __syncthreads();
     }
-    // W -= acc: all loads first, then all stores (a load after a store to the same
-    // array would otherwise wait for that store's round trip)
+    // W -= acc / es_row: all loads first, then all stores (a load after a store to the
+    // same array would otherwise wait for that store's round trip)
     const bool full = (m0 + TB <= a.d_row) && (n0 + TB <= a.n_end);
     float* wbase = a.Wws + (m0 + wr * 64 + 4 * (lane >> 5)) * a.d_col + n0 + wc * 64 + (lane & 31);
     auto off = [&](int i, int j, int e) { return (int64_t)(i * 32 + 8 * (e >> 2) + (e & 3)) * a.d_col + j * 32; };
+    auto rowm = [&](int i, int e) { return m0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
     if (full) {
         // one accumulator tile (16 values per lane) at a time keeps the register count low
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+            float inv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) inv[e] = 1.0f / a.erow[rowm(i, e)];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 float old[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) old[e] = wbase[off(i, j, e)];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) wbase[off(i, j, e)] = old[e] - acc[i][j][e];
+                for (int e = 0; e < 16; ++e) wbase[off(i, j, e)] = fmaf(-acc[i][j][e], inv[e], old[e]);
             }
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -312,9 +345,10 @@ __global__ __launch_bounds__(256) void trail_kernel(TrailArgs a) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int64_t gm = m0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    const int64_t gm = rowm(i, e);
                     const int64_t gn = n0 + wc * 64 + j * 32 + (lane & 31);
-                    if (gm < a.d_row && gn < a.n_end) a.Wws[gm * a.d_col + gn] -= acc[i][j][e];
+                    if (gm < a.d_row && gn < a.n_end)
+                        a.Wws[gm * a.d_col + gn] = fmaf(-acc[i][j][e], 1.0f / a.erow[gm], a.Wws[gm * a.d_col + gn]);
                 }
     }
 }
@@ -383,10 +417,10 @@ GPTQ_DEV void trail_issue(const TrailCopy& tc, int st) {
     });
 }
 
-struct TdFrags { bf16x8_t ah[2], al[2], bh[2], bl[2]; };
+struct TdFrags { f16x8_t ah[2], al[2], bh[2], bl[2]; };
 
 // B operand from a swizzled U tile (as trail_bfrag, with the chunk swizzle)
-GPTQ_DEV bf16x8_t td_bfrag(const uint16_t* tile, int nc0, int kk, int lane) {
+GPTQ_DEV f16x8_t td_bfrag(const uint16_t* tile, int nc0, int kk, int lane) {
     const int g = lane >> 4, j = lane & 15;
     const int n = nc0 + (g & 1) * 16 + 4 * (j & 3);
     const int k = kk + (g >> 1) * 8 + (j >> 2);
@@ -395,7 +429,7 @@ GPTQ_DEV bf16x8_t td_bfrag(const uint16_t* tile, int nc0, int kk, int lane) {
         (lds_v4i16_t*)(tile + k * TB + 8 * tswz(k, c) + 4 * half));
     const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_v4i16_t*)(tile + (k + 4) * TB + 8 * tswz(k + 4, c) + 4 * half));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // one wave's fragments for the 16-deep slice kk of a stage: A (rows wr * 64 + 32 i +
@@ -405,8 +439,8 @@ GPTQ_DEV void td_read(const uint16_t* stg, int kk, int wr, int wc, int lane, TdF
     for (int i = 0; i < 2; ++i) {
         const int m = wr * 64 + i * 32 + (lane & 31), q = (kk >> 3) + (lane >> 5);
         const int o = m * TK + 8 * (q ^ eswz(m));
-        f.ah[i] = *reinterpret_cast<const bf16x8_t*>(stg + o);
-        f.al[i] = *reinterpret_cast<const bf16x8_t*>(stg + TD_OPE + o);
+        f.ah[i] = *reinterpret_cast<const f16x8_t*>(stg + o);
+        f.al[i] = *reinterpret_cast<const f16x8_t*>(stg + TD_OPE + o);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -420,15 +454,15 @@ GPTQ_DEV void td_mfma(const TdFrags& f, f32x16_t (&acc)[2][2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[i], f.bh[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bh[j], acc[i][j], 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[i], f.bl[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bl[j], acc[i][j], 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.al[i], f.bh[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[i], f.bh[j], acc[i][j], 0, 0, 0);
     // 12 fragment reads of the next slice against 12 MFMAs: one each, in turn
     static_for<0, 12>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -477,19 +511,24 @@ __global__ __launch_bounds__(256, 1) void trail_dma_kernel(TrailArgs a) {
         });
     }
     __builtin_amdgcn_s_waitcnt(0);   // the trailing re-loads land before the workgroup ends
-    // W -= acc (whole tile): all loads first, then all stores
+    // W -= acc / es_row (whole tile): all loads first, then all stores
     float* wbase = a.Wws + (m0 + wr * 64 + 4 * (lane >> 5)) * a.d_col + n0 + wc * 64 + (lane & 31);
+    const float* ebase = a.erow + m0 + wr * 64 + 4 * (lane >> 5);
     auto off = [&](int i, int j, int e) { return (int64_t)(i * 32 + 8 * (e >> 2) + (e & 3)) * a.d_col + j * 32; };
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+        float inv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) inv[e] = 1.0f / ebase[i * 32 + 8 * (e >> 2) + (e & 3)];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             float old[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) old[e] = wbase[off(i, j, e)];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) wbase[off(i, j, e)] = old[e] - acc[i][j][e];
+            for (int e = 0; e < 16; ++e) wbase[off(i, j, e)] = fmaf(-acc[i][j][e], inv[e], old[e]);
         }
+    }
 }
 
 // Whole tiles on the direct-load kernel when the operands allow 16-byte loads at every
@@ -536,15 +575,23 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // regrouping of the rank-1 updates is exact in exact arithmetic, as for the
 // 128-column lazy blocks.
 
-// Workspace: fp32 working copy of W | E hi | E lo (bf16, d_row x QSB) | U hi | U lo
-// (bf16, d_col x d_col) | Ut hi | Ut lo (bf16, one transposed QSB x QSB diagonal block
-// of U per super-block).
+// Workspace: fp32 working copy of W | E hi | E lo (scaled fp16, d_row x QSB) | U hi |
+// U lo (scaled fp16, d_col x d_col) | Ut hi | Ut lo (scaled fp16, one transposed QSB x QSB
+// diagonal block of U per super-block) | es (fp32, d_row) | us (fp32, d_col).
 static size_t ut_bytes(int64_t d_col) { return (size_t)((d_col + QSB - 1) / QSB) * QSB * QSB * 2; }
 
 size_t quant_ws_bytes(int64_t d_row, int64_t d_col) {
     if (d_row <= 0 || d_col <= 0) return 0;
     return align256((size_t)d_row * d_col * sizeof(float)) + 2 * align256((size_t)d_row * QSB * 2) +
-           2 * align256((size_t)d_col * d_col * 2) + 2 * align256(ut_bytes(d_col));
+           2 * align256((size_t)d_col * d_col * 2) + 2 * align256(ut_bytes(d_col)) +
+           align256((size_t)d_row * sizeof(float)) + align256((size_t)d_col * sizeof(float));
+}
+
+// The split of a scaled value into fp16 hi + lo (hi = fp16(x), lo = fp16(x - hi); x - hi
+// is exact in fp32).
+GPTQ_DEV void split_f16(float x, uint16_t& h, uint16_t& l) {
+    h = f32_to_f16_bits(x);
+    l = f32_to_f16_bits(x - f16_bits_to_f32(h));
 }
 
 // The diagonal QSB x QSB blocks of U, split into bf16 hi + lo, zero past d, in the
@@ -553,7 +600,8 @@ size_t quant_ws_bytes(int64_t d_row, int64_t d_col) {
 // n % 16 + 16 ((k % 32) / 8), the eight values k = 32 s + 8 (l / 16) .. + 7 of column
 // n, so that a wave reads each operand with one contiguous 16-byte-per-lane load.
 // One workgroup per 64 x 64 tile, transposed through LDS.
-__global__ __launch_bounds__(256) void udt_kernel(const float* U, int64_t d, uint16_t* th, uint16_t* tl) {
+__global__ __launch_bounds__(256) void udt_kernel(const float* U, int64_t d, const float* us, uint16_t* th,
+                                                  uint16_t* tl) {
     __shared__ float t[64][65];
     const int b = blockIdx.y, tk = blockIdx.x / (QSB / 64), tn = blockIdx.x % (QSB / 64);
     const int64_t k0 = (int64_t)b * QSB + tk * 64, n0 = (int64_t)b * QSB + tn * 64;
@@ -564,7 +612,7 @@ __global__ __launch_bounds__(256) void udt_kernel(const float* U, int64_t d, uin
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = 4 * (tid & 15) + e;
-            t[r][c] = (k0 + r < d && n0 + c < d) ? U[(k0 + r) * d + n0 + c] : 0.f;
+            t[r][c] = (k0 + r < d && n0 + c < d) ? U[(k0 + r) * d + n0 + c] * us[k0 + r] : 0.f;
         }
     }
     __syncthreads();
@@ -578,9 +626,9 @@ __global__ __launch_bounds__(256) void udt_kernel(const float* U, int64_t d, uin
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float u0 = t[kb + 8 * h + 2 * e][n], u1 = t[kb + 8 * h + 2 * e + 1][n];
-            const uint16_t h0 = f32_to_bf16_bits(u0), h1 = f32_to_bf16_bits(u1);
-            const uint16_t l0 = f32_to_bf16_bits(u0 - bf16_bits_to_f32(h0));
-            const uint16_t l1 = f32_to_bf16_bits(u1 - bf16_bits_to_f32(h1));
+            uint16_t h0, h1, l0, l1;
+            split_f16(u0, h0, l0);
+            split_f16(u1, h1, l1);
             ph[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
             pl[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
@@ -589,35 +637,56 @@ __global__ __launch_bounds__(256) void udt_kernel(const float* U, int64_t d, uin
     }
 }
 
-// U -> bf16 hi + lo (hi = bf16(u), lo = bf16(u - hi)), once per call: every workgroup
-// of the trailing products reads the split instead of forming it again.  Eight values
-// per thread and step with 16-byte accesses when the arrays are aligned.
-__global__ void split_u_kernel(const float* U, int64_t n, uint16_t* hi, uint16_t* lo) {
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nth = (int64_t)gridDim.x * blockDim.x;
-    const bool vec = ((reinterpret_cast<uintptr_t>(U) & 15) == 0) && ((reinterpret_cast<uintptr_t>(hi) & 15) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(lo) & 15) == 0);
-    const int64_t n8 = vec ? n / 8 : 0;
-    for (int64_t i = tid; i < n8; i += nth) {
-        const f32x4_t a = reinterpret_cast<const f32x4_t*>(U)[2 * i], b = reinterpret_cast<const f32x4_t*>(U)[2 * i + 1];
+// U -> scaled fp16 hi + lo, once per call: every workgroup of the trailing products reads
+// the split instead of forming it again.  One workgroup per row k: the row's largest
+// magnitude m < 2^e (frexp) gives us_k = 2^(14 - e), so the scaled row lies in
+// (-2^14, 2^14) with its largest value at least 2^13 (U is upper triangular with a
+// positive diagonal, so m > 0; only the columns from k's 8-column piece on are read for
+// it, which also cover the zeros left of k).  Eight values per thread and step with
+// 16-byte accesses when the arrays are aligned.
+__global__ __launch_bounds__(256) void split_u_kernel(const float* U, int64_t d, uint16_t* hi, uint16_t* lo,
+                                                      float* us) {
+    __shared__ float red[4];
+    const int64_t k = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float* row = U + k * d;
+    uint16_t* hrow = hi + k * d;
+    uint16_t* lrow = lo + k * d;
+    const bool vec = (d & 7) == 0 && ((reinterpret_cast<uintptr_t>(U) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(hi) & 15) == 0) && ((reinterpret_cast<uintptr_t>(lo) & 15) == 0);
+    const int64_t n8 = vec ? d / 8 : 0;
+    float m = 0.f;
+    for (int64_t i = (k >> 3) + tid; i < n8; i += 256) {     // from the 8-column piece holding k
+        const f32x4_t a = reinterpret_cast<const f32x4_t*>(row)[2 * i], b = reinterpret_cast<const f32x4_t*>(row)[2 * i + 1];
+        m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))),
+                           fmaxf(fmaxf(fabsf(b[0]), fabsf(b[1])), fmaxf(fabsf(b[2]), fabsf(b[3])))));
+    }
+    for (int64_t c = (n8 > 0 ? 8 * n8 : k) + tid; c < d; c += 256) m = fmaxf(m, fabsf(row[c]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    (void)frexpf(m, &e);
+    const float sc = (m > 0.f && m <= 3.0e38f) ? ldexpf(1.f, 14 - e) : 1.f;
+    if (tid == 0) us[k] = sc;
+    for (int64_t i = tid; i < n8; i += 256) {
+        const f32x4_t a = reinterpret_cast<const f32x4_t*>(row)[2 * i], b = reinterpret_cast<const f32x4_t*>(row)[2 * i + 1];
         const float u[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         uint32_t ph[4], pl[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint16_t h0 = f32_to_bf16_bits(u[2 * e]), h1 = f32_to_bf16_bits(u[2 * e + 1]);
-            const uint16_t l0 = f32_to_bf16_bits(u[2 * e] - bf16_bits_to_f32(h0));
-            const uint16_t l1 = f32_to_bf16_bits(u[2 * e + 1] - bf16_bits_to_f32(h1));
-            ph[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            pl[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        for (int q = 0; q < 4; ++q) {
+            uint16_t h0, h1, l0, l1;
+            split_f16(u[2 * q] * sc, h0, l0);
+            split_f16(u[2 * q + 1] * sc, h1, l1);
+            ph[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            pl[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
-        reinterpret_cast<u32x4_t*>(hi)[i] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
-        reinterpret_cast<u32x4_t*>(lo)[i] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+        reinterpret_cast<u32x4_t*>(hrow)[i] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+        reinterpret_cast<u32x4_t*>(lrow)[i] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
     }
-    for (int64_t i = 8 * n8 + tid; i < n; i += nth) {
-        const float u = U[i];
-        const uint16_t h = f32_to_bf16_bits(u);
-        hi[i] = h;
-        lo[i] = f32_to_bf16_bits(u - bf16_bits_to_f32(h));
-    }
+    for (int64_t c = 8 * n8 + tid; c < d; c += 256) split_f16(row[c] * sc, hrow[c], lrow[c]);
 }
 
 static gptq_status launch_row_params(int bits, bool sym, bool fp4, bool mx, const float* Wws, int64_t d_row, int64_t d_col,
@@ -669,17 +738,20 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     uint16_t* Uthi = reinterpret_cast<uint16_t*>(wp);
     wp += align256(ut_bytes(d_col));
     uint16_t* Utlo = reinterpret_cast<uint16_t*>(wp);
+    wp += align256(ut_bytes(d_col));
+    float* es = reinterpret_cast<float*>(wp);
+    wp += align256((size_t)d_row * sizeof(float));
+    float* us = reinterpret_cast<float*>(wp);
     const int G = p.group_size;                 // -1: per tensor, 0: per row
     const int n_groups = (G <= 0) ? 1 : (int)(d_col / G);
 
     fill_i32(info, 1, 0, s);
     GPTQ_LAUNCH_CHECK();
-    const int64_t n = d_row * d_col;
-    const unsigned cgrid = (unsigned)std::min<int64_t>((n / 8 + 255) / 256 + 1, 4096);
+    const unsigned cgrid = (unsigned)d_row;
     switch (w_dtype) {
-        case GPTQ_F32: convert_kernel<GPTQ_F32><<<cgrid, 256, 0, s>>>(W, n, Wws, info); break;
-        case GPTQ_BF16: convert_kernel<GPTQ_BF16><<<cgrid, 256, 0, s>>>(W, n, Wws, info); break;
-        case GPTQ_F16: convert_kernel<GPTQ_F16><<<cgrid, 256, 0, s>>>(W, n, Wws, info); break;
+        case GPTQ_F32: convert_kernel<GPTQ_F32><<<cgrid, 256, 0, s>>>(W, d_col, Wws, es, info); break;
+        case GPTQ_BF16: convert_kernel<GPTQ_BF16><<<cgrid, 256, 0, s>>>(W, d_col, Wws, es, info); break;
+        case GPTQ_F16: convert_kernel<GPTQ_F16><<<cgrid, 256, 0, s>>>(W, d_col, Wws, es, info); break;
         default: return GPTQ_ERR_UNSUPPORTED;
     }
     GPTQ_LAUNCH_CHECK();
@@ -696,14 +768,13 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     }
     SweepArgs sa;
     {
-        const int64_t nu = d_col * d_col;
-        const unsigned ug = (unsigned)std::min<int64_t>((nu / 8 + 255) / 256 + 1, 4096);
-        split_u_kernel<<<ug, 256, 0, s>>>(U, nu, Uhi, Ulo);
+        split_u_kernel<<<(unsigned)d_col, 256, 0, s>>>(U, d_col, Uhi, Ulo, us);
         GPTQ_LAUNCH_CHECK();
-        udt_kernel<<<dim3((QSB / 64) * (QSB / 64), (unsigned)((d_col + QSB - 1) / QSB)), 256, 0, s>>>(U, d_col, Uthi,
-                                                                                                    Utlo);
+        udt_kernel<<<dim3((QSB / 64) * (QSB / 64), (unsigned)((d_col + QSB - 1) / QSB)), 256, 0, s>>>(U, d_col, us,
+                                                                                                    Uthi, Utlo);
         GPTQ_LAUNCH_CHECK();
     }
+    sa.es = es; sa.us = us;
     sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U;
     sa.codes = codes; sa.code_ld = (p.bits <= 4) ? d_col / 2 : d_col;
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
@@ -724,7 +795,7 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         st = sweep_launch(sa, s);
         if (st != GPTQ_OK) return st;
         // everything after the super-block, K = s1 - s0
-        TrailArgs tb{Wws, d_row, d_col, Ehi, Elo, QSB, Uhi, Ulo, s0, (int)(s1 - s0), s1, d_col, 0};
+        TrailArgs tb{Wws, d_row, d_col, Ehi, Elo, QSB, Uhi, Ulo, es, s0, (int)(s1 - s0), s1, d_col, 0};
         if ((st = trail(tb, s)) != GPTQ_OK) return st;
     }
     return GPTQ_OK;

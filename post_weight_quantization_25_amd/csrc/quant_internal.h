@@ -52,12 +52,16 @@ constexpr int QSB = 512;
 struct SweepArgs {
     const float* Wws; int64_t d_row, d_col;
     const float* U;                 // fp32 U (the diagonal blocks for the sweep)
-    // this super-block's diagonal QSB x QSB part of U split into bf16 hi + lo, zero past
-    // d_col, in MFMA B-operand order (the updates inside the super-block)
+    // this super-block's diagonal QSB x QSB part of U, row k scaled by us_k and split into
+    // fp16 hi + lo, zero past d_col, in MFMA B-operand order (the updates inside the
+    // super-block)
     const uint16_t* Uthi; const uint16_t* Utlo;
     int64_t s0, s1;                 // the super-block: columns s0 .. s1 - 1 (s1 - s0 <= QSB)
-    uint16_t* Ehi; uint16_t* Elo;   // the super-block's errors as bf16 hi + lo (hi = bf16(e),
-    int64_t lde;                    // lo = bf16(e - hi)): d_row x QSB, row stride lde
+    uint16_t* Ehi; uint16_t* Elo;   // the super-block's errors e, scaled to x = e es_r / us_k, as
+    int64_t lde;                    // fp16 hi + lo (hi = fp16(x), lo = fp16(x - hi)): d_row x QSB,
+                                    // row stride lde
+    const float* es;                // es_r per row and us_k per column (exact powers of two)
+    const float* us;
     uint8_t* codes; int64_t code_ld;
     uint16_t* scales; uint16_t* zeros; int n_groups;
     int32_t* info;

@@ -18,13 +18,14 @@
 // coefficients of the next step with two 16-byte LDS reads (prefetched one step
 // ahead).  The quantization error of column j is broadcast along the row with
 // DPP row_newbcast; group min/max use DPP butterfly reductions.
-// After a block, its errors E (16 x 128, bf16 hi + lo, staged in LDS, then held in
-// registers) update the rest of the super-block in LDS, W[:, later] -= E U[block,
-// later], on v_mfma_f32_16x16x32_bf16 with three products (hi hi + hi lo + lo hi, fp32
-// accumulation); the U operands come straight from global memory in registers, from
-// the transposed bf16 copy of the super-block's diagonal block of U (eight consecutive
-// k of one column per 16-byte load), loaded while the block's steps run.  Rows are
-// independent, so no other workgroup is involved.
+// After a block, its errors E (16 x 128, scaled by powers of two and split into fp16
+// hi + lo, staged in LDS, then held in registers) update the rest of the super-block in
+// LDS, W[:, later] -= E U[block, later], on v_mfma_f32_16x16x32_f16 with three products
+// (hi hi + hi lo + lo hi, fp32 accumulation, then divided by the row's scale); the U
+// operands come straight from global memory in registers, from the transposed scaled
+// fp16 copy of the super-block's diagonal block of U (eight consecutive k of one column
+// per 16-byte load), loaded while the block's steps run.  Rows are independent, so no
+// other workgroup is involved.
 
 #include <utility>
 
@@ -65,14 +66,14 @@ GPTQ_DEV float row_max(float v) {
 // the diagonal block (always QSB x QSB, zero past d_col, so no bounds checks): one
 // contiguous 1 KB piece per wave and operand.
 constexpr int NKK = QB / 32;
-struct UChunk { bf16x8_t h[NKK], l[NKK]; };
+struct UChunk { f16x8_t h[NKK], l[NKK]; };
 
 GPTQ_DEV void load_uchunk(const SweepArgs& a, int64_t b0, int64_t n0, int wave, int lane, UChunk& u) {
     const int64_t o = ((((n0 - a.s0) >> 4) + wave) * (QSB / 32) + ((b0 - a.s0) >> 5)) * 512 + 8 * lane;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-        u.h[kk] = *reinterpret_cast<const bf16x8_t*>(a.Uthi + o + 512 * kk);
-        u.l[kk] = *reinterpret_cast<const bf16x8_t*>(a.Utlo + o + 512 * kk);
+        u.h[kk] = *reinterpret_cast<const f16x8_t*>(a.Uthi + o + 512 * kk);
+        u.l[kk] = *reinterpret_cast<const f16x8_t*>(a.Utlo + o + 512 * kk);
     }
 }
 
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     // E split, staged; rows padded by 16 bytes so that the 16 rows of an operand read
     // fall on distinct banks
     __shared__ __attribute__((aligned(16))) uint16_t ehs[SROWS][QB + 8], els[SROWS][QB + 8];
+    __shared__ float einv[SROWS];                                      // 1 / es of the rows
     __shared__ int bad_any;
 
     const int tid = threadIdx.x;
@@ -132,6 +134,8 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     const int G = a.group;
     const float fqmin = (float)a.qmin, fqmax = (float)a.qmax, fzoff = (float)a.zoff;
     if (tid == 0) bad_any = 0;
+    const float es_row = rv ? a.es[row] : 1.f;
+    if (q == 0) einv[rl] = 1.0f / es_row;
 
     // the super-block's W for the workgroup's rows: thread t loads row t / 16,
     // columns 4 (t % 16) + 64 m (16-byte loads when rows are aligned)
@@ -194,6 +198,10 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
         if (bn + UT_N * ch < a.s1) load_uchunk(a, b0, bn + UT_N * ch, wave, lane, uch[ch]);
+    // U's row scales of this lane's columns (for the scaled errors), also in flight
+    float usc[SSLOTS];
+#pragma unroll
+    for (int i = 0; i < SSLOTS; ++i) usc[i] = (FULL || SL * i + q < nb) ? a.us[b0 + SL * i + q] : 1.f;
     // the block's W from LDS (updated by the earlier blocks of the super-block); the
     // barrier before the U staging of the first block orders the W stores above
     if (b0 == a.s0) lds_barrier();
@@ -330,16 +338,18 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     // a non-finite weight, scale or error shows up in the block's errors
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) bad = bad || !(fabsf(e[i]) <= 3.0e38f);
-    // the trailing update multiplies on bf16 MFMA with a three-term split: the split
-    // is formed here once (hi = bf16(e), lo = bf16(e - hi)) instead of in every
-    // workgroup of the product; it and the codes are staged in LDS and written as
-    // whole 16- / 4-byte pieces
+    // the trailing update multiplies on fp16 MFMA with a three-term split of the scaled
+    // errors x = e es_r / us_k: the split is formed here once (hi = fp16(x), lo =
+    // fp16(x - hi)) instead of in every workgroup of the product; it and the codes are
+    // staged in LDS and written as whole 16- / 4-byte pieces
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) {
         const int c = SL * i + q;
-        const uint16_t h = f32_to_bf16_bits(e[i]);
+        const float x = (c < nb) ? e[i] * (es_row / usc[i]) : 0.f;
+        bad = bad || !(fabsf(x) < 65504.f);
+        const uint16_t h = f32_to_f16_bits(x);
         ehs[rl][c] = h;
-        els[rl][c] = f32_to_bf16_bits(e[i] - bf16_bits_to_f32(h));
+        els[rl][c] = f32_to_f16_bits(x - f16_bits_to_f32(h));
         cl[rl][c] = (uint8_t)cv[i];
     }
     if (bad && rv) atomicOr(&bad_any, 1);
@@ -390,13 +400,16 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     // U at a time; wave w updates 16 rows x 16 columns of each chunk (its own columns of
     // Wl, so the chunks need no barrier between them)
     if (bn < a.s1) {
-        bf16x8_t eh[NKK], el[NKK];
+        f16x8_t eh[NKK], el[NKK];
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const int mr = lane & 15, ka = 32 * kk + 8 * (lane >> 4);
-            eh[kk] = *reinterpret_cast<const bf16x8_t*>(&ehs[mr][ka]);
-            el[kk] = *reinterpret_cast<const bf16x8_t*>(&els[mr][ka]);
+            eh[kk] = *reinterpret_cast<const f16x8_t*>(&ehs[mr][ka]);
+            el[kk] = *reinterpret_cast<const f16x8_t*>(&els[mr][ka]);
         }
+        float ri[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ri[r] = einv[4 * (lane >> 4) + r];
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
             const int64_t n0 = bn + UT_N * ch;
@@ -404,14 +417,14 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
             f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eh[kk], uch[ch].h[kk], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eh[kk], uch[ch].l[kk], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(el[kk], uch[ch].h[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(eh[kk], uch[ch].h[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(eh[kk], uch[ch].l[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(el[kk], uch[ch].h[kk], acc, 0, 0, 0);
             }
             // D layout: lane l holds column l % 16, rows 4 (l / 16) .. + 3
             const int nc = (int)(n0 - a.s0) + 16 * wave + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Wl[4 * (lane >> 4) + r][nc] -= acc[r];
+            for (int r = 0; r < 4; ++r) Wl[4 * (lane >> 4) + r][nc] = fmaf(-acc[r], ri[r], Wl[4 * (lane >> 4) + r][nc]);
         }
         lds_barrier();   // the next block reads these columns of Wl
     }

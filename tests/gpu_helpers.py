@@ -235,3 +235,29 @@ def check_recon(H, W, What_gpu, rep, log_fn=None):
 def recon_rows(H: np.ndarray, W: np.ndarray, What: np.ndarray) -> np.ndarray:
     D = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
     return 0.5 * np.einsum("ij,jk,ik->i", D, H, D)
+
+
+def u_residual_ratio(U, H, js, percdamp=0.01, step=2048):
+    """Property check of an fp32 factor U of (H + lambda I)^-1 = U^T U without factoring:
+    r_j = U^T U (H + lambda I) e_j - e_j on the columns js, in fp64, against the
+    componentwise bound of rounding an exact factor to fp32,
+    |r_j| <= 2 * 2^-24 |U|^T |U| |(H + lambda I) e_j|.  Returns max |r| / (4 x bound) (at
+    most 1 passes) and max |r|.  U and H (d x d, fp32) are read in row blocks of ``step``."""
+    d = H.shape[0]
+    js = np.asarray(js)
+    lam = percdamp * float(np.mean(np.diag(H).astype(np.float64)))
+    V = H[:, js].astype(np.float64)
+    V[js, np.arange(js.size)] += lam
+    a, ab = np.zeros((d, js.size)), np.zeros((d, js.size))
+    for r0 in range(0, d, step):
+        Ub = U[r0:r0 + step].astype(np.float64)
+        a[r0:r0 + step] = Ub @ V
+        ab[r0:r0 + step] = np.abs(Ub) @ np.abs(V)
+    res, bnd = np.zeros((d, js.size)), np.zeros((d, js.size))
+    for r0 in range(0, d, step):
+        Ub = U[r0:r0 + step].astype(np.float64)
+        res += Ub.T @ a[r0:r0 + step]
+        bnd += np.abs(Ub).T @ ab[r0:r0 + step]
+    res[js, np.arange(js.size)] -= 1.0
+    bound = 2.0 * 2.0 ** -24 * bnd
+    return float(np.max(np.abs(res) / (4.0 * bound + 1e-300))), float(np.max(np.abs(res)))

@@ -5,7 +5,7 @@ same row.  The "other" results here are the oracle's own runs with a decision fi
 import numpy as np
 
 import synth
-from gpu_helpers import assert_parity, check_recon, tie_consistent_parity
+from gpu_helpers import assert_parity, check_recon, tie_consistent_parity, u_residual_ratio
 from oracle import gptq_oracle as o
 
 
@@ -96,3 +96,19 @@ def test_group_scale_tie_passes_and_zero_away_from_tie_fails():
     bad = o.gptq_blocked(W, U, p, forced={("g", int(r), int(k)): (s16, int(ref.zeros[r, k]) + 1)})
     rep = tie_consistent_parity(*_as_gpu(bad, p), W, U, p, tie_window=1e-3, ref=ref)
     assert rep["unjustified"] and rep["unjustified"][0][1] == "group"
+
+
+def test_u_residual_check_passes_rounded_factor_and_catches_a_bad_tile():
+    """The property check used where the oracle cannot factor: an exact factor rounded to
+    fp32 passes; a 64 x 64 tile 1% off, or one row's tail 0.1% off, fails."""
+    L = synth.scaled(synth.config_layers(5)[1], 64, 1024, 4096)
+    X = np.concatenate([synth.x_as_f64(c) for c in synth.x_chunks(L)])
+    H = o.hessian([X]).astype(np.float32)
+    U, _ = o.prepare_u(H.astype(np.float64), 0.01)
+    U32 = U.astype(np.float32)
+    js = [0, 7, 512, 1023]
+    assert u_residual_ratio(U32, H, js, step=256)[0] <= 1.0
+    bad = U32.copy(); bad[64:128, 512:576] *= 1.01
+    assert u_residual_ratio(bad, H, js, step=256)[0] > 1.0
+    bad = U32.copy(); bad[700, 700:] *= 1.001
+    assert u_residual_ratio(bad, H, js, step=256)[0] > 1.0
