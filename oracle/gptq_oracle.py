@@ -40,7 +40,9 @@ listing were lost in extraction; the readings used here are:
   so the decision is taken as close to exact arithmetic as fp64 allows); the
   zero point likewise, Z = qmin - rne(min / S16) in fp64;
 * stored codes are unsigned: u = q (asymmetric) or q + 2^(b-1) (symmetric), stored
-  zero z = Z or 2^(b-1); dequantisation is fl32(S16) * fl32(u - z).
+  zero z = Z or 2^(b-1); dequantisation is fl32(S16) * fl32(u - z);
+* 3-bit codes are stored as a bitstream per row (eight codes in three bytes, lowest bit
+  first), the same first-value-lowest order as the guide's two int4 values per byte.
 """
 from __future__ import annotations
 
@@ -567,15 +569,28 @@ def rtn(W: np.ndarray, p: Params) -> Result:
 # Storage format and dequantisation.
 
 def pack(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Two codes per byte for bits <= 4: byte k = u[2k] | u[2k+1] << 4 (first value in
-    the low nibble); one code per byte for 8 bits.
+    """Codes of a row into bytes.  bits == 4: two codes per byte, byte k = u[2k] | u[2k+1] << 4
+    (first value in the low nibble); bits == 3: a bitstream of the row, code c in stream
+    bits 3c .. 3c + 2 (lowest bit first) and stream bit i in bit i % 8 of byte i // 8, so
+    eight codes fill three bytes; bits == 8: one code per byte.
 
-    [Quantization concepts guide, "Data types - int8 and int4": two int4 values packed
-     in one byte, the first in the low 4 bits and the second in the high 4 bits]
+    [Quantization concepts guide, "Data types - int8 and int4": sub-byte values are packed
+     into bytes, two int4 values per byte with the first in the low 4 bits and the second
+     in the high 4 bits; the 3-bit stream continues the same first-value-lowest order]
     """
     codes = np.asarray(codes, dtype=np.uint8)
     if bits == 8:
         return codes.copy()
+    if bits == 3:
+        d = codes.shape[-1]
+        if d % 8:
+            raise ValueError("3-bit rows hold a multiple of 8 codes")
+        out = np.zeros(codes.shape[:-1] + (3 * d // 8,), dtype=np.uint8)
+        for c in range(d):
+            for b in range(3):
+                i = 3 * c + b
+                out[..., i // 8] |= (((codes[..., c] >> b) & 1) << (i % 8)).astype(np.uint8)
+        return out
     if codes.shape[-1] % 2:
         raise ValueError("odd number of columns")
     lo = codes[..., 0::2] & 0xF
@@ -584,9 +599,18 @@ def pack(codes: np.ndarray, bits: int) -> np.ndarray:
 
 
 def unpack(packed: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of ``pack``: the row's codes from its bytes."""
     packed = np.asarray(packed, dtype=np.uint8)
     if bits == 8:
         return packed.copy()
+    if bits == 3:
+        d = packed.shape[-1] * 8 // 3
+        out = np.zeros(packed.shape[:-1] + (d,), dtype=np.uint8)
+        for c in range(d):
+            for b in range(3):
+                i = 3 * c + b
+                out[..., c] |= (((packed[..., i // 8] >> (i % 8)) & 1) << b).astype(np.uint8)
+        return out
     out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
     out[..., 0::2] = packed & 0xF
     out[..., 1::2] = packed >> 4

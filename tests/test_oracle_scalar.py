@@ -178,3 +178,31 @@ def test_zero_point_decided_from_the_exact_quotient():
     # exactly on the tie, -2.5 goes to the even -2: Z = 2
     S, S16, Z, zt = o.group_params(np.array([[-0.625, 0.0, 3.125]]), p)
     assert zt[0] == -2.5 and Z[0] == 2
+
+
+def test_int3_bitstream_hand_example():
+    g = _load("int3_bitstream_example.json")
+    b = o.pack(np.array([g["codes"]]), 3)
+    assert b.shape == (1, 3) and list(b[0]) == g["bytes"]
+    assert list(o.unpack(b, 3)[0]) == g["codes"]
+
+
+def test_int3_bitstream_every_position_and_value():
+    """Every residue of the eight-codes-in-three-bytes cycle: code value v alone at
+    position p of an 8-code group lands in bits 3p .. 3p + 2 of the group's three bytes
+    read as one little-endian integer, and the stream round-trips."""
+    for p in range(8):
+        for v in range(8):
+            codes = np.zeros((1, 16), dtype=np.uint8)
+            codes[0, 8 + p] = v                     # the second group of the row
+            b = o.pack(codes, 3)
+            assert b.shape == (1, 6) and not b[0, :3].any()
+            assert int.from_bytes(bytes(b[0, 3:]), "little") == v << (3 * p)
+            assert np.array_equal(o.unpack(b, 3), codes)
+    rng = np.random.default_rng(4)
+    u = rng.integers(0, 8, size=(5, 64)).astype(np.uint8)
+    assert np.array_equal(o.unpack(o.pack(u, 3), 3), u)
+    assert o.pack(u, 3).nbytes == u.size * 3 // 8     # 0.375 byte per 3-bit weight
+    # every 3-byte pattern is a valid stream of eight codes
+    allb = rng.integers(0, 256, size=(7, 3)).astype(np.uint8)
+    assert np.array_equal(o.pack(o.unpack(allb, 3), 3), allb)
