@@ -304,7 +304,7 @@ def layer_bench(g, L, dev, steps: int, warmup: int, damp: float = 0.01):
     p = g.make_params(L.bits, L.group_size, L.sym)
     ws_q = torch.empty(g.quantize_workspace_size(r, d, p), dtype=torch.uint8, device=dev)
     ng = 1 if L.group_size == 0 else d // L.group_size
-    q = g.Quantized(torch.empty((r, d // 2 if L.bits <= 4 else d), dtype=torch.uint8, device=dev),
+    q = g.Quantized(torch.empty((r, g.code_bytes(L.bits, d)), dtype=torch.uint8, device=dev),
                     torch.empty((r, ng), dtype=torch.float16, device=dev),
                     torch.empty((r, ng), dtype=torch.float16, device=dev),
                     torch.zeros(1, dtype=torch.int32, device=dev), L.bits, L.group_size, d)

@@ -87,7 +87,8 @@ gptq_status gptq_context_destroy(gptq_context* ctx);
 
 /* Quantizer settings (host struct). */
 typedef struct {
-    int32_t bits;        /* 3 or 4 (codes packed two per byte) or 8 (one per byte) */
+    int32_t bits;        /* 3 (codes as a bitstream, eight in three bytes; d_col a multiple
+                            of 8), 4 (two per byte) or 8 (one per byte) */
     int32_t group_size;  /* weights per scale/zero group along a row; must divide
                             block_size and d_col; 0 = one group per row; -1 = one range
                             for the whole matrix (per tensor: every row stores the same
@@ -182,8 +183,12 @@ gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float per
  *  U          d_col x d_col fp32 from gptq_prepare_hinv (upper triangle read; the
  *             strictly lower triangle of each 128x128 diagonal block must be 0).
  *  p          host pointer to the settings.
- *  codes      bits <= 4: d_row x d_col/2 bytes, column 2k in the low nibble of byte k,
+ *  codes      bits == 4: d_row x d_col/2 bytes, column 2k in the low nibble of byte k,
  *             column 2k+1 in the high nibble (d_col must be even);
+ *             bits == 3: d_row x 3 d_col/8 bytes, each row a bitstream with column c in
+ *             stream bits 3c .. 3c+2 (lowest bit first) and stream bit i in bit i % 8
+ *             of byte i / 8 (d_col must be a multiple of 8; the concepts guide's
+ *             first-value-lowest order of "Data types - int8 and int4" continued);
  *             bits == 8: d_row x d_col bytes.  Codes are unsigned (see gptq_params).
  *  scales_f16 d_row x n_groups fp16 bit patterns (S16); n_groups = d_col/group_size,
  *             or 1 when group_size is 0 or -1.
@@ -302,7 +307,8 @@ gptq_status gptq_obq_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int
  * Source: Quantization concepts guide, "Mapping values to fewer bits"
  * (x ~= S (q - Z)) and "Data types - int8 and int4" (unpacking two codes per byte).
  *
- *  codes, scales_f16, zeros_f16   as written by gptq_quantize_layer.
+ *  codes, scales_f16, zeros_f16   as written by gptq_quantize_layer (bits 3: the 3-bit
+ *             stream, d_col a multiple of 8, else GPTQ_ERR_INVALID_ARG).
  *  W_out      d_row x d_col, dtype out_dtype.
  */
 gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16,
@@ -333,18 +339,20 @@ gptq_status gptq_dequantize_e2m1(const uint8_t* codes, const uint16_t* scales_f1
  * fewer bits" (x ~= S (q - Z)) and "Data types - int8 and int4".
  *
  *  codes, scales_f16, zeros_f16   as written by gptq_quantize_layer (bits, group_size
- *             as there: 3 or 4 two per byte, 8 one per byte; group 0 = per row).
+ *             as there: 3 the 3-bit stream, 4 two per byte, 8 one per byte; group 0 = per
+ *             row).
  *  x          n_tokens x d_col, row pitch ldx >= d_col elements, dtype x_dtype.
  *  y          n_tokens x d_row (row pitch d_row), dtype y_dtype; written, not read.
- * Any even d_col works; d_col a multiple of 32 with 16-byte aligned code rows and x
- * rows takes the fast kernels: a single token streams the codes with fp32 multiply-adds;
- * from two tokens on, packed codes with bf16/f16 x and d_col and the group width
- * multiples of 128 go to the matrix cores (u - z decoded once per 16 tokens, exact in
+ * Any even d_col works (3-bit: a multiple of 8); d_col a multiple of 32 with 16-byte
+ * aligned code rows (3-bit: 4-byte) and x rows takes the fast kernels: a single token
+ * streams the codes with fp32 multiply-adds; from two tokens on, 3- or 4-bit codes with
+ * bf16/f16 x and d_col and the group width multiples of 128 go to the matrix cores (u - z decoded once per 16 tokens, exact in
  * x's 16-bit type for integer zeros, else completed by a second product of the
  * remainder), otherwise the codes are streamed once per four tokens.
  * Integer grids only (a layer on the E2M1 grid is dequantized with gptq_dequantize_e2m1).
- * Errors: negative sizes, bad dtypes or group width -> GPTQ_ERR_INVALID_ARG; bits not
- * 3/4/8 -> GPTQ_ERR_UNSUPPORTED; zero sizes are a no-op.
+ * Errors: negative sizes, bad dtypes or group width, or bits 3 with d_col not a multiple
+ * of 8 -> GPTQ_ERR_INVALID_ARG; bits not 3/4/8 -> GPTQ_ERR_UNSUPPORTED; zero sizes are a
+ * no-op.
  */
 gptq_status gptq_quantized_linear(const uint8_t* codes, const uint16_t* scales_f16,
                                   const uint16_t* zeros_f16, int64_t d_row, int64_t d_col,

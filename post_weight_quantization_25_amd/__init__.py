@@ -212,7 +212,7 @@ def prepare_hinv(H: torch.Tensor, percdamp: float = 0.01, U: torch.Tensor | None
 
 @dataclass
 class Quantized:
-    codes: torch.Tensor      # uint8, d_row x d_col/2 (bits <= 4) or d_row x d_col
+    codes: torch.Tensor      # uint8, d_row x code_bytes(bits, d_col)
     scales: torch.Tensor     # float16, d_row x n_groups
     zeros: torch.Tensor      # float16, d_row x n_groups (integer values)
     info: torch.Tensor       # int32 device scalar
@@ -220,6 +220,12 @@ class Quantized:
     group_size: int
     d_col: int
     fp4: bool = False        # codes on the E2M1 grid (sign bit 8 | magnitude index)
+
+
+def code_bytes(bits: int, d_col: int) -> int:
+    """Bytes of one row of stored codes: the 3-bit stream (eight codes in three bytes),
+    two 4-bit codes per byte, or one byte per code."""
+    return d_col // 8 * 3 if bits == 3 else d_col // 2 if bits == 4 else d_col
 
 
 def make_params(bits=4, group_size=128, sym=False, block_size=128, fp4=False, mx=False) -> Params:
@@ -242,7 +248,7 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: 
     p = make_params(bits, group_size, sym, block_size, fp4, mx)
     n_groups = 1 if group_size <= 0 else max(1, d_col // group_size)
     if out is None:
-        cb = d_col // 2 if bits <= 4 else d_col
+        cb = code_bytes(bits, d_col)
         out = Quantized(torch.empty((d_row, cb), dtype=torch.uint8, device=W.device),
                         torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
                         torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
@@ -283,7 +289,7 @@ def obq_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, sym: bool = False
     d_row, d_col = W.shape
     p = make_params(bits, 0, sym)
     if out is None:
-        out = Quantized(torch.empty((d_row, d_col // 2 if bits <= 4 else d_col), dtype=torch.uint8, device=W.device),
+        out = Quantized(torch.empty((d_row, code_bytes(bits, d_col)), dtype=torch.uint8, device=W.device),
                         torch.empty((d_row, 1), dtype=torch.float16, device=W.device),
                         torch.empty((d_row, 1), dtype=torch.float16, device=W.device),
                         torch.zeros(1, dtype=torch.int32, device=W.device), bits, 0, d_col)
@@ -343,7 +349,7 @@ def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = Fal
         for _, W in pairs:
             d_row, d_col = W.shape
             n_groups = 1 if group_size <= 0 else max(1, d_col // group_size)
-            outs.append(Quantized(torch.empty((d_row, d_col // 2 if bits <= 4 else d_col), dtype=torch.uint8, device=dev),
+            outs.append(Quantized(torch.empty((d_row, code_bytes(bits, d_col)), dtype=torch.uint8, device=dev),
                                   torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),
                                   torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),
                                   torch.zeros(1, dtype=torch.int32, device=dev), bits, group_size, d_col))

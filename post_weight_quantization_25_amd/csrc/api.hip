@@ -20,6 +20,7 @@ static gptq_status check_params(const gptq_params* p, int64_t d_col) {
         if (p->group_size != 32 && p->group_size != 64 && p->group_size != 128) return GPTQ_ERR_UNSUPPORTED;
     }
     if (p->bits <= 4 && (d_col & 1)) return GPTQ_ERR_INVALID_ARG;
+    if (p->bits == 3 && (d_col & 7)) return GPTQ_ERR_INVALID_ARG;   // 3-bit rows: whole 8-code groups
     return GPTQ_OK;
 }
 
@@ -170,6 +171,7 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, co
     if (bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_UNSUPPORTED;
     if (group_size > 0 && d_col % group_size != 0) return GPTQ_ERR_INVALID_ARG;
     if (bits <= 4 && (d_col & 1)) return GPTQ_ERR_INVALID_ARG;
+    if (bits == 3 && (d_col & 7)) return GPTQ_ERR_INVALID_ARG;
     if (d_row == 0 || d_col == 0) return GPTQ_OK;
     if (!codes || !scales_f16 || !zeros_f16 || !W_out) return GPTQ_ERR_INVALID_ARG;
     if (d_row > 65535) return GPTQ_ERR_UNSUPPORTED;
@@ -200,6 +202,7 @@ gptq_status gptq_quantized_linear(const uint8_t* codes, const uint16_t* scales_f
     if (bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_UNSUPPORTED;
     if (group_size > 0 && d_col % group_size != 0) return GPTQ_ERR_INVALID_ARG;
     if (bits <= 4 && (d_col & 1)) return GPTQ_ERR_INVALID_ARG;
+    if (bits == 3 && (d_col & 7)) return GPTQ_ERR_INVALID_ARG;
     if (d_row == 0 || d_col == 0 || n_tokens == 0) return GPTQ_OK;
     if (!codes || !scales_f16 || !zeros_f16 || !x || !y || ldx < d_col) return GPTQ_ERR_INVALID_ARG;
     if (d_row > 2147483647LL / 64 || d_col > 2147483647LL / 64) return GPTQ_ERR_UNSUPPORTED;

@@ -107,3 +107,12 @@ GPTQ_DEV uint32_t lds_addr(const uint16_t* p) {
     do {                                                      \
         if (hipGetLastError() != hipSuccess) return GPTQ_ERR_HIP; \
     } while (0)
+
+// Codes of the 3-bit stream: eight codes in three bytes, code c in stream bits 3c .. 3c+2
+// (lowest bit first), stream bit i in bit i % 8 of byte i / 8.  The 24 bits of an
+// 8-code group as one integer (little-endian bytes), and code e of it.
+GPTQ_DEV uint32_t load_u24(const uint8_t* p) {
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+}
+GPTQ_DEV uint32_t code3(uint32_t g24, int e) { return (g24 >> (3 * e)) & 7u; }
+

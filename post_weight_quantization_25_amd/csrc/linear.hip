@@ -6,7 +6,8 @@
 // stored tokens x d_col the output is X W^T) and its results on inference with the
 // packed weights; Quantization concepts guide, "Mapping values to fewer bits"
 // (x ~= S (q - Z)) and "Data types - int8 and int4" (two int4 values per byte, the
-// first in the low nibble).
+// first in the low nibble; 3-bit codes as a stream, eight in three bytes, the first in
+// the lowest bits).
 //
 // Decode-shaped (one to a few tokens, linear_kernel): the product streams the codes
 // once and is bound by their bytes.  A workgroup of four waves owns 4 LROWS rows
@@ -84,9 +85,26 @@ GPTQ_DEV float wave_sum(float v) {
     return v;
 }
 
-// Fast path: d_col a multiple of 32, rows of codes and x 16-byte aligned.  NT tokens per
-// pass; PACKED: two codes per byte (16 bytes per chunk), else one per byte (32 bytes).
-template <bool PACKED, int NT, gptq_dtype XT, gptq_dtype YT>
+// Code e (0 .. 31) of a 32-column chunk held in words w: CB = 4, word 2 (e / 8) + (e & 1)
+// holds column e in byte (e & 7) / 2 (the nibbles split into even and odd bytes); CB = 3,
+// the 96-bit stream of the chunk, code e in bits 3e .. 3e + 2; CB = 8, byte e & 3 of word
+// e / 4.
+template <int CB>
+GPTQ_DEV uint32_t chunk_code(const uint32_t* w, int e) {
+    if constexpr (CB == 3) {
+        const int bit = 3 * e, k = bit >> 5, sh = bit & 31;
+        return sh <= 29 ? (w[k] >> sh) & 7u : ((w[k] >> sh) | (w[k + 1] << (32 - sh))) & 7u;
+    } else if constexpr (CB == 4) {
+        return (w[2 * (e >> 3) + (e & 1)] >> (8 * ((e & 7) >> 1))) & 0xFFu;
+    } else {
+        return (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+    }
+}
+
+// Fast path: d_col a multiple of 32, rows of codes 16-byte (3-bit: 4-byte) and of x
+// 16-byte aligned.  NT tokens per pass; CB = code bits as stored: 4 (two codes per byte,
+// 16 bytes per chunk), 3 (the 3-bit stream, 12 bytes per chunk) or 8 (32 bytes).
+template <int CB, int NT, gptq_dtype XT, gptq_dtype YT>
 __global__ __launch_bounds__(64 * LWAVES) void linear_kernel(LinArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r0 = ((int64_t)blockIdx.x * LWAVES + wave) * LROWS;
@@ -120,7 +138,11 @@ __global__ __launch_bounds__(64 * LWAVES) void linear_kernel(LinArgs a) {
             for (int i = 0; i < LROWS; ++i) {
                 const int64_t r = (r0 + i < a.d_row) ? r0 + i : a.d_row - 1;
                 const uint8_t* crow = a.codes + r * a.code_ld;
-                if constexpr (PACKED) {
+                if constexpr (CB == 3) {
+                    const uint32_t* w = reinterpret_cast<const uint32_t*>(crow + c0 / 8 * 3);
+#pragma unroll
+                    for (int e = 0; e < 3; ++e) cw[i][e] = w[e];
+                } else if constexpr (CB == 4) {
                     // nibbles 0, 2, 4, .. and 1, 3, 5, .. of a word as bytes
                     const u32x4_t w = *reinterpret_cast<const u32x4_t*>(crow + c0 / 2);
 #pragma unroll
@@ -145,12 +167,7 @@ __global__ __launch_bounds__(64 * LWAVES) void linear_kernel(LinArgs a) {
                 for (int t = 0; t < NT; ++t) s[t] = 0.f;
 #pragma unroll
                 for (int e = 0; e < LCH; ++e) {
-                    // code of column c0 + e: packed, word e / 8 holds columns 8 (e / 8) .. + 7 with
-                    // the even ones in the bytes of cw[.][2 (e / 8)] and the odd ones in
-                    // cw[.][2 (e / 8) + 1]; one code per byte otherwise
-                    const uint32_t word = PACKED ? cw[i][2 * (e >> 3) + (e & 1)] : cw[i][e >> 2];
-                    const int byte = PACKED ? ((e & 7) >> 1) : (e & 3);
-                    const float d = (float)((word >> (8 * byte)) & 0xFFu) - z[i];   // exact: small integers
+                    const float d = (float)chunk_code<CB>(cw[i], e) - z[i];   // exact: small integers
 #pragma unroll
                     for (int t = 0; t < NT; ++t) s[t] = fmaf(xv[t][e], d, s[t]);
                 }
@@ -171,7 +188,7 @@ __global__ __launch_bounds__(64 * LWAVES) void linear_kernel(LinArgs a) {
 
 // General path (any even d_col, any alignment): one thread per (row, token), columns in
 // order; the same arithmetic per group.
-template <bool PACKED, gptq_dtype XT, gptq_dtype YT>
+template <int CB, gptq_dtype XT, gptq_dtype YT>
 __global__ __launch_bounds__(256) void linear_any_kernel(LinArgs a) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= a.d_row) return;
@@ -185,7 +202,8 @@ __global__ __launch_bounds__(256) void linear_any_kernel(LinArgs a) {
             const int64_t c1 = (c0 + a.G < a.d_col) ? c0 + a.G : a.d_col;
             float s = 0.f;
             for (int64_t c = c0; c < c1; ++c) {
-                const uint32_t u = PACKED ? (crow[c >> 1] >> (4 * (c & 1))) & 0xFu : crow[c];
+                const uint32_t u = CB == 3 ? code3(load_u24(crow + c / 8 * 3), (int)(c & 7))
+                                   : CB == 4 ? (crow[c >> 1] >> (4 * (c & 1))) & 0xFu : crow[c];
                 s = fmaf(load_as_f32<XT>(a.x, t * a.ldx + c), (float)u - z, s);
             }
             acc = fmaf(S, s, acc);
@@ -220,9 +238,10 @@ constexpr int MCK = 128;     // columns per chunk: four 32-deep products, one sc
 // the same 32 columns of token l % 16 of each token tile; product t of the chunk takes
 // columns 32 (l / 16) + 8 t .. + 7 from every lane, so over its four products the
 // chunk's 128 columns each enter once (the order of a sum's terms is the only thing
-// this changes).  Requires packed codes, 16-bit activations, d_col and the group width
-// multiples of 128, 16-byte aligned code and activation rows.
-template <int NTT, gptq_dtype XT, gptq_dtype YT>
+// this changes).  Requires 4-bit (16 bytes per lane, 16-byte aligned rows) or 3-bit
+// codes (12 bytes per lane, 4-byte aligned rows), 16-bit activations, d_col and the group
+// width multiples of 128, 16-byte aligned activation rows.
+template <int CB, int NTT, gptq_dtype XT, gptq_dtype YT>
 __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
     typedef std::conditional_t<XT == GPTQ_BF16, bf16x8_t, f16x8_t> frag_t;
     typedef std::conditional_t<XT == GPTQ_BF16, __bf16, _Float16> elem_t;
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
     const int64_t row = (int64_t)blockIdx.x * 16 + n16;
     const int64_t rr = row < a.d_row ? row : a.d_row - 1;       // rows past the end re-read the last
     const int64_t tok0 = (int64_t)blockIdx.y * 16 * NTT;
-    const uint8_t* crow = a.codes + rr * a.code_ld + 16 * q;
+    const uint8_t* crow = a.codes + rr * a.code_ld + (CB == 3 ? 12 : 16) * q;
     const uint16_t* xrow[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
@@ -255,7 +274,12 @@ __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
             const int c = c0 + MW * j < nck ? c0 + MW * j : c0;  // chunks past the end re-read c0
-            cw[j] = *reinterpret_cast<const u32x4_t*>(crow + (int64_t)c * (MCK / 2));
+            if constexpr (CB == 3) {
+                const uint32_t* w = reinterpret_cast<const uint32_t*>(crow + (int64_t)c * (MCK / 8 * 3));
+                cw[j] = u32x4_t{w[0], w[1], w[2], 0u};
+            } else {
+                cw[j] = *reinterpret_cast<const u32x4_t*>(crow + (int64_t)c * (MCK / 2));
+            }
             const int64_t gi = rr * a.n_groups + c / cpg;
             S[j] = f16_bits_to_f32(a.scales[gi]);
             z[j] = f16_bits_to_f32(a.zeros[gi]);
@@ -276,15 +300,25 @@ __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
             for (int tt = 0; tt < NTT; ++tt) cs[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                // element e of the operand is column 8 t + e of the lane's 32: the low
-                // nibble of byte e / 2 for even e, the high nibble for odd e
-                const uint32_t w = cw[j][t];
-                const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+                // element e of the operand is column 8 t + e of the lane's 32: 4-bit, the low
+                // nibble of byte e / 2 for even e, the high nibble for odd e; 3-bit, code e of
+                // the 24-bit group t of the lane's 96-bit stream
                 float d[8];
+                if constexpr (CB == 3) {
+                    const uint32_t g24 = t == 0 ? cw[j][0] & 0xFFFFFFu
+                                       : t == 1 ? ((cw[j][0] >> 24) | (cw[j][1] << 8)) & 0xFFFFFFu
+                                       : t == 2 ? ((cw[j][1] >> 16) | (cw[j][2] << 16)) & 0xFFFFFFu
+                                                : cw[j][2] >> 8;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    d[2 * b] = (float)((lo >> (8 * b)) & 0xFFu) - z[j];
-                    d[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu) - z[j];
+                    for (int e = 0; e < 8; ++e) d[e] = (float)code3(g24, e) - z[j];
+                } else {
+                    const uint32_t w = cw[j][t];
+                    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        d[2 * b] = (float)((lo >> (8 * b)) & 0xFFu) - z[j];
+                        d[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu) - z[j];
+                    }
                 }
                 frag_t bh;
 #pragma unroll
@@ -331,21 +365,21 @@ __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
     }
 }
 
-template <gptq_dtype XT, gptq_dtype YT>
+template <int CB, gptq_dtype XT, gptq_dtype YT>
 static void launch_mfma(const LinArgs& a, hipStream_t s) {
     const unsigned gx = (unsigned)((a.d_row + 15) / 16);
     if (a.n_tok <= 16 || LIN_NTT_MAX == 1)
-        linear_mfma_kernel<1, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
+        linear_mfma_kernel<CB, 1, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
     else if (a.n_tok <= 32 || LIN_NTT_MAX == 2)
-        linear_mfma_kernel<2, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 31) / 32)), 64 * MW, 0, s>>>(a);
-    else linear_mfma_kernel<4, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 63) / 64)), 64 * MW, 0, s>>>(a);
+        linear_mfma_kernel<CB, 2, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 31) / 32)), 64 * MW, 0, s>>>(a);
+    else linear_mfma_kernel<CB, 4, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 63) / 64)), 64 * MW, 0, s>>>(a);
 }
 
-template <bool PACKED, gptq_dtype XT, gptq_dtype YT>
+template <int CB, gptq_dtype XT, gptq_dtype YT>
 static gptq_status launch3(const LinArgs& a, int path, hipStream_t s) {
-    if constexpr (PACKED && XT != GPTQ_F32) {
+    if constexpr (CB != 8 && XT != GPTQ_F32) {
         if (path == 2) {
-            launch_mfma<XT, YT>(a, s);
+            launch_mfma<CB, XT, YT>(a, s);
             GPTQ_LAUNCH_CHECK();
             return GPTQ_OK;
         }
@@ -353,34 +387,34 @@ static gptq_status launch3(const LinArgs& a, int path, hipStream_t s) {
     const bool fast = path >= 1;
     if (!fast) {
         const unsigned ty = (unsigned)(a.n_tok < 65535 ? a.n_tok : 65535);
-        linear_any_kernel<PACKED, XT, YT><<<dim3((unsigned)((a.d_row + 255) / 256), ty), 256, 0, s>>>(a);
+        linear_any_kernel<CB, XT, YT><<<dim3((unsigned)((a.d_row + 255) / 256), ty), 256, 0, s>>>(a);
         GPTQ_LAUNCH_CHECK();
         return GPTQ_OK;
     }
     const dim3 grid((unsigned)((a.d_row + LWAVES * LROWS - 1) / (LWAVES * LROWS)));
-    if (a.n_tok == 1) linear_kernel<PACKED, 1, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
-    else if (a.n_tok == 2) linear_kernel<PACKED, 2, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
-    else linear_kernel<PACKED, 4, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
+    if (a.n_tok == 1) linear_kernel<CB, 1, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
+    else if (a.n_tok == 2) linear_kernel<CB, 2, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
+    else linear_kernel<CB, 4, XT, YT><<<grid, 64 * LWAVES, 0, s>>>(a);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
 
-template <bool PACKED, gptq_dtype XT>
+template <int CB, gptq_dtype XT>
 static gptq_status launch2(const LinArgs& a, gptq_dtype yt, int path, hipStream_t s) {
     switch (yt) {
-        case GPTQ_F32: return launch3<PACKED, XT, GPTQ_F32>(a, path, s);
-        case GPTQ_BF16: return launch3<PACKED, XT, GPTQ_BF16>(a, path, s);
-        case GPTQ_F16: return launch3<PACKED, XT, GPTQ_F16>(a, path, s);
+        case GPTQ_F32: return launch3<CB, XT, GPTQ_F32>(a, path, s);
+        case GPTQ_BF16: return launch3<CB, XT, GPTQ_BF16>(a, path, s);
+        case GPTQ_F16: return launch3<CB, XT, GPTQ_F16>(a, path, s);
     }
     return GPTQ_ERR_UNSUPPORTED;
 }
 
-template <bool PACKED>
+template <int CB>
 static gptq_status launch1(const LinArgs& a, gptq_dtype xt, gptq_dtype yt, int path, hipStream_t s) {
     switch (xt) {
-        case GPTQ_F32: return launch2<PACKED, GPTQ_F32>(a, yt, path, s);
-        case GPTQ_BF16: return launch2<PACKED, GPTQ_BF16>(a, yt, path, s);
-        case GPTQ_F16: return launch2<PACKED, GPTQ_F16>(a, yt, path, s);
+        case GPTQ_F32: return launch2<CB, GPTQ_F32>(a, yt, path, s);
+        case GPTQ_BF16: return launch2<CB, GPTQ_BF16>(a, yt, path, s);
+        case GPTQ_F16: return launch2<CB, GPTQ_F16>(a, yt, path, s);
     }
     return GPTQ_ERR_UNSUPPORTED;
 }
@@ -389,8 +423,8 @@ gptq_status linear_launch(const uint8_t* codes, const uint16_t* scales, const ui
                           int64_t d_col, int bits, int group_size, const void* x, gptq_dtype x_dtype, int64_t n_tok,
                           int64_t ldx, void* y, gptq_dtype y_dtype, hipStream_t s) {
     LinArgs a;
-    const bool packed = bits <= 4;
-    a.codes = codes; a.code_ld = packed ? d_col / 2 : d_col;
+    const int cb = bits == 3 ? 3 : bits == 4 ? 4 : 8;     // code bits as stored
+    a.codes = codes; a.code_ld = cb == 3 ? d_col / 8 * 3 : cb == 4 ? d_col / 2 : d_col;
     a.scales = scales; a.zeros = zeros;
     a.G = group_size == 0 ? d_col : group_size;
     a.n_groups = (int)(d_col / a.G);
@@ -399,15 +433,18 @@ gptq_status linear_launch(const uint8_t* codes, const uint16_t* scales, const ui
     a.d_row = d_row; a.d_col = d_col;
     const size_t xsz = x_dtype == GPTQ_F32 ? 4 : 2;
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-    // whole 32-column chunks inside one group, every chunk of codes and of x 16-byte aligned
-    const bool fast = d_col % LCH == 0 && a.G % LCH == 0 && (a.code_ld % 16) == 0 && al16(codes) && al16(x) &&
-                      ((size_t)ldx * xsz) % 16 == 0;
-    // batched tokens on the matrix cores: packed codes, 16-bit activations, whole 128-column
-    // chunks inside one group
-    const bool mfma = fast && packed && x_dtype != GPTQ_F32 && n_tok >= LIN_MFMA_MIN_TOK && d_col % MCK == 0 &&
+    // whole 32-column chunks inside one group, every chunk of codes 16-byte aligned (3-bit:
+    // 4-byte; its chunks are 12 bytes) and of x 16-byte aligned
+    const int cal = cb == 3 ? 4 : 16;
+    const bool fast = d_col % LCH == 0 && a.G % LCH == 0 && (a.code_ld % cal) == 0 &&
+                      (reinterpret_cast<uintptr_t>(codes) % cal) == 0 && al16(x) && ((size_t)ldx * xsz) % 16 == 0;
+    // batched tokens on the matrix cores: 3- or 4-bit codes, 16-bit activations, whole
+    // 128-column chunks inside one group
+    const bool mfma = fast && cb != 8 && x_dtype != GPTQ_F32 && n_tok >= LIN_MFMA_MIN_TOK && d_col % MCK == 0 &&
                       a.G % MCK == 0;
     const int path = mfma ? 2 : fast ? 1 : 0;
-    return packed ? launch1<true>(a, x_dtype, y_dtype, path, s) : launch1<false>(a, x_dtype, y_dtype, path, s);
+    return cb == 3 ? launch1<3>(a, x_dtype, y_dtype, path, s)
+         : cb == 4 ? launch1<4>(a, x_dtype, y_dtype, path, s) : launch1<8>(a, x_dtype, y_dtype, path, s);
 }
 
 }  // namespace gptq

@@ -131,9 +131,18 @@ __global__ __launch_bounds__(OBQ_T) void obq_kernel(const void* W, int64_t d_row
             }
             __syncthreads();
         }
-        // the row's codes: two per byte (first in the low nibble) or one per byte
+        // the row's codes: the 3-bit stream (three bytes per 8 codes), two per byte (first
+        // in the low nibble) or one per byte
         uint8_t* crow = codes + r * code_ld;
-        if (BITS <= 4) {
+        if (BITS == 3) {
+            for (int g8 = tid; g8 < d / 8; g8 += OBQ_T) {
+                uint32_t v = 0;
+                for (int k = 0; k < 8; ++k) v |= (uint32_t)(u[8 * g8 + k] & 7) << (3 * k);
+                crow[3 * g8] = (uint8_t)v;
+                crow[3 * g8 + 1] = (uint8_t)(v >> 8);
+                crow[3 * g8 + 2] = (uint8_t)(v >> 16);
+            }
+        } else if (BITS <= 4) {
             for (int c = tid; c < d / 2; c += OBQ_T) crow[c] = (uint8_t)(u[2 * c] | (u[2 * c + 1] << 4));
         } else {
             for (int c = tid; c < d; c += OBQ_T) crow[c] = u[c];
@@ -175,7 +184,7 @@ gptq_status obq_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t
     GPTQ_LAUNCH_CHECK();
     obq_hinv_kernel<<<dim3((unsigned)((d_col + 255) / 256), (unsigned)d_col), 256, 0, s>>>(U, d_col, Hinv);
     GPTQ_LAUNCH_CHECK();
-    const int64_t code_ld = p.bits <= 4 ? d_col / 2 : d_col;
+    const int64_t code_ld = p.bits == 3 ? d_col / 8 * 3 : p.bits <= 4 ? d_col / 2 : d_col;
     const int d = (int)d_col;
 #define OG(B, S) obq_go<B, S>(W, w_dtype, d_row, d, Hinv, F, slots, codes, code_ld, scales, zeros, info, s)
     if (p.bits == 4) { if (p.sym) OG(4, true); else OG(4, false); }

@@ -776,7 +776,8 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     }
     sa.es = es; sa.us = us;
     sa.Wws = Wws; sa.d_row = d_row; sa.d_col = d_col; sa.U = U;
-    sa.codes = codes; sa.code_ld = (p.bits <= 4) ? d_col / 2 : d_col;
+    sa.codes = codes; sa.code_ld = p.bits == 3 ? d_col / 8 * 3 : (p.bits <= 4) ? d_col / 2 : d_col;
+    sa.bits3 = p.bits == 3;
     sa.scales = scales; sa.zeros = zeros; sa.n_groups = n_groups; sa.info = info;
     sa.group = G < 0 ? 0 : G;   // per tensor: every row's parameters are set, as per row
     sa.sym = p.sym != 0; sa.packed = p.bits <= 4;
@@ -818,18 +819,23 @@ __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, con
                                int64_t d_col, int G, void* out) {
     const int64_t row = blockIdx.y;
     const int64_t chunks = (d_col + 7) / 8;
-    const int64_t code_ld = (BITS <= 4) ? d_col / 2 : d_col;
+    const int64_t code_ld = (BITS == 3) ? d_col / 8 * 3 : (BITS <= 4) ? d_col / 2 : d_col;
     const int n_groups = (G == 0) ? 1 : (int)(d_col / G);
     constexpr int OB = (OT == GPTQ_F32) ? 4 : 2;     // output bytes per value
     const bool fast = (d_col % 8 == 0) && (G % 8 == 0) &&
-                      ((reinterpret_cast<uintptr_t>(codes) & 7) == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0) &&
-                      ((code_ld * row) % ((BITS <= 4) ? 4 : 8) == 0) && ((d_col * OB) % 16 == 0);
+                      (BITS == 3 || ((reinterpret_cast<uintptr_t>(codes) & 7) == 0)) &&
+                      ((reinterpret_cast<uintptr_t>(out) & 15) == 0) &&
+                      (BITS == 3 || (code_ld * row) % ((BITS <= 4) ? 4 : 8) == 0) && ((d_col * OB) % 16 == 0);
     for (int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ch < chunks; ch += (int64_t)gridDim.x * blockDim.x) {
         const int64_t c0 = ch * 8;
         float v[8];
         if (fast) {
             uint32_t u[8];
-            if constexpr (BITS <= 4) {
+            if constexpr (BITS == 3) {
+                const uint32_t g24 = load_u24(codes + row * code_ld + c0 / 8 * 3);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] = code3(g24, e);
+            } else if constexpr (BITS <= 4) {
                 const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + row * code_ld + c0 / 2);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) u[e] = (w >> (4 * e)) & 0xFu;
@@ -864,7 +870,9 @@ __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, con
             const int64_t c = c0 + e;
             if (c >= d_col) { v[e] = 0.f; continue; }
             uint32_t u;
-            if constexpr (BITS <= 4) {
+            if constexpr (BITS == 3) {
+                u = code3(load_u24(codes + row * code_ld + c / 8 * 3), (int)(c & 7));
+            } else if constexpr (BITS <= 4) {
                 const uint8_t b = codes[row * code_ld + (c >> 1)];
                 u = (c & 1) ? (b >> 4) : (b & 0xF);
             } else {
@@ -905,6 +913,7 @@ gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const u
     const int64_t chunks = (d_col + 7) / 8;
     dim3 grid((unsigned)std::min<int64_t>((chunks + 255) / 256, 64), (unsigned)d_row);
     if (fp4) return dq_dt<4, true>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
+    if (bits == 3) return dq_dt<3>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     if (bits <= 4) return dq_dt<4>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     return dq_dt<8>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
 }

@@ -68,6 +68,7 @@ struct SweepArgs {
     int group;                      // 32, 64, 128 (power of two), or 0 = per-row params precomputed
     int qmin, qmax, zoff;           // grid and stored-code offset
     int sym; int packed;            // packed: two codes per byte
+    int bits3;                      // 3-bit stream: eight codes in three bytes
     int fp4;                        // E2M1 grid (sign bit 8 | magnitude index), zero 0
     int mx;                         // with fp4: power-of-two group scales (MXFP4)
 };

@@ -373,9 +373,20 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                 for (int c = c8; c < c8 + 8 && c < nb; ++c) { hrow[c] = ehs[r][c]; lrow[c] = els[r][c]; }
             }
         }
-        // codes: two per byte (column 2k in the low nibble) or one per byte; thread t
-        // writes 8 columns of row t / 16
-        if (grow < a.d_row) {
+        // codes: the 3-bit stream (three bytes per 8 columns; block widths are multiples
+        // of 8), two per byte (column 2k in the low nibble) or one per byte; thread t writes
+        // 8 columns of row t / 16
+        if (a.bits3) {
+            if (grow < a.d_row && c8 < nb) {
+                uint8_t* crow = a.codes + grow * a.code_ld + (b0 + c8) / 8 * 3;
+                uint32_t v = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v |= (uint32_t)(cl[r][c8 + k] & 7) << (3 * k);
+                crow[0] = (uint8_t)v;
+                crow[1] = (uint8_t)(v >> 8);
+                crow[2] = (uint8_t)(v >> 16);
+            }
+        } else if (grow < a.d_row) {
             uint8_t* crow = a.codes + grow * a.code_ld + b0 / per;
             const bool whole = FULL || nb == QB && ((reinterpret_cast<uintptr_t>(crow) & (a.packed ? 3 : 7)) == 0);
             if (a.packed) {

@@ -32,8 +32,11 @@ def layer_x(L: synth.Layer) -> np.ndarray:
 
 
 def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
-    """Plain nibble unpacking of the GPU byte layout (column 2k low nibble)."""
+    """The stored codes of the GPU byte layout: the 3-bit stream (the oracle's pinned
+    unpacking), or plain nibble unpacking (column 2k low nibble), or one per byte."""
     packed = np.asarray(packed, dtype=np.uint8)
+    if bits == 3:
+        return o.unpack(packed, 3)
     if bits == 8:
         return packed.copy()
     out = np.empty((packed.shape[0], packed.shape[1] * 2), dtype=np.uint8)

@@ -306,3 +306,15 @@ def test_noalloc_argument_errors(lib):
     assert call(64, 250) == INVALID_ARG                 # group does not divide d_col
     assert call(64, 256, w=None) == INVALID_ARG
     assert f(None, BF16, 0, 256, None, ctypes.byref(p), None, None, None, None, None) == OK
+
+
+def test_int3_rows_are_whole_8_code_groups(lib):
+    """The 3-bit stream packs eight codes into three bytes: 3-bit layers need d_col a
+    multiple of 8 in every entry point that reads or writes codes."""
+    p3 = lib.Params(3, 0, 1, 128)
+    f = lib.gptq_quantize_layer
+    assert f(FAKE, BF16, 16, 252, FAKE, ctypes.byref(p3), FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE, None) == INVALID_ARG
+    d = lib.gptq_dequantize
+    assert d(FAKE, FAKE, FAKE, 4, 252, 3, 0, FAKE, F32, None) == INVALID_ARG
+    lin = lib.gptq_quantized_linear
+    assert lin(FAKE, FAKE, FAKE, 4, 252, 3, 0, FAKE, BF16, 1, 252, FAKE, F32, None) == INVALID_ARG

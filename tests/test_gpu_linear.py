@@ -26,9 +26,10 @@ def make_case(d_row, d_col, bits, G, n, seed, frac_zeros=False):
     rng = np.random.default_rng([seed, d_row, d_col, bits, G, n])
     if bits == 8:
         packed = rng.integers(0, 256, size=(d_row, d_col), dtype=np.uint8)
+    elif bits == 3:   # every byte pattern is a 3-bit stream (eight codes in three bytes)
+        packed = rng.integers(0, 256, size=(d_row, d_col // 8 * 3), dtype=np.uint8)
     else:
-        mask = 0xFF if bits == 4 else 0x77
-        packed = (rng.integers(0, 256, size=(d_row, d_col // 2), dtype=np.uint8) & mask).astype(np.uint8)
+        packed = rng.integers(0, 256, size=(d_row, d_col // 2), dtype=np.uint8)
     ng = 1 if G == 0 else d_col // G
     scales = (rng.random((d_row, ng)) * 0.05 + 0.001).astype(np.float16)
     zeros = rng.integers(0, 2 ** bits, size=(d_row, ng)).astype(np.float16)
@@ -80,6 +81,13 @@ CASES = [
     (200, 384, 3, 128, 70, torch.bfloat16, torch.float32, 0),      # two tile rows of 64 tokens, ragged rows, 3 chunks
     (160, 2048, 4, 0, 2, torch.float16, torch.float16, 0),         # per-row group over 16 chunks
     (64, 1280, 4, 128, 33, torch.bfloat16, torch.float32, 8),      # padded x rows (16-byte aligned)
+    # the 3-bit stream (12 bytes per 32 columns): decode, general and batched kernels
+    (4096, 4096, 3, 128, 1, torch.bfloat16, torch.float32, 0),
+    (300, 512, 3, 0, 3, torch.float16, torch.float32, 0),
+    (100, 200, 3, 0, 5, torch.bfloat16, torch.float32, 0),          # width not a multiple of 32: general kernel
+    (96, 512, 3, 128, 2, torch.bfloat16, torch.float16, 3),         # x rows not 16-byte aligned: general kernel
+    (4096, 4096, 3, 128, 16, torch.bfloat16, torch.bfloat16, 0),    # batched, one full token tile
+    (272, 1024, 3, 256, 40, torch.float16, torch.float32, 0),       # batched, three token tiles
 ]
 
 

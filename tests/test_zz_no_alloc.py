@@ -24,7 +24,8 @@ def _sig(g):
 
 def _outs(torch, d_row, d_col, bits, group):
     ng = 1 if group <= 0 else d_col // group
-    return (torch.full((d_row, d_col // 2 if bits <= 4 else d_col), 0xAB, dtype=torch.uint8, device="cuda"),
+    import post_weight_quantization_25_amd as g
+    return (torch.full((d_row, g.code_bytes(bits, d_col)), 0xAB, dtype=torch.uint8, device="cuda"),
             torch.full((d_row, ng), 7.0, dtype=torch.float16, device="cuda"),
             torch.full((d_row, ng), 7.0, dtype=torch.float16, device="cuda"),
             torch.full((1,), 99, dtype=torch.int32, device="cuda"))
