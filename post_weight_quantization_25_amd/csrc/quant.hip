@@ -569,20 +569,25 @@ static gptq_status trail(const TrailArgs& ta, hipStream_t s) {
 // Host side
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Super-blocks (QSB columns) of the deferred trailing update: inside a super-block
+// Two levels of deferral of the trailing update.  Inside a super-block (QSB columns)
 // every 128-column block updates only the rest of the super-block (in the sweep
-// kernel); the columns after it get one product with K = QSB per super-block.  The
-// regrouping of the rank-1 updates is exact in exact arithmetic, as for the
-// 128-column lazy blocks.
+// kernel).  Inside a macro-block (QMB columns, QMB / QSB super-blocks) every
+// super-block then updates only the rest of the macro-block (K = QSB); the columns after
+// the macro-block get one product with K = QMB, with the errors of all its super-blocks.
+// The fp32 working copy of the later columns is therefore read and written once per
+// macro-block instead of once per super-block.  The regrouping of the rank-1 updates is
+// exact in exact arithmetic, as for the 128-column lazy blocks.
+constexpr int QMB = 2048;
+static_assert(QMB % QSB == 0, "a macro-block holds whole super-blocks");
 
-// Workspace: fp32 working copy of W | E hi | E lo (scaled fp16, d_row x QSB) | U hi |
+// Workspace: fp32 working copy of W | E hi | E lo (scaled fp16, d_row x QMB) | U hi |
 // U lo (scaled fp16, d_col x d_col) | Ut hi | Ut lo (scaled fp16, one transposed QSB x QSB
 // diagonal block of U per super-block) | es (fp32, d_row) | us (fp32, d_col).
 static size_t ut_bytes(int64_t d_col) { return (size_t)((d_col + QSB - 1) / QSB) * QSB * QSB * 2; }
 
 size_t quant_ws_bytes(int64_t d_row, int64_t d_col) {
     if (d_row <= 0 || d_col <= 0) return 0;
-    return align256((size_t)d_row * d_col * sizeof(float)) + 2 * align256((size_t)d_row * QSB * 2) +
+    return align256((size_t)d_row * d_col * sizeof(float)) + 2 * align256((size_t)d_row * QMB * 2) +
            2 * align256((size_t)d_col * d_col * 2) + 2 * align256(ut_bytes(d_col)) +
            align256((size_t)d_row * sizeof(float)) + align256((size_t)d_col * sizeof(float));
 }
@@ -728,9 +733,9 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     float* Wws = reinterpret_cast<float*>(ws);
     char* wp = reinterpret_cast<char*>(ws) + align256((size_t)d_row * d_col * sizeof(float));
     uint16_t* Ehi = reinterpret_cast<uint16_t*>(wp);
-    wp += align256((size_t)d_row * QSB * 2);
+    wp += align256((size_t)d_row * QMB * 2);
     uint16_t* Elo = reinterpret_cast<uint16_t*>(wp);
-    wp += align256((size_t)d_row * QSB * 2);
+    wp += align256((size_t)d_row * QMB * 2);
     uint16_t* Uhi = reinterpret_cast<uint16_t*>(wp);
     wp += align256((size_t)d_col * d_col * 2);
     uint16_t* Ulo = reinterpret_cast<uint16_t*>(wp);
@@ -760,7 +765,7 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
         st = launch_row_params(p.bits, p.sym != 0, p.sym >= 2, p.sym == 3, Wws, d_row, d_col, scales, zeros, info, s);
         if (st != GPTQ_OK) return st;
     } else if (G < 0) {
-        // E holds d_row x QSB bf16 values: room for 64 d_row partial ranges
+        // E holds d_row x QMB 16-bit values: room for 64 d_row partial ranges
         const int nb = (int)std::min<int64_t>(1024, 64 * d_row);
         st = launch_tensor_params(p.bits, p.sym != 0, p.sym >= 2, p.sym == 3, Wws, d_row, d_col, reinterpret_cast<float*>(Ehi), nb, scales,
                                   zeros, info, s);
@@ -786,18 +791,25 @@ gptq_status quant_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64
     sa.qmin = sa.sym ? -((1 << (p.bits - 1)) - 1) : 0;
     sa.qmax = sa.fp4 ? 6 : sa.sym ? ((1 << (p.bits - 1)) - 1) : (1 << p.bits) - 1;
     sa.zoff = (sa.sym && !sa.fp4) ? (1 << (p.bits - 1)) : 0;
-    for (int64_t s0 = 0; s0 < d_col; s0 += QSB) {
-        const int64_t s1 = std::min<int64_t>(s0 + QSB, d_col);
-        // the super-block's blocks, each followed by the update of the rest of the
-        // super-block, in one launch
-        sa.s0 = s0; sa.s1 = s1; sa.Ehi = Ehi; sa.Elo = Elo; sa.lde = QSB;
-        sa.Uthi = Uthi + (s0 / QSB) * QSB * QSB;
-        sa.Utlo = Utlo + (s0 / QSB) * QSB * QSB;
-        st = sweep_launch(sa, s);
-        if (st != GPTQ_OK) return st;
-        // everything after the super-block, K = s1 - s0
-        TrailArgs tb{Wws, d_row, d_col, Ehi, Elo, QSB, Uhi, Ulo, es, s0, (int)(s1 - s0), s1, d_col, 0};
-        if ((st = trail(tb, s)) != GPTQ_OK) return st;
+    for (int64_t m0 = 0; m0 < d_col; m0 += QMB) {
+        const int64_t m1 = std::min<int64_t>(m0 + QMB, d_col);
+        for (int64_t s0 = m0; s0 < m1; s0 += QSB) {
+            const int64_t s1 = std::min<int64_t>(s0 + QSB, m1);
+            // the super-block's blocks, each followed by the update of the rest of the
+            // super-block, in one launch; its errors go to columns s0 - m0 .. of E
+            sa.s0 = s0; sa.s1 = s1; sa.Ehi = Ehi + (s0 - m0); sa.Elo = Elo + (s0 - m0); sa.lde = QMB;
+            sa.Uthi = Uthi + (s0 / QSB) * QSB * QSB;
+            sa.Utlo = Utlo + (s0 / QSB) * QSB * QSB;
+            st = sweep_launch(sa, s);
+            if (st != GPTQ_OK) return st;
+            // the rest of the macro-block, K = s1 - s0
+            TrailArgs tn{Wws, d_row, d_col, Ehi + (s0 - m0), Elo + (s0 - m0), QMB, Uhi, Ulo, es, s0, (int)(s1 - s0),
+                         s1, m1, 0};
+            if ((st = trail(tn, s)) != GPTQ_OK) return st;
+        }
+        // everything after the macro-block, K = m1 - m0
+        TrailArgs tf{Wws, d_row, d_col, Ehi, Elo, QMB, Uhi, Ulo, es, m0, (int)(m1 - m0), m1, d_col, 0};
+        if ((st = trail(tf, s)) != GPTQ_OK) return st;
     }
     return GPTQ_OK;
 }
