@@ -531,38 +531,258 @@ __global__ __launch_bounds__(256, 1) void trail_dma_kernel(TrailArgs a) {
     }
 }
 
-// Whole tiles on the direct-load kernel when the operands allow 16-byte loads at every
-// row (K a multiple of 32, row pitches multiples of 8 elements, aligned arrays); the
-// partial last row and column of tiles (and everything otherwise) on trail_kernel.
-static gptq_status trail(const TrailArgs& ta, hipStream_t s) {
-    if (ta.n_end <= ta.n_beg || ta.K <= 0 || ta.d_row <= 0) return GPTQ_OK;
+// --------------------------------------------------------------------------
+// Large products (whole 256 x 256 tiles): the same update on the Hessian kernel's load
+// path.  Eight waves (two per SIMD), each accumulating a 64 x 128 sub-tile (2 x 4 MFMA
+// 32 x 32 tiles, fp16, three products per k step); a ring of four 16-deep stages
+// (E hi, E lo: 256 rows x 16 k; U hi, U lo: 16 k x 256 columns; 8 KB each) filled by
+// direct global -> LDS loads issued three stages ahead; the fragments of the next stage
+// are read while the MFMAs of the current one run.  Per MFMA a wave reads 512 bytes of
+// LDS (the 128 x 128 kernel: 683) and the copy writes 171 (341).  E rows are stored as
+// they lie (32 bytes, read with 16-byte reads); U rows (512 bytes) with their 16-byte
+// chunks XOR-swizzled as in the Hessian kernel and read with ds_read_b64_tr_b16.
+// Work mapping: the tiles in row-major order are cut into eight runs, one per XCD
+// (workgroup L runs on XCD L % 8), so each XCD's L2 serves few rows of E.
+constexpr int TG_BM = 256, TG_BK = 16, TG_NSTG = 4, TG_WAVES = 8;
+constexpr int TG_WM = 64, TG_WN = 128;             // wave sub-tile: waves 4 (rows) x 2 (columns)
+constexpr int TG_OPE = TG_BM * TG_BK;              // 16-bit elements of one operand of a stage
+constexpr int TG_STE = 4 * TG_OPE;                 // a stage: E hi, E lo, U hi, U lo (32 KB)
+constexpr int TG_DMA = 4;                          // 1 KB loads per wave and stage
+constexpr int TG_VM = (TG_NSTG - 2) * TG_DMA;      // loads left in flight at a stage wait
+static_assert(TG_NSTG * TG_STE * 2 <= 160 * 1024, "LDS ring exceeds the workgroup's LDS");
+
+GPTQ_DEV int tg_swz(int k, int c) {       // the Hessian kernel's chunk swizzle of 512-byte rows
+    const int r = k & 3;
+    const int f = 2 * r + ((r ^ (r >> 1)) & 1);
+    return c ^ (f << 1);
+}
+
+struct TgCopy {
+    uint32_t voff[TG_DMA];   // per-lane byte offsets of the wave's loads
+    const uint16_t* base;    // the wave's operand at stage 0 (wave-uniform)
+    int64_t sstride;         // elements between stages
+    uint32_t m0base;         // LDS byte address of the wave's share of the operand in slot 0
+};
+
+// Wave w copies 4 KB (half h = w & 1) of operand w / 2 (E hi, E lo, U hi, U lo).  E: load
+// i covers rows 32 (4 h + i) .. + 31, lane l row + l / 2, chunk l & 1 (linear in LDS).
+// U: load i covers k rows 2 (4 h + i), + 1, lane l row + l / 32, LDS chunk position l % 32
+// holding chunk tg_swz(row, l % 32).
+GPTQ_DEV TgCopy tg_copy_setup(const TrailArgs& a, const uint16_t* ring0, int64_t m0, int64_t n0, int wave, int lane) {
+    TgCopy tc;
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    const int op = w >> 1, h = w & 1;
+    tc.m0base = lds_addr(ring0) + (uint32_t)(op * TG_OPE * 2 + h * TG_DMA * 1024);
+    if (op < 2) {
+        tc.base = (op ? a.Elo : a.Ehi) + m0 * a.lde;
+        tc.sstride = TG_BK;
+#pragma unroll
+        for (int i = 0; i < TG_DMA; ++i) {
+            const int r = 32 * (TG_DMA * h + i) + (lane >> 1), q = lane & 1;
+            tc.voff[i] = (uint32_t)(((int64_t)r * a.lde + 8 * q) * 2);
+        }
+    } else {
+        tc.base = (op == 2 ? a.Uhi : a.Ulo) + a.k0 * a.d_col + n0;
+        tc.sstride = (int64_t)TG_BK * a.d_col;
+#pragma unroll
+        for (int i = 0; i < TG_DMA; ++i) {
+            const int r = 2 * (TG_DMA * h + i) + (lane >> 5), c = tg_swz(r, lane & 31);
+            tc.voff[i] = (uint32_t)(((int64_t)r * a.d_col + 8 * c) * 2);
+        }
+    }
+    return tc;
+}
+
+template <int SLOT>
+GPTQ_DEV void tg_issue(const TgCopy& tc, int st) {
+    const uint16_t* sbase = tc.base + st * tc.sstride;
+    static_for<0, TG_DMA>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        dma16<(uint32_t)(SLOT * TG_STE * 2 + i * 1024)>(tc.voff[i], sbase, tc.m0base);
+    });
+}
+
+struct TgFrags { f16x8_t ah[2], al[2], bh[4], bl[4]; };
+
+// B operand (32 columns n x 16 k) from a swizzled [k][256] U tile (two transposed reads)
+GPTQ_DEV f16x8_t tg_bfrag(const uint16_t* tile, int nc0, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int n = nc0 + (g & 1) * 16 + 4 * (j & 3);
+    const int k = (g >> 1) * 8 + (j >> 2);
+    const int c = n >> 3, half = (n >> 2) & 1;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(tile + k * TG_BM + 8 * tg_swz(k, c) + 4 * half));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(tile + (k + 4) * TG_BM + 8 * tg_swz(k + 4, c) + 4 * half));
+    return __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+GPTQ_DEV void tg_read(const uint16_t* stg, int wr, int wc, int lane, TgFrags& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = wr * TG_WM + i * 32 + (lane & 31);
+        const int o = m * TG_BK + 8 * (lane >> 5);
+        f.ah[i] = *reinterpret_cast<const f16x8_t*>(stg + o);
+        f.al[i] = *reinterpret_cast<const f16x8_t*>(stg + TG_OPE + o);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f.bh[j] = tg_bfrag(stg + 2 * TG_OPE, wc * TG_WN + j * 32, lane);
+        f.bl[j] = tg_bfrag(stg + 3 * TG_OPE, wc * TG_WN + j * 32, lane);
+    }
+}
+
+// the three products, product-major; the 20 fragment reads of the next stage are
+// interleaved with these 24 MFMAs
+GPTQ_DEV void tg_mfma(const TgFrags& f, f32x16_t (&acc)[2][4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bh[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bl[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[i], f.bh[j], acc[i][j], 0, 0, 0);
+    static_for<0, 4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
+    static_for<0, 16>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
+    static_for<0, 4>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); });
+}
+
+// a.n_beg: first column of the region; the grid enumerates nm x nn whole tiles
+__global__ __launch_bounds__(64 * TG_WAVES, 1) void trail_big_kernel(TrailArgs a, int nm, int nn) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds_ring[TG_NSTG * TG_STE];
+    const uint16_t* ring[TG_NSTG];
+    static_for<0, TG_NSTG>([&](auto I) { ring[decltype(I)::value] = lds_ring + decltype(I)::value * TG_STE; });
+    const int T = nm * nn, L = blockIdx.x;
+    const int tpx = (T + 7) / 8;
+    const int tile = (L & 7) * tpx + (L >> 3);
+    if (tile >= T) return;
+    const int64_t m0 = a.m_beg + (int64_t)(tile / nn) * TG_BM;
+    const int64_t n0 = a.n_beg + (int64_t)(tile % nn) * TG_BM;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    const int nst = a.K / TG_BK;
+    // loads of stages past the last re-load the last one (addresses stay inside the
+    // operands), so that every step leaves the same number of loads in flight
+    auto t0 = [&](int st) { return st < nst ? st : nst - 1; };
+    const TgCopy tc = tg_copy_setup(a, lds_ring, m0, n0, wave, lane);
+    static_for<0, TG_NSTG - 1>([&](auto I) { tg_issue<decltype(I)::value>(tc, t0(decltype(I)::value)); });
+    wait_vm_lgkm0<TG_VM>();
+    __syncthreads();
+    tg_issue<TG_NSTG - 1>(tc, t0(TG_NSTG - 1));
+    TgFrags f0, f1;
+    tg_read(ring[0], wr, wc, lane, f0);
+    for (int st = 0; st < nst; st += TG_NSTG) {
+        static_for<0, TG_NSTG>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if (st + u < nst) {
+                // stage st + u + 1 has landed and every wave is done with slot u
+                wait_vm_lgkm0<TG_VM>();
+                __syncthreads();
+                tg_issue<u>(tc, t0(st + u + TG_NSTG));
+                TgFrags& cur = (u & 1) ? f1 : f0;
+                TgFrags& nxt = (u & 1) ? f0 : f1;
+                tg_read(ring[(u + 1) % TG_NSTG], wr, wc, lane, nxt);
+                tg_mfma(cur, acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the trailing re-loads land before the workgroup ends
+    // W -= acc / es_row: all loads of a 32 x 128 strip first, then its stores
+    float* wbase = a.Wws + (m0 + wr * TG_WM + 4 * (lane >> 5)) * a.d_col + n0 + wc * TG_WN + (lane & 31);
+    const float* ebase = a.erow + m0 + wr * TG_WM + 4 * (lane >> 5);
+    auto off = [&](int i, int j, int e) { return (int64_t)(i * 32 + 8 * (e >> 2) + (e & 3)) * a.d_col + j * 32; };
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float inv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) inv[e] = 1.0f / ebase[i * 32 + 8 * (e >> 2) + (e & 3)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float old[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) old[e] = wbase[off(i, j, e)];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) wbase[off(i, j, e)] = fmaf(-acc[i][j][e], inv[e], old[e]);
+        }
+    }
+}
+
+// Rows [m_beg, m_end) of the product: whole 128 x 128 tiles on the direct-load kernel
+// when the operands allow 16-byte loads at every row (K a multiple of 32, row pitches
+// multiples of 8 elements, aligned arrays); the partial last row and column of tiles (and
+// everything otherwise) on trail_kernel.
+static gptq_status trail_region(const TrailArgs& ta, int64_t m_beg, int64_t m_end, int64_t n_beg, int64_t n_end,
+                                hipStream_t s) {
+    if (n_end <= n_beg || m_end <= m_beg) return GPTQ_OK;
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-    const bool dma = ta.K % TK == 0 && (ta.lde & 7) == 0 && (ta.d_col & 7) == 0 && (ta.n_beg & 7) == 0 &&
+    const bool dma = ta.K % TK == 0 && (ta.lde & 7) == 0 && (ta.d_col & 7) == 0 && (n_beg & 7) == 0 &&
                      ta.d_col < ((int64_t)1 << 25) && ta.lde < ((int64_t)1 << 20) && al16(ta.Ehi) && al16(ta.Elo) &&
                      al16(ta.Uhi) && al16(ta.Ulo);
-    const int64_t mf = dma ? (ta.d_row / TB) * TB : 0;                             // rows of whole tiles
-    const int64_t nf = dma ? ta.n_beg + ((ta.n_end - ta.n_beg) / TB) * TB : ta.n_beg;   // columns of whole tiles
-    if (mf > 0 && nf > ta.n_beg) {
+    const int64_t mf = dma ? m_beg + ((m_end - m_beg) / TB) * TB : m_beg;        // rows of whole tiles
+    const int64_t nf = dma ? n_beg + ((n_end - n_beg) / TB) * TB : n_beg;        // columns of whole tiles
+    if (mf > m_beg && nf > n_beg) {
         TrailArgs t = ta;
-        t.m_beg = 0;
-        trail_dma_kernel<<<dim3((unsigned)((nf - ta.n_beg) / TB), (unsigned)(mf / TB)), 256, 0, s>>>(t);
+        t.m_beg = m_beg; t.n_beg = n_beg;
+        trail_dma_kernel<<<dim3((unsigned)((nf - n_beg) / TB), (unsigned)((mf - m_beg) / TB)), 256, 0, s>>>(t);
         GPTQ_LAUNCH_CHECK();
     }
-    auto edge = [&](int64_t m_beg, int64_t m_end, int64_t n_beg, int64_t n_end) -> gptq_status {
-        if (m_end <= m_beg || n_end <= n_beg) return GPTQ_OK;
+    auto edge = [&](int64_t mb, int64_t me, int64_t nb, int64_t ne) -> gptq_status {
+        if (me <= mb || ne <= nb) return GPTQ_OK;
         TrailArgs t = ta;
-        t.m_beg = m_beg; t.d_row = m_end; t.n_beg = n_beg; t.n_end = n_end;
-        trail_kernel<<<dim3((unsigned)((n_end - n_beg + TB - 1) / TB), (unsigned)((m_end - m_beg + TB - 1) / TB)), 256,
-                       0, s>>>(t);
+        t.m_beg = mb; t.d_row = me; t.n_beg = nb; t.n_end = ne;
+        trail_kernel<<<dim3((unsigned)((ne - nb + TB - 1) / TB), (unsigned)((me - mb + TB - 1) / TB)), 256, 0, s>>>(t);
         GPTQ_LAUNCH_CHECK();
         return GPTQ_OK;
     };
     gptq_status st;
-    if (mf > 0 && nf > ta.n_beg) {
-        if ((st = edge(0, mf, nf, ta.n_end)) != GPTQ_OK) return st;      // last column of tiles
-        return edge(mf, ta.d_row, ta.n_beg, ta.n_end);                    // last row of tiles
+    if (mf > m_beg && nf > n_beg) {
+        if ((st = edge(m_beg, mf, nf, n_end)) != GPTQ_OK) return st;     // last column of tiles
+        return edge(mf, m_end, n_beg, n_end);                            // last row of tiles
     }
-    return edge(0, ta.d_row, ta.n_beg, ta.n_end);
+    return edge(m_beg, m_end, n_beg, n_end);
+}
+
+// W[:, n_beg:n_end] -= E U[k0:k0+K, n_beg:n_end]: whole 256 x 256 tiles on the large-tile
+// kernel when the operands allow it (K a multiple of 16, 16-byte rows) and there are at
+// least as many of them as compute units (fewer large tiles leave compute units idle that
+// four times as many 128 x 128 tiles would fill: measured slower at 4096 x 4096), the
+// rest by trail_region.
+static gptq_status trail(const TrailArgs& ta, hipStream_t s) {
+    if (ta.n_end <= ta.n_beg || ta.K <= 0 || ta.d_row <= 0) return GPTQ_OK;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool big = ta.K % TG_BK == 0 && (ta.lde & 7) == 0 && (ta.d_col & 7) == 0 && (ta.n_beg & 7) == 0 &&
+                     ta.d_col < ((int64_t)1 << 25) && ta.lde < ((int64_t)1 << 20) && al16(ta.Ehi) && al16(ta.Elo) &&
+                     al16(ta.Uhi) && al16(ta.Ulo);
+    const int64_t mb = big ? (ta.d_row / TG_BM) * TG_BM : 0;
+    const int64_t nb = big ? ta.n_beg + ((ta.n_end - ta.n_beg) / TG_BM) * TG_BM : ta.n_beg;
+    if (mb > 0 && nb > ta.n_beg && (mb / TG_BM) * ((nb - ta.n_beg) / TG_BM) >= 256) {
+        TrailArgs t = ta;
+        t.m_beg = 0;
+        const int nm = (int)(mb / TG_BM), nn = (int)((nb - ta.n_beg) / TG_BM);
+        trail_big_kernel<<<(unsigned)(8 * ((nm * nn + 7) / 8)), 64 * TG_WAVES, 0, s>>>(t, nm, nn);
+        GPTQ_LAUNCH_CHECK();
+        gptq_status st;
+        if ((st = trail_region(ta, 0, mb, nb, ta.n_end, s)) != GPTQ_OK) return st;     // last column of tiles
+        return trail_region(ta, mb, ta.d_row, ta.n_beg, ta.n_end, s);                 // last row of tiles
+    }
+    return trail_region(ta, 0, ta.d_row, ta.n_beg, ta.n_end, s);
 }
 
 // --------------------------------------------------------------------------
