@@ -80,18 +80,28 @@ def measured_traffic(launch_bytes_alg: float = 0.0, path: str | None = None, sou
 MFMA_BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy_c2.json")
 
 
-def measured_mfma_busy():
-    """MFMA-busy fraction of the Hessian and trailing-update kernels from a committed
-    rocprofv3 counter summary, or None when either source changed since it was taken."""
+SWEEP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_trail_c2_traffic.json")
+
+
+def _committed(path):
+    """A committed rocprofv3 counter summary, or None when a kernel source it names
+    changed since the counters were taken."""
     try:
-        with open(MFMA_BUSY_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     for src, h in t.get("source_sha256_16", {}).items():
         if source_hash(src) != h:
             return None
-    return t.get("mfma_busy")
+    return t
+
+
+def measured_mfma_busy():
+    """MFMA-busy fraction per kernel (Hessian, trailing update, sweep) of the 4096 x 4096
+    layer from the committed counter summary, or None when a source changed."""
+    t = _committed(MFMA_BUSY_FILE)
+    return None if t is None else t.get("mfma_busy")
 
 
 def phase_rooflines(split, r, d):
@@ -103,16 +113,23 @@ def phase_rooflines(split, r, d):
     inside a super-block run in the sweep kernel)."""
     out = {}
     sweep_ms, trail_ms = split.get("sweep"), split.get("trail")
+    traffic = _committed(SWEEP_TRAFFIC_FILE) if (r, d) == (4096, 4096) else None
+    busy = measured_mfma_busy() if (r, d) == (4096, 4096) else None
     if sweep_ms:
         byt = r * d * (4 + 4 + 0.5) + r * (d // 128) * 4 + d * 128 * 4
         gbs = byt / (sweep_ms * 1e-3) / 1e9
         out["sweep"] = {"bound": "hbm", "algorithmic_bytes": byt, "ms": sweep_ms, "achieved": gbs,
-                        "unit": "GB/s", "peak": HBM_GBS, "frac": gbs / HBM_GBS}
+                        "unit": "GB/s", "peak": HBM_GBS, "frac": gbs / HBM_GBS,
+                        "traffic": traffic["sweep_kernel"]["bytes_per_layer"] if traffic else None}
+        if traffic:
+            out["sweep"]["traffic_frac"] = traffic["sweep_kernel"]["bytes_per_layer"] / (sweep_ms * 1e-3) / 1e9 / HBM_GBS
     if trail_ms:
         fl = 2.0 * r * sum(min(512, d - s0) * (d - min(s0 + 512, d)) for s0 in range(0, d, 512))
         tf = fl / (trail_ms * 1e-3) / 1e12
         out["trail"] = {"bound": "mfma", "algorithmic_flops": fl, "ms": trail_ms, "achieved": tf,
                         "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS,
+                        "mfma_busy": busy.get("trail_dma_kernel") if busy else None,
+                        "traffic": traffic["trail_bytes_per_layer"] if traffic else None,
                         "note": "products after each super-block (the updates inside a super-block run in "
                                 "the sweep kernel); three fp16 products are issued per algorithmic one"}
     return out
@@ -199,6 +216,63 @@ def cpu_baseline(layer, sample_tokens: int, sample_rows: int):
                    f"extrapolated {total:.1f} s per layer; input generation {t_gen:.1f} s not counted"),
         "seconds_per_layer": total,
     }
+
+
+def config_cpu_baseline(layers):
+    """The fp64 oracle, unmodified, on a bounded sample of every layer of a workload, each
+    scaled to the whole layer (the sample is stated per layer):
+    * H on a token subset (8192 tokens up to d_col 12288, 1024 beyond), scaled linearly
+      in the token count;
+    * prep (the oracle's Cholesky route) in full at each distinct d_col up to 12288, timed
+      once per workload and width; at d_col 49152 the leading 12288 block is factored and
+      the time scaled by (49152 / 12288)^3;
+    * the blocked sweep on 32 and on 128 rows, extrapolated linearly in the row count (a
+      sweep's per-column cost has a part independent of the rows); at d_col 49152 with the
+      12288-wide factor and scaled by (49152 / 12288)^2 (the trailing products dominate).
+    Input generation is not counted."""
+    import numpy as np
+
+    import synth
+    from oracle import gptq_oracle as o
+    out, prep_cache, t_all = [], {}, 0.0
+    for L in layers:
+        d = L.d_col
+        tok = min(L.n_tokens, 8192 if d <= 12288 else 1024)
+        dh = min(d, 12288)
+        scales = synth.channel_scales(L)
+        chunk = synth.x_as_f64(synth.x_chunk(L, 0, scales))[:tok]
+        t0 = time.perf_counter()
+        Hs = o.hessian([chunk])
+        t_h = (time.perf_counter() - t0) * L.n_tokens / tok
+        H = Hs[:dh, :dh] * (L.n_tokens / tok)
+        if dh not in prep_cache:
+            t0 = time.perf_counter()
+            U, _ = o.prepare_u(H, 0.01)
+            prep_cache[dh] = (time.perf_counter() - t0, U)
+        t_p, U = prep_cache[dh]
+        t_p *= (d / dh) ** 3
+        Wf = synth.w_as_f64(synth.weights(L))
+        p = o.Params(bits=L.bits, group_size=L.group_size, sym=L.sym)
+        ts = []
+        for nr in (32, 128):
+            t0 = time.perf_counter()
+            o.gptq_blocked(Wf[:nr, :dh], U, p)
+            ts.append(time.perf_counter() - t0)
+        per_row = (ts[1] - ts[0]) / 96.0
+        t_s = (ts[0] + per_row * (L.d_row - 32)) * (d / dh) ** 2
+        tot = t_h + t_p + t_s
+        t_all += tot
+        out.append({"name": L.name, "seconds_per_layer": tot, "hess_s": t_h, "prep_s": t_p, "sweep_s": t_s,
+                    "sample": f"H on {tok} of {L.n_tokens} tokens; prep at d={dh}"
+                              f"{' scaled by (d/12288)^3' if d > dh else ''}; sweep on 32 and 128 rows"
+                              f"{' of a 12288-wide slice, scaled by (d/12288)^2' if d > dh else ''}, extrapolated "
+                              f"to {L.d_row} rows"})
+        del H, Hs
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    w_tot = sum(L.d_row * L.d_col for L in layers)
+    return {"value": w_tot / t_all, "unit": "weights/s", "cores": cores, "kind": "oracle",
+            "sample": "per layer, see layers (fp64 NumPy oracle; prep timed once per distinct width)",
+            "seconds_all_layers": t_all, "layers": out}
 
 
 def linear_bench(args, g, q, W, r, d):
@@ -458,6 +532,9 @@ def config_bench(args, cfg: int):
         rec["block_weights_per_s"] = tot_w / (best * 1e-3)
         rec["value"] = rec["block_weights_per_s"]
         rec["value_note"] = "block of 7 layers in one gptq_quantize_layers call, best slot count, own inputs per layer"
+    if not args.no_cpu_baseline:
+        print(f"[config {cfg}] oracle baseline on the host", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = config_cpu_baseline(synth.config_layers(cfg))
     print(json.dumps(rec), flush=True)
 
 
@@ -595,8 +672,7 @@ def main():
                      "algorithmic_flops_per_launch": flops_hess},
     }
     mb = measured_mfma_busy()
-    if mb is not None:
-        rec["roofline"]["mfma_busy"] = mb
+    rec["roofline"]["mfma_busy"] = mb.get("hess_bf16_kernel") if mb else None
     if split is not None:
         rec["kernel_ms"] = split
         rec["phase_rooflines"] = phase_rooflines(split, r, d)
