@@ -221,8 +221,10 @@ def cpu_baseline(layer, sample_tokens: int, sample_rows: int):
 def config_cpu_baseline(layers):
     """The fp64 oracle, unmodified, on a bounded sample of every layer of a workload, each
     scaled to the whole layer (the sample is stated per layer):
-    * H on a token subset (8192 tokens up to d_col 12288, 1024 beyond), scaled linearly
-      in the token count;
+    * H on a token subset (8192 tokens), scaled linearly in the token count; at d_col
+      49152 on the leading 12288 channels of 1024 tokens, scaled by (49152 / 12288)^2 as
+      well (NumPy's X^T X of a 1024 x 49152 fp64 matrix ends in a segmentation fault
+      inside its BLAS call, on this image);
     * prep (the oracle's Cholesky route) in full at each distinct d_col up to 12288, timed
       once per workload and width; at d_col 49152 the leading 12288 block is factored and
       the time scaled by (49152 / 12288)^3;
@@ -242,9 +244,9 @@ def config_cpu_baseline(layers):
         scales = synth.channel_scales(L)
         chunk = synth.x_as_f64(synth.x_chunk(L, 0, scales))[:tok]
         t0 = time.perf_counter()
-        Hs = o.hessian([chunk])
-        t_h = (time.perf_counter() - t0) * L.n_tokens / tok
-        H = Hs[:dh, :dh] * (L.n_tokens / tok)
+        Hs = o.hessian([chunk[:, :dh]])
+        t_h = (time.perf_counter() - t0) * L.n_tokens / tok * (d / dh) ** 2
+        H = Hs * (L.n_tokens / tok)
         if dh not in prep_cache:
             t0 = time.perf_counter()
             U, _ = o.prepare_u(H, 0.01)
@@ -262,8 +264,11 @@ def config_cpu_baseline(layers):
         t_s = (ts[0] + per_row * (L.d_row - 32)) * (d / dh) ** 2
         tot = t_h + t_p + t_s
         t_all += tot
+        print(f"[oracle] {L.name}: {tot:.1f} s per layer (hess {t_h:.1f}, prep {t_p:.1f}, sweep {t_s:.1f})",
+              file=sys.stderr, flush=True)
         out.append({"name": L.name, "seconds_per_layer": tot, "hess_s": t_h, "prep_s": t_p, "sweep_s": t_s,
-                    "sample": f"H on {tok} of {L.n_tokens} tokens; prep at d={dh}"
+                    "sample": f"H on {tok} of {L.n_tokens} tokens"
+                              f"{' and 12288 channels, scaled by (d/12288)^2' if d > dh else ''}; prep at d={dh}"
                               f"{' scaled by (d/12288)^3' if d > dh else ''}; sweep on 32 and 128 rows"
                               f"{' of a 12288-wide slice, scaled by (d/12288)^2' if d > dh else ''}, extrapolated "
                               f"to {L.d_row} rows"})

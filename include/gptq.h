@@ -85,6 +85,16 @@ typedef struct gptq_context gptq_context;
 gptq_status gptq_context_create(int32_t n_slots, gptq_context** ctx);
 gptq_status gptq_context_destroy(gptq_context* ctx);
 
+/*
+ * Bound of the factorization's wait (see gptq_prepare_hinv's info = -2) in calls made
+ * with this context (gptq_prepare_hinv and gptq_quantize_layers), in polls of about 128
+ * clocks; a new context has 1 << 25 (about 2 s).  0 gives up before the first poll, so
+ * that every factorization wider than 128 columns reports info = -2 with all its
+ * kernels ending normally: a way to exercise a caller's handling of that error.
+ * Errors: ctx NULL or polls < 0 -> GPTQ_ERR_INVALID_ARG.
+ */
+gptq_status gptq_context_set_wait_limit(gptq_context* ctx, int32_t polls);
+
 /* Quantizer settings (host struct). */
 typedef struct {
     int32_t bits;        /* 3 (codes as a bitstream, eight in three bytes; d_col a multiple
@@ -155,9 +165,13 @@ gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype,
  *  info     device int32: 0, or k > 0 when the trailing principal submatrix of
  *           H + lambda I of order k is not positive definite (U is then undefined),
  *           or -1 when diag(H) holds a non-finite value, or -2 when a workgroup of
- *           the factorization waited longer than its bound (about 2 s) for the
- *           diagonal block that another workgroup of the same launch publishes
- *           (U is then undefined; not expected on an idle device).
+ *           the factorization waited longer than its bound (about 2 s, or what
+ *           gptq_context_set_wait_limit set) for the diagonal block that another
+ *           workgroup of the same launch publishes (U is then undefined).  The
+ *           publishing workgroup is dispatched before every workgroup that waits for
+ *           it and depends on no other, so it runs whenever one waits, also beside
+ *           concurrent work on the device: with the default bound -2 means a device
+ *           slowed some 10^5-fold.
  */
 size_t gptq_prepare_hinv_workspace_size(int64_t d_col);
 gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float percdamp,

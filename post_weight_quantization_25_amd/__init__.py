@@ -56,6 +56,7 @@ def _load():
         "gptq_prepare_hinv_workspace_size": (sz, [i64]),
         "gptq_context_create": (ctypes.c_int, [i32, ctypes.POINTER(vp)]),
         "gptq_context_destroy": (ctypes.c_int, [vp]),
+        "gptq_context_set_wait_limit": (ctypes.c_int, [vp, ctypes.c_int32]),
         "gptq_prepare_hinv": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp, sz, vp, vp, vp]),
         "gptq_quantize_workspace_size": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_quantize_layer": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Params),
@@ -134,6 +135,11 @@ class Context:
         if not self._ptr:
             raise ValueError("context is closed")
         return self._ptr
+
+    def set_wait_limit(self, polls: int):
+        """Bound of the factorization's wait in calls with this context, in polls of
+        about 128 clocks (0: give up at once, so that the call reports info = -2)."""
+        _check(lib.gptq_context_set_wait_limit(self.ptr, int(polls)), "gptq_context_set_wait_limit")
 
     def close(self):
         if self._ptr:

@@ -54,6 +54,13 @@ gptq_status gptq_context_create(int32_t n_slots, gptq_context** ctx) {
 
 gptq_status gptq_context_destroy(gptq_context* ctx) { return context_destroy(ctx); }
 
+gptq_status gptq_context_set_wait_limit(gptq_context* ctx, int32_t polls) {
+    if (ctx == nullptr || polls < 0) return GPTQ_ERR_INVALID_ARG;
+    ctx->prep.wait_polls = polls;
+    for (auto& sl : ctx->slot) sl.aux.wait_polls = polls;
+    return GPTQ_OK;
+}
+
 // A context serves the device it was made on.
 static gptq_status check_context(const gptq_context* ctx) {
     if (ctx == nullptr) return GPTQ_OK;

@@ -15,7 +15,14 @@ gptq_status hessian_launch(float* H, const void* X, gptq_dtype dt, int64_t n, in
 
 // Auxiliary stream of the factorization (the inverse's row blocks run on it beside the
 // chain) with the events that fork it from and join it to the caller's stream.
-struct PrepAux { hipStream_t s = nullptr; hipEvent_t fork = nullptr, join = nullptr; };
+// Bound of a factorization step's wait for the next diagonal block, in polls of about
+// 128 clocks (1 << 25: about 2 s at 2 GHz; the factorization of one block takes
+// microseconds).
+constexpr int32_t PREP_WAIT_POLLS = 1 << 25;
+struct PrepAux {
+    hipStream_t s = nullptr; hipEvent_t fork = nullptr, join = nullptr;
+    int32_t wait_polls = PREP_WAIT_POLLS;
+};
 
 size_t prep_ws_bytes(int64_t d_col);
 // aux: an auxiliary stream and its events, used by this call alone (from a caller-owned

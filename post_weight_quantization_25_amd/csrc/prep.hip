@@ -514,14 +514,11 @@ struct GemmD {
     // workgroups multiply the updated tile by the transposed inverse of the next
     // diagonal block once the G_DIAG0 workgroup has published it (*flag >= step)
     int* flag; int step;
+    int wait_polls;   // bound of that wait (0: give up at once)
     // capped grid (0: one workgroup per tile): vtiles = tiles per batch entry (tpb) x
     // entries, taken by the workgroups in turn
     int vtiles, tpb;
 };
-
-// Bound of the wait for the next diagonal block (s_sleep 2 = 128 clocks per poll:
-// about 2 s at 2 GHz; the factorization of one block takes microseconds).
-constexpr int PANEL_SPIN_LIMIT = 1 << 25;
 
 // Operand chunk of GD_BK columns of k: 64 rows (m or n) x 32 k, as 4 double2 per thread.
 template <bool KMAJOR>
@@ -598,16 +595,24 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
         while (r * (r + 1) / 2 > t) --r;
         c = t - r * (r + 1) / 2;
     };
+    // t-th tile of the lower trapezoid {(mi, nj): nj <= mi < ntm, nj < w}, row-major: a
+    // triangle of w rows, then rows of w tiles
+    auto trap = [&](int t, int w, int& r, int& c) {
+        const int tt = w * (w + 1) / 2;
+        if (t < tt) tri(t, r, c);
+        else { r = w + (t - tt) / w; c = (t - tt) % w; }
+    };
     if (g.flags & G_PANEL1) {
         // tile (0, 0) first (the next diagonal block), then the tiles right of block
         // column 0, then block column 0 (the next panel, which waits for the block): in
         // a large update those workgroups start after the block is published
-        const int inner = (g.ntm - 1) * g.ntm / 2;
+        const int w = g.ntn - 1;
+        const int inner = (g.ntm <= g.ntn) ? (g.ntm - 1) * g.ntm / 2 : w * (w + 1) / 2 + (g.ntm - 1 - w) * w;
         if (bid == 0) { mi = 0; nj = 0; }
-        else if (bid <= inner) { tri(bid - 1, mi, nj); ++mi; ++nj; }
+        else if (bid <= inner) { trap(bid - 1, w, mi, nj); ++mi; ++nj; }
         else { mi = bid - inner; nj = 0; }
     } else if (g.flags & G_LOWER_C) {
-        tri(bid, mi, nj);
+        trap(bid, g.ntn, mi, nj);
     } else if (g.flags & G_TRI_B) {          // k >= n0 (B lower) or k < n0 + 64 (B^T lower)
         const int q = bid / g.ntm;
         nj = (g.flags & G_BT) ? g.ntn - 1 - q : q;
@@ -745,15 +750,16 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
                     }
                     pa[r * DLD + cc] = v;
                 }
-        // wait (bounded) until the inverse of the next diagonal block is published
+        // wait (at most wait_polls polls of about 128 clocks) until the inverse of the next
+        // diagonal block is published
         if (tid == 0) {
-            int spins = 0;
-            while (__hip_atomic_load(g.flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < g.step) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins == PANEL_SPIN_LIMIT) {
+            for (int polls = 0;; ++polls) {
+                if (polls >= g.wait_polls) {
                     atomicCAS(g.info, 0, -2);
                     break;
                 }
+                if (__hip_atomic_load(g.flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= g.step) break;
+                __builtin_amdgcn_s_sleep(2);
             }
         }
         __syncthreads();
@@ -858,6 +864,7 @@ __global__ __launch_bounds__(256) void gemm_f64_capped_kernel(GemmD g) {
 struct PrepCtx {
     double* A; double* X; double* T; int64_t d;
     int32_t* info; int* flag; hipStream_t s;
+    int32_t wait_polls;
 };
 
 static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int64_t lda, const double* B,
@@ -867,9 +874,11 @@ static gptq_status gemm(PrepCtx& c, double* C, int64_t ldc, const double* A, int
     if (M <= 0 || N <= 0 || nbatch <= 0) return GPTQ_OK;
     const int ntm = (M + GD_BM - 1) / GD_BM, ntn = (N + GD_BM - 1) / GD_BM;
     GemmD g{C, ldc, A, lda, B, ldb, M, N, K, alpha, beta, flags, sA, sB, sC, M_last, nbatch,
-            c.A, c.X, c.d, k1, n1, c.info, ntm, ntn, c.flag, step, 0, 0};
-    if ((flags & G_LOWER_C) && N != M) return GPTQ_ERR_INVALID_ARG;
-    const int ntiles = (flags & G_LOWER_C) ? ntm * (ntm + 1) / 2 : ntm * ntn;
+            c.A, c.X, c.d, k1, n1, c.info, ntm, ntn, c.flag, step, c.wait_polls, 0, 0};
+    // a lower-triangular C: the tiles on and below the diagonal of an M x N block, N <= M
+    // (a trapezoid when N < M)
+    if ((flags & G_LOWER_C) && N > M) return GPTQ_ERR_INVALID_ARG;
+    const int ntiles = (flags & G_LOWER_C) ? ntn * (ntn + 1) / 2 + (ntm - ntn) * ntn : ntm * ntn;
     dim3 grid((unsigned)ntiles, 1, nbatch);
     if (max_wg > 0 && (int64_t)ntiles * nbatch > max_wg && !(flags & (G_DIAG0 | G_PANEL1))) {
         g.vtiles = ntiles * nbatch;
@@ -925,9 +934,14 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // Block 0 and its panel have launches of their own; every later diagonal block and
 // its panel are finished inside the trailing update of the step before (tile (0, 0)
 // factors the block, the tiles below it apply its inverse), so each step of the
-// chain is one launch.  (Deferring the trailing update to blocks of 256 columns, so
-// that each step inside a block updates only the rest of that block, measured
-// slower: the rank-256 update then lies on the chain.)
+// chain is one launch.  From d = DEFER_MIN_D on, the trailing update is deferred to
+// outer blocks of DEFER_W columns: each step inside an outer block updates only the
+// rest of that block (its columns, all rows below), and the step of the block's last
+// panel applies the block's DEFER_W columns to the whole matrix after it (one product
+// with K = DEFER_W, whose tile (0, 0) and block column 0 again form the next block and
+// panel).  Every element receives the same products, grouped differently.  (At
+// d = 4096 this measured slower: the chain, not the matrix traffic, bounds the time
+// there, and the K = 256 update lies on it.)
 //
 // The inverse is assembled by row blocks B_0, B_1, .., B_last: B_0 = [0, h) with h
 // the largest 64 * 2^i below d, and each next block the largest 64 * 2^i below what
@@ -944,6 +958,19 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // remain on the caller's stream.  (A last block of 512 or 256 columns at d = 4096
 // measured slower than 1024: the auxiliary stream then still works on the blocks
 // before it when the loop ends.)
+// Deferral of the trailing update (see cholinv) from d = DEFER_MIN_D on, in outer blocks
+// of DEFER_W columns.  A step's update of the whole trailing matrix reads and writes it
+// for 2 * 64 flops per element (8 flops per byte in fp64: bound by HBM once the matrix
+// leaves the caches); deferred, the update after an outer block does 2 * DEFER_W.
+#ifndef DEFER_MIN_D
+#define DEFER_MIN_D 8192
+#endif
+#ifndef DEFER_W
+#define DEFER_W 512
+#endif
+#ifndef AUX_MAX_WG_DEFER
+#define AUX_MAX_WG_DEFER 0
+#endif
 #ifndef AUX_FORK_REST
 #define AUX_FORK_REST 2048
 #endif
@@ -971,6 +998,7 @@ static gptq_status cholinv(PrepCtx& c, const PrepAux* aux) {
         s0 += b;
     }
     const int64_t h = bs[1], sl = bs[nb], nl = d - sl;
+    if (h * h + (d - h) * sl + nl * nl > d * d) return GPTQ_ERR_INVALID_ARG;   // scratch bound
     // product scratch (doubles): the auxiliary levels (h * h), Trest (rows h .. d, row
     // pitch sl, columns 0 .. sl), the last block's levels (nl * nl); with m = d - h <= h:
     // h * h + m * sl + nl * nl <= h * h + m * d + m * m <= d * d
@@ -983,7 +1011,9 @@ static gptq_status cholinv(PrepCtx& c, const PrepAux* aux) {
     // same points (stream order then gives every dependency) with an uncapped grid.
     PrepCtx ca = c;
     if (aux) ca.s = aux->s;
-    const int aux_wg = aux ? AUX_MAX_WG : 0;
+    // (the cap keeps slots free for the latency-bound chain at moderate d; with the
+    // deferred update the auxiliary products run mostly after the chain, uncapped)
+    const int aux_wg = aux ? (d < DEFER_MIN_D ? AUX_MAX_WG : AUX_MAX_WG_DEFER) : 0;
     // block i's columns are final once the step that forms the panel of its last 64
     // columns has been enqueued (step bs[i + 1] / 64 - 2; before the loop when negative)
     int64_t fork_step[64];
@@ -1019,17 +1049,29 @@ static gptq_status cholinv(PrepCtx& c, const PrepAux* aux) {
     int nf = 0;   // blocks handed to the auxiliary stream
     while (nf < nb && fork_step[nf] < 0)
         if ((st = fork(nf++)) != GPTQ_OK) return st;
+    // deferred trailing update (large d): inside an outer block of DEFER_W columns each
+    // step updates only the rest of the outer block (all rows below), and the step of the
+    // block's last panel applies all DEFER_W columns to the matrix after the block at once
+    const int64_t defer_w = (d >= DEFER_MIN_D) ? DEFER_W : PNB;
     for (int64_t k0 = 0; k0 < d; k0 += PNB) {
         const int n = (int)std::min<int64_t>(PNB, d - k0);
         const int64_t rest = d - k0 - n;
         if (rest <= 0) break;
+        const int64_t K0 = k0 / defer_w * defer_w;                  // the outer block [K0, oe)
+        const int64_t oe = std::min<int64_t>(K0 + defer_w, d);
         // trailing update; tile (0, 0) factors diagonal block k+1, the tiles below it
         // form panel k+1
-        double* L21 = c.A + (k0 + n) * d + k0;
         double* A22 = c.A + (k0 + n) * d + k0 + n;
-        if ((st = gemm(c, A22, d, L21, d, L21, d, (int)rest, (int)rest, n, -1.0, 1.0,
-                       G_BT | G_LOWER_C | G_DIAG0 | G_PANEL1, 1, 0, 0, 0, 0, k0 + n,
-                       (int)std::min<int64_t>(PNB, rest), (int)(k0 / PNB) + 1)) != GPTQ_OK)
+        const bool inner = k0 + n < oe;
+        const int64_t kb = inner ? k0 : K0;                          // update columns kb .. k0 + n
+        double* L21 = c.A + (k0 + n) * d + kb;
+        const int kw = (int)(k0 + n - kb);
+        const int flg = G_BT | G_LOWER_C | G_DIAG0 | G_PANEL1;
+        const int n1 = (int)std::min<int64_t>(PNB, rest), step = (int)(k0 / PNB) + 1;
+        // inner: the rest of the outer block; else the whole trailing matrix
+        const int64_t ncols = inner ? oe - (k0 + n) : rest;
+        if ((st = gemm(c, A22, d, L21, d, L21, d, (int)rest, (int)ncols, kw, -1.0, 1.0, flg, 1, 0, 0, 0, 0, k0 + n,
+                       n1, step)) != GPTQ_OK)
             return st;
         while (nf < nb && fork_step[nf] == k0 / PNB)
             if ((st = fork(nf++)) != GPTQ_OK) return st;
@@ -1068,6 +1110,7 @@ gptq_status prep_launch(const float* H, float* U, int64_t d, float percdamp, voi
     const size_t t = align256(t_bytes(d));
     double* lam = reinterpret_cast<double*>(p + 2 * dd + t);
     c.d = d; c.info = info; c.s = s;
+    c.wait_polls = aux ? aux->wait_polls : PREP_WAIT_POLLS;
     c.flag = reinterpret_cast<int*>(lam + 1);    // inside the 256 reserved bytes
 
     prep_lambda_kernel<<<1, 1024, 0, s>>>(H, d, percdamp, lam, info, c.flag);

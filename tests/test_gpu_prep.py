@@ -102,3 +102,64 @@ def test_prep_with_context_is_bit_identical(d):
     Uo, _ = o.prepare_u(H32.astype(np.float64), 0.01)
     rowmax = np.max(np.abs(Uo), axis=1, keepdims=True)
     assert float(np.max(np.abs(U2.cpu().numpy() - Uo) / rowmax)) <= 1e-6
+
+
+@pytest.mark.parametrize("d", [129, 520, 3000])
+def test_prep_wait_bound_reports_minus_two(d):
+    """A wait bound of 0 polls (set from the host on the context) makes every panel
+    workgroup give up before its first poll: info = -2, every kernel ends normally, and
+    the same context with the default bound then gives the same U as a call without
+    a context."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    H32 = _h(d, 2 * d, 11)
+    Hd = torch.from_numpy(H32).cuda()
+    U1, i1 = g.prepare_hinv(Hd, 0.01)
+    with g.Context(1) as ctx:
+        ctx.set_wait_limit(0)
+        _, i2 = g.prepare_hinv(Hd, 0.01, ctx=ctx)
+        torch.cuda.synchronize()
+        log(f"wait bound 0 at d={d}: info {int(i2.item())}")
+        assert int(i2.item()) == -2
+        ctx.set_wait_limit(1 << 25)
+        U3, i3 = g.prepare_hinv(Hd, 0.01, ctx=ctx)
+        torch.cuda.synchronize()
+    assert int(i1.item()) == int(i3.item()) == 0
+    assert torch.equal(U1, U3)
+
+
+def test_prep_without_a_wait_ignores_the_bound():
+    """At d <= 128 no workgroup waits (one step, no panel tiles): info stays 0."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    H32 = _h(128, 256, 12)
+    Hd = torch.from_numpy(H32).cuda()
+    U1, _ = g.prepare_hinv(Hd, 0.01)
+    with g.Context(1) as ctx:
+        ctx.set_wait_limit(0)
+        U2, i2 = g.prepare_hinv(Hd, 0.01, ctx=ctx)
+        torch.cuda.synchronize()
+    assert int(i2.item()) == 0
+    assert torch.equal(U1, U2)
+
+
+@pytest.mark.parametrize("d", [8192, 8293])
+def test_prep_parity_deferred_update(d):
+    """From d = 8192 on the factorization defers its trailing update to outer blocks of
+    256 columns; 8293 ends in a partial outer block and a ragged tile."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    rng = np.random.default_rng([13, d])
+    G = rng.standard_normal((d, 256))
+    H = (G @ G.T) / 256.0 + np.diag(rng.lognormal(0.0, 1.0, size=d))
+    H32 = H.astype(np.float32)
+    Uo, _ = o.prepare_u(H32.astype(np.float64), 0.01)
+    U, info = g.prepare_hinv(torch.from_numpy(H32).cuda(), 0.01)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    Ug = U.cpu().numpy()
+    assert np.all(np.tril(Ug, -1) == 0.0)
+    rowmax = np.max(np.abs(Uo), axis=1, keepdims=True)
+    err = float(np.max(np.abs(Ug - Uo) / rowmax))
+    log(f"prep parity d={d} (deferred update): max |dU| / rowmax = {err:.3e}")
+    assert err <= 1e-6
