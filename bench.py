@@ -104,11 +104,11 @@ def measured_mfma_busy():
     return None if t is None else t.get("mfma_busy")
 
 
-def phase_rooflines(split, r, d):
+def phase_rooflines(split, r, d, bits: int = 4, group: int = 128):
     """Algorithmic rates of the sweep (HBM) and the trailing update (16-bit MFMA) from the
     per-phase kernel times.  Sweep bytes per layer: the fp32 working copy read once (4 B),
-    the scaled fp16 error pair written (4 B), half a byte of codes per weight, a scale and
-    a zero per group, the diagonal blocks of U (d x 128 fp32).  Trailing-kernel flops: the
+    the scaled fp16 error pair written (4 B), bits / 8 bytes of codes per weight, a scale
+    and a zero per group, the diagonal blocks of U (d x 128 fp32).  Trailing-kernel flops: the
     products after each 512-column super-block, 2 r sum_s 512 (d - s1) (the updates
     inside a super-block run in the sweep kernel)."""
     out = {}
@@ -116,7 +116,8 @@ def phase_rooflines(split, r, d):
     traffic = _committed(SWEEP_TRAFFIC_FILE) if (r, d) == (4096, 4096) else None
     busy = measured_mfma_busy() if (r, d) == (4096, 4096) else None
     if sweep_ms:
-        byt = r * d * (4 + 4 + 0.5) + r * (d // 128) * 4 + d * 128 * 4
+        ng = 1 if group <= 0 else d // group
+        byt = r * d * (4 + 4 + bits / 8) + r * ng * 4 + d * 128 * 4
         gbs = byt / (sweep_ms * 1e-3) / 1e9
         out["sweep"] = {"bound": "hbm", "algorithmic_bytes": byt, "ms": sweep_ms, "achieved": gbs,
                         "unit": "GB/s", "peak": HBM_GBS, "frac": gbs / HBM_GBS,
@@ -365,9 +366,11 @@ def _upload(L, dev):
     return X, W
 
 
-def layer_bench(g, L, dev, steps: int, warmup: int, damp: float = 0.01):
+def layer_bench(g, L, dev, steps: int, warmup: int, damp: float = 0.01, split: bool = True):
     """One layer's step (zero H, Hessian, prep, quantize, dequantize) with inputs resident:
-    warm-up steps, then the mean per phase over timed steps (HIP events on the stream)."""
+    warm-up steps, then the mean per phase over timed steps (HIP events on the stream);
+    with ``split``, one more profiled step splits the quantize phase into the sweep, the
+    trailing update and their set-up kernels."""
     import numpy as np
     import torch
     t0 = time.perf_counter()
@@ -414,10 +417,17 @@ def layer_bench(g, L, dev, steps: int, warmup: int, damp: float = 0.01):
     ph = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
           for i, nm in enumerate(["hess", "prep", "quant", "deq"])}
     ms_layer = ph["hess"] + ph["prep"] + ph["quant"]
-    return {"name": L.name, "d_row": r, "d_col": d, "n_tokens": n, "bits": L.bits, "group_size": L.group_size,
-            "sym": bool(L.sym), "phases_ms": ph, "ms_per_layer": ms_layer,
-            "ms_per_layer_quantize_only": ph["prep"] + ph["quant"],
-            "weights_per_s": r * d / (ms_layer * 1e-3), "input_generation_s": t_gen}
+    rec = {"name": L.name, "d_row": r, "d_col": d, "n_tokens": n, "bits": L.bits, "group_size": L.group_size,
+           "sym": bool(L.sym), "phases_ms": ph, "ms_per_layer": ms_layer,
+           "ms_per_layer_quantize_only": ph["prep"] + ph["quant"],
+           "weights_per_s": r * d / (ms_layer * 1e-3), "input_generation_s": t_gen}
+    if split:
+        ks, _ = kernel_split(step, steps=1)
+        rec["kernel_ms"] = ks
+        hfl = float(n) * d * (d + 1)
+        rec["hess_frac_bf16"] = hfl / (ph["hess"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+        rec["phase_rooflines"] = phase_rooflines(ks, r, d, L.bits, L.group_size)
+    return rec
 
 
 def block_bench(g, layers, dev, steps: int, warmup: int, shared: bool):
@@ -512,7 +522,7 @@ def config_bench(args, cfg: int):
     layers = []
     for L in synth.config_layers(cfg):
         print(f"[config {cfg}] {L.name} {L.d_row}x{L.d_col} n={L.n_tokens}: start", file=sys.stderr, flush=True)
-        res = layer_bench(g, L, dev, args.steps, args.warmup)
+        res = layer_bench(g, L, dev, args.steps, args.warmup, split=not args.no_kernel_split)
         print(f"[config {cfg}] {L.name}: {res['ms_per_layer']:.3f} ms/layer "
               f"(inputs {res['input_generation_s']:.1f} s)", file=sys.stderr, flush=True)
         layers.append(res)
