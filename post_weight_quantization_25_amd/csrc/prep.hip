@@ -568,6 +568,140 @@ GPTQ_DEV void gd_store(double* S, int tid, const double2 (&v)[4]) {
 constexpr int GD_TILE = GD_BM * GD_LD;
 constexpr int GD_LDS = (4 * GD_TILE > DIAG_LDS_DOUBLES) ? 4 * GD_TILE : DIAG_LDS_DOUBLES;
 
+// --------------------------------------------------------------------------
+// Direct global -> LDS operand ring for whole 64 x 64 tiles of C += A op(B) with the k
+// range a multiple of 16: four stages of 16 k (16 KB each), filled by
+// global_load_lds_dwordx4 three stages ahead; no register staging and one barrier per
+// stage.  A is row-major (k contiguous), stored [64 rows][16 k] with the 16-byte chunk c
+// of row r at chunk position c ^ ((r / 2) % 8); B is either the same (op = transpose,
+// B given as rows n) or k-major (B[k][n], n contiguous), stored [16 k][64 n] with chunk
+// c of k row k at position c ^ 8 (k % 2).  Either way the MFMA operand reads (16 rows or
+// columns at 2 consecutive k per half-wave) hit distinct banks.  The MFMAs and their
+// order are those of the register-staged loop (4 k per MFMA, k increasing), so the
+// result is the same bit for bit.
+constexpr int GX_BK = 16, GX_NST = 4, GX_DMA = 4;          // k per stage, stages, loads per wave and stage
+constexpr int GX_OP = GD_BM * GX_BK;                       // doubles of one operand in a stage
+constexpr int GX_ST = 2 * GX_OP;                           // doubles of a stage
+constexpr int GX_VM = (GX_NST - 2) * GX_DMA;               // loads left in flight at a stage wait
+static_assert(GX_NST * GX_ST <= GD_LDS && GX_NST * GX_ST <= 4 * GD_BM * GD_LD,
+              "the operand ring fits in both kernels' LDS");
+
+GPTQ_DEV int gx_swz(int r) { return (r >> 1) & 7; }        // row-major operands
+GPTQ_DEV int gx_swzk(int k) { return (k & 1) << 3; }       // k-major B
+
+struct GxCopy {
+    uint32_t voff[GX_DMA];     // per-lane byte offsets (from the operand's origin at k = kb)
+    const double* abase;       // A row m0 at k = kb; B row n0 at k = kb, or B row kb at column n0
+    const double* bbase;
+    int64_t bstage;            // doubles between B's stages
+    uint32_t m0base;           // LDS byte address of the wave's share of slot 0
+};
+
+// wave w, loads 0 and 1: A rows 8 (2 w + i) .. + 7, lane l row + l / 8, chunk position
+// l % 8.  Loads 2 and 3: B the same (transposed), or k-major: k rows 2 (2 w + i - 2) .. + 1,
+// lane l k row + l / 32, chunk position l % 32.
+template <bool BKMAJOR>
+GPTQ_DEV GxCopy gx_setup(const GemmD& g, int m0, int n0, int kb, int wave, int lane, const double* ring) {
+    GxCopy x;
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    x.abase = g.A + (int64_t)m0 * g.lda + kb;
+    x.bbase = BKMAJOR ? g.B + (int64_t)kb * g.ldb + n0 : g.B + (int64_t)n0 * g.ldb + kb;
+    x.bstage = BKMAJOR ? (int64_t)GX_BK * g.ldb : GX_BK;
+    x.m0base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) double*)ring + (uint32_t)(w * 2048);
+#pragma unroll
+    for (int i = 0; i < GX_DMA; ++i) {
+        if (i < 2 || !BKMAJOR) {
+            const int r = 8 * (2 * w + (i & 1)) + (lane >> 3);
+            const int c = (lane & 7) ^ gx_swz(r);
+            const int64_t ld = (i >> 1) ? g.ldb : g.lda;
+            x.voff[i] = (uint32_t)(((int64_t)r * ld + 2 * c) * 8);
+        } else {
+            const int k = 2 * (2 * w + (i & 1)) + (lane >> 5);
+            const int c = (lane & 31) ^ gx_swzk(k);
+            x.voff[i] = (uint32_t)(((int64_t)k * g.ldb + 2 * c) * 8);
+        }
+    }
+    return x;
+}
+
+template <int SLOT>
+GPTQ_DEV void gx_issue(const GxCopy& x, int st) {
+    const double* a = x.abase + st * GX_BK;
+    const double* b = x.bbase + st * x.bstage;
+    dma16<(uint32_t)(SLOT * GX_ST * 8 + 0)>(x.voff[0], a, x.m0base);
+    dma16<(uint32_t)(SLOT * GX_ST * 8 + 1024)>(x.voff[1], a, x.m0base);
+    dma16<(uint32_t)(SLOT * GX_ST * 8 + GX_OP * 8)>(x.voff[2], b, x.m0base);
+    dma16<(uint32_t)(SLOT * GX_ST * 8 + GX_OP * 8 + 1024)>(x.voff[3], b, x.m0base);
+}
+
+struct GxFrags { double a[4][2], b[4][2]; };   // [k step][i or j]
+
+template <bool BKMAJOR>
+GPTQ_DEV void gx_read(const double* stg, int wr, int wc, int lane, GxFrags& f) {
+#pragma unroll
+    for (int s = 0; s < GX_BK / 4; ++s) {
+        const int k = 4 * s + (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = wr * 32 + i * 16 + (lane & 15);
+            f.a[s][i] = stg[r * GX_BK + 2 * ((k >> 1) ^ gx_swz(r)) + (k & 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = wc * 32 + j * 16 + (lane & 15);
+            if constexpr (BKMAJOR)
+                f.b[s][j] = stg[GX_OP + k * GD_BM + 2 * ((r >> 1) ^ gx_swzk(k)) + (r & 1)];
+            else
+                f.b[s][j] = stg[GX_OP + r * GX_BK + 2 * ((k >> 1) ^ gx_swz(r)) + (k & 1)];
+        }
+    }
+}
+
+GPTQ_DEV void gx_mfma(const GxFrags& f, f64x4_t (&acc)[2][2]) {
+#pragma unroll
+    for (int s = 0; s < GX_BK / 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
+}
+
+// acc += A[m0 .. + 63][kb .. ke) op(B)[kb .. ke)[n0 .. + 63] through the ring
+template <bool BKMAJOR>
+GPTQ_DEV void gx_tile(const GemmD& g, int m0, int n0, int kb, int ke, double* lds, f64x4_t (&acc)[2][2]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int nst = (ke - kb) / GX_BK;
+    // loads of stages past the last re-load the last one (addresses stay inside the
+    // operands), so that every step leaves the same number of loads in flight
+    auto t0 = [&](int st) { return st < nst ? st : nst - 1; };
+    const GxCopy x = gx_setup<BKMAJOR>(g, m0, n0, kb, wave, lane, lds);
+    static_for<0, GX_NST - 1>([&](auto I) { gx_issue<decltype(I)::value>(x, t0(decltype(I)::value)); });
+    wait_vm_lgkm0<GX_VM>();
+    __syncthreads();
+    gx_issue<GX_NST - 1>(x, t0(GX_NST - 1));
+    GxFrags f0, f1;
+    gx_read<BKMAJOR>(lds, wr, wc, lane, f0);
+    for (int st = 0; st < nst; st += GX_NST) {
+        static_for<0, GX_NST>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if (st + u < nst) {
+                // stage st + u + 1 has landed and every wave is done with slot u
+                wait_vm_lgkm0<GX_VM>();
+                __syncthreads();
+                gx_issue<u>(x, t0(st + u + GX_NST));
+                GxFrags& cur = (u & 1) ? f1 : f0;
+                GxFrags& nxt = (u & 1) ? f0 : f1;
+                gx_read<BKMAJOR>(lds + ((u + 1) % GX_NST) * GX_ST, wr, wc, lane, nxt);
+                gx_mfma(cur, acc);
+            }
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the trailing re-loads land before the ring is reused
+    __syncthreads();
+}
+
 // One output tile (bid within batch entry bz).  lds: the operand double buffers, and
 // the diagonal routine's buffers in the G_DIAG0 workgroup.  FUSED: the G_DIAG0 /
 // G_PANEL1 paths are compiled in.
@@ -664,7 +798,16 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
     };
     if (pre && diag0) load_c();
 
-    const int nch = (ke > kb) ? (ke - kb + GD_BK - 1) / GD_BK : 0;
+#ifndef GD_DMA
+#define GD_DMA 1
+#endif
+    // whole tiles (even row pitches, 16-byte aligned operands, k range a multiple of 16)
+    // take the direct-load ring
+    const bool dma = GD_DMA && full && !diag0 && !panel && ke > kb && ((ke - kb) % GX_BK) == 0 &&
+                     ((g.lda | g.ldb) & 1) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15) == 0;
+    if (dma) gx_tile<BKMAJOR>(g, m0, n0, kb, ke, lds, acc);
+    const int nch = (!dma && ke > kb) ? (ke - kb + GD_BK - 1) / GD_BK : 0;
     double2 va[4], vb[4];
     if (nch > 0) {
         gd_load<false>(g.A, g.lda, g.M, m0, kb, ke, tid, va);
@@ -842,7 +985,7 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
 
 template <bool BKMAJOR>
 __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
-    __shared__ double lds[GD_LDS];
+    __shared__ __align__(16) double lds[GD_LDS];
     __shared__ int fail_s;
     gemm_f64_tile<BKMAJOR, true>(g, blockIdx.x, blockIdx.z, lds, fail_s);
 }
@@ -851,7 +994,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmD g) {
 // G_DIAG0 / G_PANEL1 work.
 template <bool BKMAJOR>
 __global__ __launch_bounds__(256) void gemm_f64_capped_kernel(GemmD g) {
-    __shared__ double lds[4 * GD_TILE];
+    __shared__ __align__(16) double lds[4 * GD_TILE];
     __shared__ int fail_s;
     for (int vt = blockIdx.x; vt < g.vtiles; vt += gridDim.x) {
         __syncthreads();   // the previous tile's last LDS reads are done
@@ -963,7 +1106,7 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // for 2 * 64 flops per element (8 flops per byte in fp64: bound by HBM once the matrix
 // leaves the caches); deferred, the update after an outer block does 2 * DEFER_W.
 #ifndef DEFER_MIN_D
-#define DEFER_MIN_D 8192
+#define DEFER_MIN_D 6144
 #endif
 #ifndef DEFER_W
 #define DEFER_W 512
