@@ -174,6 +174,9 @@ gptq_status gptq_hessian_accumulate(float* H, const void* X, gptq_dtype x_dtype,
  *           slowed some 10^5-fold.
  */
 size_t gptq_prepare_hinv_workspace_size(int64_t d_col);
+/* The same size under the name with a U type: u_dtype must be GPTQ_F32 (U is fp32; any
+ * other value gives 0). */
+size_t gptq_prepare_hinv_workspace(int64_t d_col, gptq_dtype u_dtype);
 gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float percdamp,
                               void* ws, size_t ws_bytes, int32_t* info, gptq_context* ctx, void* stream);
 
@@ -213,6 +216,8 @@ gptq_status gptq_prepare_hinv(const float* H, float* U, int64_t d_col, float per
  * Rows are independent given U; d_row == 0 is a no-op.
  */
 size_t gptq_quantize_workspace_size(int64_t d_row, int64_t d_col, const gptq_params* p);
+/* The same size under the shorter name. */
+size_t gptq_quantize_workspace(int64_t d_row, int64_t d_col, const gptq_params* p);
 gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col,
                                 const float* U, const gptq_params* p,
                                 uint8_t* codes, uint16_t* scales_f16, uint16_t* zeros_f16,

@@ -47,6 +47,10 @@ size_t gptq_prepare_hinv_workspace_size(int64_t d_col) {
     return prep_ws_bytes(d_col);
 }
 
+size_t gptq_prepare_hinv_workspace(int64_t d_col, gptq_dtype u_dtype) {
+    return u_dtype == GPTQ_F32 ? gptq_prepare_hinv_workspace_size(d_col) : 0;
+}
+
 gptq_status gptq_context_create(int32_t n_slots, gptq_context** ctx) {
     if (ctx == nullptr || n_slots < 1 || n_slots > GPTQ_LAYERS_MAX_SLOTS) return GPTQ_ERR_INVALID_ARG;
     return context_create(n_slots, ctx);
@@ -85,6 +89,10 @@ size_t gptq_quantize_workspace_size(int64_t d_row, int64_t d_col, const gptq_par
     (void)p;
     if (d_row <= 0 || d_col <= 0) return 0;
     return quant_ws_bytes(d_row, d_col);
+}
+
+size_t gptq_quantize_workspace(int64_t d_row, int64_t d_col, const gptq_params* p) {
+    return gptq_quantize_workspace_size(d_row, d_col, p);
 }
 
 gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,

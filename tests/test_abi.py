@@ -48,6 +48,8 @@ def lib():
         "gptq_hessian_workspace_size": (sz, [i64, i64]),
         "gptq_hessian_accumulate": (ctypes.c_int, [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp]),
         "gptq_prepare_hinv_workspace_size": (sz, [i64]),
+        "gptq_prepare_hinv_workspace": (sz, [i64, ctypes.c_int]),
+        "gptq_quantize_workspace": (sz, [i64, i64, ctypes.POINTER(Params)]),
         "gptq_context_create": (ctypes.c_int, [i32, ctypes.POINTER(vp)]),
         "gptq_context_destroy": (ctypes.c_int, [vp]),
         "gptq_context_set_wait_limit": (ctypes.c_int, [vp, i32]),
@@ -79,7 +81,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gptq_context_create", "gptq_context_destroy", "gptq_context_set_wait_limit",
         "gptq_hessian_workspace_size", "gptq_hessian_accumulate",
-        "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
+        "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv_workspace", "gptq_prepare_hinv",
+        "gptq_quantize_workspace",
         "gptq_quantize_workspace_size", "gptq_quantize_layer", "gptq_quantize_layer_noalloc",
         "gptq_quantize_layers_workspace_size", "gptq_quantize_layers",
         "gptq_obq_workspace_size", "gptq_obq_layer", "gptq_dequantize_e2m1",
@@ -112,6 +115,11 @@ def test_workspace_sizes(lib):
     p = lib.Params(4, 128, 0, 128)
     assert lib.gptq_quantize_workspace_size(0, 4096, ctypes.byref(p)) == 0
     assert lib.gptq_quantize_workspace_size(4096, 4096, ctypes.byref(p)) >= 4096 * 4096 * 4
+    # the shorter names give the same sizes; U is fp32 only
+    assert lib.gptq_prepare_hinv_workspace(4096, F32) == lib.gptq_prepare_hinv_workspace_size(4096)
+    assert lib.gptq_prepare_hinv_workspace(4096, BF16) == 0
+    assert lib.gptq_quantize_workspace(4096, 4096, ctypes.byref(p)) == \
+        lib.gptq_quantize_workspace_size(4096, 4096, ctypes.byref(p))
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation rejects the call first
