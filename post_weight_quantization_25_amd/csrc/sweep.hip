@@ -27,6 +27,7 @@
 // per 16-byte load), loaded while the block's steps run.  Rows are independent, so no
 // other workgroup is involved.
 
+#include <type_traits>
 #include <utility>
 
 #include "quant_internal.h"
@@ -40,7 +41,8 @@ constexpr int UT_N = 64;            // columns of U per update chunk
 
 template <int SRC>
 GPTQ_DEV float row_bcast(float v) {  // DPP row_newbcast: lane SRC of each 16-lane row to the whole row
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + SRC, 0xf, 0xf, false));
+    // (every lane reads a valid source, so no old value is needed)
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xf, 0xf, false));
 }
 template <int CTRL>
 GPTQ_DEV float dpp_f(float v) {
@@ -175,7 +177,10 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     const int nb = (int)((a.s1 - b0) < QB ? (a.s1 - b0) : QB);
     const int cb = (int)(b0 - a.s0);       // the block's first column in Wl
     float w[SSLOTS], e[SSLOTS];
-    int cv[SSLOTS];
+    // the code of each owned column: the E2M1 code, or for the integer grids q + zf as a
+    // float (converted once at the block end, off the steps' path)
+    using CodeT = typename std::conditional<FP4, int, float>::type;
+    CodeT cv[SSLOTS];
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) {
         e[i] = 0.f;
@@ -219,7 +224,11 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) { ucA[k] = u0[k]; ucA[4 + k] = u1[k]; }
     }
-    float idc = invd[0];
+    // 1 / U[j][j] of this lane's columns j = q + 16 i: the owner of column j divides its
+    // error with its own copy, so no step reads the reciprocal
+    float idv[SSLOTS];
+#pragma unroll
+    for (int i = 0; i < SSLOTS; ++i) idv[i] = invd[SL * i + q];
 
     // All 128 steps run: past nb (the last block of a width that is not a multiple of
     // 128) the weights, U and 1 / U[j][j] are 0, so those steps change nothing.
@@ -231,7 +240,6 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         // prefetch the coefficients of step j + 1, only the slots it uses (a loaded
         // value left unused lets the compiler reuse its register while the load is in
         // flight, which costs a wait every step)
-        float idn = 0.f;
         if constexpr (j + 1 < QB) {
             constexpr int i1 = (j + 1) >> 4;
             if constexpr (i1 == 0) {
@@ -250,7 +258,6 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
 #pragma unroll
                 for (int k = i1; k < SSLOTS; ++k) un[k] = Up[j + 1][q][k];
             }
-            idn = invd[j + 1];
         }
         __builtin_amdgcn_sched_barrier(0);   // issue the prefetch at the top of the step
         // a group starts at a multiple of its size (32, 64 or 128), so only every 32nd
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         const float q0 = wv * r16f;
         const float t = fmaf(fmaf(-q0, s16f, wv), r16f, q0);
         float qd;
-        int code;
+        CodeT code;
         if constexpr (FP4) {
             // nearest E2M1 value (ties to the even mantissa, 6 beyond): steps of 0.5
             // below 2, of 1 below 4, of 2 above; code = sign bit 8 | magnitude index
@@ -310,9 +317,9 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
             code = idx + ((t < 0.f && v > 0.f) ? 8 : 0);
         } else {
             qd = __builtin_amdgcn_fmed3f(rintf(t), lo, hi);
-            code = (int)(qd + zf) + a.zoff;
+            code = qd + zf;
         }
-        const float err = fmaf(-s16f, qd, wv) * idc;
+        const float err = fmaf(-s16f, qd, wv) * idv[ij];
         const float errb = row_bcast<qj>(err);
         const bool own = (q == qj);
         e[ij] = own ? err : e[ij];
@@ -329,7 +336,6 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
 #pragma unroll
         for (int i = ij; i < SSLOTS; ++i)
             if (i != in) w[i] = fmaf(-errb, uc[i], w[i]);
-        idc = idn;
     });
 
     // the next block's diagonal U: the loads are in flight during the error staging and
@@ -350,7 +356,8 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         const uint16_t h = f32_to_f16_bits(x);
         ehs[rl][c] = h;
         els[rl][c] = f32_to_f16_bits(x - f16_bits_to_f32(h));
-        cl[rl][c] = (uint8_t)cv[i];
+        if constexpr (FP4) cl[rl][c] = (uint8_t)cv[i];
+        else cl[rl][c] = (uint8_t)((int)cv[i] + a.zoff);
     }
     if (bad && rv) atomicOr(&bad_any, 1);
     // the global stores above and below need not have landed
