@@ -803,7 +803,10 @@ GPTQ_DEV void gemm_f64_tile(GemmD g, const int bid, const int bz, double* lds, i
 #endif
     // whole tiles (even row pitches, 16-byte aligned operands, k range a multiple of 16)
     // take the direct-load ring
-    const bool dma = GD_DMA && full && !diag0 && !panel && ke > kb && ((ke - kb) % GX_BK) == 0 &&
+#ifndef GD_DMA_CHAIN
+#define GD_DMA_CHAIN 1
+#endif
+    const bool dma = GD_DMA && full && (GD_DMA_CHAIN || (!diag0 && !panel)) && ke > kb && ((ke - kb) % GX_BK) == 0 &&
                      ((g.lda | g.ldb) & 1) == 0 &&
                      ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15) == 0;
     if (dma) gx_tile<BKMAJOR>(g, m0, n0, kb, ke, lds, acc);
