@@ -76,3 +76,37 @@ def test_layers_match_per_phase_calls(bits, group, sym):
                                     q.zeros.cpu().numpy().astype(np.int64), Wf, Uo, p, tie_window=CHAIN_TIE, ref=r)
         log(f"  {LW.name}:")
         assert_parity(rep, log)
+
+
+def test_layers_wait_bound_reports_minus_two():
+    """The context's wait bound reaches the factorizations of gptq_quantize_layers: with
+    0 polls every layer's prep reports info = -2 (its kernels all end), and the same
+    context with the default bound then gives the per-phase results bit for bit."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    spec = _mini_block()[:4]           # q, k, v share one input (one factorization), o its own
+    xs, pairs = {}, []
+    for LX, LW in spec:
+        if LX.name not in xs:
+            xs[LX.name] = dev_tensor(layer_x(LX), LX.x_dtype)
+        pairs.append((xs[LX.name], dev_tensor(synth.weights(LW), LW.w_dtype)))
+    with g.Context(2) as ctx:
+        ctx.set_wait_limit(0)
+        _, info = g.quantize_layers(pairs, bits=4, group_size=128, n_slots=2, ctx=ctx)
+        torch.cuda.synchronize()
+        inf = info.cpu().numpy().reshape(-1, 2)
+        log(f"wait bound 0: infos {inf.tolist()}")
+        # the factorization's status sits on each group's first layer (q and o)
+        assert inf[0, 0] == -2 and inf[3, 0] == -2, inf
+        assert inf[1, 0] == 0 and inf[2, 0] == 0, inf
+        ctx.set_wait_limit(1 << 25)
+        outs, info = g.quantize_layers(pairs, bits=4, group_size=128, n_slots=2, ctx=ctx)
+        torch.cuda.synchronize()
+    assert not info.cpu().any(), info.cpu()
+    for (X, W), q in zip(pairs, outs):
+        H = torch.zeros((X.shape[1], X.shape[1]), dtype=torch.float32, device="cuda")
+        g.hessian_accumulate(H, X)
+        U, i1 = g.prepare_hinv(H, 0.01)
+        r = g.quantize_layer(W, U, bits=4, group_size=128)
+        torch.cuda.synchronize()
+        assert torch.equal(q.codes, r.codes) and torch.equal(q.scales, r.scales) and torch.equal(q.zeros, r.zeros)
