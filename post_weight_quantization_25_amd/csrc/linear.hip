@@ -218,10 +218,10 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 #define LIN_MW 8
 #endif
 #ifndef LIN_CPW1
-#define LIN_CPW1 4
+#define LIN_CPW1 2
 #endif
 #ifndef LIN_CPW2
-#define LIN_CPW2 2
+#define LIN_CPW2 1
 #endif
 #ifndef LIN_CPW4
 #define LIN_CPW4 1
@@ -229,32 +229,43 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 #ifndef LIN_NTT_MAX
 #define LIN_NTT_MAX 4
 #endif
+#ifndef LIN_RB
+#define LIN_RB 2
+#endif
 constexpr int MW = LIN_MW;   // waves per workgroup of the batched kernel, each a share of the chunks
 constexpr int MCK = 128;     // columns per chunk: four 32-deep products, one scale
 
-// Batched kernel: a workgroup owns 16 rows and 16 NTT tokens; its waves take the row's
-// 128-column chunks in turn (wave w: chunks w, w + 8, ..).  Within a chunk lane l reads
-// the 16 code bytes 16 (l / 16) .. + 15 of row l % 16 (columns 32 (l / 16) .. + 31) and
-// the same 32 columns of token l % 16 of each token tile; product t of the chunk takes
-// columns 32 (l / 16) + 8 t .. + 7 from every lane, so over its four products the
-// chunk's 128 columns each enter once (the order of a sum's terms is the only thing
-// this changes).  Requires 4-bit (16 bytes per lane, 16-byte aligned rows) or 3-bit
-// codes (12 bytes per lane, 4-byte aligned rows), 16-bit activations, d_col and the group
-// width multiples of 128, 16-byte aligned activation rows.
-template <int CB, int NTT, gptq_dtype XT, gptq_dtype YT>
+// Batched kernel: a workgroup owns 16 RB rows and 16 NTT tokens; its waves take the
+// rows' 128-column chunks in turn (wave w: chunks w, w + 8, ..).  Within a chunk lane l
+// reads the 16 code bytes 16 (l / 16) .. + 15 of row l % 16 of each 16-row block
+// (columns 32 (l / 16) .. + 31) and the same 32 columns of token l % 16 of each token
+// tile; product t of the chunk takes columns 32 (l / 16) + 8 t .. + 7 from every lane,
+// so over its four products the chunk's 128 columns each enter once (the order of a
+// sum's terms is the only thing this changes).  Each activation fragment serves the RB
+// row blocks, so the activations are read from L2 once per 16 RB rows.  Requires 4-bit
+// (16 bytes per lane, 16-byte aligned rows) or 3-bit codes (12 bytes per lane, 4-byte
+// aligned rows), 16-bit activations, d_col and the group width multiples of 128,
+// 16-byte aligned activation rows.
+template <int CB, int NTT, int RB, gptq_dtype XT, gptq_dtype YT>
 __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
     typedef std::conditional_t<XT == GPTQ_BF16, bf16x8_t, f16x8_t> frag_t;
     typedef std::conditional_t<XT == GPTQ_BF16, __bf16, _Float16> elem_t;
     constexpr float ZMAX = XT == GPTQ_BF16 ? 240.f : 2032.f;   // |u - z| <= 255 (2047): exact
     constexpr int CPW = NTT == 1 ? LIN_CPW1 : NTT == 2 ? LIN_CPW2 : LIN_CPW4;  // chunks per wave per pass
-    __shared__ float red[MW][NTT][4][64];
+    __shared__ float red[MW][NTT * RB][4][64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n16 = lane & 15, q = lane >> 4;
-    const int64_t row = (int64_t)blockIdx.x * 16 + n16;
-    const int64_t rr = row < a.d_row ? row : a.d_row - 1;       // rows past the end re-read the last
+    const int64_t row0 = (int64_t)blockIdx.x * 16 * RB;
+    const uint8_t* crow[RB];
+    int64_t rr[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int64_t row = row0 + 16 * rb + n16;
+        rr[rb] = row < a.d_row ? row : a.d_row - 1;              // rows past the end re-read the last
+        crow[rb] = a.codes + rr[rb] * a.code_ld + (CB == 3 ? 12 : 16) * q;
+    }
     const int64_t tok0 = (int64_t)blockIdx.y * 16 * NTT;
-    const uint8_t* crow = a.codes + rr * a.code_ld + (CB == 3 ? 12 : 16) * q;
     const uint16_t* xrow[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
@@ -264,25 +275,30 @@ __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
     }
     const int nck = (int)(a.d_col / MCK);
     const int cpg = (int)(a.G / MCK);
-    f32x4_t acc[NTT];
+    f32x4_t acc[NTT][RB];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[tt][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int c0 = wave; c0 < nck; c0 += MW * CPW) {
-        u32x4_t cw[CPW], xw[CPW][NTT][4];
-        float S[CPW], z[CPW];
+        u32x4_t cw[CPW][RB], xw[CPW][NTT][4];
+        float S[CPW][RB], z[CPW][RB];
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
             const int c = c0 + MW * j < nck ? c0 + MW * j : c0;  // chunks past the end re-read c0
-            if constexpr (CB == 3) {
-                const uint32_t* w = reinterpret_cast<const uint32_t*>(crow + (int64_t)c * (MCK / 8 * 3));
-                cw[j] = u32x4_t{w[0], w[1], w[2], 0u};
-            } else {
-                cw[j] = *reinterpret_cast<const u32x4_t*>(crow + (int64_t)c * (MCK / 2));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                if constexpr (CB == 3) {
+                    const uint32_t* w = reinterpret_cast<const uint32_t*>(crow[rb] + (int64_t)c * (MCK / 8 * 3));
+                    cw[j][rb] = u32x4_t{w[0], w[1], w[2], 0u};
+                } else {
+                    cw[j][rb] = *reinterpret_cast<const u32x4_t*>(crow[rb] + (int64_t)c * (MCK / 2));
+                }
+                const int64_t gi = rr[rb] * a.n_groups + c / cpg;
+                S[j][rb] = f16_bits_to_f32(a.scales[gi]);
+                z[j][rb] = f16_bits_to_f32(a.zeros[gi]);
             }
-            const int64_t gi = rr * a.n_groups + c / cpg;
-            S[j] = f16_bits_to_f32(a.scales[gi]);
-            z[j] = f16_bits_to_f32(a.zeros[gi]);
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -293,86 +309,99 @@ __global__ __launch_bounds__(64 * MW) void linear_mfma_kernel(LinArgs a) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
             if (c0 + MW * j >= nck) break;   // wave-uniform
-            const bool exact = z[j] == rintf(z[j]) && fabsf(z[j]) <= ZMAX;
-            const bool need_lo = __ballot(!exact) != 0;
-            f32x4_t cs[NTT];
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) cs[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int rb = 0; rb < RB; ++rb) {
+                const bool exact = z[j][rb] == rintf(z[j][rb]) && fabsf(z[j][rb]) <= ZMAX;
+                const bool need_lo = __ballot(!exact) != 0;
+                f32x4_t cs[NTT];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                // element e of the operand is column 8 t + e of the lane's 32: 4-bit, the low
-                // nibble of byte e / 2 for even e, the high nibble for odd e; 3-bit, code e of
-                // the 24-bit group t of the lane's 96-bit stream
-                float d[8];
-                if constexpr (CB == 3) {
-                    const uint32_t g24 = t == 0 ? cw[j][0] & 0xFFFFFFu
-                                       : t == 1 ? ((cw[j][0] >> 24) | (cw[j][1] << 8)) & 0xFFFFFFu
-                                       : t == 2 ? ((cw[j][1] >> 16) | (cw[j][2] << 16)) & 0xFFFFFFu
-                                                : cw[j][2] >> 8;
+                for (int tt = 0; tt < NTT; ++tt) cs[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) d[e] = (float)code3(g24, e) - z[j];
-                } else {
-                    const uint32_t w = cw[j][t];
-                    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+                for (int t = 0; t < 4; ++t) {
+                    // element e of the operand is column 8 t + e of the lane's 32: 4-bit, the
+                    // low nibble of byte e / 2 for even e, the high nibble for odd e; 3-bit,
+                    // code e of the 24-bit group t of the lane's 96-bit stream
+                    float d[8];
+                    if constexpr (CB == 3) {
+                        const u32x4_t cc = cw[j][rb];
+                        const uint32_t g24 = t == 0 ? cc[0] & 0xFFFFFFu
+                                           : t == 1 ? ((cc[0] >> 24) | (cc[1] << 8)) & 0xFFFFFFu
+                                           : t == 2 ? ((cc[1] >> 16) | (cc[2] << 16)) & 0xFFFFFFu
+                                                    : cc[2] >> 8;
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        d[2 * b] = (float)((lo >> (8 * b)) & 0xFFu) - z[j];
-                        d[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu) - z[j];
+                        for (int e = 0; e < 8; ++e) d[e] = (float)code3(g24, e) - z[j][rb];
+                    } else {
+                        const uint32_t w = cw[j][rb][t];
+                        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            d[2 * b] = (float)((lo >> (8 * b)) & 0xFFu) - z[j][rb];
+                            d[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu) - z[j][rb];
+                        }
                     }
-                }
-                frag_t bh;
+                    frag_t bh;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) bh[e] = (elem_t)d[e];
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) {
-                    const frag_t xa = __builtin_bit_cast(frag_t, xw[j][tt][t]);
-                    if constexpr (XT == GPTQ_BF16) cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, cs[tt], 0, 0, 0);
-                    else cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bh, cs[tt], 0, 0, 0);
-                }
-                if (need_lo) {
-                    frag_t bl;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bl[e] = (elem_t)(d[e] - (float)bh[e]);
+                    for (int e = 0; e < 8; ++e) bh[e] = (elem_t)d[e];
 #pragma unroll
                     for (int tt = 0; tt < NTT; ++tt) {
                         const frag_t xa = __builtin_bit_cast(frag_t, xw[j][tt][t]);
-                        if constexpr (XT == GPTQ_BF16) cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, cs[tt], 0, 0, 0);
-                        else cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bl, cs[tt], 0, 0, 0);
+                        if constexpr (XT == GPTQ_BF16) cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, cs[tt], 0, 0, 0);
+                        else cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bh, cs[tt], 0, 0, 0);
+                    }
+                    if (need_lo) {
+                        frag_t bl;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) bl[e] = (elem_t)(d[e] - (float)bh[e]);
+#pragma unroll
+                        for (int tt = 0; tt < NTT; ++tt) {
+                            const frag_t xa = __builtin_bit_cast(frag_t, xw[j][tt][t]);
+                            if constexpr (XT == GPTQ_BF16) cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, cs[tt], 0, 0, 0);
+                            else cs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bl, cs[tt], 0, 0, 0);
+                        }
                     }
                 }
+                // lane l holds the sums of row l % 16 of block rb for tokens 4 (l / 16) + i
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[tt][rb][i] = fmaf(S[j][rb], cs[tt][i], acc[tt][rb][i]);
             }
-            // lane l holds the sums of row l % 16 (its own row) for tokens 4 (l / 16) + i
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[tt][i] = fmaf(S[j], cs[tt][i], acc[tt][i]);
         }
     }
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][tt][i][lane] = acc[tt][i];
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][tt * RB + rb][i][lane] = acc[tt][rb][i];
     __syncthreads();
-    // output o: token tile o / 256, token m = (o / 16) % 16 of the tile, row n = o % 16;
-    // its partial sums sit in lane n + 16 (m / 4), register m % 4, of every wave
-    for (int o = threadIdx.x; o < NTT * 256; o += 64 * MW) {
-        const int tt = o >> 8, m = (o >> 4) & 15, n = o & 15;
+    // output o: token tile o / (256 RB), row block (o / 256) % RB, token m = (o / 16) % 16
+    // of the tile, row n = o % 16; its partial sums sit in lane n + 16 (m / 4), register
+    // m % 4, of every wave
+    for (int o = threadIdx.x; o < NTT * RB * 256; o += 64 * MW) {
+        const int tr = o >> 8, m = (o >> 4) & 15, n = o & 15;
+        const int tt = tr / RB, rb = tr % RB;
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < MW; ++w) v += red[w][tt][m & 3][n + 16 * (m >> 2)];
-        const int64_t t = tok0 + 16 * tt + m, r = (int64_t)blockIdx.x * 16 + n;
+        for (int w = 0; w < MW; ++w) v += red[w][tr][m & 3][n + 16 * (m >> 2)];
+        const int64_t t = tok0 + 16 * tt + m, r = row0 + 16 * rb + n;
         if (t < a.n_tok && r < a.d_row) store_y<YT>(a.y, t * a.ldy + r, v);
     }
 }
 
 template <int CB, gptq_dtype XT, gptq_dtype YT>
 static void launch_mfma(const LinArgs& a, hipStream_t s) {
-    const unsigned gx = (unsigned)((a.d_row + 15) / 16);
+    // 16 tokens or fewer: 16-row workgroups (enough of them to fill the device); beyond,
+    // 32-row workgroups, so that each activation fragment serves two row blocks and the
+    // activations are read from L2 half as often
+    const unsigned g16 = (unsigned)((a.d_row + 15) / 16), g32 = (unsigned)((a.d_row + 31) / 32);
     if (a.n_tok <= 16 || LIN_NTT_MAX == 1)
-        linear_mfma_kernel<CB, 1, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
-    else if (a.n_tok <= 32 || LIN_NTT_MAX == 2)
-        linear_mfma_kernel<CB, 2, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 31) / 32)), 64 * MW, 0, s>>>(a);
-    else linear_mfma_kernel<CB, 4, XT, YT><<<dim3(gx, (unsigned)((a.n_tok + 63) / 64)), 64 * MW, 0, s>>>(a);
+        linear_mfma_kernel<CB, 1, 1, XT, YT><<<dim3(g16, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
+    else if (a.n_tok <= 32)
+        linear_mfma_kernel<CB, 1, LIN_RB, XT, YT><<<dim3(LIN_RB == 2 ? g32 : g16, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
+    else if (a.n_tok <= 64 || LIN_NTT_MAX == 2)
+        linear_mfma_kernel<CB, 2, LIN_RB, XT, YT><<<dim3(LIN_RB == 2 ? g32 : g16, (unsigned)((a.n_tok + 31) / 32)), 64 * MW, 0, s>>>(a);
+    else linear_mfma_kernel<CB, 4, LIN_RB, XT, YT><<<dim3(LIN_RB == 2 ? g32 : g16, (unsigned)((a.n_tok + 63) / 64)), 64 * MW, 0, s>>>(a);
 }
 
 template <int CB, gptq_dtype XT, gptq_dtype YT>

@@ -81,6 +81,8 @@ CASES = [
     (200, 384, 3, 128, 70, torch.bfloat16, torch.float32, 0),      # two tile rows of 64 tokens, ragged rows, 3 chunks
     (160, 2048, 4, 0, 2, torch.float16, torch.float16, 0),         # per-row group over 16 chunks
     (64, 1280, 4, 128, 33, torch.bfloat16, torch.float32, 8),      # padded x rows (16-byte aligned)
+    (48, 512, 4, 128, 30, torch.bfloat16, torch.float32, 0),       # 32-row workgroups, the second half past the end
+    (4096, 4096, 4, 128, 64, torch.bfloat16, torch.bfloat16, 0),   # 64 tokens of the metric layer shape
     # the 3-bit stream (12 bytes per 32 columns): decode, general and batched kernels
     (4096, 4096, 3, 128, 1, torch.bfloat16, torch.float32, 0),
     (300, 512, 3, 0, 3, torch.float16, torch.float32, 0),
