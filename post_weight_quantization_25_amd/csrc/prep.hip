@@ -1090,13 +1090,13 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // its panel are finished inside the trailing update of the step before (tile (0, 0)
 // factors the block, the tiles below it apply its inverse), so each step of the
 // chain is one launch.  From d = DEFER_MIN_D on, the trailing update is deferred to
-// outer blocks of DEFER_W columns: each step inside an outer block updates only the
-// rest of that block (its columns, all rows below), and the step of the block's last
-// panel applies the block's DEFER_W columns to the whole matrix after it (one product
-// with K = DEFER_W, whose tile (0, 0) and block column 0 again form the next block and
-// panel).  Every element receives the same products, grouped differently.  (At
-// d = 4096 this measured slower: the chain, not the matrix traffic, bounds the time
-// there, and the K = 256 update lies on it.)
+// outer blocks of W columns (DEFER_W_SMALL below DEFER_W_MIN_D, else DEFER_W): each
+// step inside an outer block updates only the rest of that block (its columns, all rows
+// below), and the step of the block's last panel applies the block's W columns to the
+// whole matrix after it (one product with K = W, whose tile (0, 0) and block column 0
+// again form the next block and panel).  Every element receives the same products,
+// grouped differently.  (At d = 4096 this measured no faster: the chain, not the matrix
+// traffic, bounds the time there, and the K = W update lies on it.)
 //
 // The inverse is assembled by row blocks B_0, B_1, .., B_last: B_0 = [0, h) with h
 // the largest 64 * 2^i below d, and each next block the largest 64 * 2^i below what
@@ -1114,14 +1114,21 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // measured slower than 1024: the auxiliary stream then still works on the blocks
 // before it when the loop ends.)
 // Deferral of the trailing update (see cholinv) from d = DEFER_MIN_D on, in outer blocks
-// of DEFER_W columns.  A step's update of the whole trailing matrix reads and writes it
-// for 2 * 64 flops per element (8 flops per byte in fp64: bound by HBM once the matrix
-// leaves the caches); deferred, the update after an outer block does 2 * DEFER_W.
+// of DEFER_W_SMALL columns below DEFER_W_MIN_D and DEFER_W from there.  A step's update
+// of the whole trailing matrix reads and writes it for 2 * 64 flops per element (8 flops
+// per byte in fp64: bound by HBM once the matrix leaves the caches); deferred, the update
+// after an outer block does 2 W.
 #ifndef DEFER_MIN_D
-#define DEFER_MIN_D 6144
+#define DEFER_MIN_D 4200
 #endif
 #ifndef DEFER_W
 #define DEFER_W 512
+#endif
+#ifndef DEFER_W_SMALL
+#define DEFER_W_SMALL 256
+#endif
+#ifndef DEFER_W_MIN_D
+#define DEFER_W_MIN_D 7168
 #endif
 #ifndef AUX_MAX_WG_DEFER
 #define AUX_MAX_WG_DEFER 0
@@ -1204,10 +1211,10 @@ static gptq_status cholinv(PrepCtx& c, const PrepAux* aux) {
     int nf = 0;   // blocks handed to the auxiliary stream
     while (nf < nb && fork_step[nf] < 0)
         if ((st = fork(nf++)) != GPTQ_OK) return st;
-    // deferred trailing update (large d): inside an outer block of DEFER_W columns each
+    // deferred trailing update (large d): inside an outer block of defer_w columns each
     // step updates only the rest of the outer block (all rows below), and the step of the
-    // block's last panel applies all DEFER_W columns to the matrix after the block at once
-    const int64_t defer_w = (d >= DEFER_MIN_D) ? DEFER_W : PNB;
+    // block's last panel applies all defer_w columns to the matrix after the block at once
+    const int64_t defer_w = (d < DEFER_MIN_D) ? PNB : (d < DEFER_W_MIN_D) ? DEFER_W_SMALL : DEFER_W;
     for (int64_t k0 = 0; k0 < d; k0 += PNB) {
         const int n = (int)std::min<int64_t>(PNB, d - k0);
         const int64_t rest = d - k0 - n;

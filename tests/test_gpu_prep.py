@@ -143,10 +143,11 @@ def test_prep_without_a_wait_ignores_the_bound():
     assert torch.equal(U1, U2)
 
 
-@pytest.mark.parametrize("d", [6200, 8192, 8293])
+@pytest.mark.parametrize("d", [4650, 6200, 8192, 8293])
 def test_prep_parity_deferred_update(d):
-    """From d = 6144 on the factorization defers its trailing update to outer blocks of
-    512 columns; 6200 and 8293 end in a partial outer block and a ragged tile."""
+    """From d = 4200 on the factorization defers its trailing update to outer blocks of
+    256 columns, from 7168 on of 512; 4650, 6200 and 8293 end in a partial outer block and
+    a ragged tile."""
     import torch
     import post_weight_quantization_25_amd as g
     rng = np.random.default_rng([13, d])
