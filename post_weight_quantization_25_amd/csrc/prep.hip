@@ -194,6 +194,14 @@ GPTQ_DEV double rsqrt_pos(double x) {
 // no L2 write-back or invalidation is needed: a release fence at device scope would
 // write back every dirty line of the L2, and an acquire fence would invalidate it for
 // every workgroup sharing it (4% of the factorization at d = 4096 and 11008).
+// v of lane l, in every lane (l a compile-time constant)
+GPTQ_DEV double bcast_lane(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 GPTQ_DEV void publish_block(int* flag, int step) {
     if (flag == nullptr) return;
     __builtin_amdgcn_s_waitcnt(0);
@@ -214,41 +222,27 @@ GPTQ_DEV void diag_block(double* a, double* xs, double* ts, int* fail_p, double*
         constexpr int c0 = decltype(P)::value * 8;
         if (fail_s) return;
         if (wave == 0) {
-            // Cholesky of the 8 x 8 top block, in every lane
-            double t[8][8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int k = 0; k <= i; ++k) t[i][k] = a[(c0 + i) * DLD + c0 + k];
-            double rd[8];
+            // every lane solves its own row of the sub-panel, one column k at a time; the
+            // top block's row k (lane c0 + k) supplies the pivot d_k (its own value at step
+            // k) and the factor entries t[k][m] of the later steps, broadcast from that lane.
+            // For the top block's rows this is the Cholesky of the 8 x 8 block with the same
+            // operands in the same order; the entries right of a row's diagonal are never read
+            const int r = lane;
+            double x[8], rd[8], t[8][8];
             int f = 0;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                double dk = t[k][k];
+            for (int k = 0; k < 8; ++k) x[k] = a[r * DLD + c0 + k];
 #pragma unroll
-                for (int m = 0; m < k; ++m) dk -= t[k][m] * t[k][m];
+            for (int k = 0; k < 8; ++k) {
+                double v = x[k];
+#pragma unroll
+                for (int m = 0; m < k; ++m) v = fma(-t[k][m], x[m], v);
+                const double dk = bcast_lane(v, c0 + k);
                 if (!(dk > 0.0) && f == 0) f = c0 + k + 1;
                 rd[k] = rsqrt_pos(dk > 0.0 ? dk : 1.0);
-                t[k][k] = (dk > 0.0 ? dk : 1.0) * rd[k];
-#pragma unroll
-                for (int i = k + 1; i < 8; ++i) {
-                    double v = t[i][k];
-#pragma unroll
-                    for (int m = 0; m < k; ++m) v -= t[i][m] * t[k][m];
-                    t[i][k] = v * rd[k];
-                }
-            }
-            // every lane at or below the sub-panel solves its row; for a row of the top
-            // block this reproduces that row of the factor bit for bit (same operands,
-            // same order), and the entries right of its diagonal are never read
-            const int r = lane;
-            double x[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                double v = a[r * DLD + c0 + k];
-#pragma unroll
-                for (int m = 0; m < k; ++m) v -= t[k][m] * x[m];
                 x[k] = v * rd[k];
+#pragma unroll
+                for (int i = k + 1; i < 8; ++i) t[i][k] = bcast_lane(x[k], c0 + i);
             }
             if (r >= c0) {
 #pragma unroll
