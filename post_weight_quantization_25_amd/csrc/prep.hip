@@ -1104,9 +1104,8 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 // columns before the end), its inverse X[B_i][B_i] (recursive doubling) and these
 // products run on the auxiliary stream, beside the remaining (latency-bound)
 // factorization steps.  After the loop only the last block's inverse and one product
-// remain on the caller's stream.  (A last block of 512 or 256 columns at d = 4096
-// measured slower than 1024: the auxiliary stream then still works on the blocks
-// before it when the loop ends.)
+// remain on the caller's stream.  (A last block of at most 512 columns measured 3%
+// faster than 1024 at d = 3000 and 4096, and the same at 11008; 256 no better.)
 // Deferral of the trailing update (see cholinv) from d = DEFER_MIN_D on, in outer blocks
 // of DEFER_W_SMALL columns below DEFER_W_MIN_D and DEFER_W from there.  A step's update
 // of the whole trailing matrix reads and writes it for 2 * 64 flops per element (8 flops
@@ -1131,7 +1130,7 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 #define AUX_FORK_REST 2048
 #endif
 #ifndef INV_LAST
-#define INV_LAST 1024
+#define INV_LAST 512
 #endif
 static gptq_status cholinv(PrepCtx& c, const PrepAux* aux) {
     const int64_t d = c.d;
