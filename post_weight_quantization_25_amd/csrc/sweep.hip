@@ -90,7 +90,8 @@ GPTQ_DEV void lds_barrier() {
 // A block's diagonal 128 x 128 part of U into registers, in the order of its LDS copy:
 // thread t holds the (row j, lane q) pairs p = t + QT m, each as the eight values
 // U[b0 + j][b0 + q + 16 i] that lane q uses in step j (zero past nb), and, in the first
-// 128 threads, the pivot U[b0 + t][b0 + t].
+// 128 threads, the pivot U[b0 + t][b0 + t].  Pair p's row j lies in 16 m .. 16 m + 15, and
+// step j touches only slots i >= j / 16 = m, so slots i < m are never read: not loaded.
 constexpr int NPAIR = QB * SL / QT;
 struct UDiag { float v[NPAIR][SSLOTS]; float piv; };
 
@@ -102,7 +103,11 @@ GPTQ_DEV void load_udiag(const SweepArgs& a, int64_t b0, int nb, int tid, UDiag&
         const int j = pr >> 4, qq = pr & (SL - 1);
         const float* src = a.U + (b0 + j) * a.d_col + b0 + qq;
 #pragma unroll
-        for (int i = 0; i < SSLOTS; ++i) u.v[m][i] = (FULL || (j < nb && qq + SL * i < nb)) ? src[SL * i] : 0.f;
+        for (int i = 0; i < SSLOTS; ++i) {
+            static_assert(QT == 16 * SL, "pair p = t + QT m has row j in 16 m .. 16 m + 15");
+            if (i < m) u.v[m][i] = 0.f;
+            else u.v[m][i] = (FULL || (j < nb && qq + SL * i < nb)) ? src[SL * i] : 0.f;
+        }
     }
     u.piv = (tid < nb) ? a.U[(b0 + tid) * a.d_col + b0 + tid] : 0.f;
 }
