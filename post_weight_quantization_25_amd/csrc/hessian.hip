@@ -422,13 +422,22 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(HessBf16Args a) {
             }
         }
     __syncthreads();
-    // mirror: thread t writes column c1 + t of the slice as row c1 + t of H
-    const int gc = c1 + tid;
+    // mirror: thread t writes column c1 + t of the slice as row c1 + t of H, i.e. the
+    // HR_ROWS consecutive entries H[c1 + t][c0 + rc HR_ROWS ..]: 16-byte stores when the
+    // whole slice lies below the diagonal and inside H with aligned rows, else one by one
+    const int gc = c1 + tid, g0 = c0 + rc * HR_ROWS;
     if (gc < a.d) {
+        if (c0 < c1 && g0 + HR_ROWS <= a.d && (a.d & 3) == 0 && (reinterpret_cast<uintptr_t>(a.H) & 15) == 0) {
+            float* dst = a.H + (int64_t)gc * a.d + g0;
 #pragma unroll
-        for (int r = 0; r < HR_ROWS; ++r) {
-            const int g = c0 + rc * HR_ROWS + r;
-            if (g < a.d && g < gc) a.H[(int64_t)gc * a.d + g] = st[r][tid];
+            for (int r = 0; r < HR_ROWS; r += 4)
+                *reinterpret_cast<f32x4_t*>(dst + r) = f32x4_t{st[r][tid], st[r + 1][tid], st[r + 2][tid], st[r + 3][tid]};
+        } else {
+#pragma unroll
+            for (int r = 0; r < HR_ROWS; ++r) {
+                const int g = g0 + r;
+                if (g < a.d && g < gc) a.H[(int64_t)gc * a.d + g] = st[r][tid];
+            }
         }
     }
 }
