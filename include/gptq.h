@@ -128,8 +128,9 @@ typedef struct {
  *  H        d_col x d_col fp32, read and written.  H is kept symmetric: both
  *           triangles are written with the same values.
  *  X        n_tokens x d_col, row stride ldx elements (ldx >= d_col), dtype x_dtype.
- *           GPTQ_BF16 products are exact in fp32 and run on bf16 MFMA;
- *           GPTQ_F32 and GPTQ_F16 run on fp32 MFMA.
+ *           GPTQ_BF16 and GPTQ_F16 products are exact in fp32; with X 16-byte aligned
+ *           and ldx a multiple of 8 they run on the 16-bit matrix cores (fp16
+ *           subnormals taken as they are), otherwise, like GPTQ_F32, on fp32 MFMA.
  *  ws       device workspace of at least gptq_hessian_workspace_size(n_tokens, d_col)
  *           bytes (the fp32 partial sums of the token splits); contents on entry are
  *           ignored.  May be NULL when the size is 0.

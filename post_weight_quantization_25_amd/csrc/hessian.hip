@@ -3,7 +3,8 @@
 // GPTQ summary page, statement of the one-layer procedure: the layer Hessian
 // H = 2 X X^T (page layout d_col x tokens; here X is tokens x d_col, so H = 2 X^T X).
 //
-// bf16 X: a symmetric rank-k update on v_mfma_f32_32x32x16_bf16.  Only tiles
+// bf16 or fp16 X (rows 16-byte aligned): a symmetric rank-k update on
+// v_mfma_f32_32x32x16_bf16 / _f16 (16-bit products are exact in fp32).  Only tiles
 // on or above the diagonal are computed (256 x 256 output tiles, one workgroup of
 // eight waves per CU, each wave accumulating a 64 x 128 sub-tile in 8 MFMAs).  X is stored
 // token-major (channels contiguous), i.e. the contraction index is the strided
@@ -18,8 +19,8 @@
 // fp32 partial tile; a second kernel sums the S partials of every element in split
 // order and updates H, so results are bitwise reproducible.
 //
-// fp32 / fp16 X: exact-product path on v_mfma_f32_16x16x4_f32, one WG per
-// 64 x 64 upper tile over all tokens (no split).
+// fp32 X, and 16-bit X whose rows are not 16-byte aligned: exact-product path on
+// v_mfma_f32_16x16x4_f32, one WG per 64 x 64 upper tile over all tokens (no split).
 
 #include <cmath>
 
@@ -191,12 +192,20 @@ GPTQ_DEV void read_slice(const uint16_t* stg, int kk, int wr, int wc, int lane, 
     for (int j = 0; j < HB_FB; ++j) f.b[j] = read_frag(stg + (DIAG ? 0 : HB_OPE), wc * HB_WN + j * 32, kk, lane);
 }
 
+// F16: the fragments hold fp16 bit patterns (the same 16-bit copies and reads), multiplied
+// on v_mfma_f32_32x32x16_f16; products of two fp16 values are exact in fp32 too.
+template <bool F16>
 GPTQ_DEV void mfma_slice(const Frags& f, f32x16_t (&acc)[HB_FA][HB_FB]) {
 #pragma unroll
     for (int i = 0; i < HB_FA; ++i)
 #pragma unroll
-        for (int j = 0; j < HB_FB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < HB_FB; ++j) {
+            if constexpr (F16)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, f.a[i]),
+                                                                   __builtin_bit_cast(f16x8_t, f.b[j]), acc[i][j], 0, 0, 0);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        }
 }
 
 // Scheduling hint for one region of the pipelined loop, which holds the LDS reads of
@@ -224,12 +233,13 @@ GPTQ_DEV void interleave_reads_mfma() {
 }
 
 // The MFMAs of one LDS stage for one wave (both slices), used by the edge path.
+template <bool F16>
 GPTQ_DEV void mfma_stage(const uint16_t* stg, int wr, int wc, int lane, f32x16_t (&acc)[HB_FA][HB_FB]) {
 #pragma unroll
     for (int kk = 0; kk < HB_BK; kk += 16) {
         Frags f;
         read_slice(stg, kk, wr, wc, lane, f);
-        mfma_slice(f, acc);
+        mfma_slice<F16>(f, acc);
     }
 }
 
@@ -259,7 +269,7 @@ GPTQ_DEV bool below_diagonal(int wave) {
 // DIAG: a diagonal tile (c0 == c1).  One operand is loaded, and the waves whose
 // sub-tile lies strictly below the diagonal (never read by the reduction) only take
 // part in the loads and barriers.
-template <bool DIAG>
+template <bool DIAG, bool F16>
 GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NSTG], int64_t t_beg, int64_t nst,
                             int c0, int c1, int wr, int wc, int wave, int lane, f32x16_t (&acc)[HB_FA][HB_FB]) {
     const bool work = !DIAG || !below_diagonal(wave);
@@ -277,7 +287,7 @@ GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NS
             if (st + u < nst) {
                 if (work) {
                     read_slice<DIAG>(ring[u], 16, wr, wc, lane, f1);
-                    mfma_slice(f0, acc);
+                    mfma_slice<F16>(f0, acc);
                     interleave_reads_mfma();
                 }
                 __builtin_amdgcn_sched_barrier(0);   // keep the phases in this order
@@ -286,7 +296,7 @@ GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NS
                 issue_stage<u>(a, sc, t0(st + u + HB_NSTG));
                 if (work) {
                     read_slice<DIAG>(ring[(u + 1) % HB_NSTG], 0, wr, wc, lane, f0);
-                    mfma_slice(f1, acc);
+                    mfma_slice<F16>(f1, acc);
                     interleave_reads_mfma();
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -298,6 +308,7 @@ GPTQ_DEV void hess_loop_dma(const HessBf16Args& a, uint16_t* const (&ring)[HB_NS
 }
 
 // Edge path: register copies, two LDS stages.
+template <bool F16>
 GPTQ_DEV void hess_loop_edge(const HessBf16Args& a, uint16_t* const (&ring)[HB_NSTG], int64_t t_beg, int64_t t_end,
                              int64_t nst, int c0, int c1, int wr, int wc, int tid, int lane, f32x16_t (&acc)[HB_FA][HB_FB]) {
     for (int64_t st = 0; st < nst; st += 2) {
@@ -306,13 +317,14 @@ GPTQ_DEV void hess_loop_edge(const HessBf16Args& a, uint16_t* const (&ring)[HB_N
             if (st + u < nst) {
                 copy_stage_edge(a, ring[u], t_beg + (st + u) * HB_BK, t_end, c0, c1, tid);
                 __syncthreads();
-                mfma_stage(ring[u], wr, wc, lane, acc);
+                mfma_stage<F16>(ring[u], wr, wc, lane, acc);
             }
         }
     }
     __syncthreads();
 }
 
+template <bool F16>
 __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a) {
     __shared__ __attribute__((aligned(16))) uint16_t lds_ring[HB_NSTG * HB_STE];  // HB_NSTG x 32 KB
     uint16_t* ring[HB_NSTG];
@@ -353,9 +365,9 @@ __global__ __launch_bounds__(HB_THREADS, 1) void hess_bf16_kernel(HessBf16Args a
                       ((reinterpret_cast<uintptr_t>(a.X) & 15) == 0) && ((a.ldx & 7) == 0) &&
                       (a.ldx < ((int64_t)1 << 25));
     if (nst > 0) {
-        if (full && c0 == c1) hess_loop_dma<true>(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
-        else if (full) hess_loop_dma<false>(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
-        else hess_loop_edge(a, ring, t_beg, t_end, nst, c0, c1, wr, wc, tid, lane, acc);
+        if (full && c0 == c1) hess_loop_dma<true, F16>(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
+        else if (full) hess_loop_dma<false, F16>(a, ring, t_beg, nst, c0, c1, wr, wc, wave, lane, acc);
+        else hess_loop_edge<F16>(a, ring, t_beg, t_end, nst, c0, c1, wr, wc, tid, lane, acc);
     }
 
     // this split's partial tile (row-major 256 x 256 fp32); the reduction reads no
@@ -571,7 +583,7 @@ size_t hessian_ws_bytes(int64_t n, int64_t d) {
 gptq_status hessian_launch(float* H, const void* X, gptq_dtype dt, int64_t n, int64_t d, int64_t ldx,
                            void* ws, size_t ws_bytes, hipStream_t stream) {
     const bool aligned = ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && ((ldx & 7) == 0);
-    if (dt == GPTQ_BF16 && aligned) {
+    if ((dt == GPTQ_BF16 || dt == GPTQ_F16) && aligned) {
         HessBf16Args a;
         const Bf16Plan p = bf16_plan(n, d);
         if (ws_bytes < hessian_ws_bytes(n, d) || ws == nullptr) return GPTQ_ERR_WORKSPACE;
@@ -579,7 +591,8 @@ gptq_status hessian_launch(float* H, const void* X, gptq_dtype dt, int64_t n, in
         a.H = H;
         a.partials = reinterpret_cast<float*>(ws);
         a.nt = p.nt; a.T = p.T; a.S = p.S; a.ks = p.ks; a.tpg = p.tpg; a.xpg = p.xpg;
-        hess_bf16_kernel<<<p.grid(), HB_THREADS, 0, stream>>>(a);
+        if (dt == GPTQ_F16) hess_bf16_kernel<true><<<p.grid(), HB_THREADS, 0, stream>>>(a);
+        else hess_bf16_kernel<false><<<p.grid(), HB_THREADS, 0, stream>>>(a);
         GPTQ_LAUNCH_CHECK();
         hess_reduce_kernel<<<p.T * (HB_BM / HR_ROWS), 256, 0, stream>>>(a);
         GPTQ_LAUNCH_CHECK();

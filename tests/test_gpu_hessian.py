@@ -9,10 +9,14 @@ from oracle import gptq_oracle as o
 pytestmark = pytest.mark.gpu
 
 
-def _x(n, d, dtype, seed):
+def _x(n, d, dtype, seed, tiny=False):
     rng = np.random.default_rng([seed, n, d])
     s = rng.lognormal(0.0, 1.0, size=d).astype(np.float32)
     s[rng.integers(d)] *= 50.0
+    if tiny:
+        # one channel entirely in fp16's subnormal range (|x| < 2^-14), so that its
+        # diagonal entry is lost if the products flush subnormal inputs
+        s[d // 3] = 2.0 ** -17
     x = rng.standard_normal((n, d), dtype=np.float32) * s
     if dtype == "bf16":
         bits = synth.f32_to_bf16_bits(x)
@@ -23,11 +27,12 @@ def _x(n, d, dtype, seed):
     return x, x.astype(np.float64)
 
 
-def _tol(n, dtype):
+def _tol(n, dtype, aligned=True):
     """Rigorous fp32 accumulation bound relative to sqrt(H_ii H_jj) (Cauchy-Schwarz):
-    gamma_m with m = sequential fp32 additions per entry (n/16 bf16 MFMA steps, or n/4
-    fp32 MFMA steps plus product rounding), plus the split partial sums; 2x margin."""
-    m = n / 16 + 64 if dtype == "bf16" else n + 64
+    gamma_m with m = sequential fp32 additions per entry (n/16 steps of the 16-bit
+    matrix-core path, or n/4 fp32 MFMA steps plus product rounding), plus the split
+    partial sums; 2x margin."""
+    m = n / 16 + 64 if dtype in ("bf16", "f16") and aligned else n + 64
     return 2.0 * m * 2.0 ** -24
 
 
@@ -57,7 +62,9 @@ def _err(Hg, Ho):
     (1000, 520, "bf16", 0, 1),     # ragged tile edge, ragged token stage
     (4160, 256, "bf16", 0, 3),     # chunked accumulation
     (2048, 512, "f32", 0, 1),      # fp32 calibration data (exact-product path)
-    (777, 200, "f16", 0, 1),
+    (777, 200, "f16", 0, 1),       # fp16 on the matrix-core path, ragged edges
+    (5000, 520, "f16", 0, 2),      # fp16, several token splits, chunked
+    (300, 136, "f16", 3, 1),       # fp16 rows not 16-byte aligned: exact-product path
     (300, 136, "bf16", 8, 1),      # strided rows (16-byte aligned)
     (300, 136, "bf16", 3, 1),      # strided rows, unaligned
     (1, 130, "bf16", 0, 1),
@@ -71,8 +78,27 @@ def test_hessian_parity(n, d, dtype, pad, chunks):
     Hg = _gpu_h(x, dtype, d, pad, chunks)
     assert np.array_equal(Hg, Hg.T)
     err = _err(Hg, Ho)
-    log(f"  max |dH|/sqrt(HiiHjj) = {err:.3e} (bound {_tol(n, dtype):.3e})")
-    assert err <= _tol(n, dtype)
+    tol = _tol(n, dtype, aligned=pad % 8 == 0)
+    log(f"  max |dH|/sqrt(HiiHjj) = {err:.3e} (bound {tol:.3e})")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_hessian_subnormal_channel(dtype):
+    """A channel whose fp16 values are all subnormal keeps its diagonal entry (and its
+    row) within the same bound: the products take subnormal inputs as they are."""
+    n, d = 2048, 264
+    x, x64 = _x(n, d, dtype, 3, tiny=True)
+    if dtype == "f16":
+        assert np.all(np.abs(x[:, d // 3].astype(np.float32)) < 2.0 ** -14)
+    Ho = o.hessian([x64])
+    Hg = _gpu_h(x, dtype, d)
+    err = _err(Hg, Ho)
+    tol = _tol(n, dtype)
+    log(f"hessian {dtype} subnormal channel: H_ii rel {abs(Hg[d // 3, d // 3] / Ho[d // 3, d // 3] - 1):.3e}, "
+        f"max |dH|/sqrt(HiiHjj) = {err:.3e} (bound {tol:.3e})")
+    assert Hg[d // 3, d // 3] > 0.0
+    assert err <= tol
 
 
 def test_hessian_accumulates_and_is_deterministic():
