@@ -21,7 +21,7 @@ ms/layer and the phase breakdown per layer.
 layers from the same U and prints their runtime ratio.
 
 --linear measures, instead of the layer step, the product of the quantized layer with
-activations read from the stored format (gptq_quantized_linear) for 1, 4, 16, 32, 64 and 128
+activations read from the stored format (gptq_quantized_linear) for 1, 4, 16, 32, 64, 128 and 256
 tokens, beside torch's bf16 product with the unquantized weights, and prints its own
 JSON line.
 """
@@ -282,7 +282,7 @@ def config_cpu_baseline(layers):
 
 
 def linear_bench(args, g, q, W, r, d):
-    """Time gptq_quantized_linear on the quantized metric layer for 1, 4, 16, 32, 64 and 128 bf16
+    """Time gptq_quantized_linear on the quantized metric layer for 1, 4, 16, 32, 64, 128 and 256 bf16
     tokens, and torch's bf16 product with the unquantized weights on the same
     activations.  Each is captured as a graph of 100 back-to-back calls (so that host
     launch overhead does not hide the kernel time) and replayed: HIP events around 5
@@ -310,7 +310,7 @@ def linear_bench(args, g, q, W, r, d):
 
     gen = torch.Generator(device="cuda").manual_seed(5)
     per = {}
-    for nt in (1, 4, 16, 32, 64, 128):
+    for nt in (1, 4, 16, 32, 64, 128, 256):
         x = torch.randn((nt, d), generator=gen, device="cuda").to(torch.bfloat16)
         y = torch.empty((nt, r), dtype=torch.bfloat16, device="cuda")
         yb = torch.empty((nt, r), dtype=torch.bfloat16, device="cuda")
@@ -327,7 +327,7 @@ def linear_bench(args, g, q, W, r, d):
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "the quantized attention projection of the layer step (4096x4096, int4 asym g128), "
-                               "bf16 activations of 1, 4, 16, 32, 64 and 128 tokens, bf16 output", "d_row": r, "d_col": d},
+                               "bf16 activations of 1, 4, 16, 32, 64, 128 and 256 tokens, bf16 output", "d_row": r, "d_col": d},
         "per_tokens": per,
         "roofline": {"kernel": "linear_kernel (1 token)", "bound": "hbm", "achieved": one["GBps"],
                      "peak": HBM_GBS, "unit": "GB/s", "frac": one["GBps"] / HBM_GBS,

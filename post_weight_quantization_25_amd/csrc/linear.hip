@@ -393,7 +393,8 @@ template <int CB, gptq_dtype XT, gptq_dtype YT>
 static void launch_mfma(const LinArgs& a, hipStream_t s) {
     // 16 tokens or fewer: 16-row workgroups (enough of them to fill the device); beyond,
     // 32-row workgroups, so that each activation fragment serves two row blocks and the
-    // activations are read from L2 half as often
+    // activations are read from L2 half as often; 64-row workgroups once there are
+    // enough of them
     const unsigned g16 = (unsigned)((a.d_row + 15) / 16), g32 = (unsigned)((a.d_row + 31) / 32);
     if (a.n_tok <= 16 || LIN_NTT_MAX == 1)
         linear_mfma_kernel<CB, 1, 1, XT, YT><<<dim3(g16, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
@@ -401,6 +402,10 @@ static void launch_mfma(const LinArgs& a, hipStream_t s) {
         linear_mfma_kernel<CB, 1, LIN_RB, XT, YT><<<dim3(LIN_RB == 2 ? g32 : g16, (unsigned)((a.n_tok + 15) / 16)), 64 * MW, 0, s>>>(a);
     else if (a.n_tok <= 64 || LIN_NTT_MAX == 2)
         linear_mfma_kernel<CB, 2, LIN_RB, XT, YT><<<dim3(LIN_RB == 2 ? g32 : g16, (unsigned)((a.n_tok + 31) / 32)), 64 * MW, 0, s>>>(a);
+    else if ((int64_t)((a.d_row + 63) / 64) * ((a.n_tok + 63) / 64) >= 256)
+        // enough 64-row x 64-token workgroups to fill the device: each activation fragment
+        // serves four row blocks (1 workgroup per CU: 128 KB of LDS for the reduction)
+        linear_mfma_kernel<CB, 4, 4, XT, YT><<<dim3((unsigned)((a.d_row + 63) / 64), (unsigned)((a.n_tok + 63) / 64)), 64 * MW, 0, s>>>(a);
     else linear_mfma_kernel<CB, 4, LIN_RB, XT, YT><<<dim3(LIN_RB == 2 ? g32 : g16, (unsigned)((a.n_tok + 63) / 64)), 64 * MW, 0, s>>>(a);
 }
 

@@ -83,6 +83,9 @@ CASES = [
     (64, 1280, 4, 128, 33, torch.bfloat16, torch.float32, 8),      # padded x rows (16-byte aligned)
     (48, 512, 4, 128, 30, torch.bfloat16, torch.float32, 0),       # 32-row workgroups, the second half past the end
     (4096, 4096, 4, 128, 64, torch.bfloat16, torch.bfloat16, 0),   # 64 tokens of the metric layer shape
+    (4096, 4096, 4, 128, 256, torch.bfloat16, torch.bfloat16, 0),  # 64-row workgroups (64 x 4 of them)
+    (4000, 256, 4, 128, 257, torch.bfloat16, torch.float32, 0),     # 64-row workgroups, ragged rows and tokens
+    (2050, 384, 3, 128, 500, torch.float16, torch.float32, 0),      # 64-row workgroups on the 3-bit stream
     # the 3-bit stream (12 bytes per 32 columns): decode, general and batched kernels
     (4096, 4096, 3, 128, 1, torch.bfloat16, torch.float32, 0),
     (300, 512, 3, 0, 3, torch.float16, torch.float32, 0),
