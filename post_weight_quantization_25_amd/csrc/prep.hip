@@ -1127,7 +1127,7 @@ static gptq_status trtri_block(PrepCtx& c, int64_t off, int64_t m, double* T, in
 #define AUX_MAX_WG_DEFER 0
 #endif
 #ifndef AUX_FORK_REST
-#define AUX_FORK_REST 2048
+#define AUX_FORK_REST 8192
 #endif
 #ifndef INV_LAST
 #define INV_LAST 512
