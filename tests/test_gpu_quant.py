@@ -42,6 +42,9 @@ CASES = [
     (65, 256, 8, 128, False, "f32"),
     (90, 320, 4, 64, False, "f32"),     # blocks 128, 128, 64
     (1, 256, 4, 128, False, "f32"),
+    # past one super-block: the trailing-update kernels and both deferral levels
+    (300, 2624, 4, 64, False, "bf16"),  # ragged row tiles and last block (64 columns), two macro-blocks
+    (130, 4160, 3, 0, True, "f32"),     # two whole macro-blocks and a 64-column tail
     # per tensor (group -1): one range for the whole matrix, stored as one group per row
     (300, 512, 4, -1, False, "f32"),
     (200, 384, 3, -1, True, "bf16"),
