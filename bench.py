@@ -99,9 +99,19 @@ def _committed(path):
 
 def measured_mfma_busy():
     """MFMA-busy fraction per kernel (Hessian, trailing update, sweep) of the 4096 x 4096
-    layer from the committed counter summary, or None when a source changed."""
-    t = _committed(MFMA_BUSY_FILE)
-    return None if t is None else t.get("mfma_busy")
+    layer from the committed counter summary; a kernel's entry is None once a file it is
+    built from changed since the counters were taken."""
+    try:
+        with open(MFMA_BUSY_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    hashes, deps = t.get("source_sha256_16", {}), t.get("kernel_sources", {})
+    out = {}
+    for k, v in t.get("mfma_busy", {}).items():
+        files = deps.get(k, list(hashes))
+        out[k] = v if files and all(f in hashes and source_hash(f) == hashes[f] for f in files) else None
+    return out
 
 
 def phase_rooflines(split, r, d, bits: int = 4, group: int = 128):
