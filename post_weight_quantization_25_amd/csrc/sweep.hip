@@ -182,9 +182,9 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
     const int nb = (int)((a.s1 - b0) < QB ? (a.s1 - b0) : QB);
     const int cb = (int)(b0 - a.s0);       // the block's first column in Wl
     float w[SSLOTS], e[SSLOTS];
-    // the code of each owned column: the E2M1 code, or for the integer grids q + zf as a
-    // float (converted once at the block end, off the steps' path)
-    using CodeT = typename std::conditional<FP4, int, float>::type;
+    // the code of each owned column, kept as a float and converted once at the block end,
+    // off the steps' path: for the integer grids q + zf, for E2M1 the signed grid value
+    using CodeT = float;
     CodeT cv[SSLOTS];
 #pragma unroll
     for (int i = 0; i < SSLOTS; ++i) {
@@ -314,12 +314,15 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         CodeT code;
         if constexpr (FP4) {
             // nearest E2M1 value (ties to the even mantissa, 6 beyond): steps of 0.5
-            // below 2, of 1 below 4, of 2 above; code = sign bit 8 | magnitude index
+            // below 2, of 1 below 4, of 2 above.  Every candidate is formed and then
+            // selected, so the step has no branches (written as nested conditional
+            // expressions, the compiler branched on them)
             const float m = fabsf(t);
-            const float v = m < 2.f ? 0.5f * rintf(2.f * m) : (m < 4.f ? rintf(m) : fminf(2.f * rintf(0.5f * m), 6.f));
+            const float v_lo = 0.5f * rintf(2.f * m), v_mid = rintf(m), v_hi = fminf(2.f * rintf(0.5f * m), 6.f);
+            float v = m < 4.f ? v_mid : v_hi;
+            v = m < 2.f ? v_lo : v;
             qd = copysignf(v, t);
-            const int idx = v < 2.f ? (int)(2.f * v) : (v < 4.f ? (int)v + 2 : (int)(0.5f * v) + 4);
-            code = idx + ((t < 0.f && v > 0.f) ? 8 : 0);
+            code = qd;
         } else {
             qd = __builtin_amdgcn_fmed3f(rintf(t), lo, hi);
             code = qd + zf;
@@ -361,8 +364,16 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         const uint16_t h = f32_to_f16_bits(x);
         ehs[rl][c] = h;
         els[rl][c] = f32_to_f16_bits(x - f16_bits_to_f32(h));
-        if constexpr (FP4) cl[rl][c] = (uint8_t)cv[i];
-        else cl[rl][c] = (uint8_t)((int)cv[i] + a.zoff);
+        if constexpr (FP4) {
+            // sign bit 8 | magnitude index (0 .. 7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6); a zero
+            // value has no sign bit
+            const float v = fabsf(cv[i]);
+            int idx = v < 4.f ? (int)v + 2 : (int)(0.5f * v) + 4;
+            idx = v < 2.f ? (int)(2.f * v) : idx;
+            cl[rl][c] = (uint8_t)(idx + (cv[i] < 0.f ? 8 : 0));
+        } else {
+            cl[rl][c] = (uint8_t)((int)cv[i] + a.zoff);
+        }
     }
     if (bad && rv) atomicOr(&bad_any, 1);
     // the global stores above and below need not have landed
