@@ -568,7 +568,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: the GPTQ layer quantizer runs on one GPU; only --gpus 1 is supported "
-              "(rows shard with no communication and H needs one all-reduce, which this build "
+              "(rows shard with no communication and H needs one all-reduce, which this library "
               "does not implement)", file=sys.stderr)
         sys.exit(2)
 

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     GPTQ_OK = 0,
     GPTQ_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size */
-    GPTQ_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+    GPTQ_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement */
     GPTQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
     GPTQ_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
     GPTQ_ERR_NOT_PD = 5,        /* used by bindings to report info > 0 */
@@ -115,7 +115,7 @@ typedef struct {
                             dequantize with gptq_dequantize_e2m1;
                          3: as 2 with S rounded up to a power of two (MXFP4).
                             Quantization concepts guide, "FP4 with block scales". */
-    int32_t block_size;  /* lazy-update block width; this build supports 128 */
+    int32_t block_size;  /* lazy-update block width; the library supports 128 */
 } gptq_params;
 
 /*
