@@ -32,7 +32,10 @@ def _problem(d_row, d_col, seed):
 @pytest.mark.parametrize("d_row,d_col,group,mx", [(300, 512, 128, False), (200, 384, 0, False), (65, 256, -1, False),
                                                   (130, 256, 32, False), (33, 320, 64, False),
                                                   (130, 256, 32, True), (200, 384, 0, True),
-                                                  (65, 256, -1, True), (300, 512, 128, True), (90, 320, 64, True)])
+                                                  (65, 256, -1, True), (300, 512, 128, True), (90, 320, 64, True),
+                                                  # several super-blocks (the trailing update between them, a
+                                                  # 256-column last one)
+                                                  (200, 1536, 128, False), (140, 1280, 32, True)])
 def test_fp4_quantize_parity(d_row, d_col, group, mx):
     import torch
     import post_weight_quantization_25_amd as g
