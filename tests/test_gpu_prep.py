@@ -164,3 +164,21 @@ def test_prep_parity_deferred_update(d):
     err = float(np.max(np.abs(Ug - Uo) / rowmax))
     log(f"prep parity d={d} (deferred update): max |dU| / rowmax = {err:.3e}")
     assert err <= 1e-6
+
+
+@pytest.mark.parametrize("d,dead", [(200, [0, 77, 199]), (1100, [5, 512, 513, 1099])])
+def test_prep_dead_channels(d, dead):
+    """Input channels that are zero in every token give zero rows and columns of H; the
+    damping alone keeps H + lambda I positive definite (no special case on either side)."""
+    log(f"prep with dead channels d={d} {dead}")
+    H32 = _h(d, max(2 * d, 64), 5)
+    H32[dead, :] = 0.0
+    H32[:, dead] = 0.0
+    Uo, _ = o.prepare_u(H32.astype(np.float64), 0.01)
+    Ug, info = _gpu_u(H32)
+    assert info == 0
+    assert np.all(np.isfinite(Ug))
+    rowmax = np.max(np.abs(Uo), axis=1, keepdims=True)
+    err = float(np.max(np.abs(Ug - Uo) / rowmax))
+    log(f"  max |dU| / rowmax = {err:.3e}")
+    assert err <= 1e-6
