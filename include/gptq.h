@@ -35,6 +35,11 @@
  *    gptq_prepare_hinv).  The call itself still returns GPTQ_OK.
  *  - Calls on one stream are ordered; concurrent calls on different streams
  *    must not share output or workspace buffers, nor a gptq_context.
+ *  - Size limits (beyond them GPTQ_ERR_UNSUPPORTED): d_col at most 65536 for
+ *    gptq_hessian_accumulate and 65535 for the factorization and the quantizers
+ *    (gptq_obq_layer: 2048); d_row at most 2^31 / 64 for the quantizers, d_row and
+ *    d_col at most 2^31 / 64 for the quantized linear.  Dequantization takes any
+ *    number of rows.
  */
 #ifndef GPTQ_MI355X_H
 #define GPTQ_MI355X_H

@@ -106,9 +106,30 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _tensor(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    """A contiguous device tensor of ``dtype`` (or one of a tuple of dtypes), ``shape`` and
+    ``device`` where given: what the kernels assume of every buffer they are handed."""
+    _dev(t, name)
+    if dtype is not None and not (t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype):
+        raise ValueError(f"{name} must have dtype {dtype}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+
+
+def _info(t: torch.Tensor, name: str, n: int, device):
+    _tensor(t, name, torch.int32, None, device)
+    if t.numel() < n:
+        raise ValueError(f"{name} must hold at least {n} int32")
+
+
 def _workspace(nbytes: int, device, ws):
+    """The caller's workspace (a uint8 device tensor) if it is large enough, else a new one."""
     if nbytes == 0:
         return None
+    if ws is not None:
+        _tensor(ws, "ws", torch.uint8, None, device)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
     return ws
@@ -179,6 +200,8 @@ def hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ws: torch.Tensor | None
     n, d = X.shape
     if d != H.shape[0]:
         raise ValueError("X width must match H")
+    if X.device != H.device:
+        raise ValueError("X and H must be on the same device")
     ws = _workspace(hessian_workspace_size(n, d), X.device, ws)
     _check(lib.gptq_hessian_accumulate(H.data_ptr(), X.data_ptr(), _DT[X.dtype], n, d, X.stride(0),
                                        ws.data_ptr() if ws is not None else None,
@@ -200,11 +223,16 @@ def prepare_hinv(H: torch.Tensor, percdamp: float = 0.01, U: torch.Tensor | None
     With a Context the triangular inverse overlaps the factorization on its auxiliary
     stream; without one every kernel runs on ``stream`` (the same U either way)."""
     _dev(H, "H")
+    if H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be a square matrix")
     d = H.shape[0]
+    _tensor(H, "H", torch.float32)
     if U is None:
         U = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    _tensor(U, "U", torch.float32, (d, d), H.device)
     if info is None:
         info = torch.zeros(1, dtype=torch.int32, device=H.device)
+    _info(info, "info", 1, H.device)
     ws = _workspace(prepare_hinv_workspace_size(d), H.device, ws)
     _check(lib.gptq_prepare_hinv(H.data_ptr(), U.data_ptr(), d, float(percdamp),
                                  ws.data_ptr() if ws is not None else None,
@@ -234,6 +262,34 @@ def code_bytes(bits: int, d_col: int) -> int:
     return d_col // 8 * 3 if bits == 3 else d_col // 2 if bits == 4 else d_col
 
 
+def _n_groups(group_size: int, d_col: int) -> int:
+    return 1 if group_size <= 0 else max(1, d_col // group_size)
+
+
+def _check_quantized(q: Quantized, name: str, d_row: int, device, zeros: bool = True):
+    """q's arrays have the shapes and dtypes its bits, group size and width imply."""
+    ng = _n_groups(q.group_size, q.d_col)
+    _tensor(q.codes, f"{name}.codes", torch.uint8, (d_row, code_bytes(q.bits, q.d_col)), device)
+    _tensor(q.scales, f"{name}.scales", torch.float16, (d_row, ng), device)
+    if zeros:
+        _tensor(q.zeros, f"{name}.zeros", torch.float16, (d_row, ng), device)
+
+
+def _check_out(q: Quantized, d_row: int, d_col: int, bits: int, group_size: int, fp4: bool, device):
+    if (q.bits, q.group_size, q.d_col, bool(q.fp4)) != (bits, group_size, d_col, bool(fp4)):
+        raise ValueError(f"out was made for bits {q.bits}, group {q.group_size}, width {q.d_col}, fp4 {q.fp4}; "
+                         f"this call has {bits}, {group_size}, {d_col}, {fp4}")
+    _check_quantized(q, "out", d_row, device)
+    _info(q.info, "out.info", 1, device)
+
+
+def _check_wu(W: torch.Tensor, U: torch.Tensor):
+    _dev(W, "W"); _dev(U, "U")
+    if W.dim() != 2 or W.dtype not in _DT:
+        raise ValueError("W must be a 2-D f32/bf16/f16 matrix")
+    _tensor(U, "U", torch.float32, (W.shape[1], W.shape[1]), W.device)
+
+
 def make_params(bits=4, group_size=128, sym=False, block_size=128, fp4=False, mx=False) -> Params:
     """sym: symmetric integer grid; fp4: the E2M1 grid (bits 4); mx: with fp4, power-of-two
     group scales (MXFP4)."""
@@ -247,18 +303,17 @@ def quantize_workspace_size(d_row: int, d_col: int, p: Params) -> int:
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, group_size: int = 128, sym: bool = False,
                    block_size: int = 128, ws: torch.Tensor | None = None, out: Quantized | None = None,
                    stream=None, fp4: bool = False, mx: bool = False) -> Quantized:
-    _dev(W, "W"); _dev(U, "U")
-    if W.dtype not in _DT or U.dtype != torch.float32:
-        raise ValueError("W must be f32/bf16/f16 and U float32")
+    _check_wu(W, U)
     d_row, d_col = W.shape
     p = make_params(bits, group_size, sym, block_size, fp4, mx)
-    n_groups = 1 if group_size <= 0 else max(1, d_col // group_size)
+    n_groups = _n_groups(group_size, d_col)
     if out is None:
         cb = code_bytes(bits, d_col)
         out = Quantized(torch.empty((d_row, cb), dtype=torch.uint8, device=W.device),
                         torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
                         torch.empty((d_row, n_groups), dtype=torch.float16, device=W.device),
                         torch.zeros(1, dtype=torch.int32, device=W.device), bits, group_size, d_col, fp4)
+    _check_out(out, d_row, d_col, bits, group_size, fp4, W.device)
     ws = _workspace(quantize_workspace_size(d_row, d_col, p), W.device, ws)
     _check(lib.gptq_quantize_layer(W.data_ptr(), _DT[W.dtype], d_row, d_col, U.data_ptr(), ctypes.byref(p),
                                    out.codes.data_ptr(), out.scales.data_ptr(), out.zeros.data_ptr(),
@@ -276,11 +331,10 @@ def quantize_layer_noalloc(W: torch.Tensor, U: torch.Tensor, out: Quantized, bit
     """gptq_quantize_layer_noalloc: as quantize_layer, with the library's per-device scratch
     in place of a workspace, into caller-allocated outputs (nothing is allocated here, so
     it can be captured in a graph).  Calls that overlap on one GPU race on the scratch."""
-    _dev(W, "W"); _dev(U, "U")
-    if W.dtype not in _DT or U.dtype != torch.float32:
-        raise ValueError("W must be f32/bf16/f16 and U float32")
+    _check_wu(W, U)
     d_row, d_col = W.shape
     p = make_params(bits, group_size, sym, 128, fp4, mx)
+    _check_out(out, d_row, d_col, bits, group_size, fp4, W.device)
     _check(lib.gptq_quantize_layer_noalloc(W.data_ptr(), _DT[W.dtype], d_row, d_col, U.data_ptr(), ctypes.byref(p),
                                            out.codes.data_ptr(), out.scales.data_ptr(), out.zeros.data_ptr(),
                                            out.info.data_ptr(), _stream(stream)),
@@ -291,7 +345,7 @@ def quantize_layer_noalloc(W: torch.Tensor, U: torch.Tensor, out: Quantized, bit
 def obq_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, sym: bool = False, ws: torch.Tensor | None = None,
               out: Quantized | None = None, stream=None) -> Quantized:
     """OBQ (gptq_obq_layer): per-row greedy order, one group per row; a timing baseline."""
-    _dev(W, "W"); _dev(U, "U")
+    _check_wu(W, U)
     d_row, d_col = W.shape
     p = make_params(bits, 0, sym)
     if out is None:
@@ -299,6 +353,7 @@ def obq_layer(W: torch.Tensor, U: torch.Tensor, bits: int = 4, sym: bool = False
                         torch.empty((d_row, 1), dtype=torch.float16, device=W.device),
                         torch.empty((d_row, 1), dtype=torch.float16, device=W.device),
                         torch.zeros(1, dtype=torch.int32, device=W.device), bits, 0, d_col)
+    _check_out(out, d_row, d_col, bits, 0, False, W.device)
     ws = _workspace(int(lib.gptq_obq_workspace_size(d_row, d_col)), W.device, ws)
     _check(lib.gptq_obq_layer(W.data_ptr(), _DT[W.dtype], d_row, d_col, U.data_ptr(), ctypes.byref(p),
                               out.codes.data_ptr(), out.scales.data_ptr(), out.zeros.data_ptr(),
@@ -342,13 +397,15 @@ def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = Fal
     layer and the device int32[2 n] status array."""
     if not pairs:
         return [], info
+    dev = pairs[0][1].device
     for X, W in pairs:
         _dev(W, "W")
         if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1 or X.dtype not in _DT or W.dtype not in _DT:
             raise ValueError("X must be 2-D with unit column stride and f32/bf16/f16, W f32/bf16/f16")
-        if X.shape[1] != W.shape[1]:
+        if W.dim() != 2 or X.shape[1] != W.shape[1]:
             raise ValueError("X and W must have the same d_col")
-    dev = pairs[0][1].device
+        if X.device != dev or W.device != dev:
+            raise ValueError("every X and W must be on one device")
     p = make_params(bits, group_size, sym)
     if outs is None:
         outs = []
@@ -359,8 +416,13 @@ def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = Fal
                                   torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),
                                   torch.empty((d_row, n_groups), dtype=torch.float16, device=dev),
                                   torch.zeros(1, dtype=torch.int32, device=dev), bits, group_size, d_col))
+    if len(outs) != len(pairs):
+        raise ValueError("outs must hold one Quantized per (X, W) pair")
+    for (_, W), q in zip(pairs, outs):
+        _check_out(q, W.shape[0], W.shape[1], bits, group_size, False, dev)
     if info is None:
         info = torch.empty(2 * len(pairs), dtype=torch.int32, device=dev)
+    _info(info, "info", 2 * len(pairs), dev)
     need = int(lib.gptq_quantize_layers_workspace_size(_layer_descs_shapes(pairs), len(pairs), n_slots))
     ws = _workspace(need, dev, ws)
     descs = _layer_descs(pairs, outs)
@@ -372,9 +434,12 @@ def quantize_layers(pairs, bits: int = 4, group_size: int = 128, sym: bool = Fal
 
 
 def dequantize(q: Quantized, out_dtype=torch.float32, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _dev(q.codes, "q.codes")
     d_row = q.codes.shape[0]
+    _check_quantized(q, "q", d_row, q.codes.device, zeros=not q.fp4)
     if out is None:
         out = torch.empty((d_row, q.d_col), dtype=out_dtype, device=q.codes.device)
+    _tensor(out, "out", tuple(_DT), (d_row, q.d_col), q.codes.device)
     if q.fp4:
         _check(lib.gptq_dequantize_e2m1(q.codes.data_ptr(), q.scales.data_ptr(), d_row, q.d_col, q.group_size,
                                         out.data_ptr(), _DT[out.dtype], _stream(stream)), "gptq_dequantize_e2m1")
@@ -395,11 +460,14 @@ def linear(q: Quantized, x: torch.Tensor, out_dtype=torch.float32, out: torch.Te
         raise ValueError("x must be a device tensor")
     if x.dtype not in _DT or x.dim() != 2 or x.shape[1] != q.d_col or (x.shape[0] > 0 and x.stride(1) != 1):
         raise ValueError("x must be a (n_tokens, d_col) f32/bf16/f16 tensor with unit column stride")
+    _dev(q.codes, "q.codes")
     d_row, n = q.codes.shape[0], x.shape[0]
+    _check_quantized(q, "q", d_row, x.device)
     if out is None:
         out = torch.empty((n, d_row), dtype=out_dtype, device=x.device)
     if not out.is_contiguous() or tuple(out.shape) != (n, d_row):
         raise ValueError("out must be a contiguous (n_tokens, d_row) tensor")
+    _tensor(out, "out", tuple(_DT), (n, d_row), x.device)
     _check(lib.gptq_quantized_linear(q.codes.data_ptr(), q.scales.data_ptr(), q.zeros.data_ptr(), d_row, q.d_col,
                                      q.bits, q.group_size, x.data_ptr(), _DT[x.dtype], n, max(x.stride(0), q.d_col),
                                      out.data_ptr(), _DT[out.dtype], _stream(stream)),

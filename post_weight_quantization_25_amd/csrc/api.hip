@@ -189,7 +189,7 @@ gptq_status gptq_dequantize(const uint8_t* codes, const uint16_t* scales_f16, co
     if (bits == 3 && (d_col & 7)) return GPTQ_ERR_INVALID_ARG;
     if (d_row == 0 || d_col == 0) return GPTQ_OK;
     if (!codes || !scales_f16 || !zeros_f16 || !W_out) return GPTQ_ERR_INVALID_ARG;
-    if (d_row > 65535) return GPTQ_ERR_UNSUPPORTED;
+    if (d_col > 2147483647LL) return GPTQ_ERR_UNSUPPORTED;   // group counts are 32-bit
     return dequant_launch(codes, scales_f16, zeros_f16, d_row, d_col, bits, group_size, W_out, out_dtype,
                           (hipStream_t)stream);
 }
@@ -201,7 +201,7 @@ gptq_status gptq_dequantize_e2m1(const uint8_t* codes, const uint16_t* scales_f1
     if (group_size > 0 && d_col % group_size != 0) return GPTQ_ERR_INVALID_ARG;
     if (d_row == 0 || d_col == 0) return GPTQ_OK;
     if (!codes || !scales_f16 || !W_out) return GPTQ_ERR_INVALID_ARG;
-    if (d_row > 65535) return GPTQ_ERR_UNSUPPORTED;
+    if (d_col > 2147483647LL) return GPTQ_ERR_UNSUPPORTED;   // group counts are 32-bit
     // the zero array is not read on this grid: pass the scales in its place
     return dequant_launch(codes, scales_f16, scales_f16, d_row, d_col, 4, group_size, W_out, out_dtype,
                           (hipStream_t)stream, true);

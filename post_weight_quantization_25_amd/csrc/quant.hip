@@ -1049,79 +1049,81 @@ GPTQ_DEV float e2m1_value(uint32_t u) {
 template <int BITS, gptq_dtype OT, bool FP4 = false>
 __global__ void dequant_kernel(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t d_row,
                                int64_t d_col, int G, void* out) {
-    const int64_t row = blockIdx.y;
     const int64_t chunks = (d_col + 7) / 8;
     const int64_t code_ld = (BITS == 3) ? d_col / 8 * 3 : (BITS <= 4) ? d_col / 2 : d_col;
     const int n_groups = (G == 0) ? 1 : (int)(d_col / G);
     constexpr int OB = (OT == GPTQ_F32) ? 4 : 2;     // output bytes per value
-    const bool fast = (d_col % 8 == 0) && (G % 8 == 0) &&
-                      (BITS == 3 || ((reinterpret_cast<uintptr_t>(codes) & 7) == 0)) &&
-                      ((reinterpret_cast<uintptr_t>(out) & 15) == 0) &&
-                      (BITS == 3 || (code_ld * row) % ((BITS <= 4) ? 4 : 8) == 0) && ((d_col * OB) % 16 == 0);
-    for (int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ch < chunks; ch += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t c0 = ch * 8;
-        float v[8];
-        if (fast) {
-            uint32_t u[8];
-            if constexpr (BITS == 3) {
-                const uint32_t g24 = load_u24(codes + row * code_ld + c0 / 8 * 3);
+    // rows beyond the grid's y extent (at most 65535) are taken in strides of it
+    for (int64_t row = blockIdx.y; row < d_row; row += gridDim.y) {
+        const bool fast = (d_col % 8 == 0) && (G % 8 == 0) &&
+                          (BITS == 3 || ((reinterpret_cast<uintptr_t>(codes) & 7) == 0)) &&
+                          ((reinterpret_cast<uintptr_t>(out) & 15) == 0) &&
+                          (BITS == 3 || (code_ld * row) % ((BITS <= 4) ? 4 : 8) == 0) && ((d_col * OB) % 16 == 0);
+        for (int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ch < chunks; ch += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t c0 = ch * 8;
+            float v[8];
+            if (fast) {
+                uint32_t u[8];
+                if constexpr (BITS == 3) {
+                    const uint32_t g24 = load_u24(codes + row * code_ld + c0 / 8 * 3);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) u[e] = code3(g24, e);
-            } else if constexpr (BITS <= 4) {
-                const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + row * code_ld + c0 / 2);
+                    for (int e = 0; e < 8; ++e) u[e] = code3(g24, e);
+                } else if constexpr (BITS <= 4) {
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + row * code_ld + c0 / 2);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) u[e] = (w >> (4 * e)) & 0xFu;
-            } else {
-                const uint2 w = *reinterpret_cast<const uint2*>(codes + row * code_ld + c0);
+                    for (int e = 0; e < 8; ++e) u[e] = (w >> (4 * e)) & 0xFu;
+                } else {
+                    const uint2 w = *reinterpret_cast<const uint2*>(codes + row * code_ld + c0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { u[e] = (w.x >> (8 * e)) & 0xFFu; u[4 + e] = (w.y >> (8 * e)) & 0xFFu; }
-            }
-            const int g = (G == 0) ? 0 : (int)(c0 / G);
-            const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
-            const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = FP4 ? sc * e2m1_value(u[e]) : sc * ((float)u[e] - z);
-            if constexpr (OT == GPTQ_F32) {
-                f32x4_t* o = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + row * d_col + c0);
-                o[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-                o[1] = f32x4_t{v[4], v[5], v[6], v[7]};
-            } else {
-                uint32_t p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = (OT == GPTQ_BF16) ? f32_to_bf16_bits(v[2 * e]) : f32_to_f16_bits(v[2 * e]);
-                    const uint32_t hi = (OT == GPTQ_BF16) ? f32_to_bf16_bits(v[2 * e + 1]) : f32_to_f16_bits(v[2 * e + 1]);
-                    p[e] = lo | (hi << 16);
+                    for (int e = 0; e < 4; ++e) { u[e] = (w.x >> (8 * e)) & 0xFFu; u[4 + e] = (w.y >> (8 * e)) & 0xFFu; }
                 }
-                *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + row * d_col + c0) = u32x4_t{p[0], p[1], p[2], p[3]};
-            }
-            continue;
-        }
+                const int g = (G == 0) ? 0 : (int)(c0 / G);
+                const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
+                const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t c = c0 + e;
-            if (c >= d_col) { v[e] = 0.f; continue; }
-            uint32_t u;
-            if constexpr (BITS == 3) {
-                u = code3(load_u24(codes + row * code_ld + c / 8 * 3), (int)(c & 7));
-            } else if constexpr (BITS <= 4) {
-                const uint8_t b = codes[row * code_ld + (c >> 1)];
-                u = (c & 1) ? (b >> 4) : (b & 0xF);
-            } else {
-                u = codes[row * code_ld + c];
-            }
-            const int g = (G == 0) ? 0 : (int)(c / G);
-            const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
-            const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
-            v[e] = FP4 ? sc * e2m1_value(u) : sc * ((float)u - z);
-        }
+                for (int e = 0; e < 8; ++e) v[e] = FP4 ? sc * e2m1_value(u[e]) : sc * ((float)u[e] - z);
+                if constexpr (OT == GPTQ_F32) {
+                    f32x4_t* o = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + row * d_col + c0);
+                    o[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+                    o[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+                } else {
+                    uint32_t p[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t c = c0 + e;
-            if (c >= d_col) break;
-            if constexpr (OT == GPTQ_F32) reinterpret_cast<float*>(out)[row * d_col + c] = v[e];
-            else if constexpr (OT == GPTQ_BF16) reinterpret_cast<uint16_t*>(out)[row * d_col + c] = f32_to_bf16_bits(v[e]);
-            else reinterpret_cast<uint16_t*>(out)[row * d_col + c] = f32_to_f16_bits(v[e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = (OT == GPTQ_BF16) ? f32_to_bf16_bits(v[2 * e]) : f32_to_f16_bits(v[2 * e]);
+                        const uint32_t hi = (OT == GPTQ_BF16) ? f32_to_bf16_bits(v[2 * e + 1]) : f32_to_f16_bits(v[2 * e + 1]);
+                        p[e] = lo | (hi << 16);
+                    }
+                    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + row * d_col + c0) = u32x4_t{p[0], p[1], p[2], p[3]};
+                }
+                continue;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t c = c0 + e;
+                if (c >= d_col) { v[e] = 0.f; continue; }
+                uint32_t u;
+                if constexpr (BITS == 3) {
+                    u = code3(load_u24(codes + row * code_ld + c / 8 * 3), (int)(c & 7));
+                } else if constexpr (BITS <= 4) {
+                    const uint8_t b = codes[row * code_ld + (c >> 1)];
+                    u = (c & 1) ? (b >> 4) : (b & 0xF);
+                } else {
+                    u = codes[row * code_ld + c];
+                }
+                const int g = (G == 0) ? 0 : (int)(c / G);
+                const float sc = f16_bits_to_f32(scales[row * n_groups + g]);
+                const float z = f16_bits_to_f32(zeros[row * n_groups + g]);
+                v[e] = FP4 ? sc * e2m1_value(u) : sc * ((float)u - z);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t c = c0 + e;
+                if (c >= d_col) break;
+                if constexpr (OT == GPTQ_F32) reinterpret_cast<float*>(out)[row * d_col + c] = v[e];
+                else if constexpr (OT == GPTQ_BF16) reinterpret_cast<uint16_t*>(out)[row * d_col + c] = f32_to_bf16_bits(v[e]);
+                else reinterpret_cast<uint16_t*>(out)[row * d_col + c] = f32_to_f16_bits(v[e]);
+            }
         }
     }
 }
@@ -1143,7 +1145,7 @@ gptq_status dequant_launch(const uint8_t* codes, const uint16_t* scales, const u
                            int64_t d_col, int bits, int group_size, void* out, gptq_dtype out_dtype,
                            hipStream_t s, bool fp4) {
     const int64_t chunks = (d_col + 7) / 8;
-    dim3 grid((unsigned)std::min<int64_t>((chunks + 255) / 256, 64), (unsigned)d_row);
+    dim3 grid((unsigned)std::min<int64_t>((chunks + 255) / 256, 64), (unsigned)std::min<int64_t>(d_row, 65535));
     if (fp4) return dq_dt<4, true>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     if (bits == 3) return dq_dt<3>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
     if (bits <= 4) return dq_dt<4>(out_dtype, grid, s, codes, scales, zeros, d_row, d_col, group_size, out);
