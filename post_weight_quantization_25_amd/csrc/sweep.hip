@@ -277,8 +277,7 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
 #pragma unroll
                     for (int i = ij; i < SSLOTS; ++i) if (i < iend) am = fmaxf(am, fabsf(w[i]));
                     am = row_max(am);
-                    sc = am > 0.f ? am / fqmax : 1.f;
-                    if (FP4 && a.mx) sc = pow2_ceil(sc);
+                    sc = am > 0.f ? range_scale16(true, 0.f, 0.f, am, fqmax, FP4 && a.mx) : 1.f;
                 } else {
                     float mx = w[ij];
                     mn = w[ij];
@@ -288,9 +287,9 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
                     mn = row_min(mn);
                     mx = row_max(mx);
                     if (mn == mx) { mn = fminf(mn, 0.f); mx = fmaxf(mx, 0.f); }
-                    sc = (mx > mn) ? (mx - mn) / (fqmax - fqmin) : 1.f;
+                    sc = (mx > mn) ? range_scale16(false, mn, mx, 0.f, fqmax - fqmin, false) : 1.f;
                 }
-                s16f = f16_bits_to_f32(f32_to_f16_bits(sc));
+                s16f = sc;   // an fp16 value
                 if (!normal_f16_scale(s16f)) { bad = true; s16f = 1.f; }
                 r16f = 1.0f / s16f;
                 zf = (FP4 || a.sym) ? 0.f : fqmin - rintf(mn / s16f);
@@ -305,7 +304,10 @@ __global__ __launch_bounds__(QT) void sweep_kernel(SweepArgs a) {
         }
         // quantize column j (owner: lane qj of the row, slot ij).  t = w / S16 correctly
         // rounded: q0 = w r with r = 1 / S16 correctly rounded, then one correction with
-        // the exact residual w - q0 S16 (Markstein); equal to the IEEE quotient.  The code
+        // the exact residual w - q0 S16 (Markstein); equal to the IEEE quotient, whose
+        // rounding to an integer is that of the exact w / S16 wherever |t| < 4096 (there a
+        // half-integer times S16 is an fp32 number, so t cannot reach or cross one that
+        // w / S16 is not).  The code
         // is rne(t) + zf clamped to the grid (zf is an integer, so this is exact).
         const float wv = w[ij];
         const float q0 = wv * r16f;

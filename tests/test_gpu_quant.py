@@ -136,6 +136,89 @@ def test_quantize_near_constant_group_reports_info():
     assert int(q.info.item()) == -1
 
 
+def _near_midpoint_groups(d_row, d_col, gsz, qspan, absmax, pow2, seed):
+    """fp32 weights whose groups have range / qspan (absmax / qspan) within 2^-24 .. 2^-28
+    relative of an fp16 rounding midpoint (pow2: just above a power of two), or on it."""
+    rng = np.random.default_rng(seed)
+    W = np.zeros((d_row, d_col), dtype=np.float32)
+    deltas = np.array([-2.0 ** -24, -2.0 ** -26, -2.0 ** -28, 0.0, 2.0 ** -28, 2.0 ** -26, 2.0 ** -24])
+    for r in range(d_row):
+        for c0 in range(0, d_col, gsz):
+            if pow2:
+                m = 2.0 ** int(rng.integers(-9, -3))
+                y = m * (1.0 + abs(rng.choice(deltas)) + 2.0 ** -30)
+            else:
+                h = np.float16(rng.uniform(2e-3, 4e-2)).view(np.uint16)
+                lo = np.array([h], dtype=np.uint16).view(np.float16)[0]
+                hi = np.array([h + 1], dtype=np.uint16).view(np.float16)[0]
+                m = (float(lo) + float(hi)) / 2.0
+                y = m * (1.0 + rng.choice(deltas))
+            v = np.empty(gsz, dtype=np.float32)
+            if absmax:
+                am = np.float32(qspan * y)
+                v[:] = rng.uniform(-0.9, 0.9, gsz) * am
+                v[rng.integers(gsz)] = am if rng.integers(2) else -am
+            else:
+                R = qspan * y
+                mn = np.float32(-rng.uniform(0.1, 0.9) * R)
+                mx = np.float32(float(mn) + R)
+                v[:] = rng.uniform(float(mn), float(mx), gsz)
+                i, j = rng.choice(gsz, 2, replace=False)
+                v[i], v[j] = mn, mx
+            W[r, c0:c0 + gsz] = v
+    return W
+
+
+@pytest.mark.parametrize("bits,group,sym,fp4,mx", [(4, 128, False, False, False), (4, 0, False, False, False),
+                                                  (8, 64, False, False, False), (4, 32, True, False, False),
+                                                  (4, 32, False, True, False), (4, 32, False, True, True)])
+def test_group_scales_are_exact_roundings(bits, group, sym, fp4, mx):
+    """With U = I nothing is compensated, so every group's range is that of the fp32
+    input.  In groups built next to an fp16 rounding midpoint of the scale (MXFP4: just
+    above a power of two), the stored scales and zeros equal the oracle's bit for bit.
+    On the asymmetric grid the range max - min is itself rounded in fp32, and rounding
+    that rounded difference's quotient would give the other neighbour in some of these
+    groups (the test shows it does); the kernel rounds the exact quotient.  An absmax
+    divided by a small integer needs no such care (its fp32 quotient never reaches an
+    fp16 midpoint it does not sit on), which the zero count of misses there shows."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    d_row, d_col = 64, 256
+    gsz = d_col if group == 0 else group
+    p = o.Params(bits=bits, group_size=group, sym=sym, fp4=fp4, mx=mx)
+    absmax = sym or fp4
+    qspan = 6.0 if fp4 else float(p.qmax if sym else p.qmax - p.qmin)
+    W = _near_midpoint_groups(d_row, d_col, gsz, qspan, absmax, mx, [bits, group, int(sym), int(fp4), int(mx)])
+    Wf = W.astype(np.float64)
+    ref = o.gptq_blocked(Wf, np.eye(d_col), p)
+    q = g.quantize_layer(torch.from_numpy(W).cuda(), torch.eye(d_col, device="cuda"), bits=bits, group_size=group,
+                         sym=sym, fp4=fp4, mx=mx)
+    torch.cuda.synchronize()
+    assert int(q.info.item()) == 0
+    s16 = q.scales.cpu().numpy()
+    assert np.array_equal(s16, ref.scales16), np.argwhere(s16 != ref.scales16)[:5]
+    if not fp4:
+        assert np.array_equal(q.zeros.cpu().numpy().astype(np.int64), ref.zeros.astype(np.int64))
+    # the fp32 quotient rounded to fp16 (or rounded up to a power of two) misses some
+    Wg = W.reshape(d_row, -1, gsz)
+    if absmax:
+        naive = np.max(np.abs(Wg), axis=2) / np.float32(qspan)
+        if mx:
+            mm, e = np.frexp(naive.astype(np.float64))
+            naive = np.ldexp(1.0, np.where(mm == 0.5, e - 1, e))
+    else:
+        naive = (np.max(Wg, axis=2) - np.min(Wg, axis=2)) / np.float32(qspan)
+    naive = naive.astype(np.float16)
+    n_miss = int(np.sum(naive != ref.scales16))
+    log(f"group scales int{bits} g{group} sym={sym} fp4={fp4} mx={mx}: {s16.size} groups equal; "
+        f"rounding the fp32 quotient would miss {n_miss}")
+    assert (n_miss == 0) if absmax else (n_miss > 0)
+    codes = unpack_codes(q.codes.cpu().numpy(), bits)
+    rep = tie_consistent_parity(codes, s16, q.zeros.cpu().numpy().astype(np.int64), Wf, np.eye(d_col), p,
+                                tie_window=1e-3, ref=ref)
+    assert_parity(rep, log)
+
+
 # 8-column vector path (width and group multiples of 8) and the element-wise path
 @pytest.mark.parametrize("bits,group,out,d_col", [(4, 128, "f32", 256), (3, 0, "bf16", 256), (4, 64, "f16", 256),
                                                   (8, 128, "f32", 256), (4, 6, "bf16", 258), (8, 12, "f32", 252),
