@@ -37,9 +37,10 @@
  *    must not share output or workspace buffers, nor a gptq_context.
  *  - Size limits (beyond them GPTQ_ERR_UNSUPPORTED): d_col at most 65536 for
  *    gptq_hessian_accumulate and 65535 for the factorization and the quantizers
- *    (gptq_obq_layer: 2048); d_row at most 2^31 / 64 for the quantizers, d_row and
- *    d_col at most 2^31 / 64 for the quantized linear.  Dequantization takes any
- *    number of rows.
+ *    (gptq_obq_layer: 2048); d_row at most 65535 * 128 = 8388480 for
+ *    gptq_quantize_layer, its _noalloc variant and gptq_quantize_layers, 2^31 / 64 for
+ *    gptq_obq_layer; for the quantized linear d_row and d_col at most 2^31 / 64 and
+ *    n_tokens at most 65535 * 64 = 4194240.  Dequantization takes any number of rows.
  */
 #ifndef GPTQ_MI355X_H
 #define GPTQ_MI355X_H

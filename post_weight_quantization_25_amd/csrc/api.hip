@@ -103,7 +103,7 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_row
     if (st != GPTQ_OK) return st;
     if (d_row == 0 || d_col == 0) return GPTQ_OK;
     if (!W || !U || !codes || !scales_f16 || !zeros_f16 || !info) return GPTQ_ERR_INVALID_ARG;
-    if (d_row > 2147483647LL / 64 || d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
+    if (d_row > QUANT_MAX_ROWS || d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
     return quant_launch(W, w_dtype, d_row, d_col, U, *p, codes, scales_f16, zeros_f16, ws, ws_bytes, info,
                         (hipStream_t)stream);
 }
@@ -116,7 +116,7 @@ gptq_status gptq_quantize_layer_noalloc(const void* W, gptq_dtype w_dtype, int64
     if (st != GPTQ_OK) return st;
     if (d_row == 0 || d_col == 0) return GPTQ_OK;
     if (!W || !U || !codes || !scales_f16 || !zeros_f16 || !info) return GPTQ_ERR_INVALID_ARG;
-    if (d_row > 2147483647LL / 64 || d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
+    if (d_row > QUANT_MAX_ROWS || d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
     if (quant_ws_bytes(d_row, d_col) > GPTQ_NOALLOC_SCRATCH_BYTES) return GPTQ_ERR_UNSUPPORTED;
     return quant_launch_noalloc(W, w_dtype, d_row, d_col, U, *p, codes, scales_f16, zeros_f16, info,
                                 (hipStream_t)stream);
@@ -135,7 +135,7 @@ static gptq_status check_layers(const gptq_layer* L, int32_t n, const gptq_param
             const gptq_status st = check_params(p, l.d_col);
             if (st != GPTQ_OK) return st;
         }
-        if (l.d_row > 2147483647LL / 64 || l.d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
+        if (l.d_row > QUANT_MAX_ROWS || l.d_col > 65535) return GPTQ_ERR_UNSUPPORTED;
     }
     return GPTQ_OK;
 }
@@ -220,7 +220,8 @@ gptq_status gptq_quantized_linear(const uint8_t* codes, const uint16_t* scales_f
     if (bits == 3 && (d_col & 7)) return GPTQ_ERR_INVALID_ARG;
     if (d_row == 0 || d_col == 0 || n_tokens == 0) return GPTQ_OK;
     if (!codes || !scales_f16 || !zeros_f16 || !x || !y || ldx < d_col) return GPTQ_ERR_INVALID_ARG;
-    if (d_row > 2147483647LL / 64 || d_col > 2147483647LL / 64) return GPTQ_ERR_UNSUPPORTED;
+    if (d_row > 2147483647LL / 64 || d_col > 2147483647LL / 64 || n_tokens > LINEAR_MAX_TOKENS)
+        return GPTQ_ERR_UNSUPPORTED;
     return linear_launch(codes, scales_f16, zeros_f16, d_row, d_col, bits, group_size, x, x_dtype, n_tokens, ldx, y,
                          y_dtype, (hipStream_t)stream);
 }

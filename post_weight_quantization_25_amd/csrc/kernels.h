@@ -49,6 +49,12 @@ gptq_status context_create(int n_slots, gptq_context** out);
 gptq_status context_destroy(gptq_context* ctx);
 
 constexpr int OBQ_MAXD = 2048;   // widest row the OBQ kernel keeps in LDS
+// Most rows of a quantizer call: the trailing-update launches put the 128-row tiles of W
+// on the grid's y extent (at most 65535).
+constexpr int64_t QUANT_MAX_ROWS = (int64_t)65535 * 128;
+// Most tokens of a quantized-linear call: its matrix-core launches put tiles of up to 64
+// tokens on the grid's y extent.
+constexpr int64_t LINEAR_MAX_TOKENS = (int64_t)65535 * 64;
 size_t obq_ws_bytes(int64_t d_row, int64_t d_col);
 gptq_status obq_launch(const void* W, gptq_dtype w_dtype, int64_t d_row, int64_t d_col, const float* U,
                        const gptq_params& p, uint8_t* codes, uint16_t* scales, uint16_t* zeros, void* ws,

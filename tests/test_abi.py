@@ -176,6 +176,8 @@ def test_quantize_argument_errors(lib):
     assert call(P(4, 128, 0, 128), W=None) == INVALID_ARG
     assert f(FAKE, BF16, 4, 256, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == INVALID_ARG
     assert call(P(4, 128, 0, 128), d_row=0, W=None) == OK    # empty
+    # rows beyond what the trailing update's grid holds (65535 tiles of 128), refused first
+    assert call(P(4, 128, 0, 128), d_row=65535 * 128 + 1) == UNSUPPORTED
 
 
 def test_dequantize_argument_errors(lib):
@@ -204,6 +206,7 @@ def test_linear_argument_errors(lib):
     assert call(codes=None) == INVALID_ARG
     assert call(y=None) == INVALID_ARG
     assert call(n=0, codes=None, x=None, y=None) == OK   # no tokens: no work
+    assert call(n=65535 * 64 + 1) == UNSUPPORTED       # more token tiles than the grid holds
 
 
 def _layers(lib, specs, ptr=FAKE):
@@ -315,6 +318,7 @@ def test_noalloc_argument_errors(lib):
     assert lib.gptq_quantize_workspace_size(4096, 4096, None) <= 256 << 20
     assert lib.gptq_quantize_workspace_size(8192, 8192, None) > 256 << 20
     assert call(8192, 8192) == UNSUPPORTED
+    assert call(65535 * 128 + 1, 256) == UNSUPPORTED    # rows beyond the trailing update's grid
     assert call(64, 256, prm=lib.Params(5, 128, 0, 128)) == UNSUPPORTED
     assert call(64, 250) == INVALID_ARG                 # group does not divide d_col
     assert call(64, 256, w=None) == INVALID_ARG
