@@ -50,6 +50,10 @@ CASES = [
     (200, 384, 3, -1, True, "bf16"),
     (65, 256, 8, -1, False, "f32"),
     (17, 200, 4, -1, False, "f32"),     # ragged last block, few rows
+    # odd widths (8-bit codes, one per byte: rows of codes at every byte alignment)
+    (40, 333, 8, 0, False, "f32"),
+    (33, 1111, 8, 0, True, "bf16"),     # past one super-block, a 87-column last block
+    (20, 2625, 8, 0, False, "f32"),     # two macro-blocks, a 65-column last block
 ]
 
 
