@@ -110,3 +110,41 @@ def test_layers_wait_bound_reports_minus_two():
         r = g.quantize_layer(W, U, bits=4, group_size=128)
         torch.cuda.synchronize()
         assert torch.equal(q.codes, r.codes) and torch.equal(q.scales, r.scales) and torch.equal(q.zeros, r.zeros)
+
+
+def test_layers_deferred_widths_match_per_phase_calls():
+    """Widths where the factorization defers its trailing update (outer blocks of 256
+    columns from 4200, of 512 from 7168; 4736 and 7424 end in partial outer blocks), two
+    and three groups in flight on the context's slot streams, each with its own auxiliary
+    stream: bit-identical to one call per phase and layer."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    c4 = synth.config_layers(4)
+    xa, xb, xc = synth.scaled(c4[6], 192, 4736, 8192), synth.scaled(c4[0], 128, 7424, 8192), \
+        synth.scaled(c4[3], 160, 4736, 8192, seed_offset=600)
+    spec = [(xa, xa), (xa, synth.scaled(c4[1], 96, 4736, 8192)), (xb, xb), (xc, xc)]
+    xs, pairs = {}, []
+    for LX, LW in spec:
+        if LX.name not in xs:
+            xs[LX.name] = dev_tensor(layer_x(LX), LX.x_dtype)
+        pairs.append((xs[LX.name], dev_tensor(synth.weights(LW), LW.w_dtype)))
+    log(f"layers at deferred widths: {[tuple(W.shape) for _, W in pairs]}")
+    ref = []
+    for X, W in pairs:
+        H = torch.zeros((X.shape[1], X.shape[1]), dtype=torch.float32, device="cuda")
+        g.hessian_accumulate(H, X)
+        U, info = g.prepare_hinv(H, 0.01)
+        q = g.quantize_layer(W, U, bits=4, group_size=128)
+        torch.cuda.synchronize()
+        assert int(info.item()) == 0 and int(q.info.item()) == 0
+        ref.append((q.codes.cpu(), q.scales.cpu(), q.zeros.cpu()))
+    with g.Context(3) as ctx:
+        for slots in (2, 3):
+            outs, info = g.quantize_layers(pairs, bits=4, group_size=128, n_slots=slots, ctx=ctx)
+            torch.cuda.synchronize()
+            assert not info.cpu().any(), info.cpu()
+            for k, (q, (c, s, z)) in enumerate(zip(outs, ref)):
+                assert torch.equal(q.codes.cpu(), c), (slots, k)
+                assert torch.equal(q.scales.cpu(), s), (slots, k)
+                assert torch.equal(q.zeros.cpu(), z), (slots, k)
+            log(f"  {slots} slots: all {len(pairs)} layers bit-identical")
