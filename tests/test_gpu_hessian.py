@@ -144,3 +144,30 @@ def test_hessian_ignores_workspace_contents(n, d):
     assert np.all(np.isfinite(Hg))
     assert np.array_equal(Hg, Hg.T)
     assert _err(Hg, Ho) <= _tol(n, "bf16")
+
+
+def test_hessian_largest_width():
+    """d_col = 65536, the widest H the library takes (every 256 x 256 tile whole, H of
+    2^32 entries): 1024 bf16 tokens, sampled entries against fp64 sums (as at the other
+    widths), the last row and column equal bit for bit."""
+    import torch
+    import post_weight_quantization_25_amd as g
+    n, d = 1024, 65536
+    rng = np.random.default_rng([17, d])
+    log(f"hessian largest width {d}, {n} tokens")
+    X = torch.from_numpy(rng.standard_normal((n, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    cols = np.array(sorted({0, 1, 255, 256, d // 2, d - 257, d - 256, d - 2, d - 1} |
+                           set(rng.choice(d, 20, replace=False).tolist())))
+    Xs = X[:, torch.from_numpy(cols).cuda()].float().cpu().numpy().astype(np.float64)
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    g.hessian_accumulate(H, X)
+    torch.cuda.synchronize()
+    ct = torch.from_numpy(cols).cuda()
+    Hs = H.index_select(0, ct).index_select(1, ct).cpu().numpy().astype(np.float64)
+    assert torch.equal(H[d - 1], H[:, d - 1]) and torch.equal(H[0], H[:, 0])
+    Ho = 2.0 * (Xs.T @ Xs)
+    dg = np.sqrt(np.diag(Ho))
+    err = float(np.max(np.abs(Hs - Ho) / np.outer(dg, dg)))
+    tol = 2.0 * (n / 16 + 64) * 2.0 ** -24
+    log(f"  sampled {cols.size}x{cols.size}: max err {err:.3e} (bound {tol:.3e})")
+    assert err <= tol
