@@ -160,3 +160,37 @@ def test_linear_no_tokens_is_a_no_op():
                     torch.zeros(1, dtype=torch.int32, device="cuda"), 4, 32, 64)
     y = g.linear(q, torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"))
     assert tuple(y.shape) == (0, 32)
+
+
+WIDE = [
+    # the wide workloads' shapes: fc1, fc2, the MLP up (int4) and down (int3) layers
+    (49152, 12288, 4, 128, 1, torch.bfloat16),
+    (49152, 12288, 4, 128, 64, torch.float32),
+    (12288, 49152, 4, 128, 1, torch.float32),
+    (12288, 49152, 4, 128, 16, torch.bfloat16),
+    (11008, 4096, 4, 128, 300, torch.float32),
+    (4096, 11008, 3, 128, 1, torch.float32),
+    (4096, 11008, 3, 128, 40, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("d_row,d_col,bits,G,n,yt", WIDE)
+def test_linear_wide_sampled(d_row, d_col, bits, G, n, yt):
+    """Full-size layers of the wide workloads, bf16 x: every output of 256 sampled rows
+    (the first, the last, random) against the oracle, to the bound above."""
+    log(f"linear wide {d_row}x{d_col} bits={bits} G={G} n={n} y={yt}")
+    packed, scales, zeros, x = make_case(d_row, d_col, bits, G, n, 23)
+    y, xu = gpu_linear(packed, scales, zeros, x, bits, G, torch.bfloat16, yt, repeat=1)
+    rng = np.random.default_rng([d_row, d_col, n])
+    rows = np.array(sorted({0, 1, d_row - 1} | set(rng.choice(d_row, 253, replace=False).tolist())))
+    codes = o.unpack(packed[rows], bits)
+    ref = o.linear(xu, codes, scales[rows], zeros[rows], G)
+    What = o.dequantize(codes, scales[rows], zeros[rows], G).astype(np.float64)
+    mag = np.abs(xu) @ np.abs(What).T
+    bound = ((d_col + 64) * 2.0 ** -23 + 2.0 ** -18) * mag
+    if yt == torch.bfloat16:
+        bound = bound + 2.0 ** -8 * np.abs(ref) + 1e-30
+    err = np.abs(y[:, rows] - ref)
+    log(f"  {rows.size} sampled rows: max |err| / bound = {float(np.max(err / np.maximum(bound, 1e-300))):.3f}")
+    assert y.shape == (n, d_row)
+    assert np.all(err <= bound)
