@@ -80,12 +80,13 @@ def test_obq_parity(d_row, d_col, bits, sym):
         assert e_g <= 1.05 * e_o + 1e-12, (r, e_g, e_o)
 
 
-def test_obq_diagonal_hessian_is_round_to_nearest():
+@pytest.mark.parametrize("d_col", [128, 2048])     # 2048: the widest row the OBQ kernel takes
+def test_obq_diagonal_hessian_is_round_to_nearest(d_col):
     import torch
     import post_weight_quantization_25_amd as g
-    rng = np.random.default_rng(3)
-    W = (rng.standard_normal((33, 128)) * 0.02).astype(np.float32)
-    dg = rng.random(128) + 0.5
+    rng = np.random.default_rng([3, d_col])
+    W = (rng.standard_normal((33, d_col)) * 0.02).astype(np.float32)
+    dg = rng.random(d_col) + 0.5
     U = np.diag(1.0 / np.sqrt(dg)).astype(np.float32)        # (diag)^-1 = U^T U
     for bits, sym in ((4, False), (3, True), (8, False)):
         p = o.Params(bits=bits, group_size=0, sym=sym)
