@@ -370,16 +370,12 @@ def test_binding_rejects_mismatched_tensors():
 
 
 
-def test_per_tensor_wide():
-    """Per-tensor grid (group -1) at 2048 x 11008 (the MLP down recipe, 16384 tokens),
-    through the GPU's own H and U: the one scale and zero, reduced over all 22.5M weights,
-    equal the oracle's from the whole matrix bit for bit; 64 sampled rows then follow the
-    oracle's sweep with that grid and the GPU's U (same tie rule)."""
+def _wide_chain(r, d, n, seed_offset, bits, group, sym=False):
+    """The MLP down recipe at r x d with n tokens through the GPU's own H, U (with a
+    context) and sweep; returns (layer, W storage bits, q, U on the host in fp64)."""
     import torch
     import post_weight_quantization_25_amd as g
-    L = synth.scaled(synth.config_layers(3)[1], 2048, 11008, 16384, seed_offset=810)
-    n, d, r = L.n_tokens, L.d_col, L.d_row
-    log(f"per-tensor wide {r}x{d}, {n} tokens, int4 asym")
+    L = synth.scaled(synth.config_layers(3)[1], r, d, n, seed_offset=seed_offset)
     dev = torch.device("cuda:0")
     X = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
     for c, arr in enumerate(synth.x_chunks(L)):
@@ -391,9 +387,25 @@ def test_per_tensor_wide():
     g.hessian_accumulate(H, X)
     with g.Context(1) as ctx:
         U, info = g.prepare_hinv(H, 0.01, ctx=ctx)
-        q = g.quantize_layer(Wd, U, bits=4, group_size=-1)
+        q = g.quantize_layer(Wd, U, bits=bits, group_size=group, sym=sym)
         torch.cuda.synchronize()
     assert int(info.item()) == 0 and int(q.info.item()) == 0
+    return L, W, q, U.cpu().numpy().astype(np.float64)
+
+
+def _sample_rows(r, seed):
+    rng = np.random.default_rng(seed)
+    return np.array(sorted({0, 1, r - 1} | set(rng.choice(r, 61, replace=False).tolist())))
+
+
+def test_per_tensor_wide():
+    """Per-tensor grid (group -1) at 2048 x 11008 (the MLP down recipe, 16384 tokens),
+    through the GPU's own H and U: the one scale and zero, reduced over all 22.5M weights,
+    equal the oracle's from the whole matrix bit for bit; 64 sampled rows then follow the
+    oracle's sweep with that grid and the GPU's U (same tie rule)."""
+    import torch
+    log("per-tensor wide 2048x11008, 16384 tokens, int4 asym")
+    L, W, q, U64 = _wide_chain(2048, 11008, 16384, 810, 4, -1)
     p = o.Params(bits=4, group_size=-1, sym=False)
     Wf_all = synth.w_as_f64(W)
     _, S16o, Zo, _ = o.group_params(Wf_all, p)      # one range over every row
@@ -401,13 +413,28 @@ def test_per_tensor_wide():
     z = q.zeros.cpu().numpy().astype(np.int64)
     assert np.all(s16 == s16[0, 0]) and np.all(z == z[0, 0])
     assert float(s16[0, 0]) == float(S16o[0]) and int(z[0, 0]) - p.zero_offset == int(Zo[0])
-    rng = np.random.default_rng([d, 810])
-    rows = np.array(sorted({0, 1, r - 1} | set(rng.choice(r, 61, replace=False).tolist())))
-    rt = torch.from_numpy(rows).to(dev)
-    codes = unpack_codes(q.codes.index_select(0, rt).cpu().numpy(), 4)
-    U64 = U.cpu().numpy().astype(np.float64)
+    rows = _sample_rows(L.d_row, [L.d_col, 810])
+    codes = unpack_codes(q.codes.index_select(0, torch.from_numpy(rows).cuda()).cpu().numpy(), 4)
     Wf = Wf_all[rows]
     forced = {("g", j, 0): (float(S16o[0]), int(Zo[0])) for j in range(rows.size)}
     ref = o.gptq_blocked(Wf, U64, p, forced=forced)
     rep = tie_consistent_parity(codes, s16[rows], z[rows], Wf, U64, p, tie_window=1e-3, ref=ref)
+    assert_parity(rep, log)
+
+
+def test_group64_wide():
+    """Groups of 64 at 2048 x 11008 through the GPU's own H and U: 64 sampled rows against
+    the oracle's sweep with that U (same tie rule and 99.9% code bar)."""
+    import torch
+    log("g64 wide 2048x11008, 16384 tokens, int4 asym")
+    L, W, q, U64 = _wide_chain(2048, 11008, 16384, 820, 4, 64)
+    rows = _sample_rows(L.d_row, [L.d_col, 820])
+    rt = torch.from_numpy(rows).cuda()
+    codes = unpack_codes(q.codes.index_select(0, rt).cpu().numpy(), 4)
+    s16 = q.scales.index_select(0, rt).cpu().numpy()
+    z = q.zeros.index_select(0, rt).cpu().numpy().astype(np.int64)
+    p = o.Params(bits=4, group_size=64, sym=False)
+    Wf = synth.w_as_f64(W[rows])
+    ref = o.gptq_blocked(Wf, U64, p)
+    rep = tie_consistent_parity(codes, s16, z, Wf, U64, p, tie_window=1e-3, ref=ref)
     assert_parity(rep, log)
